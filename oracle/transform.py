@@ -1,0 +1,172 @@
+"""The two 128-point Hadamard rotations of the EXL3 linear (oracle; test
+infrastructure).
+
+Pages
+-----
+* Input side: x*suh, then the 128-point Hadamard transform in a fixed order
+  of fp32 adds, times 2**-4 (exact), rounded once to fp16 (TensorFold PR
+  "cuda: EXL3 projections behind qlinear", "Arithmetic" step 1).  suh is one
+  value per input channel and one row per shard of a fused layer (cuda-exl3
+  page, "Notes on the format").
+* Output side: the output transform, svh and 2**-3, one rounding to bf16
+  (TensorFold PR, "Arithmetic" step 3); the caller's dtype, bf16 or fp16, is
+  emitted directly (cuda-exl3, "One op per layer").
+* The rotation is block diagonal over 128-element blocks, so splitting the
+  input dim at multiples of 128 is exact (cuda-exl3, "Tensor parallel").
+
+Readings taken where the pages are silent
+-----------------------------------------
+R8  The Hadamard matrix is Sylvester's, natural order:
+    H[i][j] = (-1)**popcount(i & j); H @ H = 128 I.
+R9  The fp32 add order is the radix-2 butterfly with strides 1, 2, 4, ..., 64
+    in ascending order; at each stage the pair (a, b) = (t[e], t[e + s]),
+    e with bit s clear, becomes (a + b, a - b).  Both rotations use it.
+R10 Rounding is to nearest, ties to even, everywhere; subnormals are kept.
+R11 Output order: fp32 butterfly, then *2**-3 (exact), then *svh in fp32,
+    then one rounding to the output dtype.  x*suh in fp32 is exact (a bf16
+    times an fp16 needs 19 significant bits).
+
+Parity status: pinned by tests/test_oracle_transform.py (H @ H = 128 I,
+agreement with scipy.linalg.hadamard, the one-hot closed forms, the float32
+replay within one fp16 ulp of the exact fp64 rotation, block diagonality).
+The fp32 add order itself (R9) is a reading; the HIP kernels must reproduce
+it bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128
+STAGES = 7
+INPUT_SCALE = 2.0 ** -4
+OUTPUT_SCALE = 2.0 ** -3
+
+
+def sylvester(n: int = BLOCK) -> np.ndarray:
+    """Reading R8 written out element by element (float64)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    pc = np.vectorize(lambda a: bin(int(a)).count("1"))(i & j)
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def butterfly(t: np.ndarray) -> np.ndarray:
+    """Reading R9: unnormalised 128-point Hadamard over the last axis.
+
+    Runs in the dtype of ``t`` (float32 for the format's order, float64 for
+    the exact reference); every add is one IEEE operation of that dtype.
+    """
+    t = np.array(t, copy=True)
+    assert t.shape[-1] % BLOCK == 0
+    lead = t.shape[:-1]
+    nblk = t.shape[-1] // BLOCK
+    t = t.reshape(lead + (nblk, BLOCK))
+    for s in range(STAGES):
+        stride = 1 << s
+        v = t.reshape(lead + (nblk, BLOCK // (2 * stride), 2, stride))
+        a = v[..., 0, :].copy()
+        b = v[..., 1, :].copy()
+        v[..., 0, :] = a + b
+        v[..., 1, :] = a - b
+        t = v.reshape(lead + (nblk, BLOCK))
+    return t.reshape(lead + (nblk * BLOCK,))
+
+
+# ---------------------------------------------------------------------------
+# bit helpers (fp16 / bf16 <-> float)
+# ---------------------------------------------------------------------------
+
+def f16_from_bits(b: np.ndarray) -> np.ndarray:
+    return np.asarray(b, dtype=np.uint16).view(np.float16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float32 (exact: bf16 is the top half of a float32)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest, ties to even (R10).
+
+    Finite inputs only (the linear produces no inf/NaN on finite inputs).
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> fp16 bits, round to nearest, ties to even (numpy's cast)."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def x_to_f32(x_bits: np.ndarray, x_dtype: str) -> np.ndarray:
+    if x_dtype == "bf16":
+        return bf16_bits_to_f32(x_bits)
+    if x_dtype == "f16":
+        return f16_from_bits(x_bits).astype(np.float32)
+    raise ValueError(x_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Input rotation
+# ---------------------------------------------------------------------------
+
+def rotate_input(x_bits: np.ndarray, suh_bits: np.ndarray, x_dtype: str = "bf16") -> np.ndarray:
+    """x~ = fp16( H128(x*suh) * 2**-4 ), in the format's fp32 order.
+
+    x_bits [M, K] (bf16 or fp16 bits), suh_bits [S, K] fp16 bits.
+    Returns fp16 bits [S, M, K]: one rotated copy of x per shard.
+    """
+    x32 = x_to_f32(x_bits, x_dtype)
+    suh32 = f16_from_bits(suh_bits).astype(np.float32)
+    out = []
+    for s in range(suh32.shape[0]):
+        t = x32 * suh32[s][None, :]  # exact in float32 (R11)
+        h = butterfly(t.astype(np.float32))
+        out.append(f32_to_f16_bits(h * np.float32(INPUT_SCALE)))
+    return np.stack(out, axis=0)
+
+
+def rotate_input_f64(x_bits: np.ndarray, suh_bits: np.ndarray, x_dtype: str = "bf16") -> np.ndarray:
+    """The exact rotation H128(x*suh)*2**-4 in float64 (no rounding), [S, M, K]."""
+    x64 = x_to_f32(x_bits, x_dtype).astype(np.float64)
+    suh64 = f16_from_bits(suh_bits).astype(np.float64)
+    return np.stack([butterfly(x64 * suh64[s][None, :]) * INPUT_SCALE
+                     for s in range(suh64.shape[0])], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Output transform
+# ---------------------------------------------------------------------------
+
+def output_transform_f32(z32: np.ndarray, svh_bits: np.ndarray, out_dtype: str) -> np.ndarray:
+    """Reading R11 in float32: butterfly, *2**-3, *svh, one rounding.
+
+    z32 [M, N] float32 -> output bits [M, N] (bf16 or fp16).
+    """
+    h = butterfly(np.asarray(z32, dtype=np.float32))
+    h = h * np.float32(OUTPUT_SCALE)
+    y = h * f16_from_bits(svh_bits).astype(np.float32)[None, :]
+    if out_dtype == "bf16":
+        return f32_to_bf16_bits(y)
+    if out_dtype == "f16":
+        return f32_to_f16_bits(y)
+    raise ValueError(out_dtype)
+
+
+def output_transform_f64(z64: np.ndarray, svh_bits: np.ndarray) -> np.ndarray:
+    """Exact output transform in float64: H128(z) * 2**-3 * svh."""
+    h = butterfly(np.asarray(z64, dtype=np.float64))
+    return h * OUTPUT_SCALE * f16_from_bits(svh_bits).astype(np.float64)[None, :]
+
+
+def reduce_parts_f32(parts: np.ndarray) -> np.ndarray:
+    """Ordered fp32 sum of K-part partials: ((p0 + p1) + p2) + ...
+
+    ``parts`` [P, M, N] float32; the first part is taken as is (no 0 + p0).
+    """
+    acc = np.array(parts[0], dtype=np.float32, copy=True)
+    for p in range(1, parts.shape[0]):
+        acc = acc + parts[p].astype(np.float32)
+    return acc

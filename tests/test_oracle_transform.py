@@ -1,0 +1,126 @@
+"""Pins for oracle.transform: the Hadamard, both rotations and the roundings."""
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import transform as tf
+
+
+def test_sylvester_matches_scipy_and_is_orthogonal():
+    h = tf.sylvester()
+    assert np.array_equal(h, scipy.linalg.hadamard(128).astype(np.float64))
+    assert np.array_equal(h @ h, 128 * np.eye(128))
+
+
+def test_butterfly_is_the_hadamard_product():
+    h = scipy.linalg.hadamard(128).astype(np.float64)
+    for j in (0, 1, 5, 64, 127):
+        e = np.zeros(128)
+        e[j] = 1.0
+        assert np.array_equal(tf.butterfly(e), h[:, j])  # one-hot closed form
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((3, 384))
+    want = (v.reshape(3, 3, 128) @ h).reshape(3, 384)  # block diagonal
+    assert np.allclose(tf.butterfly(v), want, rtol=0, atol=1e-12)
+
+
+def test_butterfly_float32_add_order():
+    # Strides ascend: with t = [1, 0, 2**-24, 2**-24, 0, ...] stage 0 forms
+    # t2 + t3 = 2**-23 first, and stage 1 adds it to t0 + t1 = 1 exactly:
+    # out[0] = 1 + 2**-23.  With descending strides t0 would meet t2 first and
+    # 1 + 2**-24 rounds (ties to even) to 1, twice: out[0] = 1.
+    t = np.zeros(128, dtype=np.float32)
+    t[0], t[2], t[3] = 1.0, 2.0 ** -24, 2.0 ** -24
+    out = tf.butterfly(t)
+    assert out.dtype == np.float32 and out[0] == np.float32(1.0 + 2.0 ** -23)
+
+
+def test_rotate_one_hot_closed_form():
+    # x = e_j (bf16 1.0 = 0x3F80), suh = 1: x~ = +-2**-4 (fp16 0x2C00 / 0xAC00)
+    # following the signs of Hadamard column j.
+    h = scipy.linalg.hadamard(128)
+    for j in (0, 3, 77, 127):
+        x = np.zeros((1, 128), dtype=np.uint16)
+        x[0, j] = 0x3F80
+        suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
+        xr = tf.rotate_input(x, suh, "bf16")[0, 0]
+        want = np.where(h[:, j] > 0, 0x2C00, 0xAC00).astype(np.uint16)
+        assert np.array_equal(xr, want)
+
+
+def test_rotate_replay_within_one_ulp_of_exact():
+    rng = np.random.default_rng(2)
+    x = tf.f32_to_bf16_bits(rng.standard_normal((9, 512)).astype(np.float32))
+    suh = (np.where(rng.integers(0, 2, (2, 512)) == 1, -1.0, 1.0)
+           * np.exp2(rng.uniform(-2, 2, (2, 512)))).astype(np.float16).view(np.uint16)
+    xr = tf.f16_from_bits(tf.rotate_input(x, suh)).astype(np.float64)
+    ex = tf.rotate_input_f64(x, suh)
+    ulp = np.spacing(np.abs(ex).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(xr - ex) <= ulp)
+    # and the suh scale really is applied per shard
+    assert not np.array_equal(xr[0], xr[1])
+
+
+def test_rotate_block_diagonal():
+    # Splitting K at a multiple of 128 is exact (the pages' tensor-parallel note).
+    rng = np.random.default_rng(3)
+    x = tf.f32_to_bf16_bits(rng.standard_normal((4, 256)).astype(np.float32))
+    suh = np.full((1, 256), 0xBC00, dtype=np.uint16)
+    whole = tf.rotate_input(x, suh)
+    left = tf.rotate_input(x[:, :128], suh[:, :128])
+    right = tf.rotate_input(x[:, 128:], suh[:, 128:])
+    assert np.array_equal(whole, np.concatenate([left, right], axis=-1))
+
+
+def test_rotate_fp16_input():
+    x = np.zeros((1, 128), dtype=np.uint16)
+    x[0, 5] = 0x4000  # fp16 2.0
+    suh = np.full((1, 128), 0x3800, dtype=np.uint16)  # 0.5
+    xr = tf.rotate_input(x, suh, "f16")[0, 0]
+    h = scipy.linalg.hadamard(128)
+    assert np.array_equal(xr, np.where(h[:, 5] > 0, 0x2C00, 0xAC00).astype(np.uint16))
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_output_one_hot_closed_form(out_dtype):
+    # z = e_j in one 128-column block: y = +-(1/8) * svh, exactly representable.
+    h = scipy.linalg.hadamard(128)
+    rng = np.random.default_rng(4)
+    svh = (np.where(rng.integers(0, 2, 256) == 1, -1.0, 1.0) * 2.0 ** rng.integers(-3, 3, 256))
+    svh_bits = svh.astype(np.float16).view(np.uint16)
+    z = np.zeros((1, 256), dtype=np.float32)
+    z[0, 128 + 9] = 1.0
+    y = tf.output_transform_f32(z, svh_bits, out_dtype)
+    want = np.zeros(256)
+    want[128:] = h[:, 9] * svh[128:] / 8
+    got = (tf.bf16_bits_to_f32(y) if out_dtype == "bf16" else tf.f16_from_bits(y)).astype(np.float64)
+    assert np.array_equal(got[0], want)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal(100000).astype(np.float32) * np.float32(1e3)
+    # explicit ties: low 16 bits exactly 0x8000, both parities of bit 16
+    # values in [1, 2) whose low 16 bits are exactly half a bf16 ulp
+    ties = ((rng.integers(0, 128, 256, dtype=np.uint32) << 16) | 0x3F808000).view(np.float32)
+    a = np.concatenate([a, ties, -ties, np.array([0.0, -0.0], np.float32)])
+    want = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(tf.f32_to_bf16_bits(a), want)
+
+
+def test_f16_rounding_matches_torch():
+    rng = np.random.default_rng(6)
+    a = rng.standard_normal(100000).astype(np.float32) * np.float32(30)
+    want = torch.from_numpy(a).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(tf.f32_to_f16_bits(a), want)
+
+
+def test_reduce_parts_is_left_to_right():
+    # ((1 + 2**-24) + 2**-24) = 1 in float32 (ties to even twice), while
+    # 1 + (2**-24 + 2**-24) = 1 + 2**-23: the order is observable.
+    parts = np.array([1.0, 2.0 ** -24, 2.0 ** -24], dtype=np.float32).reshape(3, 1, 1)
+    assert tf.reduce_parts_f32(parts)[0, 0] == np.float32(1.0)
+    # the first part is copied, not added to +0: -0.0 survives
+    neg = np.array([-0.0], dtype=np.float32).reshape(1, 1, 1)
+    assert np.signbit(tf.reduce_parts_f32(neg)[0, 0])
