@@ -1,0 +1,177 @@
+/*
+ * exl3.h -- C ABI of the MI355X (gfx950) EXL3 quantized linear.
+ *
+ *     y = had( W_q . had(x * suh) ) * svh
+ *
+ * W_q is decoded on the fly from 16x16 trellis tiles; it is never stored.
+ *
+ * Sources (the pages this library implements):
+ *   - cuda-exl3 README, "One op per layer": one call does a whole quantized
+ *     linear; all shards of a fused layer run in one GEMM, addressed by
+ *     absolute column; the output is in the caller's dtype (bf16 or fp16); the
+ *     activation transform is a separate kernel ("Two further departures").
+ *   - cuda-exl3 README, "Notes on the format": suh has one row per shard,
+ *     trellis and svh concatenate along the output dim.
+ *   - TensorFold PR "cuda: EXL3 projections behind qlinear", "What it adds":
+ *     trellis [K/16][N/16][16*bits] int16, widths 1..8, codebooks 3inst, mcg
+ *     and mul1; "Arithmetic": the rounding order (x*suh, fp32 Hadamard,
+ *     *2^-4, one rounding to fp16; fp16 products with fp32 sums; output
+ *     Hadamard, svh and 2^-3, one rounding); a shape-fixed number of K parts
+ *     summed in part order, so a row's bits do not depend on the batch.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked HOST.  The caller owns every
+ *     buffer and the stream; no call allocates, frees or synchronizes, so all
+ *     calls may be captured in a HIP graph.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it.
+ *   - Every argument is validated on the host before any HIP call.  On error
+ *     nothing is enqueued or written, the status is returned, and
+ *     exl3_last_error() names the failed check and the offending values.
+ *   - Device pointers must be 16-byte aligned.  Matrices are row-major and
+ *     dense (no strides).  fp16/bf16 data are passed as raw uint16 bits.
+ *   - Shapes: K and every shard width are multiples of 128 (the Hadamard
+ *     block); bits in 1..8; 1..EXL3_MAX_SHARDS shards; M >= 0 (M == 0 is a
+ *     no-op that returns EXL3_OK).
+ *   - Calls on distinct outputs and workspaces may run concurrently.
+ */
+#ifndef EXL3_H
+#define EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXL3_MAX_SHARDS 16
+#define EXL3_ABI_VERSION 1
+
+typedef enum {
+  EXL3_OK = 0,
+  EXL3_ERR_INVALID_ARG = 1, /* a shape, pointer, alignment or enum is wrong  */
+  EXL3_ERR_UNSUPPORTED = 2, /* valid EXL3, but outside this build's limits   */
+  EXL3_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  EXL3_ERR_LAUNCH = 4       /* the HIP runtime refused a launch              */
+} exl3_status;
+
+/* The three procedural codebooks (cuda-exl3 README, "What is supported"). */
+typedef enum { EXL3_CB_3INST = 0, EXL3_CB_MCG = 1, EXL3_CB_MUL1 = 2 } exl3_codebook;
+
+typedef enum { EXL3_F16 = 0, EXL3_BF16 = 1 } exl3_dtype;
+
+/* One EXL3 weight, possibly a fused multi-shard layer (qkv, gate_up).
+ * The weight view of the TensorFold PR ("What it adds") plus the shard map
+ * of the cuda-exl3 README ("One op per layer", "Notes on the format"). */
+typedef struct exl3_weight {
+  const uint16_t *trellis; /* [K/16][N/16][16*bits] trellis words           */
+  const uint16_t *suh;     /* fp16 bits [n_shards][K], one row per shard     */
+  const uint16_t *svh;     /* fp16 bits [N], absolute output column          */
+  int32_t K;               /* input features, multiple of 128                */
+  int32_t N;               /* output features = sum(shard_n)                 */
+  int32_t bits;            /* 1..8 bits per weight                           */
+  int32_t codebook;        /* exl3_codebook                                  */
+  int32_t n_shards;        /* 1..EXL3_MAX_SHARDS                             */
+  const int32_t *shard_n;  /* HOST [n_shards], each a multiple of 128        */
+} exl3_weight;
+
+/* Execution plan.  `parts` (P) and the K range of each part depend on
+ * (K, N, bits) only, never on M, so every row's result is bit-identical at
+ * every batch size.  `mode` and `bm` pick how the same arithmetic is
+ * scheduled and never change a bit of the output. */
+typedef enum {
+  EXL3_MODE_AUTO = -1,
+  EXL3_MODE_FUSED = 0, /* one workgroup per (M-tile, 128 columns) runs all
+                          parts in order and applies the output transform   */
+  EXL3_MODE_SLABS = 1  /* one workgroup per (M-tile, 128 columns, part)
+                          writes an fp32 partial; a second kernel sums the
+                          parts in order and applies the output transform   */
+} exl3_mode;
+
+typedef struct exl3_plan {
+  int32_t parts;       /* P >= 1 K parts                                     */
+  int32_t mode;        /* exl3_mode                                          */
+  int32_t bm;          /* rows per M-tile: 16, 32, 64 or 128                 */
+  int32_t reserved;
+  size_t workspace;    /* bytes of workspace this plan needs                 */
+} exl3_plan;
+
+/* ---------------------------------------------------------------- calls */
+
+/* Input rotation (TensorFold PR, "Arithmetic" step 1; cuda-exl3 README,
+ * "One op per layer", first bullet):
+ *   x_rot[s][m][k] = fp16_rne( 2^-4 * H128( x[m][:] * suh[s][:] )[k] )
+ * per 128-element block, for every shard s, computed in fp32 with the
+ * butterfly strides 1, 2, ..., 64 in ascending order; x*suh is exact.
+ *   x      [M][K] bf16 or fp16 bits (x_dtype)
+ *   suh    [n_shards][K] fp16 bits
+ *   x_rot  [n_shards][M][K] fp16 bits (output, written completely)
+ * Errors: EXL3_ERR_INVALID_ARG for K % 128 != 0, M < 0, n_shards out of
+ * range, a null or misaligned pointer, or an unknown dtype. */
+exl3_status exl3_input_transform(const void *x, int32_t x_dtype, int32_t M, int32_t K,
+                                 const uint16_t *suh, int32_t n_shards, uint16_t *x_rot,
+                                 void *stream);
+
+/* Bytes of workspace exl3_linear needs for `M` rows of weight `w` (0 when
+ * the plan needs none).  Returns 0 and sets exl3_last_error() if `w` is
+ * invalid. */
+size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M);
+
+/* The quantized linear on rotated activations (cuda-exl3 README, "One op per
+ * layer"; TensorFold PR, "Arithmetic" steps 2 and 3):
+ *   z[m][n] = sum_k x_rot[s(n)][m][k] * W_q[k][n]   (fp16 products, fp32 sums
+ *             in P shape-fixed K parts, summed in part order)
+ *   y[m][n] = rne_out( svh[n] * 2^-3 * H128(z[m][:])[n] )  per 128-col block
+ * where s(n) is the shard holding absolute column n.
+ *   x_rot     [n_shards][M][K] fp16 bits, as written by exl3_input_transform
+ *   y         [M][N] in y_dtype (output, written completely)
+ *   workspace at least exl3_workspace_bytes(w, M) bytes (may be NULL if 0);
+ *             its contents on entry do not matter.
+ * Errors: EXL3_ERR_INVALID_ARG for a bad weight view (see exl3_weight),
+ * pointer or dtype; EXL3_ERR_WORKSPACE if the workspace is too small;
+ * EXL3_ERR_LAUNCH if HIP refuses a launch. */
+exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y,
+                        int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The plan exl3_linear would use for M rows (HOST output). */
+exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan);
+
+/* exl3_linear with parts of the plan forced (HOST `force`; a field < 0, or
+ * EXL3_MODE_AUTO, keeps the automatic choice).  Forcing `mode` or `bm` never
+ * changes the output bits; forcing `parts` changes the K summation structure
+ * and therefore the bits (for tests and measurement). */
+exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y,
+                           int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream,
+                           const exl3_plan *force);
+
+/* Workspace bytes for exl3_linear_ex with the same `force`. */
+size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan *force);
+
+/* Human-readable status name, and the thread's last error message. */
+const char *exl3_status_str(exl3_status s);
+const char *exl3_last_error(void);
+int32_t exl3_abi_version(void);
+
+/* ------------------------------------------- test and measurement hooks */
+
+/* Every state of one codebook through the device decoder:
+ * out[s] = fp16 bits of codebook(s), s = 0..65535 (cuda-exl3 README, "What
+ * is supported"; TensorFold PR, "Tests (GB10)" first bullet). */
+exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream);
+
+/* The whole W_q [K][N] (fp16 bits) decoded by the GEMM's own staging and
+ * unpacking path (TensorFold PR, "Tests (GB10)" second bullet). */
+exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream);
+
+/* The output stage alone: y = rne_out(svh * 2^-3 * H128(z)) with
+ * z = ((z_parts[0] + z_parts[1]) + ...) in fp32, z_parts [n_parts][M][N]
+ * fp32 (TensorFold PR, "Arithmetic" step 3 and the ordered part sum). */
+exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t M,
+                                const exl3_weight *w, void *y, int32_t y_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXL3_H */

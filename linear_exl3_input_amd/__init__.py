@@ -1,0 +1,276 @@
+"""MI355X (gfx950) EXL3 quantized linear:  y = had(W_q . had(x*suh)) * svh.
+
+A thin ctypes binding over the C ABI in ``include/exl3.h`` (``libexl3.so``,
+built in-tree by ``linear_exl3_input_amd.build``).  Every step of the op runs
+in the library's HIP kernels; this module only checks tensor metadata,
+passes device pointers and the current HIP stream, and allocates outputs and
+workspace with torch.  There is no CPU or PyTorch fallback: if the library is
+missing, every call raises.
+
+Functional form, as on the cuda-exl3 page ("One op per layer"):
+
+    w = Exl3Weight(trellis, suh, svh, bits, codebook, shard_n)
+    y = forward(w, x)                      # x bf16/fp16 [M, K] -> y [M, N]
+
+or in two calls, ``input_transform`` then ``linear``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
+    "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libexl3.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "exl3.h")
+
+CODEBOOKS = {"3inst": 0, "mcg": 1, "mul1": 2}
+_F16, _BF16 = 0, 1
+MAX_SHARDS = 16
+
+EXL3_MODE_AUTO, EXL3_MODE_FUSED, EXL3_MODE_SLABS = -1, 0, 1
+
+
+class Exl3Error(RuntimeError):
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("trellis", ctypes.c_void_p), ("suh", ctypes.c_void_p), ("svh", ctypes.c_void_p),
+                ("K", ctypes.c_int32), ("N", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("codebook", ctypes.c_int32), ("n_shards", ctypes.c_int32),
+                ("shard_n", ctypes.POINTER(ctypes.c_int32))]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("parts", ctypes.c_int32), ("mode", ctypes.c_int32), ("bm", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libexl3.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"EXL3 HIP library not built: {_LIB_PATH} is missing "
+                               "(run python -m linear_exl3_input_amd.build)")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        W = ctypes.POINTER(_Weight)
+        P = ctypes.POINTER(_Plan)
+        sig = {
+            "exl3_input_transform": (i32, [vp, i32, i32, i32, vp, i32, vp, vp]),
+            "exl3_workspace_bytes": (sz, [W, i32]),
+            "exl3_workspace_bytes_ex": (sz, [W, i32, P]),
+            "exl3_linear": (i32, [W, vp, i32, vp, i32, vp, sz, vp]),
+            "exl3_linear_ex": (i32, [W, vp, i32, vp, i32, vp, sz, vp, P]),
+            "exl3_plan_query": (i32, [W, i32, P]),
+            "exl3_status_str": (ctypes.c_char_p, [i32]),
+            "exl3_last_error": (ctypes.c_char_p, []),
+            "exl3_abi_version": (i32, []),
+            "exl3_debug_codebook": (i32, [i32, vp, vp]),
+            "exl3_debug_decode": (i32, [W, vp, vp]),
+            "exl3_debug_epilogue": (i32, [vp, i32, i32, W, vp, i32, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        if L.exl3_abi_version() != 1:
+            raise RuntimeError("libexl3.so ABI version mismatch")
+        _lib = L
+        return L
+
+
+def header_symbols() -> Tuple[str, ...]:
+    """Every function the public header declares."""
+    text = open(HEADER).read()
+    return tuple(sorted(set(re.findall(r"\b(exl3_[a-z_]+)\s*\(", text))))
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = load()
+        raise Exl3Error(status, L.exl3_status_str(status).decode(), L.exl3_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev_ptr(t: torch.Tensor, name: str, dtypes) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_U16 = (torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16,)
+_H16 = (torch.float16,) + _U16
+
+
+@dataclass
+class Exl3Weight:
+    """An EXL3 weight on the GPU (trellis words, suh rows, svh, shard map)."""
+
+    trellis: torch.Tensor          # int16 [K/16, N/16, 16*bits]
+    suh: torch.Tensor              # fp16 [n_shards, K] (or [K] for one shard)
+    svh: torch.Tensor              # fp16 [N]
+    bits: int
+    codebook: int | str
+    shard_n: Optional[Sequence[int]] = None
+
+    def __post_init__(self):
+        if isinstance(self.codebook, str):
+            self.codebook = CODEBOOKS[self.codebook]
+        if self.suh.dim() == 1:
+            self.suh = self.suh.unsqueeze(0)
+        kt, nt, words = self.trellis.shape
+        self.K, self.N = kt * 16, nt * 16
+        if words != 16 * self.bits:
+            raise ValueError(f"trellis last dim {words} != 16*bits = {16 * self.bits}")
+        if self.shard_n is None:
+            self.shard_n = (self.N,)
+        self.shard_n = tuple(int(n) for n in self.shard_n)
+        self._shards = (ctypes.c_int32 * len(self.shard_n))(*self.shard_n)
+        self._view = _Weight(_dev_ptr(self.trellis, "trellis", _U16), _dev_ptr(self.suh, "suh", _H16),
+                             _dev_ptr(self.svh, "svh", _H16), self.K, self.N, self.bits, int(self.codebook),
+                             len(self.shard_n), self._shards)
+
+    @property
+    def n_shards(self) -> int:
+        return len(self.shard_n)
+
+    def view(self) -> _Weight:
+        return self._view
+
+
+# Process-wide workspace per device (the cuda-exl3 page, "VRAM": the
+# activation and split-k workspaces are process-wide, not per layer).
+_workspaces: Dict[int, torch.Tensor] = {}
+
+
+def _workspace(nbytes: int, device: torch.device) -> Tuple[int, int]:
+    if nbytes == 0:
+        return 0, 0
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[idx] = ws
+    return ws.data_ptr(), ws.numel()
+
+
+def _force(parts=None, mode=None, bm=None) -> Optional[_Plan]:
+    if parts is None and mode is None and bm is None:
+        return None
+    return _Plan(parts if parts else -1, EXL3_MODE_AUTO if mode is None else mode, bm if bm else -1, 0, 0)
+
+
+def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None) -> int:
+    f = _force(parts, mode, bm)
+    L = load()
+    n = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
+    err = L.exl3_last_error().decode()
+    if n == 0 and err:
+        raise Exl3Error(1, "EXL3_ERR_INVALID_ARG", err)
+    return n
+
+
+def plan(w: Exl3Weight, M: int) -> dict:
+    p = _Plan()
+    _check(load().exl3_plan_query(ctypes.byref(w.view()), M, ctypes.byref(p)))
+    return {"parts": p.parts, "mode": p.mode, "bm": p.bm, "workspace": p.workspace}
+
+
+def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """had(x*suh) for every shard: x [M, K] bf16/fp16 -> x_rot [S, M, K] fp16."""
+    if suh.dim() == 1:
+        suh = suh.unsqueeze(0)
+    M, K = x.shape
+    S = suh.shape[0]
+    if suh.shape[1] != K:
+        raise ValueError(f"suh has K={suh.shape[1]}, x has K={K}")
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"x dtype {x.dtype} is not bf16/fp16")
+    if out is None:
+        out = torch.empty((S, M, K), dtype=torch.float16, device=x.device)
+    L = load()
+    _check(L.exl3_input_transform(_dev_ptr(x, "x", (torch.bfloat16, torch.float16)),
+                                  _BF16 if x.dtype == torch.bfloat16 else _F16, M, K,
+                                  _dev_ptr(suh, "suh", _H16), S, _dev_ptr(out, "x_rot", _H16), _stream()))
+    return out
+
+
+def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+           out: Optional[torch.Tensor] = None, parts=None, mode=None, bm=None) -> torch.Tensor:
+    """z = x_rot . W_q per shard, then the output transform: -> y [M, N]."""
+    S, M, K = x_rot.shape
+    if S != w.n_shards or K != w.K:
+        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} does not match the weight ({w.n_shards}, M, {w.K})")
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=out_dtype, device=x_rot.device)
+    f = _force(parts, mode, bm)
+    L = load()
+    need = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
+    ws, wsn = _workspace(need, x_rot.device)
+    _check(L.exl3_linear_ex(ctypes.byref(w.view()), _dev_ptr(x_rot, "x_rot", _H16), M,
+                            _dev_ptr(out, "y", (out_dtype,)), _BF16 if out_dtype == torch.bfloat16 else _F16,
+                            ws, wsn, _stream(), ctypes.byref(f) if f else None))
+    return out
+
+
+def forward(w: Exl3Weight, x: torch.Tensor, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """The whole layer in the caller's dtype: y = had(W_q . had(x*suh)) * svh."""
+    return linear(w, input_transform(x, w.suh), out_dtype or x.dtype)
+
+
+def debug_codebook(codebook: int | str, device="cuda") -> torch.Tensor:
+    cb = CODEBOOKS[codebook] if isinstance(codebook, str) else codebook
+    out = torch.empty(65536, dtype=torch.int16, device=device)
+    _check(load().exl3_debug_codebook(cb, out.data_ptr(), _stream()))
+    return out
+
+
+def debug_decode(w: Exl3Weight) -> torch.Tensor:
+    out = torch.empty((w.K, w.N), dtype=torch.int16, device=w.trellis.device)
+    _check(load().exl3_debug_decode(ctypes.byref(w.view()), out.data_ptr(), _stream()))
+    return out
+
+
+def debug_epilogue(w: Exl3Weight, z_parts: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
+    if z_parts.dim() == 2:
+        z_parts = z_parts.unsqueeze(0)
+    P, M, N = z_parts.shape
+    out = torch.empty((M, N), dtype=out_dtype, device=z_parts.device)
+    _check(load().exl3_debug_epilogue(_dev_ptr(z_parts, "z_parts", (torch.float32,)), P, M, ctypes.byref(w.view()),
+                                      out.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _F16, _stream()))
+    return out

@@ -1,0 +1,142 @@
+// Device-side building blocks of the EXL3 linear for gfx950 (CDNA4).
+//
+// Everything here runs on a 64-wide wavefront.  The arithmetic follows the
+// TensorFold PR "cuda: EXL3 projections behind qlinear", section
+// "Arithmetic": fp32 Hadamard butterflies with a fixed add order, one fp16
+// rounding of the rotated activations, fp16 products with fp32 sums, and one
+// rounding of the output.  The codebooks follow the cuda-exl3 README, "What
+// is supported" (3inst, mcg, mul1; mcg multiplier 0xCBAC1FED from its
+// "GLM-5.3-Flash" section); the pages print no other constants, so 3inst and
+// mul1 use the constants below, and both rotations use butterfly strides
+// 1, 2, ..., 64 in ascending order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr int HBLOCK = 128;  // Hadamard block
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+// Round to nearest even (the default rounding mode of v_cvt_f16_f32).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __hip_bfloat16 h = __float2bfloat16(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// ------------------------------------------------------------- codebooks
+//
+// A state is the low 16 bits of a 32-bit register (higher bits are ignored).
+// mcg:   u = s * 0xCBAC1FED (mod 2^32), then the pair sum P(u)
+// 3inst: u = s * 0x2C9277B5 + 0x3C6EF372, then P(u)
+// P(u):  u' = (u & 0x8FFF8FFF) | 0x30003000 -> two fp16 halves in
+//        +-[0.125, 2); value = lo + hi, one fp16 rounding
+// mul1:  u = s * 0x9E3779B1, t = sum of u's bytes, value = t*alpha + beta in
+//        one fp16 fused multiply-add (alpha = 0x1EEE, beta = 0xC2E8).  It is
+//        evaluated as (1024 + t) * alpha + (beta - 1024 * alpha): the fp16
+//        0x6400 | t is exactly 1024 + t, and beta - 1024 * alpha = -10.3828125
+//        (0xC931) is an fp16, so the fused sum and its one rounding are the
+//        same.
+
+constexpr uint32_t CB_3INST = 0, CB_MCG = 1, CB_MUL1 = 2;
+
+template <uint32_t C>
+__device__ __forceinline__ uint32_t mul16_const(uint32_t s) {
+  // (s mod 2^16) * C mod 2^32 from two 16x16-bit products.
+  const uint32_t s16 = s & 0xFFFFu;
+  return s16 * (C & 0xFFFFu) + ((s16 * (C >> 16)) << 16);
+}
+
+template <uint32_t CB>
+__device__ __forceinline__ uint32_t cb_hash(uint32_t s) {
+  if constexpr (CB == CB_3INST) return mul16_const<0x2C9277B5u>(s) + 0x3C6EF372u;
+  else if constexpr (CB == CB_MCG) return mul16_const<0xCBAC1FEDu>(s);
+  else return mul16_const<0x9E3779B1u>(s);
+}
+
+__device__ __forceinline__ _Float16 pair_sum_f16(uint32_t u) {
+  const uint32_t m = (u & 0x8FFF8FFFu) | 0x30003000u;
+  const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu));
+  const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
+  return lo + hi;
+}
+
+// Two states -> two fp16 values packed in one register (s0 low, s1 high).
+template <uint32_t CB>
+__device__ __forceinline__ uint32_t decode_pair(uint32_t s0, uint32_t s1) {
+  if constexpr (CB == CB_MUL1) {
+    const uint32_t d0 = __builtin_amdgcn_udot4(cb_hash<CB>(s0), 0x01010101u, 0x6400u, false);
+    const uint32_t d1 = __builtin_amdgcn_udot4(cb_hash<CB>(s1), 0x01010101u, 0x6400u, false);
+    const half2_t h = __builtin_bit_cast(half2_t, d0 | (d1 << 16));
+    const half2_t alpha = {__builtin_bit_cast(_Float16, (uint16_t)0x1EEE),
+                           __builtin_bit_cast(_Float16, (uint16_t)0x1EEE)};
+    const half2_t c = {__builtin_bit_cast(_Float16, (uint16_t)0xC931),
+                       __builtin_bit_cast(_Float16, (uint16_t)0xC931)};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h, alpha, c));
+  } else {
+    const half2_t v = {pair_sum_f16(cb_hash<CB>(s0)), pair_sum_f16(cb_hash<CB>(s1))};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// ------------------------------------------------ wavefront Hadamard (fp32)
+//
+// Lane l holds elements 2l and 2l+1 of one 128-element block.  Stage s pairs
+// elements e and e + 2^s (e with bit s clear) into (a + b, a - b); stage 0 is
+// inside the lane, stage s >= 1 pairs lane l with lane l ^ 2^(s-1).
+__device__ __forceinline__ void hadamard128_wave(float &x0, float &x1, int lane) {
+  float a = x0 + x1;
+  float b = x0 - x1;
+#pragma unroll
+  for (int s = 1; s < 7; ++s) {
+    const int mask = 1 << (s - 1);
+    const float pa = __shfl_xor(a, mask, WAVE);
+    const float pb = __shfl_xor(b, mask, WAVE);
+    if (lane & mask) {
+      a = pa - a;
+      b = pb - b;
+    } else {
+      a = a + pa;
+      b = b + pb;
+    }
+  }
+  x0 = a;
+  x1 = b;
+}
+
+// Output stage for one 128-column block of one row, on one wave:
+// y = rne_out(svh * 2^-3 * H128(z)); lane l owns columns n0 + 2l, n0 + 2l + 1.
+template <bool OUT_BF16>
+__device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *__restrict__ svh,
+                                           uint16_t *__restrict__ yrow, int n0, int lane) {
+  hadamard128_wave(z0, z1, lane);
+  const uint32_t sv = *(const uint32_t *)(svh + n0 + 2 * lane);
+  const float y0 = (z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu);
+  const float y1 = (z1 * 0.125f) * f16_bits_to_f32(sv >> 16);
+  uint32_t packed;
+  if constexpr (OUT_BF16) packed = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+  else packed = f32_to_f16_bits(y0) | (f32_to_f16_bits(y1) << 16);
+  *(uint32_t *)(yrow + n0 + 2 * lane) = packed;
+}
+
+}  // namespace exl3

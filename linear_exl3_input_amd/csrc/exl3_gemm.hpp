@@ -1,0 +1,426 @@
+// Trellis-decode + MFMA GEMM of the EXL3 linear for gfx950.
+//
+// One workgroup (4 waves) owns a BM-row x 128-column output tile (one
+// Hadamard block of columns, so the output transform can be applied in the
+// same kernel) and a range of K.  The trellis slice it needs is streamed from
+// HBM once per M-tile (cuda-exl3 README, "Why custom kernels": a block owns
+// BM rows x BN columns and reads its trellis slice once), 128 k at a time,
+// through a two-stage LDS pipeline.  Each wave decodes the tiles of its two
+// 16-column strips straight into the B operand of v_mfma_f32_16x16x32_f16;
+// every trellis value is decoded exactly once per M-tile (cuda-exl3 README,
+// "What profiling found": decoding each tile once was the small-batch win).
+//
+// Value placement.  A 16x16 tile lists its 256 values in the order of the B
+// fragments of two m16n8k16 products (TensorFold PR "cuda: EXL3 projections
+// behind qlinear", "Arithmetic" step 2): value v = 8t + 4h + i sits at row
+// k = 2(t%4) + (i&1) + 8(i>>1), column n = t/4 + 8h.  One MFMA B operand is
+// 32 k x 16 columns.  Lane (j = lane%16, g = lane/16) of MFMA "half" h takes
+// column c = (j&7) + 8h of n-tile 2*wave + (j>>3) in k-tile g>>1, and the
+// two runs of four consecutive states v0..v0+3 and v0+8..v0+11 with
+// v0 = 32(j&7) + 4h + 16(g&1).  Those are rows 4(g&1) + {0,1,2,3,8,9,10,11}
+// of the tile, so the lane's 8 k slots are that ascending list.  The A operand
+// (rotated activations) is read at the same 8 k for row j; any k order works
+// as long as A and B agree (the FP8 DenseMlp page makes the same point).
+//
+// Bit stream.  Tile words are MSB-first; value v's 16-bit state starts at
+// bit v*bits and wraps around the tile (a run of eight 6-bit values spans a
+// 58-bit window, cuda-exl3 README, "Where the time goes").  While staging,
+// each 32-bit word is rotated by 16 so LDS holds the stream MSB-first per
+// dword, and every tile is stored with 4 pad dwords on each side (copies of
+// its last and first 4 dwords) so no lane's window wraps inside LDS.
+//
+// Summation structure (fixed by (K, N, bits), never by M): K is cut into P
+// parts of whole 128-k blocks; each part is one MFMA chain in ascending k
+// from zero; parts are added in part order, the first part copied, not added
+// to zero (TensorFold PR, "Arithmetic": a number of parts fixed by the shape,
+// added in part order).  In slab mode each workgroup runs one part and writes
+// an fp32 partial; otherwise one workgroup runs all parts and keeps the
+// running sum in registers.  Both give the same bits for every row.
+#pragma once
+
+#include "exl3_device.hpp"
+#include "exl3_launch.hpp"
+
+namespace exl3 {
+
+constexpr int STAGE_KT = 8;      // k-tiles per pipeline stage (128 k)
+constexpr int WG_NT = 8;         // n-tiles per workgroup (128 columns)
+constexpr int WG_THREADS = 256;  // 4 waves
+constexpr int A_ROW_DW = 68;     // staged x~ row: 128 fp16 (64 dwords) + 4 pad
+constexpr int Z_ROW = 132;       // epilogue z row: 128 fp32 + 4 pad
+
+template <int BITS>
+struct Geom {
+  static constexpr int TILE_DW = 8 * BITS;         // dwords per 16x16 tile
+  static constexpr int STRIDE = TILE_DW + 8;       // LDS dwords per tile (4 + tile + 4)
+  static constexpr int TILE_CHUNKS = 2 * BITS;     // 16-byte chunks per tile
+  static constexpr int ROW_CHUNKS = WG_NT * TILE_CHUNKS;
+  static constexpr int STAGE_CHUNKS = STAGE_KT * ROW_CHUNKS;
+  static constexpr int T_ITERS = (STAGE_CHUNKS + WG_THREADS - 1) / WG_THREADS;
+  static constexpr int STAGE_T_DW = STAGE_KT * WG_NT * STRIDE;
+  // dwords a lane needs: 16 + 11*bits stream bits after a start offset in [1, 32]
+  static constexpr int NY = (11 * BITS + 16 + 31) / 32;
+  static constexpr int NX = NY + 1;
+};
+
+// ---------------------------------------------------------------- staging
+
+template <int BITS>
+__device__ __forceinline__ void load_trellis_stage(u32x4_t (&treg)[Geom<BITS>::T_ITERS],
+                                                   const uint16_t *__restrict__ tr, int kb, int nb,
+                                                   int NT, int tid) {
+  using G = Geom<BITS>;
+#pragma unroll
+  for (int it = 0; it < G::T_ITERS; ++it) {
+    const int c = tid + WG_THREADS * it;
+    if (G::STAGE_CHUNKS % WG_THREADS == 0 || c < G::STAGE_CHUNKS) {
+      const int r = c / G::ROW_CHUNKS;
+      const int q = c - r * G::ROW_CHUNKS;
+      const uint16_t *src = tr + ((int64_t)(STAGE_KT * kb + r) * NT + WG_NT * nb) * (16 * BITS) + q * 8;
+      treg[it] = __builtin_nontemporal_load((const u32x4_t *)src);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t rot16(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 16); }
+
+template <int BITS>
+__device__ __forceinline__ void store_trellis_stage(const u32x4_t (&treg)[Geom<BITS>::T_ITERS],
+                                                    uint32_t *__restrict__ tb, int tid) {
+  using G = Geom<BITS>;
+#pragma unroll
+  for (int it = 0; it < G::T_ITERS; ++it) {
+    const int c = tid + WG_THREADS * it;
+    if (G::STAGE_CHUNKS % WG_THREADS == 0 || c < G::STAGE_CHUNKS) {
+      const int r = c / G::ROW_CHUNKS;
+      const int q = c - r * G::ROW_CHUNKS;
+      const int t = q / G::TILE_CHUNKS;
+      const int u = q - t * G::TILE_CHUNKS;
+      u32x4_t v = treg[it];
+      v.x = rot16(v.x);
+      v.y = rot16(v.y);
+      v.z = rot16(v.z);
+      v.w = rot16(v.w);
+      uint32_t *dst = tb + (r * WG_NT + t) * G::STRIDE;
+      *(u32x4_t *)(dst + 4 + 4 * u) = v;
+      if (u == 0) *(u32x4_t *)(dst + 4 + G::TILE_DW) = v;
+      if (u == G::TILE_CHUNKS - 1) *(u32x4_t *)(dst) = v;
+    }
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void load_a_stage(u32x4_t (&areg)[MT], const uint16_t *__restrict__ xs,
+                                             int kb, int m0, int M, int K, int tid) {
+#pragma unroll
+  for (int it = 0; it < MT; ++it) {
+    const int c = tid + WG_THREADS * it;
+    const int row = c >> 4;
+    const int q = c & 15;
+    const int m = m0 + row;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (m < M) v = *(const u32x4_t *)(xs + (int64_t)m * K + kb * 128 + q * 8);
+    areg[it] = v;
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void store_a_stage(const u32x4_t (&areg)[MT], uint32_t *__restrict__ ab, int tid) {
+#pragma unroll
+  for (int it = 0; it < MT; ++it) {
+    const int c = tid + WG_THREADS * it;
+    *(u32x4_t *)(ab + (c >> 4) * A_ROW_DW + (c & 15) * 4) = areg[it];
+  }
+}
+
+// ----------------------------------------------------------------- decode
+
+template <int D, int NY>
+__device__ __forceinline__ uint32_t window16(const uint32_t (&Y)[NY]) {
+  constexpr int a = D / 32;
+  constexpr int s = D % 32;
+  if constexpr (s <= 16) return Y[a] >> (16 - s);
+  else return __builtin_amdgcn_alignbit(Y[a], Y[a + 1], 48 - s);
+}
+
+// Decode the lane's 8 values of one MFMA B operand from a staged tile.
+// `tp` points at the tile's LDS slot; `xoff` is 4 + the first dword the lane
+// needs and `sh` = 32 - (its bit offset in that dword, in 1..32).
+template <int BITS, uint32_t CB>
+__device__ __forceinline__ half8_t decode_frag(const uint32_t *__restrict__ tp, int xoff, int sh) {
+  using G = Geom<BITS>;
+  uint32_t X[G::NX];
+#pragma unroll
+  for (int i = 0; i < G::NX; ++i) X[i] = tp[xoff + i];
+  uint32_t Y[G::NY];
+#pragma unroll
+  for (int i = 0; i < G::NY; ++i) Y[i] = __builtin_amdgcn_alignbit(X[i], X[i + 1], sh);
+  const uint32_t s0 = window16<0, G::NY>(Y);
+  const uint32_t s1 = window16<BITS, G::NY>(Y);
+  const uint32_t s2 = window16<8 * BITS, G::NY>(Y);
+  const uint32_t s3 = window16<9 * BITS, G::NY>(Y);
+  const uint32_t s4 = window16<2 * BITS, G::NY>(Y);
+  const uint32_t s5 = window16<3 * BITS, G::NY>(Y);
+  const uint32_t s6 = window16<10 * BITS, G::NY>(Y);
+  const uint32_t s7 = window16<11 * BITS, G::NY>(Y);
+  const u32x4_t r = {decode_pair<CB>(s0, s1), decode_pair<CB>(s2, s3), decode_pair<CB>(s4, s5),
+                     decode_pair<CB>(s6, s7)};
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// Per-lane constants of decode_frag for column half h.
+template <int BITS>
+__device__ __forceinline__ void lane_window(int j, int g, int h, int &xoff, int &sh) {
+  const int v0 = 32 * (j & 7) + 4 * h + 16 * (g & 1);
+  const int o = v0 * BITS;
+  const int d0 = (o + 31) / 32 - 1;  // so that o - 32*d0 is in 1..32
+  xoff = 4 + d0;
+  sh = 32 - (o - 32 * d0);
+}
+
+// Column (within the workgroup's 128) of the lane's B column / C column.
+__device__ __forceinline__ int lane_col(int wave, int j, int h) {
+  return 16 * (2 * wave + (j >> 3)) + (j & 7) + 8 * h;
+}
+
+// ------------------------------------------------------------------- GEMM
+
+template <int BITS, uint32_t CB, int MT, bool MULTI>
+__global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
+  using G = Geom<BITS>;
+  constexpr int BM = 16 * MT;
+  constexpr int STAGE_A_DW = BM * A_ROW_DW;
+  constexpr int STAGE_DW = G::STAGE_T_DW + STAGE_A_DW;
+  constexpr int Z_DW = BM * Z_ROW;
+  constexpr int LDS_DW = (2 * STAGE_DW > Z_DW) ? 2 * STAGE_DW : Z_DW;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nb = blockIdx.x;
+  const int m0 = blockIdx.z * BM;
+  const int M = p.M, K = p.K, N = p.N;
+  const int NT = N >> 4;
+  const int KB = K >> 7;
+
+  int p_begin = 0, p_end = p.parts;
+  if (p.slab_mode) {
+    p_begin = blockIdx.y;
+    p_end = p_begin + 1;
+  }
+  const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
+  const int kb_end = (int)((int64_t)p_end * KB / p.parts);
+
+  int shard = 0;
+  while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
+  const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
+
+  int xoff0, sh0, xoff1, sh1;
+  lane_window<BITS>(j, g, 0, xoff0, sh0);
+  lane_window<BITS>(j, g, 1, xoff1, sh1);
+  const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
+
+  u32x4_t treg[G::T_ITERS];
+  u32x4_t areg[MT];
+
+  float4_t acc[MT][2];
+  float4_t tot[MULTI ? MT : 1][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  int part = p_begin;
+  int part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+
+  load_trellis_stage<BITS>(treg, p.trellis, kb_begin, nb, NT, tid);
+  load_a_stage<MT>(areg, xs, kb_begin, m0, M, K, tid);
+  store_trellis_stage<BITS>(treg, lds, tid);
+  store_a_stage<MT>(areg, lds + G::STAGE_T_DW, tid);
+  if (kb_begin + 1 < kb_end) {
+    load_trellis_stage<BITS>(treg, p.trellis, kb_begin + 1, nb, NT, tid);
+    load_a_stage<MT>(areg, xs, kb_begin + 1, m0, M, K, tid);
+  }
+
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const int buf = (kb - kb_begin) & 1;
+    __syncthreads();
+    if (kb + 1 < kb_end) {
+      uint32_t *nxt = lds + (buf ^ 1) * STAGE_DW;
+      store_trellis_stage<BITS>(treg, nxt, tid);
+      store_a_stage<MT>(areg, nxt + G::STAGE_T_DW, tid);
+      if (kb + 2 < kb_end) {
+        load_trellis_stage<BITS>(treg, p.trellis, kb + 2, nb, NT, tid);
+        load_a_stage<MT>(areg, xs, kb + 2, m0, M, K, tid);
+      }
+    }
+    const uint32_t *tb = lds + buf * STAGE_DW;
+    const uint32_t *ab = tb + G::STAGE_T_DW;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      half8_t a[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t *ap = ab + (mt * 16 + j) * A_ROW_DW + 16 * ks + 8 * (g >> 1) + 2 * (g & 1);
+        const u32x2_t lo = *(const u32x2_t *)ap;
+        const u32x2_t hi = *(const u32x2_t *)(ap + 4);
+        const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
+        a[mt] = __builtin_bit_cast(half8_t, v);
+      }
+      const uint32_t *tp = tb + (tile_lane + 2 * WG_NT * ks) * G::STRIDE;
+      const half8_t b0 = decode_frag<BITS, CB>(tp, xoff0, sh0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b0, acc[mt][0], 0, 0, 0);
+      const half8_t b1 = decode_frag<BITS, CB>(tp, xoff1, sh1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b1, acc[mt][1], 0, 0, 0);
+    }
+    if constexpr (MULTI) {
+      if (kb + 1 == part_end_kb) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (part == p_begin) tot[mt][h] = acc[mt][h];
+            else tot[mt][h] = tot[mt][h] + acc[mt][h];
+            acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        ++part;
+        part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+      }
+    }
+  }
+
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[mt][h] = tot[mt][h];
+  }
+
+  if (p.slab_mode) {
+    float *__restrict__ sl = p.slabs + (int64_t)p_begin * M * N;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = nb * 128 + lane_col(wave, j, h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + mt * 16 + 4 * g + i;
+          if (row < M) sl[(int64_t)row * N + col] = acc[mt][h][i];
+        }
+      }
+    return;
+  }
+
+  __syncthreads();  // every wave is done with the stage buffers
+  float *z = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = lane_col(wave, j, h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[(mt * 16 + 4 * g + i) * Z_ROW + col] = acc[mt][h][i];
+    }
+  __syncthreads();
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+  for (int r = wave; r < BM; r += 4) {
+    const int row = m0 + r;
+    if (row >= M) break;
+    const float z0 = z[r * Z_ROW + 2 * lane];
+    const float z1 = z[r * Z_ROW + 2 * lane + 1];
+    if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+    else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+  }
+}
+
+// Decode-only kernel for tests: the same staging and decode_frag as the GEMM,
+// storing each lane's 8 values at their (k, n) instead of multiplying.
+template <int BITS, uint32_t CB>
+__global__ __launch_bounds__(WG_THREADS) void debug_decode_kernel(const DecodeParams p) {
+  using G = Geom<BITS>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[G::STAGE_T_DW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int nb = blockIdx.x, kb = blockIdx.y;
+  u32x4_t treg[G::T_ITERS];
+  load_trellis_stage<BITS>(treg, p.trellis, kb, nb, p.N >> 4, tid);
+  store_trellis_stage<BITS>(treg, lds, tid);
+  __syncthreads();
+  const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t *tp = lds + (tile_lane + 2 * WG_NT * ks) * G::STRIDE;
+    for (int h = 0; h < 2; ++h) {
+      int xoff, sh;
+      lane_window<BITS>(j, g, h, xoff, sh);
+      const half8_t b = decode_frag<BITS, CB>(tp, xoff, sh);
+      const int n = nb * 128 + lane_col(wave, j, h);
+      const int k0 = kb * 128 + 32 * ks + 16 * (g >> 1) + 4 * (g & 1);
+      const int koff[8] = {0, 1, 2, 3, 8, 9, 10, 11};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p.wq[(int64_t)(k0 + koff[e]) * p.N + n] = __builtin_bit_cast(uint16_t, b[e]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int BITS, uint32_t CB, int MT>
+hipError_t launch_gemm_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (multi) hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, true>), grid, dim3(WG_THREADS), 0, s, p);
+  else hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false>), grid, dim3(WG_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BITS, uint32_t CB>
+hipError_t launch_gemm_cb(int mt, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_gemm_t<BITS, CB, 1>(multi, p, grid, s);
+    case 2: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
+    case 4: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS>
+hipError_t launch_gemm_bits(int cb, int mt, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  switch (cb) {
+    case 0: return launch_gemm_cb<BITS, CB_3INST>(mt, multi, p, grid, s);
+    case 1: return launch_gemm_cb<BITS, CB_MCG>(mt, multi, p, grid, s);
+    case 2: return launch_gemm_cb<BITS, CB_MUL1>(mt, multi, p, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS>
+hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
+  const dim3 grid(p.N / 128, p.K / 128);
+  switch (cb) {
+    case 0: hipLaunchKernelGGL((debug_decode_kernel<BITS, CB_3INST>), grid, dim3(WG_THREADS), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((debug_decode_kernel<BITS, CB_MCG>), grid, dim3(WG_THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((debug_decode_kernel<BITS, CB_MUL1>), grid, dim3(WG_THREADS), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace exl3
+
+#define EXL3_DEFINE_BITS(B)                                                                        \
+  namespace exl3 {                                                                                 \
+  hipError_t launch_gemm_b##B(int cb, int mt, bool multi, const GemmParams &p, dim3 grid,          \
+                              hipStream_t s) {                                                     \
+    return launch_gemm_bits<B>(cb, mt, multi, p, grid, s);                                         \
+  }                                                                                                \
+  hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s) {              \
+    return launch_decode_bits<B>(cb, p, s);                                                        \
+  }                                                                                                \
+  }

@@ -1,0 +1,303 @@
+// Host side of the C ABI declared in include/exl3.h: argument validation,
+// the shape-only K-part rule, the schedule choice, and kernel launches.
+//
+// Every check runs before any HIP call, so a rejected call touches no device
+// state (the cuda-exl3 README, "Loading into a dim vLLM has padded", asks
+// for errors that say which check failed and by how much; the TensorFold PR
+// refuses what it cannot read, "What it adds").
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/exl3.h"
+#include "exl3_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+exl3_status fail(exl3_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int32_t MAX_M = 1 << 20;
+constexpr int32_t MAX_KN = 1 << 24;
+
+exl3_status check_ptr(const void *p, const char *name) {
+  if (p == nullptr) return fail(EXL3_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(EXL3_ERR_INVALID_ARG, "%s=%p is not 16-byte aligned", name, p);
+  return EXL3_OK;
+}
+
+exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_suh) {
+  if (w == nullptr) return fail(EXL3_ERR_INVALID_ARG, "weight view is NULL");
+  if (w->bits < 1 || w->bits > 8) return fail(EXL3_ERR_INVALID_ARG, "bits=%d, must be 1..8", w->bits);
+  if (w->codebook < EXL3_CB_3INST || w->codebook > EXL3_CB_MUL1)
+    return fail(EXL3_ERR_INVALID_ARG, "codebook=%d, must be 0 (3inst), 1 (mcg) or 2 (mul1)", w->codebook);
+  if (w->K <= 0 || w->K % 128 != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "K=%d must be a positive multiple of 128 (off by %d)", w->K,
+                w->K > 0 ? w->K % 128 : w->K);
+  if (w->N <= 0 || w->N % 128 != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "N=%d must be a positive multiple of 128 (off by %d)", w->N,
+                w->N > 0 ? w->N % 128 : w->N);
+  if (w->K > MAX_KN || w->N > MAX_KN)
+    return fail(EXL3_ERR_UNSUPPORTED, "K=%d or N=%d exceeds the supported %d", w->K, w->N, MAX_KN);
+  if (w->n_shards < 1 || w->n_shards > EXL3_MAX_SHARDS)
+    return fail(EXL3_ERR_INVALID_ARG, "n_shards=%d, must be 1..%d", w->n_shards, EXL3_MAX_SHARDS);
+  if (w->shard_n == nullptr) return fail(EXL3_ERR_INVALID_ARG, "shard_n (host array) is NULL");
+  int64_t total = 0;
+  for (int s = 0; s < w->n_shards; ++s) {
+    const int32_t n = w->shard_n[s];
+    if (n <= 0 || n % 128 != 0)
+      return fail(EXL3_ERR_INVALID_ARG, "shard %d width %d must be a positive multiple of 128 (off by %d)", s, n,
+                  n > 0 ? n % 128 : n);
+    total += n;
+  }
+  if (total != w->N)
+    return fail(EXL3_ERR_INVALID_ARG, "shard widths sum to %lld but N=%d (off by %lld)", (long long)total, w->N,
+                (long long)(total - w->N));
+  exl3_status st;
+  if (need_trellis && (st = check_ptr(w->trellis, "trellis")) != EXL3_OK) return st;
+  if (need_suh && (st = check_ptr(w->suh, "suh")) != EXL3_OK) return st;
+  if ((st = check_ptr(w->svh, "svh")) != EXL3_OK) return st;
+  return EXL3_OK;
+}
+
+// K parts: a function of (K, N, bits) only.  Enough (column block, part)
+// pairs to occupy the GPU at decode sizes (about 1024), parts of at least
+// two 128-k blocks, and the fp32 partial traffic at 16 rows kept under ~60%
+// of the trellis bytes (the cuda-exl3 README caps split-k accumulator
+// traffic at ~30% of the weight bytes and discounts it 2x when it stays in
+// cache, "Two further departures" and "Where the time goes").  P divides the
+// number of 128-k blocks so every part has the same length.
+int32_t choose_parts(int32_t K, int32_t N, int32_t bits) {
+  const int32_t kb = K / 128;
+  const int32_t nblk = N / 128;
+  int32_t want = (1024 + nblk - 1) / nblk;
+  const int32_t cap_len = std::max(1, kb / 2);
+  const int32_t cap_traffic = std::max(1, (int32_t)(0.6 * (double)K * bits / 1024.0));
+  int32_t pmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
+  for (int32_t p = pmax; p >= 1; --p)
+    if (kb % p == 0) return p;
+  return 1;
+}
+
+struct Plan {
+  int32_t parts;
+  int32_t mode;
+  int32_t bm;
+  size_t workspace;
+};
+
+exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out) {
+  Plan pl;
+  pl.parts = choose_parts(w->K, w->N, w->bits);
+  if (force && force->parts > 0) {
+    if (force->parts > w->K / 128)
+      return fail(EXL3_ERR_INVALID_ARG, "forced parts=%d exceeds the %d blocks of 128 in K", force->parts,
+                  w->K / 128);
+    pl.parts = force->parts;
+  }
+  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  if (force && force->bm > 0) {
+    if (force->bm != 16 && force->bm != 32 && force->bm != 64)
+      return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32 or 64", force->bm);
+    pl.bm = force->bm;
+  }
+  pl.mode = (pl.parts > 1 && M <= 64) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
+  if (force && force->mode != EXL3_MODE_AUTO && force->mode >= 0) {
+    if (force->mode != EXL3_MODE_FUSED && force->mode != EXL3_MODE_SLABS)
+      return fail(EXL3_ERR_INVALID_ARG, "forced mode=%d, must be 0 (fused) or 1 (slabs)", force->mode);
+    pl.mode = force->mode;
+  }
+  if (pl.parts == 1) pl.mode = EXL3_MODE_FUSED;  // one part: nothing to sum
+  pl.workspace = pl.mode == EXL3_MODE_SLABS ? (size_t)pl.parts * (size_t)M * (size_t)w->N * sizeof(float) : 0;
+  *out = pl;
+  return EXL3_OK;
+}
+
+exl3_status launch_error(hipError_t e, const char *what) {
+  return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t exl3_abi_version(void) { return EXL3_ABI_VERSION; }
+
+const char *exl3_status_str(exl3_status s) {
+  switch (s) {
+    case EXL3_OK: return "EXL3_OK";
+    case EXL3_ERR_INVALID_ARG: return "EXL3_ERR_INVALID_ARG";
+    case EXL3_ERR_UNSUPPORTED: return "EXL3_ERR_UNSUPPORTED";
+    case EXL3_ERR_WORKSPACE: return "EXL3_ERR_WORKSPACE";
+    case EXL3_ERR_LAUNCH: return "EXL3_ERR_LAUNCH";
+  }
+  return "EXL3_ERR_UNKNOWN";
+}
+
+const char *exl3_last_error(void) { return g_last_error; }
+
+exl3_status exl3_input_transform(const void *x, int32_t x_dtype, int32_t M, int32_t K, const uint16_t *suh,
+                                 int32_t n_shards, uint16_t *x_rot, void *stream) {
+  clear_error();
+  if (x_dtype != EXL3_F16 && x_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "x_dtype=%d, must be 0 (fp16) or 1 (bf16)", x_dtype);
+  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
+  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
+  if (K <= 0 || K % 128 != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "K=%d must be a positive multiple of 128 (off by %d)", K, K > 0 ? K % 128 : K);
+  if (K > MAX_KN) return fail(EXL3_ERR_UNSUPPORTED, "K=%d exceeds the supported %d", K, MAX_KN);
+  if (n_shards < 1 || n_shards > EXL3_MAX_SHARDS)
+    return fail(EXL3_ERR_INVALID_ARG, "n_shards=%d, must be 1..%d", n_shards, EXL3_MAX_SHARDS);
+  exl3_status st;
+  if ((st = check_ptr(suh, "suh")) != EXL3_OK) return st;
+  if (M == 0) return EXL3_OK;
+  if ((st = check_ptr(x, "x")) != EXL3_OK) return st;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_input_transform(x, x_dtype == EXL3_BF16, M, K, suh, n_shards, x_rot,
+                                                    (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "input transform launch");
+}
+
+size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan *force) {
+  clear_error();
+  if (validate_weight(w, false, false) != EXL3_OK) return 0;
+  if (M < 0 || M > MAX_M) {
+    fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
+    return 0;
+  }
+  Plan pl;
+  if (make_plan(w, M, force, &pl) != EXL3_OK) return 0;
+  return pl.workspace;
+}
+
+size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M) { return exl3_workspace_bytes_ex(w, M, nullptr); }
+
+exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan) {
+  clear_error();
+  exl3_status st = validate_weight(w, false, false);
+  if (st != EXL3_OK) return st;
+  if (plan == nullptr) return fail(EXL3_ERR_INVALID_ARG, "plan (host output) is NULL");
+  if (M < 0 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
+  Plan pl;
+  if ((st = make_plan(w, M, nullptr, &pl)) != EXL3_OK) return st;
+  plan->parts = pl.parts;
+  plan->mode = pl.mode;
+  plan->bm = pl.bm;
+  plan->reserved = 0;
+  plan->workspace = pl.workspace;
+  return EXL3_OK;
+}
+
+exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream, const exl3_plan *force) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
+  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
+  Plan pl;
+  if ((st = make_plan(w, M, force, &pl)) != EXL3_OK) return st;
+  if (M == 0) return EXL3_OK;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  if (pl.workspace > 0) {
+    if (workspace == nullptr || workspace_bytes < pl.workspace)
+      return fail(EXL3_ERR_WORKSPACE, "workspace of %zu bytes at %p; this plan needs %zu (short by %zu)",
+                  workspace_bytes, workspace, pl.workspace,
+                  pl.workspace > workspace_bytes ? pl.workspace - workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(EXL3_ERR_INVALID_ARG, "workspace=%p is not 16-byte aligned", workspace);
+  }
+
+  exl3::GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.trellis = w->trellis;
+  p.x_rot = x_rot;
+  p.svh = w->svh;
+  p.y = y;
+  p.slabs = static_cast<float *>(workspace);
+  p.M = M;
+  p.K = w->K;
+  p.N = w->N;
+  p.parts = pl.parts;
+  p.slab_mode = pl.mode == EXL3_MODE_SLABS ? 1 : 0;
+  p.out_bf16 = y_dtype == EXL3_BF16 ? 1 : 0;
+  p.n_shards = w->n_shards;
+  int32_t end = 0;
+  for (int s = 0; s < w->n_shards; ++s) {
+    end += w->shard_n[s] / 128;
+    p.shard_end_blk[s] = end;
+  }
+  const int mt = pl.bm / 16;
+  const dim3 grid((unsigned)(w->N / 128), (unsigned)(p.slab_mode ? pl.parts : 1),
+                  (unsigned)((M + pl.bm - 1) / pl.bm));
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = exl3::launch_gemm(w->bits, w->codebook, mt, !p.slab_mode && pl.parts > 1, p, grid, s);
+  if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
+  if (p.slab_mode) {
+    e = exl3::launch_epilogue(p.slabs, pl.parts, M, w->N, w->svh, y, p.out_bf16 != 0, s);
+    if (e != hipSuccess) return launch_error(e, "part-sum epilogue launch");
+  }
+  return EXL3_OK;
+}
+
+exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  return exl3_linear_ex(w, x_rot, M, y, y_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream) {
+  clear_error();
+  if (codebook < EXL3_CB_3INST || codebook > EXL3_CB_MUL1)
+    return fail(EXL3_ERR_INVALID_ARG, "codebook=%d, must be 0..2", codebook);
+  exl3_status st;
+  if ((st = check_ptr(out, "out")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_debug_codebook(codebook, out, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "codebook launch");
+}
+
+exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  if ((st = check_ptr(wq, "wq")) != EXL3_OK) return st;
+  exl3::DecodeParams p;
+  p.trellis = w->trellis;
+  p.wq = wq;
+  p.K = w->K;
+  p.N = w->N;
+  const hipError_t e = exl3::launch_debug_decode(w->bits, w->codebook, p, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "decode launch");
+}
+
+exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t M, const exl3_weight *w, void *y,
+                                int32_t y_dtype, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, false, false);
+  if (st != EXL3_OK) return st;
+  if (n_parts < 1 || n_parts > 4096) return fail(EXL3_ERR_INVALID_ARG, "n_parts=%d, must be 1..4096", n_parts);
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (M < 0 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
+  if (M == 0) return EXL3_OK;
+  if ((st = check_ptr(z_parts, "z_parts")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  const hipError_t e =
+      exl3::launch_epilogue(z_parts, n_parts, M, w->N, w->svh, y, y_dtype == EXL3_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "epilogue launch");
+}
+
+}  // extern "C"

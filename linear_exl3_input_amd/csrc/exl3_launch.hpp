@@ -1,0 +1,60 @@
+// Host-side launch interface between the C-ABI (exl3_host.cpp) and the
+// kernels (the .hip files).  Plain structs of device pointers and sizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+constexpr int MAX_SHARDS = 16;
+
+struct GemmParams {
+  const uint16_t *trellis;  // [K/16][N/16][16*bits]
+  const uint16_t *x_rot;    // [n_shards][M][K] fp16 bits
+  const uint16_t *svh;      // [N] fp16 bits
+  void *y;                  // [M][N] bf16/fp16 (fused mode)
+  float *slabs;             // [P][M][N] fp32 (slab mode)
+  int32_t M, K, N;
+  int32_t parts;            // P
+  int32_t slab_mode;        // 1: one part per workgroup (blockIdx.y), write slab
+  int32_t out_bf16;
+  int32_t n_shards;
+  int32_t shard_end_blk[MAX_SHARDS];  // exclusive end of shard s, in 128-col blocks
+};
+
+struct DecodeParams {
+  const uint16_t *trellis;
+  uint16_t *wq;  // [K][N] fp16 bits
+  int32_t K, N;
+};
+
+// Launchers (one per bit width; codebook and rows-per-tile are runtime
+// choices that select a template instance).  Return hipSuccess or the
+// launch error.
+hipError_t launch_gemm(int bits, int cb, int mt, bool multi_part, const GemmParams &p, dim3 grid,
+                       hipStream_t s);
+hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s);
+
+hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
+                                  int32_t n_shards, uint16_t *x_rot, hipStream_t s);
+hipError_t launch_epilogue(const float *slabs, int32_t parts, int32_t M, int32_t N, const uint16_t *svh,
+                           void *y, bool out_bf16, hipStream_t s);
+hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
+
+// Per-bit-width entry points, defined in gemm_b<bits>.hip.
+#define EXL3_DECLARE_BITS(B)                                                                  \
+  hipError_t launch_gemm_b##B(int cb, int mt, bool multi_part, const GemmParams &p, dim3 grid, \
+                              hipStream_t s);                                                  \
+  hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);
+EXL3_DECLARE_BITS(1)
+EXL3_DECLARE_BITS(2)
+EXL3_DECLARE_BITS(3)
+EXL3_DECLARE_BITS(4)
+EXL3_DECLARE_BITS(5)
+EXL3_DECLARE_BITS(6)
+EXL3_DECLARE_BITS(7)
+EXL3_DECLARE_BITS(8)
+#undef EXL3_DECLARE_BITS
+
+}  // namespace exl3

@@ -1,0 +1,145 @@
+// Input rotation, ordered split-k output stage and the codebook hook.
+#include "exl3_device.hpp"
+#include "exl3_launch.hpp"
+
+namespace exl3 {
+
+// ------------------------------------------------------- input rotation
+//
+// x~[s][m][:] = fp16_rne(2^-4 * H128(x[m][:] * suh[s][:])) per 128 block
+// (TensorFold PR "cuda: EXL3 projections behind qlinear", "Arithmetic" step
+// 1).  One wave per (row, 128-block); x is read once and reused for every
+// shard's suh row (cuda-exl3 README, "One op per layer": all shards in one
+// launch, reading x once, with bf16 -> fp32 folded into the load).  x*suh is
+// exact in fp32, so the product may be contracted into an add freely.
+template <bool X_BF16>
+__global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__restrict__ x,
+                                                              const uint16_t *__restrict__ suh,
+                                                              uint16_t *__restrict__ x_rot, int32_t M,
+                                                              int32_t K, int32_t n_shards) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int kblocks = K >> 7;
+  if (item >= (int64_t)M * kblocks) return;  // whole wave exits together
+  const int64_t m = item / kblocks;
+  const int k0 = (int)(item - m * kblocks) * 128 + 2 * lane;
+  const uint32_t xv = *(const uint32_t *)(x + m * K + k0);
+  float x0, x1;
+  if constexpr (X_BF16) {
+    x0 = bf16_bits_to_f32(xv & 0xFFFFu);
+    x1 = bf16_bits_to_f32(xv >> 16);
+  } else {
+    x0 = f16_bits_to_f32(xv & 0xFFFFu);
+    x1 = f16_bits_to_f32(xv >> 16);
+  }
+  for (int s = 0; s < n_shards; ++s) {
+    const uint32_t sv = *(const uint32_t *)(suh + (int64_t)s * K + k0);
+    float t0 = x0 * f16_bits_to_f32(sv & 0xFFFFu);
+    float t1 = x1 * f16_bits_to_f32(sv >> 16);
+    hadamard128_wave(t0, t1, lane);
+    const uint32_t packed = f32_to_f16_bits(t0 * 0.0625f) | (f32_to_f16_bits(t1 * 0.0625f) << 16);
+    *(uint32_t *)(x_rot + ((int64_t)s * M + m) * K + k0) = packed;
+  }
+}
+
+hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
+                                  int32_t n_shards, uint16_t *x_rot, hipStream_t s) {
+  const int64_t items = (int64_t)M * (K / 128);
+  const dim3 grid((unsigned)((items + 3) / 4));
+  if (x_bf16)
+    hipLaunchKernelGGL((input_transform_kernel<true>), grid, dim3(256), 0, s, (const uint16_t *)x, suh, x_rot,
+                       M, K, n_shards);
+  else
+    hipLaunchKernelGGL((input_transform_kernel<false>), grid, dim3(256), 0, s, (const uint16_t *)x, suh, x_rot,
+                       M, K, n_shards);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- ordered part sum + output
+//
+// z = ((part0 + part1) + part2) + ... in fp32, then y = rne(svh * 2^-3 *
+// H128(z)) (TensorFold PR, "Arithmetic" step 3 and its ordered part sum).
+// One wave per (row, 128-column block).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t parts,
+                                                       int32_t M, int32_t N, const uint16_t *__restrict__ svh,
+                                                       uint16_t *__restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nblocks = N >> 7;
+  if (item >= (int64_t)M * nblocks) return;
+  const int64_t m = item / nblocks;
+  const int n0 = (int)(item - m * nblocks) * 128;
+  const int64_t slab = (int64_t)M * N;
+  const float *src = slabs + m * N + n0 + 2 * lane;
+  float2 acc = *(const float2 *)src;
+  for (int p = 1; p < parts; ++p) {
+    const float2 v = *(const float2 *)(src + p * slab);
+    acc.x = acc.x + v.x;
+    acc.y = acc.y + v.y;
+  }
+  output_row<OUT_BF16>(acc.x, acc.y, svh, y + m * N, n0, lane);
+}
+
+hipError_t launch_epilogue(const float *slabs, int32_t parts, int32_t M, int32_t N, const uint16_t *svh,
+                           void *y, bool out_bf16, hipStream_t s) {
+  const int64_t items = (int64_t)M * (N / 128);
+  const dim3 grid((unsigned)((items + 3) / 4));
+  if (out_bf16)
+    hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, parts, M, N, svh, (uint16_t *)y);
+  else
+    hipLaunchKernelGGL((epilogue_kernel<false>), grid, dim3(256), 0, s, slabs, parts, M, N, svh, (uint16_t *)y);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ codebook hook
+//
+// Every state through decode_pair, the function the GEMM's decoder uses.
+template <uint32_t CB>
+__global__ __launch_bounds__(256) void codebook_kernel(uint32_t *__restrict__ out) {
+  const uint32_t i = blockIdx.x * 256 + threadIdx.x;  // pair index, 0..32767
+  out[i] = decode_pair<CB>(2 * i, 2 * i + 1);
+}
+
+hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s) {
+  const dim3 grid(32768 / 256);
+  switch (cb) {
+    case 0: hipLaunchKernelGGL((codebook_kernel<CB_3INST>), grid, dim3(256), 0, s, (uint32_t *)out); break;
+    case 1: hipLaunchKernelGGL((codebook_kernel<CB_MCG>), grid, dim3(256), 0, s, (uint32_t *)out); break;
+    case 2: hipLaunchKernelGGL((codebook_kernel<CB_MUL1>), grid, dim3(256), 0, s, (uint32_t *)out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ bit-width dispatch
+
+hipError_t launch_gemm(int bits, int cb, int mt, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_gemm_b1(cb, mt, multi, p, grid, s);
+    case 2: return launch_gemm_b2(cb, mt, multi, p, grid, s);
+    case 3: return launch_gemm_b3(cb, mt, multi, p, grid, s);
+    case 4: return launch_gemm_b4(cb, mt, multi, p, grid, s);
+    case 5: return launch_gemm_b5(cb, mt, multi, p, grid, s);
+    case 6: return launch_gemm_b6(cb, mt, multi, p, grid, s);
+    case 7: return launch_gemm_b7(cb, mt, multi, p, grid, s);
+    case 8: return launch_gemm_b8(cb, mt, multi, p, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_debug_decode_b1(cb, p, s);
+    case 2: return launch_debug_decode_b2(cb, p, s);
+    case 3: return launch_debug_decode_b3(cb, p, s);
+    case 4: return launch_debug_decode_b4(cb, p, s);
+    case 5: return launch_debug_decode_b5(cb, p, s);
+    case 6: return launch_debug_decode_b6(cb, p, s);
+    case 7: return launch_debug_decode_b7(cb, p, s);
+    case 8: return launch_debug_decode_b8(cb, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace exl3

@@ -1,0 +1,3 @@
+// Trellis GEMM and decode kernels for 2-bit weights (all codebooks).
+#include "exl3_gemm.hpp"
+EXL3_DEFINE_BITS(2)

@@ -1,0 +1,130 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+plans from the shape alone, and rejects bad arguments before any HIP call.
+No call here reaches a kernel launch (there is no GPU on this machine)."""
+import ctypes
+import os
+
+import pytest
+
+import linear_exl3_input_amd as ex
+import workloads as wl
+
+LIB = ex.lib_path()
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libexl3.so not built")
+
+FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced
+
+
+def view(K, shards, bits, cb, trellis=FAKE, suh=FAKE, svh=FAKE):
+    arr = (ctypes.c_int32 * len(shards))(*shards)
+    w = ex._Weight(trellis, suh, svh, K, sum(shards), bits, cb, len(shards), arr)
+    w._keep = arr
+    return w
+
+
+def last_error():
+    return ex.load().exl3_last_error().decode()
+
+
+def test_exports_every_header_symbol():
+    L = ex.load()
+    names = ex.header_symbols()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.exl3_abi_version() == 1
+
+
+def test_status_strings():
+    L = ex.load()
+    assert L.exl3_status_str(0) == b"EXL3_OK"
+    assert L.exl3_status_str(3) == b"EXL3_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("K,shards,bits,cb,msg", [
+    (100, (128,), 4, 1, "K=100 must be a positive multiple of 128"),
+    (256, (100, 156), 4, 1, "shard 0 width 100"),
+    (256, (128, 128), 9, 1, "bits=9"),
+    (256, (128,), 0, 1, "bits=0"),
+    (256, (128,), 4, 3, "codebook=3"),
+])
+def test_bad_weight_rejected(K, shards, bits, cb, msg):
+    L = ex.load()
+    w = view(K, shards, bits, cb)
+    st = L.exl3_linear(ctypes.byref(w), FAKE, 4, FAKE, 1, None, 0, None)
+    assert st == 1
+    assert msg in last_error()
+
+
+def test_shard_sum_mismatch_rejected():
+    L = ex.load()
+    w = view(256, (128, 256), 4, 1)
+    w.N = 256  # shards sum to 384
+    st = L.exl3_linear(ctypes.byref(w), FAKE, 4, FAKE, 1, None, 0, None)
+    assert st == 1 and "sum to 384 but N=256 (off by 128)" in last_error()
+
+
+def test_pointer_checks():
+    L = ex.load()
+    w = view(256, (128,), 4, 1, trellis=0)
+    assert L.exl3_linear(ctypes.byref(w), FAKE, 4, FAKE, 1, None, 0, None) == 1
+    assert "trellis is NULL" in last_error()
+    w = view(256, (128,), 4, 1, trellis=FAKE + 4)
+    assert L.exl3_linear(ctypes.byref(w), FAKE, 4, FAKE, 1, None, 0, None) == 1
+    assert "not 16-byte aligned" in last_error()
+    w = view(256, (128,), 4, 1)
+    assert L.exl3_linear(ctypes.byref(w), FAKE + 2, 4, FAKE, 1, None, 0, None) == 1
+    assert "x_rot" in last_error()
+    assert L.exl3_linear(ctypes.byref(w), FAKE, 4, FAKE, 7, None, 0, None) == 1
+    assert "y_dtype=7" in last_error()
+    assert L.exl3_linear(ctypes.byref(w), FAKE, -1, FAKE, 1, None, 0, None) == 1
+
+
+def test_workspace_too_small_rejected():
+    L = ex.load()
+    w = view(4096, (2048,), 4, 1)  # P > 1, slab mode at 16 rows
+    need = L.exl3_workspace_bytes(ctypes.byref(w), 16)
+    assert need > 0
+    st = L.exl3_linear(ctypes.byref(w), FAKE, 16, FAKE, 1, FAKE, need - 16, None)
+    assert st == 3 and "short by 16" in last_error()
+
+
+def test_zero_rows_needs_nothing():
+    L = ex.load()
+    w = view(256, (128,), 4, 1)
+    assert L.exl3_linear(ctypes.byref(w), None, 0, None, 1, None, 0, None) == 0
+    assert L.exl3_input_transform(None, 1, 0, 256, FAKE, 1, None, None) == 0
+
+
+def test_input_transform_checks():
+    L = ex.load()
+    assert L.exl3_input_transform(FAKE, 1, 4, 200, FAKE, 1, FAKE, None) == 1
+    assert L.exl3_input_transform(FAKE, 1, 4, 256, FAKE, 0, FAKE, None) == 1
+    assert L.exl3_input_transform(FAKE, 1, 4, 256, FAKE, 17, FAKE, None) == 1
+    assert L.exl3_input_transform(FAKE, 2, 4, 256, FAKE, 1, FAKE, None) == 1
+    assert L.exl3_input_transform(FAKE, 1, 4, 256, None, 1, FAKE, None) == 1
+
+
+def _plan(w, M):
+    p = ex._Plan()
+    assert ex.load().exl3_plan_query(ctypes.byref(w), M, ctypes.byref(p)) == 0
+    return p
+
+
+def test_parts_depend_on_shape_only():
+    for lay in wl.LAYERS:
+        w = view(lay.K, lay.shards, lay.bits, lay.cb)
+        parts = {_plan(w, M).parts for M in (1, 16, 64, 65, 512, 4096)}
+        assert len(parts) == 1, (lay.name, parts)
+        P = parts.pop()
+        assert (lay.K // 128) % P == 0
+
+
+def test_plan_modes_and_workspace():
+    w = view(17408, (5120,), 6, 2)
+    small, big = _plan(w, 16), _plan(w, 512)
+    assert small.parts == big.parts > 1
+    assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == small.parts * 16 * 5120 * 4
+    assert big.mode == ex.EXL3_MODE_FUSED and big.workspace == 0
+    head = view(4096, (154880,), 6, 2)
+    assert _plan(head, 1).parts == 1 and _plan(head, 1).workspace == 0

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact where the format fixes every rounding (codebooks, unpacking, the
+input rotation, the output stage given z); within the rounding-order bound of
+the oracle (and worst-column relative error <= 5e-3) for the whole linear,
+whose fp32 sums run inside the matrix unit in an order the pages leave open.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_exl3_input_amd as ex
+import workloads as wl
+from oracle import format as ofmt
+from oracle import linear as olin
+from oracle import transform as otf
+from gpu_util import banner, bits16, dev16, weight, x_dev
+
+pytestmark = pytest.mark.gpu
+
+CB_NAMES = ("3inst", "mcg", "mul1")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ex.load()
+    torch.cuda.init()
+
+
+# ------------------------------------------------------------ bit-exact parts
+
+@pytest.mark.parametrize("cb", CB_NAMES)
+def test_codebook_every_state(cb):
+    banner(f"codebook {cb}")
+    got = bits16(ex.debug_codebook(cb))
+    want = ofmt.codebook_table(wl.CB_ID[cb])
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} states differ, first {bad[:5]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("cb", CB_NAMES)
+def test_decode_every_width_and_codebook(bits, cb):
+    banner(f"decode bits={bits} cb={cb}")
+    lay = wl.small_layer(f"dec_b{bits}_{cb}", 256, (384,), bits, cb, (1,), seed=40 + bits)
+    t = wl.gen_all(lay)
+    got = bits16(ex.debug_decode(weight(t)))
+    want = ofmt.dequantize_bits(t.trellis, bits, lay.cb)
+    bad = np.argwhere(got != want)
+    assert bad.shape[0] == 0, f"{bad.shape[0]} weights differ, first (k, n) {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M,K,S", [(1, 128, 1), (7, 384, 3), (33, 1024, 2), (130, 256, 1)])
+def test_input_transform_bit_exact(x_dtype, M, K, S):
+    banner(f"input transform {x_dtype} M={M} K={K} S={S}")
+    rng = np.random.default_rng(1000 + M + K + S)
+    xf = rng.standard_normal((M, K)).astype(np.float32) * 3
+    x = otf.f32_to_bf16_bits(xf) if x_dtype == "bf16" else otf.f32_to_f16_bits(xf)
+    suh = (np.where(rng.integers(0, 2, (S, K)) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, (S, K)))
+           ).astype(np.float16).view(np.uint16)
+    got = bits16(ex.input_transform(x_dev(x, x_dtype), dev16(suh, torch.float16)))
+    want = otf.rotate_input(x, suh, x_dtype)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+def test_input_transform_one_hot_closed_form():
+    import scipy.linalg
+    h = scipy.linalg.hadamard(128)
+    x = np.zeros((128, 128), dtype=np.uint16)
+    x[np.arange(128), np.arange(128)] = 0x3F80  # row j = e_j (bf16 1.0)
+    suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
+    got = bits16(ex.input_transform(x_dev(x), dev16(suh, torch.float16)))[0]
+    want = np.where(h.T > 0, 0x2C00, 0xAC00).astype(np.uint16)  # row j = signs of column j
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("P,M,N", [(1, 3, 128), (3, 17, 384), (8, 64, 256)])
+def test_output_stage_bit_exact(out_dtype, P, M, N):
+    banner(f"epilogue {out_dtype} P={P} M={M} N={N}")
+    rng = np.random.default_rng(2000 + P + M + N)
+    z = (rng.standard_normal((P, M, N)) * np.exp2(rng.integers(-6, 6, (P, M, N)))).astype(np.float32)
+    svh = (np.where(rng.integers(0, 2, N) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, N))
+           ).astype(np.float16).view(np.uint16)
+    lay = wl.small_layer("ep", 128, (N,), 4, "mcg")
+    trellis = np.zeros((8, N // 16, 64), dtype=np.uint16)
+    suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
+    w = ex.Exl3Weight(dev16(trellis), dev16(suh, torch.float16), dev16(svh, torch.float16), 4, "mcg", (N,))
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
+    got = bits16(ex.debug_epilogue(w, torch.from_numpy(z).cuda(), dt))
+    want = otf.output_transform_f32(otf.reduce_parts_f32(z), svh, out_dtype)
+    assert np.array_equal(got, want)
+    del lay
+
+
+# ------------------------------------------------------- the whole linear
+
+def _run(t, out_dtype="bf16", M=None, x_dtype="bf16", **force):
+    x = t.x if M is None else t.x[:M]
+    w = weight(t)
+    xr = ex.input_transform(x_dev(x, x_dtype), w.suh)
+    y = ex.linear(w, xr, torch.bfloat16 if out_dtype == "bf16" else torch.float16, **force)
+    torch.cuda.synchronize()
+    return bits16(y)
+
+
+def _check(t, y, out_dtype="bf16", M=None, x_dtype="bf16"):
+    lay = t.layer
+    x = t.x if M is None else t.x[:M]
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, x, x_dtype)
+    res = olin.check(y, ref, t.svh, lay.K, out_dtype)
+    banner(f"{lay.name} M={x.shape[0]} {out_dtype}: {res}")
+    assert res.ok, str(res)
+    return res
+
+
+SMALL = [wl.small_layer(f"lin_b{b}_{cb}", 256, (256,), b, cb, (5,), seed=60 + b) for b in range(1, 9)
+         for cb in CB_NAMES]
+
+
+@pytest.mark.parametrize("lay", SMALL, ids=lambda l: l.name)
+def test_linear_every_width_and_codebook(lay):
+    t = wl.gen_all(lay)
+    _check(t, _run(t))
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("magnitudes", [False, True])
+def test_linear_two_shards(out_dtype, magnitudes):
+    lay = wl.small_layer("two_shards", 384, (128, 256), 6, "mul1", (33,), seed=7)
+    t = wl.gen_all(lay, magnitudes=magnitudes)
+    _check(t, _run(t, out_dtype), out_dtype)
+
+
+def test_linear_fp16_activations():
+    lay = wl.small_layer("f16x", 512, (256,), 5, "mcg", (9,), seed=8)
+    t = wl.gen_all(lay)
+    rng = np.random.default_rng(9)
+    t.x = otf.f32_to_f16_bits(rng.standard_normal((9, 512)).astype(np.float32))
+    _check(t, _run(t, x_dtype="f16"), x_dtype="f16")
+
+
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 33, 64, 65, 130])
+def test_linear_ragged_rows(M):
+    lay = wl.small_layer("ragged", 1024, (256,), 4, "3inst", (130,), seed=10)
+    t = wl.gen_all(lay)
+    _check(t, _run(t, M=M), M=M)
+
+
+@pytest.mark.parametrize("parts", [1, 2, 4, 8])
+def test_schedules_agree_bit_for_bit(parts):
+    """mode and rows-per-tile never change a bit; every part count is in bound."""
+    lay = wl.small_layer("sched", 1024, (128, 256), 6, "mul1", (70,), seed=11)
+    t = wl.gen_all(lay)
+    outs = {}
+    for mode in (ex.EXL3_MODE_FUSED, ex.EXL3_MODE_SLABS):
+        for bm in (16, 32, 64):
+            outs[(mode, bm)] = _run(t, parts=parts, mode=mode, bm=bm)
+    first = next(iter(outs.values()))
+    for key, y in outs.items():
+        assert np.array_equal(y, first), f"schedule {key} differs"
+    _check(t, first)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_row_alone_equals_row_in_batch():
+    """A row's bytes are the same at every batch size (prefix rows)."""
+    lay = wl.small_layer("inv", 2048, (512,), 4, "mcg", (96,), seed=12)
+    t = wl.gen_all(lay)
+    full = _run(t)
+    for M in (1, 2, 15, 16, 17, 40, 64, 65):
+        part = _run(t, M=M)
+        assert np.array_equal(part, full[:M]), f"M={M}"
+    # and a single row moved to another position of a batch
+    x = t.x.copy()
+    x[50] = t.x[3]
+    t2 = wl.Tensors(lay, t.trellis, t.suh, t.svh, x)
+    assert np.array_equal(_run(t2)[50], full[3])
+
+
+def test_repeat_runs_identical():
+    lay = wl.small_layer("rep", 2048, (256,), 6, "mul1", (20,), seed=13)
+    t = wl.gen_all(lay)
+    a = _run(t)
+    for _ in range(3):
+        assert np.array_equal(_run(t), a)
+
+
+def test_svh_sign_and_zero_columns():
+    lay = wl.small_layer("svh", 512, (256,), 3, "3inst", (11,), seed=14)
+    t = wl.gen_all(lay, magnitudes=True)
+    y = _run(t)
+    neg = wl.Tensors(lay, t.trellis, t.suh, t.svh ^ np.uint16(0x8000), t.x)
+    assert np.array_equal(_run(neg), y ^ np.uint16(0x8000))
+    svh = t.svh.copy()
+    svh[[0, 77, 200]] = 0
+    zero = wl.Tensors(lay, t.trellis, t.suh, svh, t.x)
+    yz = _run(zero)
+    assert np.all(yz[:, [0, 77, 200]] & np.uint16(0x7FFF) == 0)
+
+
+def test_doubling_x_doubles_y():
+    lay = wl.small_layer("dbl", 512, (128,), 5, "mul1", (8,), seed=15)
+    t = wl.gen_all(lay)
+    xr = otf.rotate_input(t.x, t.suh)
+    assert np.all((xr & 0x7C00) != 0)  # no fp16 subnormal in x~, so scaling by 2 is exact
+    y = _run(t)
+    x2 = t.x + np.uint16(0x0080)  # bf16 exponent + 1 (no zeros / subnormals in x)
+    assert np.all((t.x & 0x7F80) != 0)
+    y2 = _run(wl.Tensors(lay, t.trellis, t.suh, t.svh, x2))
+    f = lambda b: otf.bf16_bits_to_f32(b).astype(np.float64)
+    assert np.array_equal(f(y2), 2.0 * f(y))
+
+
+def test_two_shard_call_equals_two_single_calls():
+    lay = wl.small_layer("i3", 512, (256, 128), 4, "mcg", (19,), seed=16)
+    t = wl.gen_all(lay)
+    fused = _run(t, parts=1)
+    c0 = 0
+    for s, n in enumerate(lay.shards):
+        sub = wl.Layer("sub", lay.K, (n,), lay.bits, lay.codebook, lay.M_values, lay.seed_base)
+        ts = wl.Tensors(sub, t.trellis[:, c0 // 16:(c0 + n) // 16].copy(), t.suh[s:s + 1].copy(),
+                        t.svh[c0:c0 + n].copy(), t.x)
+        assert np.array_equal(_run(ts, parts=1), fused[:, c0:c0 + n])
+        c0 += n
+
+
+def test_zero_rows_is_a_noop():
+    lay = wl.small_layer("m0", 256, (128,), 2, "mul1", (1,), seed=17)
+    t = wl.gen_all(lay)
+    w = weight(t)
+    xr = torch.empty((1, 0, 256), dtype=torch.float16, device="cuda")
+    y = ex.linear(w, xr)
+    assert y.shape == (0, 128)
+
+
+# --------------------------------------------- full-size workloads, sampled
+
+FULL = [("small_1024x1024_b4_3inst", 16), ("expert_4096x2048_b4_mcg", 512), ("expert_2048x4096_b4_mcg", 16),
+        ("q_proj_5120x12288_b6_mul1", 128), ("down_proj_17408x5120_b6_mul1", 16),
+        ("gate_up_5120x2x17408_b5_mul1", 2048), ("lm_head_4096x154880_b6_mul1", 16)]
+
+
+@pytest.mark.parametrize("name,M", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, M):
+    lay = wl.layer(name)
+    banner(f"full size {name} M={M}")
+    t = wl.gen_all(lay, M=M)
+    w = weight(t)
+    xr = ex.input_transform(x_dev(t.x), w.suh)
+    y = bits16(ex.linear(w, xr, torch.bfloat16))
+    # batch invariance at the real shape: the first row alone
+    y1 = bits16(ex.linear(w, xr[:, :1].contiguous(), torch.bfloat16))
+    assert np.array_equal(y1[0], y[0])
+    rows = sorted({0, M // 2, M - 1})
+    nblk = lay.N // 128
+    blocks = sorted({0, nblk // 3, nblk - 1} | ({lay.shards[0] // 128} if lay.n_shards > 1 else set()))
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
+    ysel = y[rows][:, ref.cols]
+    res = olin.check(ysel, ref, t.svh, lay.K, "bf16")
+    banner(f"{name} M={M} sampled rows {rows} blocks {blocks}: {res}")
+    assert res.ok, str(res)
