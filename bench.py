@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--pool-mb", type=int, default=640, help="weight pool size (defeats the 256 MB cache)")
-    ap.add_argument("--timing-reps", type=int, default=20)
+    ap.add_argument("--timing-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
     args = ap.parse_args()
@@ -203,53 +203,54 @@ def main():
     value = 100.0 * sol_step / (ms_per_step / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, SoL {sol_step * 1e3:.4f} ms -> {value:.2f}% SoL")
 
-    # ---- per-launch kernel timing with HIP events on the launch stream
+    # ---- per-launch timing with HIP events on the launch stream: R launches
+    # back to back between one event pair, queued behind a spin kernel so the
+    # GPU never waits on the host inside the pair (an event pair per launch
+    # costs several microseconds on this stack, more than the small kernels).
     spin = getattr(torch.cuda, "_sleep", None)
+
+    def time_calls(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        if spin is not None:
+            spin(int(1e7))
+        e0.record(stream)
+        for r in range(reps):
+            fn(r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # microseconds per call
+
     per_shape = []
     with torch.cuda.stream(stream):
         for li, (lay, ws, x, xr, y) in enumerate(per_layer):
             for M in Ms:
-                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                       torch.cuda.Event(enable_timing=True)) for _ in range(args.timing_reps)]
-                torch.cuda.synchronize()
-                if spin is not None:
-                    spin(int(2e7))  # ~10 ms of spinning so the launches below queue up behind it
-                for r, (e0, e1, e2) in enumerate(ev):
-                    w = ws[(r * 7 + 3) % copies]
-                    e0.record(stream)
-                    ex.input_transform(x[:M], w.suh, out=xr[M])
-                    e1.record(stream)
-                    ex.linear(w, xr[M], torch.bfloat16, out=y[M])
-                    e2.record(stream)
-                torch.cuda.synchronize()
-                t_in = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1, _ in ev)
-                t_lin = sorted(e1.elapsed_time(e2) * 1e3 for _, e1, e2 in ev)
-                med_in = t_in[len(t_in) // 2]
-                avg_lin = sum(t_lin) / len(t_lin)
-                med_lin = t_lin[len(t_lin) // 2]
+                pick = lambda r: ws[(r * 7 + 3) % copies]
+                t_in = time_calls(lambda r: ex.input_transform(x[:M], pick(r).suh, out=xr[M]), args.timing_reps)
+                t_lin = time_calls(lambda r: ex.linear(pick(r), xr[M], torch.bfloat16, out=y[M]), args.timing_reps)
                 pl = ex.plan(ws[0], M)
                 byts = lay.weight_bytes()
                 flops = 2.0 * M * lay.K * lay.N
                 sol = sol_seconds(M, lay.K, lay.N, lay.bits)
                 per_shape.append({
                     "layer": lay.name, "M": M, "K": lay.K, "N": lay.N, "bits": lay.bits, "codebook": lay.codebook,
-                    "plan": pl, "transform_us": round(med_in, 3), "linear_us": round(med_lin, 3),
-                    "linear_avg_us": round(avg_lin, 3), "linear_min_us": round(t_lin[0], 3),
-                    "GBps": round(byts / (med_lin * 1e-6) / 1e9, 1),
-                    "TFLOPS": round(flops / (med_lin * 1e-6) / 1e12, 2),
-                    "pct_sol": round(100.0 * sol / (med_lin * 1e-6), 2),
-                    "pct_sol_with_transform": round(100.0 * sol / ((med_lin + med_in) * 1e-6), 2),
+                    "plan": pl, "transform_us": round(t_in, 3), "linear_us": round(t_lin, 3),
+                    "kernels_per_linear": 2 if pl["mode"] == ex.EXL3_MODE_SLABS else 1,
+                    "GBps": round(byts / (t_lin * 1e-6) / 1e9, 1),
+                    "TFLOPS": round(flops / (t_lin * 1e-6) / 1e12, 2),
+                    "pct_sol": round(100.0 * sol / (t_lin * 1e-6), 2),
+                    "pct_sol_with_transform": round(100.0 * sol / ((t_lin + t_in) * 1e-6), 2),
                     "bound": "mfma" if flops / MFMA_F16_FLOPS > byts / HBM_BPS else "hbm",
                 })
-                log(f"{lay.name} M={M}: plan {pl}, transform {med_in:.2f} us, linear {med_lin:.2f} us "
+                log(f"{lay.name} M={M}: plan {pl}, transform {t_in:.2f} us, linear {t_lin:.2f} us "
                     f"({per_shape[-1]['GBps']} GB/s, {per_shape[-1]['TFLOPS']} TFLOP/s, "
                     f"{per_shape[-1]['pct_sol']}% SoL)")
 
     # ---- roofline of the dominant single-kernel linear call class
     single = [s for s in per_shape if s["plan"]["mode"] == ex.EXL3_MODE_FUSED] or per_shape
-    dom = max(single, key=lambda s: s["linear_avg_us"])
+    dom = max(single, key=lambda s: s["linear_us"])
     lay = wl.layer(dom["layer"])
-    secs = dom["linear_avg_us"] * 1e-6
+    secs = dom["linear_us"] * 1e-6
     if dom["bound"] == "mfma":
         achieved = 2.0 * dom["M"] * lay.K * lay.N / secs / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s"}
@@ -259,7 +260,7 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
     roof["kernel"] = f"exl3 gemm_kernel, {dom['layer']} M={dom['M']} (plan {dom['plan']})"
-    roof["avg_launch_us"] = dom["linear_avg_us"]
+    roof["avg_launch_us"] = dom["linear_us"]
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         try:

@@ -92,7 +92,7 @@ typedef enum {
 typedef struct exl3_plan {
   int32_t parts;       /* P >= 1 K parts                                     */
   int32_t mode;        /* exl3_mode                                          */
-  int32_t bm;          /* rows per M-tile: 16, 32, 64 or 128                 */
+  int32_t bm;          /* rows per M-tile: 16, 32, 64, 128 or 256           */
   int32_t reserved;
   size_t workspace;    /* bytes of workspace this plan needs                 */
 } exl3_plan;
@@ -106,7 +106,11 @@ typedef struct exl3_plan {
  * butterfly strides 1, 2, ..., 64 in ascending order; x*suh is exact.
  *   x      [M][K] bf16 or fp16 bits (x_dtype)
  *   suh    [n_shards][K] fp16 bits
- *   x_rot  [n_shards][M][K] fp16 bits (output, written completely)
+ *   x_rot  [n_shards][M][K] fp16 bits (output, written completely), in
+ *          FRAGMENT ORDER: within every aligned group of 32 k the eight
+ *          4-element chunks are stored in the order 0, 2, 1, 3, 4, 6, 5, 7,
+ *          so that the 8 values one matrix-core lane multiplies are 16
+ *          contiguous bytes.  Only the memory order differs from the formula.
  * Errors: EXL3_ERR_INVALID_ARG for K % 128 != 0, M < 0, n_shards out of
  * range, a null or misaligned pointer, or an unknown dtype. */
 exl3_status exl3_input_transform(const void *x, int32_t x_dtype, int32_t M, int32_t K,
@@ -124,7 +128,8 @@ size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M);
  *             in P shape-fixed K parts, summed in part order)
  *   y[m][n] = rne_out( svh[n] * 2^-3 * H128(z[m][:])[n] )  per 128-col block
  * where s(n) is the shard holding absolute column n.
- *   x_rot     [n_shards][M][K] fp16 bits, as written by exl3_input_transform
+ *   x_rot     [n_shards][M][K] fp16 bits in fragment order, as written by
+ *             exl3_input_transform
  *   y         [M][N] in y_dtype (output, written completely)
  *   workspace at least exl3_workspace_bytes(w, M) bytes (may be NULL if 0);
  *             its contents on entry do not matter.

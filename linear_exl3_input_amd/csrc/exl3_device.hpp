@@ -60,25 +60,64 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 constexpr uint32_t CB_3INST = 0, CB_MCG = 1, CB_MUL1 = 2;
 
-template <uint32_t C>
+// 16-bit x 16-bit products in full-rate VALU ops.  v_mad_u32_u16 and the
+// packed 16-bit ops read only the low halves they are told to, so a state may
+// carry garbage above bit 15.  (Written as inline asm: the compiler otherwise
+// masks the state and uses the quarter-rate v_mul_lo_u32.)
+__device__ __forceinline__ uint32_t mad_u32_u16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+// {lo: 0, hi: (a[15:0] * kh) mod 2^16} for k = kh << 16.
+__device__ __forceinline__ uint32_t pk_mul_lo_u16_dup(uint32_t a, uint32_t k) {
+  uint32_t d;
+  asm("v_pk_mul_lo_u16 %0, %1, %2 op_sel_hi:[0,1]" : "=v"(d) : "v"(a), "v"(k));
+  return d;
+}
+// {lo: c[15:0], hi: (a[15:0] * kh + c[31:16]) mod 2^16} for k = kh << 16.
+__device__ __forceinline__ uint32_t pk_mad_u16_dup(uint32_t a, uint32_t k, uint32_t c) {
+  uint32_t d;
+  asm("v_pk_mad_u16 %0, %1, %2, %3 op_sel_hi:[0,1,1]" : "=v"(d) : "v"(a), "v"(k), "v"(c));
+  return d;
+}
+
+// (s mod 2^16) * C + B  (mod 2^32) in two full-rate ops:
+//   t = {B_lo, (s * C_hi + B_hi) mod 2^16};  u = s * C_lo + t.
+template <uint32_t C, uint32_t B>
 __device__ __forceinline__ uint32_t mul16_const(uint32_t s) {
-  // (s mod 2^16) * C mod 2^32 from two 16x16-bit products.
-  const uint32_t s16 = s & 0xFFFFu;
-  return s16 * (C & 0xFFFFu) + ((s16 * (C >> 16)) << 16);
+  const uint32_t kh = C & 0xFFFF0000u;
+  uint32_t t;
+  if constexpr (B == 0) t = pk_mul_lo_u16_dup(s, kh);
+  else t = pk_mad_u16_dup(s, kh, B);
+  return mad_u32_u16(s, C & 0xFFFFu, t);
 }
 
 template <uint32_t CB>
 __device__ __forceinline__ uint32_t cb_hash(uint32_t s) {
-  if constexpr (CB == CB_3INST) return mul16_const<0x2C9277B5u>(s) + 0x3C6EF372u;
-  else if constexpr (CB == CB_MCG) return mul16_const<0xCBAC1FEDu>(s);
-  else return mul16_const<0x9E3779B1u>(s);
+  if constexpr (CB == CB_3INST) return mul16_const<0x2C9277B5u, 0x3C6EF372u>(s);
+  else if constexpr (CB == CB_MCG) return mul16_const<0xCBAC1FEDu, 0u>(s);
+  else return mul16_const<0x9E3779B1u, 0u>(s);
 }
 
-__device__ __forceinline__ _Float16 pair_sum_f16(uint32_t u) {
-  const uint32_t m = (u & 0x8FFF8FFFu) | 0x30003000u;
-  const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu));
-  const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
-  return lo + hi;
+// P(u) for two words: lo half = P(u0), hi half = P(u1).  Each fp16 add reads
+// the two halves of one masked word (SDWA selects) and writes one half of the
+// result, the other half preserved.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(o));
+  return d;
+}
+
+__device__ __forceinline__ uint32_t pair_sum2(uint32_t u0, uint32_t u1) {
+  const uint32_t m0 = and_or(u0, 0x8FFF8FFFu, 0x30003000u);
+  const uint32_t m1 = and_or(u1, 0x8FFF8FFFu, 0x30003000u);
+  uint32_t r;
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1"
+      : "=v"(r) : "v"(m0));
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0 src1_sel:WORD_1"
+      : "+v"(r) : "v"(m1));
+  return r;
 }
 
 // Two states -> two fp16 values packed in one register (s0 low, s1 high).
@@ -94,9 +133,29 @@ __device__ __forceinline__ uint32_t decode_pair(uint32_t s0, uint32_t s1) {
                        __builtin_bit_cast(_Float16, (uint16_t)0xC931)};
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h, alpha, c));
   } else {
-    const half2_t v = {pair_sum_f16(cb_hash<CB>(s0)), pair_sum_f16(cb_hash<CB>(s1))};
-    return __builtin_bit_cast(uint32_t, v);
+    return pair_sum2(cb_hash<CB>(s0), cb_hash<CB>(s1));
   }
+}
+
+// Keep an fp32 value as an fp32 register value: stops the compiler from
+// fusing the product that produced it into a mixed-precision convert (which
+// would round once instead of rounding to fp32 and then to the output type).
+__device__ __forceinline__ float keep_f32(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// ----------------------------------------------- rotated-activation layout
+//
+// x~ is stored in "fragment order": inside every aligned group of 32 k, the
+// 4-element chunks are stored in the order 0, 2, 1, 3, 4, 6, 5, 7 (chunk
+// index bits b2 b1 b0 stored at b2 b0 b1).  Lane group g of an MFMA operand
+// holds k = 16(g>>1) + 4(g&1) + {0,1,2,3,8,9,10,11}, which is then the
+// contiguous run 8g..8g+7.  The values are those of the natural order.
+__device__ __forceinline__ int frag_order_k(int k) {
+  const int c = (k >> 2) & 7;
+  const int cs = (c & 4) | ((c & 1) << 1) | ((c >> 1) & 1);
+  return (k & ~31) | (cs << 2) | (k & 3);
 }
 
 // ------------------------------------------------ wavefront Hadamard (fp32)
@@ -131,8 +190,8 @@ __device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *_
                                            uint16_t *__restrict__ yrow, int n0, int lane) {
   hadamard128_wave(z0, z1, lane);
   const uint32_t sv = *(const uint32_t *)(svh + n0 + 2 * lane);
-  const float y0 = (z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu);
-  const float y1 = (z1 * 0.125f) * f16_bits_to_f32(sv >> 16);
+  const float y0 = keep_f32((z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu));
+  const float y1 = keep_f32((z1 * 0.125f) * f16_bits_to_f32(sv >> 16));
   uint32_t packed;
   if constexpr (OUT_BF16) packed = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
   else packed = f32_to_f16_bits(y0) | (f32_to_f16_bits(y1) << 16);

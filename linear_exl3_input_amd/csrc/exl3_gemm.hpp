@@ -263,13 +263,8 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
     for (int ks = 0; ks < 4; ++ks) {
       half8_t a[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t *ap = ab + (mt * 16 + j) * A_ROW_DW + 16 * ks + 8 * (g >> 1) + 2 * (g & 1);
-        const u32x2_t lo = *(const u32x2_t *)ap;
-        const u32x2_t hi = *(const u32x2_t *)(ap + 4);
-        const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
-        a[mt] = __builtin_bit_cast(half8_t, v);
-      }
+      for (int mt = 0; mt < MT; ++mt)  // x~ is in fragment order: 16 contiguous bytes
+        a[mt] = *(const half8_t *)(ab + (mt * 16 + j) * A_ROW_DW + 16 * ks + 4 * g);
       const uint32_t *tp = tb + (tile_lane + 2 * WG_NT * ks) * G::STRIDE;
       const half8_t b0 = decode_frag<BITS, CB>(tp, xoff0, sh0);
 #pragma unroll
@@ -341,6 +336,204 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
   }
 }
 
+// ------------------------------------------------------------- tall GEMM
+//
+// For larger M: a BM = 64*WM row x 128 column tile on 4 waves, wave w owning
+// rows [16*WM*w, 16*WM*(w+1)) of the tile against all 128 columns.  Wave w
+// still decodes the B operands of n-tiles 2w and 2w+1, exactly as gemm_kernel
+// does; the eight decoded operands of a k-step are exchanged through LDS, so
+// each trellis value is decoded once per BM rows and reused by WM*8 MFMAs per
+// lane-set.  A (x~) goes from L2 straight into registers, one whole 128-k
+// stage ahead.  Same k slots, same k-step order, same parts and the same part
+// fold as gemm_kernel, so every output bit is the same.
+
+template <int WM>
+__device__ __forceinline__ void load_a_tall(half8_t (&a)[4][WM], const uint16_t *__restrict__ xs, int arow, int M,
+                                            int K, int k0, int g) {
+#pragma unroll
+  for (int mf = 0; mf < WM; ++mf) {
+    const int row = arow + 16 * mf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      half8_t v = {};
+      if (row < M) v = *(const half8_t *)(xs + (int64_t)row * K + k0 + 32 * ks + 8 * g);
+      a[ks][mf] = v;
+    }
+  }
+}
+
+template <int BITS, uint32_t CB, int WM, bool MULTI>
+__global__ __launch_bounds__(WG_THREADS, 1) void gemm_tall_kernel(const GemmParams p) {
+  using G = Geom<BITS>;
+  constexpr int BM = 64 * WM;
+  constexpr int BFRAG_DW = 256;           // one decoded B operand: 64 lanes x 16 bytes
+  constexpr int BBUF_DW = 8 * BFRAG_DW;   // the eight operands of one k-step
+  constexpr int ZW_DW = 16 * Z_ROW;       // one wave's 16-row slice of z
+  constexpr int MAIN_DW = 2 * G::STAGE_T_DW + 2 * BBUF_DW;
+  constexpr int LDS_DW = MAIN_DW > 4 * ZW_DW ? MAIN_DW : 4 * ZW_DW;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
+  uint32_t *const tbuf = lds;
+  uint32_t *const bbuf = lds + 2 * G::STAGE_T_DW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nb = blockIdx.x;
+  const int m0 = blockIdx.z * BM;
+  const int M = p.M, K = p.K, N = p.N;
+  const int NT = N >> 4;
+  const int KB = K >> 7;
+
+  int p_begin = 0, p_end = p.parts;
+  if (p.slab_mode) {
+    p_begin = blockIdx.y;
+    p_end = p_begin + 1;
+  }
+  const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
+  const int kb_end = (int)((int64_t)p_end * KB / p.parts);
+  const int nst = kb_end - kb_begin;
+
+  int shard = 0;
+  while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
+  const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
+  const int arow = m0 + wave * 16 * WM + j;
+
+  int xoff0, sh0, xoff1, sh1;
+  lane_window<BITS>(j, g, 0, xoff0, sh0);
+  lane_window<BITS>(j, g, 1, xoff1, sh1);
+  const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
+  uint32_t *const bdst0 = bbuf + (2 * wave + 0) * BFRAG_DW + 4 * lane;
+  uint32_t *const bdst1 = bbuf + (2 * wave + 1) * BFRAG_DW + 4 * lane;
+
+  u32x4_t treg[G::T_ITERS];
+  half8_t a0[4][WM], a1[4][WM];
+  float4_t acc[WM][8];
+  float4_t tot[MULTI ? WM : 1][MULTI ? 8 : 1];
+#pragma unroll
+  for (int mf = 0; mf < WM; ++mf)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[mf][f] = float4_t{0.f, 0.f, 0.f, 0.f};
+  int part = p_begin;
+  int part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+
+  // prologue: stages 0 and 1 in LDS, stage 2 in flight, A of stage 0, B of k-step 0
+  load_trellis_stage<BITS>(treg, p.trellis, kb_begin, nb, NT, tid);
+  load_a_tall<WM>(a0, xs, arow, M, K, kb_begin * 128, g);
+  store_trellis_stage<BITS>(treg, tbuf, tid);
+  if (nst > 1) {
+    load_trellis_stage<BITS>(treg, p.trellis, kb_begin + 1, nb, NT, tid);
+    store_trellis_stage<BITS>(treg, tbuf + G::STAGE_T_DW, tid);
+  }
+  if (nst > 2) load_trellis_stage<BITS>(treg, p.trellis, kb_begin + 2, nb, NT, tid);
+  __syncthreads();
+  {
+    const uint32_t *tp = tbuf + tile_lane * G::STRIDE;
+    *(half8_t *)bdst0 = decode_frag<BITS, CB>(tp, xoff0, sh0);
+    *(half8_t *)bdst1 = decode_frag<BITS, CB>(tp, xoff1, sh1);
+  }
+  __syncthreads();
+
+  auto run_stage = [&](int st, half8_t(&cur)[4][WM], half8_t(&nxt)[4][WM]) {
+    const int kb = kb_begin + st;
+    if (st + 1 < nst) load_a_tall<WM>(nxt, xs, arow, M, K, (kb + 1) * 128, g);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int i = 4 * st + ks;
+      const uint32_t *bsrc = bbuf + (i & 1) * BBUF_DW + 4 * lane;
+      half8_t b[8];
+#pragma unroll
+      for (int f = 0; f < 8; ++f) b[f] = *(const half8_t *)(bsrc + f * BFRAG_DW);
+      const uint32_t *tp = nullptr;
+      if (ks < 3) tp = tbuf + (st & 1) * G::STAGE_T_DW + (tile_lane + 2 * WG_NT * (ks + 1)) * G::STRIDE;
+      else if (st + 1 < nst) tp = tbuf + ((st + 1) & 1) * G::STAGE_T_DW + tile_lane * G::STRIDE;
+      if (tp != nullptr) {
+        const int o = ((i + 1) & 1) * BBUF_DW;
+        *(half8_t *)(bdst0 + o) = decode_frag<BITS, CB>(tp, xoff0, sh0);
+        *(half8_t *)(bdst1 + o) = decode_frag<BITS, CB>(tp, xoff1, sh1);
+      }
+#pragma unroll
+      for (int mf = 0; mf < WM; ++mf)
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+          acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[ks][mf], b[f], acc[mf][f], 0, 0, 0);
+      if constexpr (MULTI) {
+        if (ks == 3 && kb + 1 == part_end_kb) {
+#pragma unroll
+          for (int mf = 0; mf < WM; ++mf)
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+              if (part == p_begin) tot[mf][f] = acc[mf][f];
+              else tot[mf][f] = tot[mf][f] + acc[mf][f];
+              acc[mf][f] = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
+          ++part;
+          part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+        }
+      }
+      __syncthreads();
+    }
+    if (st + 2 < nst) {
+      store_trellis_stage<BITS>(treg, tbuf + (st & 1) * G::STAGE_T_DW, tid);
+      if (st + 3 < nst) load_trellis_stage<BITS>(treg, p.trellis, kb + 3, nb, NT, tid);
+    }
+  };
+
+  for (int st = 0;;) {
+    run_stage(st, a0, a1);
+    if (++st == nst) break;
+    run_stage(st, a1, a0);
+    if (++st == nst) break;
+  }
+
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int mf = 0; mf < WM; ++mf)
+#pragma unroll
+      for (int f = 0; f < 8; ++f) acc[mf][f] = tot[mf][f];
+  }
+
+  const int wrow = m0 + wave * 16 * WM;
+  if (p.slab_mode) {
+    float *__restrict__ sl = p.slabs + (int64_t)p_begin * M * N;
+#pragma unroll
+    for (int mf = 0; mf < WM; ++mf)
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        const int col = nb * 128 + lane_col(f >> 1, j, f & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wrow + 16 * mf + 4 * g + i;
+          if (row < M) sl[(int64_t)row * N + col] = acc[mf][f][i];
+        }
+      }
+    return;
+  }
+
+  float *z = reinterpret_cast<float *>(lds) + wave * ZW_DW;
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+#pragma unroll
+  for (int mf = 0; mf < WM; ++mf) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int col = lane_col(f >> 1, j, f & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[(4 * g + i) * Z_ROW + col] = acc[mf][f][i];
+    }
+    __syncthreads();
+    for (int r = 0; r < 16; ++r) {
+      const int row = wrow + 16 * mf + r;
+      if (row >= M) break;
+      const float z0 = z[r * Z_ROW + 2 * lane];
+      const float z1 = z[r * Z_ROW + 2 * lane + 1];
+      if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+      else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+    }
+    __syncthreads();
+  }
+}
+
 // Decode-only kernel for tests: the same staging and decode_frag as the GEMM,
 // storing each lane's 8 values at their (k, n) instead of multiplying.
 template <int BITS, uint32_t CB>
@@ -360,13 +553,16 @@ __global__ __launch_bounds__(WG_THREADS) void debug_decode_kernel(const DecodePa
     for (int h = 0; h < 2; ++h) {
       int xoff, sh;
       lane_window<BITS>(j, g, h, xoff, sh);
-      const half8_t b = decode_frag<BITS, CB>(tp, xoff, sh);
+      // Read the halves through a u32x4: extracting _Float16 elements of the
+      // half8 vector and bit-casting them one by one miscompiles (every
+      // element came out equal to element 0).
+      const u32x4_t b = __builtin_bit_cast(u32x4_t, decode_frag<BITS, CB>(tp, xoff, sh));
       const int n = nb * 128 + lane_col(wave, j, h);
       const int k0 = kb * 128 + 32 * ks + 16 * (g >> 1) + 4 * (g & 1);
       const int koff[8] = {0, 1, 2, 3, 8, 9, 10, 11};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        p.wq[(int64_t)(k0 + koff[e]) * p.N + n] = __builtin_bit_cast(uint16_t, b[e]);
+        p.wq[(int64_t)(k0 + koff[e]) * p.N + n] = (uint16_t)(b[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -380,22 +576,32 @@ hipError_t launch_gemm_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t
   return hipGetLastError();
 }
 
+template <int BITS, uint32_t CB, int WM>
+hipError_t launch_tall_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (multi) hipLaunchKernelGGL((gemm_tall_kernel<BITS, CB, WM, true>), grid, dim3(WG_THREADS), 0, s, p);
+  else hipLaunchKernelGGL((gemm_tall_kernel<BITS, CB, WM, false>), grid, dim3(WG_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128/256 -> gemm_tall_kernel.
 template <int BITS, uint32_t CB>
-hipError_t launch_gemm_cb(int mt, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  switch (mt) {
-    case 1: return launch_gemm_t<BITS, CB, 1>(multi, p, grid, s);
-    case 2: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
-    case 4: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
+hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  switch (bm) {
+    case 16: return launch_gemm_t<BITS, CB, 1>(multi, p, grid, s);
+    case 32: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
+    case 64: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
+    case 128: return launch_tall_t<BITS, CB, 2>(multi, p, grid, s);
+    case 256: return launch_tall_t<BITS, CB, 4>(multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int BITS>
-hipError_t launch_gemm_bits(int cb, int mt, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm_bits(int cb, int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   switch (cb) {
-    case 0: return launch_gemm_cb<BITS, CB_3INST>(mt, multi, p, grid, s);
-    case 1: return launch_gemm_cb<BITS, CB_MCG>(mt, multi, p, grid, s);
-    case 2: return launch_gemm_cb<BITS, CB_MUL1>(mt, multi, p, grid, s);
+    case 0: return launch_gemm_cb<BITS, CB_3INST>(bm, multi, p, grid, s);
+    case 1: return launch_gemm_cb<BITS, CB_MCG>(bm, multi, p, grid, s);
+    case 2: return launch_gemm_cb<BITS, CB_MUL1>(bm, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -416,9 +622,9 @@ hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
 
 #define EXL3_DEFINE_BITS(B)                                                                        \
   namespace exl3 {                                                                                 \
-  hipError_t launch_gemm_b##B(int cb, int mt, bool multi, const GemmParams &p, dim3 grid,          \
+  hipError_t launch_gemm_b##B(int cb, int bm, bool multi, const GemmParams &p, dim3 grid,          \
                               hipStream_t s) {                                                     \
-    return launch_gemm_bits<B>(cb, mt, multi, p, grid, s);                                         \
+    return launch_gemm_bits<B>(cb, bm, multi, p, grid, s);                                         \
   }                                                                                                \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s) {              \
     return launch_decode_bits<B>(cb, p, s);                                                        \

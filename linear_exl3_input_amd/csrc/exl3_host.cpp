@@ -107,10 +107,10 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
                   w->K / 128);
     pl.parts = force->parts;
   }
-  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
   if (force && force->bm > 0) {
-    if (force->bm != 16 && force->bm != 32 && force->bm != 64)
-      return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32 or 64", force->bm);
+    if (force->bm != 16 && force->bm != 32 && force->bm != 64 && force->bm != 128 && force->bm != 256)
+      return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32, 64, 128 or 256", force->bm);
     pl.bm = force->bm;
   }
   pl.mode = (pl.parts > 1 && M <= 64) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
@@ -241,11 +241,10 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     end += w->shard_n[s] / 128;
     p.shard_end_blk[s] = end;
   }
-  const int mt = pl.bm / 16;
   const dim3 grid((unsigned)(w->N / 128), (unsigned)(p.slab_mode ? pl.parts : 1),
                   (unsigned)((M + pl.bm - 1) / pl.bm));
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = exl3::launch_gemm(w->bits, w->codebook, mt, !p.slab_mode && pl.parts > 1, p, grid, s);
+  hipError_t e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, !p.slab_mode && pl.parts > 1, p, grid, s);
   if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
   if (p.slab_mode) {
     e = exl3::launch_epilogue(p.slabs, pl.parts, M, w->N, w->svh, y, p.out_bf16 != 0, s);

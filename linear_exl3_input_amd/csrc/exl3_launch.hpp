@@ -29,10 +29,11 @@ struct DecodeParams {
   int32_t K, N;
 };
 
-// Launchers (one per bit width; codebook and rows-per-tile are runtime
-// choices that select a template instance).  Return hipSuccess or the
+// Launchers (one per bit width; codebook and rows-per-tile bm are runtime
+// choices that select a template instance: bm 16/32/64 -> gemm_kernel,
+// 128/256 -> gemm_tall_kernel).  Return hipSuccess or the
 // launch error.
-hipError_t launch_gemm(int bits, int cb, int mt, bool multi_part, const GemmParams &p, dim3 grid,
+hipError_t launch_gemm(int bits, int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid,
                        hipStream_t s);
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s);
 
@@ -44,7 +45,7 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
 
 // Per-bit-width entry points, defined in gemm_b<bits>.hip.
 #define EXL3_DECLARE_BITS(B)                                                                  \
-  hipError_t launch_gemm_b##B(int cb, int mt, bool multi_part, const GemmParams &p, dim3 grid, \
+  hipError_t launch_gemm_b##B(int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid, \
                               hipStream_t s);                                                  \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);
 EXL3_DECLARE_BITS(1)

@@ -11,7 +11,9 @@ namespace exl3 {
 // 1).  One wave per (row, 128-block); x is read once and reused for every
 // shard's suh row (cuda-exl3 README, "One op per layer": all shards in one
 // launch, reading x once, with bf16 -> fp32 folded into the load).  x*suh is
-// exact in fp32, so the product may be contracted into an add freely.
+// exact in fp32, so the product may be contracted into an add freely.  The
+// output is stored in fragment order (frag_order_k), so that one MFMA lane's
+// eight A values are 16 contiguous bytes.
 template <bool X_BF16>
 __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ suh,
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
     float t1 = x1 * f16_bits_to_f32(sv >> 16);
     hadamard128_wave(t0, t1, lane);
     const uint32_t packed = f32_to_f16_bits(t0 * 0.0625f) | (f32_to_f16_bits(t1 * 0.0625f) << 16);
-    *(uint32_t *)(x_rot + ((int64_t)s * M + m) * K + k0) = packed;
+    *(uint32_t *)(x_rot + ((int64_t)s * M + m) * K + frag_order_k(k0)) = packed;
   }
 }
 
@@ -114,16 +116,16 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s) {
 
 // ------------------------------------------------------ bit-width dispatch
 
-hipError_t launch_gemm(int bits, int cb, int mt, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm(int bits, int cb, int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   switch (bits) {
-    case 1: return launch_gemm_b1(cb, mt, multi, p, grid, s);
-    case 2: return launch_gemm_b2(cb, mt, multi, p, grid, s);
-    case 3: return launch_gemm_b3(cb, mt, multi, p, grid, s);
-    case 4: return launch_gemm_b4(cb, mt, multi, p, grid, s);
-    case 5: return launch_gemm_b5(cb, mt, multi, p, grid, s);
-    case 6: return launch_gemm_b6(cb, mt, multi, p, grid, s);
-    case 7: return launch_gemm_b7(cb, mt, multi, p, grid, s);
-    case 8: return launch_gemm_b8(cb, mt, multi, p, grid, s);
+    case 1: return launch_gemm_b1(cb, bm, multi, p, grid, s);
+    case 2: return launch_gemm_b2(cb, bm, multi, p, grid, s);
+    case 3: return launch_gemm_b3(cb, bm, multi, p, grid, s);
+    case 4: return launch_gemm_b4(cb, bm, multi, p, grid, s);
+    case 5: return launch_gemm_b5(cb, bm, multi, p, grid, s);
+    case 6: return launch_gemm_b6(cb, bm, multi, p, grid, s);
+    case 7: return launch_gemm_b7(cb, bm, multi, p, grid, s);
+    case 8: return launch_gemm_b8(cb, bm, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

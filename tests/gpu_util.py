@@ -28,3 +28,12 @@ def x_dev(x_bits: np.ndarray, x_dtype: str = "bf16") -> torch.Tensor:
 
 def banner(msg: str) -> None:
     print(f"[gpu] {msg}", flush=True)
+
+
+def frag_order(x_rot_natural: np.ndarray) -> np.ndarray:
+    """The documented x_rot memory order: within each aligned group of 32 k
+    the 4-element chunks are stored as 0, 2, 1, 3, 4, 6, 5, 7."""
+    a = np.asarray(x_rot_natural)
+    lead, K = a.shape[:-1], a.shape[-1]
+    v = a.reshape(lead + (K // 32, 8, 4))
+    return v[..., [0, 2, 1, 3, 4, 6, 5, 7], :].reshape(lead + (K,))

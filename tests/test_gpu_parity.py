@@ -14,7 +14,7 @@ import workloads as wl
 from oracle import format as ofmt
 from oracle import linear as olin
 from oracle import transform as otf
-from gpu_util import banner, bits16, dev16, weight, x_dev
+from gpu_util import banner, bits16, dev16, frag_order, weight, x_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_input_transform_bit_exact(x_dtype, M, K, S):
     suh = (np.where(rng.integers(0, 2, (S, K)) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, (S, K)))
            ).astype(np.float16).view(np.uint16)
     got = bits16(ex.input_transform(x_dev(x, x_dtype), dev16(suh, torch.float16)))
-    want = otf.rotate_input(x, suh, x_dtype)
+    want = frag_order(otf.rotate_input(x, suh, x_dtype))
     assert got.shape == want.shape
     assert np.array_equal(got, want)
 
@@ -73,7 +73,7 @@ def test_input_transform_one_hot_closed_form():
     suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
     got = bits16(ex.input_transform(x_dev(x), dev16(suh, torch.float16)))[0]
     want = np.where(h.T > 0, 0x2C00, 0xAC00).astype(np.uint16)  # row j = signs of column j
-    assert np.array_equal(got, want)
+    assert np.array_equal(got, frag_order(want))
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
@@ -142,9 +142,9 @@ def test_linear_fp16_activations():
     _check(t, _run(t, x_dtype="f16"), x_dtype="f16")
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 33, 64, 65, 130])
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 33, 64, 65, 130, 257, 300])
 def test_linear_ragged_rows(M):
-    lay = wl.small_layer("ragged", 1024, (256,), 4, "3inst", (130,), seed=10)
+    lay = wl.small_layer("ragged", 1024, (256,), 4, "3inst", (300,), seed=10)
     t = wl.gen_all(lay)
     _check(t, _run(t, M=M), M=M)
 
@@ -156,7 +156,7 @@ def test_schedules_agree_bit_for_bit(parts):
     t = wl.gen_all(lay)
     outs = {}
     for mode in (ex.EXL3_MODE_FUSED, ex.EXL3_MODE_SLABS):
-        for bm in (16, 32, 64):
+        for bm in (16, 32, 64, 128, 256):
             outs[(mode, bm)] = _run(t, parts=parts, mode=mode, bm=bm)
     first = next(iter(outs.values()))
     for key, y in outs.items():
@@ -171,7 +171,7 @@ def test_row_alone_equals_row_in_batch():
     lay = wl.small_layer("inv", 2048, (512,), 4, "mcg", (96,), seed=12)
     t = wl.gen_all(lay)
     full = _run(t)
-    for M in (1, 2, 15, 16, 17, 40, 64, 65):
+    for M in (1, 2, 15, 16, 17, 40, 64, 65, 95):
         part = _run(t, M=M)
         assert np.array_equal(part, full[:M]), f"M={M}"
     # and a single row moved to another position of a batch
