@@ -74,17 +74,19 @@ exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_s
 
 // K parts: a function of (K, N, bits) only.  Enough (column block, part)
 // pairs to occupy the GPU at decode sizes (about 1024), parts of at least
-// two 128-k blocks, and the fp32 partial traffic at 16 rows kept under ~60%
-// of the trellis bytes (the cuda-exl3 README caps split-k accumulator
-// traffic at ~30% of the weight bytes and discounts it 2x when it stays in
-// cache, "Two further departures" and "Where the time goes").  P divides the
-// number of 128-k blocks so every part has the same length.
+// two 128-k blocks, and the fp32 partial traffic at 16 rows kept near the
+// trellis bytes it helps to stream (the cuda-exl3 README caps split-k
+// accumulator traffic at ~30% of the weight bytes and discounts it when it
+// stays in cache, "Two further departures" and "Where the time goes"; on
+// this GPU the partials of a decode-size call stay in the 256 MB cache, so
+// the cap is looser).  P divides the number of 128-k blocks so every part has
+// the same length.
 int32_t choose_parts(int32_t K, int32_t N, int32_t bits) {
   const int32_t kb = K / 128;
   const int32_t nblk = N / 128;
   int32_t want = (1024 + nblk - 1) / nblk;
   const int32_t cap_len = std::max(1, kb / 2);
-  const int32_t cap_traffic = std::max(1, (int32_t)(0.6 * (double)K * bits / 1024.0));
+  const int32_t cap_traffic = std::max(1, (int32_t)(1.2 * (double)K * bits / 1024.0));
   int32_t pmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
   for (int32_t p = pmax; p >= 1; --p)
     if (kb % p == 0) return p;
@@ -107,13 +109,17 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
                   w->K / 128);
     pl.parts = force->parts;
   }
-  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
+  // Rows per tile: the measured best of the tile shapes at each M.
+  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
   if (force && force->bm > 0) {
     if (force->bm != 16 && force->bm != 32 && force->bm != 64 && force->bm != 128 && force->bm != 256)
       return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32, 64, 128 or 256", force->bm);
     pl.bm = force->bm;
   }
-  pl.mode = (pl.parts > 1 && M <= 64) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
+  // Separate fp32 partials while they are small enough to stay in cache;
+  // beyond that one workgroup runs all parts of its tile.
+  const double slab_bytes = (double)pl.parts * (double)M * (double)w->N * 4.0;
+  pl.mode = (pl.parts > 1 && slab_bytes <= 64.0 * 1024 * 1024) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
   if (force && force->mode != EXL3_MODE_AUTO && force->mode >= 0) {
     if (force->mode != EXL3_MODE_FUSED && force->mode != EXL3_MODE_SLABS)
       return fail(EXL3_ERR_INVALID_ARG, "forced mode=%d, must be 0 (fused) or 1 (slabs)", force->mode);

@@ -122,9 +122,10 @@ def test_parts_depend_on_shape_only():
 
 def test_plan_modes_and_workspace():
     w = view(17408, (5120,), 6, 2)
-    small, big = _plan(w, 16), _plan(w, 512)
+    small, big = _plan(w, 16), _plan(w, 4096)
     assert small.parts == big.parts > 1
     assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == small.parts * 16 * 5120 * 4
     assert big.mode == ex.EXL3_MODE_FUSED and big.workspace == 0
+    assert small.bm == 16 and _plan(w, 24).bm == 32 and big.bm == 64
     head = view(4096, (154880,), 6, 2)
     assert _plan(head, 1).parts == 1 and _plan(head, 1).workspace == 0
