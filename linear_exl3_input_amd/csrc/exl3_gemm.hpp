@@ -38,6 +38,8 @@
 // running sum in registers.  Both give the same bits for every row.
 #pragma once
 
+#include <type_traits>
+
 #include "exl3_device.hpp"
 #include "exl3_launch.hpp"
 
@@ -57,6 +59,7 @@ struct Geom {
   static constexpr int ROW_CHUNKS = WG_NT * TILE_CHUNKS;
   static constexpr int STAGE_CHUNKS = STAGE_KT * ROW_CHUNKS;
   static constexpr int T_ITERS = (STAGE_CHUNKS + WG_THREADS - 1) / WG_THREADS;
+  static constexpr int T_MIN = STAGE_CHUNKS / WG_THREADS;  // loads every wave issues per stage
   static constexpr int STAGE_T_DW = STAGE_KT * WG_NT * STRIDE;
   // dwords a lane needs: 16 + 11*bits stream bits after a start offset in [1, 32]
   static constexpr int NY = (11 * BITS + 16 + 31) / 32;
@@ -166,6 +169,38 @@ __device__ __forceinline__ half8_t decode_frag(const uint32_t *__restrict__ tp, 
   const u32x4_t r = {decode_pair<CB>(s0, s1), decode_pair<CB>(s2, s3), decode_pair<CB>(s4, s5),
                      decode_pair<CB>(s6, s7)};
   return __builtin_bit_cast(half8_t, r);
+}
+
+// decode_frag in pieces, so that a caller can spread the work between
+// matrix-core instructions: load the lane's dwords, normalize them, then
+// produce one packed pair of values (k = 0..3) at a time.
+template <int BITS>
+__device__ __forceinline__ void frag_load(const uint32_t *__restrict__ tp, int xoff, uint32_t (&X)[Geom<BITS>::NX]) {
+#pragma unroll
+  for (int i = 0; i < Geom<BITS>::NX; ++i) X[i] = tp[xoff + i];
+}
+
+template <int BITS>
+__device__ __forceinline__ void frag_normalize(const uint32_t (&X)[Geom<BITS>::NX], int sh,
+                                               uint32_t (&Y)[Geom<BITS>::NY]) {
+#pragma unroll
+  for (int i = 0; i < Geom<BITS>::NY; ++i) Y[i] = __builtin_amdgcn_alignbit(X[i], X[i + 1], sh);
+}
+
+template <int BITS, uint32_t CB, int K>
+__device__ __forceinline__ uint32_t frag_pair(const uint32_t (&Y)[Geom<BITS>::NY]) {
+  // slot order of the lane's states: v0, v0+1, v0+8, v0+9, v0+2, v0+3, v0+10, v0+11
+  constexpr int D0 = (K == 0 ? 0 : K == 1 ? 8 : K == 2 ? 2 : 10) * BITS;
+  constexpr int D1 = D0 + BITS;
+  return decode_pair<CB>(window16<D0, Geom<BITS>::NY>(Y), window16<D1, Geom<BITS>::NY>(Y));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // Per-lane constants of decode_frag for column half h.
@@ -336,44 +371,58 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
   }
 }
 
-// ------------------------------------------------------------- tall GEMM
+// -------------------------------------------------------------- big GEMM
 //
-// For larger M: a BM = 64*WM row x 128 column tile on 4 waves, wave w owning
-// rows [16*WM*w, 16*WM*(w+1)) of the tile against all 128 columns.  Wave w
-// still decodes the B operands of n-tiles 2w and 2w+1, exactly as gemm_kernel
-// does; the eight decoded operands of a k-step are exchanged through LDS, so
-// each trellis value is decoded once per BM rows and reused by WM*8 MFMAs per
-// lane-set.  A (x~) goes from L2 straight into registers, one whole 128-k
-// stage ahead.  Same k slots, same k-step order, same parts and the same part
-// fold as gemm_kernel, so every output bit is the same.
+// For larger M: a BM = 16*MT row x 128 column tile (MT = 8 or 16) on 4 waves.
+// As in gemm_kernel, wave w decodes the B operands of n-tiles 2w and 2w+1 and
+// keeps them in registers, now against all BM rows, so each trellis value is
+// decoded once per BM rows and feeds 2*MT MFMAs per lane-set.  The rotated
+// activations go HBM/L2 -> LDS by direct loads (global_load_lds_dwordx4, no
+// registers involved) into a ring of k-step slots, PF k-steps ahead; each
+// 16-row fragment occupies 1 KB in exactly the lane order of the MFMA A
+// operand (x~ is in fragment order), so reading it is one conflict-free
+// ds_read_b128 per lane.  The decode of k-step i+1 is interleaved with the
+// MFMAs of k-step i.  Rows past M load row M-1 (finite, discarded).  Same
+// k slots, k-step order, parts and part fold as gemm_kernel: same bits.
 
-template <int WM>
-__device__ __forceinline__ void load_a_tall(half8_t (&a)[4][WM], const uint16_t *__restrict__ xs, int arow, int M,
-                                            int K, int k0, int g) {
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int MT>
+__device__ __forceinline__ void issue_a_dma(uint32_t *__restrict__ slot, const uint16_t *__restrict__ xs, int m0,
+                                            int M, int K, int k, int wave, int lane) {
+  // wave w loads fragments w, w+4, ... of this k-step; lane L of a fragment
+  // holds row (L & 15) and k-chunk (L >> 4)
 #pragma unroll
-  for (int mf = 0; mf < WM; ++mf) {
-    const int row = arow + 16 * mf;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      half8_t v = {};
-      if (row < M) v = *(const half8_t *)(xs + (int64_t)row * K + k0 + 32 * ks + 8 * g);
-      a[ks][mf] = v;
-    }
+  for (int t = 0; t < MT / 4; ++t) {
+    const int mf = wave + 4 * t;
+    int row = m0 + 16 * mf + (lane & 15);
+    row = row < M ? row : M - 1;
+    const uint16_t *src = xs + (int64_t)row * K + k + 8 * (lane >> 4);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)(slot + mf * 256), 16, 0, 0);
   }
 }
 
-template <int BITS, uint32_t CB, int WM, bool MULTI>
-__global__ __launch_bounds__(WG_THREADS, 1) void gemm_tall_kernel(const GemmParams p) {
+template <int BITS, uint32_t CB, int MT, bool MULTI>
+__global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParams p) {
   using G = Geom<BITS>;
-  constexpr int BM = 64 * WM;
-  constexpr int BFRAG_DW = 256;           // one decoded B operand: 64 lanes x 16 bytes
-  constexpr int BBUF_DW = 8 * BFRAG_DW;   // the eight operands of one k-step
-  constexpr int ZW_DW = 16 * Z_ROW;       // one wave's 16-row slice of z
-  constexpr int MAIN_DW = 2 * G::STAGE_T_DW + 2 * BBUF_DW;
-  constexpr int LDS_DW = MAIN_DW > 4 * ZW_DW ? MAIN_DW : 4 * ZW_DW;
+  constexpr int BM = 16 * MT;
+  constexpr int PF = 2;                 // A prefetch distance (k-steps)
+  constexpr int NSLOT = 4;              // ring slots; a slot is rewritten 2 steps after its last read
+  constexpr int ASLOT_DW = MT * 256;    // MT fragments x 64 lanes x 16 bytes
+  constexpr int A_DW = NSLOT * ASLOT_DW;
+  constexpr int MAIN_DW = A_DW + 2 * G::STAGE_T_DW;
+  constexpr int ZROWS = 64;             // output stage: 64 rows per pass
+  constexpr int Z_DW = ZROWS * Z_ROW;
+  constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
+  constexpr int DMA_PER_STEP = MT / 4;  // direct loads per wave per k-step
   __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
-  uint32_t *const tbuf = lds;
-  uint32_t *const bbuf = lds + 2 * G::STAGE_T_DW;
+  uint32_t *const abuf = lds;
+  uint32_t *const tbuf = lds + A_DW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,143 +443,174 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_tall_kernel(const GemmPara
   const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
   const int kb_end = (int)((int64_t)p_end * KB / p.parts);
   const int nst = kb_end - kb_begin;
+  const int nks = 4 * nst;
+  const int k_begin = kb_begin * 128;
 
   int shard = 0;
   while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
   const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
-  const int arow = m0 + wave * 16 * WM + j;
 
   int xoff0, sh0, xoff1, sh1;
   lane_window<BITS>(j, g, 0, xoff0, sh0);
   lane_window<BITS>(j, g, 1, xoff1, sh1);
   const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
-  uint32_t *const bdst0 = bbuf + (2 * wave + 0) * BFRAG_DW + 4 * lane;
-  uint32_t *const bdst1 = bbuf + (2 * wave + 1) * BFRAG_DW + 4 * lane;
 
   u32x4_t treg[G::T_ITERS];
-  half8_t a0[4][WM], a1[4][WM];
-  float4_t acc[WM][8];
-  float4_t tot[MULTI ? WM : 1][MULTI ? 8 : 1];
+  float4_t acc[MT][2];
+  float4_t tot[MULTI ? MT : 1][2];
 #pragma unroll
-  for (int mf = 0; mf < WM; ++mf)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int f = 0; f < 8; ++f) acc[mf][f] = float4_t{0.f, 0.f, 0.f, 0.f};
-  int part = p_begin;
-  int part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
-
-  // prologue: stages 0 and 1 in LDS, stage 2 in flight, A of stage 0, B of k-step 0
+    for (int h = 0; h < 2; ++h) acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // prologue: A for the first PF k-steps, trellis stage 0 in LDS, stage 1 in
+  // registers.  Prefetch indices past the end are clamped to the last stage or
+  // k-step, so the loop below has no branches (the extra loads are in bounds
+  // and their results unused).
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    issue_a_dma<MT>(abuf + i * ASLOT_DW, xs, m0, M, K, k_begin + 32 * min(i, nks - 1), wave, lane);
   load_trellis_stage<BITS>(treg, p.trellis, kb_begin, nb, NT, tid);
-  load_a_tall<WM>(a0, xs, arow, M, K, kb_begin * 128, g);
   store_trellis_stage<BITS>(treg, tbuf, tid);
-  if (nst > 1) {
-    load_trellis_stage<BITS>(treg, p.trellis, kb_begin + 1, nb, NT, tid);
-    store_trellis_stage<BITS>(treg, tbuf + G::STAGE_T_DW, tid);
-  }
-  if (nst > 2) load_trellis_stage<BITS>(treg, p.trellis, kb_begin + 2, nb, NT, tid);
+  load_trellis_stage<BITS>(treg, p.trellis, kb_begin + min(1, nst - 1), nb, NT, tid);
   __syncthreads();
-  {
-    const uint32_t *tp = tbuf + tile_lane * G::STRIDE;
-    *(half8_t *)bdst0 = decode_frag<BITS, CB>(tp, xoff0, sh0);
-    *(half8_t *)bdst1 = decode_frag<BITS, CB>(tp, xoff1, sh1);
-  }
-  __syncthreads();
+  half8_t b0 = decode_frag<BITS, CB>(tbuf + tile_lane * G::STRIDE, xoff0, sh0);
+  half8_t b1 = decode_frag<BITS, CB>(tbuf + tile_lane * G::STRIDE, xoff1, sh1);
 
-  auto run_stage = [&](int st, half8_t(&cur)[4][WM], half8_t(&nxt)[4][WM]) {
-    const int kb = kb_begin + st;
-    if (st + 1 < nst) load_a_tall<WM>(nxt, xs, arow, M, K, (kb + 1) * 128, g);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int i = 4 * st + ks;
-      const uint32_t *bsrc = bbuf + (i & 1) * BBUF_DW + 4 * lane;
-      half8_t b[8];
-#pragma unroll
-      for (int f = 0; f < 8; ++f) b[f] = *(const half8_t *)(bsrc + f * BFRAG_DW);
-      const uint32_t *tp = nullptr;
-      if (ks < 3) tp = tbuf + (st & 1) * G::STAGE_T_DW + (tile_lane + 2 * WG_NT * (ks + 1)) * G::STRIDE;
-      else if (st + 1 < nst) tp = tbuf + ((st + 1) & 1) * G::STAGE_T_DW + tile_lane * G::STRIDE;
-      if (tp != nullptr) {
-        const int o = ((i + 1) & 1) * BBUF_DW;
-        *(half8_t *)(bdst0 + o) = decode_frag<BITS, CB>(tp, xoff0, sh0);
-        *(half8_t *)(bdst1 + o) = decode_frag<BITS, CB>(tp, xoff1, sh1);
-      }
-#pragma unroll
-      for (int mf = 0; mf < WM; ++mf)
-#pragma unroll
-        for (int f = 0; f < 8; ++f)
-          acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[ks][mf], b[f], acc[mf][f], 0, 0, 0);
-      if constexpr (MULTI) {
-        if (ks == 3 && kb + 1 == part_end_kb) {
-#pragma unroll
-          for (int mf = 0; mf < WM; ++mf)
-#pragma unroll
-            for (int f = 0; f < 8; ++f) {
-              if (part == p_begin) tot[mf][f] = acc[mf][f];
-              else tot[mf][f] = tot[mf][f] + acc[mf][f];
-              acc[mf][f] = float4_t{0.f, 0.f, 0.f, 0.f};
-            }
-          ++part;
-          part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+  int st = 0;
+  auto run_stages = [&](int st_end) {
+    for (; st < st_end; ++st) {
+      // stage st is in tbuf[st & 1]; store stage st+1 and start loading st+2
+      uint32_t *const tcur = tbuf + (st & 1) * G::STAGE_T_DW;
+      uint32_t *const tnxt = tbuf + ((st + 1) & 1) * G::STAGE_T_DW;
+      store_trellis_stage<BITS>(treg, tnxt, tid);
+      auto kstep = [&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        const int i = 4 * st + ks;
+        issue_a_dma<MT>(abuf + ((i + PF) % NSLOT) * ASLOT_DW, xs, m0, M, K, k_begin + 32 * min(i + PF, nks - 1),
+                        wave, lane);
+        asm volatile("" ::: "memory");  // keep the issue order the counts below assume
+        // Vector-memory ops complete in issue order.  This wave's direct loads
+        // for k-step i are done once no more than the ops issued after them
+        // are outstanding: the PF later groups, plus the trellis loads issued
+        // after k-step 0 of this stage while they are younger than group i.
+        if constexpr (ks == 1 || ks == 2) wait_vmcnt<PF * DMA_PER_STEP + G::T_MIN>();
+        else wait_vmcnt<PF * DMA_PER_STEP>();
+        __syncthreads();  // the other waves' loads for k-step i, and the stores above
+        if constexpr (ks == 0) {
+          load_trellis_stage<BITS>(treg, p.trellis, kb_begin + min(st + 2, nst - 1), nb, NT, tid);
+          asm volatile("" ::: "memory");
         }
-      }
-      __syncthreads();
-    }
-    if (st + 2 < nst) {
-      store_trellis_stage<BITS>(treg, tbuf + (st & 1) * G::STAGE_T_DW, tid);
-      if (st + 3 < nst) load_trellis_stage<BITS>(treg, p.trellis, kb + 3, nb, NT, tid);
+        // The next k-step's B operands are decoded in 10 pieces (2 normalize,
+        // 8 pairs) spread between this step's MFMA pairs; sched_barrier keeps
+        // the interleaving, so the VALU work issues while the matrix core is
+        // busy instead of before it.
+        const uint32_t *tp = ks < 3 ? tcur + (tile_lane + 2 * WG_NT * (ks + 1)) * G::STRIDE
+                                    : tnxt + tile_lane * G::STRIDE;
+        uint32_t X0[G::NX], X1[G::NX], Y0[G::NY], Y1[G::NY];
+        u32x4_t nb0, nb1;
+        frag_load<BITS>(tp, xoff0, X0);
+        frag_load<BITS>(tp, xoff1, X1);
+        const uint32_t *as = abuf + (i % NSLOT) * ASLOT_DW + 4 * lane;
+        half8_t a[3];
+        a[0] = *(const half8_t *)(as);
+        a[1] = *(const half8_t *)(as + 256);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, MT>([&](auto mt_c) {
+          constexpr int mt = decltype(mt_c)::value;
+          acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt % 3], b0, acc[mt][0], 0, 0, 0);
+          acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt % 3], b1, acc[mt][1], 0, 0, 0);
+          if constexpr (mt + 2 < MT) a[(mt + 2) % 3] = *(const half8_t *)(as + (mt + 2) * 256);
+          static_for<mt * 10 / MT, (mt + 1) * 10 / MT>([&](auto pc) {
+            constexpr int piece = decltype(pc)::value;
+            if constexpr (piece == 0) frag_normalize<BITS>(X0, sh0, Y0);
+            else if constexpr (piece < 5) nb0[piece - 1] = frag_pair<BITS, CB, piece - 1>(Y0);
+            else if constexpr (piece == 5) frag_normalize<BITS>(X1, sh1, Y1);
+            else nb1[piece - 6] = frag_pair<BITS, CB, piece - 6>(Y1);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        const half8_t n0 = __builtin_bit_cast(half8_t, nb0);
+        const half8_t n1 = __builtin_bit_cast(half8_t, nb1);
+        b0 = n0;
+        b1 = n1;
+      };
+      kstep(std::integral_constant<int, 0>{});
+      kstep(std::integral_constant<int, 1>{});
+      kstep(std::integral_constant<int, 2>{});
+      kstep(std::integral_constant<int, 3>{});
     }
   };
 
-  for (int st = 0;;) {
-    run_stage(st, a0, a1);
-    if (++st == nst) break;
-    run_stage(st, a1, a0);
-    if (++st == nst) break;
-  }
-
   if constexpr (MULTI) {
+    // first part copied, later parts added in part order
+    run_stages((int)((int64_t)(p_begin + 1) * KB / p.parts) - kb_begin);
 #pragma unroll
-    for (int mf = 0; mf < WM; ++mf)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int f = 0; f < 8; ++f) acc[mf][f] = tot[mf][f];
+      for (int h = 0; h < 2; ++h) {
+        tot[mt][h] = acc[mt][h];
+        acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    for (int part = p_begin + 1; part < p_end; ++part) {
+      run_stages((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          tot[mt][h] = tot[mt][h] + acc[mt][h];
+          acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[mt][h] = tot[mt][h];
+  } else {
+    run_stages(nst);
   }
+  wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
 
-  const int wrow = m0 + wave * 16 * WM;
   if (p.slab_mode) {
     float *__restrict__ sl = p.slabs + (int64_t)p_begin * M * N;
 #pragma unroll
-    for (int mf = 0; mf < WM; ++mf)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int col = nb * 128 + lane_col(f >> 1, j, f & 1);
+      for (int h = 0; h < 2; ++h) {
+        const int col = nb * 128 + lane_col(wave, j, h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = wrow + 16 * mf + 4 * g + i;
-          if (row < M) sl[(int64_t)row * N + col] = acc[mf][f][i];
+          const int row = m0 + mt * 16 + 4 * g + i;
+          if (row < M) sl[(int64_t)row * N + col] = acc[mt][h][i];
         }
       }
     return;
   }
 
-  float *z = reinterpret_cast<float *>(lds) + wave * ZW_DW;
+  // output transform, 64 rows at a time through LDS
+  float *z = reinterpret_cast<float *>(lds);
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
 #pragma unroll
-  for (int mf = 0; mf < WM; ++mf) {
+  for (int pass = 0; pass < MT / 4; ++pass) {
+    __syncthreads();
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int col = lane_col(f >> 1, j, f & 1);
+    for (int q = 0; q < 4; ++q) {
+      const int mt = 4 * pass + q;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[(4 * g + i) * Z_ROW + col] = acc[mf][f][i];
+      for (int h = 0; h < 2; ++h) {
+        const int col = lane_col(wave, j, h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[(q * 16 + 4 * g + i) * Z_ROW + col] = acc[mt][h][i];
+      }
     }
     __syncthreads();
-    for (int r = 0; r < 16; ++r) {
-      const int row = wrow + 16 * mf + r;
+    for (int r = wave; r < ZROWS; r += 4) {
+      const int row = m0 + pass * ZROWS + r;
       if (row >= M) break;
       const float z0 = z[r * Z_ROW + 2 * lane];
       const float z1 = z[r * Z_ROW + 2 * lane + 1];
       if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
       else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
     }
-    __syncthreads();
   }
 }
 
@@ -576,22 +656,22 @@ hipError_t launch_gemm_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t
   return hipGetLastError();
 }
 
-template <int BITS, uint32_t CB, int WM>
-hipError_t launch_tall_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (multi) hipLaunchKernelGGL((gemm_tall_kernel<BITS, CB, WM, true>), grid, dim3(WG_THREADS), 0, s, p);
-  else hipLaunchKernelGGL((gemm_tall_kernel<BITS, CB, WM, false>), grid, dim3(WG_THREADS), 0, s, p);
+template <int BITS, uint32_t CB, int MT>
+hipError_t launch_big_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (multi) hipLaunchKernelGGL((gemm_big_kernel<BITS, CB, MT, true>), grid, dim3(WG_THREADS), 0, s, p);
+  else hipLaunchKernelGGL((gemm_big_kernel<BITS, CB, MT, false>), grid, dim3(WG_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
-// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128/256 -> gemm_tall_kernel.
+// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128/256 -> gemm_big_kernel.
 template <int BITS, uint32_t CB>
 hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   switch (bm) {
     case 16: return launch_gemm_t<BITS, CB, 1>(multi, p, grid, s);
     case 32: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
     case 64: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
-    case 128: return launch_tall_t<BITS, CB, 2>(multi, p, grid, s);
-    case 256: return launch_tall_t<BITS, CB, 4>(multi, p, grid, s);
+    case 128: return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
+    case 256: return launch_big_t<BITS, CB, 16>(multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

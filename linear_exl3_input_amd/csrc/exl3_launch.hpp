@@ -31,7 +31,7 @@ struct DecodeParams {
 
 // Launchers (one per bit width; codebook and rows-per-tile bm are runtime
 // choices that select a template instance: bm 16/32/64 -> gemm_kernel,
-// 128/256 -> gemm_tall_kernel).  Return hipSuccess or the
+// 128/256 -> gemm_big_kernel).  Return hipSuccess or the
 // launch error.
 hipError_t launch_gemm(int bits, int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid,
                        hipStream_t s);
