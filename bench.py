@@ -156,7 +156,7 @@ def main():
         suh, svh = d16(t.suh, torch.float16), d16(t.svh, torch.float16)
         ws = [ex.Exl3Weight(p, suh, svh, lay.bits, lay.codebook, lay.shards) for p in pool]
         x = d16(t.x, torch.bfloat16)
-        xr = {M: torch.empty((lay.n_shards, M, lay.K), dtype=torch.float16, device=dev) for M in Ms}
+        xr = {M: torch.empty(ex.rot_shape(lay.n_shards, M, lay.K), dtype=torch.float16, device=dev) for M in Ms}
         y = {M: torch.empty((M, lay.N), dtype=torch.bfloat16, device=dev) for M in Ms}
         per_layer.append((lay, ws, x, xr, y))
     # workspace for the largest need, allocated before capture

@@ -106,11 +106,15 @@ typedef struct exl3_plan {
  * butterfly strides 1, 2, ..., 64 in ascending order; x*suh is exact.
  *   x      [M][K] bf16 or fp16 bits (x_dtype)
  *   suh    [n_shards][K] fp16 bits
- *   x_rot  [n_shards][M][K] fp16 bits (output, written completely), in
- *          FRAGMENT ORDER: within every aligned group of 32 k the eight
- *          4-element chunks are stored in the order 0, 2, 1, 3, 4, 6, 5, 7,
- *          so that the 8 values one matrix-core lane multiplies are 16
- *          contiguous bytes.  Only the memory order differs from the formula.
+ *   x_rot  fp16 bits (output, written completely), n_shards * M * K values
+ *          in K-STEP TILES: x_rot[s][k/32][m][pos(k%32)], i.e. for every
+ *          shard the K/32 groups of 32 k are stored one after another, each
+ *          holding all M rows (64 bytes per row), so the 32-k slice of any
+ *          run of rows is one contiguous block.  Within a row's 32 values the
+ *          eight 4-element chunks are stored in the order 0, 2, 1, 3, 4, 6,
+ *          5, 7 (pos), so the 8 values one matrix-core lane multiplies are 16
+ *          contiguous bytes.  Only the memory order differs from the formula;
+ *          for M == 1 it is the row itself, chunk-permuted.
  * Errors: EXL3_ERR_INVALID_ARG for K % 128 != 0, M < 0, n_shards out of
  * range, a null or misaligned pointer, or an unknown dtype. */
 exl3_status exl3_input_transform(const void *x, int32_t x_dtype, int32_t M, int32_t K,
@@ -128,7 +132,7 @@ size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M);
  *             in P shape-fixed K parts, summed in part order)
  *   y[m][n] = rne_out( svh[n] * 2^-3 * H128(z[m][:])[n] )  per 128-col block
  * where s(n) is the shard holding absolute column n.
- *   x_rot     [n_shards][M][K] fp16 bits in fragment order, as written by
+ *   x_rot     n_shards * M * K fp16 bits in the k-step tile order written by
  *             exl3_input_transform
  *   y         [M][N] in y_dtype (output, written completely)
  *   workspace at least exl3_workspace_bytes(w, M) bytes (may be NULL if 0);

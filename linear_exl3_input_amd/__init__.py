@@ -209,8 +209,15 @@ def plan(w: Exl3Weight, M: int) -> dict:
     return {"parts": p.parts, "mode": p.mode, "bm": p.bm, "workspace": p.workspace}
 
 
+def rot_shape(n_shards: int, M: int, K: int) -> tuple:
+    """Shape of the rotated activations: n_shards x K/32 k-step tiles of M rows
+    x 32 values (the row's 32 values in fragment order)."""
+    return (n_shards, K // 32, M, 32)
+
+
 def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """had(x*suh) for every shard: x [M, K] bf16/fp16 -> x_rot [S, M, K] fp16."""
+    """had(x*suh) for every shard: x [M, K] bf16/fp16 -> x_rot fp16 of shape
+    [S, K/32, M, 32] (the k-step tile order the GEMM reads; see rot_shape)."""
     if suh.dim() == 1:
         suh = suh.unsqueeze(0)
     M, K = x.shape
@@ -220,7 +227,9 @@ def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tens
     if x.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError(f"x dtype {x.dtype} is not bf16/fp16")
     if out is None:
-        out = torch.empty((S, M, K), dtype=torch.float16, device=x.device)
+        out = torch.empty(rot_shape(S, M, K), dtype=torch.float16, device=x.device)
+    elif tuple(out.shape) != rot_shape(S, M, K):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {rot_shape(S, M, K)}")
     L = load()
     _check(L.exl3_input_transform(_dev_ptr(x, "x", (torch.bfloat16, torch.float16)),
                                   _BF16 if x.dtype == torch.bfloat16 else _F16, M, K,
@@ -231,9 +240,12 @@ def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tens
 def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
            out: Optional[torch.Tensor] = None, parts=None, mode=None, bm=None) -> torch.Tensor:
     """z = x_rot . W_q per shard, then the output transform: -> y [M, N]."""
-    S, M, K = x_rot.shape
-    if S != w.n_shards or K != w.K:
-        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} does not match the weight ({w.n_shards}, M, {w.K})")
+    if x_rot.dim() != 4 or x_rot.shape[3] != 32:
+        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
+    S, KC, M, _ = x_rot.shape
+    if S != w.n_shards or 32 * KC != w.K:
+        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} does not match the weight "
+                         f"{rot_shape(w.n_shards, M, w.K)}")
     if out_dtype not in (torch.bfloat16, torch.float16):
         raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
     if out is None:

@@ -122,7 +122,8 @@ __device__ __forceinline__ void load_a_stage(u32x4_t (&areg)[MT], const uint16_t
     const int q = c & 15;
     const int m = m0 + row;
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if (m < M) v = *(const u32x4_t *)(xs + (int64_t)m * K + kb * 128 + q * 8);
+    // x~ is in k-step tiles: k-step 4kb + q/4 of row m, 16-byte chunk q%4
+    if (m < M) v = *(const u32x4_t *)(xs + ((int64_t)(4 * kb + (q >> 2)) * M + m) * 32 + (q & 3) * 8);
     areg[it] = v;
   }
 }
@@ -385,6 +386,20 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 // MFMAs of k-step i.  Rows past M load row M-1 (finite, discarded).  Same
 // k slots, k-step order, parts and part fold as gemm_kernel: same bits.
 
+// Workgroup barrier that waits only for this wave's LDS operations.
+// __syncthreads() also drains every outstanding global load (the release
+// fence of the memory model), which would cancel the direct-to-LDS prefetch
+// that is meant to stay in flight across barriers; completion of those loads
+// is tracked explicitly with wait_vmcnt.
+// The wait is the builtin (s_waitcnt lgkmcnt(0), encoding 0xC07F) so the
+// compiler's own wait insertion knows LDS results are in after it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -401,7 +416,7 @@ __device__ __forceinline__ void issue_a_dma(uint32_t *__restrict__ slot, const u
     const int mf = wave + 4 * t;
     int row = m0 + 16 * mf + (lane & 15);
     row = row < M ? row : M - 1;
-    const uint16_t *src = xs + (int64_t)row * K + k + 8 * (lane >> 4);
+    const uint16_t *src = xs + ((int64_t)(k >> 5) * M + row) * 32 + 8 * (lane >> 4);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                      (__attribute__((address_space(3))) void *)(slot + mf * 256), 16, 0, 0);
   }
@@ -495,7 +510,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
         // after k-step 0 of this stage while they are younger than group i.
         if constexpr (ks == 1 || ks == 2) wait_vmcnt<PF * DMA_PER_STEP + G::T_MIN>();
         else wait_vmcnt<PF * DMA_PER_STEP>();
-        __syncthreads();  // the other waves' loads for k-step i, and the stores above
+        barrier_lds();  // the other waves' loads for k-step i, and the stores above
         if constexpr (ks == 0) {
           load_trellis_stage<BITS>(treg, p.trellis, kb_begin + min(st + 2, nst - 1), nb, NT, tid);
           asm volatile("" ::: "memory");
@@ -663,7 +678,11 @@ hipError_t launch_big_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t 
   return hipGetLastError();
 }
 
-// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128/256 -> gemm_big_kernel.
+template <int BITS, uint32_t CB>
+hipError_t launch_wide_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
+
+// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128 -> gemm_big_kernel,
+// 256 -> gemm_wide_kernel (512 threads).
 template <int BITS, uint32_t CB>
 hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   switch (bm) {
@@ -671,7 +690,7 @@ hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hi
     case 32: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
     case 64: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
     case 128: return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
-    case 256: return launch_big_t<BITS, CB, 16>(multi, p, grid, s);
+    case 256: return launch_wide_t<BITS, CB>(multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,8 +12,10 @@ namespace exl3 {
 // shard's suh row (cuda-exl3 README, "One op per layer": all shards in one
 // launch, reading x once, with bf16 -> fp32 folded into the load).  x*suh is
 // exact in fp32, so the product may be contracted into an add freely.  The
-// output is stored in fragment order (frag_order_k), so that one MFMA lane's
-// eight A values are 16 contiguous bytes.
+// output is stored in k-step tiles, x~[s][k/32][m][32], with the 32 values of
+// a row in fragment order (frag_order_k), so that one MFMA lane's eight A
+// values are 16 contiguous bytes and one k-step of a run of rows is one
+// contiguous block.
 template <bool X_BF16>
 __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ suh,
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
     float t1 = x1 * f16_bits_to_f32(sv >> 16);
     hadamard128_wave(t0, t1, lane);
     const uint32_t packed = f32_to_f16_bits(t0 * 0.0625f) | (f32_to_f16_bits(t1 * 0.0625f) << 16);
-    *(uint32_t *)(x_rot + ((int64_t)s * M + m) * K + frag_order_k(k0)) = packed;
+    const int64_t tile = (int64_t)s * (K >> 5) + (k0 >> 5);
+    *(uint32_t *)(x_rot + (tile * M + m) * 32 + (frag_order_k(k0) & 31)) = packed;
   }
 }
 

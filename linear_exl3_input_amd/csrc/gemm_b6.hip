@@ -1,3 +1,3 @@
 // Trellis GEMM and decode kernels for 6-bit weights (all codebooks).
-#include "exl3_gemm.hpp"
+#include "exl3_gemm_wide.hpp"
 EXL3_DEFINE_BITS(6)

@@ -30,10 +30,11 @@ def banner(msg: str) -> None:
     print(f"[gpu] {msg}", flush=True)
 
 
-def frag_order(x_rot_natural: np.ndarray) -> np.ndarray:
-    """The documented x_rot memory order: within each aligned group of 32 k
-    the 4-element chunks are stored as 0, 2, 1, 3, 4, 6, 5, 7."""
+def rot_layout(x_rot_natural: np.ndarray) -> np.ndarray:
+    """The documented x_rot memory order of a natural [S, M, K] array: k-step
+    tiles [S, K/32, M, 32], and within a row's 32 values the 4-element chunks
+    stored as 0, 2, 1, 3, 4, 6, 5, 7."""
     a = np.asarray(x_rot_natural)
-    lead, K = a.shape[:-1], a.shape[-1]
-    v = a.reshape(lead + (K // 32, 8, 4))
-    return v[..., [0, 2, 1, 3, 4, 6, 5, 7], :].reshape(lead + (K,))
+    S, M, K = a.shape
+    v = a.reshape(S, M, K // 32, 8, 4)[..., [0, 2, 1, 3, 4, 6, 5, 7], :].reshape(S, M, K // 32, 32)
+    return np.ascontiguousarray(v.transpose(0, 2, 1, 3))

@@ -14,7 +14,7 @@ import workloads as wl
 from oracle import format as ofmt
 from oracle import linear as olin
 from oracle import transform as otf
-from gpu_util import banner, bits16, dev16, frag_order, weight, x_dev
+from gpu_util import banner, bits16, dev16, rot_layout, weight, x_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_input_transform_bit_exact(x_dtype, M, K, S):
     suh = (np.where(rng.integers(0, 2, (S, K)) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, (S, K)))
            ).astype(np.float16).view(np.uint16)
     got = bits16(ex.input_transform(x_dev(x, x_dtype), dev16(suh, torch.float16)))
-    want = frag_order(otf.rotate_input(x, suh, x_dtype))
+    want = rot_layout(otf.rotate_input(x, suh, x_dtype))
     assert got.shape == want.shape
     assert np.array_equal(got, want)
 
@@ -71,9 +71,9 @@ def test_input_transform_one_hot_closed_form():
     x = np.zeros((128, 128), dtype=np.uint16)
     x[np.arange(128), np.arange(128)] = 0x3F80  # row j = e_j (bf16 1.0)
     suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
-    got = bits16(ex.input_transform(x_dev(x), dev16(suh, torch.float16)))[0]
+    got = bits16(ex.input_transform(x_dev(x), dev16(suh, torch.float16)))
     want = np.where(h.T > 0, 0x2C00, 0xAC00).astype(np.uint16)  # row j = signs of column j
-    assert np.array_equal(got, frag_order(want))
+    assert np.array_equal(got, rot_layout(want[None]))
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
@@ -232,7 +232,7 @@ def test_zero_rows_is_a_noop():
     lay = wl.small_layer("m0", 256, (128,), 2, "mul1", (1,), seed=17)
     t = wl.gen_all(lay)
     w = weight(t)
-    xr = torch.empty((1, 0, 256), dtype=torch.float16, device="cuda")
+    xr = torch.empty(ex.rot_shape(1, 0, 256), dtype=torch.float16, device="cuda")
     y = ex.linear(w, xr)
     assert y.shape == (0, 128)
 
@@ -253,7 +253,7 @@ def test_full_size_sampled(name, M):
     xr = ex.input_transform(x_dev(t.x), w.suh)
     y = bits16(ex.linear(w, xr, torch.bfloat16))
     # batch invariance at the real shape: the first row alone
-    y1 = bits16(ex.linear(w, xr[:, :1].contiguous(), torch.bfloat16))
+    y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
     assert np.array_equal(y1[0], y[0])
     rows = sorted({0, M // 2, M - 1})
     nblk = lay.N // 128
