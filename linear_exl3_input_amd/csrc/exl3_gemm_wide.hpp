@@ -6,21 +6,29 @@
 // share a column quarter split the decode: wave (wq, rh) decodes half h = rh
 // of each k-step's B and the pair swaps the halves through LDS, so every
 // trellis value is still decoded once per 256 rows while each wave does half
-// the decode work.  On this GPU a wave's own VALU work hides only about two
-// VALU instructions per MFMA; the second wave on the SIMD fills the rest.
+// the decode work.
+//
+// The two partners run on the same SIMD (wave w and w+4) and are scheduled
+// in opposite phases: the rh = 0 wave issues its sixteen MFMAs first and then
+// decodes, the rh = 1 wave decodes first and then issues its MFMAs, so one
+// wave's VALU work runs while the other wave's MFMAs occupy the matrix core
+// (a wave's own VALU instructions hide behind only about two MFMAs each).
 //
 // Data movement is by direct loads to LDS (global_load_lds_dwordx4), which
-// need no registers and stay in flight across barriers:
-//   - the trellis, in stages of 128 k x 128 columns, into a ring of three
-//     stage slots, issued two stages ahead.  Tiles are stored raw (16-bit
-//     words as they are in memory) with one 16-byte pad chunk on each side
-//     (the tile's last chunk before it, its first chunk after it), so a
+// need no registers and stay in flight across barriers.  The rh = 0 waves
+// load x~, the rh = 1 waves load the trellis, so that x~ loads (L2 hits)
+// never wait behind trellis loads (HBM) in a wave's in-order load queue:
+//   - the trellis, in stages of 128 k x 128 columns, into a ring of TSLOTS
+//     stage slots, issued TSLOTS-1 stages ahead.  Tiles are stored raw
+//     (16-bit words as they are in memory) with one 16-byte pad chunk on each
+//     side (the tile's last chunk before it, its first chunk after it), so a
 //     lane's window never wraps.  The word order is repaired in the decoder:
 //     for even widths a lane's first stream bit is byte aligned and one
 //     v_perm_b32 per window dword both reorders the words and aligns the
 //     window; odd widths rotate each dword by 16 first.
-//   - the rotated activations x~, one k-step (32 k x 256 rows, 16 KB) per
-//     ring slot, PF k-steps ahead.
+//   - the rotated activations x~, one k-step (32 k x 256 rows, 16 KB, one
+//     contiguous block in the k-step tile layout) per ring slot, PF k-steps
+//     ahead.
 // Barriers wait only for LDS operations (barrier_lds); the direct loads are
 // waited for with exact vmcnt counts.
 //
@@ -37,13 +45,14 @@ struct Wide {
   static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 256;
+  static constexpr int LOADERS = 4;                      // waves per load role
   static constexpr int TSTRIDE = 8 * BITS + 8;           // dwords per padded tile
   static constexpr int T_CHUNKS = 64 * (2 * BITS + 2);   // 16-byte chunks per padded stage
-  static constexpr int T_OPS = (T_CHUNKS + THREADS - 1) / THREADS;  // direct loads per wave per stage
-  static constexpr int JUNK_CHUNKS = T_OPS * THREADS - T_CHUNKS;    // landing area for the surplus
+  static constexpr int T_OPS = (T_CHUNKS + 64 * LOADERS - 1) / (64 * LOADERS);  // per trellis wave per stage
+  static constexpr int JUNK_CHUNKS = T_OPS * 64 * LOADERS - T_CHUNKS;           // landing area for the surplus
   static constexpr int TSLOT_DW = T_CHUNKS * 4;
-  static constexpr int TSLOTS = 3;
-  static constexpr int A_OPS = BM / 16 / WAVES;          // direct loads per wave per k-step
+  static constexpr int TSLOTS = 4;
+  static constexpr int A_OPS = BM / 16 / LOADERS;        // direct loads per x~ wave per k-step
   static constexpr int ASLOT_DW = BM * 16;               // 256 rows x 32 fp16
   static constexpr int XB_DW = WAVES * 256;              // one decoded B half per wave
   static constexpr int FIXED_DW = TSLOTS * TSLOT_DW + JUNK_CHUNKS * 4 + 2 * XB_DW;
@@ -51,7 +60,7 @@ struct Wide {
   // x~ prefetch distance in k-steps.  x~ of k-step i+1 is complete at the
   // barrier that ends k-step i-1, so a wave reads its first fragments of
   // k-step i+1 before the barrier that starts it.
-  static constexpr int PF = FIXED_DW + 6 * ASLOT_DW <= LDS_LIMIT_DW ? 5 : 4;
+  static constexpr int PF = FIXED_DW + 5 * ASLOT_DW <= LDS_LIMIT_DW ? 4 : 3;
   static constexpr int ASLOTS = PF + 1;
   static constexpr int MAIN_DW = FIXED_DW + ASLOTS * ASLOT_DW;
   static constexpr int Z_DW = 64 * Z_ROW;
@@ -62,16 +71,16 @@ struct Wide {
   static_assert(T_CHUNKS % 64 == 0, "each direct load lands whole in a stage or in the surplus area");
   static_assert(LDS_DW <= LDS_LIMIT_DW, "LDS budget");
 
-  // Direct loads this wave issues after the x~ loads of k-step i+2, up to the
-  // wait at the end of k-step i (ks = i % 4): the x~ loads of k-steps
-  // i+3 .. i+PF and the trellis loads issued at k-steps i+2-PF .. i whose
-  // ks is 3 (one trellis stage is issued at ks == 3, after that k-step's
-  // x~ loads).  Vector-memory operations complete in issue order, so the
-  // wait also covers every earlier trellis stage.
-  static constexpr int loads_after(int ks) {
-    int t = 0;
-    for (int k = ks + 2 - PF; k <= ks; ++k) t += ((k % 4) + 4) % 4 == 3 ? 1 : 0;
-    return A_OPS * (PF - 2) + T_OPS * t;
+  // x~ waves: at the end of k-step i, x~ of k-step i+2 must have landed.
+  // Issued after it are the x~ loads of k-steps i+3 .. i+PF.  Vector-memory
+  // operations complete in issue order.
+  static constexpr int A_WAIT = A_OPS * (PF - 2);
+  // trellis waves: at the end of k-step i (ks = i % 4, stage st = i / 4) the
+  // stage the next k-step decodes from, (i + 2) / 4, must have landed.  Stage
+  // st + TSLOTS is issued at ks == 3 of stage st, so the stages issued after
+  // the needed one number TSLOTS - 1 + [ks == 3] - [ks >= 2].
+  static constexpr int t_wait(int ks) {
+    return T_OPS * (TSLOTS - 1 + (ks == 3 ? 1 : 0) - (ks >= 2 ? 1 : 0));
   }
 };
 
@@ -104,24 +113,25 @@ __device__ __forceinline__ void wide_normalize(const uint32_t (&X)[Wide<BITS>::N
   }
 }
 
-template <int BITS, uint32_t CB, bool MULTI>
+template <int BITS, uint32_t CB, bool MULTI, int SCHED = 1>
 __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   using W = Wide<BITS>;
   constexpr int PF = W::PF;
   constexpr int ASLOTS = W::ASLOTS;
+  constexpr int TSLOTS = W::TSLOTS;
   // x~ fragments read ahead across the barrier (fewer when the part fold's
   // second accumulator set needs the registers)
   constexpr int NPRE = MULTI ? 4 : 8;
   __shared__ __attribute__((aligned(16))) uint32_t lds[W::LDS_DW];
   uint32_t *const tring = lds;
-  uint32_t *const junk = lds + W::TSLOTS * W::TSLOT_DW;
+  uint32_t *const junk = lds + TSLOTS * W::TSLOT_DW;
   uint32_t *const xbuf = junk + W::JUNK_CHUNKS * 4;
   uint32_t *const aring = xbuf + 2 * W::XB_DW;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wq = wave & 3;
-  const int rh = wave >> 2;
+  const int rh = wave >> 2;  // 0: x~ loads, MFMA first; 1: trellis loads, decode first
   const int j = lane & 15;
   const int g = lane >> 4;
   const int nb = blockIdx.x;
@@ -145,53 +155,58 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
   const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
 
-  // ---- trellis direct loads: per-lane source offsets (16-bit words) of the
-  // chunk that lands at this lane's LDS position in each issue round
-  const uint16_t *const tr0 = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8) * (16 * BITS);
-  const int64_t tr_stage = (int64_t)8 * NT * (16 * BITS);
-  uint32_t t_src[W::T_OPS];
+  // ---- load sources.  The rh = 0 waves use src[t] for x~ fragment
+  // wq + 4t (rows 16(wq+4t) .. +15; lane L loads row L%16, k-chunk L/16;
+  // rows past M load row M-1).  The rh = 1 waves use src[r] for the trellis
+  // chunk that lands at this lane's LDS position in round r.
+  // Offsets are in 16-bit words from a_base / t_base (wave-uniform).
+  const uint16_t *const a_base = xs + (int64_t)(k_begin >> 5) * M * 32;
+  const uint16_t *const t_base = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8) * (16 * BITS);
+  uint32_t src[W::A_OPS > W::T_OPS ? W::A_OPS : W::T_OPS];
+  if (rh == 0) {
 #pragma unroll
-  for (int r = 0; r < W::T_OPS; ++r) {
-    const int q = r * W::THREADS + wave * 64 + lane;
-    if (q < W::T_CHUNKS) {
-      const int t = q / (2 * BITS + 2);
-      const int c = q - t * (2 * BITS + 2);
-      const int sc = c == 0 ? 2 * BITS - 1 : (c == 2 * BITS + 1 ? 0 : c - 1);
-      t_src[r] = (uint32_t)(((t >> 3) * NT + (t & 7)) * (16 * BITS) + sc * 8);
-    } else {
-      t_src[r] = (uint32_t)((lane % (2 * BITS)) * 8);
+    for (int t = 0; t < W::A_OPS; ++t) {
+      int row = m0 + 16 * (wq + W::LOADERS * t) + (lane & 15);
+      row = row < M ? row : M - 1;
+      src[t] = (uint32_t)(row * 32 + 8 * (lane >> 4));
     }
-  }
-  auto issue_trellis = [&](int stage, int slot) {
-    const uint16_t *base = tr0 + (int64_t)min(stage, nst - 1) * tr_stage;
-    uint32_t *const dst0 = tring + slot * W::TSLOT_DW;
+  } else {
 #pragma unroll
     for (int r = 0; r < W::T_OPS; ++r) {
-      const int q0 = r * W::THREADS + wave * 64;
-      uint32_t *dst = q0 < W::T_CHUNKS ? dst0 + q0 * 4 : junk + (q0 - W::T_CHUNKS) * 4;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + t_src[r]),
-                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+      const int q = r * 64 * W::LOADERS + wq * 64 + lane;
+      uint32_t off;
+      if (q < W::T_CHUNKS) {
+        const int t = q / (2 * BITS + 2);
+        const int c = q - t * (2 * BITS + 2);
+        const int sc = c == 0 ? 2 * BITS - 1 : (c == 2 * BITS + 1 ? 0 : c - 1);
+        off = (uint32_t)(((t >> 3) * NT + (t & 7)) * (16 * BITS) + sc * 8);
+      } else {
+        off = (uint32_t)((lane % (2 * BITS)) * 8);
+      }
+      src[r] = off;
     }
-  };
-  // ---- x~ direct loads: fragment mf = wave + 8t holds rows 16mf .. 16mf+15;
-  // lane L of it loads row L%16, k-chunk L/16 (x~ is in k-step tiles, so a
-  // fragment is 1 KB contiguous).  Rows past M load row M-1.
-  const uint16_t *a_src[W::A_OPS];
-#pragma unroll
-  for (int t = 0; t < W::A_OPS; ++t) {
-    int row = m0 + 16 * (wave + W::WAVES * t) + (lane & 15);
-    row = row < M ? row : M - 1;
-    a_src[t] = xs + ((int64_t)(k_begin >> 5) * M + row) * 32 + 8 * (lane >> 4);
   }
-  const int64_t a_kstep = (int64_t)M * 32;  // 16-bit words per k-step tile
+  const int64_t a_kstep = (int64_t)M * 32;                 // 16-bit words per x~ k-step tile
+  const int64_t tr_stage = (int64_t)8 * NT * (16 * BITS);  // 16-bit words per trellis stage
   auto issue_a = [&](int kstep, int slot) {
-    const int64_t k = a_kstep * min(kstep, nks - 1);
+    const uint16_t *const base = a_base + a_kstep * min(kstep, nks - 1);
     uint32_t *const dst0 = aring + slot * W::ASLOT_DW;
 #pragma unroll
     for (int t = 0; t < W::A_OPS; ++t)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a_src[t] + k),
-                                       (__attribute__((address_space(3))) void *)(dst0 + (wave + W::WAVES * t) * 256),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + src[t]),
+                                       (__attribute__((address_space(3))) void *)(dst0 + (wq + W::LOADERS * t) * 256),
                                        16, 0, 0);
+  };
+  auto issue_trellis = [&](int stage, int slot) {
+    const uint16_t *const base = t_base + tr_stage * min(stage, nst - 1);
+    uint32_t *const dst0 = tring + slot * W::TSLOT_DW;
+#pragma unroll
+    for (int r = 0; r < W::T_OPS; ++r) {
+      const int q0 = r * 64 * W::LOADERS + wq * 64;
+      uint32_t *dst = q0 < W::T_CHUNKS ? dst0 + q0 * 4 : junk + (q0 - W::T_CHUNKS) * 4;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + src[r]),
+                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
   };
 
   // ---- per-lane decode constants (half h = rh of n-tiles 2wq, 2wq+1)
@@ -224,12 +239,15 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: trellis stages 0..2, x~ k-steps 0..PF-1, own B of k-step 0
-  issue_trellis(0, 0);
-  issue_trellis(1, 1);
+  // ---- prologue: trellis stages 0 .. TSLOTS-1, x~ k-steps 0 .. PF-1, own B
+  // of k-step 0, first x~ fragments of k-step 0
+  if (rh == 0) {
 #pragma unroll
-  for (int i = 0; i < PF; ++i) issue_a(i, i);
-  issue_trellis(2, 2);
+    for (int i = 0; i < PF; ++i) issue_a(i, i);
+  } else {
+#pragma unroll
+    for (int s = 0; s < TSLOTS; ++s) issue_trellis(s, s);
+  }
   wait_vmcnt<0>();
   barrier_lds();
   u32x4_t b_own = decode_own(tring, 0);
@@ -242,20 +260,20 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   int st = 0;
   int ts0 = 0;     // trellis slot of stage st
   int as_cur = 0;  // x~ slot of k-step 4*st
-  auto run_stages = [&](int st_end) {
+  auto run_stages = [&](int st_end, auto ph_c) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph_c)::value;  // == rh
     for (; st < st_end; ++st) {
-      const int ts1 = ts0 == W::TSLOTS - 1 ? 0 : ts0 + 1;
-      auto kstep = [&](auto ks_c) {
+      const int ts1 = ts0 == TSLOTS - 1 ? 0 : ts0 + 1;
+      auto kstep = [&](auto ks_c) __attribute__((always_inline)) {
         constexpr int ks = decltype(ks_c)::value;
         const int i = 4 * st + ks;
         int as = as_cur + ks;
         as = as >= ASLOTS ? as - ASLOTS : as;
         const int as_pf = as == 0 ? ASLOTS - 1 : as - 1;  // (i + PF) % ASLOTS, PF = ASLOTS - 1
         const int as_nx = as == ASLOTS - 1 ? 0 : as + 1;   // (i + 1) % ASLOTS
-        issue_a(i + PF, as_pf);
-        asm volatile("" ::: "memory");  // keep the issue order loads_after() counts
-        if constexpr (ks == 3) issue_trellis(st + 3, ts0);
-        asm volatile("" ::: "memory");
+        if constexpr (PH == 0) issue_a(i + PF, as_pf);
+        else if constexpr (ks == 3) issue_trellis(st + TSLOTS, ts0);
+        asm volatile("" ::: "memory");  // keep the issue order the waits count
         const u32x4_t b_par = *(const u32x4_t *)(xb_par0 + (i & 1) * W::XB_DW);
         const half8_t B0 = __builtin_bit_cast(half8_t, b_own);
         const half8_t B1 = __builtin_bit_cast(half8_t, b_par);
@@ -266,31 +284,59 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
 #pragma unroll
         for (int q = 0; q < W::NX; ++q) X[q] = tp[q];
         const uint32_t *as_n = a_lane + as_nx * W::ASLOT_DW;
-        // a_cur[0 .. NPRE-1] hold this k-step's first x~ fragments (read
-        // during the previous k-step), so the own-half products start right
-        // after the barrier; the partner-half products follow, while the next
-        // k-step's fragments are read (x~ of k-step i+1 is complete by now).
-        u32x4_t nb4;
         if constexpr (NPRE < 8) {
           const uint32_t *as_p = a_lane + as * W::ASLOT_DW;
 #pragma unroll
           for (int q = NPRE; q < 8; ++q) a_cur[q] = *(const half8_t *)(as_p + q * 256);
         }
+        u32x4_t nb4;
+        auto decode = [&]() __attribute__((always_inline)) {
+          wide_normalize<BITS>(X, sel, sh, Y);
+          nb4[0] = frag_pair<BITS, CB, 0>(Y);
+          nb4[1] = frag_pair<BITS, CB, 1>(Y);
+          nb4[2] = frag_pair<BITS, CB, 2>(Y);
+          nb4[3] = frag_pair<BITS, CB, 3>(Y);
+          *(u32x4_t *)(xb_own0 + ((i + 1) & 1) * W::XB_DW) = nb4;
+        };
+        // own-half products first (operands in registers), then the
+        // partner half, while the next k-step's first fragments are read
+        // (x~ of k-step i+1 is complete by now)
+        auto products = [&]() __attribute__((always_inline)) {
+          static_for<0, 16>([&](auto it_c) {
+            constexpr int it = decltype(it_c)::value;
+            if constexpr (it < 8) {
+              acc[it][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it], B0, acc[it][0], 0, 0, 0);
+            } else {
+              acc[it - 8][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it - 8], B1, acc[it - 8][1], 0, 0, 0);
+              if constexpr (it - 8 < NPRE) a_nxt[it - 8] = *(const half8_t *)(as_n + (it - 8) * 256);
+            }
+          });
+        };
         __builtin_amdgcn_sched_barrier(0);
-        static_for<0, 16>([&](auto it_c) {
-          constexpr int it = decltype(it_c)::value;
-          if constexpr (it < 8) {
-            acc[it][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it], B0, acc[it][0], 0, 0, 0);
-          } else {
-            acc[it - 8][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it - 8], B1, acc[it - 8][1], 0, 0, 0);
-            if constexpr (it - 8 < NPRE) a_nxt[it - 8] = *(const half8_t *)(as_n + (it - 8) * 256);
-          }
-          if constexpr (it == 2) wide_normalize<BITS>(X, sel, sh, Y);
-          if constexpr (it >= 3 && it < 7) nb4[it - 3] = frag_pair<BITS, CB, it - 3>(Y);
-          if constexpr (it == 7) *(u32x4_t *)(xb_own0 + ((i + 1) & 1) * W::XB_DW) = nb4;
+        if constexpr (SCHED == 1) {
+          // interleaved: each MFMA followed by about three VALU instructions
+          // of the decode (a wave issues VALU at most every ~8 cycles, so
+          // the decode is spread over the whole k-step in both waves)
+          products();
+          decode();
+          static_for<0, 16>([&](auto it_c) {
+            constexpr int it = decltype(it_c)::value;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+            if constexpr (it >= 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          });
+        } else if constexpr (PH == 0) {
+          products();
           __builtin_amdgcn_sched_barrier(0);
-        });
-        wait_vmcnt<W::loads_after(ks)>();
+          decode();
+        } else {
+          decode();
+          __builtin_amdgcn_sched_barrier(0);
+          products();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PH == 0) wait_vmcnt<W::A_WAIT>();
+        else wait_vmcnt<W::t_wait(ks)>();
         barrier_lds();
         b_own = nb4;
 #pragma unroll
@@ -305,9 +351,11 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
     }
   };
 
+  // the whole K loop, for one phase (the branch on rh is taken once)
+  auto main_loop = [&](auto ph_c) __attribute__((always_inline)) {
   if constexpr (MULTI) {
     // first part copied, later parts added in part order
-    run_stages((int)((int64_t)(p_begin + 1) * KB / p.parts) - kb_begin);
+    run_stages((int)((int64_t)(p_begin + 1) * KB / p.parts) - kb_begin, ph_c);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -316,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
         acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
     for (int part = p_begin + 1; part < p_end; ++part) {
-      run_stages((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin);
+      run_stages((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin, ph_c);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -330,8 +378,11 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[mt][h] = tot[mt][h];
   } else {
-    run_stages(nst);
+    run_stages(nst, ph_c);
   }
+  };
+  if (rh == 0) main_loop(std::integral_constant<int, 0>{});
+  else main_loop(std::integral_constant<int, 1>{});
   wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
   barrier_lds();
 
