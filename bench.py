@@ -47,11 +47,26 @@ WORKLOADS = {
 }
 DEFAULT_WORKLOAD = "expert_4096x2048+2048x4096_b4_mcg"
 
-KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_device.hpp"]
+KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_device.hpp", "exl3_misc.hip"]
 
 
 def sol_seconds(M, K, N, bits):
     return max(K * N * bits / 8 / HBM_BPS, 2.0 * M * K * N / MFMA_F16_FLOPS)
+
+
+def kernel_key(lay, plan) -> str:
+    """The GEMM template instance a call launches (what rocprof's per-kernel
+    statistics group by): tile family and rows, width, codebook, part fold."""
+    bm = plan["bm"]
+    multi = plan["mode"] == 0 and plan["parts"] > 1
+    cb = {"3inst": 0, "mcg": 1, "mul1": 2}[lay.codebook]
+    if bm <= 64:
+        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}>"
+    elif bm == 128:
+        name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, {str(multi).lower()}>"
+    else:
+        name = f"exl3::gemm_wide_kernel<{lay.bits}, {cb}u, {bm // 2}, {str(multi).lower()}, 1>"
+    return name
 
 
 def kernel_hash() -> str:
@@ -120,6 +135,10 @@ def main():
     ap.add_argument("--timing-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--only", default=None, metavar="LAYER:M",
+                    help="counter runs: launch only this call class (transform + linear), --steps times")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="counter runs: copy MB of device memory --steps times (a kernel of known bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -136,7 +155,19 @@ def main():
     ex.load()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB x {args.steps}")
+        return
     names, Ms = WORKLOADS[args.workload]
+    if args.only:
+        oname, oM = args.only.split(":")
+        names, Ms = [oname], (int(oM),)
     layers = [wl.layer(n) for n in names]
     M_max = max(Ms)
 
@@ -175,8 +206,16 @@ def main():
             for M in Ms:
                 call(li, M, copy)
 
-    # ---- one graph per weight copy
     stream = torch.cuda.Stream()
+    if args.only:
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup + args.steps):
+                step(i % copies)
+        torch.cuda.synchronize()
+        log(f"ran {args.only} x {args.warmup + args.steps}")
+        return
+
+    # ---- one graph per weight copy
     graphs = []
     with torch.cuda.stream(stream):
         step(0)
@@ -246,32 +285,60 @@ def main():
                     f"({per_shape[-1]['GBps']} GB/s, {per_shape[-1]['TFLOPS']} TFLOP/s, "
                     f"{per_shape[-1]['pct_sol']}% SoL)")
 
-    # ---- roofline of the dominant single-kernel linear call class
-    single = [s for s in per_shape if s["plan"]["mode"] == ex.EXL3_MODE_FUSED] or per_shape
-    dom = max(single, key=lambda s: s["linear_us"])
-    lay = wl.layer(dom["layer"])
-    secs = dom["linear_us"] * 1e-6
-    if dom["bound"] == "mfma":
-        achieved = 2.0 * dom["M"] * lay.K * lay.N / secs / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s"}
+    # ---- roofline of the dominant kernel: the GEMM template instance with
+    # the most time per step.  A slab-mode call is the GEMM plus the ordered
+    # part sum + output transform kernel; that second kernel is timed alone
+    # (same parts, rows and columns) and subtracted, so the GEMM's average
+    # launch duration is what rocprof reports for it.
+    with torch.cuda.stream(stream):
+        for s_ in per_shape:
+            s_["gemm_us"] = s_["linear_us"]
+            s_["epilogue_us"] = 0.0
+            if s_["plan"]["mode"] == ex.EXL3_MODE_SLABS:
+                li = [l.name for l in layers].index(s_["layer"])
+                lay_, ws_ = per_layer[li][0], per_layer[li][1]
+                zp = torch.zeros((s_["plan"]["parts"], (s_["M"] + 3) // 4, lay_.N, 4), dtype=torch.float32,
+                                 device=dev)
+                yo = torch.empty((s_["M"], lay_.N), dtype=torch.bfloat16, device=dev)
+                t_epi = time_calls(lambda r: ex.debug_epilogue(ws_[0], zp, s_["M"], out=yo), args.timing_reps)
+                s_["epilogue_us"] = round(t_epi, 3)
+                s_["gemm_us"] = round(s_["linear_us"] - t_epi, 3)
+                del zp
+            s_["kernel"] = kernel_key(wl.layer(s_["layer"]), s_["plan"])
+    groups = {}
+    for s_ in per_shape:
+        groups.setdefault(s_["kernel"], []).append(s_)
+    dom_key = max(groups, key=lambda k: sum(g["gemm_us"] for g in groups[k]))
+    dom = groups[dom_key]
+    secs = sum(g["gemm_us"] for g in dom) * 1e-6
+    bound = max(dom, key=lambda g: g["gemm_us"])["bound"]
+    if bound == "mfma":
+        work = sum(2.0 * g["M"] * g["K"] * g["N"] for g in dom)
+        roof = {"bound": "mfma", "achieved": round(work / secs / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s"}
     else:
-        achieved = lay.weight_bytes() / secs / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s"}
+        work = sum(g["K"] * g["N"] * g["bits"] / 8 for g in dom)
+        roof = {"bound": "hbm", "achieved": round(work / secs / 1e9, 1), "peak": 8000.0, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    roof["kernel"] = f"exl3 gemm_kernel, {dom['layer']} M={dom['M']} (plan {dom['plan']})"
-    roof["avg_launch_us"] = dom["linear_us"]
+    roof["kernel"] = dom_key
+    roof["launches"] = [f"{g['layer']} M={g['M']}" for g in dom]
+    roof["avg_launch_us"] = round(secs * 1e6 / len(dom), 3)
+    roof["work_per_launch"] = ("2*M*K*N flops" if bound == "mfma" else "K*N*bits/8 trellis bytes")
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            key = f"{dom['layer']}:M={dom['M']}"
-            ent = tj.get("entries", {}).get(key)
+            ent = tj.get("entries", {}).get(dom_key)
             if ent and tj.get("kernel_hash") == kernel_hash():
-                roof["traffic"] = {"fetch_bytes": ent["fetch_bytes"], "write_bytes": ent["write_bytes"],
-                                   "algorithmic_bytes": lay.weight_bytes()}
+                n = len(dom)
+                roof["traffic"] = {"fetch_bytes_per_launch": ent["fetch_bytes"], "write_bytes_per_launch":
+                                   ent["write_bytes"], "algorithmic_trellis_bytes_per_launch":
+                                   sum(g["K"] * g["N"] * g["bits"] / 8 for g in dom) / n,
+                                   "scale": ent.get("scale")}
         except Exception as e:  # a malformed file only loses the traffic field
             log(f"traffic file unreadable: {e}")
+    log(f"roofline: {dom_key} over {roof['launches']}: {roof['achieved']} {roof['unit']} = "
+        f"{100 * roof['frac']:.1f}% of peak, {roof['avg_launch_us']} us per launch")
 
     line = {
         "metric": "EXL3 linear achieved GB/s + TFLOPS and %SoL vs max(HBM,MFMA) per (M,K,N,bits)",

@@ -92,7 +92,9 @@ typedef enum {
 typedef struct exl3_plan {
   int32_t parts;       /* P >= 1 K parts                                     */
   int32_t mode;        /* exl3_mode                                          */
-  int32_t bm;          /* rows per M-tile: 16, 32, 64, 128 or 256           */
+  int32_t bm;          /* rows per M-tile: 16, 32, 64, 128, 256 or 512;
+                          512 only with one part per workgroup (parts == 1
+                          or slab mode), else EXL3_ERR_UNSUPPORTED          */
   int32_t reserved;
   size_t workspace;    /* bytes of workspace this plan needs                 */
 } exl3_plan;
@@ -173,9 +175,11 @@ exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream);
  * unpacking path (TensorFold PR, "Tests (GB10)" second bullet). */
 exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream);
 
-/* The output stage alone: y = rne_out(svh * 2^-3 * H128(z)) with
- * z = ((z_parts[0] + z_parts[1]) + ...) in fp32, z_parts [n_parts][M][N]
- * fp32 (TensorFold PR, "Arithmetic" step 3 and the ordered part sum). */
+/* The output stage alone, the kernel slab mode runs after the GEMM:
+ * y = rne_out(svh * 2^-3 * H128(z)) with z = ((z_parts[0] + z_parts[1]) + ...)
+ * in fp32 (TensorFold PR, "Arithmetic" step 3 and the ordered part sum).
+ * z_parts is in the partial-slab layout [n_parts][ceil(M/4)][N][4] fp32:
+ * element (part, m, n) at ((part * ceil(M/4) + m/4) * N + n) * 4 + m%4. */
 exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t M,
                                 const exl3_weight *w, void *y, int32_t y_dtype, void *stream);
 

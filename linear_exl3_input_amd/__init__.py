@@ -278,11 +278,16 @@ def debug_decode(w: Exl3Weight) -> torch.Tensor:
     return out
 
 
-def debug_epilogue(w: Exl3Weight, z_parts: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
-    if z_parts.dim() == 2:
-        z_parts = z_parts.unsqueeze(0)
-    P, M, N = z_parts.shape
-    out = torch.empty((M, N), dtype=out_dtype, device=z_parts.device)
+def debug_epilogue(w: Exl3Weight, z_parts: torch.Tensor, M: int, out_dtype=torch.bfloat16,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Ordered part sum + output transform of fp32 partials in the slab
+    layout [P, ceil(M/4), N, 4] (see slab_layout)."""
+    if z_parts.dim() != 4 or z_parts.shape[1] != (M + 3) // 4 or z_parts.shape[3] != 4:
+        raise ValueError(f"z_parts shape {tuple(z_parts.shape)} is not [P, ceil(M/4), N, 4] for M={M}")
+    P, _, N, _ = z_parts.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=z_parts.device)
+    out_dtype = out.dtype
     _check(load().exl3_debug_epilogue(_dev_ptr(z_parts, "z_parts", (torch.float32,)), P, M, ctypes.byref(w.view()),
                                       out.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _F16, _stream()))
     return out

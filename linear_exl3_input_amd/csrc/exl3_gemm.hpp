@@ -34,7 +34,7 @@
 // from zero; parts are added in part order, the first part copied, not added
 // to zero (TensorFold PR, "Arithmetic": a number of parts fixed by the shape,
 // added in part order).  In slab mode each workgroup runs one part and writes
-// an fp32 partial; otherwise one workgroup runs all parts and keeps the
+// an fp32 partial (store_partial); otherwise one workgroup runs all parts and keeps the
 // running sum in registers.  Both give the same bits for every row.
 #pragma once
 
@@ -219,6 +219,19 @@ __device__ __forceinline__ int lane_col(int wave, int j, int h) {
   return 16 * (2 * wave + (j >> 3)) + (j & 7) + 8 * h;
 }
 
+// One accumulator of a lane (rows row0 .. row0+3 of column col; row0 is a
+// multiple of 4) into the fp32 partial of K part `part`.  Partials are laid
+// out [part][M/4][N][4] (rows padded to a multiple of 4, padding rows hold
+// finite values of clamped or zero rows): a lane's four values are one
+// 16-byte store and a wave's stores fill whole cache lines.
+__device__ __forceinline__ void store_partial(float *__restrict__ slabs, int part, int M, int N, int row0, int col,
+                                              float4_t v) {
+  if (row0 < M) {
+    const int64_t M4 = (M + 3) >> 2;
+    *(float4_t *)(slabs + (((int64_t)part * M4 + (row0 >> 2)) * N + col) * 4) = v;
+  }
+}
+
 // ------------------------------------------------------------------- GEMM
 
 template <int BITS, uint32_t CB, int MT, bool MULTI>
@@ -335,18 +348,11 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
   }
 
   if (p.slab_mode) {
-    float *__restrict__ sl = p.slabs + (int64_t)p_begin * M * N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int col = nb * 128 + lane_col(wave, j, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m0 + mt * 16 + 4 * g + i;
-          if (row < M) sl[(int64_t)row * N + col] = acc[mt][h][i];
-        }
-      }
+      for (int h = 0; h < 2; ++h)
+        store_partial(p.slabs, p_begin, M, N, m0 + mt * 16 + 4 * g, nb * 128 + lane_col(wave, j, h), acc[mt][h]);
     return;
   }
 
@@ -586,18 +592,11 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
   wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
 
   if (p.slab_mode) {
-    float *__restrict__ sl = p.slabs + (int64_t)p_begin * M * N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int col = nb * 128 + lane_col(wave, j, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m0 + mt * 16 + 4 * g + i;
-          if (row < M) sl[(int64_t)row * N + col] = acc[mt][h][i];
-        }
-      }
+      for (int h = 0; h < 2; ++h)
+        store_partial(p.slabs, p_begin, M, N, m0 + mt * 16 + 4 * g, nb * 128 + lane_col(wave, j, h), acc[mt][h]);
     return;
   }
 
@@ -679,10 +678,11 @@ hipError_t launch_big_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t 
 }
 
 template <int BITS, uint32_t CB>
-hipError_t launch_wide_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
+hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
 
 // bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128 -> gemm_big_kernel,
-// 256 -> gemm_wide_kernel (512 threads).
+// 256/512 -> gemm_wide_kernel (512 threads; 512 for a single part per
+// workgroup only).
 template <int BITS, uint32_t CB>
 hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   switch (bm) {
@@ -690,7 +690,8 @@ hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hi
     case 32: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
     case 64: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
     case 128: return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
-    case 256: return launch_wide_t<BITS, CB>(multi, p, grid, s);
+    case 256:
+    case 512: return launch_wide_t<BITS, CB>(bm, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -40,27 +40,31 @@
 
 namespace exl3 {
 
-template <int BITS>
+template <int BITS, int RW>
 struct Wide {
   static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BM = 256;
+  static constexpr int MF = RW / 16;                     // 16-row fragments per wave
+  static constexpr int BM = 2 * RW;
   static constexpr int LOADERS = 4;                      // waves per load role
   static constexpr int TSTRIDE = 8 * BITS + 8;           // dwords per padded tile
   static constexpr int T_CHUNKS = 64 * (2 * BITS + 2);   // 16-byte chunks per padded stage
   static constexpr int T_OPS = (T_CHUNKS + 64 * LOADERS - 1) / (64 * LOADERS);  // per trellis wave per stage
   static constexpr int JUNK_CHUNKS = T_OPS * 64 * LOADERS - T_CHUNKS;           // landing area for the surplus
   static constexpr int TSLOT_DW = T_CHUNKS * 4;
-  static constexpr int TSLOTS = 4;
+  static constexpr int TSLOTS = RW == 128 ? 4 : (BITS <= 6 ? 3 : 2);
   static constexpr int A_OPS = BM / 16 / LOADERS;        // direct loads per x~ wave per k-step
-  static constexpr int ASLOT_DW = BM * 16;               // 256 rows x 32 fp16
+  static constexpr int ASLOT_DW = BM * 16;               // BM rows x 32 fp16
   static constexpr int XB_DW = WAVES * 256;              // one decoded B half per wave
   static constexpr int FIXED_DW = TSLOTS * TSLOT_DW + JUNK_CHUNKS * 4 + 2 * XB_DW;
   static constexpr int LDS_LIMIT_DW = 160 * 1024 / 4;
-  // x~ prefetch distance in k-steps.  x~ of k-step i+1 is complete at the
-  // barrier that ends k-step i-1, so a wave reads its first fragments of
-  // k-step i+1 before the barrier that starts it.
-  static constexpr int PF = FIXED_DW + 5 * ASLOT_DW <= LDS_LIMIT_DW ? 4 : 3;
+  // x~ prefetch distance in k-steps (as deep as LDS allows).  With PF >= 3
+  // (AHEAD) x~ of k-step i+1 is complete at the barrier that ends k-step
+  // i-1, and a wave reads its first fragments of k-step i+1 before the
+  // barrier that starts it.
+  static constexpr int PF = FIXED_DW + 5 * ASLOT_DW <= LDS_LIMIT_DW ? 4
+                            : FIXED_DW + 4 * ASLOT_DW <= LDS_LIMIT_DW ? 3 : 2;
+  static constexpr bool AHEAD = PF >= 3 && RW == 128;
   static constexpr int ASLOTS = PF + 1;
   static constexpr int MAIN_DW = FIXED_DW + ASLOTS * ASLOT_DW;
   static constexpr int Z_DW = 64 * Z_ROW;
@@ -71,10 +75,10 @@ struct Wide {
   static_assert(T_CHUNKS % 64 == 0, "each direct load lands whole in a stage or in the surplus area");
   static_assert(LDS_DW <= LDS_LIMIT_DW, "LDS budget");
 
-  // x~ waves: at the end of k-step i, x~ of k-step i+2 must have landed.
-  // Issued after it are the x~ loads of k-steps i+3 .. i+PF.  Vector-memory
-  // operations complete in issue order.
-  static constexpr int A_WAIT = A_OPS * (PF - 2);
+  // x~ waves: at the end of k-step i, x~ of k-step i+2 (AHEAD) or i+1 must
+  // have landed.  Issued after it are the x~ loads of the later k-steps up
+  // to i+PF.  Vector-memory operations complete in issue order.
+  static constexpr int A_WAIT = A_OPS * (AHEAD ? PF - 2 : PF - 1);
   // trellis waves: at the end of k-step i (ks = i % 4, stage st = i / 4) the
   // stage the next k-step decodes from, (i + 2) / 4, must have landed.  Stage
   // st + TSLOTS is issued at ks == 3 of stage st, so the stages issued after
@@ -98,9 +102,9 @@ __device__ __forceinline__ void lane_window_perm(int j, int g, int h, int &doff,
 }
 
 template <int BITS>
-__device__ __forceinline__ void wide_normalize(const uint32_t (&X)[Wide<BITS>::NX], uint32_t sel, int sh,
-                                               uint32_t (&Y)[Wide<BITS>::NY]) {
-  using W = Wide<BITS>;
+__device__ __forceinline__ void wide_normalize(const uint32_t (&X)[Geom<BITS>::NX], uint32_t sel, int sh,
+                                               uint32_t (&Y)[Geom<BITS>::NY]) {
+  using W = Wide<BITS, 128>;
   if constexpr (W::PERM) {
 #pragma unroll
     for (int i = 0; i < W::NY; ++i) Y[i] = __builtin_amdgcn_perm(X[i + 1], X[i], sel);
@@ -113,15 +117,18 @@ __device__ __forceinline__ void wide_normalize(const uint32_t (&X)[Wide<BITS>::N
   }
 }
 
-template <int BITS, uint32_t CB, bool MULTI, int SCHED = 1>
+template <int BITS, uint32_t CB, int RW, bool MULTI, int SCHED = 1>
 __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
-  using W = Wide<BITS>;
+  using W = Wide<BITS, RW>;
+  constexpr int MF = W::MF;
   constexpr int PF = W::PF;
   constexpr int ASLOTS = W::ASLOTS;
   constexpr int TSLOTS = W::TSLOTS;
   // x~ fragments read ahead across the barrier (fewer when the part fold's
-  // second accumulator set needs the registers)
-  constexpr int NPRE = MULTI ? 4 : 8;
+  // second accumulator set needs the registers; none without AHEAD)
+  constexpr int NPRE = !W::AHEAD ? 0 : (MULTI ? 4 : 8);
+  static_assert(!W::AHEAD || MF == 8, "read-ahead schedule is for 128-row waves");
+  static_assert(!(MULTI && RW > 128), "two accumulator sets of 256 rows do not fit");
   __shared__ __attribute__((aligned(16))) uint32_t lds[W::LDS_DW];
   uint32_t *const tring = lds;
   uint32_t *const junk = lds + TSLOTS * W::TSLOT_DW;
@@ -229,13 +236,13 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   };
   uint32_t *const xb_own0 = xbuf + wave * 256 + 4 * lane;
   const uint32_t *const xb_par0 = xbuf + (wave ^ 4) * 256 + 4 * lane;
-  const uint32_t *const a_lane = aring + rh * 8 * 256 + 4 * lane;
+  const uint32_t *const a_lane = aring + rh * MF * 256 + 4 * lane;
 
   // acc[mt][0]: own half (h = rh), acc[mt][1]: the partner's half
-  float4_t acc[8][2];
-  float4_t tot[MULTI ? 8 : 1][2];
+  float4_t acc[MF][2];
+  float4_t tot[MULTI ? MF : 1][2];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < MF; ++mt)
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   barrier_lds();
   u32x4_t b_own = decode_own(tring, 0);
   *(u32x4_t *)xb_own0 = b_own;
-  half8_t a_cur[8], a_nxt[NPRE];
+  half8_t a_cur[8], a_nxt[NPRE > 0 ? NPRE : 1];
 #pragma unroll
   for (int q = 0; q < NPRE; ++q) a_cur[q] = *(const half8_t *)(a_lane + q * 256);
   barrier_lds();
@@ -267,8 +274,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
       auto kstep = [&](auto ks_c) __attribute__((always_inline)) {
         constexpr int ks = decltype(ks_c)::value;
         const int i = 4 * st + ks;
-        int as = as_cur + ks;
-        as = as >= ASLOTS ? as - ASLOTS : as;
+        const int as = (as_cur + ks) % ASLOTS;  // x~ slot of k-step i
         const int as_pf = as == 0 ? ASLOTS - 1 : as - 1;  // (i + PF) % ASLOTS, PF = ASLOTS - 1
         const int as_nx = as == ASLOTS - 1 ? 0 : as + 1;   // (i + 1) % ASLOTS
         if constexpr (PH == 0) issue_a(i + PF, as_pf);
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
 #pragma unroll
         for (int q = 0; q < W::NX; ++q) X[q] = tp[q];
         const uint32_t *as_n = a_lane + as_nx * W::ASLOT_DW;
-        if constexpr (NPRE < 8) {
-          const uint32_t *as_p = a_lane + as * W::ASLOT_DW;
+        const uint32_t *as_p = a_lane + as * W::ASLOT_DW;
+        if constexpr (NPRE > 0 && NPRE < 8) {
 #pragma unroll
           for (int q = NPRE; q < 8; ++q) a_cur[q] = *(const half8_t *)(as_p + q * 256);
         }
@@ -302,15 +308,29 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
         // partner half, while the next k-step's first fragments are read
         // (x~ of k-step i+1 is complete by now)
         auto products = [&]() __attribute__((always_inline)) {
-          static_for<0, 16>([&](auto it_c) {
-            constexpr int it = decltype(it_c)::value;
-            if constexpr (it < 8) {
-              acc[it][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it], B0, acc[it][0], 0, 0, 0);
-            } else {
-              acc[it - 8][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it - 8], B1, acc[it - 8][1], 0, 0, 0);
-              if constexpr (it - 8 < NPRE) a_nxt[it - 8] = *(const half8_t *)(as_n + (it - 8) * 256);
-            }
-          });
+          if constexpr (NPRE > 0) {
+            static_for<0, 16>([&](auto it_c) {
+              constexpr int it = decltype(it_c)::value;
+              if constexpr (it < 8) {
+                acc[it][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it], B0, acc[it][0], 0, 0, 0);
+              } else {
+                acc[it - 8][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[it - 8], B1, acc[it - 8][1], 0, 0, 0);
+                if constexpr (it - 8 < NPRE) a_nxt[it - 8] = *(const half8_t *)(as_n + (it - 8) * 256);
+              }
+            });
+          } else {
+            // fragment mt read RD fragments ahead of its two products
+            constexpr int RD = 3;
+            half8_t af[MF];
+#pragma unroll
+            for (int q = 0; q < RD; ++q) af[q] = *(const half8_t *)(as_p + q * 256);
+            static_for<0, MF>([&](auto mt_c) {
+              constexpr int mt = decltype(mt_c)::value;
+              if constexpr (mt + RD < MF) af[mt + RD] = *(const half8_t *)(as_p + (mt + RD) * 256);
+              acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], B0, acc[mt][0], 0, 0, 0);
+              acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], B1, acc[mt][1], 0, 0, 0);
+            });
+          }
         };
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SCHED == 1) {
@@ -319,11 +339,12 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
           // the decode is spread over the whole k-step in both waves)
           products();
           decode();
-          static_for<0, 16>([&](auto it_c) {
+          static_for<0, 2 * MF>([&](auto it_c) {
             constexpr int it = decltype(it_c)::value;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
-            if constexpr (it >= 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, MF == 8 ? 3 : 2, 0);  // VALU
+            if constexpr (NPRE > 0 ? it >= 8 : (it % 2 == 0 && it / 2 + 3 < MF))
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
           });
         } else if constexpr (PH == 0) {
           products();
@@ -341,13 +362,14 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
         b_own = nb4;
 #pragma unroll
         for (int q = 0; q < NPRE; ++q) a_cur[q] = a_nxt[q];
+        (void)as_n;
       };
       kstep(std::integral_constant<int, 0>{});
       kstep(std::integral_constant<int, 1>{});
       kstep(std::integral_constant<int, 2>{});
       kstep(std::integral_constant<int, 3>{});
       ts0 = ts1;
-      as_cur = as_cur + 4 >= ASLOTS ? as_cur + 4 - ASLOTS : as_cur + 4;
+      as_cur = (as_cur + 4) % ASLOTS;  // four k-steps per stage; ASLOTS may be 3
     }
   };
 
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
     // first part copied, later parts added in part order
     run_stages((int)((int64_t)(p_begin + 1) * KB / p.parts) - kb_begin, ph_c);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < MF; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         tot[mt][h] = acc[mt][h];
@@ -366,7 +388,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
     for (int part = p_begin + 1; part < p_end; ++part) {
       run_stages((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin, ph_c);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < MF; ++mt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           tot[mt][h] = tot[mt][h] + acc[mt][h];
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
         }
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < MF; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[mt][h] = tot[mt][h];
   } else {
@@ -390,30 +412,26 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   const int col_own = lane_col(wq, j, rh);
   const int col_par = lane_col(wq, j, rh ^ 1);
   if (p.slab_mode) {
-    float *__restrict__ sl = p.slabs + (int64_t)p_begin * M * N + nb * 128;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + rh * 128 + mt * 16 + 4 * g + i;
-        if (row < M) {
-          sl[(int64_t)row * N + col_own] = acc[mt][0][i];
-          sl[(int64_t)row * N + col_par] = acc[mt][1][i];
-        }
-      }
+    for (int mt = 0; mt < MF; ++mt) {
+      const int row0 = m0 + rh * RW + mt * 16 + 4 * g;
+      store_partial(p.slabs, p_begin, M, N, row0, nb * 128 + col_own, acc[mt][0]);
+      store_partial(p.slabs, p_begin, M, N, row0, nb * 128 + col_par, acc[mt][1]);
+    }
     return;
   }
 
   // output transform, 64 rows per pass through LDS
   float *z = reinterpret_cast<float *>(lds);
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+  constexpr int PPH = RW / 64;  // passes per row half
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = 0; pass < 2 * PPH; ++pass) {
     if (pass > 0) barrier_lds();
-    if (rh == (pass >> 1)) {
+    if (rh == pass / PPH) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int mt = 4 * (pass & 1) + q;
+        const int mt = 4 * (pass % PPH) + q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           z[(q * 16 + 4 * g + i) * Z_ROW + col_own] = acc[mt][0][i];
@@ -433,10 +451,18 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   }
 }
 
+// bm 256: 128-row waves (both fold modes); bm 512: 256-row waves, single
+// part per workgroup only (the host never asks for the fold there).
 template <int BITS, uint32_t CB>
-hipError_t launch_wide_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (multi) hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, true>), grid, dim3(512), 0, s, p);
-  else hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, false>), grid, dim3(512), 0, s, p);
+hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (bm == 256) {
+    if (multi) hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 128, true>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 128, false>), grid, dim3(512), 0, s, p);
+  } else if (bm == 512 && !multi) {
+    hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 256, false>), grid, dim3(512), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -109,24 +109,37 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
                   w->K / 128);
     pl.parts = force->parts;
   }
-  // Rows per tile: the measured best of the tile shapes at each M.
-  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  // Rows per tile: the smallest tile that holds M rows, up to 512 (the
+  // measured best at every layer shape and batch of the plan sweep).
+  pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 128 ? 128 : M <= 256 ? 256 : 512;
+  const bool bm_forced = force && force->bm > 0;
   if (force && force->bm > 0) {
-    if (force->bm != 16 && force->bm != 32 && force->bm != 64 && force->bm != 128 && force->bm != 256)
-      return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32, 64, 128 or 256", force->bm);
+    if (force->bm != 16 && force->bm != 32 && force->bm != 64 && force->bm != 128 && force->bm != 256 &&
+        force->bm != 512)
+      return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32, 64, 128, 256 or 512", force->bm);
     pl.bm = force->bm;
   }
-  // Separate fp32 partials while they are small enough to stay in cache;
-  // beyond that one workgroup runs all parts of its tile.
+  // Separate fp32 partials (one workgroup per part: P times the workgroups)
+  // while their traffic is small next to the GEMM's; beyond 192 MiB one
+  // workgroup runs all parts of its tile.
   const double slab_bytes = (double)pl.parts * (double)M * (double)w->N * 4.0;
-  pl.mode = (pl.parts > 1 && slab_bytes <= 64.0 * 1024 * 1024) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
+  pl.mode = (pl.parts > 1 && slab_bytes <= 192.0 * 1024 * 1024) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
   if (force && force->mode != EXL3_MODE_AUTO && force->mode >= 0) {
     if (force->mode != EXL3_MODE_FUSED && force->mode != EXL3_MODE_SLABS)
       return fail(EXL3_ERR_INVALID_ARG, "forced mode=%d, must be 0 (fused) or 1 (slabs)", force->mode);
     pl.mode = force->mode;
   }
   if (pl.parts == 1) pl.mode = EXL3_MODE_FUSED;  // one part: nothing to sum
-  pl.workspace = pl.mode == EXL3_MODE_SLABS ? (size_t)pl.parts * (size_t)M * (size_t)w->N * sizeof(float) : 0;
+  // a fused multi-part tile keeps two accumulator sets: at most 256 rows
+  if (!bm_forced && pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1) pl.bm = 256;
+  // 512-row tiles hold one accumulator set: one part per workgroup only
+  if (pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1)
+    return fail(EXL3_ERR_UNSUPPORTED, "bm=512 runs one K part per workgroup; %d parts need mode=slabs or bm<=256",
+                pl.parts);
+  // slab layout [parts][ceil(M/4)][N][4] fp32 (rows padded to a multiple of 4)
+  pl.workspace = pl.mode == EXL3_MODE_SLABS
+                     ? (size_t)pl.parts * (size_t)((M + 3) / 4) * 4 * (size_t)w->N * sizeof(float)
+                     : 0;
   *out = pl;
   return EXL3_OK;
 }

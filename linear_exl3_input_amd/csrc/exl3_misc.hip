@@ -64,7 +64,12 @@ hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t
 //
 // z = ((part0 + part1) + part2) + ... in fp32, then y = rne(svh * 2^-3 *
 // H128(z)) (TensorFold PR, "Arithmetic" step 3 and its ordered part sum).
-// One wave per (row, 128-column block).
+// The partials are stored [part][M/4][N][4] (rows padded to a multiple of 4):
+// the four rows of one column are 16 contiguous bytes, which is what a GEMM
+// lane holds for one output column, so both the GEMM's stores and these
+// loads move whole cache lines.  One wave per (4-row group, 128-column
+// block): lane l loads columns 2l and 2l+1 of the four rows, every part's
+// loads are in flight before the ordered adds, then four output rows.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t parts,
                                                        int32_t M, int32_t N, const uint16_t *__restrict__ svh,
@@ -72,23 +77,39 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nblocks = N >> 7;
-  if (item >= (int64_t)M * nblocks) return;
-  const int64_t m = item / nblocks;
-  const int n0 = (int)(item - m * nblocks) * 128;
-  const int64_t slab = (int64_t)M * N;
-  const float *src = slabs + m * N + n0 + 2 * lane;
-  float2 acc = *(const float2 *)src;
-  for (int p = 1; p < parts; ++p) {
-    const float2 v = *(const float2 *)(src + p * slab);
-    acc.x = acc.x + v.x;
-    acc.y = acc.y + v.y;
+  const int M4 = (M + 3) >> 2;
+  if (item >= (int64_t)M4 * nblocks) return;
+  const int64_t m4 = item / nblocks;
+  const int n0 = (int)(item - m4 * nblocks) * 128;
+  const int64_t slab = (int64_t)M4 * N * 4;
+  const float4_t *src = reinterpret_cast<const float4_t *>(slabs + (m4 * N + n0 + 2 * lane) * 4);
+  float4_t a0 = src[0], a1 = src[1];
+  constexpr int U = 8;
+  for (int p = 1; p < parts; p += U) {
+    float4_t v0[U], v1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (p + u < parts) {
+        v0[u] = src[(p + u) * slab / 4];
+        v1[u] = src[(p + u) * slab / 4 + 1];
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (p + u < parts) {
+        a0 = a0 + v0[u];
+        a1 = a1 + v1[u];
+      }
   }
-  output_row<OUT_BF16>(acc.x, acc.y, svh, y + m * N, n0, lane);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t m = 4 * m4 + r;
+    if (m < M) output_row<OUT_BF16>(a0[r], a1[r], svh, y + m * N, n0, lane);
+  }
 }
 
 hipError_t launch_epilogue(const float *slabs, int32_t parts, int32_t M, int32_t N, const uint16_t *svh,
                            void *y, bool out_bf16, hipStream_t s) {
-  const int64_t items = (int64_t)M * (N / 128);
+  const int64_t items = (int64_t)((M + 3) / 4) * (N / 128);
   const dim3 grid((unsigned)((items + 3) / 4));
   if (out_bf16)
     hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, parts, M, N, svh, (uint16_t *)y);

@@ -38,3 +38,13 @@ def rot_layout(x_rot_natural: np.ndarray) -> np.ndarray:
     S, M, K = a.shape
     v = a.reshape(S, M, K // 32, 8, 4)[..., [0, 2, 1, 3, 4, 6, 5, 7], :].reshape(S, M, K // 32, 32)
     return np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+
+
+def slab_layout(z: np.ndarray) -> np.ndarray:
+    """fp32 partials [P, M, N] -> the slab layout [P, ceil(M/4), N, 4]
+    (padding rows zero)."""
+    P, M, N = z.shape
+    M4 = (M + 3) // 4
+    pad = np.zeros((P, 4 * M4, N), dtype=z.dtype)
+    pad[:, :M] = z
+    return np.ascontiguousarray(pad.reshape(P, M4, 4, N).transpose(0, 1, 3, 2))

@@ -126,6 +126,22 @@ def test_plan_modes_and_workspace():
     assert small.parts == big.parts > 1
     assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == small.parts * 16 * 5120 * 4
     assert big.mode == ex.EXL3_MODE_FUSED and big.workspace == 0
-    assert small.bm == 16 and _plan(w, 24).bm == 32 and big.bm == 64
+    assert small.bm == 16 and _plan(w, 24).bm == 32 and big.bm == 256
+    mid = _plan(w, 512)  # 17 parts x 512 x 5120 x 4 B = 178 MB of partials: slabs of 512 rows
+    assert mid.mode == ex.EXL3_MODE_SLABS and mid.bm == 512
     head = view(4096, (154880,), 6, 2)
     assert _plan(head, 1).parts == 1 and _plan(head, 1).workspace == 0
+
+
+def test_forced_512_row_tile_needs_one_part_per_workgroup():
+    L = ex.load()
+    w = view(4096, (2048,), 4, 1)
+    fused_multi = ex._Plan(4, ex.EXL3_MODE_FUSED, 512, 0, 0)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(fused_multi)) == 0
+    assert "bm=512" in last_error()
+    slabs = ex._Plan(4, ex.EXL3_MODE_SLABS, 512, 0, 0)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(slabs)) == 4 * 600 * 2048 * 4
+    single = ex._Plan(1, ex.EXL3_MODE_AUTO, 512, 0, 0)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(single)) == 0
+    assert L.exl3_linear_ex(ctypes.byref(w), FAKE, 600, FAKE, 1, FAKE, 1 << 30, None,
+                            ctypes.byref(fused_multi)) == 2  # EXL3_ERR_UNSUPPORTED, before any launch

@@ -14,7 +14,7 @@ import workloads as wl
 from oracle import format as ofmt
 from oracle import linear as olin
 from oracle import transform as otf
-from gpu_util import banner, bits16, dev16, rot_layout, weight, x_dev
+from gpu_util import banner, bits16, dev16, rot_layout, slab_layout, weight, x_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +89,7 @@ def test_output_stage_bit_exact(out_dtype, P, M, N):
     suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
     w = ex.Exl3Weight(dev16(trellis), dev16(suh, torch.float16), dev16(svh, torch.float16), 4, "mcg", (N,))
     dt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
-    got = bits16(ex.debug_epilogue(w, torch.from_numpy(z).cuda(), dt))
+    got = bits16(ex.debug_epilogue(w, torch.from_numpy(slab_layout(z)).cuda(), M, dt))
     want = otf.output_transform_f32(otf.reduce_parts_f32(z), svh, out_dtype)
     assert np.array_equal(got, want)
     del lay
@@ -156,12 +156,29 @@ def test_schedules_agree_bit_for_bit(parts):
     t = wl.gen_all(lay)
     outs = {}
     for mode in (ex.EXL3_MODE_FUSED, ex.EXL3_MODE_SLABS):
-        for bm in (16, 32, 64, 128, 256):
+        for bm in (16, 32, 64, 128, 256, 512):
+            if bm == 512 and mode == ex.EXL3_MODE_FUSED and parts > 1:
+                continue  # one accumulator set per 512-row workgroup
             outs[(mode, bm)] = _run(t, parts=parts, mode=mode, bm=bm)
     first = next(iter(outs.values()))
     for key, y in outs.items():
         assert np.array_equal(y, first), f"schedule {key} differs"
     _check(t, first)
+
+
+@pytest.mark.parametrize("bits,cb", [(6, "mul1"), (5, "3inst"), (8, "mcg"), (3, "mul1")])
+@pytest.mark.parametrize("M", [300, 600])
+def test_large_tiles_ragged(bits, cb, M):
+    """The 256- and 512-row tiles on a ragged last tile: bit-identical to the
+    64-row tile, for one part and for slabs of two parts."""
+    banner(f"large tiles {bits}-bit {cb} M={M}")
+    lay = wl.small_layer("tall", 1024, (256,), bits, cb, (M,), seed=30 + bits)
+    t = wl.gen_all(lay)
+    for parts, mode in ((1, ex.EXL3_MODE_FUSED), (2, ex.EXL3_MODE_SLABS)):
+        ref = _run(t, parts=parts, mode=mode, bm=64)
+        for bm in (256, 512):
+            assert np.array_equal(_run(t, parts=parts, mode=mode, bm=bm), ref), f"bm={bm} parts={parts}"
+    _check(t, ref)
 
 
 # ---------------------------------------------------------------- invariants
