@@ -380,7 +380,7 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 
 // -------------------------------------------------------------- big GEMM
 //
-// For larger M: a BM = 16*MT row x 128 column tile (MT = 8 or 16) on 4 waves.
+// For M around 128: a BM = 16*MT row x 128 column tile (MT = 8) on 4 waves.
 // As in gemm_kernel, wave w decodes the B operands of n-tiles 2w and 2w+1 and
 // keeps them in registers, now against all BM rows, so each trellis value is
 // decoded once per BM rows and feeds 2*MT MFMAs per lane-set.  The rotated
