@@ -124,12 +124,15 @@ __device__ __forceinline__ uint32_t pair_sum2(uint32_t u0, uint32_t u1) {
 template <uint32_t CB>
 __device__ __forceinline__ uint32_t decode_pair(uint32_t s0, uint32_t s1) {
   if constexpr (CB == CB_MUL1) {
-    // 0x6400 + the sum of the hash's four bytes, by v_sad_u8 (sum of
-    // |byte - 0|).  v_dot4_u32_u8 computes the same but runs ~2x slower
-    // while another wave on the SIMD issues MFMAs.
-    const uint32_t d0 = __builtin_amdgcn_sad_u8(cb_hash<CB>(s0), 0u, 0x6400u);
-    const uint32_t d1 = __builtin_amdgcn_sad_u8(cb_hash<CB>(s1), 0u, 0x6400u);
-    const half2_t h = __builtin_bit_cast(half2_t, d0 | (d1 << 16));
+    // 0x6400 + the sum of the hash's four bytes, for both states, packed as
+    // two fp16 bit patterns: v_sad_u8 adds the byte sum of state 0 (sum of
+    // |byte - 0|, at most 1020, so no carry leaves the low half) and
+    // v_sad_hi_u8 adds the byte sum of state 1 shifted into the high half.
+    // (v_dot4_u32_u8 computes the same sums but runs ~2x slower while
+    // another wave on the SIMD issues MFMAs.)
+    const uint32_t d0 = __builtin_amdgcn_sad_u8(cb_hash<CB>(s0), 0u, 0x64006400u);
+    const uint32_t d01 = __builtin_amdgcn_sad_hi_u8(cb_hash<CB>(s1), 0u, d0);
+    const half2_t h = __builtin_bit_cast(half2_t, d01);
     const half2_t alpha = {__builtin_bit_cast(_Float16, (uint16_t)0x1EEE),
                            __builtin_bit_cast(_Float16, (uint16_t)0x1EEE)};
     const half2_t c = {__builtin_bit_cast(_Float16, (uint16_t)0xC931),

@@ -112,31 +112,6 @@ __device__ __forceinline__ void store_trellis_stage(const u32x4_t (&treg)[Geom<B
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void load_a_stage(u32x4_t (&areg)[MT], const uint16_t *__restrict__ xs,
-                                             int kb, int m0, int M, int K, int tid) {
-#pragma unroll
-  for (int it = 0; it < MT; ++it) {
-    const int c = tid + WG_THREADS * it;
-    const int row = c >> 4;
-    const int q = c & 15;
-    const int m = m0 + row;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    // x~ is in k-step tiles: k-step 4kb + q/4 of row m, 16-byte chunk q%4
-    if (m < M) v = *(const u32x4_t *)(xs + ((int64_t)(4 * kb + (q >> 2)) * M + m) * 32 + (q & 3) * 8);
-    areg[it] = v;
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void store_a_stage(const u32x4_t (&areg)[MT], uint32_t *__restrict__ ab, int tid) {
-#pragma unroll
-  for (int it = 0; it < MT; ++it) {
-    const int c = tid + WG_THREADS * it;
-    *(u32x4_t *)(ab + (c >> 4) * A_ROW_DW + (c & 15) * 4) = areg[it];
-  }
-}
-
 // ----------------------------------------------------------------- decode
 
 template <int D, int NY>
@@ -219,6 +194,111 @@ __device__ __forceinline__ int lane_col(int wave, int j, int h) {
   return 16 * (2 * wave + (j >> 3)) + (j & 7) + 8 * h;
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations.
+// __syncthreads() also drains every outstanding global load (the release
+// fence of the memory model), which would cancel the direct-to-LDS prefetch
+// that is meant to stay in flight across barriers; completion of those loads
+// is tracked explicitly with wait_vmcnt.
+// The wait is the builtin (s_waitcnt lgkmcnt(0), encoding 0xC07F) so the
+// compiler's own wait insertion knows LDS results are in after it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ------------------------------------------------------------ raw tiles
+//
+// Trellis tiles loaded straight to LDS (global_load_lds_dwordx4) are stored
+// raw: the 16-bit words as in memory, so each dword holds two stream words in
+// swapped order.  Each tile gets one 16-byte pad chunk on each side (its last
+// chunk before it, its first chunk after it), so no lane's window wraps.  A
+// stage (128 k x 128 columns = 8 x 8 tiles, tile t = 8*ktile + ntile) is
+// 64 * (2*BITS + 2) chunks.
+
+template <int BITS>
+struct RawGeom {
+  static constexpr int TSTRIDE = 8 * BITS + 8;          // dwords per padded tile
+  static constexpr int T_CHUNKS = 64 * (2 * BITS + 2);  // 16-byte chunks per padded stage
+  static constexpr int TSLOT_DW = T_CHUNKS * 4;
+  static constexpr int NY = Geom<BITS>::NY;
+  static constexpr int NX = Geom<BITS>::NX;
+  static constexpr bool PERM = BITS % 2 == 0;
+};
+
+// Source offset (16-bit words from the stage's first tile) of padded chunk
+// q of a stage; q past the stage (surplus lanes of the last load) reads a
+// chunk of tile 0 that lands in a scratch area.
+template <int BITS>
+__device__ __forceinline__ uint32_t raw_chunk_src(int q, int NT) {
+  constexpr int TC = 2 * BITS + 2;
+  if (q >= 64 * TC) return (uint32_t)((q % (2 * BITS)) * 8);
+  const int t = q / TC;
+  const int c = q - t * TC;
+  const int sc = c == 0 ? 2 * BITS - 1 : (c == 2 * BITS + 1 ? 0 : c - 1);
+  return (uint32_t)(((t >> 3) * NT + (t & 7)) * (16 * BITS) + sc * 8);
+}
+
+// Window of the lane's 8 states for even widths: start dword (after the
+// front pad) and the v_perm_b32 selector that turns raw dwords d, d+1 into
+// the 32 stream bits starting at the lane's (byte-aligned) first bit.
+// Stream byte t of a raw dword is its little-endian byte (1, 0, 3, 2)[t].
+template <int BITS>
+__device__ __forceinline__ void lane_window_perm(int j, int g, int h, int &doff, uint32_t &sel) {
+  const int v0 = 32 * (j & 7) + 4 * h + 16 * (g & 1);
+  const int o = v0 * BITS;
+  doff = 4 + (o >> 5);
+  const int r = (o >> 3) & 3;
+  sel = r == 0 ? 0x01000302u : r == 1 ? 0x00030205u : r == 2 ? 0x03020504u : 0x02050407u;
+}
+
+// Per-lane window constants for half h: start dword, perm selector (even
+// widths) or alignbit shift (odd widths: each dword is rotated by 16 first).
+template <int BITS>
+__device__ __forceinline__ void raw_lane_window(int j, int g, int h, int &doff, uint32_t &sel, int &sh) {
+  sel = 0;
+  sh = 0;
+  if constexpr (RawGeom<BITS>::PERM) lane_window_perm<BITS>(j, g, h, doff, sel);
+  else lane_window<BITS>(j, g, h, doff, sh);
+}
+
+template <int BITS>
+__device__ __forceinline__ void raw_normalize(const uint32_t (&X)[Geom<BITS>::NX], uint32_t sel, int sh,
+                                              uint32_t (&Y)[Geom<BITS>::NY]) {
+  using R = RawGeom<BITS>;
+  if constexpr (R::PERM) {
+#pragma unroll
+    for (int i = 0; i < R::NY; ++i) Y[i] = __builtin_amdgcn_perm(X[i + 1], X[i], sel);
+  } else {
+    uint32_t Z[R::NX];
+#pragma unroll
+    for (int i = 0; i < R::NX; ++i) Z[i] = rot16(X[i]);
+#pragma unroll
+    for (int i = 0; i < R::NY; ++i) Y[i] = __builtin_amdgcn_alignbit(Z[i], Z[i + 1], sh);
+  }
+}
+
+// The lane's 8 values of one B operand from a raw tile (tp = tile start +
+// doff in LDS).
+template <int BITS, uint32_t CB>
+__device__ __forceinline__ u32x4_t raw_decode_frag(const uint32_t *__restrict__ tp, uint32_t sel, int sh) {
+  uint32_t X[Geom<BITS>::NX], Y[Geom<BITS>::NY];
+#pragma unroll
+  for (int i = 0; i < Geom<BITS>::NX; ++i) X[i] = tp[i];
+  raw_normalize<BITS>(X, sel, sh, Y);
+  return u32x4_t{frag_pair<BITS, CB, 0>(Y), frag_pair<BITS, CB, 1>(Y), frag_pair<BITS, CB, 2>(Y),
+                 frag_pair<BITS, CB, 3>(Y)};
+}
+
+// ------------------------------------------------------------------- GEMM
+
 // One accumulator of a lane (rows row0 .. row0+3 of column col; row0 is a
 // multiple of 4) into the fp32 partial of K part `part`.  Partials are laid
 // out [part][M/4][N][4] (rows padded to a multiple of 4, padding rows hold
@@ -232,21 +312,32 @@ __device__ __forceinline__ void store_partial(float *__restrict__ slabs, int par
   }
 }
 
-// ------------------------------------------------------------------- GEMM
-
+// BM = 16*MT rows (16, 32, 64) x 128 columns on 4 waves; wave w decodes
+// n-tiles 2w, 2w+1 (both column halves) and multiplies them against all BM
+// rows.  Both operands arrive by direct loads to LDS into two stage slots
+// (raw trellis tiles, and x~ in its k-step tile layout, 4 k-steps x BM rows
+// x 64 B per stage); the first two stages are issued together, so a short
+// workgroup (two stages at the larger part counts) waits for memory once.
+// Barriers wait only for LDS operations; the loads are waited for by count.
+// Rows past M load row M-1 (finite, never stored).
 template <int BITS, uint32_t CB, int MT, bool MULTI>
 __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
-  using G = Geom<BITS>;
+  using R = RawGeom<BITS>;
   constexpr int BM = 16 * MT;
-  constexpr int STAGE_A_DW = BM * A_ROW_DW;
-  constexpr int STAGE_DW = G::STAGE_T_DW + STAGE_A_DW;
+  constexpr int T_OPS = (R::T_CHUNKS + WG_THREADS - 1) / WG_THREADS;  // trellis loads per wave per stage
+  constexpr int JUNK = T_OPS * WG_THREADS - R::T_CHUNKS;
+  constexpr int A_SLOT_DW = BM * 64;                                  // x~: 4 k-steps x BM rows x 64 B
+  constexpr int SLOT_DW = R::TSLOT_DW + A_SLOT_DW;
+  constexpr int OPS = T_OPS + MT;                                     // loads per wave per stage
+  constexpr int MAIN_DW = 2 * SLOT_DW + JUNK * 4;
   constexpr int Z_DW = BM * Z_ROW;
-  constexpr int LDS_DW = (2 * STAGE_DW > Z_DW) ? 2 * STAGE_DW : Z_DW;
+  constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
+  static_assert(R::T_CHUNKS % 64 == 0, "each direct load lands whole in a slot or in the surplus area");
   __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
+  uint32_t *const junk = lds + 2 * SLOT_DW;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
   const int g = lane >> 4;
   const int nb = blockIdx.x;
@@ -262,18 +353,50 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
   }
   const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
   const int kb_end = (int)((int64_t)p_end * KB / p.parts);
+  const int nst = kb_end - kb_begin;
 
   int shard = 0;
   while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
   const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
 
-  int xoff0, sh0, xoff1, sh1;
-  lane_window<BITS>(j, g, 0, xoff0, sh0);
-  lane_window<BITS>(j, g, 1, xoff1, sh1);
-  const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
+  // load sources: 16-bit word offsets from the stage bases
+  const uint16_t *const t_base = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8) * (16 * BITS);
+  const int64_t t_stage = (int64_t)8 * NT * (16 * BITS);
+  uint32_t t_src[T_OPS];
+#pragma unroll
+  for (int r = 0; r < T_OPS; ++r) t_src[r] = raw_chunk_src<BITS>(r * WG_THREADS + wave * 64 + lane, NT);
+  const uint16_t *const a_base = xs + (int64_t)kb_begin * 4 * M * 32;
+  const int64_t a_stage = (int64_t)4 * M * 32;
+  uint32_t a_src[MT];
+#pragma unroll
+  for (int r = 0; r < MT; ++r) {
+    const int c = r * WG_THREADS + wave * 64 + lane;  // chunk: k-step c/(4BM), row (c/4)%BM, 16 B piece c%4
+    int row = m0 + (c >> 2) % BM;
+    row = row < M ? row : M - 1;
+    a_src[r] = (uint32_t)(((c / (4 * BM)) * M + row) * 32 + (c & 3) * 8);
+  }
+  auto issue_stage = [&](int stage, int slot) __attribute__((always_inline)) {
+    const int st = min(stage, nst - 1);
+    uint32_t *const ts = lds + slot * SLOT_DW;
+#pragma unroll
+    for (int r = 0; r < T_OPS; ++r) {
+      const int q0 = r * WG_THREADS + wave * 64;
+      uint32_t *dst = q0 < R::T_CHUNKS ? ts + q0 * 4 : junk + (q0 - R::T_CHUNKS) * 4;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(t_base + st * t_stage + t_src[r]),
+                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a_base + st * a_stage + a_src[r]),
+                                       (__attribute__((address_space(3))) void *)(ts + R::TSLOT_DW + (r * WG_THREADS + wave * 64) * 4),
+                                       16, 0, 0);
+  };
 
-  u32x4_t treg[G::T_ITERS];
-  u32x4_t areg[MT];
+  int doff0, sh0, doff1, sh1;
+  uint32_t sel0, sel1;
+  raw_lane_window<BITS>(j, g, 0, doff0, sel0, sh0);
+  raw_lane_window<BITS>(j, g, 1, doff1, sel1, sh1);
+  const int tile_lane = ((g >> 1) * WG_NT + 2 * wave + (j >> 3)) * R::TSTRIDE;
 
   float4_t acc[MT][2];
   float4_t tot[MULTI ? MT : 1][2];
@@ -282,70 +405,66 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  int part = p_begin;
-  int part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+  issue_stage(0, 0);
+  issue_stage(1, 1);
+  wait_vmcnt<OPS>();  // stage 0 landed (stage 1's loads were issued after it)
+  barrier_lds();
 
-  load_trellis_stage<BITS>(treg, p.trellis, kb_begin, nb, NT, tid);
-  load_a_stage<MT>(areg, xs, kb_begin, m0, M, K, tid);
-  store_trellis_stage<BITS>(treg, lds, tid);
-  store_a_stage<MT>(areg, lds + G::STAGE_T_DW, tid);
-  if (kb_begin + 1 < kb_end) {
-    load_trellis_stage<BITS>(treg, p.trellis, kb_begin + 1, nb, NT, tid);
-    load_a_stage<MT>(areg, xs, kb_begin + 1, m0, M, K, tid);
-  }
-
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const int buf = (kb - kb_begin) & 1;
-    __syncthreads();
-    if (kb + 1 < kb_end) {
-      uint32_t *nxt = lds + (buf ^ 1) * STAGE_DW;
-      store_trellis_stage<BITS>(treg, nxt, tid);
-      store_a_stage<MT>(areg, nxt + G::STAGE_T_DW, tid);
-      if (kb + 2 < kb_end) {
-        load_trellis_stage<BITS>(treg, p.trellis, kb + 2, nb, NT, tid);
-        load_a_stage<MT>(areg, xs, kb + 2, m0, M, K, tid);
-      }
-    }
-    const uint32_t *tb = lds + buf * STAGE_DW;
-    const uint32_t *ab = tb + G::STAGE_T_DW;
+  int s = 0;
+  auto run_stages = [&](int s_end) __attribute__((always_inline)) {
+    for (; s < s_end; ++s) {
+      const uint32_t *const tb = lds + (s & 1) * SLOT_DW;
+      const uint32_t *const ab = tb + R::TSLOT_DW + 16 * j + 4 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      half8_t a[MT];
+      for (int ks = 0; ks < 4; ++ks) {
+        half8_t a[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)  // x~ is in fragment order: 16 contiguous bytes
-        a[mt] = *(const half8_t *)(ab + (mt * 16 + j) * A_ROW_DW + 16 * ks + 4 * g);
-      const uint32_t *tp = tb + (tile_lane + 2 * WG_NT * ks) * G::STRIDE;
-      const half8_t b0 = decode_frag<BITS, CB>(tp, xoff0, sh0);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b0, acc[mt][0], 0, 0, 0);
-      const half8_t b1 = decode_frag<BITS, CB>(tp, xoff1, sh1);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b1, acc[mt][1], 0, 0, 0);
-    }
-    if constexpr (MULTI) {
-      if (kb + 1 == part_end_kb) {
+        for (int mt = 0; mt < MT; ++mt) a[mt] = *(const half8_t *)(ab + (ks * BM + mt * 16) * 16);
+        const uint32_t *tp = tb + tile_lane + 2 * WG_NT * ks * R::TSTRIDE;
+        const half8_t b0 = __builtin_bit_cast(half8_t, raw_decode_frag<BITS, CB>(tp + doff0, sel0, sh0));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
+          acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b0, acc[mt][0], 0, 0, 0);
+        const half8_t b1 = __builtin_bit_cast(half8_t, raw_decode_frag<BITS, CB>(tp + doff1, sel1, sh1));
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            if (part == p_begin) tot[mt][h] = acc[mt][h];
-            else tot[mt][h] = tot[mt][h] + acc[mt][h];
-            acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        ++part;
-        part_end_kb = (int)((int64_t)(part + 1) * KB / p.parts);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b1, acc[mt][1], 0, 0, 0);
       }
+      barrier_lds();           // every wave is done with slot s&1
+      issue_stage(s + 2, s & 1);
+      wait_vmcnt<OPS>();       // stage s+1 landed
+      barrier_lds();
     }
-  }
+  };
 
   if constexpr (MULTI) {
+    // first part copied, later parts added in part order
+    run_stages((int)((int64_t)(p_begin + 1) * KB / p.parts) - kb_begin);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        tot[mt][h] = acc[mt][h];
+        acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    for (int part = p_begin + 1; part < p_end; ++part) {
+      run_stages((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          tot[mt][h] = tot[mt][h] + acc[mt][h];
+          acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[mt][h] = tot[mt][h];
+  } else {
+    run_stages(nst);
   }
+  wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
 
   if (p.slab_mode) {
 #pragma unroll
@@ -356,7 +475,7 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
     return;
   }
 
-  __syncthreads();  // every wave is done with the stage buffers
+  barrier_lds();  // every wave is done with the stage slots
   float *z = reinterpret_cast<float *>(lds);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -366,7 +485,7 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[(mt * 16 + 4 * g + i) * Z_ROW + col] = acc[mt][h][i];
     }
-  __syncthreads();
+  barrier_lds();
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
   for (int r = wave; r < BM; r += 4) {
     const int row = m0 + r;
@@ -391,26 +510,6 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 // ds_read_b128 per lane.  The decode of k-step i+1 is interleaved with the
 // MFMAs of k-step i.  Rows past M load row M-1 (finite, discarded).  Same
 // k slots, k-step order, parts and part fold as gemm_kernel: same bits.
-
-// Workgroup barrier that waits only for this wave's LDS operations.
-// __syncthreads() also drains every outstanding global load (the release
-// fence of the memory model), which would cancel the direct-to-LDS prefetch
-// that is meant to stay in flight across barriers; completion of those loads
-// is tracked explicitly with wait_vmcnt.
-// The wait is the builtin (s_waitcnt lgkmcnt(0), encoding 0xC07F) so the
-// compiler's own wait insertion knows LDS results are in after it.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int MT>
 __device__ __forceinline__ void issue_a_dma(uint32_t *__restrict__ slot, const uint16_t *__restrict__ xs, int m0,

@@ -88,35 +88,6 @@ struct Wide {
   }
 };
 
-// Window of the lane's 8 states for even widths: start dword (after the
-// front pad) and the v_perm_b32 selector that turns raw dwords d, d+1 into
-// the 32 stream bits starting at the lane's (byte-aligned) first bit.
-// Stream byte t of a raw dword is its little-endian byte (1, 0, 3, 2)[t].
-template <int BITS>
-__device__ __forceinline__ void lane_window_perm(int j, int g, int h, int &doff, uint32_t &sel) {
-  const int v0 = 32 * (j & 7) + 4 * h + 16 * (g & 1);
-  const int o = v0 * BITS;
-  doff = 4 + (o >> 5);
-  const int r = (o >> 3) & 3;
-  sel = r == 0 ? 0x01000302u : r == 1 ? 0x00030205u : r == 2 ? 0x03020504u : 0x02050407u;
-}
-
-template <int BITS>
-__device__ __forceinline__ void wide_normalize(const uint32_t (&X)[Geom<BITS>::NX], uint32_t sel, int sh,
-                                               uint32_t (&Y)[Geom<BITS>::NY]) {
-  using W = Wide<BITS, 128>;
-  if constexpr (W::PERM) {
-#pragma unroll
-    for (int i = 0; i < W::NY; ++i) Y[i] = __builtin_amdgcn_perm(X[i + 1], X[i], sel);
-  } else {
-    uint32_t Z[W::NX];
-#pragma unroll
-    for (int i = 0; i < W::NX; ++i) Z[i] = rot16(X[i]);
-#pragma unroll
-    for (int i = 0; i < W::NY; ++i) Y[i] = __builtin_amdgcn_alignbit(Z[i], Z[i + 1], sh);
-  }
-}
-
 template <int BITS, uint32_t CB, int RW, bool MULTI, int SCHED = 1>
 __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   using W = Wide<BITS, RW>;
@@ -230,7 +201,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
     uint32_t X[W::NX], Y[W::NY];
 #pragma unroll
     for (int i = 0; i < W::NX; ++i) X[i] = tp[i];
-    wide_normalize<BITS>(X, sel, sh, Y);
+    raw_normalize<BITS>(X, sel, sh, Y);
     return u32x4_t{frag_pair<BITS, CB, 0>(Y), frag_pair<BITS, CB, 1>(Y), frag_pair<BITS, CB, 2>(Y),
                    frag_pair<BITS, CB, 3>(Y)};
   };
@@ -297,7 +268,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
         }
         u32x4_t nb4;
         auto decode = [&]() __attribute__((always_inline)) {
-          wide_normalize<BITS>(X, sel, sh, Y);
+          raw_normalize<BITS>(X, sel, sh, Y);
           nb4[0] = frag_pair<BITS, CB, 0>(Y);
           nb4[1] = frag_pair<BITS, CB, 1>(Y);
           nb4[2] = frag_pair<BITS, CB, 2>(Y);
