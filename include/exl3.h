@@ -46,7 +46,7 @@ extern "C" {
 #endif
 
 #define EXL3_MAX_SHARDS 16
-#define EXL3_ABI_VERSION 1
+#define EXL3_ABI_VERSION 2
 
 typedef enum {
   EXL3_OK = 0,
@@ -89,13 +89,31 @@ typedef enum {
                           parts in order and applies the output transform   */
 } exl3_mode;
 
+/* How weights are decoded.  Both decoders produce the same fp16 values
+ * (the table is filled by the ALU decoder) and run the same MFMA chains. */
+typedef enum {
+  EXL3_DECODER_AUTO = -1,
+  EXL3_DECODER_ALU = 0,  /* tile kernels (bm rows per workgroup): every
+                            weight decoded by vector ALU instructions        */
+  EXL3_DECODER_TABLE = 1 /* M <= 16 only: one persistent 1024-thread
+                            workgroup per CU fills a 65,536-entry state ->
+                            fp16 table in LDS and decodes half of the
+                            weights through it, the rest by the ALU          */
+} exl3_decoder;
+
 typedef struct exl3_plan {
   int32_t parts;       /* P >= 1 K parts                                     */
   int32_t mode;        /* exl3_mode                                          */
   int32_t bm;          /* rows per M-tile: 16, 32, 64, 128, 256 or 512;
                           512 only with one part per workgroup (parts == 1
-                          or slab mode), else EXL3_ERR_UNSUPPORTED          */
-  int32_t reserved;
+                          or slab mode), else EXL3_ERR_UNSUPPORTED.  The
+                          table decoder reports 16                         */
+  int32_t decoder;     /* exl3_decoder.  Automatic: TABLE for M <= 16 on
+                          layers of at least 2^25 weights and at most
+                          2 GiB of trellis, else ALU.  In a
+                          forced plan 0 means ALU; TABLE with M > 16 is
+                          EXL3_ERR_UNSUPPORTED; forcing bm alone selects
+                          ALU                                               */
   size_t workspace;    /* bytes of workspace this plan needs                 */
 } exl3_plan;
 
@@ -149,8 +167,8 @@ exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, 
 exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan);
 
 /* exl3_linear with parts of the plan forced (HOST `force`; a field < 0, or
- * EXL3_MODE_AUTO, keeps the automatic choice).  Forcing `mode` or `bm` never
- * changes the output bits; forcing `parts` changes the K summation structure
+ * EXL3_MODE_AUTO / EXL3_DECODER_AUTO, keeps the automatic choice).  Forcing
+ * `mode`, `bm` or `decoder` never changes the output bits; forcing `parts` changes the K summation structure
  * and therefore the bits (for tests and measurement). */
 exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y,
                            int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream,

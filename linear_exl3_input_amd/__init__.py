@@ -39,6 +39,7 @@ _F16, _BF16 = 0, 1
 MAX_SHARDS = 16
 
 EXL3_MODE_AUTO, EXL3_MODE_FUSED, EXL3_MODE_SLABS = -1, 0, 1
+EXL3_DECODER_AUTO, EXL3_DECODER_ALU, EXL3_DECODER_TABLE = -1, 0, 1
 
 
 class Exl3Error(RuntimeError):
@@ -57,7 +58,7 @@ class _Weight(ctypes.Structure):
 
 class _Plan(ctypes.Structure):
     _fields_ = [("parts", ctypes.c_int32), ("mode", ctypes.c_int32), ("bm", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
+                ("decoder", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
 
 
 _lib = None
@@ -99,7 +100,7 @@ def load() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
-        if L.exl3_abi_version() != 1:
+        if L.exl3_abi_version() != 2:
             raise RuntimeError("libexl3.so ABI version mismatch")
         _lib = L
         return L
@@ -187,14 +188,15 @@ def _workspace(nbytes: int, device: torch.device) -> Tuple[int, int]:
     return ws.data_ptr(), ws.numel()
 
 
-def _force(parts=None, mode=None, bm=None) -> Optional[_Plan]:
-    if parts is None and mode is None and bm is None:
+def _force(parts=None, mode=None, bm=None, decoder=None) -> Optional[_Plan]:
+    if parts is None and mode is None and bm is None and decoder is None:
         return None
-    return _Plan(parts if parts else -1, EXL3_MODE_AUTO if mode is None else mode, bm if bm else -1, 0, 0)
+    return _Plan(parts if parts else -1, EXL3_MODE_AUTO if mode is None else mode, bm if bm else -1,
+                 EXL3_DECODER_AUTO if decoder is None else decoder, 0)
 
 
-def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None) -> int:
-    f = _force(parts, mode, bm)
+def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decoder=None) -> int:
+    f = _force(parts, mode, bm, decoder)
     L = load()
     n = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     err = L.exl3_last_error().decode()
@@ -206,7 +208,7 @@ def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None) -> in
 def plan(w: Exl3Weight, M: int) -> dict:
     p = _Plan()
     _check(load().exl3_plan_query(ctypes.byref(w.view()), M, ctypes.byref(p)))
-    return {"parts": p.parts, "mode": p.mode, "bm": p.bm, "workspace": p.workspace}
+    return {"parts": p.parts, "mode": p.mode, "bm": p.bm, "decoder": p.decoder, "workspace": p.workspace}
 
 
 def rot_shape(n_shards: int, M: int, K: int) -> tuple:
@@ -238,7 +240,8 @@ def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tens
 
 
 def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
-           out: Optional[torch.Tensor] = None, parts=None, mode=None, bm=None) -> torch.Tensor:
+           out: Optional[torch.Tensor] = None, parts=None, mode=None, bm=None,
+           decoder=None) -> torch.Tensor:
     """z = x_rot . W_q per shard, then the output transform: -> y [M, N]."""
     if x_rot.dim() != 4 or x_rot.shape[3] != 32:
         raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
@@ -250,7 +253,7 @@ def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bf
         raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
     if out is None:
         out = torch.empty((M, w.N), dtype=out_dtype, device=x_rot.device)
-    f = _force(parts, mode, bm)
+    f = _force(parts, mode, bm, decoder)
     L = load()
     need = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     ws, wsn = _workspace(need, x_rot.device)

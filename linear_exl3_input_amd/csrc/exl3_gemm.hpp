@@ -825,6 +825,9 @@ hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
                               hipStream_t s) {                                                     \
     return launch_gemm_bits<B>(cb, bm, multi, p, grid, s);                                         \
   }                                                                                                \
+  hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s) {             \
+    return launch_table_bits<B>(cb, p, grid, s);                                                   \
+  }                                                                                                \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s) {              \
     return launch_decode_bits<B>(cb, p, s);                                                        \
   }                                                                                                \

@@ -97,8 +97,16 @@ struct Plan {
   int32_t parts;
   int32_t mode;
   int32_t bm;
+  int32_t decoder;
   size_t workspace;
 };
+
+// The table decoder pays a fixed cost per CU (filling a 65,536-entry table)
+// that the layer's weights have to amortize.
+constexpr double TABLE_MIN_WEIGHTS = 33554432.0;  // 2^25
+constexpr int32_t TABLE_MAX_M = 16;
+// The table kernel addresses the trellis with 32-bit byte offsets.
+constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
 
 exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out) {
   Plan pl;
@@ -113,6 +121,22 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   // measured best at every layer shape and batch of the plan sweep).
   pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 128 ? 128 : M <= 256 ? 256 : 512;
   const bool bm_forced = force && force->bm > 0;
+  const double weights = (double)w->K * (double)w->N;
+  const bool table_fits = weights * w->bits / 8.0 <= TABLE_MAX_TRELLIS_BYTES;
+  pl.decoder = (M <= TABLE_MAX_M && weights >= TABLE_MIN_WEIGHTS && table_fits) ? EXL3_DECODER_TABLE
+                                                                                : EXL3_DECODER_ALU;
+  if (bm_forced) pl.decoder = EXL3_DECODER_ALU;
+  if (force && force->decoder >= 0) {
+    if (force->decoder != EXL3_DECODER_ALU && force->decoder != EXL3_DECODER_TABLE)
+      return fail(EXL3_ERR_INVALID_ARG, "forced decoder=%d, must be 0 (alu) or 1 (table)", force->decoder);
+    if (force->decoder == EXL3_DECODER_TABLE && M > TABLE_MAX_M)
+      return fail(EXL3_ERR_UNSUPPORTED, "the table decoder takes at most %d rows; M=%d (over by %d)", TABLE_MAX_M,
+                  M, M - TABLE_MAX_M);
+    if (force->decoder == EXL3_DECODER_TABLE && !table_fits)
+      return fail(EXL3_ERR_UNSUPPORTED, "the table decoder reads at most %.0f trellis bytes; this weight has %.0f",
+                  TABLE_MAX_TRELLIS_BYTES, weights * w->bits / 8.0);
+    pl.decoder = force->decoder;
+  }
   if (force && force->bm > 0) {
     if (force->bm != 16 && force->bm != 32 && force->bm != 64 && force->bm != 128 && force->bm != 256 &&
         force->bm != 512)
@@ -130,6 +154,7 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
     pl.mode = force->mode;
   }
   if (pl.parts == 1) pl.mode = EXL3_MODE_FUSED;  // one part: nothing to sum
+  if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = 16;
   // a fused multi-part tile keeps two accumulator sets: at most 256 rows
   if (!bm_forced && pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1) pl.bm = 256;
   // 512-row tiles hold one accumulator set: one part per workgroup only
@@ -142,6 +167,25 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
                      : 0;
   *out = pl;
   return EXL3_OK;
+}
+
+// Compute units of the current device (queried once per device).
+hipError_t device_cus(int *out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return hipSuccess;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return hipSuccess;
 }
 
 exl3_status launch_error(hipError_t e, const char *what) {
@@ -214,7 +258,7 @@ exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan) {
   plan->parts = pl.parts;
   plan->mode = pl.mode;
   plan->bm = pl.bm;
-  plan->reserved = 0;
+  plan->decoder = pl.decoder;
   plan->workspace = pl.workspace;
   return EXL3_OK;
 }
@@ -260,11 +304,21 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     end += w->shard_n[s] / 128;
     p.shard_end_blk[s] = end;
   }
-  const dim3 grid((unsigned)(w->N / 128), (unsigned)(p.slab_mode ? pl.parts : 1),
-                  (unsigned)((M + pl.bm - 1) / pl.bm));
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, !p.slab_mode && pl.parts > 1, p, grid, s);
-  if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
+  hipError_t e;
+  if (pl.decoder == EXL3_DECODER_TABLE) {
+    int cus = 0;
+    if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
+    const int64_t units = (int64_t)(w->N / 128) * (p.slab_mode ? pl.parts : 1);
+    const int grid = (int)std::min<int64_t>(cus, (units + 3) / 4);
+    e = exl3::launch_gemm_table(w->bits, w->codebook, p, grid, s);
+    if (e != hipSuccess) return launch_error(e, "table GEMM launch");
+  } else {
+    const dim3 grid((unsigned)(w->N / 128), (unsigned)(p.slab_mode ? pl.parts : 1),
+                    (unsigned)((M + pl.bm - 1) / pl.bm));
+    e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, !p.slab_mode && pl.parts > 1, p, grid, s);
+    if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
+  }
   if (p.slab_mode) {
     e = exl3::launch_epilogue(p.slabs, pl.parts, M, w->N, w->svh, y, p.out_bf16 != 0, s);
     if (e != hipSuccess) return launch_error(e, "part-sum epilogue launch");

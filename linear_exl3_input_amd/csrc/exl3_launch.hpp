@@ -31,11 +31,14 @@ struct DecodeParams {
 
 // Launchers (one per bit width; codebook and rows-per-tile bm are runtime
 // choices that select a template instance: bm 16/32/64 -> gemm_kernel,
-// 128/256 -> gemm_big_kernel).  Return hipSuccess or the
+// 128 -> gemm_big_kernel, 256/512 -> gemm_wide_kernel).  Return hipSuccess or the
 // launch error.
 hipError_t launch_gemm(int bits, int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid,
                        hipStream_t s);
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s);
+// Table-decode GEMM (M <= 16): `grid` persistent workgroups of 1024 threads,
+// one per CU; fused (parts folded in order) or slab mode as in p.
+hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hipStream_t s);
 
 hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
                                   int32_t n_shards, uint16_t *x_rot, hipStream_t s);
@@ -47,7 +50,8 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
 #define EXL3_DECLARE_BITS(B)                                                                  \
   hipError_t launch_gemm_b##B(int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid, \
                               hipStream_t s);                                                  \
-  hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);
+  hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);            \
+  hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s);
 EXL3_DECLARE_BITS(1)
 EXL3_DECLARE_BITS(2)
 EXL3_DECLARE_BITS(3)

@@ -154,6 +154,20 @@ hipError_t launch_gemm(int bits, int cb, int bm, bool multi, const GemmParams &p
   }
 }
 
+hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_table_b1(cb, p, grid, s);
+    case 2: return launch_table_b2(cb, p, grid, s);
+    case 3: return launch_table_b3(cb, p, grid, s);
+    case 4: return launch_table_b4(cb, p, grid, s);
+    case 5: return launch_table_b5(cb, p, grid, s);
+    case 6: return launch_table_b6(cb, p, grid, s);
+    case 7: return launch_table_b7(cb, p, grid, s);
+    case 8: return launch_table_b8(cb, p, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s) {
   switch (bits) {
     case 1: return launch_debug_decode_b1(cb, p, s);

@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(L, name), name
-    assert L.exl3_abi_version() == 1
+    assert L.exl3_abi_version() == 2
 
 
 def test_status_strings():
@@ -145,3 +145,28 @@ def test_forced_512_row_tile_needs_one_part_per_workgroup():
     assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(single)) == 0
     assert L.exl3_linear_ex(ctypes.byref(w), FAKE, 600, FAKE, 1, FAKE, 1 << 30, None,
                             ctypes.byref(fused_multi)) == 2  # EXL3_ERR_UNSUPPORTED, before any launch
+
+
+def test_table_decoder_choice_and_limits():
+    """M <= 16 on layers of 2^25 weights or more: the table decoder (reported
+    with bm 16); forcing it above 16 rows, or an unknown decoder, is refused
+    before any launch."""
+    L = ex.load()
+    head = view(4096, (154880,), 6, 2)
+    for M in (1, 8, 16):
+        p = _plan(head, M)
+        assert p.decoder == ex.EXL3_DECODER_TABLE and p.bm == 16, M
+    assert _plan(head, 17).decoder == ex.EXL3_DECODER_ALU
+    assert _plan(view(5120, (12288,), 6, 2), 1).decoder == ex.EXL3_DECODER_TABLE  # 62.9M weights
+    assert _plan(view(4096, (2048,), 4, 1), 1).decoder == ex.EXL3_DECODER_ALU     # 8.4M weights
+    small = view(1024, (1024,), 4, 0)
+    slabs = ex._Plan(4, ex.EXL3_MODE_SLABS, -1, ex.EXL3_DECODER_TABLE, 0)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(small), 16, ctypes.byref(slabs)) == 4 * 16 * 1024 * 4
+    too_tall = ex._Plan(-1, -1, -1, ex.EXL3_DECODER_TABLE, 0)
+    assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 17, FAKE, 1, FAKE, 1 << 30, None,
+                            ctypes.byref(too_tall)) == 2  # EXL3_ERR_UNSUPPORTED
+    assert "at most 16 rows" in last_error()
+    unknown = ex._Plan(-1, -1, -1, 7, 0)
+    assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 4, FAKE, 1, FAKE, 1 << 30, None,
+                            ctypes.byref(unknown)) == 1  # EXL3_ERR_INVALID_ARG
+    assert "decoder=7" in last_error()

@@ -181,6 +181,41 @@ def test_large_tiles_ragged(bits, cb, M):
     _check(t, ref)
 
 
+TABLE_CASES = [(1, "3inst"), (2, "mul1"), (3, "mcg"), (4, "mcg"), (5, "mul1"), (6, "mul1"), (7, "3inst"),
+               (8, "mul1")]
+
+
+@pytest.mark.parametrize("bits,cb", TABLE_CASES)
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_table_decoder_matches_alu(bits, cb, M):
+    """The table decoder against the ALU tile kernel: the same bits for one
+    part, a fused multi-part fold, and slabs; two shards, ragged rows."""
+    banner(f"table decoder {bits}-bit {cb} M={M}")
+    lay = wl.small_layer(f"table_b{bits}_{cb}", 1024, (256, 384), bits, cb, (16,), seed=80 + bits)
+    t = wl.gen_all(lay)
+    y = None
+    for parts, mode in ((1, ex.EXL3_MODE_FUSED), (2, ex.EXL3_MODE_FUSED), (4, ex.EXL3_MODE_SLABS),
+                        (8, ex.EXL3_MODE_SLABS)):
+        ref = _run(t, M=M, parts=parts, mode=mode, decoder=ex.EXL3_DECODER_ALU)
+        y = _run(t, M=M, parts=parts, mode=mode, decoder=ex.EXL3_DECODER_TABLE)
+        assert np.array_equal(y, ref), f"parts={parts} mode={mode}"
+    _check(t, y, M=M)
+
+
+@pytest.mark.parametrize("mode", [ex.EXL3_MODE_FUSED, ex.EXL3_MODE_SLABS])
+def test_table_decoder_several_units_per_team(mode):
+    """Slabs: 2048 units, more than the 4 teams of every CU, so each team
+    streams two units back to back.  Fused: 8 parts folded per column block
+    at K = 8192.  Both give the ALU kernel's bits; fp16 output."""
+    banner(f"table decoder, many units, mode {mode}")
+    lay = wl.small_layer("table_units", 8192, (4096,), 4, "mcg", (3,), seed=91)
+    t = wl.gen_all(lay)
+    parts = 64 if mode == ex.EXL3_MODE_SLABS else 8
+    ref = _run(t, "f16", parts=parts, mode=mode, decoder=ex.EXL3_DECODER_ALU)
+    y = _run(t, "f16", parts=parts, mode=mode, decoder=ex.EXL3_DECODER_TABLE)
+    assert np.array_equal(y, ref)
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_row_alone_equals_row_in_batch():
@@ -272,6 +307,9 @@ def test_full_size_sampled(name, M):
     # batch invariance at the real shape: the first row alone
     y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
     assert np.array_equal(y1[0], y[0])
+    if M <= 16:  # both decoders at the real shape
+        for dec in (ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE):
+            assert np.array_equal(bits16(ex.linear(w, xr, torch.bfloat16, decoder=dec)), y), f"decoder {dec}"
     rows = sorted({0, M // 2, M - 1})
     nblk = lay.N // 128
     blocks = sorted({0, nblk // 3, nblk - 1} | ({lay.shards[0] // 128} if lay.n_shards > 1 else set()))
