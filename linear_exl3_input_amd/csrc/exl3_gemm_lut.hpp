@@ -23,7 +23,8 @@
 // Work: a unit is one 128-column block and one K part (slab mode) or one
 // block and all parts (fused mode, parts folded in part order).  The 16
 // waves are 4 teams of 4 waves; wave tw of a team multiplies n-tiles 2tw,
-// 2tw+1 against the (up to) 16 rows.  A team walks its units as one
+// 2tw+1 against the (up to) 16 rows.  Units are dealt to the workgroups in
+// turn (unit u to workgroup u mod G, team (u / G) mod 4).  A team walks its units as one
 // continuous stream of k-steps, so the loads of the next unit are in flight
 // while the current one finishes.  Same MFMA shape, k-slot order, k-step
 // order and parts as the tile kernels, so the same bits.
@@ -136,7 +137,9 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
 
   auto make_unit = [&](int r) __attribute__((always_inline)) {
     TblUnit u;
-    const int id = (r * (int)gridDim.x + (int)blockIdx.x) * TBL_TEAMS + team;
+    // units go round the workgroups first, so that fewer units than teams
+    // still spread over every CU
+    const int id = (r * TBL_TEAMS + team) * (int)gridDim.x + (int)blockIdx.x;
     if (r >= rounds || id >= units) {
       u.t = 0;
       u.a = xrot;

@@ -310,7 +310,7 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     int cus = 0;
     if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
     const int64_t units = (int64_t)(w->N / 128) * (p.slab_mode ? pl.parts : 1);
-    const int grid = (int)std::min<int64_t>(cus, (units + 3) / 4);
+    const int grid = (int)std::min<int64_t>(cus, units);
     e = exl3::launch_gemm_table(w->bits, w->codebook, p, grid, s);
     if (e != hipSuccess) return launch_error(e, "table GEMM launch");
   } else {
