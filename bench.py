@@ -47,7 +47,7 @@ WORKLOADS = {
 }
 DEFAULT_WORKLOAD = "expert_4096x2048+2048x4096_b4_mcg"
 
-KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_device.hpp", "exl3_misc.hip"]
+KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_gemm_lut.hpp", "exl3_device.hpp", "exl3_misc.hip"]
 
 
 def sol_seconds(M, K, N, bits):
@@ -60,6 +60,8 @@ def kernel_key(lay, plan) -> str:
     bm = plan["bm"]
     multi = plan["mode"] == 0 and plan["parts"] > 1
     cb = {"3inst": 0, "mcg": 1, "mul1": 2}[lay.codebook]
+    if plan.get("decoder") == 1:
+        return f"exl3::gemm_table_kernel<{lay.bits}, {cb}u, 2>"
     if bm <= 64:
         name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}>"
     elif bm == 128:
@@ -287,22 +289,26 @@ def main():
 
     # ---- roofline of the dominant kernel: the GEMM template instance with
     # the most time per step.  A slab-mode call is the GEMM plus the ordered
-    # part sum + output transform kernel; that second kernel is timed alone
-    # (same parts, rows and columns) and subtracted, so the GEMM's average
-    # launch duration is what rocprof reports for it.
+    # part sum + output transform kernel; each is timed alone (the GEMM
+    # stage through the part-sums hook with the call's own plan, the output
+    # stage through its hook), so the GEMM's average launch duration is the
+    # one rocprof reports for it.
     with torch.cuda.stream(stream):
         for s_ in per_shape:
             s_["gemm_us"] = s_["linear_us"]
             s_["epilogue_us"] = 0.0
             if s_["plan"]["mode"] == ex.EXL3_MODE_SLABS:
                 li = [l.name for l in layers].index(s_["layer"])
-                lay_, ws_ = per_layer[li][0], per_layer[li][1]
-                zp = torch.zeros((s_["plan"]["parts"], (s_["M"] + 3) // 4, lay_.N, 4), dtype=torch.float32,
-                                 device=dev)
+                lay_, ws_, xr_ = per_layer[li][0], per_layer[li][1], per_layer[li][3]
+                pl_ = s_["plan"]
+                zp = torch.zeros((pl_["parts"], (s_["M"] + 3) // 4, lay_.N, 4), dtype=torch.float32, device=dev)
                 yo = torch.empty((s_["M"], lay_.N), dtype=torch.bfloat16, device=dev)
                 t_epi = time_calls(lambda r: ex.debug_epilogue(ws_[0], zp, s_["M"], out=yo), args.timing_reps)
+                t_gemm = time_calls(lambda r: ex.debug_parts(ws_[(r * 7 + 3) % copies], xr_[s_["M"]],
+                                                             parts=pl_["parts"], bm=pl_["bm"], decoder=pl_["decoder"],
+                                                             out=zp), args.timing_reps)
                 s_["epilogue_us"] = round(t_epi, 3)
-                s_["gemm_us"] = round(s_["linear_us"] - t_epi, 3)
+                s_["gemm_us"] = round(t_gemm, 3)
                 del zp
             s_["kernel"] = kernel_key(wl.layer(s_["layer"]), s_["plan"])
     groups = {}
@@ -351,7 +357,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 products, f32 sums, bf16 out",
+        "dtype": "f16",
         "data": "synthetic (seeded uniform trellis, +-1 suh/svh, N(0,1) bf16 x)",
         "config": {"workload": args.workload, "layers": [
             {"K": l.K, "N": l.N, "shards": list(l.shards), "bits": l.bits, "codebook": l.codebook} for l in layers],

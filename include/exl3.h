@@ -193,6 +193,19 @@ exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream);
  * unpacking path (TensorFold PR, "Tests (GB10)" second bullet). */
 exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream);
 
+/* The trellis GEMM stage alone, the kernel slab mode runs before the
+ * output stage: the fp32 sum of every K part,
+ *   z_parts[p][m/4][n][m%4] = sum_{k in part p} x~[s(n)][m][k] * W_q[k][n]
+ * (TensorFold PR, "Arithmetic" step 2, with the ordered K parts of the
+ * cuda-exl3 README's split-k, "Two further departures").  The plan is the
+ * one exl3_linear would use, or `force` (HOST, may be NULL) as in
+ * exl3_linear_ex, with the mode set to slabs; x_rot as for exl3_linear.
+ * z_parts (device) needs P * ceil(M/4) * 4 * N * 4 bytes (z_bytes, checked;
+ * EXL3_ERR_WORKSPACE if short); rows past M in the last group of four hold
+ * unspecified finite values.  Exactly what exl3_debug_epilogue reads. */
+exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_t M, float *z_parts,
+                             size_t z_bytes, void *stream, const exl3_plan *force);
+
 /* The output stage alone, the kernel slab mode runs after the GEMM:
  * y = rne_out(svh * 2^-3 * H128(z)) with z = ((z_parts[0] + z_parts[1]) + ...)
  * in fp32 (TensorFold PR, "Arithmetic" step 3 and the ordered part sum).

@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
-    "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue",
+    "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue", "debug_parts",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,7 @@ def load() -> ctypes.CDLL:
             "exl3_debug_codebook": (i32, [i32, vp, vp]),
             "exl3_debug_decode": (i32, [W, vp, vp]),
             "exl3_debug_epilogue": (i32, [vp, i32, i32, W, vp, i32, vp]),
+            "exl3_debug_parts": (i32, [W, vp, i32, vp, sz, vp, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -278,6 +279,26 @@ def debug_codebook(codebook: int | str, device="cuda") -> torch.Tensor:
 def debug_decode(w: Exl3Weight) -> torch.Tensor:
     out = torch.empty((w.K, w.N), dtype=torch.int16, device=w.trellis.device)
     _check(load().exl3_debug_decode(ctypes.byref(w.view()), out.data_ptr(), _stream()))
+    return out
+
+
+def debug_parts(w: Exl3Weight, x_rot: torch.Tensor, parts=None, bm=None, decoder=None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The trellis GEMM stage alone: the fp32 sum of every K part, in the
+    slab layout [P, ceil(M/4), N, 4] (what debug_epilogue reads)."""
+    if x_rot.dim() != 4 or x_rot.shape[3] != 32:
+        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
+    M = x_rot.shape[2]
+    P = parts if parts else plan(w, M)["parts"]
+    shape = (P, (M + 3) // 4, w.N, 4)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x_rot.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.float32:
+        raise ValueError(f"out is {tuple(out.shape)} {out.dtype}, expected {shape} float32")
+    f = _force(parts, EXL3_MODE_SLABS, bm, decoder)
+    _check(load().exl3_debug_parts(ctypes.byref(w.view()), _dev_ptr(x_rot, "x_rot", _H16), M,
+                                   _dev_ptr(out, "z_parts", (torch.float32,)), out.numel() * 4, _stream(),
+                                   ctypes.byref(f)))
     return out
 
 

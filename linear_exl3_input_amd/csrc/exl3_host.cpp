@@ -74,23 +74,51 @@ exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_s
 
 // K parts: a function of (K, N, bits) only.  Enough (column block, part)
 // pairs to occupy the GPU at decode sizes (about 1024), parts of at least
-// two 128-k blocks, and the fp32 partial traffic at 16 rows kept near the
-// trellis bytes it helps to stream (the cuda-exl3 README caps split-k
-// accumulator traffic at ~30% of the weight bytes and discounts it when it
-// stays in cache, "Two further departures" and "Where the time goes"; on
-// this GPU the partials of a decode-size call stay in the 256 MB cache, so
-// the cap is looser).  P divides the number of 128-k blocks so every part has
+// four 128-k blocks (or four parts of two blocks, for short K), and the fp32
+// partial traffic at 16 rows kept near the trellis bytes it helps to stream
+// (the cuda-exl3 README caps split-k accumulator traffic at ~30% of the
+// weight bytes and discounts it when it stays in cache, "Two further
+// departures" and "Where the time goes"; on this GPU the partials of a
+// decode-size call stay in the 256 MB cache, so the cap is looser).  Shorter
+// parts help one-row calls little and cost batched ones partial traffic: at
+// K=4096, N=2048 eight parts against sixteen are 9% slower at one row and
+// 26% faster at 512.  P divides the number of 128-k blocks so every part has
 // the same length.
 int32_t choose_parts(int32_t K, int32_t N, int32_t bits) {
   const int32_t kb = K / 128;
   const int32_t nblk = N / 128;
   int32_t want = (1024 + nblk - 1) / nblk;
-  const int32_t cap_len = std::max(1, kb / 2);
+  const int32_t cap_len = std::max(1, std::max(kb / 4, std::min(kb / 2, 4)));
   const int32_t cap_traffic = std::max(1, (int32_t)(1.2 * (double)K * bits / 1024.0));
   int32_t pmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
   for (int32_t p = pmax; p >= 1; --p)
     if (kb % p == 0) return p;
   return 1;
+}
+
+// Compute units of the current device (queried once per device).
+hipError_t device_cus(int *out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return hipSuccess;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return hipSuccess;
+}
+
+// The CU count for planning; 256 (an MI355X) when no device is visible.
+int device_cus_or_default() {
+  int n = 0;
+  return device_cus(&n) == hipSuccess ? n : 256;
 }
 
 struct Plan {
@@ -157,6 +185,12 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = 16;
   // a fused multi-part tile keeps two accumulator sets: at most 256 rows
   if (!bm_forced && pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1) pl.bm = 256;
+  // 512-row tiles run one workgroup per CU: with fewer tiles than CUs,
+  // 256-row tiles (twice the workgroups) finish first
+  if (!bm_forced && pl.bm == 512) {
+    const int64_t tiles = (int64_t)(w->N / 128) * (pl.mode == EXL3_MODE_SLABS ? pl.parts : 1) * ((M + 511) / 512);
+    if (tiles < device_cus_or_default()) pl.bm = 256;
+  }
   // 512-row tiles hold one accumulator set: one part per workgroup only
   if (pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1)
     return fail(EXL3_ERR_UNSUPPORTED, "bm=512 runs one K part per workgroup; %d parts need mode=slabs or bm<=256",
@@ -169,24 +203,8 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   return EXL3_OK;
 }
 
-// Compute units of the current device (queried once per device).
-hipError_t device_cus(int *out) {
-  static int cache[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
-    return hipSuccess;
-  }
-  int n = 0;
-  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  if (n < 1) n = 1;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  *out = n;
-  return hipSuccess;
-}
+exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype, float *slabs,
+                       const Plan &pl, hipStream_t s, bool with_output);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -285,13 +303,24 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     if (!aligned16(workspace)) return fail(EXL3_ERR_INVALID_ARG, "workspace=%p is not 16-byte aligned", workspace);
   }
 
+  return run_linear(w, x_rot, M, y, y_dtype, static_cast<float *>(workspace), pl, (hipStream_t)stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The GEMM stage of a plan (partials to `slabs` in slab mode), then, if
+// `with_output` and in slab mode, the ordered part sum + output transform.
+exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype, float *slabs,
+                       const Plan &pl, hipStream_t s, bool with_output) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.trellis = w->trellis;
   p.x_rot = x_rot;
   p.svh = w->svh;
   p.y = y;
-  p.slabs = static_cast<float *>(workspace);
+  p.slabs = slabs;
   p.M = M;
   p.K = w->K;
   p.N = w->N;
@@ -304,7 +333,6 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     end += w->shard_n[s] / 128;
     p.shard_end_blk[s] = end;
   }
-  const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (pl.decoder == EXL3_DECODER_TABLE) {
     int cus = 0;
@@ -319,16 +347,49 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, !p.slab_mode && pl.parts > 1, p, grid, s);
     if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
   }
-  if (p.slab_mode) {
+  if (p.slab_mode && with_output) {
     e = exl3::launch_epilogue(p.slabs, pl.parts, M, w->N, w->svh, y, p.out_bf16 != 0, s);
     if (e != hipSuccess) return launch_error(e, "part-sum epilogue launch");
   }
   return EXL3_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                         void *workspace, size_t workspace_bytes, void *stream) {
   return exl3_linear_ex(w, x_rot, M, y, y_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_t M, float *z_parts,
+                             size_t z_bytes, void *stream, const exl3_plan *force) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
+  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
+  exl3_plan f;
+  if (force) f = *force;
+  else {
+    f.parts = -1;
+    f.bm = -1;
+    f.decoder = EXL3_DECODER_AUTO;
+    f.workspace = 0;
+  }
+  f.mode = EXL3_MODE_SLABS;
+  Plan pl;
+  if ((st = make_plan(w, M, &f, &pl)) != EXL3_OK) return st;
+  if (M == 0) return EXL3_OK;
+  pl.mode = EXL3_MODE_SLABS;  // also for one part
+  const size_t need = (size_t)pl.parts * (size_t)((M + 3) / 4) * 4 * (size_t)w->N * sizeof(float);
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  if ((st = check_ptr(z_parts, "z_parts")) != EXL3_OK) return st;
+  if (z_bytes < need)
+    return fail(EXL3_ERR_WORKSPACE, "z_parts holds %zu bytes; %d parts of %d rows need %zu (short by %zu)", z_bytes,
+                pl.parts, M, need, need - z_bytes);
+  return run_linear(w, x_rot, M, nullptr, EXL3_BF16, z_parts, pl, (hipStream_t)stream, false);
 }
 
 exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream) {

@@ -147,6 +147,15 @@ def test_forced_512_row_tile_needs_one_part_per_workgroup():
                             ctypes.byref(fused_multi)) == 2  # EXL3_ERR_UNSUPPORTED, before any launch
 
 
+def test_part_sums_hook_checks_its_buffer():
+    L = ex.load()
+    w = view(1024, (256,), 4, 1)
+    f = ex._Plan(4, -1, -1, -1, 0)
+    need = 4 * 4 * 256 * 4  # 4 parts x 4 rows x 256 columns x fp32
+    assert L.exl3_debug_parts(ctypes.byref(w), FAKE, 3, FAKE, need - 16, None, ctypes.byref(f)) == 3
+    assert "short by 16" in last_error()
+
+
 def test_table_decoder_choice_and_limits():
     """M <= 16 on layers of 2^25 weights or more: the table decoder (reported
     with bm 16); forcing it above 16 rows, or an unknown decoder, is refused

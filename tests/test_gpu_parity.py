@@ -216,6 +216,40 @@ def test_table_decoder_several_units_per_team(mode):
     assert np.array_equal(y, ref)
 
 
+@pytest.mark.parametrize("decoder", [ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE])
+@pytest.mark.parametrize("parts", [1, 3, 8])
+def test_part_sums_stage(decoder, parts):
+    """The GEMM stage alone: every K part's fp32 sum within the rounding
+    bound of its own length against the fp64 sum over that part's k range
+    (3 parts of 8 blocks: 2, 3 and 3 blocks); and the output stage applied
+    to those parts is bit for bit the whole linear."""
+    banner(f"part sums, decoder {decoder}, {parts} parts")
+    lay = wl.small_layer("parts", 1024, (256, 128), 5, "mcg", (13,), seed=95)
+    t = wl.gen_all(lay)
+    w = weight(t)
+    xr = ex.input_transform(x_dev(t.x), w.suh)
+    z = ex.debug_parts(w, xr, parts=parts, decoder=decoder)
+    torch.cuda.synchronize()
+    M, N, K = t.x.shape[0], lay.N, lay.K
+    zn = z.cpu().numpy().transpose(0, 1, 3, 2).reshape(parts, -1, N)[:, :M]  # [P, M, N]
+    x64 = otf.f16_from_bits(otf.rotate_input(t.x, t.suh, "bf16")).astype(np.float64)  # [S, M, K]
+    wq = ofmt.dequantize(t.trellis, lay.bits, lay.cb)  # [K, N]
+    col_shard = olin.shard_of_columns(lay.shards)
+    kb = K // 128
+    for p in range(parts):
+        k0, k1 = 128 * (p * kb // parts), 128 * ((p + 1) * kb // parts)
+        for s in range(lay.n_shards):
+            cols = np.nonzero(col_shard == s)[0]
+            exact = x64[s][:, k0:k1] @ wq[k0:k1, cols]
+            absd = np.abs(x64[s][:, k0:k1]) @ np.abs(wq[k0:k1, cols])
+            err = np.abs(zn[p][:, cols] - exact)
+            lim = olin.gamma(k1 - k0, olin.U_ACC) * absd
+            assert np.all(err <= lim), f"part {p} shard {s}: worst {np.max(err - lim)} over the bound"
+    y = bits16(ex.linear(w, xr, torch.bfloat16, parts=parts, decoder=decoder))
+    y2 = bits16(ex.debug_epilogue(w, z, M))
+    assert np.array_equal(y, y2)
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_row_alone_equals_row_in_batch():
