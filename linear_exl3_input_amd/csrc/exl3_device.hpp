@@ -102,7 +102,11 @@ __device__ __forceinline__ uint32_t cb_hash(uint32_t s) {
 
 // P(u) for two words: lo half = P(u0), hi half = P(u1).  Each fp16 add reads
 // the two halves of one masked word (SDWA selects) and writes one half of the
-// result, the other half preserved.
+// result, the other half preserved.  The result usually feeds a matrix-core
+// instruction, which must not read a VGPR sooner than two wait states after a
+// VALU instruction wrote it; the compiler cannot see writes made inside asm
+// and so does not count them, hence the s_nop 1 after the last add (without
+// it an MFMA one instruction later read a stale operand).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   uint32_t d;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(o));
@@ -115,7 +119,8 @@ __device__ __forceinline__ uint32_t pair_sum2(uint32_t u0, uint32_t u1) {
   uint32_t r;
   asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1"
       : "=v"(r) : "v"(m0));
-  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0 src1_sel:WORD_1"
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0 src1_sel:WORD_1\n\t"
+      "s_nop 1"
       : "+v"(r) : "v"(m1));
   return r;
 }
