@@ -56,14 +56,16 @@ def sol_seconds(M, K, N, bits):
 
 def kernel_key(lay, plan) -> str:
     """The GEMM template instance a call launches (what rocprof's per-kernel
-    statistics group by): tile family and rows, width, codebook, part fold."""
-    bm = plan["bm"]
-    multi = plan["mode"] == 0 and plan["parts"] > 1
+    statistics group by): tile family and rows, width, codebook, part fold
+    in registers, quads of waves (the host's rule, mirrored)."""
+    bm, unit = plan["bm"], plan["unit"]
     cb = {"3inst": 0, "mcg": 1, "mul1": 2}[lay.codebook]
     if plan.get("decoder") == 1:
         return f"exl3::gemm_table_kernel<{lay.bits}, {cb}u, 2>"
+    quads = unit if (bm <= 64 and unit in (2, 4) and (lay.K // 128) % plan["parts"] == 0) else 1
+    multi = unit > 1 and quads == 1
     if bm <= 64:
-        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}>"
+        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}, {quads}>"
     elif bm == 128:
         name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, {str(multi).lower()}>"
     else:
@@ -276,7 +278,7 @@ def main():
                 per_shape.append({
                     "layer": lay.name, "M": M, "K": lay.K, "N": lay.N, "bits": lay.bits, "codebook": lay.codebook,
                     "plan": pl, "transform_us": round(t_in, 3), "linear_us": round(t_lin, 3),
-                    "kernels_per_linear": 2 if pl["mode"] == ex.EXL3_MODE_SLABS else 1,
+                    "kernels_per_linear": pl["launches"],
                     "GBps": round(byts / (t_lin * 1e-6) / 1e9, 1),
                     "TFLOPS": round(flops / (t_lin * 1e-6) / 1e12, 2),
                     "pct_sol": round(100.0 * sol / (t_lin * 1e-6), 2),
@@ -288,25 +290,28 @@ def main():
                     f"{per_shape[-1]['pct_sol']}% SoL)")
 
     # ---- roofline of the dominant kernel: the GEMM template instance with
-    # the most time per step.  A slab-mode call is the GEMM plus the ordered
-    # part sum + output transform kernel; each is timed alone (the GEMM
-    # stage through the part-sums hook with the call's own plan, the output
-    # stage through its hook), so the GEMM's average launch duration is the
-    # one rocprof reports for it.
+    # the most time per step.  A two-launch slab call is the GEMM plus the
+    # ordered part sum + output transform kernel; each is timed alone (the
+    # GEMM stage through the part-sums hook with the call's own plan and
+    # unit, the output stage through its hook), so the GEMM's average launch
+    # duration is the one rocprof reports for it.  A one-launch call (fused,
+    # or slabs summed by the tile's last workgroup) is its GEMM kernel.
     with torch.cuda.stream(stream):
         for s_ in per_shape:
             s_["gemm_us"] = s_["linear_us"]
             s_["epilogue_us"] = 0.0
-            if s_["plan"]["mode"] == ex.EXL3_MODE_SLABS:
+            if s_["plan"]["mode"] == ex.EXL3_MODE_SLABS and s_["plan"]["launches"] == 2:
                 li = [l.name for l in layers].index(s_["layer"])
                 lay_, ws_, xr_ = per_layer[li][0], per_layer[li][1], per_layer[li][3]
                 pl_ = s_["plan"]
-                zp = torch.zeros((pl_["parts"], (s_["M"] + 3) // 4, lay_.N, 4), dtype=torch.float32, device=dev)
+                n_sl = pl_["parts"] // pl_["unit"]
+                zp = torch.zeros((n_sl, (s_["M"] + 3) // 4, lay_.N, 4), dtype=torch.float32, device=dev)
                 yo = torch.empty((s_["M"], lay_.N), dtype=torch.bfloat16, device=dev)
                 t_epi = time_calls(lambda r: ex.debug_epilogue(ws_[0], zp, s_["M"], out=yo), args.timing_reps)
                 t_gemm = time_calls(lambda r: ex.debug_parts(ws_[(r * 7 + 3) % copies], xr_[s_["M"]],
-                                                             parts=pl_["parts"], bm=pl_["bm"], decoder=pl_["decoder"],
-                                                             out=zp), args.timing_reps)
+                                                             parts=pl_["parts"], groups=pl_["groups"],
+                                                             unit=pl_["unit"], bm=pl_["bm"],
+                                                             decoder=pl_["decoder"], out=zp), args.timing_reps)
                 s_["epilogue_us"] = round(t_epi, 3)
                 s_["gemm_us"] = round(t_gemm, 3)
                 del zp

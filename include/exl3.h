@@ -46,7 +46,12 @@ extern "C" {
 #endif
 
 #define EXL3_MAX_SHARDS 16
-#define EXL3_ABI_VERSION 2
+#define EXL3_ABI_VERSION 3
+
+/* The first EXL3_WORKSPACE_COUNTER_BYTES of every workspace hold per-tile
+ * arrival counters (see exl3_linear): they must be zero before the first
+ * call that uses the workspace, and every call leaves them zero. */
+#define EXL3_WORKSPACE_COUNTER_BYTES 65536
 
 typedef enum {
   EXL3_OK = 0,
@@ -76,17 +81,25 @@ typedef struct exl3_weight {
   const int32_t *shard_n;  /* HOST [n_shards], each a multiple of 128        */
 } exl3_weight;
 
-/* Execution plan.  `parts` (P) and the K range of each part depend on
- * (K, N, bits) only, never on M, so every row's result is bit-identical at
- * every batch size.  `mode` and `bm` pick how the same arithmetic is
- * scheduled and never change a bit of the output. */
+/* Execution plan.  `parts` (P), `groups` (G) and the K range of each part
+ * depend on (K, N, bits) only, never on M, so every row's result is
+ * bit-identical at every batch size.  The fp32 sum over K is the fixed tree:
+ * each part is one chain of matrix-core products in ascending k starting from
+ * zero; the P/G consecutive parts of a group are added in part order (first
+ * part copied); the group sums are added in group order (first copied).  With
+ * G == P this is the plain ((p0 + p1) + p2) + ... of the TensorFold PR
+ * ("Arithmetic").  `mode`, `bm`, `decoder` and `unit` pick how the same
+ * arithmetic is scheduled and never change a bit of the output. */
 typedef enum {
   EXL3_MODE_AUTO = -1,
   EXL3_MODE_FUSED = 0, /* one workgroup per (M-tile, 128 columns) runs all
-                          parts in order and applies the output transform   */
-  EXL3_MODE_SLABS = 1  /* one workgroup per (M-tile, 128 columns, part)
-                          writes an fp32 partial; a second kernel sums the
-                          parts in order and applies the output transform   */
+                          parts in order and applies the output transform
+                          (one group, or one part per group)                */
+  EXL3_MODE_SLABS = 1  /* one workgroup per (M-tile, 128 columns, unit of
+                          parts) writes the unit's fp32 sum as a partial
+                          slab; the slabs are summed in order and the output
+                          transform applied by the tile's last workgroup
+                          (the finisher) or by a second kernel              */
 } exl3_mode;
 
 /* How weights are decoded.  Both decoders produce the same fp16 values
@@ -102,7 +115,9 @@ typedef enum {
 } exl3_decoder;
 
 typedef struct exl3_plan {
-  int32_t parts;       /* P >= 1 K parts                                     */
+  int32_t parts;       /* P >= 1 K parts, all of whole 128-k blocks          */
+  int32_t groups;      /* G >= 1 groups, G divides P; when P/G > 1 every
+                          part has the same length (P divides K/128)        */
   int32_t mode;        /* exl3_mode                                          */
   int32_t bm;          /* rows per M-tile: 16, 32, 64, 128, 256 or 512;
                           512 only with one part per workgroup (parts == 1
@@ -114,7 +129,13 @@ typedef struct exl3_plan {
                           forced plan 0 means ALU; TABLE with M > 16 is
                           EXL3_ERR_UNSUPPORTED; forcing bm alone selects
                           ALU                                               */
-  size_t workspace;    /* bytes of workspace this plan needs                 */
+  int32_t unit;        /* slab mode: parts per workgroup unit (one slab per
+                          unit): P/G (one slab per group) automatically; 1
+                          (one slab per part) may be forced.  Fused: P      */
+  int32_t launches;    /* kernels one exl3_linear call enqueues (output;
+                          ignored in a forced plan)                         */
+  size_t workspace;    /* bytes of workspace this plan needs: 0, or
+                          EXL3_WORKSPACE_COUNTER_BYTES + the slabs          */
 } exl3_plan;
 
 /* ---------------------------------------------------------------- calls */
@@ -149,14 +170,21 @@ size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M);
 /* The quantized linear on rotated activations (cuda-exl3 README, "One op per
  * layer"; TensorFold PR, "Arithmetic" steps 2 and 3):
  *   z[m][n] = sum_k x_rot[s(n)][m][k] * W_q[k][n]   (fp16 products, fp32 sums
- *             in P shape-fixed K parts, summed in part order)
+ *             in P shape-fixed K parts, summed in the plan's fixed order)
  *   y[m][n] = rne_out( svh[n] * 2^-3 * H128(z[m][:])[n] )  per 128-col block
  * where s(n) is the shard holding absolute column n.
  *   x_rot     n_shards * M * K fp16 bits in the k-step tile order written by
  *             exl3_input_transform
  *   y         [M][N] in y_dtype (output, written completely)
- *   workspace at least exl3_workspace_bytes(w, M) bytes (may be NULL if 0);
- *             its contents on entry do not matter.
+ *   workspace at least exl3_workspace_bytes(w, M) bytes (may be NULL if 0).
+ *             Its first EXL3_WORKSPACE_COUNTER_BYTES are arrival counters that
+ *             must be zero on entry (allocate the workspace zeroed once) and
+ *             are zero again when the call's kernels end; the rest may hold
+ *             anything.  A workspace serves one call at a time.
+ * In slab mode the workgroups of a tile that finish first store their
+ * partial and count their arrival; the last to arrive sums the partials in
+ * the plan's order and writes y (TensorFold PR, "Arithmetic": the last part
+ * to finish adds the parts in part order).  No workgroup waits for another.
  * Errors: EXL3_ERR_INVALID_ARG for a bad weight view (see exl3_weight),
  * pointer or dtype; EXL3_ERR_WORKSPACE if the workspace is too small;
  * EXL3_ERR_LAUNCH if HIP refuses a launch. */
@@ -166,10 +194,13 @@ exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, 
 /* The plan exl3_linear would use for M rows (HOST output). */
 exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan);
 
-/* exl3_linear with parts of the plan forced (HOST `force`; a field < 0, or
+/* exl3_linear with parts of the plan forced (HOST `force`; a field <= 0, or
  * EXL3_MODE_AUTO / EXL3_DECODER_AUTO, keeps the automatic choice).  Forcing
- * `mode`, `bm` or `decoder` never changes the output bits; forcing `parts` changes the K summation structure
- * and therefore the bits (for tests and measurement). */
+ * `mode`, `bm`, `decoder` or `unit` never changes the output bits; forcing
+ * `parts` (with `groups`, else G = P) changes the K summation tree and
+ * therefore the bits (for tests and measurement).  `groups` may only be
+ * forced together with `parts`; mode FUSED with G > 1 groups of several parts
+ * is EXL3_ERR_UNSUPPORTED (the fused fold has one level). */
 exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y,
                            int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream,
                            const exl3_plan *force);
@@ -194,24 +225,30 @@ exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream);
 exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream);
 
 /* The trellis GEMM stage alone, the kernel slab mode runs before the
- * output stage: the fp32 sum of every K part,
- *   z_parts[p][m/4][n][m%4] = sum_{k in part p} x~[s(n)][m][k] * W_q[k][n]
- * (TensorFold PR, "Arithmetic" step 2, with the ordered K parts of the
- * cuda-exl3 README's split-k, "Two further departures").  The plan is the
- * one exl3_linear would use, or `force` (HOST, may be NULL) as in
- * exl3_linear_ex, with the mode set to slabs; x_rot as for exl3_linear.
- * z_parts (device) needs P * ceil(M/4) * 4 * N * 4 bytes (z_bytes, checked;
+ * output stage: the fp32 sum of every K part (unit 1, the default), or of
+ * every group (force->unit = P/G, the automatic slab plan's own stage),
+ *   z_parts[u][m/4][n][m%4] = sum_{k in unit u} x~[s(n)][m][k] * W_q[k][n]
+ * with the parts of a unit added in part order (TensorFold PR, "Arithmetic"
+ * step 2, with the ordered K parts of the cuda-exl3 README's split-k, "Two
+ * further departures").  The plan is the one exl3_linear would use, or
+ * `force` (HOST, may be NULL) as in exl3_linear_ex, with the mode set to
+ * slabs; x_rot as for exl3_linear.  z_parts (device) needs
+ * (P/unit) * ceil(M/4) * 4 * N * 4 bytes (z_bytes, checked;
  * EXL3_ERR_WORKSPACE if short); rows past M in the last group of four hold
  * unspecified finite values.  Exactly what exl3_debug_epilogue reads. */
 exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_t M, float *z_parts,
                              size_t z_bytes, void *stream, const exl3_plan *force);
 
-/* The output stage alone, the kernel slab mode runs after the GEMM:
- * y = rne_out(svh * 2^-3 * H128(z)) with z = ((z_parts[0] + z_parts[1]) + ...)
- * in fp32 (TensorFold PR, "Arithmetic" step 3 and the ordered part sum).
- * z_parts is in the partial-slab layout [n_parts][ceil(M/4)][N][4] fp32:
- * element (part, m, n) at ((part * ceil(M/4) + m/4) * N + n) * 4 + m%4. */
-exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t M,
+/* The output stage alone, the stage slab mode runs after the GEMM:
+ * y = rne_out(svh * 2^-3 * H128(z)) with z the fp32 sum of the n_parts slabs
+ * in `groups` groups of n_parts/groups consecutive slabs: each group added in
+ * slab order (first copied), then the groups in order (first copied); with
+ * groups == n_parts, z = ((z_parts[0] + z_parts[1]) + ...) (TensorFold PR,
+ * "Arithmetic" step 3 and the ordered part sum).  z_parts is in the
+ * partial-slab layout [n_parts][ceil(M/4)][N][4] fp32: element (part, m, n)
+ * at ((part * ceil(M/4) + m/4) * N + n) * 4 + m%4.  EXL3_ERR_INVALID_ARG if
+ * groups does not divide n_parts. */
+exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t groups, int32_t M,
                                 const exl3_weight *w, void *y, int32_t y_dtype, void *stream);
 
 #ifdef __cplusplus

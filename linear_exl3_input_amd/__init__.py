@@ -57,8 +57,13 @@ class _Weight(ctypes.Structure):
 
 
 class _Plan(ctypes.Structure):
-    _fields_ = [("parts", ctypes.c_int32), ("mode", ctypes.c_int32), ("bm", ctypes.c_int32),
-                ("decoder", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
+    _fields_ = [("parts", ctypes.c_int32), ("groups", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("bm", ctypes.c_int32), ("decoder", ctypes.c_int32), ("unit", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
+
+
+ABI_VERSION = 3
+COUNTER_BYTES = 65536  # EXL3_WORKSPACE_COUNTER_BYTES: zeroed arrival counters at the workspace's start
 
 
 _lib = None
@@ -94,14 +99,14 @@ def load() -> ctypes.CDLL:
             "exl3_abi_version": (i32, []),
             "exl3_debug_codebook": (i32, [i32, vp, vp]),
             "exl3_debug_decode": (i32, [W, vp, vp]),
-            "exl3_debug_epilogue": (i32, [vp, i32, i32, W, vp, i32, vp]),
+            "exl3_debug_epilogue": (i32, [vp, i32, i32, i32, W, vp, i32, vp]),
             "exl3_debug_parts": (i32, [W, vp, i32, vp, sz, vp, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
-        if L.exl3_abi_version() != 2:
+        if L.exl3_abi_version() != ABI_VERSION:
             raise RuntimeError("libexl3.so ABI version mismatch")
         _lib = L
         return L
@@ -174,7 +179,10 @@ class Exl3Weight:
 
 
 # Process-wide workspace per device (the cuda-exl3 page, "VRAM": the
-# activation and split-k workspaces are process-wide, not per layer).
+# activation and split-k workspaces are process-wide, not per layer).  It is
+# allocated zeroed: its first COUNTER_BYTES are the arrival counters that
+# every call expects zero and leaves zero.  Calls on one device's stream use
+# it one after another.
 _workspaces: Dict[int, torch.Tensor] = {}
 
 
@@ -184,20 +192,21 @@ def _workspace(nbytes: int, device: torch.device) -> Tuple[int, int]:
     idx = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(idx)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[idx] = ws
     return ws.data_ptr(), ws.numel()
 
 
-def _force(parts=None, mode=None, bm=None, decoder=None) -> Optional[_Plan]:
-    if parts is None and mode is None and bm is None and decoder is None:
+def _force(parts=None, mode=None, bm=None, decoder=None, groups=None, unit=None) -> Optional[_Plan]:
+    if parts is None and mode is None and bm is None and decoder is None and groups is None and unit is None:
         return None
-    return _Plan(parts if parts else -1, EXL3_MODE_AUTO if mode is None else mode, bm if bm else -1,
-                 EXL3_DECODER_AUTO if decoder is None else decoder, 0)
+    return _Plan(parts if parts else -1, groups if groups else -1, EXL3_MODE_AUTO if mode is None else mode,
+                 bm if bm else -1, EXL3_DECODER_AUTO if decoder is None else decoder, unit if unit else -1, 0, 0)
 
 
-def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decoder=None) -> int:
-    f = _force(parts, mode, bm, decoder)
+def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decoder=None, groups=None,
+                    unit=None) -> int:
+    f = _force(parts, mode, bm, decoder, groups, unit)
     L = load()
     n = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     err = L.exl3_last_error().decode()
@@ -209,7 +218,8 @@ def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decod
 def plan(w: Exl3Weight, M: int) -> dict:
     p = _Plan()
     _check(load().exl3_plan_query(ctypes.byref(w.view()), M, ctypes.byref(p)))
-    return {"parts": p.parts, "mode": p.mode, "bm": p.bm, "decoder": p.decoder, "workspace": p.workspace}
+    return {"parts": p.parts, "groups": p.groups, "mode": p.mode, "bm": p.bm, "decoder": p.decoder,
+            "unit": p.unit, "launches": p.launches, "workspace": p.workspace}
 
 
 def rot_shape(n_shards: int, M: int, K: int) -> tuple:
@@ -242,7 +252,7 @@ def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tens
 
 def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
            out: Optional[torch.Tensor] = None, parts=None, mode=None, bm=None,
-           decoder=None) -> torch.Tensor:
+           decoder=None, groups=None, unit=None) -> torch.Tensor:
     """z = x_rot . W_q per shard, then the output transform: -> y [M, N]."""
     if x_rot.dim() != 4 or x_rot.shape[3] != 32:
         raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
@@ -254,7 +264,7 @@ def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bf
         raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
     if out is None:
         out = torch.empty((M, w.N), dtype=out_dtype, device=x_rot.device)
-    f = _force(parts, mode, bm, decoder)
+    f = _force(parts, mode, bm, decoder, groups, unit)
     L = load()
     need = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     ws, wsn = _workspace(need, x_rot.device)
@@ -283,19 +293,20 @@ def debug_decode(w: Exl3Weight) -> torch.Tensor:
 
 
 def debug_parts(w: Exl3Weight, x_rot: torch.Tensor, parts=None, bm=None, decoder=None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The trellis GEMM stage alone: the fp32 sum of every K part, in the
-    slab layout [P, ceil(M/4), N, 4] (what debug_epilogue reads)."""
+                out: Optional[torch.Tensor] = None, groups=None, unit=None) -> torch.Tensor:
+    """The trellis GEMM stage alone: the fp32 sum of every K part (unit 1,
+    the default) or of every unit of `unit` parts, in the slab layout
+    [P/unit, ceil(M/4), N, 4] (what debug_epilogue reads)."""
     if x_rot.dim() != 4 or x_rot.shape[3] != 32:
         raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
     M = x_rot.shape[2]
     P = parts if parts else plan(w, M)["parts"]
-    shape = (P, (M + 3) // 4, w.N, 4)
+    shape = (P // (unit or 1), (M + 3) // 4, w.N, 4)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x_rot.device)
     elif tuple(out.shape) != shape or out.dtype != torch.float32:
         raise ValueError(f"out is {tuple(out.shape)} {out.dtype}, expected {shape} float32")
-    f = _force(parts, EXL3_MODE_SLABS, bm, decoder)
+    f = _force(parts, EXL3_MODE_SLABS, bm, decoder, groups, unit)
     _check(load().exl3_debug_parts(ctypes.byref(w.view()), _dev_ptr(x_rot, "x_rot", _H16), M,
                                    _dev_ptr(out, "z_parts", (torch.float32,)), out.numel() * 4, _stream(),
                                    ctypes.byref(f)))
@@ -303,15 +314,17 @@ def debug_parts(w: Exl3Weight, x_rot: torch.Tensor, parts=None, bm=None, decoder
 
 
 def debug_epilogue(w: Exl3Weight, z_parts: torch.Tensor, M: int, out_dtype=torch.bfloat16,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, groups: Optional[int] = None) -> torch.Tensor:
     """Ordered part sum + output transform of fp32 partials in the slab
-    layout [P, ceil(M/4), N, 4] (see slab_layout)."""
+    layout [P, ceil(M/4), N, 4]: `groups` groups of P/groups consecutive
+    slabs (default P: the plain ordered fold)."""
     if z_parts.dim() != 4 or z_parts.shape[1] != (M + 3) // 4 or z_parts.shape[3] != 4:
         raise ValueError(f"z_parts shape {tuple(z_parts.shape)} is not [P, ceil(M/4), N, 4] for M={M}")
     P, _, N, _ = z_parts.shape
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=z_parts.device)
     out_dtype = out.dtype
-    _check(load().exl3_debug_epilogue(_dev_ptr(z_parts, "z_parts", (torch.float32,)), P, M, ctypes.byref(w.view()),
+    _check(load().exl3_debug_epilogue(_dev_ptr(z_parts, "z_parts", (torch.float32,)), P, groups or P, M,
+                                      ctypes.byref(w.view()),
                                       out.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _F16, _stream()))
     return out

@@ -209,4 +209,58 @@ __device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *_
   *(uint32_t *)(yrow + n0 + 2 * lane) = packed;
 }
 
+// Ordered sum of K-part partials for four rows of one 128-column block, then
+// the output stage of those rows.  Slabs are [n_slabs][M4][N][4] fp32 (the
+// four rows of a column are 16 contiguous bytes); lane l holds columns
+// n0 + 2l, n0 + 2l + 1.  The sum is the shape-fixed two-level order: each run
+// of fold_q consecutive slabs (one group of parts) is folded in order, the
+// first slab copied, and the group sums are folded in group order, the first
+// copied (TensorFold PR, "Arithmetic": a shape-fixed number of parts added in
+// part order, so a row's bits do not depend on the batch).  With fold_q = 1
+// it is the plain fold ((s0 + s1) + s2) + ...  Loads are issued U slabs at
+// a time before their adds.
+template <bool OUT_BF16, int U = 8>
+__device__ __forceinline__ void reduce_rows4(const float *__restrict__ slabs, int n_slabs, int fold_q,
+                                             int64_t slab_floats, int N, int64_t m4, int n0,
+                                             const uint16_t *__restrict__ svh, uint16_t *__restrict__ y,
+                                             int64_t row0, int rows, int lane) {
+  const float4_t *src = reinterpret_cast<const float4_t *>(slabs + (m4 * N + n0 + 2 * lane) * 4);
+  const int64_t st = slab_floats / 4;  // float4s per slab
+  float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
+  int iq = 0;  // position of slab i inside its group
+  for (int i0 = 0; i0 < n_slabs; i0 += U) {
+    float4_t v0[U], v1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + u < n_slabs) {
+        v0[u] = src[(i0 + u) * st];
+        v1[u] = src[(i0 + u) * st + 1];
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + u < n_slabs) {
+        if (iq == 0) {
+          g0 = v0[u];
+          g1 = v1[u];
+        } else {
+          g0 = g0 + v0[u];
+          g1 = g1 + v1[u];
+        }
+        if (++iq == fold_q) {
+          iq = 0;
+          if (i0 + u + 1 == fold_q) {
+            t0 = g0;
+            t1 = g1;
+          } else {
+            t0 = t0 + g0;
+            t1 = t1 + g1;
+          }
+        }
+      }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (r < rows) output_row<OUT_BF16>(t0[r], t1[r], svh, y + (row0 + r) * N, n0, lane);
+}
+
 }  // namespace exl3

@@ -299,58 +299,233 @@ __device__ __forceinline__ u32x4_t raw_decode_frag(const uint32_t *__restrict__ 
 
 // ------------------------------------------------------------------- GEMM
 
-// One accumulator of a lane (rows row0 .. row0+3 of column col; row0 is a
-// multiple of 4) into the fp32 partial of K part `part`.  Partials are laid
-// out [part][M/4][N][4] (rows padded to a multiple of 4, padding rows hold
-// finite values of clamped or zero rows): a lane's four values are one
-// 16-byte store and a wave's stores fill whole cache lines.
-__device__ __forceinline__ void store_partial(float *__restrict__ slabs, int part, int M, int N, int row0, int col,
+// One accumulator of a lane (slab rows row0 .. row0+3 of column col; row0 is
+// a multiple of 4) into partial slab `slab`.  Slabs are laid out
+// [slab][rows/4][N][4] (rows padded to a multiple of 4, padding rows hold
+// finite values of clamped rows): a lane's four values are one 16-byte store
+// and a wave's stores fill whole cache lines.
+__device__ __forceinline__ void store_partial(float *__restrict__ slabs, int slab, int rows, int N, int row0, int col,
                                               float4_t v) {
-  if (row0 < M) {
-    const int64_t M4 = (M + 3) >> 2;
-    *(float4_t *)(slabs + (((int64_t)part * M4 + (row0 >> 2)) * N + col) * 4) = v;
+  if (row0 < rows) {
+    const int64_t M4 = (rows + 3) >> 2;
+    *(float4_t *)(slabs + (((int64_t)slab * M4 + (row0 >> 2)) * N + col) * 4) = v;
   }
 }
 
-// BM = 16*MT rows (16, 32, 64) x 128 columns on 4 waves; wave w decodes
-// n-tiles 2w, 2w+1 (both column halves) and multiplies them against all BM
-// rows.  Both operands arrive by direct loads to LDS into two stage slots
-// (raw trellis tiles, and x~ in its k-step tile layout, 4 k-steps x BM rows
-// x 64 B per stage); the first two stages are issued together, so a short
-// workgroup (two stages at the larger part counts) waits for memory once.
-// Barriers wait only for LDS operations; the loads are waited for by count.
-// Rows past M load row M-1 (finite, never stored).
-template <int BITS, uint32_t CB, int MT, bool MULTI>
-__global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
+// ------------------------------------------------------------ finisher
+//
+// The last of a tile's workgroups to finish adds the tile's partial slabs in
+// order and applies the output stage (TensorFold PR, "Arithmetic": the last
+// part to finish adds the parts in part order).  No workgroup waits for
+// another, so nothing can hang.
+//
+// Visibility across the GPU's L2 caches (one per XCD) without fences that
+// write back and invalidate a whole L2 (measured at 10-30 us per call): the
+// partials are written with device-coherent stores (sc1, the cache policy of
+// an agent-scope atomic store) and every writer waits until its stores have
+// completed (vmcnt 0) before the workgroup counts its arrival with an
+// agent-scope atomic add; the last workgroup to arrive reads the partials
+// with device-coherent loads (sc1).  Slab bytes stay below 2 GiB (32-bit
+// buffer offsets; the host caps slabs far lower).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const GemmParams &p) {
+  const int rows = p.row_end - p.row_base;
+  const uint32_t bytes = (uint32_t)((int64_t)gridDim.y * ((rows + 3) >> 2) * p.N * 16);
+  return __builtin_amdgcn_make_buffer_rsrc(p.slabs, (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr int CPOL_SC1 = 16;  // device-scope coherent access
+
+// store_partial through the coherent path.
+__device__ __forceinline__ void store_partial_coherent(__amdgpu_buffer_rsrc_t rs, int slab, int rows, int N,
+                                                       int row0, int col, float4_t v) {
+  if (row0 < rows) {
+    const uint32_t M4 = (uint32_t)((rows + 3) >> 2);
+    const uint32_t off = (((uint32_t)slab * M4 + (uint32_t)(row0 >> 2)) * (uint32_t)N + (uint32_t)col) * 16u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, off, 0, CPOL_SC1);
+  }
+}
+
+// Arrival: every thread's stores have completed; one thread adds 1 to the
+// tile's counter.  Returns true (uniformly) in the tile's last workgroup.
+__device__ __forceinline__ bool arrive_last(const GemmParams &p) {
+  __shared__ int s_last;
+  wait_vmcnt<0>();
+  __syncthreads();
+  const uint32_t tile = blockIdx.z * gridDim.x + blockIdx.x;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             gridDim.y - 1;
+  __syncthreads();
+  return s_last != 0;
+}
+
+// The last workgroup's work on its tile (rows m0 .. m0+bm-1 of the launch,
+// 128 columns of block blockIdx.x), with n_waves waves and `lds_bytes` of
+// free LDS at `lds`.  The tile's slabs form G = n_slabs / fold_q groups of
+// fold_q consecutive slabs.  Items (4-row group r, group gi) are dealt to the
+// waves: each folds its group's slabs in slab order (first copied) into LDS,
+// so all loads of a wave's item are in flight together and the waves' items
+// overlap; then wave r folds the group sums of 4-row group r in group order
+// (first copied) and writes the rows.  The same fp32 adds in the same order as
+// reduce_rows4 (which serves when the items do not fit the LDS).  The
+// tile's counter is reset to zero for the next call.
+__device__ __forceinline__ void finish_tile(const GemmParams &p, int m0, int bm, int wave_all, int n_waves,
+                                            int lane, float *lds, int lds_bytes) {
+  const int rows = p.row_end - p.row_base;
+  const int M4 = (rows + 3) >> 2;
+  const int N = p.N;
+  const int n_slabs = gridDim.y;
+  const int fq = p.fold_q;
+  const int G = n_slabs / fq;
+  const int rt = min(bm, p.row_end - m0);  // rows of this tile
+  const int r4 = (rt + 3) >> 2;
+  const int n0 = blockIdx.x * 128;
+  const int m4_0 = (m0 - p.row_base) >> 2;
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+  const __amdgpu_buffer_rsrc_t rs = slab_rsrc(p);
+  const uint32_t slab_stride = (uint32_t)M4 * (uint32_t)N * 16u;  // bytes per slab
+  auto load2 = [&](int slab, int m4, float4_t &a, float4_t &b) __attribute__((always_inline)) {
+    const uint32_t off = (uint32_t)slab * slab_stride + ((uint32_t)m4 * (uint32_t)N + (uint32_t)(n0 + 2 * lane)) * 16u;
+    a = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL_SC1));
+    b = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, CPOL_SC1));
+  };
+  if (r4 * G * 2048 <= lds_bytes && fq <= 8) {
+    float4_t *const gs = reinterpret_cast<float4_t *>(lds);  // [r][gi][lane][2]
+    for (int it = wave_all; it < r4 * G; it += n_waves) {
+      const int r = it / G;
+      const int gi = it - r * G;
+      float4_t v0[8], v1[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < fq) load2(gi * fq + q, m4_0 + r, v0[q], v1[q]);
+      float4_t g0 = v0[0], g1 = v1[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if (q < fq) {
+          g0 = g0 + v0[q];
+          g1 = g1 + v1[q];
+        }
+      gs[(it * 64 + lane) * 2] = g0;
+      gs[(it * 64 + lane) * 2 + 1] = g1;
+    }
+    __syncthreads();
+    for (int r = wave_all; r < r4; r += n_waves) {
+      float4_t t0 = gs[(r * G * 64 + lane) * 2], t1 = gs[(r * G * 64 + lane) * 2 + 1];
+      for (int gi = 1; gi < G; ++gi) {
+        t0 = t0 + gs[((r * G + gi) * 64 + lane) * 2];
+        t1 = t1 + gs[((r * G + gi) * 64 + lane) * 2 + 1];
+      }
+      const int r0 = m0 + 4 * r;
+      const int nr = min(4, p.row_end - r0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nr) {
+          if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
+          else output_row<false>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
+        }
+    }
+  } else {
+    // one wave per 4-row group, slabs in order (reduce_rows4's order)
+    for (int r = wave_all; r < r4; r += n_waves) {
+      float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
+      for (int sl = 0; sl < n_slabs; ++sl) {
+        float4_t a, b;
+        load2(sl, m4_0 + r, a, b);
+        const int iq = sl % fq;
+        if (iq == 0) {
+          g0 = a;
+          g1 = b;
+        } else {
+          g0 = g0 + a;
+          g1 = g1 + b;
+        }
+        if (iq == fq - 1) {
+          if (sl == fq - 1) {
+            t0 = g0;
+            t1 = g1;
+          } else {
+            t0 = t0 + g0;
+            t1 = t1 + g1;
+          }
+        }
+      }
+      const int r0 = m0 + 4 * r;
+      const int nr = min(4, p.row_end - r0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nr) {
+          if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
+          else output_row<false>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
+        }
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(p.counters + blockIdx.z * gridDim.x + blockIdx.x, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS dwords of one stage slot of gemm_kernel (raw trellis tiles + x~) and of
+// a quad's private area (NSLOT slots + the landing area of surplus loads).
+template <int BITS, int MT>
+struct SmallGeom {
   using R = RawGeom<BITS>;
-  constexpr int BM = 16 * MT;
-  constexpr int T_OPS = (R::T_CHUNKS + WG_THREADS - 1) / WG_THREADS;  // trellis loads per wave per stage
-  constexpr int JUNK = T_OPS * WG_THREADS - R::T_CHUNKS;
-  constexpr int A_SLOT_DW = BM * 64;                                  // x~: 4 k-steps x BM rows x 64 B
-  constexpr int SLOT_DW = R::TSLOT_DW + A_SLOT_DW;
-  constexpr int OPS = T_OPS + MT;                                     // loads per wave per stage
-  constexpr int MAIN_DW = 2 * SLOT_DW + JUNK * 4;
+  static constexpr int BM = 16 * MT;
+  static constexpr int T_OPS = (R::T_CHUNKS + WG_THREADS - 1) / WG_THREADS;  // trellis loads per wave per stage
+  static constexpr int JUNK = T_OPS * WG_THREADS - R::T_CHUNKS;
+  static constexpr int A_SLOT_DW = BM * 64;  // x~: 4 k-steps x BM rows x 64 B
+  static constexpr int SLOT_DW = R::TSLOT_DW + A_SLOT_DW;
+  static constexpr int OPS = T_OPS + MT;     // loads per wave per stage
+  static constexpr int area(int nslot) { return nslot * SLOT_DW + JUNK * 4; }
+};
+
+// BM = 16*MT rows (16, 32, 64) x 128 columns.  A workgroup is QD quads of 4
+// waves; quad q computes K part (unit start + q) when QD > 1, or the whole
+// unit (MULTI: its parts folded in order in registers) when QD == 1.  Wave w
+// of a quad decodes n-tiles 2w, 2w+1 (both column halves) and multiplies them
+// against all BM rows.  Both operands arrive by direct loads to LDS into the
+// quad's stage slots (raw trellis tiles, and x~ in its k-step tile layout, 4
+// k-steps x BM rows x 64 B per stage): two slots, the first two stages issued
+// together, when QD quads of two slots fit in LDS, else one slot.  Barriers
+// wait only for LDS operations; the loads are waited for by count.  The
+// quads' part sums are then folded in part order through LDS.  Rows past the
+// launch's last row load that row (finite, never stored).
+template <int BITS, uint32_t CB, int MT, bool MULTI, int QD>
+__global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams p) {
+  using R = RawGeom<BITS>;
+  using S = SmallGeom<BITS, MT>;
+  constexpr int BM = S::BM;
+  constexpr int T_OPS = S::T_OPS;
+  constexpr int OPS = S::OPS;
+  constexpr int SLOT_DW = S::SLOT_DW;
+  constexpr int NSLOT = QD * S::area(2) * 4 <= 152 * 1024 ? 2 : 1;
+  constexpr int QUAD_DW = S::area(NSLOT);
+  constexpr int MAIN_DW = QD * QUAD_DW;
   constexpr int Z_DW = BM * Z_ROW;
   constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
   static_assert(R::T_CHUNKS % 64 == 0, "each direct load lands whole in a slot or in the surplus area");
+  static_assert(!MULTI || QD == 1, "a quad computes one part when the workgroup has several");
+  static_assert(LDS_DW * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
-  uint32_t *const junk = lds + 2 * SLOT_DW;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qd = wave_all >> 2;
+  const int wave = wave_all & 3;
+  uint32_t *const qlds = lds + qd * QUAD_DW;
+  uint32_t *const junk = qlds + NSLOT * SLOT_DW;
   const int j = lane & 15;
   const int g = lane >> 4;
   const int nb = blockIdx.x;
-  const int m0 = blockIdx.z * BM;
+  const int m0 = p.row_base + blockIdx.z * BM;
+  const int rend = p.row_end;
   const int M = p.M, K = p.K, N = p.N;
   const int NT = N >> 4;
   const int KB = K >> 7;
 
-  int p_begin = 0, p_end = p.parts;
-  if (p.slab_mode) {
-    p_begin = blockIdx.y;
-    p_end = p_begin + 1;
-  }
+  const int u0 = blockIdx.y * p.unit;  // first part of the workgroup's unit
+  const int p_begin = QD > 1 ? u0 + qd : u0;
+  const int p_end = QD > 1 ? p_begin + 1 : u0 + p.unit;
   const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
   const int kb_end = (int)((int64_t)p_end * KB / p.parts);
   const int nst = kb_end - kb_begin;
@@ -372,22 +547,21 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
   for (int r = 0; r < MT; ++r) {
     const int c = r * WG_THREADS + wave * 64 + lane;  // chunk: k-step c/(4BM), row (c/4)%BM, 16 B piece c%4
     int row = m0 + (c >> 2) % BM;
-    row = row < M ? row : M - 1;
+    row = row < rend ? row : rend - 1;
     a_src[r] = (uint32_t)(((c / (4 * BM)) * M + row) * 32 + (c & 3) * 8);
   }
   auto issue_stage = [&](int stage, int slot) __attribute__((always_inline)) {
-    const int st = min(stage, nst - 1);
-    uint32_t *const ts = lds + slot * SLOT_DW;
+    uint32_t *const ts = qlds + slot * SLOT_DW;
 #pragma unroll
     for (int r = 0; r < T_OPS; ++r) {
       const int q0 = r * WG_THREADS + wave * 64;
       uint32_t *dst = q0 < R::T_CHUNKS ? ts + q0 * 4 : junk + (q0 - R::T_CHUNKS) * 4;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(t_base + st * t_stage + t_src[r]),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(t_base + stage * t_stage + t_src[r]),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < MT; ++r)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a_base + st * a_stage + a_src[r]),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a_base + stage * a_stage + a_src[r]),
                                        (__attribute__((address_space(3))) void *)(ts + R::TSLOT_DW + (r * WG_THREADS + wave * 64) * 4),
                                        16, 0, 0);
   };
@@ -405,15 +579,21 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[mt][h] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Every quad has the same number of stages (the host gives a several-quad
+  // unit equal parts), so all waves meet the same barriers.
   issue_stage(0, 0);
-  issue_stage(1, 1);
-  wait_vmcnt<OPS>();  // stage 0 landed (stage 1's loads were issued after it)
+  if (NSLOT == 2 && nst > 1) {
+    issue_stage(1, 1);
+    wait_vmcnt<OPS>();  // stage 0 landed (stage 1's loads were issued after it)
+  } else {
+    wait_vmcnt<0>();
+  }
   barrier_lds();
 
   int s = 0;
   auto run_stages = [&](int s_end) __attribute__((always_inline)) {
     for (; s < s_end; ++s) {
-      const uint32_t *const tb = lds + (s & 1) * SLOT_DW;
+      const uint32_t *const tb = qlds + (NSLOT == 2 ? (s & 1) : 0) * SLOT_DW;
       const uint32_t *const ab = tb + R::TSLOT_DW + 16 * j + 4 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -430,9 +610,18 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
         for (int mt = 0; mt < MT; ++mt)
           acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b1, acc[mt][1], 0, 0, 0);
       }
-      barrier_lds();           // every wave is done with slot s&1
-      issue_stage(s + 2, s & 1);
-      wait_vmcnt<OPS>();       // stage s+1 landed
+      barrier_lds();  // every wave is done with this slot
+      if constexpr (NSLOT == 2) {
+        if (s + 2 < nst) {
+          issue_stage(s + 2, s & 1);
+          wait_vmcnt<OPS>();  // stage s+1 landed
+        } else {
+          wait_vmcnt<0>();
+        }
+      } else if (s + 1 < nst) {
+        issue_stage(s + 1, 0);
+        wait_vmcnt<0>();
+      }
       barrier_lds();
     }
   };
@@ -464,32 +653,85 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
   } else {
     run_stages(nst);
   }
-  wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
+  wait_vmcnt<0>();
+
+  // The quads' parts in part order through LDS (the stage slots are free:
+  // the last stage ended with a barrier): z = part 0, z = z + part 1, ...;
+  // the last quad adds its part in registers and holds the unit's sum.
+  float *z = reinterpret_cast<float *>(lds);
+  if constexpr (QD > 1) {
+    for (int q = 0; q < QD - 1; ++q) {
+      if (qd == q) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int col = lane_col(wave, j, h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float *zi = z + (mt * 16 + 4 * g + i) * Z_ROW + col;
+              *zi = q == 0 ? acc[mt][h][i] : *zi + acc[mt][h][i];
+            }
+          }
+      }
+      barrier_lds();
+    }
+    if (qd == QD - 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = lane_col(wave, j, h);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][h][i] = z[(mt * 16 + 4 * g + i) * Z_ROW + col] + acc[mt][h][i];
+        }
+    }
+  }
+  const bool writer = qd == QD - 1;
 
   if (p.slab_mode) {
+    const int rows = rend - p.row_base;
+    if (p.counters == nullptr) {
+      if (writer) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        store_partial(p.slabs, p_begin, M, N, m0 + mt * 16 + 4 * g, nb * 128 + lane_col(wave, j, h), acc[mt][h]);
+          for (int h = 0; h < 2; ++h)
+            store_partial(p.slabs, blockIdx.y, rows, N, m0 - p.row_base + mt * 16 + 4 * g,
+                          nb * 128 + lane_col(wave, j, h), acc[mt][h]);
+      }
+      return;
+    }
+    if (writer) {
+      const __amdgpu_buffer_rsrc_t rs = slab_rsrc(p);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          store_partial_coherent(rs, blockIdx.y, rows, N, m0 - p.row_base + mt * 16 + 4 * g,
+                                 nb * 128 + lane_col(wave, j, h), acc[mt][h]);
+    }
+    if (!arrive_last(p)) return;
+    finish_tile(p, m0, BM, wave_all, 4 * QD, lane, z, LDS_DW * 4);
     return;
   }
 
-  barrier_lds();  // every wave is done with the stage slots
-  float *z = reinterpret_cast<float *>(lds);
+  if constexpr (QD == 1) barrier_lds();  // every wave is done with the stage slots
+  if (writer) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int col = lane_col(wave, j, h);
+      for (int h = 0; h < 2; ++h) {
+        const int col = lane_col(wave, j, h);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[(mt * 16 + 4 * g + i) * Z_ROW + col] = acc[mt][h][i];
-    }
+        for (int i = 0; i < 4; ++i) z[(mt * 16 + 4 * g + i) * Z_ROW + col] = acc[mt][h][i];
+      }
+  }
   barrier_lds();
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-  for (int r = wave; r < BM; r += 4) {
+  for (int r = wave_all; r < BM; r += 4 * QD) {
     const int row = m0 + r;
-    if (row >= M) break;
+    if (row >= rend) break;
     const float z0 = z[r * Z_ROW + 2 * lane];
     const float z1 = z[r * Z_ROW + 2 * lane + 1];
     if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
@@ -513,14 +755,14 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_kernel(const GemmParams p) {
 
 template <int MT>
 __device__ __forceinline__ void issue_a_dma(uint32_t *__restrict__ slot, const uint16_t *__restrict__ xs, int m0,
-                                            int M, int K, int k, int wave, int lane) {
+                                            int M, int rend, int k, int wave, int lane) {
   // wave w loads fragments w, w+4, ... of this k-step; lane L of a fragment
   // holds row (L & 15) and k-chunk (L >> 4)
 #pragma unroll
   for (int t = 0; t < MT / 4; ++t) {
     const int mf = wave + 4 * t;
     int row = m0 + 16 * mf + (lane & 15);
-    row = row < M ? row : M - 1;
+    row = row < rend ? row : rend - 1;
     const uint16_t *src = xs + ((int64_t)(k >> 5) * M + row) * 32 + 8 * (lane >> 4);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                      (__attribute__((address_space(3))) void *)(slot + mf * 256), 16, 0, 0);
@@ -550,16 +792,14 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
   const int j = lane & 15;
   const int g = lane >> 4;
   const int nb = blockIdx.x;
-  const int m0 = blockIdx.z * BM;
+  const int m0 = p.row_base + blockIdx.z * BM;
+  const int rend = p.row_end;
   const int M = p.M, K = p.K, N = p.N;
   const int NT = N >> 4;
   const int KB = K >> 7;
 
-  int p_begin = 0, p_end = p.parts;
-  if (p.slab_mode) {
-    p_begin = blockIdx.y;
-    p_end = p_begin + 1;
-  }
+  const int p_begin = blockIdx.y * p.unit;  // the workgroup's unit: parts p_begin .. p_end-1
+  const int p_end = p_begin + p.unit;
   const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
   const int kb_end = (int)((int64_t)p_end * KB / p.parts);
   const int nst = kb_end - kb_begin;
@@ -588,7 +828,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
   // and their results unused).
 #pragma unroll
   for (int i = 0; i < PF; ++i)
-    issue_a_dma<MT>(abuf + i * ASLOT_DW, xs, m0, M, K, k_begin + 32 * min(i, nks - 1), wave, lane);
+    issue_a_dma<MT>(abuf + i * ASLOT_DW, xs, m0, M, rend, k_begin + 32 * min(i, nks - 1), wave, lane);
   load_trellis_stage<BITS>(treg, p.trellis, kb_begin, nb, NT, tid);
   store_trellis_stage<BITS>(treg, tbuf, tid);
   load_trellis_stage<BITS>(treg, p.trellis, kb_begin + min(1, nst - 1), nb, NT, tid);
@@ -606,7 +846,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
       auto kstep = [&](auto ks_c) {
         constexpr int ks = decltype(ks_c)::value;
         const int i = 4 * st + ks;
-        issue_a_dma<MT>(abuf + ((i + PF) % NSLOT) * ASLOT_DW, xs, m0, M, K, k_begin + 32 * min(i + PF, nks - 1),
+        issue_a_dma<MT>(abuf + ((i + PF) % NSLOT) * ASLOT_DW, xs, m0, M, rend, k_begin + 32 * min(i + PF, nks - 1),
                         wave, lane);
         asm volatile("" ::: "memory");  // keep the issue order the counts below assume
         // Vector-memory ops complete in issue order.  This wave's direct loads
@@ -695,7 +935,8 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        store_partial(p.slabs, p_begin, M, N, m0 + mt * 16 + 4 * g, nb * 128 + lane_col(wave, j, h), acc[mt][h]);
+        store_partial(p.slabs, blockIdx.y, rend - p.row_base, N, m0 - p.row_base + mt * 16 + 4 * g,
+                      nb * 128 + lane_col(wave, j, h), acc[mt][h]);
     return;
   }
 
@@ -718,7 +959,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
     __syncthreads();
     for (int r = wave; r < ZROWS; r += 4) {
       const int row = m0 + pass * ZROWS + r;
-      if (row >= M) break;
+      if (row >= rend) break;
       const float z0 = z[r * Z_ROW + 2 * lane];
       const float z1 = z[r * Z_ROW + 2 * lane + 1];
       if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
@@ -762,10 +1003,19 @@ __global__ __launch_bounds__(WG_THREADS) void debug_decode_kernel(const DecodePa
 
 // ---------------------------------------------------------------- launchers
 
+// quads > 1: one part per quad (no register fold); otherwise `multi` folds
+// the workgroup's parts in registers.
 template <int BITS, uint32_t CB, int MT>
-hipError_t launch_gemm_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (multi) hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, true>), grid, dim3(WG_THREADS), 0, s, p);
-  else hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false>), grid, dim3(WG_THREADS), 0, s, p);
+hipError_t launch_gemm_t(int quads, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  switch (quads) {
+    case 1:
+      if (multi) hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, true, 1>), grid, dim3(WG_THREADS), 0, s, p);
+      else hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 1>), grid, dim3(WG_THREADS), 0, s, p);
+      break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 2>), grid, dim3(2 * WG_THREADS), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 4>), grid, dim3(4 * WG_THREADS), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -783,11 +1033,12 @@ hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hip
 // 256/512 -> gemm_wide_kernel (512 threads; 512 for a single part per
 // workgroup only).
 template <int BITS, uint32_t CB>
-hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm_cb(int bm, int quads, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (bm > 64 && quads != 1) return hipErrorInvalidValue;
   switch (bm) {
-    case 16: return launch_gemm_t<BITS, CB, 1>(multi, p, grid, s);
-    case 32: return launch_gemm_t<BITS, CB, 2>(multi, p, grid, s);
-    case 64: return launch_gemm_t<BITS, CB, 4>(multi, p, grid, s);
+    case 16: return launch_gemm_t<BITS, CB, 1>(quads, multi, p, grid, s);
+    case 32: return launch_gemm_t<BITS, CB, 2>(quads, multi, p, grid, s);
+    case 64: return launch_gemm_t<BITS, CB, 4>(quads, multi, p, grid, s);
     case 128: return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
     case 256:
     case 512: return launch_wide_t<BITS, CB>(bm, multi, p, grid, s);
@@ -796,11 +1047,11 @@ hipError_t launch_gemm_cb(int bm, bool multi, const GemmParams &p, dim3 grid, hi
 }
 
 template <int BITS>
-hipError_t launch_gemm_bits(int cb, int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm_bits(int cb, int bm, int quads, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   switch (cb) {
-    case 0: return launch_gemm_cb<BITS, CB_3INST>(bm, multi, p, grid, s);
-    case 1: return launch_gemm_cb<BITS, CB_MCG>(bm, multi, p, grid, s);
-    case 2: return launch_gemm_cb<BITS, CB_MUL1>(bm, multi, p, grid, s);
+    case 0: return launch_gemm_cb<BITS, CB_3INST>(bm, quads, multi, p, grid, s);
+    case 1: return launch_gemm_cb<BITS, CB_MCG>(bm, quads, multi, p, grid, s);
+    case 2: return launch_gemm_cb<BITS, CB_MUL1>(bm, quads, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -821,9 +1072,9 @@ hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
 
 #define EXL3_DEFINE_BITS(B)                                                                        \
   namespace exl3 {                                                                                 \
-  hipError_t launch_gemm_b##B(int cb, int bm, bool multi, const GemmParams &p, dim3 grid,          \
+  hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool multi, const GemmParams &p, dim3 grid, \
                               hipStream_t s) {                                                     \
-    return launch_gemm_bits<B>(cb, bm, multi, p, grid, s);                                         \
+    return launch_gemm_bits<B>(cb, bm, quads, multi, p, grid, s);                                  \
   }                                                                                                \
   hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s) {             \
     return launch_table_bits<B>(cb, p, grid, s);                                                   \

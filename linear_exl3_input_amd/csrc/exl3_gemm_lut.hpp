@@ -20,8 +20,9 @@
 // k-steps ahead; the window is normalized once and all 16 states are cut out
 // at compile-time bit offsets.
 //
-// Work: a unit is one 128-column block and one K part (slab mode) or one
-// block and all parts (fused mode, parts folded in part order).  The 16
+// Work: a unit is one 128-column block and the parts of one workgroup unit
+// (slab mode: p.unit consecutive parts, their sum stored as one slab) or all
+// parts (fused mode), folded in part order at every part end.  The 16
 // waves are 4 teams of 4 waves; wave tw of a team multiplies n-tiles 2tw,
 // 2tw+1 against the (up to) 16 rows.  Units are dealt to the workgroups in
 // turn (unit u to workgroup u mod G, team (u / G) mod 4).  A team walks its units as one
@@ -95,7 +96,8 @@ struct TblUnit {
   uint32_t t;     // trellis byte offset of the unit's first k-step: tile (first k-tile, n-tile 0 of the block)
   const char *a;  // x~ bytes of the unit's first k-step (row 0, k-group 0)
   int nks;        // k-steps (4 per 128-k block; 0: no unit)
-  int nb, part;   // column block; first part (slab mode: the part)
+  int nb, part;   // column block; first part of the unit
+  int slab;       // slab mode: the unit's slab
   int kb_begin;
 };
 
@@ -122,7 +124,9 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
   const int P = p.parts;
   const int nblk = N >> 7;
   const bool slab = p.slab_mode != 0;
-  const int units = slab ? nblk * P : nblk;
+  const int NU = P / p.unit;  // units per column block (slab mode)
+  const int units = slab ? nblk * NU : nblk;
+  const int rows = p.row_end - p.row_base;
   const int stride = gridDim.x * TBL_TEAMS;
   const int rounds = (units + stride - 1) / stride;
 
@@ -146,15 +150,17 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
       u.nks = 0;
       u.nb = 0;
       u.part = 0;
+      u.slab = 0;
       u.kb_begin = 0;
       return u;
     }
     // the divisions run on the vector unit: keep their (wave-uniform)
     // results in scalar registers, so the addresses built from them are too
-    u.nb = __builtin_amdgcn_readfirstlane(slab ? id / P : id);
-    u.part = slab ? id - u.nb * P : 0;
+    u.nb = __builtin_amdgcn_readfirstlane(slab ? id / NU : id);
+    u.slab = slab ? id - u.nb * NU : 0;
+    u.part = u.slab * p.unit;
     u.kb_begin = __builtin_amdgcn_readfirstlane((int)((int64_t)u.part * KB / P));
-    const int kb_end = __builtin_amdgcn_readfirstlane(slab ? (int)((int64_t)(u.part + 1) * KB / P) : KB);
+    const int kb_end = __builtin_amdgcn_readfirstlane((int)((int64_t)(u.part + p.unit) * KB / P));
     u.nks = 4 * (kb_end - u.kb_begin);
     int shard = 0;
     while (shard + 1 < p.n_shards && u.nb >= p.shard_end_blk[shard]) ++shard;
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
     const uint32_t tile = (uint32_t)((g >> 1) * NT + 2 * tw + (j >> 3)) * (TILE_DW * 4);
     wraps = d + NX > TILE_DW;
     // rows past M read row M-1 (finite; their results are never stored)
-    const uint32_t a0 = (uint32_t)(((j < M ? j : M - 1) * 32 + 8 * g) * 2);
+    const uint32_t a0 = (uint32_t)((p.row_base + (j < rows ? j : rows - 1)) * 32 * 2 + 8 * g * 2);
 #pragma unroll
     for (int sl = 0; sl < DEPTH; ++sl) {
       t_win[sl] = tile + 4u * d + (uint32_t)(sl * tsb);
@@ -239,14 +245,10 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float4_t tot0 = acc0, tot1 = acc1;
     if (cu.nks > 0) {
-      // fused mode folds at every part end (first part copied); slab mode
-      // has one part per unit
-      // part q ends at block floor((q+1)*KB/P): KB/P blocks a part plus one
-      // more whenever the running remainder passes P
-      const int pq = KB / P, pr = KB - (KB / P) * P;
+      // fold at every part end (first part copied, later parts added in
+      // part order); part q ends at block floor((q+1)*KB/P)
       int fold_part = cu.part;
-      int fold_rem = pr;
-      int fold_ks = slab ? cu.nks : 4 * (pq + (pr >= P ? 1 : 0));
+      int fold_ks = 4 * ((int)((int64_t)(fold_part + 1) * KB / P) - cu.kb_begin);
       // refills: k-steps ks0+DEPTH.. of this unit, else the next unit's
       // first DEPTH, else (no next unit) this group again, unused
       uint32_t rt = cu.t;
@@ -291,22 +293,14 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
           acc0 = float4_t{0.f, 0.f, 0.f, 0.f};
           acc1 = float4_t{0.f, 0.f, 0.f, 0.f};
           ++fold_part;
-          if (!slab) {
-            fold_rem += pr;
-            int step = pq;
-            if (fold_rem >= P) {
-              fold_rem -= P;
-              step += 1;
-            }
-            fold_ks += 4 * step;
-          }
+          fold_ks = 4 * ((int)((int64_t)(fold_part + 1) * KB / P) - cu.kb_begin);
         }
       }
     }
     if (slab) {
       if (cu.nks > 0) {
-        store_partial(p.slabs, cu.part, M, N, 4 * g, cu.nb * 128 + lane_col(tw, j, 0), tot0);
-        store_partial(p.slabs, cu.part, M, N, 4 * g, cu.nb * 128 + lane_col(tw, j, 1), tot1);
+        store_partial(p.slabs, cu.slab, rows, N, 4 * g, cu.nb * 128 + lane_col(tw, j, 0), tot0);
+        store_partial(p.slabs, cu.slab, rows, N, 4 * g, cu.nb * 128 + lane_col(tw, j, 1), tot1);
       }
     } else {
       // output transform of the team's block through its LDS rows; every
@@ -320,11 +314,12 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
       barrier_lds();
       if (cu.nks > 0) {
         uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-        for (int row = tw; row < M; row += 4) {
-          const float z0 = zb[row * 128 + 2 * lane];
-          const float z1 = zb[row * 128 + 2 * lane + 1];
-          if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, cu.nb * 128, lane);
-          else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, cu.nb * 128, lane);
+        for (int r = tw; r < rows; r += 4) {
+          const float z0 = zb[r * 128 + 2 * lane];
+          const float z1 = zb[r * 128 + 2 * lane + 1];
+          const int64_t row = p.row_base + r;
+          if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
+          else output_row<false>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
         }
       }
       barrier_lds();

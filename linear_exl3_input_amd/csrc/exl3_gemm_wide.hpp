@@ -113,16 +113,14 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   const int j = lane & 15;
   const int g = lane >> 4;
   const int nb = blockIdx.x;
-  const int m0 = blockIdx.z * W::BM;
+  const int m0 = p.row_base + blockIdx.z * W::BM;
+  const int rend = p.row_end;
   const int M = p.M, K = p.K, N = p.N;
   const int NT = N >> 4;
   const int KB = K >> 7;
 
-  int p_begin = 0, p_end = p.parts;
-  if (p.slab_mode) {
-    p_begin = blockIdx.y;
-    p_end = p_begin + 1;
-  }
+  const int p_begin = blockIdx.y * p.unit;  // the workgroup's unit: parts p_begin .. p_end-1
+  const int p_end = p_begin + p.unit;
   const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
   const int kb_end = (int)((int64_t)p_end * KB / p.parts);
   const int nst = kb_end - kb_begin;
@@ -145,7 +143,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
 #pragma unroll
     for (int t = 0; t < W::A_OPS; ++t) {
       int row = m0 + 16 * (wq + W::LOADERS * t) + (lane & 15);
-      row = row < M ? row : M - 1;
+      row = row < rend ? row : rend - 1;
       src[t] = (uint32_t)(row * 32 + 8 * (lane >> 4));
     }
   } else {
@@ -383,11 +381,12 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   const int col_own = lane_col(wq, j, rh);
   const int col_par = lane_col(wq, j, rh ^ 1);
   if (p.slab_mode) {
+    const int rows = rend - p.row_base;
 #pragma unroll
     for (int mt = 0; mt < MF; ++mt) {
-      const int row0 = m0 + rh * RW + mt * 16 + 4 * g;
-      store_partial(p.slabs, p_begin, M, N, row0, nb * 128 + col_own, acc[mt][0]);
-      store_partial(p.slabs, p_begin, M, N, row0, nb * 128 + col_par, acc[mt][1]);
+      const int row0 = m0 - p.row_base + rh * RW + mt * 16 + 4 * g;
+      store_partial(p.slabs, blockIdx.y, rows, N, row0, nb * 128 + col_own, acc[mt][0]);
+      store_partial(p.slabs, blockIdx.y, rows, N, row0, nb * 128 + col_par, acc[mt][1]);
     }
     return;
   }
@@ -413,7 +412,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
     barrier_lds();
     for (int r = wave; r < 64; r += W::WAVES) {
       const int row = m0 + pass * 64 + r;
-      if (row >= M) break;
+      if (row >= rend) break;
       const float z0 = z[r * Z_ROW + 2 * lane];
       const float z1 = z[r * Z_ROW + 2 * lane + 1];
       if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);

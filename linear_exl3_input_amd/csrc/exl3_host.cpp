@@ -72,28 +72,41 @@ exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_s
   return EXL3_OK;
 }
 
-// K parts: a function of (K, N, bits) only.  Enough (column block, part)
-// pairs to occupy the GPU at decode sizes (about 1024), parts of at least
-// four 128-k blocks (or four parts of two blocks, for short K), and the fp32
+// K groups: a function of (K, N, bits) only.  Enough (column block, group)
+// pairs to occupy the GPU at decode sizes (about 1024), groups of at least
+// four 128-k blocks (or four groups of two blocks, for short K), and the fp32
 // partial traffic at 16 rows kept near the trellis bytes it helps to stream
 // (the cuda-exl3 README caps split-k accumulator traffic at ~30% of the
 // weight bytes and discounts it when it stays in cache, "Two further
 // departures" and "Where the time goes"; on this GPU the partials of a
 // decode-size call stay in the 256 MB cache, so the cap is looser).  Shorter
-// parts help one-row calls little and cost batched ones partial traffic: at
-// K=4096, N=2048 eight parts against sixteen are 9% slower at one row and
-// 26% faster at 512.  P divides the number of 128-k blocks so every part has
-// the same length.
-int32_t choose_parts(int32_t K, int32_t N, int32_t bits) {
+// groups help one-row calls little and cost batched ones partial traffic: at
+// K=4096, N=2048 eight groups against sixteen are 9% slower at one row and
+// 26% faster at 512 (when every group was one part).  G divides the number
+// of 128-k blocks so every group has the same length.
+int32_t choose_groups(int32_t K, int32_t N, int32_t bits) {
   const int32_t kb = K / 128;
   const int32_t nblk = N / 128;
   int32_t want = (1024 + nblk - 1) / nblk;
   const int32_t cap_len = std::max(1, std::max(kb / 4, std::min(kb / 2, 4)));
   const int32_t cap_traffic = std::max(1, (int32_t)(1.2 * (double)K * bits / 1024.0));
-  int32_t pmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
-  for (int32_t p = pmax; p >= 1; --p)
-    if (kb % p == 0) return p;
+  int32_t gmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
+  for (int32_t g = gmax; g >= 1; --g)
+    if (kb % g == 0) return g;
   return 1;
+}
+
+// Parts per group: also a function of the shape only.  A small layer (fewer
+// than 512 column-block x group pairs, too few workgroups to give every SIMD
+// of the GPU work at one row) splits each group into 4 (or 2) equal parts, so
+// a one-row call runs one workgroup of four- (two-) part quads per group;
+// larger layers keep one part per group.
+int32_t choose_q(int32_t K, int32_t N, int32_t groups) {
+  const int32_t kb = K / 128;
+  const int32_t nblk = N / 128;
+  if ((int64_t)nblk * groups >= 512) return 1;
+  const int32_t len = kb / groups;
+  return len % 4 == 0 ? 4 : len % 2 == 0 ? 2 : 1;
 }
 
 // Compute units of the current device (queried once per device).
@@ -122,10 +135,17 @@ int device_cus_or_default() {
 }
 
 struct Plan {
-  int32_t parts;
+  int32_t parts;     // P
+  int32_t groups;    // G
   int32_t mode;
   int32_t bm;
   int32_t decoder;
+  int32_t unit;      // parts per workgroup unit
+  int32_t quads;     // small tiles: one part per quad of waves
+  bool multi;        // the workgroup folds unit > 1 parts in registers
+  bool finisher;     // slab mode: the last workgroup of a tile does the output
+  int32_t chunk;     // rows per launch
+  int32_t launches;  // kernels per exl3_linear call
   size_t workspace;
 };
 
@@ -135,16 +155,39 @@ constexpr double TABLE_MIN_WEIGHTS = 33554432.0;  // 2^25
 constexpr int32_t TABLE_MAX_M = 16;
 // The table kernel addresses the trellis with 32-bit byte offsets.
 constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
+// Partial slabs beyond this go through the fused fold (or row chunks).
+constexpr double SLAB_CAP_BYTES = 192.0 * 1024 * 1024;
+// Tiles the finisher's counters can hold (one 32-bit counter each).
+constexpr int64_t MAX_COUNTERS = EXL3_WORKSPACE_COUNTER_BYTES / 4;
+
+size_t slab_bytes(int32_t n_slabs, int32_t rows, int32_t N) {
+  return (size_t)n_slabs * (size_t)((rows + 3) / 4) * 4 * (size_t)N * sizeof(float);
+}
 
 exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out) {
   Plan pl;
-  pl.parts = choose_parts(w->K, w->N, w->bits);
+  const int32_t KB = w->K / 128;
+  const int32_t nblk = w->N / 128;
+  pl.groups = choose_groups(w->K, w->N, w->bits);
+  pl.parts = pl.groups * choose_q(w->K, w->N, pl.groups);
   if (force && force->parts > 0) {
-    if (force->parts > w->K / 128)
-      return fail(EXL3_ERR_INVALID_ARG, "forced parts=%d exceeds the %d blocks of 128 in K", force->parts,
-                  w->K / 128);
+    if (force->parts > KB)
+      return fail(EXL3_ERR_INVALID_ARG, "forced parts=%d exceeds the %d blocks of 128 in K", force->parts, KB);
     pl.parts = force->parts;
+    pl.groups = force->parts;
+    if (force->groups > 0) {
+      if (force->parts % force->groups != 0)
+        return fail(EXL3_ERR_INVALID_ARG, "forced groups=%d do not divide parts=%d (remainder %d)", force->groups,
+                    force->parts, force->parts % force->groups);
+      pl.groups = force->groups;
+    }
+  } else if (force && force->groups > 0) {
+    return fail(EXL3_ERR_INVALID_ARG, "forced groups=%d needs forced parts", force->groups);
   }
+  const int32_t Q = pl.parts / pl.groups;
+  if (Q > 1 && KB % pl.parts != 0)
+    return fail(EXL3_ERR_UNSUPPORTED, "%d parts in groups of %d need equal parts: %d blocks of 128 leave %d",
+                pl.parts, Q, KB, KB % pl.parts);
   // Rows per tile: the smallest tile that holds M rows, up to 512 (the
   // measured best at every layer shape and batch of the plan sweep).
   pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : M <= 128 ? 128 : M <= 256 ? 256 : 512;
@@ -165,46 +208,83 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
                   TABLE_MAX_TRELLIS_BYTES, weights * w->bits / 8.0);
     pl.decoder = force->decoder;
   }
-  if (force && force->bm > 0) {
+  if (bm_forced) {
     if (force->bm != 16 && force->bm != 32 && force->bm != 64 && force->bm != 128 && force->bm != 256 &&
         force->bm != 512)
       return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32, 64, 128, 256 or 512", force->bm);
     pl.bm = force->bm;
   }
-  // Separate fp32 partials (one workgroup per part: P times the workgroups)
-  // while their traffic is small next to the GEMM's; beyond 192 MiB one
-  // workgroup runs all parts of its tile.
-  const double slab_bytes = (double)pl.parts * (double)M * (double)w->N * 4.0;
-  pl.mode = (pl.parts > 1 && slab_bytes <= 192.0 * 1024 * 1024) ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
+  if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = 16;
+  // Mode.  One group: a workgroup folds all parts (one level).  One part per
+  // group: separate fp32 partials (one workgroup per part: P times the
+  // workgroups) while their traffic is small next to the GEMM's; beyond
+  // 192 MiB one workgroup folds all parts of its tile.  Several parts per
+  // group in several groups: always partials, one slab per group (the fused
+  // fold is one level), in row chunks that keep the slabs within 192 MiB.
+  const size_t full_slabs = slab_bytes(pl.groups, M, w->N);
+  if (pl.parts == 1 || pl.groups == 1) pl.mode = EXL3_MODE_FUSED;
+  else if (Q > 1) pl.mode = EXL3_MODE_SLABS;
+  else pl.mode = (double)full_slabs <= SLAB_CAP_BYTES ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
   if (force && force->mode != EXL3_MODE_AUTO && force->mode >= 0) {
     if (force->mode != EXL3_MODE_FUSED && force->mode != EXL3_MODE_SLABS)
       return fail(EXL3_ERR_INVALID_ARG, "forced mode=%d, must be 0 (fused) or 1 (slabs)", force->mode);
+    if (force->mode == EXL3_MODE_FUSED && pl.groups > 1 && Q > 1)
+      return fail(EXL3_ERR_UNSUPPORTED, "mode=fused folds one level; %d groups of %d parts need mode=slabs",
+                  pl.groups, Q);
     pl.mode = force->mode;
   }
   if (pl.parts == 1) pl.mode = EXL3_MODE_FUSED;  // one part: nothing to sum
-  if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = 16;
-  // a fused multi-part tile keeps two accumulator sets: at most 256 rows
-  if (!bm_forced && pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1) pl.bm = 256;
+  // Workgroup unit: all parts (fused), else one group per slab; the
+  // part-sums hook (and a forced unit of 1) writes one slab per part.
+  pl.unit = pl.mode == EXL3_MODE_FUSED ? pl.parts : Q;
+  if (force && force->unit > 0 && pl.mode == EXL3_MODE_SLABS) {
+    if (force->unit != 1 && force->unit != Q)
+      return fail(EXL3_ERR_INVALID_ARG, "forced unit=%d, must be 1 or the %d parts of a group", force->unit, Q);
+    pl.unit = force->unit;
+  }
+  // 512-row tiles hold one accumulator set: a unit of one part only
+  if (pl.bm == 512 && pl.unit > 1) {
+    if (bm_forced)
+      return fail(EXL3_ERR_UNSUPPORTED, "bm=512 runs one K part per workgroup; units of %d parts need bm<=256",
+                  pl.unit);
+    pl.bm = 256;
+  }
   // 512-row tiles run one workgroup per CU: with fewer tiles than CUs,
   // 256-row tiles (twice the workgroups) finish first
   if (!bm_forced && pl.bm == 512) {
-    const int64_t tiles = (int64_t)(w->N / 128) * (pl.mode == EXL3_MODE_SLABS ? pl.parts : 1) * ((M + 511) / 512);
+    const int64_t tiles =
+        (int64_t)nblk * (pl.mode == EXL3_MODE_SLABS ? pl.parts / pl.unit : 1) * ((M + 511) / 512);
     if (tiles < device_cus_or_default()) pl.bm = 256;
   }
-  // 512-row tiles hold one accumulator set: one part per workgroup only
-  if (pl.bm == 512 && pl.mode == EXL3_MODE_FUSED && pl.parts > 1)
-    return fail(EXL3_ERR_UNSUPPORTED, "bm=512 runs one K part per workgroup; %d parts need mode=slabs or bm<=256",
-                pl.parts);
-  // slab layout [parts][ceil(M/4)][N][4] fp32 (rows padded to a multiple of 4)
+  // Small tiles: a unit of 2 or 4 equal parts runs as that many quads of
+  // waves, one part each; other units fold in registers.
+  pl.quads = 1;
+  pl.multi = pl.unit > 1;
+  if (pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && (pl.unit == 2 || pl.unit == 4) && KB % pl.parts == 0) {
+    pl.quads = pl.unit;
+    pl.multi = false;
+  }
+  const int32_t n_slabs = pl.parts / pl.unit;
+  pl.chunk = M;
+  if (pl.mode == EXL3_MODE_SLABS && (double)slab_bytes(n_slabs, M, w->N) > SLAB_CAP_BYTES) {
+    const double per_tile = (double)slab_bytes(n_slabs, pl.bm, w->N);
+    pl.chunk = (int32_t)std::max<double>(pl.bm, std::floor(SLAB_CAP_BYTES / per_tile) * pl.bm);
+    pl.chunk = std::min(pl.chunk, M);
+  }
+  pl.finisher = pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 &&
+                (int64_t)nblk * ((pl.chunk + pl.bm - 1) / pl.bm) <= MAX_COUNTERS;
+  pl.launches = pl.mode == EXL3_MODE_SLABS && !pl.finisher ? 2 : 1;
+  if (pl.chunk < M && M > 0) pl.launches *= (M + pl.chunk - 1) / pl.chunk;
+  // counters, then slabs [n_slabs][ceil(chunk/4)][N][4] fp32
   pl.workspace = pl.mode == EXL3_MODE_SLABS
-                     ? (size_t)pl.parts * (size_t)((M + 3) / 4) * 4 * (size_t)w->N * sizeof(float)
+                     ? (size_t)EXL3_WORKSPACE_COUNTER_BYTES + slab_bytes(n_slabs, pl.chunk, w->N)
                      : 0;
   *out = pl;
   return EXL3_OK;
 }
 
-exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype, float *slabs,
-                       const Plan &pl, hipStream_t s, bool with_output);
+exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
+                       uint32_t *counters, float *slabs, const Plan &pl, hipStream_t s, bool with_output);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -274,9 +354,12 @@ exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan) {
   Plan pl;
   if ((st = make_plan(w, M, nullptr, &pl)) != EXL3_OK) return st;
   plan->parts = pl.parts;
+  plan->groups = pl.groups;
   plan->mode = pl.mode;
   plan->bm = pl.bm;
   plan->decoder = pl.decoder;
+  plan->unit = pl.unit;
+  plan->launches = pl.launches;
   plan->workspace = pl.workspace;
   return EXL3_OK;
 }
@@ -303,17 +386,23 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
     if (!aligned16(workspace)) return fail(EXL3_ERR_INVALID_ARG, "workspace=%p is not 16-byte aligned", workspace);
   }
 
-  return run_linear(w, x_rot, M, y, y_dtype, static_cast<float *>(workspace), pl, (hipStream_t)stream, true);
+  uint32_t *counters = static_cast<uint32_t *>(workspace);
+  float *slabs = pl.workspace > 0
+                     ? reinterpret_cast<float *>(static_cast<char *>(workspace) + EXL3_WORKSPACE_COUNTER_BYTES)
+                     : nullptr;
+  return run_linear(w, x_rot, M, y, y_dtype, counters, slabs, pl, (hipStream_t)stream, true);
 }
 
 }  // extern "C"
 
 namespace {
 
-// The GEMM stage of a plan (partials to `slabs` in slab mode), then, if
-// `with_output` and in slab mode, the ordered part sum + output transform.
-exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype, float *slabs,
-                       const Plan &pl, hipStream_t s, bool with_output) {
+// The GEMM stage of a plan, in row chunks of pl.chunk rows: partials to
+// `slabs` in slab mode, then, if `with_output` and in slab mode, the ordered
+// part sum + output transform (in the GEMM's last workgroup of each tile when
+// the plan has the finisher, else as a second kernel).
+exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
+                       uint32_t *counters, float *slabs, const Plan &pl, hipStream_t s, bool with_output) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.trellis = w->trellis;
@@ -321,10 +410,13 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
   p.svh = w->svh;
   p.y = y;
   p.slabs = slabs;
+  p.counters = with_output && pl.finisher ? counters : nullptr;
   p.M = M;
   p.K = w->K;
   p.N = w->N;
   p.parts = pl.parts;
+  p.unit = pl.unit;
+  p.fold_q = pl.parts / pl.groups / pl.unit;  // slabs per group
   p.slab_mode = pl.mode == EXL3_MODE_SLABS ? 1 : 0;
   p.out_bf16 = y_dtype == EXL3_BF16 ? 1 : 0;
   p.n_shards = w->n_shards;
@@ -333,23 +425,29 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
     end += w->shard_n[s] / 128;
     p.shard_end_blk[s] = end;
   }
+  const int32_t n_units = p.slab_mode ? pl.parts / pl.unit : 1;
   hipError_t e;
-  if (pl.decoder == EXL3_DECODER_TABLE) {
-    int cus = 0;
-    if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
-    const int64_t units = (int64_t)(w->N / 128) * (p.slab_mode ? pl.parts : 1);
-    const int grid = (int)std::min<int64_t>(cus, units);
-    e = exl3::launch_gemm_table(w->bits, w->codebook, p, grid, s);
-    if (e != hipSuccess) return launch_error(e, "table GEMM launch");
-  } else {
-    const dim3 grid((unsigned)(w->N / 128), (unsigned)(p.slab_mode ? pl.parts : 1),
-                    (unsigned)((M + pl.bm - 1) / pl.bm));
-    e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, !p.slab_mode && pl.parts > 1, p, grid, s);
-    if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
-  }
-  if (p.slab_mode && with_output) {
-    e = exl3::launch_epilogue(p.slabs, pl.parts, M, w->N, w->svh, y, p.out_bf16 != 0, s);
-    if (e != hipSuccess) return launch_error(e, "part-sum epilogue launch");
+  for (int32_t r0 = 0; r0 < M; r0 += pl.chunk) {
+    p.row_base = r0;
+    p.row_end = std::min(M, r0 + pl.chunk);
+    if (pl.decoder == EXL3_DECODER_TABLE) {
+      int cus = 0;
+      if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
+      const int64_t units = (int64_t)(w->N / 128) * n_units;
+      const int grid = (int)std::min<int64_t>(cus, units);
+      e = exl3::launch_gemm_table(w->bits, w->codebook, p, grid, s);
+      if (e != hipSuccess) return launch_error(e, "table GEMM launch");
+    } else {
+      const dim3 grid((unsigned)(w->N / 128), (unsigned)n_units,
+                      (unsigned)((p.row_end - p.row_base + pl.bm - 1) / pl.bm));
+      e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, pl.quads, pl.multi, p, grid, s);
+      if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
+    }
+    if (p.slab_mode && with_output && p.counters == nullptr) {
+      e = exl3::launch_epilogue(p.slabs, n_units, p.fold_q, p.row_base, p.row_end, w->N, w->svh, y,
+                                p.out_bf16 != 0, s);
+      if (e != hipSuccess) return launch_error(e, "part-sum epilogue launch");
+    }
   }
   return EXL3_OK;
 }
@@ -374,22 +472,38 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
   if (force) f = *force;
   else {
     f.parts = -1;
+    f.groups = -1;
     f.bm = -1;
     f.decoder = EXL3_DECODER_AUTO;
+    f.unit = -1;
+    f.launches = 0;
     f.workspace = 0;
   }
   f.mode = EXL3_MODE_SLABS;
+  if (f.unit <= 0) f.unit = 1;  // one slab per part unless asked otherwise
   Plan pl;
   if ((st = make_plan(w, M, &f, &pl)) != EXL3_OK) return st;
   if (M == 0) return EXL3_OK;
   pl.mode = EXL3_MODE_SLABS;  // also for one part
-  const size_t need = (size_t)pl.parts * (size_t)((M + 3) / 4) * 4 * (size_t)w->N * sizeof(float);
+  pl.unit = pl.parts == 1 ? 1 : pl.unit;
+  if (pl.bm == 512 && pl.unit > 1) pl.bm = 256;
+  pl.quads = 1;
+  pl.multi = pl.unit > 1;
+  if (pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && (pl.unit == 2 || pl.unit == 4) &&
+      (w->K / 128) % pl.parts == 0) {
+    pl.quads = pl.unit;
+    pl.multi = false;
+  }
+  pl.chunk = M;
+  pl.finisher = false;
+  const int32_t n_slabs = pl.parts / pl.unit;
+  const size_t need = slab_bytes(n_slabs, M, w->N);
   if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
   if ((st = check_ptr(z_parts, "z_parts")) != EXL3_OK) return st;
   if (z_bytes < need)
-    return fail(EXL3_ERR_WORKSPACE, "z_parts holds %zu bytes; %d parts of %d rows need %zu (short by %zu)", z_bytes,
-                pl.parts, M, need, need - z_bytes);
-  return run_linear(w, x_rot, M, nullptr, EXL3_BF16, z_parts, pl, (hipStream_t)stream, false);
+    return fail(EXL3_ERR_WORKSPACE, "z_parts holds %zu bytes; %d slabs of %d rows need %zu (short by %zu)", z_bytes,
+                n_slabs, M, need, need - z_bytes);
+  return run_linear(w, x_rot, M, nullptr, EXL3_BF16, nullptr, z_parts, pl, (hipStream_t)stream, false);
 }
 
 exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream) {
@@ -416,20 +530,22 @@ exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream) 
   return e == hipSuccess ? EXL3_OK : launch_error(e, "decode launch");
 }
 
-exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t M, const exl3_weight *w, void *y,
-                                int32_t y_dtype, void *stream) {
+exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t groups, int32_t M,
+                                const exl3_weight *w, void *y, int32_t y_dtype, void *stream) {
   clear_error();
   exl3_status st = validate_weight(w, false, false);
   if (st != EXL3_OK) return st;
   if (n_parts < 1 || n_parts > 4096) return fail(EXL3_ERR_INVALID_ARG, "n_parts=%d, must be 1..4096", n_parts);
+  if (groups < 1 || n_parts % groups != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "groups=%d must be positive and divide n_parts=%d", groups, n_parts);
   if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
     return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
   if (M < 0 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
   if (M == 0) return EXL3_OK;
   if ((st = check_ptr(z_parts, "z_parts")) != EXL3_OK) return st;
   if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
-  const hipError_t e =
-      exl3::launch_epilogue(z_parts, n_parts, M, w->N, w->svh, y, y_dtype == EXL3_BF16, (hipStream_t)stream);
+  const hipError_t e = exl3::launch_epilogue(z_parts, n_parts, n_parts / groups, 0, M, w->N, w->svh, y,
+                                             y_dtype == EXL3_BF16, (hipStream_t)stream);
   return e == hipSuccess ? EXL3_OK : launch_error(e, "epilogue launch");
 }
 

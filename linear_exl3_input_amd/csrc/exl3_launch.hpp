@@ -11,13 +11,22 @@ constexpr int MAX_SHARDS = 16;
 
 struct GemmParams {
   const uint16_t *trellis;  // [K/16][N/16][16*bits]
-  const uint16_t *x_rot;    // [n_shards][M][K] fp16 bits
+  const uint16_t *x_rot;    // [n_shards][K/32][M][32] fp16 bits (k-step tiles)
   const uint16_t *svh;      // [N] fp16 bits
-  void *y;                  // [M][N] bf16/fp16 (fused mode)
-  float *slabs;             // [P][M][N] fp32 (slab mode)
-  int32_t M, K, N;
-  int32_t parts;            // P
-  int32_t slab_mode;        // 1: one part per workgroup (blockIdx.y), write slab
+  void *y;                  // [M][N] bf16/fp16
+  float *slabs;             // [units][ceil(rows/4)][N][4] fp32 (slab mode)
+  uint32_t *counters;       // slab mode: per-tile arrival counters (zero on
+                            // entry, left zero); null: partials only
+  int32_t M;                // rows of x_rot (the row stride of its k-step tiles)
+  int32_t row_base;         // this launch computes rows [row_base, row_end);
+  int32_t row_end;          // slab row r is row row_base + r
+  int32_t K, N;
+  int32_t parts;            // P K parts
+  int32_t unit;             // parts per workgroup unit: a workgroup folds the
+                            // parts [unit*blockIdx.y, unit*(blockIdx.y+1)) in
+                            // order (fused mode: unit = P, blockIdx.y = 0)
+  int32_t fold_q;           // finisher: consecutive slabs that form one group
+  int32_t slab_mode;        // 1: write the unit's sum to slab blockIdx.y
   int32_t out_bf16;
   int32_t n_shards;
   int32_t shard_end_blk[MAX_SHARDS];  // exclusive end of shard s, in 128-col blocks
@@ -33,7 +42,7 @@ struct DecodeParams {
 // choices that select a template instance: bm 16/32/64 -> gemm_kernel,
 // 128 -> gemm_big_kernel, 256/512 -> gemm_wide_kernel).  Return hipSuccess or the
 // launch error.
-hipError_t launch_gemm(int bits, int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid,
+hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool multi_part, const GemmParams &p, dim3 grid,
                        hipStream_t s);
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s);
 // Table-decode GEMM (M <= 16): `grid` persistent workgroups of 1024 threads,
@@ -42,14 +51,17 @@ hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hi
 
 hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
                                   int32_t n_shards, uint16_t *x_rot, hipStream_t s);
-hipError_t launch_epilogue(const float *slabs, int32_t parts, int32_t M, int32_t N, const uint16_t *svh,
-                           void *y, bool out_bf16, hipStream_t s);
+// Ordered sum of n_slabs partial slabs (groups of fold_q consecutive slabs
+// folded first, then the groups in order) + output transform, for rows
+// [row_base, row_end) (slab row r = row row_base + r).
+hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, int32_t row_base, int32_t row_end,
+                           int32_t N, const uint16_t *svh, void *y, bool out_bf16, hipStream_t s);
 hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
 
 // Per-bit-width entry points, defined in gemm_b<bits>.hip.
 #define EXL3_DECLARE_BITS(B)                                                                  \
-  hipError_t launch_gemm_b##B(int cb, int bm, bool multi_part, const GemmParams &p, dim3 grid, \
-                              hipStream_t s);                                                  \
+  hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool multi_part, const GemmParams &p,    \
+                              dim3 grid, hipStream_t s);                                        \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);            \
   hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s);
 EXL3_DECLARE_BITS(1)

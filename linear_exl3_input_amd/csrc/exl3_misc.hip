@@ -62,59 +62,42 @@ hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t
 
 // ------------------------------------------------- ordered part sum + output
 //
-// z = ((part0 + part1) + part2) + ... in fp32, then y = rne(svh * 2^-3 *
+// z = the ordered sum of the partial slabs (reduce_rows4: groups of fold_q
+// slabs, then the groups, each in order) in fp32, then y = rne(svh * 2^-3 *
 // H128(z)) (TensorFold PR, "Arithmetic" step 3 and its ordered part sum).
-// The partials are stored [part][M/4][N][4] (rows padded to a multiple of 4):
+// The partials are stored [slab][M4][N][4] (rows padded to a multiple of 4):
 // the four rows of one column are 16 contiguous bytes, which is what a GEMM
 // lane holds for one output column, so both the GEMM's stores and these
 // loads move whole cache lines.  One wave per (4-row group, 128-column
-// block): lane l loads columns 2l and 2l+1 of the four rows, every part's
-// loads are in flight before the ordered adds, then four output rows.
+// block) of rows [row_base, row_end).
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t parts,
-                                                       int32_t M, int32_t N, const uint16_t *__restrict__ svh,
+__global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t n_slabs,
+                                                       int32_t fold_q, int32_t row_base, int32_t row_end,
+                                                       int32_t N, const uint16_t *__restrict__ svh,
                                                        uint16_t *__restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nblocks = N >> 7;
-  const int M4 = (M + 3) >> 2;
+  const int rows = row_end - row_base;
+  const int M4 = (rows + 3) >> 2;
   if (item >= (int64_t)M4 * nblocks) return;
   const int64_t m4 = item / nblocks;
   const int n0 = (int)(item - m4 * nblocks) * 128;
-  const int64_t slab = (int64_t)M4 * N * 4;
-  const float4_t *src = reinterpret_cast<const float4_t *>(slabs + (m4 * N + n0 + 2 * lane) * 4);
-  float4_t a0 = src[0], a1 = src[1];
-  constexpr int U = 8;
-  for (int p = 1; p < parts; p += U) {
-    float4_t v0[U], v1[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (p + u < parts) {
-        v0[u] = src[(p + u) * slab / 4];
-        v1[u] = src[(p + u) * slab / 4 + 1];
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (p + u < parts) {
-        a0 = a0 + v0[u];
-        a1 = a1 + v1[u];
-      }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t m = 4 * m4 + r;
-    if (m < M) output_row<OUT_BF16>(a0[r], a1[r], svh, y + m * N, n0, lane);
-  }
+  const int64_t r0 = 4 * m4;
+  reduce_rows4<OUT_BF16>(slabs, n_slabs, fold_q, (int64_t)M4 * N * 4, N, m4, n0, svh, y, row_base + r0,
+                         (int)min((int64_t)4, rows - r0), lane);
 }
 
-hipError_t launch_epilogue(const float *slabs, int32_t parts, int32_t M, int32_t N, const uint16_t *svh,
-                           void *y, bool out_bf16, hipStream_t s) {
-  const int64_t items = (int64_t)((M + 3) / 4) * (N / 128);
+hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, int32_t row_base, int32_t row_end,
+                           int32_t N, const uint16_t *svh, void *y, bool out_bf16, hipStream_t s) {
+  const int64_t items = (int64_t)((row_end - row_base + 3) / 4) * (N / 128);
   const dim3 grid((unsigned)((items + 3) / 4));
   if (out_bf16)
-    hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, parts, M, N, svh, (uint16_t *)y);
+    hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end, N,
+                       svh, (uint16_t *)y);
   else
-    hipLaunchKernelGGL((epilogue_kernel<false>), grid, dim3(256), 0, s, slabs, parts, M, N, svh, (uint16_t *)y);
+    hipLaunchKernelGGL((epilogue_kernel<false>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end,
+                       N, svh, (uint16_t *)y);
   return hipGetLastError();
 }
 
@@ -140,16 +123,17 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s) {
 
 // ------------------------------------------------------ bit-width dispatch
 
-hipError_t launch_gemm(int bits, int cb, int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool multi, const GemmParams &p, dim3 grid,
+                       hipStream_t s) {
   switch (bits) {
-    case 1: return launch_gemm_b1(cb, bm, multi, p, grid, s);
-    case 2: return launch_gemm_b2(cb, bm, multi, p, grid, s);
-    case 3: return launch_gemm_b3(cb, bm, multi, p, grid, s);
-    case 4: return launch_gemm_b4(cb, bm, multi, p, grid, s);
-    case 5: return launch_gemm_b5(cb, bm, multi, p, grid, s);
-    case 6: return launch_gemm_b6(cb, bm, multi, p, grid, s);
-    case 7: return launch_gemm_b7(cb, bm, multi, p, grid, s);
-    case 8: return launch_gemm_b8(cb, bm, multi, p, grid, s);
+    case 1: return launch_gemm_b1(cb, bm, quads, multi, p, grid, s);
+    case 2: return launch_gemm_b2(cb, bm, quads, multi, p, grid, s);
+    case 3: return launch_gemm_b3(cb, bm, quads, multi, p, grid, s);
+    case 4: return launch_gemm_b4(cb, bm, quads, multi, p, grid, s);
+    case 5: return launch_gemm_b5(cb, bm, quads, multi, p, grid, s);
+    case 6: return launch_gemm_b6(cb, bm, quads, multi, p, grid, s);
+    case 7: return launch_gemm_b7(cb, bm, quads, multi, p, grid, s);
+    case 8: return launch_gemm_b8(cb, bm, quads, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

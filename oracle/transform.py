@@ -161,12 +161,27 @@ def output_transform_f64(z64: np.ndarray, svh_bits: np.ndarray) -> np.ndarray:
     return h * OUTPUT_SCALE * f16_from_bits(svh_bits).astype(np.float64)[None, :]
 
 
-def reduce_parts_f32(parts: np.ndarray) -> np.ndarray:
-    """Ordered fp32 sum of K-part partials: ((p0 + p1) + p2) + ...
+def reduce_parts_f32(parts: np.ndarray, groups: int | None = None) -> np.ndarray:
+    """Ordered fp32 sum of K-part partials.
 
-    ``parts`` [P, M, N] float32; the first part is taken as is (no 0 + p0).
+    With ``groups`` = G (default P, one part per group): the P/G consecutive
+    parts of each group are added in part order, then the G group sums in
+    group order, each fold taking its first term as is (no 0 + p0).  With
+    G = P this is ((p0 + p1) + p2) + ..., the "last part adds the parts in
+    part order" of the TensorFold PR ("Arithmetic"); the grouped tree is the
+    library's reading for small layers, fixed by the shape like P itself.
+
+    ``parts`` [P, M, N] float32.
     """
-    acc = np.array(parts[0], dtype=np.float32, copy=True)
-    for p in range(1, parts.shape[0]):
-        acc = acc + parts[p].astype(np.float32)
-    return acc
+    P = parts.shape[0]
+    G = P if groups is None else groups
+    if G < 1 or P % G:
+        raise ValueError(f"{G} groups do not divide {P} parts")
+    q = P // G
+    total = None
+    for gi in range(G):
+        gsum = np.array(parts[gi * q], dtype=np.float32, copy=True)
+        for p in range(gi * q + 1, (gi + 1) * q):
+            gsum = gsum + parts[p].astype(np.float32)
+        total = gsum if total is None else total + gsum
+    return total

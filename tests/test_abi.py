@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(L, name), name
-    assert L.exl3_abi_version() == 2
+    assert L.exl3_abi_version() == ex.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -111,20 +111,57 @@ def _plan(w, M):
     return p
 
 
+def F(parts=-1, mode=-1, bm=-1, decoder=-1, groups=-1, unit=-1):
+    """A forced plan (fields <= 0 keep the automatic choice)."""
+    return ex._Plan(parts, groups, mode, bm, decoder, unit, 0, 0)
+
+
+CB = ex.COUNTER_BYTES
+
+
 def test_parts_depend_on_shape_only():
     for lay in wl.LAYERS:
         w = view(lay.K, lay.shards, lay.bits, lay.cb)
-        parts = {_plan(w, M).parts for M in (1, 16, 64, 65, 512, 4096)}
-        assert len(parts) == 1, (lay.name, parts)
-        P = parts.pop()
-        assert (lay.K // 128) % P == 0
+        trees = {(_plan(w, M).parts, _plan(w, M).groups) for M in (1, 16, 64, 65, 512, 4096)}
+        assert len(trees) == 1, (lay.name, trees)
+        P, G = trees.pop()
+        assert (lay.K // 128) % P == 0 and P % G == 0
+
+
+def test_small_layers_split_groups_into_parts():
+    """Fewer than 512 (column block, group) pairs: each group of 4 (or 2)
+    blocks splits into parts of one block; larger layers keep one part per
+    group."""
+    expert = view(4096, (2048,), 4, 1)  # 16 blocks x 8 groups = 128 pairs
+    p = _plan(expert, 1)
+    assert (p.parts, p.groups, p.unit, p.mode, p.launches) == (32, 8, 4, ex.EXL3_MODE_SLABS, 1)
+    assert p.workspace == CB + 8 * 4 * 2048 * 4
+    p = _plan(expert, 512)  # group slabs, separate output kernel
+    assert (p.parts, p.groups, p.unit, p.bm, p.launches) == (32, 8, 4, 256, 2)
+    assert p.workspace == CB + 8 * 512 * 2048 * 4
+    assert _plan(view(2048, (4096,), 4, 1), 16).parts == 16
+    assert _plan(view(1024, (1024,), 4, 0), 1).parts == 8 and _plan(view(1024, (1024,), 4, 0), 1).groups == 4
+    q = _plan(view(5120, (12288,), 6, 2), 32)  # 96 blocks x 10 groups: one part per group
+    assert (q.parts, q.groups) == (10, 10)
+
+
+def test_row_chunks_keep_slabs_bounded():
+    """Several parts per group at a batch whose group slabs exceed 192 MiB:
+    slab mode in row chunks (one chunk's slabs in the workspace)."""
+    w = view(4096, (4096,), 4, 1)  # 32 blocks x 8 groups of 4 parts
+    p = _plan(w, 4096)
+    assert p.mode == ex.EXL3_MODE_SLABS and p.groups == 8 and p.parts == 32
+    assert p.workspace <= CB + 192 * 2 ** 20 and p.launches > 2
+    L = ex.load()
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4096, ctypes.byref(F(mode=ex.EXL3_MODE_FUSED))) == 0
+    assert "fused folds one level" in last_error()
 
 
 def test_plan_modes_and_workspace():
     w = view(17408, (5120,), 6, 2)
     small, big = _plan(w, 16), _plan(w, 4096)
     assert small.parts == big.parts > 1
-    assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == small.parts * 16 * 5120 * 4
+    assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == CB + small.parts * 16 * 5120 * 4
     assert big.mode == ex.EXL3_MODE_FUSED and big.workspace == 0
     assert small.bm == 16 and _plan(w, 24).bm == 32 and big.bm == 256
     mid = _plan(w, 512)  # 17 parts x 512 x 5120 x 4 B = 178 MB of partials: slabs of 512 rows
@@ -136,12 +173,15 @@ def test_plan_modes_and_workspace():
 def test_forced_512_row_tile_needs_one_part_per_workgroup():
     L = ex.load()
     w = view(4096, (2048,), 4, 1)
-    fused_multi = ex._Plan(4, ex.EXL3_MODE_FUSED, 512, 0, 0)
+    fused_multi = F(4, ex.EXL3_MODE_FUSED, 512, 0)
     assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(fused_multi)) == 0
     assert "bm=512" in last_error()
-    slabs = ex._Plan(4, ex.EXL3_MODE_SLABS, 512, 0, 0)
-    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(slabs)) == 4 * 600 * 2048 * 4
-    single = ex._Plan(1, ex.EXL3_MODE_AUTO, 512, 0, 0)
+    slabs = F(4, ex.EXL3_MODE_SLABS, 512, 0)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(slabs)) == CB + 4 * 600 * 2048 * 4
+    grouped = F(4, ex.EXL3_MODE_SLABS, 512, 0, groups=2)  # units of 2 parts: two accumulator sets
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(grouped)) == 0
+    assert "units of 2 parts" in last_error()
+    single = F(1, ex.EXL3_MODE_AUTO, 512, 0)
     assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 600, ctypes.byref(single)) == 0
     assert L.exl3_linear_ex(ctypes.byref(w), FAKE, 600, FAKE, 1, FAKE, 1 << 30, None,
                             ctypes.byref(fused_multi)) == 2  # EXL3_ERR_UNSUPPORTED, before any launch
@@ -150,7 +190,7 @@ def test_forced_512_row_tile_needs_one_part_per_workgroup():
 def test_part_sums_hook_checks_its_buffer():
     L = ex.load()
     w = view(1024, (256,), 4, 1)
-    f = ex._Plan(4, -1, -1, -1, 0)
+    f = F(4)
     need = 4 * 4 * 256 * 4  # 4 parts x 4 rows x 256 columns x fp32
     assert L.exl3_debug_parts(ctypes.byref(w), FAKE, 3, FAKE, need - 16, None, ctypes.byref(f)) == 3
     assert "short by 16" in last_error()
@@ -169,13 +209,35 @@ def test_table_decoder_choice_and_limits():
     assert _plan(view(5120, (12288,), 6, 2), 1).decoder == ex.EXL3_DECODER_TABLE  # 62.9M weights
     assert _plan(view(4096, (2048,), 4, 1), 1).decoder == ex.EXL3_DECODER_ALU     # 8.4M weights
     small = view(1024, (1024,), 4, 0)
-    slabs = ex._Plan(4, ex.EXL3_MODE_SLABS, -1, ex.EXL3_DECODER_TABLE, 0)
-    assert L.exl3_workspace_bytes_ex(ctypes.byref(small), 16, ctypes.byref(slabs)) == 4 * 16 * 1024 * 4
-    too_tall = ex._Plan(-1, -1, -1, ex.EXL3_DECODER_TABLE, 0)
+    slabs = F(4, ex.EXL3_MODE_SLABS, -1, ex.EXL3_DECODER_TABLE)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(small), 16, ctypes.byref(slabs)) == CB + 4 * 16 * 1024 * 4
+    too_tall = F(decoder=ex.EXL3_DECODER_TABLE)
     assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 17, FAKE, 1, FAKE, 1 << 30, None,
                             ctypes.byref(too_tall)) == 2  # EXL3_ERR_UNSUPPORTED
     assert "at most 16 rows" in last_error()
-    unknown = ex._Plan(-1, -1, -1, 7, 0)
+    unknown = F(decoder=7)
     assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 4, FAKE, 1, FAKE, 1 << 30, None,
                             ctypes.byref(unknown)) == 1  # EXL3_ERR_INVALID_ARG
     assert "decoder=7" in last_error()
+
+
+def test_forced_groups_checked():
+    L = ex.load()
+    w = view(1024, (256,), 4, 1)  # 8 blocks of 128 in K
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4, ctypes.byref(F(4, groups=3))) == 0
+    assert "groups=3 do not divide parts=4" in last_error()
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4, ctypes.byref(F(groups=2))) == 0
+    assert "needs forced parts" in last_error()
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4, ctypes.byref(F(6, groups=3))) == 0
+    assert "equal parts" in last_error()  # 6 parts of 8 blocks, grouped: unequal
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4, ctypes.byref(F(4, groups=2))) == CB + 2 * 4 * 256 * 4
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4, ctypes.byref(F(4, groups=2, unit=1))) == CB + 4 * 4 * 256 * 4
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4, ctypes.byref(F(4, groups=2, unit=3))) == 0
+    assert "unit=3" in last_error()
+
+
+def test_epilogue_hook_checks_groups():
+    L = ex.load()
+    w = view(256, (256,), 4, 1)
+    assert L.exl3_debug_epilogue(FAKE, 6, 4, 3, ctypes.byref(w), FAKE, 1, None) == 1
+    assert "groups=4" in last_error()

@@ -77,9 +77,10 @@ def test_input_transform_one_hot_closed_form():
 
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("P,M,N", [(1, 3, 128), (3, 17, 384), (8, 64, 256)])
-def test_output_stage_bit_exact(out_dtype, P, M, N):
-    banner(f"epilogue {out_dtype} P={P} M={M} N={N}")
+@pytest.mark.parametrize("P,G,M,N", [(1, 1, 3, 128), (3, 3, 17, 384), (8, 8, 64, 256), (8, 2, 9, 256),
+                                     (12, 3, 5, 128)])
+def test_output_stage_bit_exact(out_dtype, P, G, M, N):
+    banner(f"epilogue {out_dtype} P={P} G={G} M={M} N={N}")
     rng = np.random.default_rng(2000 + P + M + N)
     z = (rng.standard_normal((P, M, N)) * np.exp2(rng.integers(-6, 6, (P, M, N)))).astype(np.float32)
     svh = (np.where(rng.integers(0, 2, N) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, N))
@@ -89,8 +90,8 @@ def test_output_stage_bit_exact(out_dtype, P, M, N):
     suh = np.full((1, 128), 0x3C00, dtype=np.uint16)
     w = ex.Exl3Weight(dev16(trellis), dev16(suh, torch.float16), dev16(svh, torch.float16), 4, "mcg", (N,))
     dt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
-    got = bits16(ex.debug_epilogue(w, torch.from_numpy(slab_layout(z)).cuda(), M, dt))
-    want = otf.output_transform_f32(otf.reduce_parts_f32(z), svh, out_dtype)
+    got = bits16(ex.debug_epilogue(w, torch.from_numpy(slab_layout(z)).cuda(), M, dt, groups=G))
+    want = otf.output_transform_f32(otf.reduce_parts_f32(z, G), svh, out_dtype)
     assert np.array_equal(got, want)
     del lay
 
@@ -248,6 +249,90 @@ def test_part_sums_stage(decoder, parts):
     y = bits16(ex.linear(w, xr, torch.bfloat16, parts=parts, decoder=decoder))
     y2 = bits16(ex.debug_epilogue(w, z, M))
     assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("M", [5, 40, 100, 300])
+def test_grouped_tree_schedules_agree(M):
+    """Eight one-block parts in two groups (the small-layer tree): quads of
+    waves with the finishing workgroup (16-64 rows), register folds of a
+    group (128-256 rows), one slab per part with the two-level output stage,
+    and the GEMM stage + output stage hooks all give the same bits, within
+    the bound of the oracle."""
+    banner(f"grouped tree M={M}")
+    lay = wl.small_layer("tree", 1024, (256, 128), 5, "mcg", (M,), seed=97)
+    t = wl.gen_all(lay)
+    outs = {}
+    for bm in (16, 32, 64, 128, 256):
+        if bm < M and bm < 64:
+            continue
+        for unit in (None, 1):
+            outs[(bm, unit)] = _run(t, parts=8, groups=2, bm=bm, unit=unit, mode=ex.EXL3_MODE_SLABS)
+    if M <= 16:
+        outs["table"] = _run(t, parts=8, groups=2, decoder=ex.EXL3_DECODER_TABLE)
+        outs["table, part slabs"] = _run(t, parts=8, groups=2, decoder=ex.EXL3_DECODER_TABLE, unit=1)
+    first = next(iter(outs.values()))
+    for key, y in outs.items():
+        assert np.array_equal(y, first), f"schedule {key} differs"
+    w = weight(t)
+    xr = ex.input_transform(x_dev(t.x), w.suh)
+    z = ex.debug_parts(w, xr, parts=8, groups=2)
+    assert np.array_equal(bits16(ex.debug_epilogue(w, z, M, groups=2)), first)
+    zg = ex.debug_parts(w, xr, parts=8, groups=2, unit=4)
+    assert np.array_equal(bits16(ex.debug_epilogue(w, zg, M)), first)
+    _check(t, first)
+
+
+def test_grouped_tree_is_not_the_flat_fold():
+    """The grouped tree and the flat fold of the same eight parts are both
+    within the bound, and their bits differ somewhere (the tree is real)."""
+    lay = wl.small_layer("tree2", 1024, (512,), 4, "mcg", (64,), seed=98)
+    t = wl.gen_all(lay)
+    flat = _run(t, parts=8)
+    tree = _run(t, parts=8, groups=2)
+    _check(t, flat)
+    _check(t, tree)
+    assert not np.array_equal(flat, tree)
+
+
+def test_finisher_counters_stay_zero():
+    """The finishing workgroup resets its tile's counter: after calls of
+    several plans on one workspace the counter area is zero again, and a
+    call after them gives the same bits as the first."""
+    lay = wl.small_layer("fin", 2048, (512,), 4, "mcg", (64,), seed=99)
+    t = wl.gen_all(lay)
+    w = weight(t)
+    assert ex.plan(w, 16)["launches"] == 1 and ex.plan(w, 16)["groups"] < ex.plan(w, 16)["parts"]
+    first = _run(t, M=16)
+    for M in (1, 7, 33, 64, 16):
+        _run(t, M=M)
+    torch.cuda.synchronize()
+    ws = ex._workspaces[torch.cuda.current_device()]
+    assert int(torch.count_nonzero(ws[:ex.COUNTER_BYTES])) == 0
+    assert np.array_equal(_run(t, M=16), first)
+
+
+def test_row_chunks():
+    """4096 x 4096, 4 bits (32 column blocks x 8 groups of 4 parts) at 1600
+    rows: the group slabs exceed 192 MiB, so the call runs in row chunks.
+    Rows from both chunks equal the same rows computed alone, and sampled
+    outputs are within the oracle's bound."""
+    lay = wl.small_layer("chunks", 4096, (4096,), 4, "mcg", (1600,), seed=96)
+    t = wl.gen_all(lay)
+    w = weight(t)
+    pl = ex.plan(w, 1600)
+    banner(f"row chunks: plan {pl}")
+    assert pl["mode"] == ex.EXL3_MODE_SLABS and pl["launches"] > 2
+    xr = ex.input_transform(x_dev(t.x), w.suh)
+    y = bits16(ex.linear(w, xr, torch.bfloat16))
+    rows = [0, 777, 1599]
+    for r in rows:
+        xr1 = ex.input_transform(x_dev(t.x[r:r + 1]), w.suh)
+        assert np.array_equal(bits16(ex.linear(w, xr1, torch.bfloat16))[0], y[r]), f"row {r}"
+    blocks = [0, 17, 31]
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
+    res = olin.check(y[rows][:, ref.cols], ref, t.svh, lay.K, "bf16")
+    banner(f"row chunks sampled: {res}")
+    assert res.ok, str(res)
 
 
 # ---------------------------------------------------------------- invariants

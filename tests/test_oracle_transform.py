@@ -124,3 +124,16 @@ def test_reduce_parts_is_left_to_right():
     # the first part is copied, not added to +0: -0.0 survives
     neg = np.array([-0.0], dtype=np.float32).reshape(1, 1, 1)
     assert np.signbit(tf.reduce_parts_f32(neg)[0, 0])
+
+
+def test_reduce_parts_grouped_tree():
+    # Groups of two: (1 + 2**-24) = 1 (tie to even) and (2**-24 + 2**-24) =
+    # 2**-23 exactly, so the grouped total is 1 + 2**-23, while the flat
+    # left-to-right fold absorbs every 2**-24 into 1 and stays at 1.
+    parts = np.array([1.0, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24], dtype=np.float32).reshape(4, 1, 1)
+    assert tf.reduce_parts_f32(parts)[0, 0] == np.float32(1.0)
+    assert tf.reduce_parts_f32(parts, groups=4)[0, 0] == np.float32(1.0)
+    assert tf.reduce_parts_f32(parts, groups=1)[0, 0] == np.float32(1.0)
+    assert tf.reduce_parts_f32(parts, groups=2)[0, 0] == np.float32(1.0 + 2.0 ** -23)
+    with pytest.raises(ValueError):
+        tf.reduce_parts_f32(parts, groups=3)
