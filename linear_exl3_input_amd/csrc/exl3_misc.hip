@@ -8,48 +8,139 @@ namespace exl3 {
 //
 // x~[s][m][:] = fp16_rne(2^-4 * H128(x[m][:] * suh[s][:])) per 128 block
 // (TensorFold PR "cuda: EXL3 projections behind qlinear", "Arithmetic" step
-// 1).  One wave per (row, 128-block); x is read once and reused for every
-// shard's suh row (cuda-exl3 README, "One op per layer": all shards in one
-// launch, reading x once, with bf16 -> fp32 folded into the load).  x*suh is
-// exact in fp32, so the product may be contracted into an add freely.  The
-// output is stored in k-step tiles, x~[s][k/32][m][32], with the 32 values of
-// a row in fragment order (frag_order_k), so that one MFMA lane's eight A
-// values are 16 contiguous bytes and one k-step of a run of rows is one
-// contiguous block.
+// 1).  x is read once and reused for every shard's suh row (cuda-exl3 README,
+// "One op per layer": all shards in one launch, reading x once, with bf16 ->
+// fp32 folded into the load).  x*suh is exact in fp32.
+//
+// Sixteen lanes per (row, 128-block), four rows of one block per wave (or,
+// below four rows, four blocks of one row).  Lane L of a block
+// holds the 8 values one 16-byte piece of the k-step tile layout stores: of
+// 32-group j = L/4 and piece q = L%4, k = 32j + 16(q/2) + 4(q%2) +
+// {0,1,2,3, 8,9,10,11} (the fragment order of frag_order_k).  The butterfly
+// strides 1, 2 and 8 pair values inside the lane; strides 4, 16, 32 and 64
+// pair lane L with L^1, L^2, L^4 and L^8, whose values arrive by DPP lane
+// moves (no LDS).  The stages run in the fixed order 1, 2, 4, ..., 64 and
+// every add is the same fp32 add as in hadamard128_wave, so the result is
+// the same to the bit.  Each lane then stores its 8 fp16 as one 16-byte
+// piece; four lanes fill a row's 64-byte k-group.
+
+// Lane value of lane^1, ^2, ^4, ^8 (within 16 lanes) by DPP: quad_perm
+// [1,0,3,2]; quad_perm [2,3,0,1]; half-row mirror (i -> 7-i) then quad_perm
+// [3,2,1,0] (7 - (i^3) = i^4 for i < 8); row rotate by 8.
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (X == 1) r = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false);
+  else if constexpr (X == 2) r = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false);
+  else if constexpr (X == 4)
+    r = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF,
+                                    false);
+  else r = __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, r);
+}
+
+// One cross-lane butterfly stage: the lane whose bit is clear keeps a + b
+// (its value a, the partner's b), the other keeps b' - a' with its partner
+// a' = the clear lane's value: the same two fp32 operations as in-lane.
+template <int X>
+__device__ __forceinline__ void xstage(float (&t)[8], bool upper) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = lane_xor<X>(t[e]);
+    t[e] = upper ? p - t[e] : t[e] + p;
+  }
+}
+
+// In-lane stage: pairs (e, e + d) for e with bit d clear.
+template <int D>
+__device__ __forceinline__ void lstage(float (&t)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if ((e & D) == 0) {
+      const float a = t[e], b = t[e + D];
+      t[e] = a + b;
+      t[e + D] = a - b;
+    }
+}
+
 template <bool X_BF16>
 __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ suh,
                                                               uint16_t *__restrict__ x_rot, int32_t M,
                                                               int32_t K, int32_t n_shards) {
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int L = lane & 15;
   const int kblocks = K >> 7;
-  if (item >= (int64_t)M * kblocks) return;  // whole wave exits together
-  const int64_t m = item / kblocks;
-  const int k0 = (int)(item - m * kblocks) * 128 + 2 * lane;
-  const uint32_t xv = *(const uint32_t *)(x + m * K + k0);
-  float x0, x1;
-  if constexpr (X_BF16) {
-    x0 = bf16_bits_to_f32(xv & 0xFFFFu);
-    x1 = bf16_bits_to_f32(xv >> 16);
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t m;
+  int kb;
+  bool live;
+  if (M >= 4) {
+    // item = (group of 4 rows, block): row 4*rg + lane/16
+    const int64_t rgroups = ((int64_t)M + 3) >> 2;
+    if (item >= rgroups * kblocks) return;  // whole wave exits together
+    const int64_t rg = item / kblocks;
+    kb = (int)(item - rg * kblocks);
+    m = 4 * rg + (lane >> 4);
+    live = m < M;
   } else {
-    x0 = f16_bits_to_f32(xv & 0xFFFFu);
-    x1 = f16_bits_to_f32(xv >> 16);
+    // few rows: item = (row, group of 4 blocks): block 4*bg + lane/16
+    const int bgroups = (kblocks + 3) >> 2;
+    if (item >= (int64_t)M * bgroups) return;
+    m = item / bgroups;
+    kb = 4 * (int)(item - m * bgroups) + (lane >> 4);
+    live = kb < kblocks;
+    kb = live ? kb : 0;
+  }
+  const int j = L >> 2, q = L & 3;
+  const int k0 = kb * 128 + 32 * j + 16 * (q >> 1) + 4 * (q & 1);  // the lane's first k; the second run at k0 + 8
+  float xv[8];
+  {
+    u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
+    if (live) {
+      lo = *(const u32x2_t *)(x + m * K + k0);
+      hi = *(const u32x2_t *)(x + m * K + k0 + 8);
+    }
+    const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[2 * i] = X_BF16 ? bf16_bits_to_f32(w[i] & 0xFFFFu) : f16_bits_to_f32(w[i] & 0xFFFFu);
+      xv[2 * i + 1] = X_BF16 ? bf16_bits_to_f32(w[i] >> 16) : f16_bits_to_f32(w[i] >> 16);
+    }
   }
   for (int s = 0; s < n_shards; ++s) {
-    const uint32_t sv = *(const uint32_t *)(suh + (int64_t)s * K + k0);
-    float t0 = x0 * f16_bits_to_f32(sv & 0xFFFFu);
-    float t1 = x1 * f16_bits_to_f32(sv >> 16);
-    hadamard128_wave(t0, t1, lane);
-    const uint32_t packed = f32_to_f16_bits(t0 * 0.0625f) | (f32_to_f16_bits(t1 * 0.0625f) << 16);
-    const int64_t tile = (int64_t)s * (K >> 5) + (k0 >> 5);
-    *(uint32_t *)(x_rot + (tile * M + m) * 32 + (frag_order_k(k0) & 31)) = packed;
+    const u32x2_t slo = *(const u32x2_t *)(suh + (int64_t)s * K + k0);
+    const u32x2_t shi = *(const u32x2_t *)(suh + (int64_t)s * K + k0 + 8);
+    const uint32_t sw[4] = {slo.x, slo.y, shi.x, shi.y};
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[2 * i] = xv[2 * i] * f16_bits_to_f32(sw[i] & 0xFFFFu);
+      t[2 * i + 1] = xv[2 * i + 1] * f16_bits_to_f32(sw[i] >> 16);
+    }
+    // t[0..3] = k0 + 0..3, t[4..7] = k0 + 8..11
+    lstage<1>(t);                // stride 1
+    lstage<2>(t);                // stride 2
+    xstage<1>(t, (L & 1) != 0);  // stride 4: piece q ^ 1
+    lstage<4>(t);                // stride 8: the lane's two runs
+    xstage<2>(t, (L & 2) != 0);  // stride 16: piece q ^ 2
+    xstage<4>(t, (L & 4) != 0);  // stride 32: group j ^ 1
+    xstage<8>(t, (L & 8) != 0);  // stride 64: group j ^ 2
+    if (live) {
+      u32x4_t o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_f16_bits(t[2 * i] * 0.0625f) | (f32_to_f16_bits(t[2 * i + 1] * 0.0625f) << 16);
+      const int64_t tile = (int64_t)s * (K >> 5) + kb * 4 + j;
+      *(u32x4_t *)(x_rot + (tile * M + m) * 32 + 8 * q) = o;
+    }
   }
 }
 
 hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
                                   int32_t n_shards, uint16_t *x_rot, hipStream_t s) {
-  const int64_t items = (int64_t)M * (K / 128);
+  const int64_t items = M >= 4 ? (((int64_t)M + 3) / 4) * (K / 128) : (int64_t)M * ((K / 128 + 3) / 4);
   const dim3 grid((unsigned)((items + 3) / 4));
   if (x_bf16)
     hipLaunchKernelGGL((input_transform_kernel<true>), grid, dim3(256), 0, s, (const uint16_t *)x, suh, x_rot,

@@ -51,7 +51,7 @@ def test_decode_every_width_and_codebook(bits, cb):
 
 
 @pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("M,K,S", [(1, 128, 1), (7, 384, 3), (33, 1024, 2), (130, 256, 1)])
+@pytest.mark.parametrize("M,K,S", [(1, 128, 1), (7, 384, 3), (33, 1024, 2), (130, 256, 1), (517, 4096, 2), (3, 640, 2), (2, 4096, 1)])
 def test_input_transform_bit_exact(x_dtype, M, K, S):
     banner(f"input transform {x_dtype} M={M} K={K} S={S}")
     rng = np.random.default_rng(1000 + M + K + S)
