@@ -301,8 +301,34 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
             });
           }
         };
+        // Without the read-ahead across the barrier (256-row waves): a ring
+        // of four x~ fragments read three ahead of their products, and the
+        // decode cut into six pieces between the product pairs, each step
+        // fenced so the compiler keeps the reads early (left to itself, at
+        // this register pressure it issued every read just before its use).
+        auto products_pipelined = [&]() __attribute__((always_inline)) {
+          constexpr int RD = 3;
+          half8_t af[4];
+#pragma unroll
+          for (int q = 0; q < RD; ++q) af[q] = *(const half8_t *)(as_p + q * 256);
+          static_for<0, MF>([&](auto mt_c) {
+            constexpr int mt = decltype(mt_c)::value;
+            if constexpr (mt + RD < MF) af[(mt + RD) % 4] = *(const half8_t *)(as_p + (mt + RD) * 256);
+            acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt % 4], B0, acc[mt][0], 0, 0, 0);
+            acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt % 4], B1, acc[mt][1], 0, 0, 0);
+            static_for<mt * 6 / MF, (mt + 1) * 6 / MF>([&](auto pc) {
+              constexpr int piece = decltype(pc)::value;
+              if constexpr (piece == 0) raw_normalize<BITS>(X, sel, sh, Y);
+              else if constexpr (piece < 5) nb4[piece - 1] = frag_pair<BITS, CB, piece - 1>(Y);
+              else *(u32x4_t *)(xb_own0 + ((i + 1) & 1) * W::XB_DW) = nb4;
+            });
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        };
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (SCHED == 1) {
+        if constexpr (SCHED == 1 && NPRE == 0) {
+          products_pipelined();
+        } else if constexpr (SCHED == 1) {
           // interleaved: each MFMA followed by about three VALU instructions
           // of the decode (a wave issues VALU at most every ~8 cycles, so
           // the decode is spread over the whole k-step in both waves)
