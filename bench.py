@@ -65,7 +65,8 @@ def kernel_key(lay, plan) -> str:
     quads = unit if (bm <= 64 and unit in (2, 4) and (lay.K // 128) % plan["parts"] == 0) else 1
     multi = unit > 1 and quads == 1
     if bm <= 64:
-        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}, {quads}>"
+        qw = plan["wg_cols"] // 32
+        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}, {quads}, {qw}>"
     elif bm == 128:
         name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, {str(multi).lower()}>"
     else:

@@ -46,7 +46,7 @@ extern "C" {
 #endif
 
 #define EXL3_MAX_SHARDS 16
-#define EXL3_ABI_VERSION 3
+#define EXL3_ABI_VERSION 4
 
 /* The first EXL3_WORKSPACE_COUNTER_BYTES of every workspace hold per-tile
  * arrival counters (see exl3_linear): they must be zero before the first
@@ -134,6 +134,11 @@ typedef struct exl3_plan {
                           (one slab per part) may be forced.  Fused: P      */
   int32_t launches;    /* kernels one exl3_linear call enqueues (output;
                           ignored in a forced plan)                         */
+  int32_t wg_cols;     /* columns per GEMM workgroup: 128, or 64 for 16-64
+                          row tiles in slab mode when a layer has fewer
+                          workgroups than compute units (then both halves'
+                          workgroups of a 128-column block are summed by the
+                          output stage); may be forced                      */
   size_t workspace;    /* bytes of workspace this plan needs: 0, or
                           EXL3_WORKSPACE_COUNTER_BYTES + the slabs          */
 } exl3_plan;

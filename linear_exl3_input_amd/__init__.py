@@ -59,10 +59,10 @@ class _Weight(ctypes.Structure):
 class _Plan(ctypes.Structure):
     _fields_ = [("parts", ctypes.c_int32), ("groups", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("decoder", ctypes.c_int32), ("unit", ctypes.c_int32),
-                ("launches", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
+                ("launches", ctypes.c_int32), ("wg_cols", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
 
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 COUNTER_BYTES = 65536  # EXL3_WORKSPACE_COUNTER_BYTES: zeroed arrival counters at the workspace's start
 
 
@@ -197,16 +197,18 @@ def _workspace(nbytes: int, device: torch.device) -> Tuple[int, int]:
     return ws.data_ptr(), ws.numel()
 
 
-def _force(parts=None, mode=None, bm=None, decoder=None, groups=None, unit=None) -> Optional[_Plan]:
-    if parts is None and mode is None and bm is None and decoder is None and groups is None and unit is None:
+def _force(parts=None, mode=None, bm=None, decoder=None, groups=None, unit=None, wg_cols=None) -> Optional[_Plan]:
+    if (parts is None and mode is None and bm is None and decoder is None and groups is None and unit is None
+            and wg_cols is None):
         return None
     return _Plan(parts if parts else -1, groups if groups else -1, EXL3_MODE_AUTO if mode is None else mode,
-                 bm if bm else -1, EXL3_DECODER_AUTO if decoder is None else decoder, unit if unit else -1, 0, 0)
+                 bm if bm else -1, EXL3_DECODER_AUTO if decoder is None else decoder, unit if unit else -1, 0,
+                 wg_cols if wg_cols else -1, 0)
 
 
 def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decoder=None, groups=None,
-                    unit=None) -> int:
-    f = _force(parts, mode, bm, decoder, groups, unit)
+                    unit=None, wg_cols=None) -> int:
+    f = _force(parts, mode, bm, decoder, groups, unit, wg_cols)
     L = load()
     n = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     err = L.exl3_last_error().decode()
@@ -219,7 +221,7 @@ def plan(w: Exl3Weight, M: int) -> dict:
     p = _Plan()
     _check(load().exl3_plan_query(ctypes.byref(w.view()), M, ctypes.byref(p)))
     return {"parts": p.parts, "groups": p.groups, "mode": p.mode, "bm": p.bm, "decoder": p.decoder,
-            "unit": p.unit, "launches": p.launches, "workspace": p.workspace}
+            "unit": p.unit, "launches": p.launches, "wg_cols": p.wg_cols, "workspace": p.workspace}
 
 
 def rot_shape(n_shards: int, M: int, K: int) -> tuple:
@@ -252,7 +254,7 @@ def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tens
 
 def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
            out: Optional[torch.Tensor] = None, parts=None, mode=None, bm=None,
-           decoder=None, groups=None, unit=None) -> torch.Tensor:
+           decoder=None, groups=None, unit=None, wg_cols=None) -> torch.Tensor:
     """z = x_rot . W_q per shard, then the output transform: -> y [M, N]."""
     if x_rot.dim() != 4 or x_rot.shape[3] != 32:
         raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
@@ -264,7 +266,7 @@ def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bf
         raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
     if out is None:
         out = torch.empty((M, w.N), dtype=out_dtype, device=x_rot.device)
-    f = _force(parts, mode, bm, decoder, groups, unit)
+    f = _force(parts, mode, bm, decoder, groups, unit, wg_cols)
     L = load()
     need = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     ws, wsn = _workspace(need, x_rot.device)
@@ -293,7 +295,7 @@ def debug_decode(w: Exl3Weight) -> torch.Tensor:
 
 
 def debug_parts(w: Exl3Weight, x_rot: torch.Tensor, parts=None, bm=None, decoder=None,
-                out: Optional[torch.Tensor] = None, groups=None, unit=None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, groups=None, unit=None, wg_cols=None) -> torch.Tensor:
     """The trellis GEMM stage alone: the fp32 sum of every K part (unit 1,
     the default) or of every unit of `unit` parts, in the slab layout
     [P/unit, ceil(M/4), N, 4] (what debug_epilogue reads)."""
@@ -306,7 +308,7 @@ def debug_parts(w: Exl3Weight, x_rot: torch.Tensor, parts=None, bm=None, decoder
         out = torch.empty(shape, dtype=torch.float32, device=x_rot.device)
     elif tuple(out.shape) != shape or out.dtype != torch.float32:
         raise ValueError(f"out is {tuple(out.shape)} {out.dtype}, expected {shape} float32")
-    f = _force(parts, EXL3_MODE_SLABS, bm, decoder, groups, unit)
+    f = _force(parts, EXL3_MODE_SLABS, bm, decoder, groups, unit, wg_cols)
     _check(load().exl3_debug_parts(ctypes.byref(w.view()), _dev_ptr(x_rot, "x_rot", _H16), M,
                                    _dev_ptr(out, "z_parts", (torch.float32,)), out.numel() * 4, _stream(),
                                    ctypes.byref(f)))

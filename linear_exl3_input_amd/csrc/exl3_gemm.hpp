@@ -236,14 +236,15 @@ struct RawGeom {
 // Source offset (16-bit words from the stage's first tile) of padded chunk
 // q of a stage; q past the stage (surplus lanes of the last load) reads a
 // chunk of tile 0 that lands in a scratch area.
-template <int BITS>
+// A stage is 8 k-tiles x NTS n-tiles (NTS = 8: 128 columns, 4: 64).
+template <int BITS, int NTS = 8>
 __device__ __forceinline__ uint32_t raw_chunk_src(int q, int NT) {
   constexpr int TC = 2 * BITS + 2;
-  if (q >= 64 * TC) return (uint32_t)((q % (2 * BITS)) * 8);
+  if (q >= 8 * NTS * TC) return (uint32_t)((q % (2 * BITS)) * 8);
   const int t = q / TC;
   const int c = q - t * TC;
   const int sc = c == 0 ? 2 * BITS - 1 : (c == 2 * BITS + 1 ? 0 : c - 1);
-  return (uint32_t)(((t >> 3) * NT + (t & 7)) * (16 * BITS) + sc * 8);
+  return (uint32_t)(((t / NTS) * NT + (t % NTS)) * (16 * BITS) + sc * 8);
 }
 
 // Window of the lane's 8 states for even widths: start dword (after the
@@ -347,21 +348,21 @@ __device__ __forceinline__ void store_partial_coherent(__amdgpu_buffer_rsrc_t rs
 }
 
 // Arrival: every thread's stores have completed; one thread adds 1 to the
-// tile's counter.  Returns true (uniformly) in the tile's last workgroup.
-__device__ __forceinline__ bool arrive_last(const GemmParams &p) {
+// tile's counter.  Returns true (uniformly) in the last of the tile's
+// `arrivals` workgroups.
+__device__ __forceinline__ bool arrive_last(const GemmParams &p, uint32_t tile, uint32_t arrivals) {
   __shared__ int s_last;
   wait_vmcnt<0>();
   __syncthreads();
-  const uint32_t tile = blockIdx.z * gridDim.x + blockIdx.x;
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             gridDim.y - 1;
+             arrivals - 1;
   __syncthreads();
   return s_last != 0;
 }
 
 // The last workgroup's work on its tile (rows m0 .. m0+bm-1 of the launch,
-// 128 columns of block blockIdx.x), with n_waves waves and `lds_bytes` of
+// the 128 columns of block nb), with n_waves waves and `lds_bytes` of
 // free LDS at `lds`.  The tile's slabs form G = n_slabs / fold_q groups of
 // fold_q consecutive slabs.  Items (4-row group r, group gi) are dealt to the
 // waves: each folds its group's slabs in slab order (first copied) into LDS,
@@ -370,8 +371,8 @@ __device__ __forceinline__ bool arrive_last(const GemmParams &p) {
 // (first copied) and writes the rows.  The same fp32 adds in the same order as
 // reduce_rows4 (which serves when the items do not fit the LDS).  The
 // tile's counter is reset to zero for the next call.
-__device__ __forceinline__ void finish_tile(const GemmParams &p, int m0, int bm, int wave_all, int n_waves,
-                                            int lane, float *lds, int lds_bytes) {
+__device__ __forceinline__ void finish_tile(const GemmParams &p, uint32_t tile, int nb, int m0, int bm, int wave_all,
+                                            int n_waves, int lane, float *lds, int lds_bytes) {
   const int rows = p.row_end - p.row_base;
   const int M4 = (rows + 3) >> 2;
   const int N = p.N;
@@ -380,7 +381,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, int m0, int bm,
   const int G = n_slabs / fq;
   const int rt = min(bm, p.row_end - m0);  // rows of this tile
   const int r4 = (rt + 3) >> 2;
-  const int n0 = blockIdx.x * 128;
+  const int n0 = nb * 128;
   const int m4_0 = (m0 - p.row_base) >> 2;
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
   const __amdgpu_buffer_rsrc_t rs = slab_rsrc(p);
@@ -460,63 +461,75 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, int m0, int bm,
         }
     }
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(p.counters + blockIdx.z * gridDim.x + blockIdx.x, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // LDS dwords of one stage slot of gemm_kernel (raw trellis tiles + x~) and of
 // a quad's private area (NSLOT slots + the landing area of surplus loads).
-template <int BITS, int MT>
+// A quad is QW waves on 32*QW columns (QW = 4: a whole 128-column block;
+// QW = 2: half of one).
+template <int BITS, int MT, int QW>
 struct SmallGeom {
-  using R = RawGeom<BITS>;
   static constexpr int BM = 16 * MT;
-  static constexpr int T_OPS = (R::T_CHUNKS + WG_THREADS - 1) / WG_THREADS;  // trellis loads per wave per stage
-  static constexpr int JUNK = T_OPS * WG_THREADS - R::T_CHUNKS;
-  static constexpr int A_SLOT_DW = BM * 64;  // x~: 4 k-steps x BM rows x 64 B
-  static constexpr int SLOT_DW = R::TSLOT_DW + A_SLOT_DW;
-  static constexpr int OPS = T_OPS + MT;     // loads per wave per stage
+  static constexpr int QT = 64 * QW;                        // threads per quad
+  static constexpr int NTS = 2 * QW;                        // n-tiles per stage row
+  static constexpr int TSTRIDE = 8 * BITS + 8;              // dwords per padded tile
+  static constexpr int T_CHUNKS = 8 * NTS * (2 * BITS + 2);  // 16-byte chunks per padded stage
+  static constexpr int TSLOT_DW = T_CHUNKS * 4;
+  static constexpr int T_OPS = (T_CHUNKS + QT - 1) / QT;    // trellis loads per wave per stage
+  static constexpr int JUNK = T_OPS * QT - T_CHUNKS;
+  static constexpr int A_SLOT_DW = BM * 64;                 // x~: 4 k-steps x BM rows x 64 B
+  static constexpr int A_OPS = 16 * BM / QT;                // x~ loads per wave per stage
+  static constexpr int SLOT_DW = TSLOT_DW + A_SLOT_DW;
+  static constexpr int OPS = T_OPS + A_OPS;                 // loads per wave per stage
   static constexpr int area(int nslot) { return nslot * SLOT_DW + JUNK * 4; }
+  static_assert(16 * BM % QT == 0, "x~ loads divide evenly over the quad");
+  static_assert(T_CHUNKS % 64 == 0, "each direct load lands whole in a slot or in the surplus area");
 };
 
-// BM = 16*MT rows (16, 32, 64) x 128 columns.  A workgroup is QD quads of 4
-// waves; quad q computes K part (unit start + q) when QD > 1, or the whole
-// unit (MULTI: its parts folded in order in registers) when QD == 1.  Wave w
-// of a quad decodes n-tiles 2w, 2w+1 (both column halves) and multiplies them
-// against all BM rows.  Both operands arrive by direct loads to LDS into the
+// BM = 16*MT rows (16, 32, 64) x 32*QW columns (QW = 4: one 128-column
+// block; QW = 2: half of one, so that a layer with few tiles keeps twice the
+// workgroups, slab mode only).  A workgroup is QD quads of QW waves; quad q
+// computes K part (unit start + q) when QD > 1, or the whole unit (MULTI: its
+// parts folded in order in registers) when QD == 1.  Wave w of a quad
+// decodes n-tiles 2w, 2w+1 of its columns (both column halves) and
+// multiplies them against all BM rows.  Both operands arrive by direct loads to LDS into the
 // quad's stage slots (raw trellis tiles, and x~ in its k-step tile layout, 4
 // k-steps x BM rows x 64 B per stage): two slots, the first two stages issued
 // together, when QD quads of two slots fit in LDS, else one slot.  Barriers
 // wait only for LDS operations; the loads are waited for by count.  The
 // quads' part sums are then folded in part order through LDS.  Rows past the
 // launch's last row load that row (finite, never stored).
-template <int BITS, uint32_t CB, int MT, bool MULTI, int QD>
-__global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams p) {
-  using R = RawGeom<BITS>;
-  using S = SmallGeom<BITS, MT>;
+template <int BITS, uint32_t CB, int MT, bool MULTI, int QD, int QW>
+__global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) {
+  using S = SmallGeom<BITS, MT, QW>;
   constexpr int BM = S::BM;
+  constexpr int QT = S::QT;
+  constexpr int NTS = S::NTS;
   constexpr int T_OPS = S::T_OPS;
+  constexpr int A_OPS = S::A_OPS;
   constexpr int OPS = S::OPS;
   constexpr int SLOT_DW = S::SLOT_DW;
+  constexpr int TSTRIDE = S::TSTRIDE;
   constexpr int NSLOT = QD * S::area(2) * 4 <= 152 * 1024 ? 2 : 1;
   constexpr int QUAD_DW = S::area(NSLOT);
   constexpr int MAIN_DW = QD * QUAD_DW;
   constexpr int Z_DW = BM * Z_ROW;
   constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
-  static_assert(R::T_CHUNKS % 64 == 0, "each direct load lands whole in a slot or in the surplus area");
   static_assert(!MULTI || QD == 1, "a quad computes one part when the workgroup has several");
   static_assert(LDS_DW * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
 
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qd = wave_all >> 2;
-  const int wave = wave_all & 3;
+  const int qd = wave_all / QW;
+  const int wave = wave_all % QW;
   uint32_t *const qlds = lds + qd * QUAD_DW;
   uint32_t *const junk = qlds + NSLOT * SLOT_DW;
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int nb = blockIdx.x;
+  const int nb = QW == 4 ? (int)blockIdx.x : (int)blockIdx.x >> 1;  // 128-column block
+  const int c0 = QW == 4 ? 0 : 64 * ((int)blockIdx.x & 1);         // first column of the slice in it
   const int m0 = p.row_base + blockIdx.z * BM;
   const int rend = p.row_end;
   const int M = p.M, K = p.K, N = p.N;
@@ -535,17 +548,17 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
   const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
 
   // load sources: 16-bit word offsets from the stage bases
-  const uint16_t *const t_base = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8) * (16 * BITS);
+  const uint16_t *const t_base = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8 + c0 / 16) * (16 * BITS);
   const int64_t t_stage = (int64_t)8 * NT * (16 * BITS);
   uint32_t t_src[T_OPS];
 #pragma unroll
-  for (int r = 0; r < T_OPS; ++r) t_src[r] = raw_chunk_src<BITS>(r * WG_THREADS + wave * 64 + lane, NT);
+  for (int r = 0; r < T_OPS; ++r) t_src[r] = raw_chunk_src<BITS, NTS>(r * QT + wave * 64 + lane, NT);
   const uint16_t *const a_base = xs + (int64_t)kb_begin * 4 * M * 32;
   const int64_t a_stage = (int64_t)4 * M * 32;
-  uint32_t a_src[MT];
+  uint32_t a_src[A_OPS];
 #pragma unroll
-  for (int r = 0; r < MT; ++r) {
-    const int c = r * WG_THREADS + wave * 64 + lane;  // chunk: k-step c/(4BM), row (c/4)%BM, 16 B piece c%4
+  for (int r = 0; r < A_OPS; ++r) {
+    const int c = r * QT + wave * 64 + lane;  // chunk: k-step c/(4BM), row (c/4)%BM, 16 B piece c%4
     int row = m0 + (c >> 2) % BM;
     row = row < rend ? row : rend - 1;
     a_src[r] = (uint32_t)(((c / (4 * BM)) * M + row) * 32 + (c & 3) * 8);
@@ -554,15 +567,15 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
     uint32_t *const ts = qlds + slot * SLOT_DW;
 #pragma unroll
     for (int r = 0; r < T_OPS; ++r) {
-      const int q0 = r * WG_THREADS + wave * 64;
-      uint32_t *dst = q0 < R::T_CHUNKS ? ts + q0 * 4 : junk + (q0 - R::T_CHUNKS) * 4;
+      const int q0 = r * QT + wave * 64;
+      uint32_t *dst = q0 < S::T_CHUNKS ? ts + q0 * 4 : junk + (q0 - S::T_CHUNKS) * 4;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(t_base + stage * t_stage + t_src[r]),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < MT; ++r)
+    for (int r = 0; r < A_OPS; ++r)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a_base + stage * a_stage + a_src[r]),
-                                       (__attribute__((address_space(3))) void *)(ts + R::TSLOT_DW + (r * WG_THREADS + wave * 64) * 4),
+                                       (__attribute__((address_space(3))) void *)(ts + S::TSLOT_DW + (r * QT + wave * 64) * 4),
                                        16, 0, 0);
   };
 
@@ -570,7 +583,7 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
   uint32_t sel0, sel1;
   raw_lane_window<BITS>(j, g, 0, doff0, sel0, sh0);
   raw_lane_window<BITS>(j, g, 1, doff1, sel1, sh1);
-  const int tile_lane = ((g >> 1) * WG_NT + 2 * wave + (j >> 3)) * R::TSTRIDE;
+  const int tile_lane = ((g >> 1) * NTS + 2 * wave + (j >> 3)) * TSTRIDE;
 
   float4_t acc[MT][2];
   float4_t tot[MULTI ? MT : 1][2];
@@ -594,13 +607,13 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
   auto run_stages = [&](int s_end) __attribute__((always_inline)) {
     for (; s < s_end; ++s) {
       const uint32_t *const tb = qlds + (NSLOT == 2 ? (s & 1) : 0) * SLOT_DW;
-      const uint32_t *const ab = tb + R::TSLOT_DW + 16 * j + 4 * g;
+      const uint32_t *const ab = tb + S::TSLOT_DW + 16 * j + 4 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         half8_t a[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) a[mt] = *(const half8_t *)(ab + (ks * BM + mt * 16) * 16);
-        const uint32_t *tp = tb + tile_lane + 2 * WG_NT * ks * R::TSTRIDE;
+        const uint32_t *tp = tb + tile_lane + 2 * NTS * ks * TSTRIDE;
         const half8_t b0 = __builtin_bit_cast(half8_t, raw_decode_frag<BITS, CB>(tp + doff0, sel0, sh0));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -698,7 +711,7 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             store_partial(p.slabs, blockIdx.y, rows, N, m0 - p.row_base + mt * 16 + 4 * g,
-                          nb * 128 + lane_col(wave, j, h), acc[mt][h]);
+                          nb * 128 + c0 + lane_col(wave, j, h), acc[mt][h]);
       }
       return;
     }
@@ -709,13 +722,17 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           store_partial_coherent(rs, blockIdx.y, rows, N, m0 - p.row_base + mt * 16 + 4 * g,
-                                 nb * 128 + lane_col(wave, j, h), acc[mt][h]);
+                                 nb * 128 + c0 + lane_col(wave, j, h), acc[mt][h]);
     }
-    if (!arrive_last(p)) return;
-    finish_tile(p, m0, BM, wave_all, 4 * QD, lane, z, LDS_DW * 4);
+    // the tile is the 128-column block: both halves' workgroups arrive
+    const uint32_t tile = blockIdx.z * (gridDim.x * QW / 4) + nb;
+    if (!arrive_last(p, tile, gridDim.y * (4 / QW))) return;
+    finish_tile(p, tile, nb, m0, BM, wave_all, QW * QD, lane, z, LDS_DW * 4);
     return;
   }
 
+  // fused: the output stage needs the whole 128-column block (QW == 4)
+  if constexpr (QW == 4) {
   if constexpr (QD == 1) barrier_lds();  // every wave is done with the stage slots
   if (writer) {
 #pragma unroll
@@ -729,13 +746,14 @@ __global__ __launch_bounds__(WG_THREADS * QD) void gemm_kernel(const GemmParams 
   }
   barrier_lds();
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-  for (int r = wave_all; r < BM; r += 4 * QD) {
+  for (int r = wave_all; r < BM; r += QW * QD) {
     const int row = m0 + r;
     if (row >= rend) break;
     const float z0 = z[r * Z_ROW + 2 * lane];
     const float z1 = z[r * Z_ROW + 2 * lane + 1];
     if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
     else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+  }
   }
 }
 
@@ -1004,16 +1022,27 @@ __global__ __launch_bounds__(WG_THREADS) void debug_decode_kernel(const DecodePa
 // ---------------------------------------------------------------- launchers
 
 // quads > 1: one part per quad (no register fold); otherwise `multi` folds
-// the workgroup's parts in registers.
+// the workgroup's parts in registers.  half: 64-column workgroups (quads of
+// two waves; slab mode only, no register fold).
 template <int BITS, uint32_t CB, int MT>
-hipError_t launch_gemm_t(int quads, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm_t(int quads, bool half, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (half) {
+    if (multi || !p.slab_mode) return hipErrorInvalidValue;
+    switch (quads) {
+      case 1: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 1, 2>), grid, dim3(128), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 2, 2>), grid, dim3(256), 0, s, p); break;
+      case 4: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 4, 2>), grid, dim3(512), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (quads) {
     case 1:
-      if (multi) hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, true, 1>), grid, dim3(WG_THREADS), 0, s, p);
-      else hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 1>), grid, dim3(WG_THREADS), 0, s, p);
+      if (multi) hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, true, 1, 4>), grid, dim3(WG_THREADS), 0, s, p);
+      else hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 1, 4>), grid, dim3(WG_THREADS), 0, s, p);
       break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 2>), grid, dim3(2 * WG_THREADS), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 4>), grid, dim3(4 * WG_THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 2, 4>), grid, dim3(2 * WG_THREADS), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 4, 4>), grid, dim3(4 * WG_THREADS), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1033,12 +1062,12 @@ hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hip
 // 256/512 -> gemm_wide_kernel (512 threads; 512 for a single part per
 // workgroup only).
 template <int BITS, uint32_t CB>
-hipError_t launch_gemm_cb(int bm, int quads, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (bm > 64 && quads != 1) return hipErrorInvalidValue;
+hipError_t launch_gemm_cb(int bm, int quads, bool half, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (bm > 64 && (quads != 1 || half)) return hipErrorInvalidValue;
   switch (bm) {
-    case 16: return launch_gemm_t<BITS, CB, 1>(quads, multi, p, grid, s);
-    case 32: return launch_gemm_t<BITS, CB, 2>(quads, multi, p, grid, s);
-    case 64: return launch_gemm_t<BITS, CB, 4>(quads, multi, p, grid, s);
+    case 16: return launch_gemm_t<BITS, CB, 1>(quads, half, multi, p, grid, s);
+    case 32: return launch_gemm_t<BITS, CB, 2>(quads, half, multi, p, grid, s);
+    case 64: return launch_gemm_t<BITS, CB, 4>(quads, half, multi, p, grid, s);
     case 128: return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
     case 256:
     case 512: return launch_wide_t<BITS, CB>(bm, multi, p, grid, s);
@@ -1047,11 +1076,12 @@ hipError_t launch_gemm_cb(int bm, int quads, bool multi, const GemmParams &p, di
 }
 
 template <int BITS>
-hipError_t launch_gemm_bits(int cb, int bm, int quads, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemm_bits(int cb, int bm, int quads, bool half, bool multi, const GemmParams &p, dim3 grid,
+                            hipStream_t s) {
   switch (cb) {
-    case 0: return launch_gemm_cb<BITS, CB_3INST>(bm, quads, multi, p, grid, s);
-    case 1: return launch_gemm_cb<BITS, CB_MCG>(bm, quads, multi, p, grid, s);
-    case 2: return launch_gemm_cb<BITS, CB_MUL1>(bm, quads, multi, p, grid, s);
+    case 0: return launch_gemm_cb<BITS, CB_3INST>(bm, quads, half, multi, p, grid, s);
+    case 1: return launch_gemm_cb<BITS, CB_MCG>(bm, quads, half, multi, p, grid, s);
+    case 2: return launch_gemm_cb<BITS, CB_MUL1>(bm, quads, half, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1072,9 +1102,9 @@ hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
 
 #define EXL3_DEFINE_BITS(B)                                                                        \
   namespace exl3 {                                                                                 \
-  hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool multi, const GemmParams &p, dim3 grid, \
-                              hipStream_t s) {                                                     \
-    return launch_gemm_bits<B>(cb, bm, quads, multi, p, grid, s);                                  \
+  hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool half, bool multi, const GemmParams &p, \
+                              dim3 grid, hipStream_t s) {                                          \
+    return launch_gemm_bits<B>(cb, bm, quads, half, multi, p, grid, s);                            \
   }                                                                                                \
   hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s) {             \
     return launch_table_bits<B>(cb, p, grid, s);                                                   \

@@ -142,6 +142,7 @@ struct Plan {
   int32_t decoder;
   int32_t unit;      // parts per workgroup unit
   int32_t quads;     // small tiles: one part per quad of waves
+  bool half;         // small tiles: 64-column workgroups
   bool multi;        // the workgroup folds unit > 1 parts in registers
   bool finisher;     // slab mode: the last workgroup of a tile does the output
   int32_t chunk;     // rows per launch
@@ -273,6 +274,22 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   }
   pl.finisher = pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 &&
                 (int64_t)nblk * ((pl.chunk + pl.bm - 1) / pl.bm) <= MAX_COUNTERS;
+  // Small tiles in slab mode with fewer workgroups than CUs: split each
+  // 128-column block between two workgroups of half the waves (the same
+  // per-wave work on twice the CUs; the finishing workgroup or the output
+  // kernel sums both halves' slabs).
+  pl.half = pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && !pl.multi &&
+            (int64_t)nblk * n_slabs * ((pl.chunk + pl.bm - 1) / pl.bm) < device_cus_or_default();
+  if (force && force->wg_cols > 0) {
+    if (force->wg_cols != 64 && force->wg_cols != 128)
+      return fail(EXL3_ERR_INVALID_ARG, "forced wg_cols=%d, must be 64 or 128", force->wg_cols);
+    if (force->wg_cols == 64 &&
+        !(pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && !pl.multi))
+      return fail(EXL3_ERR_UNSUPPORTED,
+                  "64-column workgroups need slab mode, the ALU decoder, at most 64 rows per tile and no register "
+                  "fold (mode=%d decoder=%d bm=%d unit=%d)", pl.mode, pl.decoder, pl.bm, pl.unit);
+    pl.half = force->wg_cols == 64;
+  }
   pl.launches = pl.mode == EXL3_MODE_SLABS && !pl.finisher ? 2 : 1;
   if (pl.chunk < M && M > 0) pl.launches *= (M + pl.chunk - 1) / pl.chunk;
   // counters, then slabs [n_slabs][ceil(chunk/4)][N][4] fp32
@@ -360,6 +377,7 @@ exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan) {
   plan->decoder = pl.decoder;
   plan->unit = pl.unit;
   plan->launches = pl.launches;
+  plan->wg_cols = pl.half ? 64 : 128;
   plan->workspace = pl.workspace;
   return EXL3_OK;
 }
@@ -438,9 +456,9 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
       e = exl3::launch_gemm_table(w->bits, w->codebook, p, grid, s);
       if (e != hipSuccess) return launch_error(e, "table GEMM launch");
     } else {
-      const dim3 grid((unsigned)(w->N / 128), (unsigned)n_units,
+      const dim3 grid((unsigned)(w->N / 128 * (pl.half ? 2 : 1)), (unsigned)n_units,
                       (unsigned)((p.row_end - p.row_base + pl.bm - 1) / pl.bm));
-      e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, pl.quads, pl.multi, p, grid, s);
+      e = exl3::launch_gemm(w->bits, w->codebook, pl.bm, pl.quads, pl.half, pl.multi, p, grid, s);
       if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
     }
     if (p.slab_mode && with_output && p.counters == nullptr) {
@@ -477,6 +495,7 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
     f.decoder = EXL3_DECODER_AUTO;
     f.unit = -1;
     f.launches = 0;
+    f.wg_cols = -1;
     f.workspace = 0;
   }
   f.mode = EXL3_MODE_SLABS;
@@ -496,6 +515,7 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
   }
   pl.chunk = M;
   pl.finisher = false;
+  pl.half = f.wg_cols == 64 && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && !pl.multi;
   const int32_t n_slabs = pl.parts / pl.unit;
   const size_t need = slab_bytes(n_slabs, M, w->N);
   if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;

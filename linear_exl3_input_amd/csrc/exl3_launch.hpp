@@ -42,8 +42,8 @@ struct DecodeParams {
 // choices that select a template instance: bm 16/32/64 -> gemm_kernel,
 // 128 -> gemm_big_kernel, 256/512 -> gemm_wide_kernel).  Return hipSuccess or the
 // launch error.
-hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool multi_part, const GemmParams &p, dim3 grid,
-                       hipStream_t s);
+hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool half, bool multi_part, const GemmParams &p,
+                       dim3 grid, hipStream_t s);
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s);
 // Table-decode GEMM (M <= 16): `grid` persistent workgroups of 1024 threads,
 // one per CU; fused (parts folded in order) or slab mode as in p.
@@ -60,8 +60,8 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
 
 // Per-bit-width entry points, defined in gemm_b<bits>.hip.
 #define EXL3_DECLARE_BITS(B)                                                                  \
-  hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool multi_part, const GemmParams &p,    \
-                              dim3 grid, hipStream_t s);                                        \
+  hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool half, bool multi_part,              \
+                              const GemmParams &p, dim3 grid, hipStream_t s);                   \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);            \
   hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s);
 EXL3_DECLARE_BITS(1)

@@ -214,17 +214,17 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s) {
 
 // ------------------------------------------------------ bit-width dispatch
 
-hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool multi, const GemmParams &p, dim3 grid,
+hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool half, bool multi, const GemmParams &p, dim3 grid,
                        hipStream_t s) {
   switch (bits) {
-    case 1: return launch_gemm_b1(cb, bm, quads, multi, p, grid, s);
-    case 2: return launch_gemm_b2(cb, bm, quads, multi, p, grid, s);
-    case 3: return launch_gemm_b3(cb, bm, quads, multi, p, grid, s);
-    case 4: return launch_gemm_b4(cb, bm, quads, multi, p, grid, s);
-    case 5: return launch_gemm_b5(cb, bm, quads, multi, p, grid, s);
-    case 6: return launch_gemm_b6(cb, bm, quads, multi, p, grid, s);
-    case 7: return launch_gemm_b7(cb, bm, quads, multi, p, grid, s);
-    case 8: return launch_gemm_b8(cb, bm, quads, multi, p, grid, s);
+    case 1: return launch_gemm_b1(cb, bm, quads, half, multi, p, grid, s);
+    case 2: return launch_gemm_b2(cb, bm, quads, half, multi, p, grid, s);
+    case 3: return launch_gemm_b3(cb, bm, quads, half, multi, p, grid, s);
+    case 4: return launch_gemm_b4(cb, bm, quads, half, multi, p, grid, s);
+    case 5: return launch_gemm_b5(cb, bm, quads, half, multi, p, grid, s);
+    case 6: return launch_gemm_b6(cb, bm, quads, half, multi, p, grid, s);
+    case 7: return launch_gemm_b7(cb, bm, quads, half, multi, p, grid, s);
+    case 8: return launch_gemm_b8(cb, bm, quads, half, multi, p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

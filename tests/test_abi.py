@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(L, name), name
-    assert L.exl3_abi_version() == ex.ABI_VERSION == 3
+    assert L.exl3_abi_version() == ex.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -111,9 +111,9 @@ def _plan(w, M):
     return p
 
 
-def F(parts=-1, mode=-1, bm=-1, decoder=-1, groups=-1, unit=-1):
+def F(parts=-1, mode=-1, bm=-1, decoder=-1, groups=-1, unit=-1, wg_cols=-1):
     """A forced plan (fields <= 0 keep the automatic choice)."""
-    return ex._Plan(parts, groups, mode, bm, decoder, unit, 0, 0)
+    return ex._Plan(parts, groups, mode, bm, decoder, unit, 0, wg_cols, 0)
 
 
 CB = ex.COUNTER_BYTES

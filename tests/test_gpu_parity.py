@@ -161,6 +161,8 @@ def test_schedules_agree_bit_for_bit(parts):
             if bm == 512 and mode == ex.EXL3_MODE_FUSED and parts > 1:
                 continue  # one accumulator set per 512-row workgroup
             outs[(mode, bm)] = _run(t, parts=parts, mode=mode, bm=bm)
+            if mode == ex.EXL3_MODE_SLABS and parts > 1 and bm <= 64:
+                outs[(mode, bm, 64)] = _run(t, parts=parts, mode=mode, bm=bm, wg_cols=64)
     first = next(iter(outs.values()))
     for key, y in outs.items():
         assert np.array_equal(y, first), f"schedule {key} differs"
@@ -267,6 +269,10 @@ def test_grouped_tree_schedules_agree(M):
             continue
         for unit in (None, 1):
             outs[(bm, unit)] = _run(t, parts=8, groups=2, bm=bm, unit=unit, mode=ex.EXL3_MODE_SLABS)
+            if bm <= 64:  # 64- and 128-column workgroups
+                for cols in (64, 128):
+                    outs[(bm, unit, cols)] = _run(t, parts=8, groups=2, bm=bm, unit=unit, mode=ex.EXL3_MODE_SLABS,
+                                                  wg_cols=cols)
     if M <= 16:
         outs["table"] = _run(t, parts=8, groups=2, decoder=ex.EXL3_DECODER_TABLE)
         outs["table, part slabs"] = _run(t, parts=8, groups=2, decoder=ex.EXL3_DECODER_TABLE, unit=1)
@@ -277,6 +283,9 @@ def test_grouped_tree_schedules_agree(M):
     xr = ex.input_transform(x_dev(t.x), w.suh)
     z = ex.debug_parts(w, xr, parts=8, groups=2)
     assert np.array_equal(bits16(ex.debug_epilogue(w, z, M, groups=2)), first)
+    if M <= 64:
+        z64 = ex.debug_parts(w, xr, parts=8, groups=2, bm=64, wg_cols=64)
+        assert torch.equal(z64, z)
     zg = ex.debug_parts(w, xr, parts=8, groups=2, unit=4)
     assert np.array_equal(bits16(ex.debug_epilogue(w, zg, M)), first)
     _check(t, first)
