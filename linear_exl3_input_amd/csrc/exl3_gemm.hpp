@@ -347,6 +347,57 @@ __device__ __forceinline__ void store_partial_coherent(__amdgpu_buffer_rsrc_t rs
   }
 }
 
+// The ordered sum (reduce_rows4's order: fold_q slabs per group, then the
+// groups) of four rows of one 128-column block read through the coherent
+// path, U slabs' loads in flight per round trip, then the output stage of
+// the `rows` (<= 4) rows.  slab_stride: bytes per slab.
+template <int U>
+__device__ __forceinline__ void fold_rows4_coherent(__amdgpu_buffer_rsrc_t rs, int n_slabs, int fq,
+                                                    uint32_t slab_stride, int N, int m4, int n0,
+                                                    const GemmParams &p, int64_t row0, int rows, int lane) {
+  const uint32_t base = ((uint32_t)m4 * (uint32_t)N + (uint32_t)(n0 + 2 * lane)) * 16u;
+  float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
+  int iq = 0;
+  for (int i0 = 0; i0 < n_slabs; i0 += U) {
+    float4_t v0[U], v1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + u < n_slabs) {
+        const uint32_t off = (uint32_t)(i0 + u) * slab_stride + base;
+        v0[u] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL_SC1));
+        v1[u] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, CPOL_SC1));
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + u < n_slabs) {
+        if (iq == 0) {
+          g0 = v0[u];
+          g1 = v1[u];
+        } else {
+          g0 = g0 + v0[u];
+          g1 = g1 + v1[u];
+        }
+        if (++iq == fq) {
+          iq = 0;
+          if (i0 + u + 1 == fq) {
+            t0 = g0;
+            t1 = g1;
+          } else {
+            t0 = t0 + g0;
+            t1 = t1 + g1;
+          }
+        }
+      }
+  }
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < rows) {
+      if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, y + (row0 + i) * N, n0, lane);
+      else output_row<false>(t0[i], t1[i], p.svh, y + (row0 + i) * N, n0, lane);
+    }
+}
+
 // Arrival: every thread's stores have completed; one thread adds 1 to the
 // tile's counter.  Returns true (uniformly) in the last of the tile's
 // `arrivals` workgroups.
@@ -391,18 +442,18 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, uint32_t tile, 
     a = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL_SC1));
     b = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, CPOL_SC1));
   };
-  if (r4 * G * 2048 <= lds_bytes && fq <= 8) {
+  if (r4 * G * 2048 <= lds_bytes && fq <= 4) {
     float4_t *const gs = reinterpret_cast<float4_t *>(lds);  // [r][gi][lane][2]
     for (int it = wave_all; it < r4 * G; it += n_waves) {
       const int r = it / G;
       const int gi = it - r * G;
-      float4_t v0[8], v1[8];
+      float4_t v0[4], v1[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < 4; ++q)
         if (q < fq) load2(gi * fq + q, m4_0 + r, v0[q], v1[q]);
       float4_t g0 = v0[0], g1 = v1[0];
 #pragma unroll
-      for (int q = 1; q < 8; ++q)
+      for (int q = 1; q < 4; ++q)
         if (q < fq) {
           g0 = g0 + v0[q];
           g1 = g1 + v1[q];
@@ -428,38 +479,9 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, uint32_t tile, 
     }
   } else {
     // one wave per 4-row group, slabs in order (reduce_rows4's order)
-    for (int r = wave_all; r < r4; r += n_waves) {
-      float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
-      for (int sl = 0; sl < n_slabs; ++sl) {
-        float4_t a, b;
-        load2(sl, m4_0 + r, a, b);
-        const int iq = sl % fq;
-        if (iq == 0) {
-          g0 = a;
-          g1 = b;
-        } else {
-          g0 = g0 + a;
-          g1 = g1 + b;
-        }
-        if (iq == fq - 1) {
-          if (sl == fq - 1) {
-            t0 = g0;
-            t1 = g1;
-          } else {
-            t0 = t0 + g0;
-            t1 = t1 + g1;
-          }
-        }
-      }
-      const int r0 = m0 + 4 * r;
-      const int nr = min(4, p.row_end - r0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < nr) {
-          if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
-          else output_row<false>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
-        }
-    }
+    for (int r = wave_all; r < r4; r += n_waves)
+      fold_rows4_coherent<4>(rs, n_slabs, fq, slab_stride, N, m4_0 + r, n0, p, m0 + 4 * r, min(4, p.row_end - (m0 + 4 * r)),
+                          lane);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
