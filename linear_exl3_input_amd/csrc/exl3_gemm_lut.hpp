@@ -1,4 +1,4 @@
-// Table-decode GEMM for M <= 16 rows.
+// Table-decode GEMM for M <= 32 rows.
 //
 // At a handful of rows the op streams the trellis once and its cost is the
 // decode: the ALU decode of the tile kernels spends about five VALU
@@ -101,7 +101,7 @@ struct TblUnit {
   int kb_begin;
 };
 
-template <int BITS, uint32_t CB, int TP>
+template <int BITS, uint32_t CB, int TP, int MT>
 __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmParams p) {
   using G = TblGeom<BITS>;
   constexpr int NX = G::NX, NY = G::NY, TILE_DW = G::TILE_DW;
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
   // last dword is the tile's first, read by a second load.  Slot sl of a
   // group of DEPTH k-steps is k-step sl after the group's first: the
   // offsets include sl k-steps, so a group's loads share one scalar offset.
-  uint32_t t_win[DEPTH], t_first[DEPTH], a_off[DEPTH];
+  uint32_t t_win[DEPTH], t_first[DEPTH], a_off[DEPTH][MT];
   uint32_t sel;
   bool wraps;
   {
@@ -185,13 +185,17 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
     const int d = o >> 5;
     const uint32_t tile = (uint32_t)((g >> 1) * NT + 2 * tw + (j >> 3)) * (TILE_DW * 4);
     wraps = d + NX > TILE_DW;
-    // rows past M read row M-1 (finite; their results are never stored)
-    const uint32_t a0 = (uint32_t)((p.row_base + (j < rows ? j : rows - 1)) * 32 * 2 + 8 * g * 2);
 #pragma unroll
     for (int sl = 0; sl < DEPTH; ++sl) {
       t_win[sl] = tile + 4u * d + (uint32_t)(sl * tsb);
       t_first[sl] = tile + (uint32_t)(sl * tsb);
-      a_off[sl] = a0 + (uint32_t)(sl * asb);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        // row 16*mt + j; rows past the launch's last read that row (finite;
+        // their results are never stored)
+        const int row = 16 * mt + j < rows ? 16 * mt + j : rows - 1;
+        a_off[sl][mt] = (uint32_t)((p.row_base + row) * 64 + 16 * g) + (uint32_t)(sl * asb);
+      }
     }
     // raw dwords hold two stream words swapped; a start on a dword boundary
     // swaps them back, a start mid-dword takes the high word of X[i] and the
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
 
   uint32_t X[DEPTH][NX];
   uint32_t T0[DEPTH];
-  half8_t A[DEPTH];
+  half8_t A[DEPTH][MT];
 
   // (The empty asm keeps the x~ offset next to its load, so the load takes
   // the scalar-base + 32-bit-offset form instead of a 64-bit address built
@@ -227,8 +231,11 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
       if constexpr (NX == 5) X[sl][4] = __builtin_amdgcn_raw_buffer_load_b32(trs, t_win[sl] + 16u, to, 0);
     }
     T0[sl] = __builtin_amdgcn_raw_buffer_load_b32(trs, t_first[sl], to, 0);
-    asm volatile("" : "+v"(a_off[sl]));
-    A[sl] = *(const half8_t *)(ap + a_off[sl]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      asm volatile("" : "+v"(a_off[sl][mt]));
+      A[sl][mt] = *(const half8_t *)(ap + a_off[sl][mt]);
+    }
   };
 
   TblUnit cu = make_unit(0);
@@ -242,8 +249,14 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
   barrier_lds();
 
   for (int r = 0; r < rounds; ++r) {
-    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    float4_t tot0 = acc0, tot1 = acc1;
+    float4_t acc0[MT], acc1[MT], tot0[MT], tot1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc0[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      acc1[mt] = acc0[mt];
+      tot0[mt] = acc0[mt];
+      tot1[mt] = acc0[mt];
+    }
     if (cu.nks > 0) {
       // fold at every part end (first part copied, later parts added in
       // part order); part q ends at block floor((q+1)*KB/P)
@@ -278,20 +291,28 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
           table_pairs_of<BITS, TP, 1>(Y, table, f1);
           alu_pairs<BITS, CB, TP, 0>(Y, f0);
           alu_pairs<BITS, CB, TP, 1>(Y, f1);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl], __builtin_bit_cast(half8_t, f0), acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl], __builtin_bit_cast(half8_t, f1), acc1, 0, 0, 0);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            acc0[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl][mt], __builtin_bit_cast(half8_t, f0), acc0[mt], 0,
+                                                              0, 0);
+            acc1[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl][mt], __builtin_bit_cast(half8_t, f1), acc1[mt], 0,
+                                                              0, 0);
+          }
           load_slot(sc, rt, ra);
         });
         if (ks0 + DEPTH == fold_ks) {
-          if (fold_part == cu.part) {
-            tot0 = acc0;
-            tot1 = acc1;
-          } else {
-            tot0 = tot0 + acc0;
-            tot1 = tot1 + acc1;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            if (fold_part == cu.part) {
+              tot0[mt] = acc0[mt];
+              tot1[mt] = acc1[mt];
+            } else {
+              tot0[mt] = tot0[mt] + acc0[mt];
+              tot1[mt] = tot1[mt] + acc1[mt];
+            }
+            acc0[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            acc1[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
           }
-          acc0 = float4_t{0.f, 0.f, 0.f, 0.f};
-          acc1 = float4_t{0.f, 0.f, 0.f, 0.f};
           ++fold_part;
           fold_ks = 4 * ((int)((int64_t)(fold_part + 1) * KB / P) - cu.kb_begin);
         }
@@ -299,30 +320,36 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
     }
     if (slab) {
       if (cu.nks > 0) {
-        store_partial(p.slabs, cu.slab, rows, N, 4 * g, cu.nb * 128 + lane_col(tw, j, 0), tot0);
-        store_partial(p.slabs, cu.slab, rows, N, 4 * g, cu.nb * 128 + lane_col(tw, j, 1), tot1);
-      }
-    } else {
-      // output transform of the team's block through its LDS rows; every
-      // wave of the workgroup takes part in the barriers
-      float *const zb = zbuf_all + team * (16 * 128);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        zb[(4 * g + i) * 128 + lane_col(tw, j, 0)] = tot0[i];
-        zb[(4 * g + i) * 128 + lane_col(tw, j, 1)] = tot1[i];
-      }
-      barrier_lds();
-      if (cu.nks > 0) {
-        uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-        for (int r = tw; r < rows; r += 4) {
-          const float z0 = zb[r * 128 + 2 * lane];
-          const float z1 = zb[r * 128 + 2 * lane + 1];
-          const int64_t row = p.row_base + r;
-          if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
-          else output_row<false>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
+        for (int mt = 0; mt < MT; ++mt) {
+          store_partial(p.slabs, cu.slab, rows, N, 16 * mt + 4 * g, cu.nb * 128 + lane_col(tw, j, 0), tot0[mt]);
+          store_partial(p.slabs, cu.slab, rows, N, 16 * mt + 4 * g, cu.nb * 128 + lane_col(tw, j, 1), tot1[mt]);
         }
       }
-      barrier_lds();
+    } else {
+      // output transform of the team's block through its LDS rows, 16 rows
+      // at a time; every wave of the workgroup takes part in the barriers
+      float *const zb = zbuf_all + team * (16 * 128);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          zb[(4 * g + i) * 128 + lane_col(tw, j, 0)] = tot0[mt][i];
+          zb[(4 * g + i) * 128 + lane_col(tw, j, 1)] = tot1[mt][i];
+        }
+        barrier_lds();
+        if (cu.nks > 0) {
+          uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+          for (int r = tw; r < 16 && 16 * mt + r < rows; r += 4) {
+            const float z0 = zb[r * 128 + 2 * lane];
+            const float z1 = zb[r * 128 + 2 * lane + 1];
+            const int64_t row = p.row_base + 16 * mt + r;
+            if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
+            else output_row<false>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
+          }
+        }
+        barrier_lds();
+      }
     }
     cu = nu;
     nu = make_unit(r + 2);
@@ -340,10 +367,14 @@ constexpr int table_pairs(int) { return EXL3_TABLE_PAIRS; }
 constexpr int table_pairs(int) { return 2; }
 #endif
 
+// One 16-row A fragment per decoded B operand up to 16 rows, two up to 32.
 template <int BITS, uint32_t CB>
 hipError_t launch_table_t(const GemmParams &p, int grid, hipStream_t s) {
   constexpr int TP = table_pairs(BITS);
-  hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
+  const int rows = p.row_end - p.row_base;
+  if (rows <= 16) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 1>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
+  else if (rows <= 32) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 2>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
