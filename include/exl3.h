@@ -108,10 +108,11 @@ typedef enum {
   EXL3_DECODER_AUTO = -1,
   EXL3_DECODER_ALU = 0,  /* tile kernels (bm rows per workgroup): every
                             weight decoded by vector ALU instructions        */
-  EXL3_DECODER_TABLE = 1 /* M <= 32 only: one persistent 1024-thread
+  EXL3_DECODER_TABLE = 1 /* M <= 64 only: one persistent 1024-thread
                             workgroup per CU fills a 65,536-entry state ->
                             fp16 table in LDS and decodes half of the
-                            weights through it, the rest by the ALU          */
+                            weights through it, the rest by the ALU (512
+                            threads above 32 rows)                           */
 } exl3_decoder;
 
 typedef struct exl3_plan {
@@ -122,11 +123,11 @@ typedef struct exl3_plan {
   int32_t bm;          /* rows per M-tile: 16, 32, 64, 128, 256 or 512;
                           512 only with one part per workgroup (parts == 1
                           or slab mode), else EXL3_ERR_UNSUPPORTED.  The
-                          table decoder reports 16 (up to 16 rows) or 32    */
-  int32_t decoder;     /* exl3_decoder.  Automatic: TABLE for M <= 32 on
+                          table decoder reports 16, 32 or 64                */
+  int32_t decoder;     /* exl3_decoder.  Automatic: TABLE for M <= 64 on
                           layers of at least 2^25 weights and at most
                           2 GiB of trellis, else ALU.  In a
-                          forced plan 0 means ALU; TABLE with M > 32 is
+                          forced plan 0 means ALU; TABLE with M > 64 is
                           EXL3_ERR_UNSUPPORTED; forcing bm alone selects
                           ALU                                               */
   int32_t unit;        /* slab mode: parts per workgroup unit (one slab per

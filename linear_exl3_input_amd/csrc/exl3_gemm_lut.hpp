@@ -101,8 +101,10 @@ struct TblUnit {
   int kb_begin;
 };
 
-template <int BITS, uint32_t CB, int TP, int MT>
-__global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmParams p) {
+// TEAMS teams of 4 waves: 4 (1024 threads, 128 VGPRs a wave) up to 32 rows,
+// 2 (512 threads, 256 VGPRs) for the four A fragments of up to 64 rows.
+template <int BITS, uint32_t CB, int TP, int MT, int TEAMS = 4>
+__global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmParams p) {
   using G = TblGeom<BITS>;
   constexpr int NX = G::NX, NY = G::NY, TILE_DW = G::TILE_DW;
   constexpr int DEPTH = TBL_DEPTH;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
   const int NU = P / p.unit;  // units per column block (slab mode)
   const int units = slab ? nblk * NU : nblk;
   const int rows = p.row_end - p.row_base;
-  const int stride = gridDim.x * TBL_TEAMS;
+  const int stride = gridDim.x * TEAMS;
   const int rounds = (units + stride - 1) / stride;
 
   const int64_t tsb = (int64_t)2 * NT * TILE_DW * 4;  // trellis bytes per k-step (two k-tiles)
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
     TblUnit u;
     // units go round the workgroups first, so that fewer units than teams
     // still spread over every CU
-    const int id = (r * TBL_TEAMS + team) * (int)gridDim.x + (int)blockIdx.x;
+    const int id = (r * TEAMS + team) * (int)gridDim.x + (int)blockIdx.x;
     if (r >= rounds || id >= units) {
       u.t = 0;
       u.a = xrot;
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(TBL_THREADS, 1) void gemm_table_kernel(const GemmPa
   static_for<0, DEPTH>([&](auto sc) { load_slot(sc, cu.t, cu.a); });
 
   // ---- the table, two states per thread and store (overlaps the first loads)
-  for (int s2 = tid; s2 < 32768; s2 += TBL_THREADS) lds[s2] = decode_pair<CB>(2 * s2, 2 * s2 + 1);
+  for (int s2 = tid; s2 < 32768; s2 += 256 * TEAMS) lds[s2] = decode_pair<CB>(2 * s2, 2 * s2 + 1);
   barrier_lds();
 
   for (int r = 0; r < rounds; ++r) {
@@ -367,13 +369,15 @@ constexpr int table_pairs(int) { return EXL3_TABLE_PAIRS; }
 constexpr int table_pairs(int) { return 2; }
 #endif
 
-// One 16-row A fragment per decoded B operand up to 16 rows, two up to 32.
+// One 16-row A fragment per decoded B operand up to 16 rows, two up to 32,
+// four (two teams per workgroup) up to 64.
 template <int BITS, uint32_t CB>
 hipError_t launch_table_t(const GemmParams &p, int grid, hipStream_t s) {
   constexpr int TP = table_pairs(BITS);
   const int rows = p.row_end - p.row_base;
   if (rows <= 16) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 1>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
   else if (rows <= 32) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 2>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
+  else if (rows <= 64) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 4, 2>), dim3(grid), dim3(512), 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -153,7 +153,7 @@ struct Plan {
 // The table decoder pays a fixed cost per CU (filling a 65,536-entry table)
 // that the layer's weights have to amortize.
 constexpr double TABLE_MIN_WEIGHTS = 33554432.0;  // 2^25
-constexpr int32_t TABLE_MAX_M = 32;
+constexpr int32_t TABLE_MAX_M = 64;
 // The table kernel addresses the trellis with 32-bit byte offsets.
 constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
 // Partial slabs beyond this go through the fused fold (or row chunks).
@@ -215,7 +215,7 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
       return fail(EXL3_ERR_INVALID_ARG, "forced bm=%d, must be 16, 32, 64, 128, 256 or 512", force->bm);
     pl.bm = force->bm;
   }
-  if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = M <= 16 ? 16 : 32;
+  if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : 64;
   // Mode.  One group: a workgroup folds all parts (one level).  One part per
   // group: separate fp32 partials (one workgroup per part: P times the
   // workgroups) while their traffic is small next to the GEMM's; beyond

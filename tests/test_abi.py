@@ -197,9 +197,9 @@ def test_part_sums_hook_checks_its_buffer():
 
 
 def test_table_decoder_choice_and_limits():
-    """M <= 32 on layers of 2^25 weights or more: the table decoder (reported
-    with bm 16 up to 16 rows, 32 above); forcing it above 32 rows, or an
-    unknown decoder, is refused before any launch."""
+    """M <= 64 on layers of 2^25 weights or more: the table decoder (reported
+    with bm 16, 32 or 64); forcing it above 64 rows, or an unknown decoder,
+    is refused before any launch."""
     L = ex.load()
     head = view(4096, (154880,), 6, 2)
     for M in (1, 8, 16):
@@ -208,16 +208,19 @@ def test_table_decoder_choice_and_limits():
     for M in (17, 24, 32):
         p = _plan(head, M)
         assert p.decoder == ex.EXL3_DECODER_TABLE and p.bm == 32, M
-    assert _plan(head, 33).decoder == ex.EXL3_DECODER_ALU
+    for M in (33, 64):
+        p = _plan(head, M)
+        assert p.decoder == ex.EXL3_DECODER_TABLE and p.bm == 64, M
+    assert _plan(head, 65).decoder == ex.EXL3_DECODER_ALU
     assert _plan(view(5120, (12288,), 6, 2), 1).decoder == ex.EXL3_DECODER_TABLE  # 62.9M weights
     assert _plan(view(4096, (2048,), 4, 1), 1).decoder == ex.EXL3_DECODER_ALU     # 8.4M weights
     small = view(1024, (1024,), 4, 0)
     slabs = F(4, ex.EXL3_MODE_SLABS, -1, ex.EXL3_DECODER_TABLE)
     assert L.exl3_workspace_bytes_ex(ctypes.byref(small), 16, ctypes.byref(slabs)) == CB + 4 * 16 * 1024 * 4
     too_tall = F(decoder=ex.EXL3_DECODER_TABLE)
-    assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 33, FAKE, 1, FAKE, 1 << 30, None,
+    assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 65, FAKE, 1, FAKE, 1 << 30, None,
                             ctypes.byref(too_tall)) == 2  # EXL3_ERR_UNSUPPORTED
-    assert "at most 32 rows" in last_error()
+    assert "at most 64 rows" in last_error()
     unknown = F(decoder=7)
     assert L.exl3_linear_ex(ctypes.byref(small), FAKE, 4, FAKE, 1, FAKE, 1 << 30, None,
                             ctypes.byref(unknown)) == 1  # EXL3_ERR_INVALID_ARG

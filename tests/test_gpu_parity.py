@@ -189,12 +189,12 @@ TABLE_CASES = [(1, "3inst"), (2, "mul1"), (3, "mcg"), (4, "mcg"), (5, "mul1"), (
 
 
 @pytest.mark.parametrize("bits,cb", TABLE_CASES)
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 33, 64])
 def test_table_decoder_matches_alu(bits, cb, M):
     """The table decoder against the ALU tile kernel: the same bits for one
     part, a fused multi-part fold, and slabs; two shards, ragged rows."""
     banner(f"table decoder {bits}-bit {cb} M={M}")
-    lay = wl.small_layer(f"table_b{bits}_{cb}", 1024, (256, 384), bits, cb, (32,), seed=80 + bits)
+    lay = wl.small_layer(f"table_b{bits}_{cb}", 1024, (256, 384), bits, cb, (64,), seed=80 + bits)
     t = wl.gen_all(lay)
     y = None
     for parts, mode in ((1, ex.EXL3_MODE_FUSED), (2, ex.EXL3_MODE_FUSED), (4, ex.EXL3_MODE_SLABS),
@@ -421,6 +421,7 @@ def test_zero_rows_is_a_noop():
 
 FULL = [("small_1024x1024_b4_3inst", 16), ("expert_4096x2048_b4_mcg", 512), ("expert_2048x4096_b4_mcg", 16),
         ("q_proj_5120x12288_b6_mul1", 128), ("q_proj_5120x12288_b6_mul1", 24), ("down_proj_17408x5120_b6_mul1", 16),
+        ("down_proj_17408x5120_b6_mul1", 64),
         ("gate_up_5120x2x17408_b5_mul1", 2048), ("lm_head_4096x154880_b6_mul1", 16)]
 
 
@@ -435,7 +436,7 @@ def test_full_size_sampled(name, M):
     # batch invariance at the real shape: the first row alone
     y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
     assert np.array_equal(y1[0], y[0])
-    if M <= 32:  # both decoders at the real shape
+    if M <= 64:  # both decoders at the real shape
         for dec in (ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE):
             assert np.array_equal(bits16(ex.linear(w, xr, torch.bfloat16, decoder=dec)), y), f"decoder {dec}"
     rows = sorted({0, M // 2, M - 1})
