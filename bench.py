@@ -47,7 +47,8 @@ WORKLOADS = {
 }
 DEFAULT_WORKLOAD = "expert_4096x2048+2048x4096_b4_mcg"
 
-KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_gemm_lut.hpp", "exl3_device.hpp", "exl3_misc.hip"]
+KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_gemm_lut.hpp", "exl3_gemm_dense.hpp", "exl3_device.hpp",
+                  "exl3_misc.hip"]
 
 
 def sol_seconds(M, K, N, bits):
@@ -62,6 +63,8 @@ def kernel_key(lay, plan) -> str:
     cb = {"3inst": 0, "mcg": 1, "mul1": 2}[lay.codebook]
     if plan.get("decoder") == 1:
         return f"exl3::gemm_table_kernel<{lay.bits}, {cb}u, 2>"
+    if plan.get("decoder") == 2:
+        return f"exl3::gemm_dense_kernel<{str(unit > 1).lower()}>"
     quads = unit if (bm <= 64 and unit in (2, 4) and (lay.K // 128) % plan["parts"] == 0) else 1
     multi = unit > 1 and quads == 1
     if bm <= 64:

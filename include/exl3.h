@@ -108,11 +108,15 @@ typedef enum {
   EXL3_DECODER_AUTO = -1,
   EXL3_DECODER_ALU = 0,  /* tile kernels (bm rows per workgroup): every
                             weight decoded by vector ALU instructions        */
-  EXL3_DECODER_TABLE = 1 /* M <= 64 only: one persistent 1024-thread
+  EXL3_DECODER_TABLE = 1, /* M <= 64 only: one persistent 1024-thread
                             workgroup per CU fills a 65,536-entry state ->
                             fp16 table in LDS and decodes half of the
                             weights through it, the rest by the ALU (512
                             threads above 32 rows)                           */
+  EXL3_DECODER_DENSE = 2 /* large batches: the whole W_q is decoded once
+                            into the workspace (K*N fp16, as matrix-core
+                            operand fragments), then a dense GEMM in
+                            256-row tiles reads it; same bits             */
 } exl3_decoder;
 
 typedef struct exl3_plan {

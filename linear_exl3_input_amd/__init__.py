@@ -39,7 +39,7 @@ _F16, _BF16 = 0, 1
 MAX_SHARDS = 16
 
 EXL3_MODE_AUTO, EXL3_MODE_FUSED, EXL3_MODE_SLABS = -1, 0, 1
-EXL3_DECODER_AUTO, EXL3_DECODER_ALU, EXL3_DECODER_TABLE = -1, 0, 1
+EXL3_DECODER_AUTO, EXL3_DECODER_ALU, EXL3_DECODER_TABLE, EXL3_DECODER_DENSE = -1, 0, 1, 2
 
 
 class Exl3Error(RuntimeError):

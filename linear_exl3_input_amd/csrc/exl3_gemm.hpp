@@ -1041,6 +1041,42 @@ __global__ __launch_bounds__(WG_THREADS) void debug_decode_kernel(const DecodePa
   }
 }
 
+// Dequantize to B fragments: the whole W_q once, in the order the matrix
+// core reads it, for the dense GEMM of large batches.  Fragment f = 2w + h
+// of 32-k step ks and 128-column block nb is the B operand wave w of a tile
+// kernel decodes for column half h (n-tiles 2w, 2w+1): lane L holds its 8
+// fp16 values as 16 contiguous bytes, so
+//   wf[((ks * nblk + nb) * 8 + f) * 64 + L]  (16 bytes each)
+// and one k-step of a block is 8 KB.  The same staging and decode_frag as
+// the tile kernels, so the same fp16 values.  One workgroup per 128 k x 128
+// columns.
+template <int BITS, uint32_t CB>
+__global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const DecodeParams p) {
+  using G = Geom<BITS>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[G::STAGE_T_DW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int nb = blockIdx.x, kb = blockIdx.y;
+  const int nblk = p.N >> 7;
+  u32x4_t treg[G::T_ITERS];
+  load_trellis_stage<BITS>(treg, p.trellis, kb, nb, p.N >> 4, tid);
+  store_trellis_stage<BITS>(treg, lds, tid);
+  __syncthreads();
+  const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
+  u32x4_t *const wf = reinterpret_cast<u32x4_t *>(p.wq);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t *tp = lds + (tile_lane + 2 * WG_NT * ks) * G::STRIDE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int xoff, sh;
+      lane_window<BITS>(j, g, h, xoff, sh);
+      const u32x4_t b = __builtin_bit_cast(u32x4_t, decode_frag<BITS, CB>(tp, xoff, sh));
+      wf[(((int64_t)(4 * kb + ks) * nblk + nb) * 8 + 2 * wave + h) * 64 + lane] = b;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 // quads > 1: one part per quad (no register fold); otherwise `multi` folds
@@ -1109,6 +1145,18 @@ hipError_t launch_gemm_bits(int cb, int bm, int quads, bool half, bool multi, co
 }
 
 template <int BITS>
+hipError_t launch_dequant_bits(int cb, const DecodeParams &p, hipStream_t s) {
+  const dim3 grid(p.N / 128, p.K / 128);
+  switch (cb) {
+    case 0: hipLaunchKernelGGL((dequant_kernel<BITS, CB_3INST>), grid, dim3(WG_THREADS), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((dequant_kernel<BITS, CB_MCG>), grid, dim3(WG_THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((dequant_kernel<BITS, CB_MUL1>), grid, dim3(WG_THREADS), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
 hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
   const dim3 grid(p.N / 128, p.K / 128);
   switch (cb) {
@@ -1133,5 +1181,8 @@ hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
   }                                                                                                \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s) {              \
     return launch_decode_bits<B>(cb, p, s);                                                        \
+  }                                                                                                \
+  hipError_t launch_dequant_b##B(int cb, const DecodeParams &p, hipStream_t s) {                   \
+    return launch_dequant_bits<B>(cb, p, s);                                                       \
   }                                                                                                \
   }

@@ -1,0 +1,235 @@
+// Dense GEMM over dequantized B fragments, for large batches on gfx950.
+//
+// At a few hundred rows and more the trellis decode inside the tile kernels
+// (about five VALU instructions per weight, interleaved with the matrix-core
+// work and the LDS traffic of the rotated activations) keeps the matrix core
+// busy well under half the time.  Decoding the layer once into fp16 B
+// fragments (dequant_kernel: K*N*2 bytes of workspace) and then running a
+// plain MFMA GEMM over them takes the decode out of the loop.  Every MFMA
+// multiplies the same A and B fragments (same lanes, same k slots) in the
+// same k-step order, and the K parts are folded the same way, so the result
+// has the same bits as the decoding kernels.
+//
+// Tile: 256 rows x 128 columns on 8 waves, two per SIMD, so each wave has at
+// most 256 registers and the compiler keeps the accumulators in ordinary
+// VGPRs (with 4 waves and 512 registers a wave it moved them through the
+// accumulation registers with copies around every MFMA, a third of the
+// matrix-core rate).  Wave w = 2*rw + cw owns rows 64*rw .. +63 (A fragments
+// 4rw .. 4rw+3) and the 64 columns of B fragments 4cw .. 4cw+3 (fragment
+// f = 2w' + h is column half h of n-tiles 2w', 2w'+1): per 32-k step it
+// reads 4 A and 4 B fragments from LDS and issues 16 MFMAs into 64
+// accumulators (64 more hold the part fold).  Both operands arrive by
+// direct-to-LDS loads into a ring of DN_PF k-step slots (16 KB of x~ rows
+// m0 .. m0+255, contiguous in the k-step tile layout, and the block's 8 KB of
+// fragments, contiguous in the dequantized layout), in lane order, so every
+// LDS read is one conflict-free ds_read_b128.  Per k-step: wait for the next
+// k-step's loads, one barrier, issue the loads of the k-step DN_PF ahead into
+// the slot just consumed, read the next k-step's fragments into the second
+// register set, then the 16 MFMAs on the first.
+#pragma once
+
+#include "exl3_gemm.hpp"
+
+namespace exl3 {
+
+constexpr int DN_THREADS = 512;
+constexpr int DN_BM = 256;
+constexpr int DN_PF = 6;                          // ring slots, k-steps in flight
+constexpr int DN_A_DW = 16 * 256;                 // 16 fragments of 16 rows: 16 KB
+constexpr int DN_B_DW = 8 * 256;                  // 8 fragments: 8 KB
+constexpr int DN_SLOT_DW = DN_A_DW + DN_B_DW;
+constexpr int DN_LOADS = DN_SLOT_DW / DN_THREADS / 4;  // 16-byte loads per lane per k-step (3)
+
+// Tile order.  Workgroups go to the 8 XCDs (each with its own L2) in turn:
+// workgroup L runs on XCD L % 8.  Each XCD takes a contiguous range of the
+// tile order, and the order runs through up to 8 row tiles of one column
+// block before the next block, so the row tiles that read the same B block
+// run together on one XCD and share its L2 (and the workgroups an XCD holds
+// at a time read the same few x~ row tiles).  A bijection for any count;
+// only the speed depends on the dispatch order.
+__device__ __forceinline__ void dense_tile(int L, int total, int mtiles, int &nb, int &mt) {
+  const int q = total >> 3, r = total & 7, x = L & 7;
+  const int T = x * q + (x < r ? x : r) + (L >> 3);
+  const int nblk = total / mtiles;
+  const int g = T / (nblk * 8);             // group of 8 row tiles
+  const int gs = mtiles - 8 * g < 8 ? mtiles - 8 * g : 8;
+  const int rem = T - g * nblk * 8;
+  nb = rem / gs;
+  mt = 8 * g + rem % gs;
+}
+
+template <bool MULTI>
+__global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmParams p) {
+  constexpr int PF = DN_PF;
+  constexpr int MAIN_DW = PF * DN_SLOT_DW;
+  constexpr int Z_DW = 64 * Z_ROW;
+  constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
+  static_assert(LDS_DW * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rw = wave >> 1;
+  const int cw = wave & 1;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  int nb, mt;
+  dense_tile(blockIdx.x, gridDim.x, (p.row_end - p.row_base + DN_BM - 1) / DN_BM, nb, mt);
+  const int m0 = p.row_base + mt * DN_BM;
+  const int rend = p.row_end;
+  const int M = p.M, K = p.K, N = p.N;
+  const int KB = K >> 7;
+  const int nblk = N >> 7;
+
+  const int p_begin = blockIdx.y * p.unit;
+  const int p_end = p_begin + p.unit;
+  const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
+  const int kb_end = (int)((int64_t)p_end * KB / p.parts);
+  const int ks_begin = 4 * kb_begin;
+  const int nks = 4 * (kb_end - kb_begin);
+
+  int shard = 0;
+  while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
+  const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
+
+  // Load sources (16-bit words).  A: the lane's chunk of fragment 8r + wave
+  // of a k-step: row 16(8r + wave) + (lane & 15), 16-byte piece lane >> 4
+  // (rows past the launch's last load that row: finite, never stored).  B:
+  // chunk 64 wave + lane of the block's 8 KB.
+  uint32_t a_src[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    int row = m0 + 16 * (8 * r + wave) + (lane & 15);
+    row = row < rend ? row : rend - 1;
+    a_src[r] = (uint32_t)(row * 32 + 8 * (lane >> 4));
+  }
+  auto issue = [&](int ks, int slot) __attribute__((always_inline)) {
+    const int kk = ks_begin + (ks < nks ? ks : nks - 1);
+    uint32_t *const sl = lds + slot * DN_SLOT_DW;
+    const uint16_t *const abase = xs + (int64_t)kk * M * 32;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(abase + a_src[r]),
+                                       (__attribute__((address_space(3))) void *)(sl + (8 * r + wave) * 256), 16, 0,
+                                       0);
+    const uint16_t *const bbase = p.dense + ((int64_t)kk * nblk + nb) * (8 * 64 * 8);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(bbase + (wave * 64 + lane) * 8),
+                                     (__attribute__((address_space(3))) void *)(sl + DN_A_DW + wave * 256), 16, 0, 0);
+  };
+
+  half8_t A[2][4], B[2][4];
+  auto read_frags = [&](int ks, int set) __attribute__((always_inline)) {
+    const uint32_t *const sl = lds + (ks % PF) * DN_SLOT_DW + 4 * lane;
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) B[set][fi] = *(const half8_t *)(sl + DN_A_DW + (4 * cw + fi) * 256);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[set][m] = *(const half8_t *)(sl + (4 * rw + m) * 256);
+  };
+
+  float4_t acc[4][4];
+  float4_t tot[MULTI ? 4 : 1][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) acc[m][fi] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i < PF; ++i) issue(i, i);
+  wait_vmcnt<DN_LOADS * (PF - 1)>();  // k-step 0 landed
+  barrier_lds();
+  read_frags(0, 0);
+
+  // part boundaries (in k-steps from ks_begin): part q ends at block
+  // floor((q+1)*KB/P); the first part's sum is copied, later ones added
+  int part = p_begin;
+  int part_end = 4 * ((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin);
+
+  auto step = [&](int i, auto set_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(set_c)::value;
+    wait_vmcnt<DN_LOADS * (PF - 2)>();  // k-step i+1 landed
+    barrier_lds();                        // ... for every wave; slot i % PF is free
+    issue(i + PF, i % PF);
+    if (i + 1 < nks) read_frags(i + 1, cur ^ 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+        acc[m][fi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cur][m], B[cur][fi], acc[m][fi], 0, 0, 0);
+    if constexpr (MULTI) {
+      if (i + 1 == part_end) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int fi = 0; fi < 4; ++fi) {
+            tot[m][fi] = part == p_begin ? acc[m][fi] : tot[m][fi] + acc[m][fi];
+            acc[m][fi] = float4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        ++part;
+        part_end = 4 * ((int)((int64_t)(part + 1) * KB / p.parts) - kb_begin);
+      }
+    }
+  };
+  // nks is a multiple of 4: two k-steps per trip keep the register sets static
+  for (int i = 0; i < nks; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
+  }
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi) acc[m][fi] = tot[m][fi];
+  }
+  wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
+  barrier_lds();
+
+  // lane's column (within the block) of acc[.][fi]: fragment f = 4cw + fi is
+  // column half f & 1 of n-tiles 2(f >> 1), 2(f >> 1) + 1
+  int col[4];
+#pragma unroll
+  for (int fi = 0; fi < 4; ++fi) col[fi] = lane_col((4 * cw + fi) >> 1, j, (4 * cw + fi) & 1);
+
+  if (p.slab_mode) {
+    const int rows = rend - p.row_base;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+        store_partial(p.slabs, blockIdx.y, rows, N, m0 - p.row_base + 64 * rw + 16 * m + 4 * g, nb * 128 + col[fi],
+                      acc[m][fi]);
+    return;
+  }
+
+  // output transform, 64 rows (one row of waves) per pass through LDS
+  float *z = reinterpret_cast<float *>(lds);
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    if (pass > 0) barrier_lds();
+    if (rw == pass) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[(m * 16 + 4 * g + e) * Z_ROW + col[fi]] = acc[m][fi][e];
+    }
+    barrier_lds();
+    for (int r = wave; r < 64; r += 8) {
+      const int row = m0 + pass * 64 + r;
+      if (row >= rend) break;
+      const float z0 = z[r * Z_ROW + 2 * lane];
+      const float z1 = z[r * Z_ROW + 2 * lane + 1];
+      if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+      else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+    }
+  }
+}
+
+hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (multi) hipLaunchKernelGGL((gemm_dense_kernel<true>), grid, dim3(DN_THREADS), 0, s, p);
+  else hipLaunchKernelGGL((gemm_dense_kernel<false>), grid, dim3(DN_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace exl3

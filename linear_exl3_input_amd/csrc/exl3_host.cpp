@@ -147,6 +147,8 @@ struct Plan {
   bool finisher;     // slab mode: the last workgroup of a tile does the output
   int32_t chunk;     // rows per launch
   int32_t launches;  // kernels per exl3_linear call
+  size_t slab_off;   // workspace byte offsets of the slabs and the dense W_q
+  size_t dense_off;
   size_t workspace;
 };
 
@@ -160,6 +162,13 @@ constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
 constexpr double SLAB_CAP_BYTES = 192.0 * 1024 * 1024;
 // Tiles the finisher's counters can hold (one 32-bit counter each).
 constexpr int64_t MAX_COUNTERS = EXL3_WORKSPACE_COUNTER_BYTES / 4;
+// Dense path (dequantize once, then a plain MFMA GEMM): batches and layers
+// large enough for the K*N*2 bytes of fp16 fragments to pay off.  Measured:
+// gate_up 5120 x 34816 at 2048 rows 986 -> 937 us, at 4096 rows
+// 1847 -> 1661 us; at 512 rows it loses on every layer shape (lm_head
+// 761 -> 1081 us: its fp16 fragments are 1.27 GB against 476 MB of trellis).
+constexpr int32_t DENSE_MIN_M = 2048;
+constexpr double DENSE_MIN_WEIGHTS = 33554432.0;
 
 size_t slab_bytes(int32_t n_slabs, int32_t rows, int32_t N) {
   return (size_t)n_slabs * (size_t)((rows + 3) / 4) * 4 * (size_t)N * sizeof(float);
@@ -196,11 +205,14 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   const double weights = (double)w->K * (double)w->N;
   const bool table_fits = weights * w->bits / 8.0 <= TABLE_MAX_TRELLIS_BYTES;
   pl.decoder = (M <= TABLE_MAX_M && weights >= TABLE_MIN_WEIGHTS && table_fits) ? EXL3_DECODER_TABLE
-                                                                                : EXL3_DECODER_ALU;
+                : (M >= DENSE_MIN_M && weights >= DENSE_MIN_WEIGHTS) ? EXL3_DECODER_DENSE
+                                                                    : EXL3_DECODER_ALU;
   if (bm_forced) pl.decoder = EXL3_DECODER_ALU;
   if (force && force->decoder >= 0) {
-    if (force->decoder != EXL3_DECODER_ALU && force->decoder != EXL3_DECODER_TABLE)
-      return fail(EXL3_ERR_INVALID_ARG, "forced decoder=%d, must be 0 (alu) or 1 (table)", force->decoder);
+    if (force->decoder != EXL3_DECODER_ALU && force->decoder != EXL3_DECODER_TABLE &&
+        force->decoder != EXL3_DECODER_DENSE)
+      return fail(EXL3_ERR_INVALID_ARG, "forced decoder=%d, must be 0 (alu), 1 (table) or 2 (dense)",
+                  force->decoder);
     if (force->decoder == EXL3_DECODER_TABLE && M > TABLE_MAX_M)
       return fail(EXL3_ERR_UNSUPPORTED, "the table decoder takes at most %d rows; M=%d (over by %d)", TABLE_MAX_M,
                   M, M - TABLE_MAX_M);
@@ -216,6 +228,7 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
     pl.bm = force->bm;
   }
   if (pl.decoder == EXL3_DECODER_TABLE) pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : 64;
+  if (pl.decoder == EXL3_DECODER_DENSE) pl.bm = 256;  // the dense kernel's tile
   // Mode.  One group: a workgroup folds all parts (one level).  One part per
   // group: separate fp32 partials (one workgroup per part: P times the
   // workgroups) while their traffic is small next to the GEMM's; beyond
@@ -294,16 +307,22 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   }
   pl.launches = pl.mode == EXL3_MODE_SLABS && !pl.finisher ? 2 : 1;
   if (pl.chunk < M && M > 0) pl.launches *= (M + pl.chunk - 1) / pl.chunk;
-  // counters, then slabs [n_slabs][ceil(chunk/4)][N][4] fp32
-  pl.workspace = pl.mode == EXL3_MODE_SLABS
-                     ? (size_t)EXL3_WORKSPACE_COUNTER_BYTES + slab_bytes(n_slabs, pl.chunk, w->N)
-                     : 0;
+  if (pl.decoder == EXL3_DECODER_DENSE) pl.launches += 1;  // the dequantization
+  // counters, then slabs [n_slabs][ceil(chunk/4)][N][4] fp32, then (dense)
+  // W_q as B fragments, K*N fp16
+  pl.slab_off = EXL3_WORKSPACE_COUNTER_BYTES;
+  pl.dense_off = pl.slab_off + (pl.mode == EXL3_MODE_SLABS ? slab_bytes(n_slabs, pl.chunk, w->N) : 0);
+  pl.dense_off = (pl.dense_off + 255) & ~(size_t)255;
+  pl.workspace = pl.decoder == EXL3_DECODER_DENSE ? pl.dense_off + (size_t)w->K * (size_t)w->N * 2
+                 : pl.mode == EXL3_MODE_SLABS     ? pl.slab_off + slab_bytes(n_slabs, pl.chunk, w->N)
+                                                  : 0;
   *out = pl;
   return EXL3_OK;
 }
 
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
-                       uint32_t *counters, float *slabs, const Plan &pl, hipStream_t s, bool with_output);
+                       uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
+                       bool with_output);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -407,10 +426,11 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
   }
 
   uint32_t *counters = static_cast<uint32_t *>(workspace);
-  float *slabs = pl.workspace > 0
-                     ? reinterpret_cast<float *>(static_cast<char *>(workspace) + EXL3_WORKSPACE_COUNTER_BYTES)
-                     : nullptr;
-  return run_linear(w, x_rot, M, y, y_dtype, counters, slabs, pl, (hipStream_t)stream, true);
+  float *slabs = pl.workspace > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.slab_off) : nullptr;
+  uint16_t *dense =
+      pl.decoder == EXL3_DECODER_DENSE ? reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + pl.dense_off)
+                                       : nullptr;
+  return run_linear(w, x_rot, M, y, y_dtype, counters, slabs, dense, pl, (hipStream_t)stream, true);
 }
 
 }  // extern "C"
@@ -422,7 +442,8 @@ namespace {
 // part sum + output transform (in the GEMM's last workgroup of each tile when
 // the plan has the finisher, else as a second kernel).
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
-                       uint32_t *counters, float *slabs, const Plan &pl, hipStream_t s, bool with_output) {
+                       uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
+                       bool with_output) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.trellis = w->trellis;
@@ -447,10 +468,25 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
   }
   const int32_t n_units = p.slab_mode ? pl.parts / pl.unit : 1;
   hipError_t e;
+  if (pl.decoder == EXL3_DECODER_DENSE) {
+    exl3::DecodeParams dp;
+    dp.trellis = w->trellis;
+    dp.wq = dense;
+    dp.K = w->K;
+    dp.N = w->N;
+    if ((e = exl3::launch_dequant(w->bits, w->codebook, dp, s)) != hipSuccess) return launch_error(e, "dequant launch");
+    p.dense = dense;
+  }
   for (int32_t r0 = 0; r0 < M; r0 += pl.chunk) {
     p.row_base = r0;
     p.row_end = std::min(M, r0 + pl.chunk);
-    if (pl.decoder == EXL3_DECODER_TABLE) {
+    if (pl.decoder == EXL3_DECODER_DENSE) {
+      // one dimension of tiles (column blocks x 256-row tiles), ordered
+      // inside the kernel; units on y
+      const dim3 grid((unsigned)(w->N / 128 * ((p.row_end - p.row_base + 255) / 256)), (unsigned)n_units, 1);
+      e = exl3::launch_gemm_dense(pl.multi, p, grid, s);
+      if (e != hipSuccess) return launch_error(e, "dense GEMM launch");
+    } else if (pl.decoder == EXL3_DECODER_TABLE) {
       int cus = 0;
       if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
       const int64_t units = (int64_t)(w->N / 128) * n_units;
@@ -525,7 +561,9 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
   if (z_bytes < need)
     return fail(EXL3_ERR_WORKSPACE, "z_parts holds %zu bytes; %d slabs of %d rows need %zu (short by %zu)", z_bytes,
                 n_slabs, M, need, need - z_bytes);
-  return run_linear(w, x_rot, M, nullptr, EXL3_BF16, nullptr, z_parts, pl, (hipStream_t)stream, false);
+  if (pl.decoder == EXL3_DECODER_DENSE)
+    return fail(EXL3_ERR_UNSUPPORTED, "the part-sums hook runs the decoding kernels; decoder=dense needs a workspace");
+  return run_linear(w, x_rot, M, nullptr, EXL3_BF16, nullptr, z_parts, nullptr, pl, (hipStream_t)stream, false);
 }
 
 exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream) {

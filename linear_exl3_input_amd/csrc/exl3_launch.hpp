@@ -13,6 +13,7 @@ struct GemmParams {
   const uint16_t *trellis;  // [K/16][N/16][16*bits]
   const uint16_t *x_rot;    // [n_shards][K/32][M][32] fp16 bits (k-step tiles)
   const uint16_t *svh;      // [N] fp16 bits
+  const uint16_t *dense;    // dense path: W_q as B fragments (dequant_kernel order)
   void *y;                  // [M][N] bf16/fp16
   float *slabs;             // [units][ceil(rows/4)][N][4] fp32 (slab mode)
   uint32_t *counters;       // slab mode: per-tile arrival counters (zero on
@@ -45,6 +46,11 @@ struct DecodeParams {
 hipError_t launch_gemm(int bits, int cb, int bm, int quads, bool half, bool multi_part, const GemmParams &p,
                        dim3 grid, hipStream_t s);
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s);
+// W_q as matrix-core B fragments (p.wq: K*N fp16 in the fragment order of
+// dequant_kernel), and the dense GEMM over them (same arithmetic as the tile
+// kernels: p.trellis unused, p.dense the fragments), 256-row tiles.
+hipError_t launch_dequant(int bits, int cb, const DecodeParams &p, hipStream_t s);
+hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
 // Table-decode GEMM (M <= 16): `grid` persistent workgroups of 1024 threads,
 // one per CU; fused (parts folded in order) or slab mode as in p.
 hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hipStream_t s);
@@ -63,6 +69,7 @@ hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
   hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool half, bool multi_part,              \
                               const GemmParams &p, dim3 grid, hipStream_t s);                   \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);            \
+  hipError_t launch_dequant_b##B(int cb, const DecodeParams &p, hipStream_t s);                 \
   hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s);
 EXL3_DECLARE_BITS(1)
 EXL3_DECLARE_BITS(2)

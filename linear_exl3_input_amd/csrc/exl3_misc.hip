@@ -243,6 +243,20 @@ hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hi
   }
 }
 
+hipError_t launch_dequant(int bits, int cb, const DecodeParams &p, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_dequant_b1(cb, p, s);
+    case 2: return launch_dequant_b2(cb, p, s);
+    case 3: return launch_dequant_b3(cb, p, s);
+    case 4: return launch_dequant_b4(cb, p, s);
+    case 5: return launch_dequant_b5(cb, p, s);
+    case 6: return launch_dequant_b6(cb, p, s);
+    case 7: return launch_dequant_b7(cb, p, s);
+    case 8: return launch_dequant_b8(cb, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s) {
   switch (bits) {
     case 1: return launch_debug_decode_b1(cb, p, s);

@@ -162,8 +162,12 @@ def test_plan_modes_and_workspace():
     small, big = _plan(w, 16), _plan(w, 4096)
     assert small.parts == big.parts > 1
     assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == CB + small.parts * 16 * 5120 * 4
-    assert big.mode == ex.EXL3_MODE_FUSED and big.workspace == 0
+    # 4096 rows of a 89M-weight layer: dequantize once into K*N fp16, dense GEMM
+    assert big.mode == ex.EXL3_MODE_FUSED and big.decoder == ex.EXL3_DECODER_DENSE
+    assert big.workspace == CB + 17408 * 5120 * 2 and big.launches == 2
     assert small.bm == 16 and _plan(w, 24).bm == 32 and big.bm == 256
+    assert _plan(w, 2047).decoder == ex.EXL3_DECODER_ALU and _plan(w, 2048).decoder == ex.EXL3_DECODER_DENSE
+    assert _plan(view(4096, (2048,), 4, 1), 4096).decoder == ex.EXL3_DECODER_ALU  # 8.4M weights
     mid = _plan(w, 512)  # 17 parts x 512 x 5120 x 4 B = 178 MB of partials: slabs of 512 rows
     assert mid.mode == ex.EXL3_MODE_SLABS and mid.bm == 512
     head = view(4096, (154880,), 6, 2)
@@ -247,3 +251,19 @@ def test_epilogue_hook_checks_groups():
     w = view(256, (256,), 4, 1)
     assert L.exl3_debug_epilogue(FAKE, 6, 4, 3, ctypes.byref(w), FAKE, 1, None) == 1
     assert "groups=4" in last_error()
+
+
+def test_dense_decoder_plan_and_limits():
+    """Forced decoder=2: K*N fp16 of B fragments after the counters and the
+    slabs (256-byte aligned); the part-sums hook refuses it (it has no
+    workspace to decode into)."""
+    L = ex.load()
+    w = view(1024, (384,), 4, 1)
+    fused = F(1, ex.EXL3_MODE_FUSED, -1, ex.EXL3_DECODER_DENSE)
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 300, ctypes.byref(fused)) == CB + 1024 * 384 * 2
+    slabs = F(4, ex.EXL3_MODE_SLABS, -1, ex.EXL3_DECODER_DENSE)
+    slab_b = 4 * 20 * 384 * 4  # 4 parts x 17 rows padded to 20 x 384 columns x fp32
+    assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 17, ctypes.byref(slabs)) == \
+        ((CB + slab_b + 255) // 256) * 256 + 1024 * 384 * 2
+    assert L.exl3_debug_parts(ctypes.byref(w), FAKE, 17, FAKE, 1 << 30, None, ctypes.byref(slabs)) == 2
+    assert "decoder=dense" in last_error()

@@ -219,6 +219,28 @@ def test_table_decoder_several_units_per_team(mode):
     assert np.array_equal(y, ref)
 
 
+DENSE_CASES = [(1, "mul1"), (2, "3inst"), (3, "mcg"), (4, "mcg"), (5, "mul1"), (6, "mul1"), (7, "3inst"), (8, "mcg")]
+
+
+@pytest.mark.parametrize("bits,cb", DENSE_CASES)
+@pytest.mark.parametrize("M", [1, 17, 256, 300, 600])
+def test_dense_decoder_matches_alu(bits, cb, M):
+    """Dequantize-then-GEMM against the ALU tile kernel: the same bits for
+    one part, a register fold of 2 and of 3 unequal parts, one slab per part
+    and grouped slabs; two shards, ragged rows past a 256-row tile."""
+    banner(f"dense decoder {bits}-bit {cb} M={M}")
+    lay = wl.small_layer(f"dense_b{bits}_{cb}", 1024, (256, 384), bits, cb, (600,), seed=120 + bits)
+    t = wl.gen_all(lay)
+    y = None
+    for force in (dict(parts=1), dict(parts=2, mode=ex.EXL3_MODE_FUSED), dict(parts=3, mode=ex.EXL3_MODE_FUSED),
+                  dict(parts=4, mode=ex.EXL3_MODE_SLABS), dict(parts=8, groups=2, mode=ex.EXL3_MODE_SLABS)):
+        ref = _run(t, M=M, decoder=ex.EXL3_DECODER_ALU, **force)
+        y = _run(t, M=M, decoder=ex.EXL3_DECODER_DENSE, **force)
+        assert np.array_equal(y, ref), f"{force}"
+    if M <= 300:
+        _check(t, y, M=M)
+
+
 @pytest.mark.parametrize("decoder", [ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE])
 @pytest.mark.parametrize("parts", [1, 3, 8])
 def test_part_sums_stage(decoder, parts):
@@ -436,8 +458,9 @@ def test_full_size_sampled(name, M):
     # batch invariance at the real shape: the first row alone
     y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
     assert np.array_equal(y1[0], y[0])
-    if M <= 64:  # both decoders at the real shape
-        for dec in (ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE):
+    if M <= 64 or M >= 512:  # the other decoders at the real shape
+        for dec in (ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE) if M <= 64 else (ex.EXL3_DECODER_ALU,
+                                                                                ex.EXL3_DECODER_DENSE):
             assert np.array_equal(bits16(ex.linear(w, xr, torch.bfloat16, decoder=dec)), y), f"decoder {dec}"
     rows = sorted({0, M // 2, M - 1})
     nblk = lay.N // 128
