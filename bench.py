@@ -293,6 +293,42 @@ def main():
                     f"({per_shape[-1]['GBps']} GB/s, {per_shape[-1]['TFLOPS']} TFLOP/s, "
                     f"{per_shape[-1]['pct_sol']}% SoL)")
 
+    # ---- rulers measured in this run: a streaming read of 2 GiB, a pure fp16
+    # matrix-core loop, and per layer the decode path alone (the tile
+    # kernels' trellis staging and decode without products or stores), so
+    # the figures can be read against what this GPU delivers to simple
+    # kernels as well as against the data-sheet peaks.
+    with torch.cuda.stream(stream):
+        big = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        rw = torch.empty(ex.RULER_WORDS, dtype=torch.int32, device=dev)
+        t_rd = time_calls(lambda r: ex.debug_stream_read(big, out=rw), 5)
+        hbm_ruler = big.numel() / (t_rd * 1e-6)
+        del big
+        iters = 2000
+        rf = torch.empty(ex.RULER_WORDS, dtype=torch.float32, device=dev)
+        t_mf = time_calls(lambda r: ex.debug_mfma_loop(iters, out=rf), 5)
+        mfma_ruler = ex.mfma_loop_flops(iters) / (t_mf * 1e-6)
+        decode = {}
+        for li, (lay, ws, x, xr, y) in enumerate(per_layer):
+            ro = torch.empty((lay.K // 128, lay.N // 128), dtype=torch.int32, device=dev)
+            t_dr = time_calls(lambda r: ex.debug_decode_rate(ws[(r * 7 + 3) % copies], out=ro), args.timing_reps)
+            decode[lay.name] = {"us": round(t_dr, 3),
+                                "weights_per_s": float(f"{lay.K * lay.N / (t_dr * 1e-6):.4g}"),
+                                "trellis_GBps": round(lay.weight_bytes() / (t_dr * 1e-6) / 1e9, 1)}
+    rulers = {"hbm_read_GBps": round(hbm_ruler / 1e9, 1), "mfma_f16_TFLOPS": round(mfma_ruler / 1e12, 1),
+              "decode": decode, "spec": {"hbm_GBps": HBM_BPS / 1e9, "mfma_f16_TFLOPS": MFMA_F16_FLOPS / 1e12},
+              "how": "stream read: 2 GiB, 262144 threads, 16-byte loads; mfma: 4096 waves x 16 independent "
+                     "v_mfma_f32_16x16x32_f16 chains x 2000; decode: trellis staging + decode per 128x128 block, "
+                     "weight copies cycled"}
+    att_step = 0.0
+    for s_ in per_shape:
+        att = max(s_["K"] * s_["N"] * s_["bits"] / 8 / hbm_ruler, 2.0 * s_["M"] * s_["K"] * s_["N"] / mfma_ruler)
+        s_["pct_attainable"] = round(100.0 * att / (s_["linear_us"] * 1e-6), 2)
+        att_step += att
+    rulers["step_pct_of_attainable"] = round(100.0 * att_step / (ms_per_step / 1e3), 3)
+    log(f"rulers: stream read {rulers['hbm_read_GBps']} GB/s, mfma {rulers['mfma_f16_TFLOPS']} TFLOP/s, "
+        f"decode {decode}; step at {rulers['step_pct_of_attainable']}% of the rulers' bound")
+
     # ---- roofline of the dominant kernel: the GEMM template instance with
     # the most time per step.  A two-launch slab call is the GEMM plus the
     # ordered part sum + output transform kernel; each is timed alone (the
@@ -352,6 +388,8 @@ def main():
                                    "scale": ent.get("scale")}
         except Exception as e:  # a malformed file only loses the traffic field
             log(f"traffic file unreadable: {e}")
+    roof["ruler_peak"] = rulers["mfma_f16_TFLOPS"] if roof["unit"] == "TFLOP/s" else rulers["hbm_read_GBps"]
+    roof["ruler_frac"] = round(roof["achieved"] / roof["ruler_peak"], 4)
     log(f"roofline: {dom_key} over {roof['launches']}: {roof['achieved']} {roof['unit']} = "
         f"{100 * roof['frac']:.1f}% of peak, {roof['avg_launch_us']} us per launch")
 
@@ -373,6 +411,7 @@ def main():
             "M": list(Ms), "weight_copies": copies, "sol_ms_per_step": round(sol_step * 1e3, 5),
             "parallelism": "single GPU"},
         "roofline": roof,
+        "rulers": rulers,
         "per_shape": per_shape,
     }
     if not args.no_cpu_baseline:

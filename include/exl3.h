@@ -130,10 +130,11 @@ typedef struct exl3_plan {
                           table decoder reports 16, 32 or 64                */
   int32_t decoder;     /* exl3_decoder.  Automatic: TABLE for M <= 64 on
                           layers of at least 2^25 weights and at most
-                          2 GiB of trellis, else ALU.  In a
+                          2 GiB of trellis, DENSE for M >= 2048 on layers
+                          of at least 2^25 weights, else ALU.  In a
                           forced plan 0 means ALU; TABLE with M > 64 is
                           EXL3_ERR_UNSUPPORTED; forcing bm alone selects
-                          ALU                                               */
+                          ALU.  DENSE runs 256-row tiles                     */
   int32_t unit;        /* slab mode: parts per workgroup unit (one slab per
                           unit): P/G (one slab per group) automatically; 1
                           (one slab per part) may be forced.  Fused: P      */
@@ -145,7 +146,9 @@ typedef struct exl3_plan {
                           workgroups of a 128-column block are summed by the
                           output stage); may be forced                      */
   size_t workspace;    /* bytes of workspace this plan needs: 0, or
-                          EXL3_WORKSPACE_COUNTER_BYTES + the slabs          */
+                          EXL3_WORKSPACE_COUNTER_BYTES + the slabs, and
+                          for DENSE then (256-byte aligned) K*N fp16 of
+                          dequantized weights                               */
 } exl3_plan;
 
 /* ---------------------------------------------------------------- calls */
@@ -260,6 +263,37 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
  * groups does not divide n_parts. */
 exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t groups, int32_t M,
                                 const exl3_weight *w, void *y, int32_t y_dtype, void *stream);
+
+/* ------------------------------------------------- measurement rulers
+ * Not part of the layer API: simple kernels that measure, in the same run
+ * as the layer timings, what this GPU's HBM, matrix cores and decode path
+ * deliver, so the layer figures can be read against attainable rates as
+ * well as the data-sheet peaks (speed of light as max of weight bytes over
+ * HBM bandwidth and 2*M*K*N over fp16 matrix-core peak: EXL3 survey of the
+ * pages, "Measurement").  Each writes EXL3_RULER_WORDS words (or one word
+ * per weight block) to a caller-owned device buffer and is asynchronous on
+ * `stream`. */
+#define EXL3_RULER_WORDS 262144
+
+/* Streaming read of buf[0 .. bytes): EXL3_RULER_WORDS threads each XOR the
+ * 4-byte words of their grid-stride share of the 16-byte words into
+ * out[t], so the XOR of all out words is the XOR of the whole buffer.
+ * EXL3_ERR_INVALID_ARG unless bytes is a positive multiple of 16 and buf and
+ * out are 16-byte aligned. */
+exl3_status exl3_debug_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
+
+/* Matrix-core loop: EXL3_RULER_WORDS / 64 waves each run `iters` rounds of
+ * 16 independent v_mfma_f32_16x16x32_f16 chains with every A and B element
+ * the fp16 value `one` (bits); out[t] (float) = the sum of the lane's 16
+ * chains' first elements = 512 * iters * one^2 while exact.  Work:
+ * 16384 * 16 * iters * EXL3_RULER_WORDS / 64 flops.  iters in 1 .. 2^20. */
+exl3_status exl3_debug_mfma_loop(int32_t iters, uint16_t one, float *out, void *stream);
+
+/* Decode ruler: every weight of `w` staged and decoded as the GEMM kernels
+ * do, with no matrix products and no weight stores.  out[kb * (N/128) + nb]
+ * (uint32, (K/128) * (N/128) words) = XOR of block (kb, nb)'s decoded fp16
+ * values at even k in the low 16 bits and at odd k in the high 16 bits. */
+exl3_status exl3_debug_decode_rate(const exl3_weight *w, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

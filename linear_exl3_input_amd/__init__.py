@@ -28,6 +28,7 @@ import torch
 __all__ = [
     "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
     "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue", "debug_parts",
+    "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +102,9 @@ def load() -> ctypes.CDLL:
             "exl3_debug_decode": (i32, [W, vp, vp]),
             "exl3_debug_epilogue": (i32, [vp, i32, i32, i32, W, vp, i32, vp]),
             "exl3_debug_parts": (i32, [W, vp, i32, vp, sz, vp, P]),
+            "exl3_debug_stream_read": (i32, [vp, sz, vp, vp]),
+            "exl3_debug_mfma_loop": (i32, [i32, ctypes.c_uint16, vp, vp]),
+            "exl3_debug_decode_rate": (i32, [W, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -329,4 +333,43 @@ def debug_epilogue(w: Exl3Weight, z_parts: torch.Tensor, M: int, out_dtype=torch
     _check(load().exl3_debug_epilogue(_dev_ptr(z_parts, "z_parts", (torch.float32,)), P, groups or P, M,
                                       ctypes.byref(w.view()),
                                       out.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _F16, _stream()))
+    return out
+
+
+# ---------------------------------------------------------------- rulers
+RULER_WORDS = 262144
+
+
+def debug_stream_read(buf: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Streaming read of a whole device buffer (measurement ruler): returns
+    RULER_WORDS int32 whose XOR is the XOR of the buffer's 4-byte words."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(RULER_WORDS, dtype=torch.int32, device=buf.device)
+    _check(load().exl3_debug_stream_read(buf.data_ptr(), nbytes, _dev_ptr(out, "out", (torch.int32,)), _stream()))
+    return out
+
+
+def debug_mfma_loop(iters: int, one: int = 0x3C00, device="cuda", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Matrix-core ruler: RULER_WORDS/64 waves x iters x 16 fp16 MFMAs of
+    16x16x32 with all operands `one` (fp16 bits); returns the lanes' sums."""
+    if out is None:
+        out = torch.empty(RULER_WORDS, dtype=torch.float32, device=device)
+    _check(load().exl3_debug_mfma_loop(iters, one, _dev_ptr(out, "out", (torch.float32,)), _stream()))
+    return out
+
+
+def mfma_loop_flops(iters: int) -> float:
+    return 16384.0 * 16 * iters * (RULER_WORDS // 64)
+
+
+def debug_decode_rate(w: Exl3Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode ruler: stage and decode every weight as the GEMM kernels do, no
+    products; returns [K/128, N/128] int32 block XORs (low half: even k, high
+    half: odd k of the fp16 W_q values)."""
+    if out is None:
+        out = torch.empty((w.K // 128, w.N // 128), dtype=torch.int32, device=w.trellis.device)
+    _check(load().exl3_debug_decode_rate(ctypes.byref(w.view()), _dev_ptr(out, "out", (torch.int32,)), _stream()))
     return out

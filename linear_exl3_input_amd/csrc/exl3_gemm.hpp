@@ -1077,6 +1077,51 @@ __global__ __launch_bounds__(WG_THREADS) void dequant_kernel(const DecodeParams 
   }
 }
 
+// Decode-rate ruler: the same trellis staging and decode as the tile kernels
+// for one 128 x 128 block per workgroup, with no matrix-core work and no
+// weight stores: the 4-byte words of every decoded fragment are XOR-reduced
+// into one word per block, out[kb * nblk + nb].  The low half of that word
+// is the XOR of the block's fp16 values at even k, the high half at odd k
+// (a fragment's words pair k offsets 0-1, 2-3, 8-9, 10-11).  Its time is the
+// fastest any decoding kernel can stream the trellis (decode-VALU roof).
+template <int BITS, uint32_t CB>
+__global__ __launch_bounds__(WG_THREADS) void decode_rate_kernel(const DecodeParams p) {
+  using G = Geom<BITS>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[G::STAGE_T_DW];
+  __shared__ uint32_t red[WG_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int nb = blockIdx.x, kb = blockIdx.y;
+  const int nblk = p.N >> 7;
+  u32x4_t treg[G::T_ITERS];
+  load_trellis_stage<BITS>(treg, p.trellis, kb, nb, p.N >> 4, tid);
+  store_trellis_stage<BITS>(treg, lds, tid);
+  __syncthreads();
+  const int tile_lane = (g >> 1) * WG_NT + 2 * wave + (j >> 3);
+  uint32_t x = 0;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t *tp = lds + (tile_lane + 2 * WG_NT * ks) * G::STRIDE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int xoff, sh;
+      lane_window<BITS>(j, g, h, xoff, sh);
+      const u32x4_t b = __builtin_bit_cast(u32x4_t, decode_frag<BITS, CB>(tp, xoff, sh));
+      x ^= b[0] ^ b[1] ^ b[2] ^ b[3];
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x ^= (uint32_t)__shfl_xor((int)x, d, 64);
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < WG_THREADS / 64; ++w) t ^= red[w];
+    reinterpret_cast<uint32_t *>(p.wq)[kb * nblk + nb] = t;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 // quads > 1: one part per quad (no register fold); otherwise `multi` folds
@@ -1157,6 +1202,18 @@ hipError_t launch_dequant_bits(int cb, const DecodeParams &p, hipStream_t s) {
 }
 
 template <int BITS>
+hipError_t launch_decode_rate_bits(int cb, const DecodeParams &p, hipStream_t s) {
+  const dim3 grid(p.N / 128, p.K / 128);
+  switch (cb) {
+    case 0: hipLaunchKernelGGL((decode_rate_kernel<BITS, CB_3INST>), grid, dim3(WG_THREADS), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_rate_kernel<BITS, CB_MCG>), grid, dim3(WG_THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_rate_kernel<BITS, CB_MUL1>), grid, dim3(WG_THREADS), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
 hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
   const dim3 grid(p.N / 128, p.K / 128);
   switch (cb) {
@@ -1184,5 +1241,8 @@ hipError_t launch_decode_bits(int cb, const DecodeParams &p, hipStream_t s) {
   }                                                                                                \
   hipError_t launch_dequant_b##B(int cb, const DecodeParams &p, hipStream_t s) {                   \
     return launch_dequant_bits<B>(cb, p, s);                                                       \
+  }                                                                                                \
+  hipError_t launch_decode_rate_b##B(int cb, const DecodeParams &p, hipStream_t s) {               \
+    return launch_decode_rate_bits<B>(cb, p, s);                                                   \
   }                                                                                                \
   }

@@ -590,6 +590,40 @@ exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream) 
   return e == hipSuccess ? EXL3_OK : launch_error(e, "decode launch");
 }
 
+exl3_status exl3_debug_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  clear_error();
+  exl3_status st;
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "bytes=%zu, must be a positive multiple of 16", bytes);
+  if ((st = check_ptr(buf, "buf")) != EXL3_OK) return st;
+  if ((st = check_ptr(out, "out")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_stream_read(buf, bytes, out, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "stream-read launch");
+}
+
+exl3_status exl3_debug_mfma_loop(int32_t iters, uint16_t one, float *out, void *stream) {
+  clear_error();
+  exl3_status st;
+  if (iters < 1 || iters > (1 << 20)) return fail(EXL3_ERR_INVALID_ARG, "iters=%d, must be 1..%d", iters, 1 << 20);
+  if ((st = check_ptr(out, "out")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_mfma_loop(iters, one, out, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "mfma-loop launch");
+}
+
+exl3_status exl3_debug_decode_rate(const exl3_weight *w, uint32_t *out, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  if ((st = check_ptr(out, "out")) != EXL3_OK) return st;
+  exl3::DecodeParams p;
+  p.trellis = w->trellis;
+  p.wq = reinterpret_cast<uint16_t *>(out);
+  p.K = w->K;
+  p.N = w->N;
+  const hipError_t e = exl3::launch_decode_rate(w->bits, w->codebook, p, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "decode-rate launch");
+}
+
 exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t groups, int32_t M,
                                 const exl3_weight *w, void *y, int32_t y_dtype, void *stream) {
   clear_error();

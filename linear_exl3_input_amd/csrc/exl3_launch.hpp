@@ -64,12 +64,25 @@ hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, 
                            int32_t N, const uint16_t *svh, void *y, bool out_bf16, hipStream_t s);
 hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
 
+// Measurement rulers.  decode_rate: the tile kernels' trellis staging and
+// decode alone, one XOR word per 128 x 128 block into p.wq (as uint32_t).
+// stream_read: XOR of every 16-byte word of `bytes` (a multiple of 16) into
+// RULER_THREADS words.  mfma_loop: `iters` rounds of 16 independent
+// v_mfma_f32_16x16x32_f16 chains per wave on RULER_THREADS / 64 waves, with
+// every A and B element equal to `one`; lane word = the sum of its 16
+// chains' first elements.
+constexpr int RULER_THREADS = 1 << 18;
+hipError_t launch_decode_rate(int bits, int cb, const DecodeParams &p, hipStream_t s);
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
+hipError_t launch_mfma_loop(int32_t iters, uint16_t one, float *out, hipStream_t s);
+
 // Per-bit-width entry points, defined in gemm_b<bits>.hip.
 #define EXL3_DECLARE_BITS(B)                                                                  \
   hipError_t launch_gemm_b##B(int cb, int bm, int quads, bool half, bool multi_part,              \
                               const GemmParams &p, dim3 grid, hipStream_t s);                   \
   hipError_t launch_debug_decode_b##B(int cb, const DecodeParams &p, hipStream_t s);            \
   hipError_t launch_dequant_b##B(int cb, const DecodeParams &p, hipStream_t s);                 \
+  hipError_t launch_decode_rate_b##B(int cb, const DecodeParams &p, hipStream_t s);             \
   hipError_t launch_table_b##B(int cb, const GemmParams &p, int grid, hipStream_t s);
 EXL3_DECLARE_BITS(1)
 EXL3_DECLARE_BITS(2)

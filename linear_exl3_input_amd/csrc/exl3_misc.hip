@@ -257,6 +257,20 @@ hipError_t launch_dequant(int bits, int cb, const DecodeParams &p, hipStream_t s
   }
 }
 
+hipError_t launch_decode_rate(int bits, int cb, const DecodeParams &p, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_decode_rate_b1(cb, p, s);
+    case 2: return launch_decode_rate_b2(cb, p, s);
+    case 3: return launch_decode_rate_b3(cb, p, s);
+    case 4: return launch_decode_rate_b4(cb, p, s);
+    case 5: return launch_decode_rate_b5(cb, p, s);
+    case 6: return launch_decode_rate_b6(cb, p, s);
+    case 7: return launch_decode_rate_b7(cb, p, s);
+    case 8: return launch_decode_rate_b8(cb, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStream_t s) {
   switch (bits) {
     case 1: return launch_debug_decode_b1(cb, p, s);

@@ -267,3 +267,15 @@ def test_dense_decoder_plan_and_limits():
         ((CB + slab_b + 255) // 256) * 256 + 1024 * 384 * 2
     assert L.exl3_debug_parts(ctypes.byref(w), FAKE, 17, FAKE, 1 << 30, None, ctypes.byref(slabs)) == 2
     assert "decoder=dense" in last_error()
+
+
+def test_ruler_hooks_check_arguments():
+    L = ex.load()
+    assert L.exl3_debug_stream_read(FAKE, 24, FAKE, None) == 1  # not a multiple of 16
+    assert "bytes=24" in last_error()
+    assert L.exl3_debug_stream_read(FAKE + 8, 32, FAKE, None) == 1
+    assert "not 16-byte aligned" in last_error()
+    assert L.exl3_debug_mfma_loop(0, 0x3C00, FAKE, None) == 1
+    assert "iters=0" in last_error()
+    assert L.exl3_debug_decode_rate(ctypes.byref(view(1024, (256,), 4, 1)), None, None) == 1
+    assert "out is NULL" in last_error()

@@ -439,6 +439,44 @@ def test_zero_rows_is_a_noop():
     assert y.shape == (0, 128)
 
 
+# ------------------------------------------------ measurement rulers
+
+def test_stream_read_ruler_xor():
+    """The streaming-read ruler reads every word once: the XOR of its output
+    words is the XOR of the buffer (a ragged size: not a multiple of the
+    grid's 4-load stride)."""
+    rng = np.random.default_rng(301)
+    host = rng.integers(0, 2**32, (1 << 20) + 12, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    out = ex.debug_stream_read(buf)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(host)
+
+
+def test_mfma_loop_ruler_closed_form():
+    """All-ones operands: every lane's 16 chains hold 32 * iters each."""
+    out = ex.debug_mfma_loop(100)
+    torch.cuda.synchronize()
+    assert torch.all(out == 16 * 32 * 100)
+    half = ex.debug_mfma_loop(3, one=0x3800)  # 0.5: 16 * 32 * 3 * 0.25
+    assert torch.all(half == 16 * 32 * 3 * 0.25)
+
+
+@pytest.mark.parametrize("bits,cb", [(1, "3inst"), (4, "mcg"), (6, "mul1"), (8, "3inst")])
+def test_decode_rate_ruler_block_xor(bits, cb):
+    """The decode ruler decodes every weight of every block: its block words
+    are the XORs of the oracle's fp16 W_q bits at even (low half) and odd
+    (high half) k of each 128 x 128 block."""
+    lay = wl.small_layer(f"ruler_b{bits}_{cb}", 384, (256, 128), bits, cb, (1,), seed=310 + bits)
+    t = wl.gen_all(lay)
+    got = ex.debug_decode_rate(weight(t)).cpu().numpy().view(np.uint32)
+    wq = ofmt.dequantize_bits(t.trellis, bits, lay.cb).astype(np.uint32)  # [K, N] fp16 bits
+    blk = wq.reshape(lay.K // 128, 128, lay.N // 128, 128)
+    lo = np.bitwise_xor.reduce(np.bitwise_xor.reduce(blk[:, 0::2], axis=1), axis=2)
+    hi = np.bitwise_xor.reduce(np.bitwise_xor.reduce(blk[:, 1::2], axis=1), axis=2)
+    assert np.array_equal(got, lo | (hi << 16))
+
+
 # --------------------------------------------- full-size workloads, sampled
 
 FULL = [("small_1024x1024_b4_3inst", 16), ("expert_4096x2048_b4_mcg", 512), ("expert_2048x4096_b4_mcg", 16),
