@@ -268,13 +268,22 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps  # microseconds per call
 
+    def time_batches(fn, reps, batches=5):
+        """The pages' protocol: batches of `reps` calls after the warm-up, each
+        timed by one event pair; returns (median, min) of the per-call means."""
+        ts = sorted(time_calls(fn, reps) for _ in range(batches))
+        return ts[len(ts) // 2], ts[0]
+
     per_shape = []
     with torch.cuda.stream(stream):
         for li, (lay, ws, x, xr, y) in enumerate(per_layer):
             for M in Ms:
                 pick = lambda r: ws[(r * 7 + 3) % copies]
                 t_in = time_calls(lambda r: ex.input_transform(x[:M], pick(r).suh, out=xr[M]), args.timing_reps)
-                t_lin = time_calls(lambda r: ex.linear(pick(r), xr[M], torch.bfloat16, out=y[M]), args.timing_reps)
+                t_lin, t_lin_min = time_batches(lambda r: ex.linear(pick(r), xr[M], torch.bfloat16, out=y[M]),
+                                                args.timing_reps)
+                # warm: the same weight copy every call (L2/MALL-resident when it fits)
+                t_warm = time_calls(lambda r: ex.linear(ws[0], xr[M], torch.bfloat16, out=y[M]), args.timing_reps)
                 pl = ex.plan(ws[0], M)
                 byts = lay.weight_bytes()
                 flops = 2.0 * M * lay.K * lay.N
@@ -282,6 +291,7 @@ def main():
                 per_shape.append({
                     "layer": lay.name, "M": M, "K": lay.K, "N": lay.N, "bits": lay.bits, "codebook": lay.codebook,
                     "plan": pl, "transform_us": round(t_in, 3), "linear_us": round(t_lin, 3),
+                    "linear_us_min": round(t_lin_min, 3), "linear_us_warm": round(t_warm, 3),
                     "kernels_per_linear": pl["launches"],
                     "GBps": round(byts / (t_lin * 1e-6) / 1e9, 1),
                     "TFLOPS": round(flops / (t_lin * 1e-6) / 1e12, 2),
