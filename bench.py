@@ -145,6 +145,9 @@ def main():
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--only", default=None, metavar="LAYER:M",
                     help="counter runs: launch only this call class (transform + linear), --steps times")
+    ap.add_argument("--tune", action="store_true",
+                    help="time every schedule of each call's part tree on the weight pool first (same bits) and "
+                         "run the fastest")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="counter runs: copy MB of device memory --steps times (a kernel of known bytes)")
     args = ap.parse_args()
@@ -198,6 +201,14 @@ def main():
         xr = {M: torch.empty(ex.rot_shape(lay.n_shards, M, lay.K), dtype=torch.float16, device=dev) for M in Ms}
         y = {M: torch.empty((M, lay.N), dtype=torch.bfloat16, device=dev) for M in Ms}
         per_layer.append((lay, ws, x, xr, y))
+    tuned = {}
+    if args.tune:
+        ex.tune_clear()
+        for lay, ws, x, xr, y in per_layer:
+            for M in Ms:
+                ex.input_transform(x[:M], ws[0].suh, out=xr[M])
+                tuned[f"{lay.name} M={M}"] = ex.tune(ws, xr[M], reps=max(3, min(20, copies)))
+                log(f"tuned {lay.name} M={M}: {tuned[f'{lay.name} M={M}']}")
     # workspace for the largest need, allocated before capture
     need = max(ex.workspace_bytes(ws[0], M) for (lay, ws, x, xr, y) in per_layer for M in Ms)
     if need:
@@ -419,6 +430,7 @@ def main():
         "config": {"workload": args.workload, "layers": [
             {"K": l.K, "N": l.N, "shards": list(l.shards), "bits": l.bits, "codebook": l.codebook} for l in layers],
             "M": list(Ms), "weight_copies": copies, "sol_ms_per_step": round(sol_step * 1e3, 5),
+            "schedules": "tuned on the weight pool (same bits)" if args.tune else "planner",
             "parallelism": "single GPU"},
         "roofline": roof,
         "rulers": rulers,

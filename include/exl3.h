@@ -129,8 +129,9 @@ typedef struct exl3_plan {
                           or slab mode), else EXL3_ERR_UNSUPPORTED.  The
                           table decoder reports 16, 32 or 64                */
   int32_t decoder;     /* exl3_decoder.  Automatic: TABLE for M <= 64 on
-                          layers of at least 2^25 weights and at most
-                          2 GiB of trellis, DENSE for M >= 2048 on layers
+                          layers of at least 2^25 weights (2^26 when
+                          M <= 16) and at most 2 GiB of trellis, DENSE
+                          for M >= 2048 on layers
                           of at least 2^25 weights, else ALU.  In a
                           forced plan 0 means ALU; TABLE with M > 64 is
                           EXL3_ERR_UNSUPPORTED; forcing bm alone selects
@@ -220,6 +221,45 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
 
 /* Workspace bytes for exl3_linear_ex with the same `force`. */
 size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan *force);
+
+/* ------------------------------------------------ schedule autotuner
+ * (cuda-exl3 README, "Where the time goes": the best tile tier depends on
+ * the shape, not only the batch, so the tiers are timed once per distinct
+ * shape and the winner cached; tuning is skipped under graph capture, where
+ * the planner's cost model is the fallback.)  Every candidate is a schedule
+ * of the shape's own part tree (decoder, rows per tile, mode, unit,
+ * workgroup width), so tuning never changes an output bit.  The table is
+ * process-wide, keyed by (K, N, bits, codebook, shard widths, M bucket =
+ * the next power of two >= M); exl3_linear, exl3_workspace_bytes and
+ * exl3_plan_query use a tuned schedule when no plan is forced and it is
+ * valid at their M, else the planner's.  Tune before sizing workspaces: a
+ * tuned schedule may need more workspace than the planner's.
+ *
+ * exl3_tune runs every candidate that fits `workspace` once untimed and
+ * `reps` times between two events on `stream` (it synchronizes the
+ * stream), writing y each time, and records the fastest (the planner's
+ * unless beaten by more than 2%); *best (HOST, may be NULL) receives it.
+ * `ws` (HOST) holds n_w views of the same shape, e.g. copies of one weight
+ * whose trellises together exceed the caches: the timed calls cycle
+ * through them, so the timing sees weights streamed from HBM as a model's
+ * layers are (one view times a warm, cache-resident weight).
+ * EXL3_ERR_INVALID_ARG if a view differs in shape; EXL3_ERR_UNSUPPORTED
+ * while the stream is being captured; EXL3_ERR_WORKSPACE if no candidate
+ * fits. */
+exl3_status exl3_tune(const exl3_weight *ws, int32_t n_w, const uint16_t *x_rot, int32_t M, void *y,
+                      int32_t y_dtype, void *workspace, size_t workspace_bytes, int32_t reps, void *stream,
+                      exl3_plan *best);
+
+/* Workspace that fits every candidate exl3_tune tries for M rows. */
+size_t exl3_tune_workspace_bytes(const exl3_weight *w, int32_t M);
+
+/* Record a schedule for (shape, M bucket) as exl3_tune would (e.g. one
+ * tuned earlier and saved): validated like a forced plan; its parts and
+ * groups must be the shape's own (EXL3_ERR_INVALID_ARG otherwise). */
+exl3_status exl3_tune_set(const exl3_weight *w, int32_t M, const exl3_plan *plan);
+
+/* Forget every tuned schedule. */
+void exl3_tune_clear(void);
 
 /* Human-readable status name, and the thread's last error message. */
 const char *exl3_status_str(exl3_status s);

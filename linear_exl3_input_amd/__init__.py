@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
     "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue", "debug_parts",
-    "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops",
+    "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops", "tune", "tune_clear",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +105,10 @@ def load() -> ctypes.CDLL:
             "exl3_debug_stream_read": (i32, [vp, sz, vp, vp]),
             "exl3_debug_mfma_loop": (i32, [i32, ctypes.c_uint16, vp, vp]),
             "exl3_debug_decode_rate": (i32, [W, vp, vp]),
+            "exl3_tune": (i32, [W, i32, vp, i32, vp, i32, vp, sz, i32, vp, P]),
+            "exl3_tune_workspace_bytes": (sz, [W, i32]),
+            "exl3_tune_set": (i32, [W, i32, P]),
+            "exl3_tune_clear": (None, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -373,3 +377,40 @@ def debug_decode_rate(w: Exl3Weight, out: Optional[torch.Tensor] = None) -> torc
         out = torch.empty((w.K // 128, w.N // 128), dtype=torch.int32, device=w.trellis.device)
     _check(load().exl3_debug_decode_rate(ctypes.byref(w.view()), _dev_ptr(out, "out", (torch.int32,)), _stream()))
     return out
+
+
+# ----------------------------------------------------------- autotuner
+def _plan_dict(p: _Plan) -> dict:
+    return {"parts": p.parts, "groups": p.groups, "mode": p.mode, "bm": p.bm, "decoder": p.decoder,
+            "unit": p.unit, "launches": p.launches, "wg_cols": p.wg_cols, "workspace": p.workspace}
+
+
+def tune(w, x_rot: torch.Tensor, reps: int = 5) -> dict:
+    """Time every schedule of the shape's part tree on these rows (eager, not
+    under graph capture) and record the fastest for the shape and M bucket;
+    later unforced calls use it.  `w` is one Exl3Weight or a list of copies
+    of one shape, cycled by the timed calls (copies that exceed the caches
+    time cold weights).  Returns the chosen plan."""
+    copies = list(w) if isinstance(w, (list, tuple)) else [w]
+    arr = (_Weight * len(copies))(*[c.view() for c in copies])
+    S, KC, M, _ = x_rot.shape
+    L = load()
+    need = L.exl3_tune_workspace_bytes(ctypes.byref(copies[0].view()), M)
+    if need == 0 and L.exl3_last_error():
+        _check(1)
+    ws, wsn = _workspace(need, x_rot.device)
+    y = torch.empty((M, copies[0].N), dtype=torch.bfloat16, device=x_rot.device)
+    best = _Plan()
+    _check(L.exl3_tune(arr, len(copies), _dev_ptr(x_rot, "x_rot", _H16), M, y.data_ptr(), _BF16, ws, wsn,
+                       reps, _stream(), ctypes.byref(best)))
+    return _plan_dict(best)
+
+
+def tune_set(w: Exl3Weight, M: int, plan: dict) -> None:
+    f = _Plan(plan["parts"], plan["groups"], plan["mode"], plan["bm"], plan["decoder"], plan["unit"], 0,
+              plan["wg_cols"], 0)
+    _check(load().exl3_tune_set(ctypes.byref(w.view()), M, ctypes.byref(f)))
+
+
+def tune_clear() -> None:
+    load().exl3_tune_clear()

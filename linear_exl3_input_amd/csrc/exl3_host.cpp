@@ -9,6 +9,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
 
 #include "../../include/exl3.h"
 #include "exl3_launch.hpp"
@@ -153,8 +156,12 @@ struct Plan {
 };
 
 // The table decoder pays a fixed cost per CU (filling a 65,536-entry table)
-// that the layer's weights have to amortize.
-constexpr double TABLE_MIN_WEIGHTS = 33554432.0;  // 2^25
+// that the layer's weights have to amortize.  Up to 16 rows the ALU tiles
+// with the finishing workgroup (one launch) beat it below 2^26 weights
+// (measured by the schedule tuner on q_proj 5120 x 12288: 22.9 -> 20.3 us at
+// one row, 24.1 -> 22.9 at 16), above 16 rows from 2^25.
+constexpr double TABLE_MIN_WEIGHTS = 33554432.0;         // 2^25
+constexpr double TABLE_MIN_WEIGHTS_SMALL_M = 67108864.0;  // 2^26, M <= 16
 constexpr int32_t TABLE_MAX_M = 64;
 // The table kernel addresses the trellis with 32-bit byte offsets.
 constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
@@ -204,7 +211,8 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   const bool bm_forced = force && force->bm > 0;
   const double weights = (double)w->K * (double)w->N;
   const bool table_fits = weights * w->bits / 8.0 <= TABLE_MAX_TRELLIS_BYTES;
-  pl.decoder = (M <= TABLE_MAX_M && weights >= TABLE_MIN_WEIGHTS && table_fits) ? EXL3_DECODER_TABLE
+  pl.decoder = (M <= TABLE_MAX_M && weights >= (M <= 16 ? TABLE_MIN_WEIGHTS_SMALL_M : TABLE_MIN_WEIGHTS) &&
+                table_fits) ? EXL3_DECODER_TABLE
                 : (M >= DENSE_MIN_M && weights >= DENSE_MIN_WEIGHTS) ? EXL3_DECODER_DENSE
                                                                     : EXL3_DECODER_ALU;
   if (bm_forced) pl.decoder = EXL3_DECODER_ALU;
@@ -328,6 +336,124 @@ exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ------------------------------------------------------- tuned schedules
+//
+// The schedule autotuner (cuda-exl3 README, "Where the time goes": the best
+// tile tier depends on the shape, so the kernel times the tiers once per
+// shape and caches the winner, skipped under graph capture, with the cost
+// model as the fallback).  Every candidate here is a schedule of the same
+// shape-fixed part tree, so no choice changes a result bit.  Key: the shape
+// and the M bucket (the next power of two >= M).
+
+struct TuneKey {
+  int32_t K, N, bits, codebook, n_shards, mb;
+  int32_t shard_n[EXL3_MAX_SHARDS];
+  bool operator<(const TuneKey &o) const { return std::memcmp(this, &o, sizeof(TuneKey)) < 0; }
+};
+
+std::mutex g_tune_mu;
+std::map<TuneKey, exl3_plan> g_tuned;
+
+int32_t m_bucket(int32_t M) {
+  int32_t b = 1;
+  while (b < M && b < (1 << 30)) b <<= 1;
+  return b;
+}
+
+TuneKey tune_key(const exl3_weight *w, int32_t M) {
+  TuneKey k;
+  std::memset(&k, 0, sizeof k);
+  k.K = w->K;
+  k.N = w->N;
+  k.bits = w->bits;
+  k.codebook = w->codebook;
+  k.n_shards = w->n_shards;
+  k.mb = m_bucket(M);
+  for (int s = 0; s < w->n_shards && s < EXL3_MAX_SHARDS; ++s) k.shard_n[s] = w->shard_n[s];
+  return k;
+}
+
+// The plan a call runs: the forced one; else the tuned one for the shape and
+// M bucket if it is valid at this M; else the planner's.
+exl3_status plan_for(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out) {
+  if (force) return make_plan(w, M, force, out);
+  exl3_plan tuned;
+  bool have = false;
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto it = g_tuned.find(tune_key(w, M));
+    if (it != g_tuned.end()) {
+      tuned = it->second;
+      have = true;
+    }
+  }
+  if (have && make_plan(w, M, &tuned, out) == EXL3_OK) return EXL3_OK;
+  return make_plan(w, M, nullptr, out);
+}
+
+bool same_schedule(const Plan &a, const Plan &b) {
+  return a.parts == b.parts && a.groups == b.groups && a.mode == b.mode && a.bm == b.bm && a.decoder == b.decoder &&
+         a.unit == b.unit && a.quads == b.quads && a.half == b.half && a.multi == b.multi &&
+         a.finisher == b.finisher && a.chunk == b.chunk;
+}
+
+exl3_plan as_force(const Plan &pl) {
+  exl3_plan f;
+  f.parts = pl.parts;
+  f.groups = pl.groups;
+  f.mode = pl.mode;
+  f.bm = pl.bm;
+  f.decoder = pl.decoder;
+  f.unit = pl.unit;
+  f.launches = 0;
+  f.wg_cols = pl.half ? 64 : 128;
+  f.workspace = 0;
+  return f;
+}
+
+// Candidate schedules for M rows: the planner's, then every valid mix of
+// decoder, rows per tile (the planner's tier, one and two below, one above),
+// mode, unit and workgroup width, without repeats.
+std::vector<Plan> tune_candidates(const exl3_weight *w, int32_t M) {
+  std::vector<Plan> out;
+  Plan base;
+  if (make_plan(w, M, nullptr, &base) != EXL3_OK) return out;
+  out.push_back(base);
+  auto add = [&](const exl3_plan &f) {
+    Plan pl;
+    if (make_plan(w, M, &f, &pl) != EXL3_OK) return;
+    for (const Plan &q : out)
+      if (same_schedule(q, pl)) return;
+    out.push_back(pl);
+  };
+  std::vector<int32_t> bms;
+  for (int32_t b : {base.bm / 4, base.bm / 2, base.bm, base.bm * 2})
+    if (b >= 16 && b <= 512) bms.push_back(b);
+  const int32_t decoders[] = {EXL3_DECODER_ALU, EXL3_DECODER_TABLE, EXL3_DECODER_DENSE};
+  for (int32_t dec : decoders) {
+    if (dec == EXL3_DECODER_DENSE && M < 256) continue;
+    for (int32_t bm : bms) {
+      if (dec != EXL3_DECODER_ALU && bm != bms[0]) continue;  // those decoders fix their own tile
+      for (int32_t mode : {EXL3_MODE_AUTO, EXL3_MODE_FUSED, EXL3_MODE_SLABS})
+        for (int32_t unit : {-1, 1})
+          for (int32_t cols : {-1, 64}) {
+            exl3_plan f;
+            f.parts = base.parts;
+            f.groups = base.groups;
+            f.mode = mode;
+            f.bm = dec == EXL3_DECODER_ALU ? bm : -1;
+            f.decoder = dec;
+            f.unit = unit;
+            f.launches = 0;
+            f.wg_cols = cols;
+            f.workspace = 0;
+            add(f);
+          }
+    }
+  }
+  return out;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,7 +503,7 @@ size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan 
     return 0;
   }
   Plan pl;
-  if (make_plan(w, M, force, &pl) != EXL3_OK) return 0;
+  if (plan_for(w, M, force, &pl) != EXL3_OK) return 0;
   return pl.workspace;
 }
 
@@ -390,7 +516,7 @@ exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan) {
   if (plan == nullptr) return fail(EXL3_ERR_INVALID_ARG, "plan (host output) is NULL");
   if (M < 0 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
   Plan pl;
-  if ((st = make_plan(w, M, nullptr, &pl)) != EXL3_OK) return st;
+  if ((st = plan_for(w, M, nullptr, &pl)) != EXL3_OK) return st;
   plan->parts = pl.parts;
   plan->groups = pl.groups;
   plan->mode = pl.mode;
@@ -413,7 +539,7 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
   if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
   if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
   Plan pl;
-  if ((st = make_plan(w, M, force, &pl)) != EXL3_OK) return st;
+  if ((st = plan_for(w, M, force, &pl)) != EXL3_OK) return st;
   if (M == 0) return EXL3_OK;
   if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
   if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
@@ -515,6 +641,140 @@ extern "C" {
 exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                         void *workspace, size_t workspace_bytes, void *stream) {
   return exl3_linear_ex(w, x_rot, M, y, y_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t exl3_tune_workspace_bytes(const exl3_weight *w, int32_t M) {
+  clear_error();
+  if (validate_weight(w, false, false) != EXL3_OK) return 0;
+  if (M < 1 || M > MAX_M) {
+    fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 1..%d", M, MAX_M);
+    return 0;
+  }
+  size_t need = 0;
+  for (const Plan &pl : tune_candidates(w, M)) need = std::max(need, pl.workspace);
+  clear_error();  // candidates the planner refuses are skipped, not errors
+  return need;
+}
+
+exl3_status exl3_tune_set(const exl3_weight *w, int32_t M, const exl3_plan *plan) {
+  clear_error();
+  exl3_status st = validate_weight(w, false, false);
+  if (st != EXL3_OK) return st;
+  if (plan == nullptr) return fail(EXL3_ERR_INVALID_ARG, "plan is NULL");
+  if (M < 1 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 1..%d", M, MAX_M);
+  Plan pl, base;
+  if ((st = make_plan(w, M, plan, &pl)) != EXL3_OK) return st;
+  if ((st = make_plan(w, M, nullptr, &base)) != EXL3_OK) return st;
+  if (pl.parts != base.parts || pl.groups != base.groups)
+    return fail(EXL3_ERR_INVALID_ARG, "a tuned schedule keeps the shape's tree: parts=%d groups=%d, the shape has %d/%d",
+                pl.parts, pl.groups, base.parts, base.groups);
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tuned[tune_key(w, M)] = as_force(pl);
+  return EXL3_OK;
+}
+
+void exl3_tune_clear(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tuned.clear();
+}
+
+exl3_status exl3_tune(const exl3_weight *ws, int32_t n_w, const uint16_t *x_rot, int32_t M, void *y,
+                      int32_t y_dtype, void *workspace, size_t workspace_bytes, int32_t reps, void *stream,
+                      exl3_plan *best) {
+  clear_error();
+  if (ws == nullptr) return fail(EXL3_ERR_INVALID_ARG, "weight views are NULL");
+  if (n_w < 1 || n_w > 65536) return fail(EXL3_ERR_INVALID_ARG, "n_w=%d, must be 1..65536", n_w);
+  const exl3_weight *w = ws;
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  for (int32_t c = 1; c < n_w; ++c) {
+    if ((st = validate_weight(&ws[c], true, false)) != EXL3_OK) return st;
+    bool same = ws[c].K == w->K && ws[c].N == w->N && ws[c].bits == w->bits && ws[c].codebook == w->codebook &&
+                ws[c].n_shards == w->n_shards;
+    for (int s = 0; same && s < w->n_shards; ++s) same = ws[c].shard_n[s] == w->shard_n[s];
+    if (!same) return fail(EXL3_ERR_INVALID_ARG, "weight copy %d has another shape than copy 0", c);
+  }
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (M < 1 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 1..%d", M, MAX_M);
+  if (reps < 1 || reps > 1000) return fail(EXL3_ERR_INVALID_ARG, "reps=%d, must be 1..1000", reps);
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  if (workspace != nullptr && !aligned16(workspace))
+    return fail(EXL3_ERR_INVALID_ARG, "workspace=%p is not 16-byte aligned", workspace);
+  const hipStream_t s = (hipStream_t)stream;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return fail(EXL3_ERR_UNSUPPORTED, "cannot tune while the stream is being captured (it times with events and "
+                "synchronizes); tune in eager warm-up, then capture");
+  std::vector<Plan> cands = tune_candidates(w, M);
+  clear_error();
+  if (cands.empty()) return fail(EXL3_ERR_INVALID_ARG, "no schedule for this shape");
+  hipEvent_t e0, e1;
+  if ((e = hipEventCreate(&e0)) != hipSuccess) return launch_error(e, "event create");
+  if ((e = hipEventCreate(&e1)) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return launch_error(e, "event create");
+  }
+  uint32_t *counters = static_cast<uint32_t *>(workspace);
+  // Two passes over the candidates (each keeps its faster pass, so a clock
+  // or cache drift during one pass does not decide), each timing at least
+  // `reps` calls and at least 2 ms.
+  std::vector<float> per_call(cands.size(), -1.f);
+  for (int pass = 0; pass < 2 && st == EXL3_OK; ++pass) {
+    for (size_t i = 0; i < cands.size(); ++i) {
+      const Plan &pl = cands[i];
+      if (pl.workspace > 0 && (workspace == nullptr || workspace_bytes < pl.workspace)) continue;
+      float *slabs =
+          pl.workspace > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.slab_off) : nullptr;
+      uint16_t *dense = pl.decoder == EXL3_DECODER_DENSE
+                            ? reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + pl.dense_off)
+                            : nullptr;
+      auto timed = [&](int n, float *ms) -> exl3_status {
+        if ((e = hipEventRecord(e0, s)) != hipSuccess) return launch_error(e, "event record");
+        exl3_status r = EXL3_OK;
+        for (int k = 0; k < n && r == EXL3_OK; ++k)
+          r = run_linear(&ws[(k + 1) % n_w], x_rot, M, y, y_dtype, counters, slabs, dense, pl, s, true);
+        if (r != EXL3_OK) return r;
+        if ((e = hipEventRecord(e1, s)) != hipSuccess || (e = hipEventSynchronize(e1)) != hipSuccess)
+          return launch_error(e, "event wait");
+        if ((e = hipEventElapsedTime(ms, e0, e1)) != hipSuccess) return launch_error(e, "event time");
+        return EXL3_OK;
+      };
+      float ms1 = 0.f, ms = 0.f;
+      // one untimed call, one timed call to size the batch, then the batch
+      if ((st = run_linear(w, x_rot, M, y, y_dtype, counters, slabs, dense, pl, s, true)) != EXL3_OK) break;
+      if ((st = timed(1, &ms1)) != EXL3_OK) break;
+      const int n = std::min(1000, std::max(reps, (int)(2.0f / std::max(ms1, 1e-4f)) + 1));
+      if ((st = timed(n, &ms)) != EXL3_OK) break;
+      const float t = ms / n;
+      if (per_call[i] < 0.f || t < per_call[i]) per_call[i] = t;
+    }
+  }
+  int best_i = -1;
+  for (size_t i = 0; i < cands.size(); ++i)
+    if (per_call[i] >= 0.f && (best_i < 0 || per_call[i] < per_call[best_i])) best_i = (int)i;
+  const float base_ms = per_call[0], best_ms = best_i >= 0 ? per_call[best_i] : 0.f;
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != EXL3_OK) return st;
+  if (best_i < 0)
+    return fail(EXL3_ERR_WORKSPACE, "no candidate schedule fits the %zu-byte workspace (exl3_tune_workspace_bytes "
+                "gives the size that fits all)", workspace_bytes);
+  // keep the planner's schedule unless a candidate beats it by more than 2%
+  if (best_i != 0 && base_ms > 0.f && best_ms > 0.98f * base_ms) best_i = 0;
+  const Plan &win = cands[best_i];
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tuned[tune_key(w, M)] = as_force(win);
+  }
+  if (best) {
+    *best = as_force(win);
+    best->launches = win.launches;
+    best->workspace = win.workspace;
+  }
+  return EXL3_OK;
 }
 
 exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_t M, float *z_parts,

@@ -216,7 +216,10 @@ def test_table_decoder_choice_and_limits():
         p = _plan(head, M)
         assert p.decoder == ex.EXL3_DECODER_TABLE and p.bm == 64, M
     assert _plan(head, 65).decoder == ex.EXL3_DECODER_ALU
-    assert _plan(view(5120, (12288,), 6, 2), 1).decoder == ex.EXL3_DECODER_TABLE  # 62.9M weights
+    qp = view(5120, (12288,), 6, 2)  # 62.9M weights: the ALU tiles up to 16 rows, the table above
+    assert _plan(qp, 1).decoder == _plan(qp, 16).decoder == ex.EXL3_DECODER_ALU
+    assert _plan(qp, 17).decoder == _plan(qp, 64).decoder == ex.EXL3_DECODER_TABLE
+    assert _plan(view(17408, (5120,), 6, 2), 1).decoder == ex.EXL3_DECODER_TABLE  # 89M weights
     assert _plan(view(4096, (2048,), 4, 1), 1).decoder == ex.EXL3_DECODER_ALU     # 8.4M weights
     small = view(1024, (1024,), 4, 0)
     slabs = F(4, ex.EXL3_MODE_SLABS, -1, ex.EXL3_DECODER_TABLE)
@@ -279,3 +282,45 @@ def test_ruler_hooks_check_arguments():
     assert "iters=0" in last_error()
     assert L.exl3_debug_decode_rate(ctypes.byref(view(1024, (256,), 4, 1)), None, None) == 1
     assert "out is NULL" in last_error()
+
+
+def test_tuned_schedules_table():
+    """exl3_tune_set records a schedule for (shape, M bucket); unforced plan
+    queries and workspace sizes follow it inside the bucket and only there;
+    a schedule with another tree is refused; exl3_tune_clear forgets."""
+    L = ex.load()
+    L.exl3_tune_clear()
+    w = view(5120, (12288,), 6, 2)
+    base = _plan(w, 100)
+    assert base.bm == 128
+    f = F(base.parts, ex.EXL3_MODE_SLABS, 64, ex.EXL3_DECODER_ALU, base.groups)
+    assert L.exl3_tune_set(ctypes.byref(w), 100, ctypes.byref(f)) == 0
+    for M in (65, 100, 128):  # bucket 128
+        p = _plan(w, M)
+        assert p.bm == 64 and p.parts == base.parts and p.decoder == ex.EXL3_DECODER_ALU, M
+        assert L.exl3_workspace_bytes(ctypes.byref(w), M) == p.workspace
+    assert _plan(w, 129).bm == 256 and _plan(w, 64).decoder == ex.EXL3_DECODER_TABLE  # other buckets
+    other = view(5120, (12288, 128), 6, 2)  # another shard map is another shape
+    assert _plan(other, 100).bm == 128
+    bad = F(base.parts * 2, -1, 64, ex.EXL3_DECODER_ALU)
+    assert L.exl3_tune_set(ctypes.byref(w), 100, ctypes.byref(bad)) == 1
+    assert "keeps the shape's tree" in last_error()
+    L.exl3_tune_clear()
+    assert _plan(w, 100).bm == 128
+
+
+def test_tune_checks_arguments_and_sizes():
+    L = ex.load()
+    w = view(5120, (12288,), 6, 2)
+    p = ex._Plan()
+    assert L.exl3_tune(ctypes.byref(w), 1, FAKE, 16, FAKE, 1, FAKE, 1 << 30, 0, None, ctypes.byref(p)) == 1
+    assert "reps=0" in last_error()
+    assert L.exl3_tune(ctypes.byref(w), 1, None, 16, FAKE, 1, FAKE, 1 << 30, 3, None, ctypes.byref(p)) == 1
+    assert L.exl3_tune(ctypes.byref(w), 1, FAKE, 0, FAKE, 1, FAKE, 1 << 30, 3, None, ctypes.byref(p)) == 1
+    w2 = view(5120, (12160, 128), 6, 2)  # kept alive: the copy's shard map points into it
+    pair = (ex._Weight * 2)(w, w2)
+    assert L.exl3_tune(pair, 2, FAKE, 16, FAKE, 1, FAKE, 1 << 30, 3, None, ctypes.byref(p)) == 1
+    assert "copy 1 has another shape" in last_error()
+    # the candidates at 512 rows include the dense decoder's K*N fp16
+    assert L.exl3_tune_workspace_bytes(ctypes.byref(w), 512) >= CB + 5120 * 12288 * 2
+    assert L.exl3_tune_workspace_bytes(ctypes.byref(w), 16) >= L.exl3_workspace_bytes(ctypes.byref(w), 16)
