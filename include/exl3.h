@@ -46,7 +46,7 @@ extern "C" {
 #endif
 
 #define EXL3_MAX_SHARDS 16
-#define EXL3_ABI_VERSION 4
+#define EXL3_ABI_VERSION 5
 
 /* The first EXL3_WORKSPACE_COUNTER_BYTES of every workspace hold per-tile
  * arrival counters (see exl3_linear): they must be zero before the first
@@ -79,6 +79,9 @@ typedef struct exl3_weight {
   int32_t codebook;        /* exl3_codebook                                  */
   int32_t n_shards;        /* 1..EXL3_MAX_SHARDS                             */
   const int32_t *shard_n;  /* HOST [n_shards], each a multiple of 128        */
+  const uint16_t *bias;    /* fp16 bits [N] or NULL: the format's bias
+                              (cuda-exl3 README, "VRAM"), added in fp32 to
+                              svh * 2^-3 * H128(z) before the one rounding    */
 } exl3_weight;
 
 /* Execution plan.  `parts` (P), `groups` (G) and the K range of each part
@@ -175,6 +178,19 @@ typedef struct exl3_plan {
 exl3_status exl3_input_transform(const void *x, int32_t x_dtype, int32_t M, int32_t K,
                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot,
                                  void *stream);
+
+/* The input rotation of a down projection with SwiGLU folded in (cuda-exl3
+ * README, "MoE throughput": SwiGLU folded into the down projection's input
+ * transform).  gate_up [M][2K] in `dtype` (bf16 or fp16) is the gate_up
+ * layer's output, gate = columns 0..K-1, up = K..2K-1; the value rotated is
+ * what the unfused pair would store:
+ *   act[m][k] = rne_dtype( silu(g) * u ),  silu(g) = g / (1 + e^-g)
+ * in fp32, e^x by Cody-Waite range reduction (ln 2 split into a 12-bit head
+ * and a tail) and the degree-7 Taylor polynomial of e^r, every step one IEEE
+ * fp32 operation in a fixed order, then x_rot exactly as
+ * exl3_input_transform(act).  Errors as exl3_input_transform. */
+exl3_status exl3_input_transform_swiglu(const void *gate_up, int32_t dtype, int32_t M, int32_t K,
+                                        const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, void *stream);
 
 /* Bytes of workspace exl3_linear needs for `M` rows of weight `w` (0 when
  * the plan needs none).  Returns 0 and sets exl3_last_error() if `w` is

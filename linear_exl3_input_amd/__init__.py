@@ -29,6 +29,7 @@ __all__ = [
     "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
     "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue", "debug_parts",
     "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops", "tune", "tune_clear",
+    "input_transform_swiglu",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,7 +55,7 @@ class _Weight(ctypes.Structure):
     _fields_ = [("trellis", ctypes.c_void_p), ("suh", ctypes.c_void_p), ("svh", ctypes.c_void_p),
                 ("K", ctypes.c_int32), ("N", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("codebook", ctypes.c_int32), ("n_shards", ctypes.c_int32),
-                ("shard_n", ctypes.POINTER(ctypes.c_int32))]
+                ("shard_n", ctypes.POINTER(ctypes.c_int32)), ("bias", ctypes.c_void_p)]
 
 
 class _Plan(ctypes.Structure):
@@ -63,7 +64,7 @@ class _Plan(ctypes.Structure):
                 ("launches", ctypes.c_int32), ("wg_cols", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
 
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 COUNTER_BYTES = 65536  # EXL3_WORKSPACE_COUNTER_BYTES: zeroed arrival counters at the workspace's start
 
 
@@ -90,6 +91,7 @@ def load() -> ctypes.CDLL:
         P = ctypes.POINTER(_Plan)
         sig = {
             "exl3_input_transform": (i32, [vp, i32, i32, i32, vp, i32, vp, vp]),
+            "exl3_input_transform_swiglu": (i32, [vp, i32, i32, i32, vp, i32, vp, vp]),
             "exl3_workspace_bytes": (sz, [W, i32]),
             "exl3_workspace_bytes_ex": (sz, [W, i32, P]),
             "exl3_linear": (i32, [W, vp, i32, vp, i32, vp, sz, vp]),
@@ -160,6 +162,7 @@ class Exl3Weight:
     bits: int
     codebook: int | str
     shard_n: Optional[Sequence[int]] = None
+    bias: Optional[torch.Tensor] = None  # fp16 [N], added before the output rounding
 
     def __post_init__(self):
         if isinstance(self.codebook, str):
@@ -174,9 +177,12 @@ class Exl3Weight:
             self.shard_n = (self.N,)
         self.shard_n = tuple(int(n) for n in self.shard_n)
         self._shards = (ctypes.c_int32 * len(self.shard_n))(*self.shard_n)
+        if self.bias is not None and self.bias.numel() != self.N:
+            raise ValueError(f"bias has {self.bias.numel()} values, the layer {self.N} columns")
         self._view = _Weight(_dev_ptr(self.trellis, "trellis", _U16), _dev_ptr(self.suh, "suh", _H16),
                              _dev_ptr(self.svh, "svh", _H16), self.K, self.N, self.bits, int(self.codebook),
-                             len(self.shard_n), self._shards)
+                             len(self.shard_n), self._shards,
+                             _dev_ptr(self.bias, "bias", _H16) if self.bias is not None else None)
 
     @property
     def n_shards(self) -> int:
@@ -257,6 +263,31 @@ def input_transform(x: torch.Tensor, suh: torch.Tensor, out: Optional[torch.Tens
     _check(L.exl3_input_transform(_dev_ptr(x, "x", (torch.bfloat16, torch.float16)),
                                   _BF16 if x.dtype == torch.bfloat16 else _F16, M, K,
                                   _dev_ptr(suh, "suh", _H16), S, _dev_ptr(out, "x_rot", _H16), _stream()))
+    return out
+
+
+def input_transform_swiglu(gate_up: torch.Tensor, suh: torch.Tensor,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The down projection's input rotation with SwiGLU folded in: gate_up
+    [M, 2K] bf16/fp16 (gate = first K columns, up = last K) -> x_rot of
+    act = rne(silu(gate) * up), as input_transform(act) would give."""
+    if suh.dim() == 1:
+        suh = suh.unsqueeze(0)
+    M, K2 = gate_up.shape
+    K = K2 // 2
+    S = suh.shape[0]
+    if K2 % 2 or suh.shape[1] != K:
+        raise ValueError(f"gate_up has {K2} columns, suh K={suh.shape[1]}: expected 2*K")
+    if gate_up.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"gate_up dtype {gate_up.dtype} is not bf16/fp16")
+    if out is None:
+        out = torch.empty(rot_shape(S, M, K), dtype=torch.float16, device=gate_up.device)
+    elif tuple(out.shape) != rot_shape(S, M, K):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {rot_shape(S, M, K)}")
+    _check(load().exl3_input_transform_swiglu(_dev_ptr(gate_up, "gate_up", (torch.bfloat16, torch.float16)),
+                                              _BF16 if gate_up.dtype == torch.bfloat16 else _F16, M, K,
+                                              _dev_ptr(suh, "suh", _H16), S, _dev_ptr(out, "x_rot", _H16),
+                                              _stream()))
     return out
 
 

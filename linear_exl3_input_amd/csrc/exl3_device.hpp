@@ -195,14 +195,22 @@ __device__ __forceinline__ void hadamard128_wave(float &x0, float &x1, int lane)
 }
 
 // Output stage for one 128-column block of one row, on one wave:
-// y = rne_out(svh * 2^-3 * H128(z)); lane l owns columns n0 + 2l, n0 + 2l + 1.
+// y = rne_out(svh * 2^-3 * H128(z) [+ bias]), the bias (fp16, optional)
+// added in fp32 before the one rounding; lane l owns columns n0 + 2l,
+// n0 + 2l + 1.
 template <bool OUT_BF16>
 __device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *__restrict__ svh,
-                                           uint16_t *__restrict__ yrow, int n0, int lane) {
+                                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ yrow, int n0,
+                                           int lane) {
   hadamard128_wave(z0, z1, lane);
   const uint32_t sv = *(const uint32_t *)(svh + n0 + 2 * lane);
-  const float y0 = keep_f32((z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu));
-  const float y1 = keep_f32((z1 * 0.125f) * f16_bits_to_f32(sv >> 16));
+  float y0 = keep_f32((z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu));
+  float y1 = keep_f32((z1 * 0.125f) * f16_bits_to_f32(sv >> 16));
+  if (bias != nullptr) {
+    const uint32_t bv = *(const uint32_t *)(bias + n0 + 2 * lane);
+    y0 = keep_f32(y0 + f16_bits_to_f32(bv & 0xFFFFu));
+    y1 = keep_f32(y1 + f16_bits_to_f32(bv >> 16));
+  }
   uint32_t packed;
   if constexpr (OUT_BF16) packed = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
   else packed = f32_to_f16_bits(y0) | (f32_to_f16_bits(y1) << 16);
@@ -222,8 +230,8 @@ __device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *_
 template <bool OUT_BF16, int U = 8>
 __device__ __forceinline__ void reduce_rows4(const float *__restrict__ slabs, int n_slabs, int fold_q,
                                              int64_t slab_floats, int N, int64_t m4, int n0,
-                                             const uint16_t *__restrict__ svh, uint16_t *__restrict__ y,
-                                             int64_t row0, int rows, int lane) {
+                                             const uint16_t *__restrict__ svh, const uint16_t *__restrict__ bias,
+                                             uint16_t *__restrict__ y, int64_t row0, int rows, int lane) {
   const float4_t *src = reinterpret_cast<const float4_t *>(slabs + (m4 * N + n0 + 2 * lane) * 4);
   const int64_t st = slab_floats / 4;  // float4s per slab
   float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
@@ -260,7 +268,7 @@ __device__ __forceinline__ void reduce_rows4(const float *__restrict__ slabs, in
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (r < rows) output_row<OUT_BF16>(t0[r], t1[r], svh, y + (row0 + r) * N, n0, lane);
+    if (r < rows) output_row<OUT_BF16>(t0[r], t1[r], svh, bias, y + (row0 + r) * N, n0, lane);
 }
 
 }  // namespace exl3

@@ -393,8 +393,8 @@ __device__ __forceinline__ void fold_rows4_coherent(__amdgpu_buffer_rsrc_t rs, i
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i < rows) {
-      if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, y + (row0 + i) * N, n0, lane);
-      else output_row<false>(t0[i], t1[i], p.svh, y + (row0 + i) * N, n0, lane);
+      if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, p.bias, y + (row0 + i) * N, n0, lane);
+      else output_row<false>(t0[i], t1[i], p.svh, p.bias, y + (row0 + i) * N, n0, lane);
     }
 }
 
@@ -473,8 +473,8 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, uint32_t tile, 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < nr) {
-          if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
-          else output_row<false>(t0[i], t1[i], p.svh, y + (int64_t)(r0 + i) * N, n0, lane);
+          if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, p.bias, y + (int64_t)(r0 + i) * N, n0, lane);
+          else output_row<false>(t0[i], t1[i], p.svh, p.bias, y + (int64_t)(r0 + i) * N, n0, lane);
         }
     }
   } else {
@@ -773,8 +773,8 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
     if (row >= rend) break;
     const float z0 = z[r * Z_ROW + 2 * lane];
     const float z1 = z[r * Z_ROW + 2 * lane + 1];
-    if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
-    else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+    if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
+    else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
   }
   }
 }
@@ -1002,8 +1002,8 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
       if (row >= rend) break;
       const float z0 = z[r * Z_ROW + 2 * lane];
       const float z1 = z[r * Z_ROW + 2 * lane + 1];
-      if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
-      else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
+      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
     }
   }
 }

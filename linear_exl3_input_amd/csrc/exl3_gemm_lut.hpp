@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
             const float z0 = zb[r * 128 + 2 * lane];
             const float z1 = zb[r * 128 + 2 * lane + 1];
             const int64_t row = p.row_base + 16 * mt + r;
-            if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
-            else output_row<false>(z0, z1, p.svh, y + row * N, cu.nb * 128, lane);
+            if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + row * N, cu.nb * 128, lane);
+            else output_row<false>(z0, z1, p.svh, p.bias, y + row * N, cu.nb * 128, lane);
           }
         }
         barrier_lds();

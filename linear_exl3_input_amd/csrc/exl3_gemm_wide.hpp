@@ -441,8 +441,8 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
       if (row >= rend) break;
       const float z0 = z[r * Z_ROW + 2 * lane];
       const float z1 = z[r * Z_ROW + 2 * lane + 1];
-      if (p.out_bf16) output_row<true>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
-      else output_row<false>(z0, z1, p.svh, y + (int64_t)row * N, nb * 128, lane);
+      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
+      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
     }
   }
 }

@@ -71,6 +71,7 @@ exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_s
   exl3_status st;
   if (need_trellis && (st = check_ptr(w->trellis, "trellis")) != EXL3_OK) return st;
   if (need_suh && (st = check_ptr(w->suh, "suh")) != EXL3_OK) return st;
+  if (w->bias != nullptr && (st = check_ptr(w->bias, "bias")) != EXL3_OK) return st;
   if ((st = check_ptr(w->svh, "svh")) != EXL3_OK) return st;
   return EXL3_OK;
 }
@@ -336,6 +337,29 @@ exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Both input transforms: every argument checked before the launch.
+exl3_status input_transform_checked(const void *x, int32_t x_dtype, bool swiglu, int32_t M, int32_t K,
+                                    const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, void *stream) {
+  clear_error();
+  if (x_dtype != EXL3_F16 && x_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "x_dtype=%d, must be 0 (fp16) or 1 (bf16)", x_dtype);
+  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
+  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
+  if (K <= 0 || K % 128 != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "K=%d must be a positive multiple of 128 (off by %d)", K, K > 0 ? K % 128 : K);
+  if (K > MAX_KN) return fail(EXL3_ERR_UNSUPPORTED, "K=%d exceeds the supported %d", K, MAX_KN);
+  if (n_shards < 1 || n_shards > EXL3_MAX_SHARDS)
+    return fail(EXL3_ERR_INVALID_ARG, "n_shards=%d, must be 1..%d", n_shards, EXL3_MAX_SHARDS);
+  exl3_status st;
+  if ((st = check_ptr(suh, "suh")) != EXL3_OK) return st;
+  if (M == 0) return EXL3_OK;
+  if ((st = check_ptr(x, swiglu ? "gate_up" : "x")) != EXL3_OK) return st;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_input_transform(x, x_dtype == EXL3_BF16, swiglu, M, K, suh, n_shards, x_rot,
+                                                    (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "input transform launch");
+}
+
 // ------------------------------------------------------- tuned schedules
 //
 // The schedule autotuner (cuda-exl3 README, "Where the time goes": the best
@@ -475,24 +499,12 @@ const char *exl3_last_error(void) { return g_last_error; }
 
 exl3_status exl3_input_transform(const void *x, int32_t x_dtype, int32_t M, int32_t K, const uint16_t *suh,
                                  int32_t n_shards, uint16_t *x_rot, void *stream) {
-  clear_error();
-  if (x_dtype != EXL3_F16 && x_dtype != EXL3_BF16)
-    return fail(EXL3_ERR_INVALID_ARG, "x_dtype=%d, must be 0 (fp16) or 1 (bf16)", x_dtype);
-  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
-  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
-  if (K <= 0 || K % 128 != 0)
-    return fail(EXL3_ERR_INVALID_ARG, "K=%d must be a positive multiple of 128 (off by %d)", K, K > 0 ? K % 128 : K);
-  if (K > MAX_KN) return fail(EXL3_ERR_UNSUPPORTED, "K=%d exceeds the supported %d", K, MAX_KN);
-  if (n_shards < 1 || n_shards > EXL3_MAX_SHARDS)
-    return fail(EXL3_ERR_INVALID_ARG, "n_shards=%d, must be 1..%d", n_shards, EXL3_MAX_SHARDS);
-  exl3_status st;
-  if ((st = check_ptr(suh, "suh")) != EXL3_OK) return st;
-  if (M == 0) return EXL3_OK;
-  if ((st = check_ptr(x, "x")) != EXL3_OK) return st;
-  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
-  const hipError_t e = exl3::launch_input_transform(x, x_dtype == EXL3_BF16, M, K, suh, n_shards, x_rot,
-                                                    (hipStream_t)stream);
-  return e == hipSuccess ? EXL3_OK : launch_error(e, "input transform launch");
+  return input_transform_checked(x, x_dtype, false, M, K, suh, n_shards, x_rot, stream);
+}
+
+exl3_status exl3_input_transform_swiglu(const void *gate_up, int32_t dtype, int32_t M, int32_t K,
+                                        const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, void *stream) {
+  return input_transform_checked(gate_up, dtype, true, M, K, suh, n_shards, x_rot, stream);
 }
 
 size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan *force) {
@@ -575,6 +587,7 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
   p.trellis = w->trellis;
   p.x_rot = x_rot;
   p.svh = w->svh;
+  p.bias = w->bias;
   p.y = y;
   p.slabs = slabs;
   p.counters = with_output && pl.finisher ? counters : nullptr;
@@ -626,7 +639,7 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
       if (e != hipSuccess) return launch_error(e, "trellis GEMM launch");
     }
     if (p.slab_mode && with_output && p.counters == nullptr) {
-      e = exl3::launch_epilogue(p.slabs, n_units, p.fold_q, p.row_base, p.row_end, w->N, w->svh, y,
+      e = exl3::launch_epilogue(p.slabs, n_units, p.fold_q, p.row_base, p.row_end, w->N, w->svh, w->bias, y,
                                 p.out_bf16 != 0, s);
       if (e != hipSuccess) return launch_error(e, "part-sum epilogue launch");
     }
@@ -898,7 +911,7 @@ exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t g
   if (M == 0) return EXL3_OK;
   if ((st = check_ptr(z_parts, "z_parts")) != EXL3_OK) return st;
   if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
-  const hipError_t e = exl3::launch_epilogue(z_parts, n_parts, n_parts / groups, 0, M, w->N, w->svh, y,
+  const hipError_t e = exl3::launch_epilogue(z_parts, n_parts, n_parts / groups, 0, M, w->N, w->svh, w->bias, y,
                                              y_dtype == EXL3_BF16, (hipStream_t)stream);
   return e == hipSuccess ? EXL3_OK : launch_error(e, "epilogue launch");
 }

@@ -14,6 +14,7 @@ struct GemmParams {
   const uint16_t *x_rot;    // [n_shards][K/32][M][32] fp16 bits (k-step tiles)
   const uint16_t *svh;      // [N] fp16 bits
   const uint16_t *dense;    // dense path: W_q as B fragments (dequant_kernel order)
+  const uint16_t *bias;     // [N] fp16 added before the output rounding, or null
   void *y;                  // [M][N] bf16/fp16
   float *slabs;             // [units][ceil(rows/4)][N][4] fp32 (slab mode)
   uint32_t *counters;       // slab mode: per-tile arrival counters (zero on
@@ -55,13 +56,16 @@ hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, hipStre
 // one per CU; fused (parts folded in order) or slab mode as in p.
 hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hipStream_t s);
 
-hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
-                                  int32_t n_shards, uint16_t *x_rot, hipStream_t s);
+// swiglu: x is the gate_up output [M][2K]; the rotated value is
+// rne_dtype(silu(gate) * up) (see input_transform_kernel).
+hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32_t M, int32_t K,
+                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s);
 // Ordered sum of n_slabs partial slabs (groups of fold_q consecutive slabs
 // folded first, then the groups in order) + output transform, for rows
 // [row_base, row_end) (slab row r = row row_base + r).
 hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, int32_t row_base, int32_t row_end,
-                           int32_t N, const uint16_t *svh, void *y, bool out_bf16, hipStream_t s);
+                           int32_t N, const uint16_t *svh, const uint16_t *bias, void *y, bool out_bf16,
+                           hipStream_t s);
 hipError_t launch_debug_codebook(int cb, uint16_t *out, hipStream_t s);
 
 // Measurement rulers.  decode_rate: the tile kernels' trellis staging and

@@ -64,7 +64,42 @@ __device__ __forceinline__ void lstage(float (&t)[8]) {
     }
 }
 
+// SwiGLU folded into the rotation (cuda-exl3 README, "MoE throughput"): x is
+// then the gate_up layer's output [M][2K] (gate = columns 0..K-1, up =
+// K..2K-1) and the rotated value is act = rne_dtype(silu(g) * u), computed
+// in fp32 exactly as the unfused pair would store it.  e^x by Cody-Waite
+// range reduction (ln 2 split into a 12-bit head, so n * head is exact, and
+// a tail) and the degree-7 Taylor polynomial of e^r on |r| <= ln2/2, every
+// step one IEEE fp32 operation in a fixed order (no contraction: keep_f32),
+// so the result is reproducible bit for bit.
+__device__ __forceinline__ float exp_taylor_f32(float x) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr float LN2_HI = (float)(2839.0 / 4096.0);
+  constexpr float LN2_LO = (float)(0.6931471805599453 - 2839.0 / 4096.0);
+  x = x < -104.f ? -104.f : (x > 104.f ? 104.f : x);  // NaN passes through
+  const float n = __builtin_rintf(keep_f32(x * LOG2E));
+  const float r = keep_f32(keep_f32(x - keep_f32(n * LN2_HI)) - keep_f32(n * LN2_LO));
+  float p = (float)(1.0 / 5040.0);
+  p = keep_f32(keep_f32(p * r) + (float)(1.0 / 720.0));
+  p = keep_f32(keep_f32(p * r) + (float)(1.0 / 120.0));
+  p = keep_f32(keep_f32(p * r) + (float)(1.0 / 24.0));
+  p = keep_f32(keep_f32(p * r) + (float)(1.0 / 6.0));
+  p = keep_f32(keep_f32(p * r) + 0.5f);
+  p = keep_f32(keep_f32(p * r) + 1.0f);
+  p = keep_f32(keep_f32(p * r) + 1.0f);
+  return __builtin_ldexpf(p, n != n ? 0 : (int)n);
+}
+
 template <bool X_BF16>
+__device__ __forceinline__ float swiglu_act(uint32_t gbits, uint32_t ubits) {
+  const float g = X_BF16 ? bf16_bits_to_f32(gbits) : f16_bits_to_f32(gbits);
+  const float u = X_BF16 ? bf16_bits_to_f32(ubits) : f16_bits_to_f32(ubits);
+  const float silu = g / keep_f32(1.0f + exp_taylor_f32(-g));
+  const float a = keep_f32(keep_f32(silu) * u);
+  return X_BF16 ? bf16_bits_to_f32(f32_to_bf16_bits(a)) : f16_bits_to_f32(f32_to_f16_bits(a));
+}
+
+template <bool X_BF16, bool SWIGLU>
 __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ suh,
                                                               uint16_t *__restrict__ x_rot, int32_t M,
@@ -96,7 +131,23 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
   const int j = L >> 2, q = L & 3;
   const int k0 = kb * 128 + 32 * j + 16 * (q >> 1) + 4 * (q & 1);  // the lane's first k; the second run at k0 + 8
   float xv[8];
-  {
+  if constexpr (SWIGLU) {
+    u32x2_t glo = {0u, 0u}, ghi = {0u, 0u}, ulo = {0u, 0u}, uhi = {0u, 0u};
+    if (live) {
+      const uint16_t *row = x + m * 2 * K;
+      glo = *(const u32x2_t *)(row + k0);
+      ghi = *(const u32x2_t *)(row + k0 + 8);
+      ulo = *(const u32x2_t *)(row + K + k0);
+      uhi = *(const u32x2_t *)(row + K + k0 + 8);
+    }
+    const uint32_t gw[4] = {glo.x, glo.y, ghi.x, ghi.y};
+    const uint32_t uw[4] = {ulo.x, ulo.y, uhi.x, uhi.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[2 * i] = swiglu_act<X_BF16>(gw[i] & 0xFFFFu, uw[i] & 0xFFFFu);
+      xv[2 * i + 1] = swiglu_act<X_BF16>(gw[i] >> 16, uw[i] >> 16);
+    }
+  } else {
     u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
     if (live) {
       lo = *(const u32x2_t *)(x + m * K + k0);
@@ -138,16 +189,20 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
   }
 }
 
-hipError_t launch_input_transform(const void *x, bool x_bf16, int32_t M, int32_t K, const uint16_t *suh,
-                                  int32_t n_shards, uint16_t *x_rot, hipStream_t s) {
+hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32_t M, int32_t K,
+                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s) {
   const int64_t items = M >= 4 ? (((int64_t)M + 3) / 4) * (K / 128) : (int64_t)M * ((K / 128 + 3) / 4);
   const dim3 grid((unsigned)((items + 3) / 4));
-  if (x_bf16)
-    hipLaunchKernelGGL((input_transform_kernel<true>), grid, dim3(256), 0, s, (const uint16_t *)x, suh, x_rot,
-                       M, K, n_shards);
+  const uint16_t *xp = static_cast<const uint16_t *>(x);
+  if (x_bf16 && swiglu)
+    hipLaunchKernelGGL((input_transform_kernel<true, true>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K, n_shards);
+  else if (x_bf16)
+    hipLaunchKernelGGL((input_transform_kernel<true, false>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K, n_shards);
+  else if (swiglu)
+    hipLaunchKernelGGL((input_transform_kernel<false, true>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K, n_shards);
   else
-    hipLaunchKernelGGL((input_transform_kernel<false>), grid, dim3(256), 0, s, (const uint16_t *)x, suh, x_rot,
-                       M, K, n_shards);
+    hipLaunchKernelGGL((input_transform_kernel<false, false>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K,
+                       n_shards);
   return hipGetLastError();
 }
 
@@ -165,7 +220,7 @@ template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t n_slabs,
                                                        int32_t fold_q, int32_t row_base, int32_t row_end,
                                                        int32_t N, const uint16_t *__restrict__ svh,
-                                                       uint16_t *__restrict__ y) {
+                                                       const uint16_t *__restrict__ bias, uint16_t *__restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nblocks = N >> 7;
@@ -175,20 +230,21 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__
   const int64_t m4 = item / nblocks;
   const int n0 = (int)(item - m4 * nblocks) * 128;
   const int64_t r0 = 4 * m4;
-  reduce_rows4<OUT_BF16>(slabs, n_slabs, fold_q, (int64_t)M4 * N * 4, N, m4, n0, svh, y, row_base + r0,
+  reduce_rows4<OUT_BF16>(slabs, n_slabs, fold_q, (int64_t)M4 * N * 4, N, m4, n0, svh, bias, y, row_base + r0,
                          (int)min((int64_t)4, rows - r0), lane);
 }
 
 hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, int32_t row_base, int32_t row_end,
-                           int32_t N, const uint16_t *svh, void *y, bool out_bf16, hipStream_t s) {
+                           int32_t N, const uint16_t *svh, const uint16_t *bias, void *y, bool out_bf16,
+                           hipStream_t s) {
   const int64_t items = (int64_t)((row_end - row_base + 3) / 4) * (N / 128);
   const dim3 grid((unsigned)((items + 3) / 4));
   if (out_bf16)
     hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end, N,
-                       svh, (uint16_t *)y);
+                       svh, bias, (uint16_t *)y);
   else
     hipLaunchKernelGGL((epilogue_kernel<false>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end,
-                       N, svh, (uint16_t *)y);
+                       N, svh, bias, (uint16_t *)y);
   return hipGetLastError();
 }
 

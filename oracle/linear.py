@@ -75,11 +75,13 @@ class Reference:
     absdot: np.ndarray    # float64 [M, Nsel]  sum_k |x~ w|
     y: np.ndarray         # float64 [M, Nsel]  exact output
     cols: np.ndarray      # absolute column index of each selected column
+    bias: bool = False    # y includes the layer's bias
 
 
 def reference(trellis: np.ndarray, suh_bits: np.ndarray, svh_bits: np.ndarray,
               shards: Sequence[int], bits: int, cb: int, x_bits: np.ndarray,
-              x_dtype: str = "bf16", col_blocks: Sequence[int] | None = None) -> Reference:
+              x_dtype: str = "bf16", col_blocks: Sequence[int] | None = None,
+              bias_bits: np.ndarray | None = None) -> Reference:
     """fp64 reference for all columns, or for the 128-column blocks listed.
 
     ``trellis`` [K/16, N/16, 16*bits]; ``suh_bits`` [S, K]; ``svh_bits`` [N];
@@ -104,9 +106,9 @@ def reference(trellis: np.ndarray, suh_bits: np.ndarray, svh_bits: np.ndarray,
         s = shard_col[128 * b]
         z[:, 128 * i:128 * i + 128] = xr[s] @ w
         a[:, 128 * i:128 * i + 128] = np.abs(xr[s]) @ np.abs(w)
-    y = tf.output_transform_f64(z, svh_bits[cols])
+    y = tf.output_transform_f64(z, svh_bits[cols], None if bias_bits is None else bias_bits[cols])
     del K
-    return Reference(x_rot, z, a, y, cols)
+    return Reference(x_rot, z, a, y, cols, bias_bits is not None)
 
 
 def bound(ref: Reference, svh_bits: np.ndarray, K: int, out_dtype: str) -> np.ndarray:
@@ -119,7 +121,12 @@ def bound(ref: Reference, svh_bits: np.ndarray, K: int, out_dtype: str) -> np.nd
     blk = np.repeat(blk, 128, axis=1)
     svh = np.abs(tf.f16_from_bits(svh_bits[ref.cols]).astype(np.float64))[None, :]
     u_o = U_OUT[out_dtype]
-    return u_o * np.abs(ref.y) + (1.0 + u_o) * tf.OUTPUT_SCALE * svh * blk + A_OUT[out_dtype]
+    scaled = tf.OUTPUT_SCALE * svh * blk
+    if ref.bias:
+        # the fp32 add of the bias: one more rounding of at most U_F32 of
+        # the sum, whose distance from y* is at most the scaled term
+        scaled = scaled + U_F32 * (np.abs(ref.y) + scaled)
+    return u_o * np.abs(ref.y) + (1.0 + u_o) * scaled + A_OUT[out_dtype]
 
 
 def out_bits_to_f64(y_bits: np.ndarray, out_dtype: str) -> np.ndarray:

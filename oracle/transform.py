@@ -34,6 +34,8 @@ it bit for bit.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 BLOCK = 128
@@ -140,14 +142,20 @@ def rotate_input_f64(x_bits: np.ndarray, suh_bits: np.ndarray, x_dtype: str = "b
 # Output transform
 # ---------------------------------------------------------------------------
 
-def output_transform_f32(z32: np.ndarray, svh_bits: np.ndarray, out_dtype: str) -> np.ndarray:
-    """Reading R11 in float32: butterfly, *2**-3, *svh, one rounding.
+def output_transform_f32(z32: np.ndarray, svh_bits: np.ndarray, out_dtype: str,
+                         bias_bits: np.ndarray | None = None) -> np.ndarray:
+    """Reading R11 in float32: butterfly, *2**-3, *svh, one rounding.  The
+    format's optional bias (cuda-exl3 README, "VRAM": trellis, suh/svh and
+    bias are what is stored) is added in float32 right before that rounding
+    (reading R16: one rounding for the whole output stage).
 
     z32 [M, N] float32 -> output bits [M, N] (bf16 or fp16).
     """
     h = butterfly(np.asarray(z32, dtype=np.float32))
     h = h * np.float32(OUTPUT_SCALE)
     y = h * f16_from_bits(svh_bits).astype(np.float32)[None, :]
+    if bias_bits is not None:
+        y = y + f16_from_bits(bias_bits).astype(np.float32)[None, :]
     if out_dtype == "bf16":
         return f32_to_bf16_bits(y)
     if out_dtype == "f16":
@@ -155,10 +163,13 @@ def output_transform_f32(z32: np.ndarray, svh_bits: np.ndarray, out_dtype: str) 
     raise ValueError(out_dtype)
 
 
-def output_transform_f64(z64: np.ndarray, svh_bits: np.ndarray) -> np.ndarray:
-    """Exact output transform in float64: H128(z) * 2**-3 * svh."""
+def output_transform_f64(z64: np.ndarray, svh_bits: np.ndarray, bias_bits: np.ndarray | None = None) -> np.ndarray:
+    """Exact output transform in float64: H128(z) * 2**-3 * svh (+ bias)."""
     h = butterfly(np.asarray(z64, dtype=np.float64))
-    return h * OUTPUT_SCALE * f16_from_bits(svh_bits).astype(np.float64)[None, :]
+    y = h * OUTPUT_SCALE * f16_from_bits(svh_bits).astype(np.float64)[None, :]
+    if bias_bits is not None:
+        y = y + f16_from_bits(bias_bits).astype(np.float64)[None, :]
+    return y
 
 
 def reduce_parts_f32(parts: np.ndarray, groups: int | None = None) -> np.ndarray:
@@ -185,3 +196,52 @@ def reduce_parts_f32(parts: np.ndarray, groups: int | None = None) -> np.ndarray
             gsum = gsum + parts[p].astype(np.float32)
         total = gsum if total is None else total + gsum
     return total
+
+
+# ------------------------------------------------- SwiGLU before the rotation
+#
+# Reading R17: the down projection's input transform may take the gate_up
+# layer's output directly (cuda-exl3 README, "MoE throughput": SwiGLU folded
+# into the down projection's input transform) and computes exactly what the
+# unfused pair would: act = rne_dtype(silu(g) * u) in float32, then the
+# ordinary rotation of act.  exp is spelled out so that every step is one
+# IEEE float32 operation in a fixed order: Cody-Waite range reduction
+# (x = n ln2 + r, ln 2 split into a 12-bit head, so n * head is exact, and a
+# tail) and the degree-7 Taylor polynomial of e^r on |r| <= ln2 / 2
+# (truncation below 1e-8 relative), scaled by 2^n.
+
+EXP_LOG2E = np.float32(1.4426950408889634)
+EXP_LN2_HI = np.float32(2839.0 / 4096.0)
+EXP_LN2_LO = np.float32(0.6931471805599453 - 2839.0 / 4096.0)
+EXP_CLAMP = np.float32(104.0)  # e^104 overflows float32, e^-104 underflows to 0
+EXP_TAYLOR = [np.float32(1.0 / math.factorial(i)) for i in range(8)]
+
+
+def exp_f32(x: np.ndarray) -> np.ndarray:
+    """e^x in float32 by the fixed sequence above (NaN stays NaN)."""
+    x = np.asarray(x, dtype=np.float32)
+    x = np.where(x < -EXP_CLAMP, -EXP_CLAMP, np.where(x > EXP_CLAMP, EXP_CLAMP, x)).astype(np.float32)
+    n = np.rint(x * EXP_LOG2E)
+    r = (x - n * EXP_LN2_HI) - n * EXP_LN2_LO
+    p = np.full_like(r, EXP_TAYLOR[7])
+    for c in EXP_TAYLOR[6::-1]:
+        p = p * r + c
+    ni = np.where(np.isnan(n), 0, n).astype(np.int32)
+    with np.errstate(over="ignore"):
+        return np.ldexp(p, ni).astype(np.float32)
+
+
+def silu_f32(g: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float32)
+    return (g / (np.float32(1.0) + exp_f32(-g))).astype(np.float32)
+
+
+def swiglu_bits(gate_up_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """[M, 2K] gate_up output bits (gate = columns 0..K-1, up = K..2K-1) ->
+    act [M, K] bits of the same dtype: rne_dtype(silu(g) * u) in float32."""
+    a = np.asarray(gate_up_bits, dtype=np.uint16)
+    K = a.shape[1] // 2
+    to32 = bf16_bits_to_f32 if dtype == "bf16" else (lambda b: f16_from_bits(b).astype(np.float32))
+    g, u = to32(a[:, :K]), to32(a[:, K:])
+    act = (silu_f32(g) * u).astype(np.float32)
+    return f32_to_bf16_bits(act) if dtype == "bf16" else f32_to_f16_bits(act)

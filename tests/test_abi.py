@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(L, name), name
-    assert L.exl3_abi_version() == ex.ABI_VERSION == 4
+    assert L.exl3_abi_version() == ex.ABI_VERSION == 5
 
 
 def test_status_strings():
@@ -324,3 +324,18 @@ def test_tune_checks_arguments_and_sizes():
     # the candidates at 512 rows include the dense decoder's K*N fp16
     assert L.exl3_tune_workspace_bytes(ctypes.byref(w), 512) >= CB + 5120 * 12288 * 2
     assert L.exl3_tune_workspace_bytes(ctypes.byref(w), 16) >= L.exl3_workspace_bytes(ctypes.byref(w), 16)
+
+
+def test_bias_and_swiglu_transform_checks():
+    L = ex.load()
+    w = view(1024, (256,), 4, 1)
+    w.bias = FAKE + 2  # misaligned
+    assert L.exl3_workspace_bytes(ctypes.byref(w), 4) == 0
+    assert "bias" in last_error() and "not 16-byte aligned" in last_error()
+    w.bias = FAKE
+    assert L.exl3_workspace_bytes(ctypes.byref(w), 4) > 0
+    assert L.exl3_input_transform_swiglu(FAKE, 1, 4, 100, FAKE, 1, FAKE, None) == 1
+    assert "K=100" in last_error()
+    assert L.exl3_input_transform_swiglu(None, 1, 4, 128, FAKE, 1, FAKE, None) == 1
+    assert "gate_up is NULL" in last_error()
+    assert L.exl3_input_transform_swiglu(FAKE, 1, 0, 128, FAKE, 1, FAKE, None) == 0  # no rows: nothing to do

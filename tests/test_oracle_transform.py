@@ -137,3 +137,66 @@ def test_reduce_parts_grouped_tree():
     assert tf.reduce_parts_f32(parts, groups=2)[0, 0] == np.float32(1.0 + 2.0 ** -23)
     with pytest.raises(ValueError):
         tf.reduce_parts_f32(parts, groups=3)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_output_bias_closed_forms(out_dtype):
+    """The bias (reading R16): z = 0 gives rne_out(bias) exactly; a one-hot z
+    of value v in a block gives rne_out(fp32(+-v * 2**-3 * svh) + bias) in
+    every column of the block, the sign that of the Hadamard column."""
+    rng = np.random.default_rng(7)
+    N = 256
+    svh = (np.where(rng.integers(0, 2, N) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, N))).astype(np.float16)
+    bias = (rng.standard_normal(N) * 3).astype(np.float16)
+    rnd = tf.f32_to_bf16_bits if out_dtype == "bf16" else tf.f32_to_f16_bits
+    zero = tf.output_transform_f32(np.zeros((2, N), np.float32), svh.view(np.uint16), out_dtype, bias.view(np.uint16))
+    assert np.array_equal(zero, np.broadcast_to(rnd(bias.astype(np.float32)), (2, N)))
+    h = scipy.linalg.hadamard(128)
+    z = np.zeros((1, N), np.float32)
+    z[0, 128 + 5] = v = np.float32(3.75)
+    got = tf.output_transform_f32(z, svh.view(np.uint16), out_dtype, bias.view(np.uint16))
+    sgn = np.concatenate([np.zeros(128), h[:, 5]])
+    want = np.empty(N, np.float32)
+    for n in range(N):
+        a = np.float32(np.float32(np.float32(sgn[n]) * v) * np.float32(0.125)) * np.float32(svh[n])
+        want[n] = np.float32(a + np.float32(bias[n]))
+    assert np.array_equal(got[0], rnd(want))
+    # without a bias the old result
+    assert np.array_equal(tf.output_transform_f32(z, svh.view(np.uint16), out_dtype),
+                          rnd((np.float32(0.125) * np.float32(3.75) * sgn.astype(np.float32)
+                               * svh.astype(np.float32)).astype(np.float32))[None])
+
+
+def test_exp_f32_against_the_exponential():
+    """Reading R17's exp: within 2 ulp of float64 e^x over the whole finite
+    range, exact at 0, overflow to inf and underflow to 0 past +-104."""
+    x = np.linspace(-87, 88, 100001).astype(np.float32)
+    e = tf.exp_f32(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    assert np.all(np.abs(e - ref) <= 2 * np.spacing(ref.astype(np.float32)).astype(np.float64))
+    edge = tf.exp_f32(np.array([0.0, 200.0, -200.0], np.float32))
+    assert edge[0] == 1.0 and np.isinf(edge[1]) and edge[2] == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_swiglu_against_float64(dtype):
+    """act = rne(silu(g) * u): within one output ulp of the float64 value for
+    every pair (the fp32 steps round at most a few fp32 ulps), and equal to
+    the float64 value's rounding for nearly all; silu(0) = 0 exactly and the
+    sign of u carries through."""
+    rng = np.random.default_rng(11)
+    M, K = 64, 512
+    f = (rng.standard_normal((M, 2 * K)) * np.exp2(rng.uniform(-6, 4, (M, 2 * K)))).astype(np.float32)
+    bits = tf.f32_to_bf16_bits(f) if dtype == "bf16" else tf.f32_to_f16_bits(f)
+    act = tf.swiglu_bits(bits, dtype)
+    to64 = (lambda b: tf.bf16_bits_to_f32(b).astype(np.float64)) if dtype == "bf16" else \
+        (lambda b: tf.f16_from_bits(b).astype(np.float64))
+    g, u = to64(bits[:, :K]), to64(bits[:, K:])
+    exact = g / (1.0 + np.exp(-g)) * u
+    rnd = tf.f32_to_bf16_bits if dtype == "bf16" else tf.f32_to_f16_bits
+    want = rnd(exact.astype(np.float32))
+    assert np.mean(act == want) > 0.999
+    off = act != want  # anywhere else: the neighbouring code of the same sign (one output ulp)
+    assert np.all(np.abs(act[off].astype(np.int32) - want[off].astype(np.int32)) == 1)
+    zero = np.zeros((1, 256), np.uint16)
+    assert np.all(tf.swiglu_bits(zero, dtype) == 0)
