@@ -69,7 +69,7 @@ def kernel_key(lay, plan) -> str:
     multi = unit > 1 and quads == 1
     if bm <= 64:
         qw = plan["wg_cols"] // 32
-        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}, {quads}, {qw}>"
+        name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}, {quads}, {qw}, false>"
     elif bm == 128:
         name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, {str(multi).lower()}>"
     else:

@@ -320,6 +320,66 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
 exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t groups, int32_t M,
                                 const exl3_weight *w, void *y, int32_t y_dtype, void *stream);
 
+/* ---------------------------------------------- mixture of experts
+ * Routed experts as one grouped GEMM (cuda-exl3 README, "What is
+ * supported": the (token, expert) pairs are sorted by expert and each
+ * expert's run is padded to whole row blocks, so every block belongs to one
+ * expert and the GEMM offsets the trellis by the block's expert; blocks of
+ * no expert are skipped; "Determinism": routed rows are written and each
+ * token's top-k rows summed in a fixed order in fp32, rounded once).  Each
+ * routed row has exactly the bits exl3_linear gives that token on its
+ * expert's weight alone (the part tree is the expert shape's own).
+ *
+ * Pair p = t * topk + j is token t's j-th expert.  The routed buffers have
+ * exl3_moe_rows_max(T, topk, E, block) rows: at most T*topk pairs plus the
+ * padding of every expert with pairs, in whole blocks (0 if that exceeds
+ * the supported rows). */
+int32_t exl3_moe_rows_max(int32_t T, int32_t topk, int32_t E, int32_t block);
+
+/* topk_ids [T][topk] int32 (device; ids outside 0..E-1 drop their pair) ->
+ *   row_pair     [rows]          pair of each routed row, -1 for padding
+ *   block_expert [rows / block]  expert of each row block, -1 after the last
+ *   pair_row     [T * topk]      routed row of each pair, -1 if dropped
+ * Expert e's pairs occupy rows start(e) .. start(e) + count(e) - 1, start(e)
+ * the whole-block padded counts of the experts before it; within that run
+ * the order of the pairs may vary between runs (every result is the same).
+ * block 16, 32 or 64; E <= 4096; topk <= 64.  One workgroup. */
+exl3_status exl3_moe_align(const int32_t *topk_ids, int32_t T, int32_t topk, int32_t E, int32_t block,
+                           int32_t *row_pair, int32_t *block_expert, int32_t *pair_row, void *stream);
+
+/* The input rotation of every routed row: row r rotates token row_pair[r] /
+ * topk of x ([T][K], or with `swiglu` the gate_up output [T][2K] as in
+ * exl3_input_transform_swiglu) with the suh rows of its block's expert,
+ * suh [E][n_shards][K] fp16; padding rows rotate zeros.  x_rot as from
+ * exl3_input_transform for `rows` rows (rows = exl3_moe_rows_max). */
+exl3_status exl3_moe_input_transform(const void *x, int32_t x_dtype, int32_t swiglu, int32_t T, int32_t K,
+                                     const uint16_t *suh, int32_t n_shards, int32_t E, const int32_t *row_pair,
+                                     const int32_t *block_expert, int32_t topk, int32_t block, int32_t rows,
+                                     uint16_t *x_rot, void *stream);
+
+/* Workspace for exl3_moe_linear (same validity rules as exl3_workspace_bytes). */
+size_t exl3_moe_workspace_bytes(const exl3_weight *w, int32_t rows, int32_t block);
+
+/* The grouped GEMM: `w` describes expert 0 and the E experts are stacked
+ * behind it at fixed strides: trellis [E][K/16][N/16][16*bits], suh
+ * [E][n_shards][K], svh [E][N], bias [E][N] (if any).  Row block b of x_rot
+ * (rows = a multiple of `block`) is multiplied by expert block_expert[b]'s
+ * weight (skipped when -1) into y [rows][N]; rows of padding hold
+ * unspecified values.  The ALU tiles of `block` rows with the output stage
+ * in the GEMM.  Errors as exl3_linear; EXL3_ERR_UNSUPPORTED if the rows
+ * need more finishing counters than the workspace holds and the tree has no
+ * fused schedule. */
+exl3_status exl3_moe_linear(const exl3_weight *w, int32_t E, const uint16_t *x_rot, int32_t rows,
+                            const int32_t *block_expert, int32_t block, void *y, int32_t y_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* out[t][n] = rne_dtype( sum over j of topk_weights[t][j] * y_routed[pair_row[t*topk+j]][n] ),
+ * the sum in fp32 from 0 in j order, each product rounded to fp32 before it
+ * is added; dropped pairs add nothing.  y_routed [rows][N] and out [T][N] in
+ * `dtype`; topk_weights fp32 [T][topk]; N even. */
+exl3_status exl3_moe_combine(const void *y_routed, int32_t dtype, const int32_t *pair_row, const float *topk_weights,
+                             int32_t T, int32_t topk, int32_t N, void *out, void *stream);
+
 /* ------------------------------------------------- measurement rulers
  * Not part of the layer API: simple kernels that measure, in the same run
  * as the layer timings, what this GPU's HBM, matrix cores and decode path

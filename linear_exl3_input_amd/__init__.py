@@ -29,7 +29,8 @@ __all__ = [
     "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
     "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue", "debug_parts",
     "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops", "tune", "tune_clear",
-    "input_transform_swiglu",
+    "input_transform_swiglu", "MoeWeight", "moe_rows_max", "moe_align", "moe_input_transform", "moe_linear",
+    "moe_combine", "moe_forward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -111,6 +112,13 @@ def load() -> ctypes.CDLL:
             "exl3_tune_workspace_bytes": (sz, [W, i32]),
             "exl3_tune_set": (i32, [W, i32, P]),
             "exl3_tune_clear": (None, []),
+            "exl3_moe_rows_max": (i32, [i32, i32, i32, i32]),
+            "exl3_moe_align": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "exl3_moe_input_transform": (i32, [vp, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32, i32, i32, vp,
+                                               vp]),
+            "exl3_moe_workspace_bytes": (sz, [W, i32, i32]),
+            "exl3_moe_linear": (i32, [W, i32, vp, i32, vp, i32, vp, i32, vp, sz, vp]),
+            "exl3_moe_combine": (i32, [vp, i32, vp, vp, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -445,3 +453,101 @@ def tune_set(w: Exl3Weight, M: int, plan: dict) -> None:
 
 def tune_clear() -> None:
     load().exl3_tune_clear()
+
+
+# ----------------------------------------------------- mixture of experts
+class MoeWeight:
+    """E experts of one shape, stacked: trellis [E, K/16, N/16, 16*bits],
+    suh [E, n_shards, K], svh [E, N], bias [E, N] or None.  The library sees
+    expert 0's view and steps to expert e by the fixed strides."""
+
+    def __init__(self, trellis, suh, svh, bits, codebook, shard_n=None, bias=None):
+        if suh.dim() == 2:
+            suh = suh.unsqueeze(1)
+        self.E = trellis.shape[0]
+        if suh.shape[0] != self.E or svh.shape[0] != self.E or (bias is not None and bias.shape[0] != self.E):
+            raise ValueError("trellis, suh, svh (and bias) must stack the same number of experts")
+        for t in (trellis, suh, svh) + ((bias,) if bias is not None else ()):
+            if not t.is_contiguous():
+                raise ValueError("expert stacks must be contiguous")
+        self.stack = (trellis, suh, svh, bias)
+        self.first = Exl3Weight(trellis[0], suh[0], svh[0], bits, codebook, shard_n,
+                                bias[0] if bias is not None else None)
+        self.K, self.N, self.bits, self.n_shards = self.first.K, self.first.N, bits, self.first.n_shards
+
+    def expert(self, e: int) -> Exl3Weight:
+        trellis, suh, svh, bias = self.stack
+        return Exl3Weight(trellis[e], suh[e], svh[e], self.bits, self.first.codebook, self.first.shard_n,
+                          bias[e] if bias is not None else None)
+
+
+def moe_rows_max(T: int, topk: int, E: int, block: int = 16) -> int:
+    return int(load().exl3_moe_rows_max(T, topk, E, block))
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, block: int = 16):
+    """topk_ids [T, topk] int32 -> (row_pair [rows], block_expert [rows/block],
+    pair_row [T*topk]) int32 on the same device."""
+    T, k = topk_ids.shape
+    rows = moe_rows_max(T, k, E, block)
+    dev = topk_ids.device
+    row_pair = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(rows // block, 1), dtype=torch.int32, device=dev)
+    pair_row = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    _check(load().exl3_moe_align(_dev_ptr(topk_ids.contiguous(), "topk_ids", (torch.int32,)), T, k, E, block,
+                                 row_pair.data_ptr(), block_expert.data_ptr(), pair_row.data_ptr(), _stream()))
+    return row_pair[:rows], block_expert[:rows // block], pair_row[:T * k]
+
+
+def moe_input_transform(x: torch.Tensor, w: MoeWeight, route, topk: int, block: int = 16,
+                        swiglu: bool = False) -> torch.Tensor:
+    row_pair, block_expert, _ = route
+    T = x.shape[0]
+    K = w.K
+    if x.shape[1] != (2 * K if swiglu else K):
+        raise ValueError(f"x has {x.shape[1]} columns, expected {2 * K if swiglu else K}")
+    rows = moe_rows_max(T, topk, w.E, block)
+    out = torch.empty(rot_shape(w.n_shards, rows, K), dtype=torch.float16, device=x.device)
+    _check(load().exl3_moe_input_transform(_dev_ptr(x, "x", (torch.bfloat16, torch.float16)),
+                                           _BF16 if x.dtype == torch.bfloat16 else _F16, int(swiglu), T, K,
+                                           _dev_ptr(w.stack[1], "suh", _H16), w.n_shards, w.E,
+                                           row_pair.data_ptr(), block_expert.data_ptr(), topk, block, rows,
+                                           out.data_ptr(), _stream()))
+    return out
+
+
+def moe_linear(w: MoeWeight, x_rot: torch.Tensor, block_expert: torch.Tensor, block: int = 16,
+               out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    rows = x_rot.shape[2]
+    L = load()
+    need = L.exl3_moe_workspace_bytes(ctypes.byref(w.first.view()), rows, block)
+    if need == 0 and L.exl3_last_error():
+        _check(1)
+    ws, wsn = _workspace(need, x_rot.device)
+    y = torch.empty((rows, w.N), dtype=out_dtype, device=x_rot.device)
+    _check(L.exl3_moe_linear(ctypes.byref(w.first.view()), w.E, _dev_ptr(x_rot, "x_rot", _H16), rows,
+                             _dev_ptr(block_expert, "block_expert", (torch.int32,)), block, y.data_ptr(),
+                             _BF16 if out_dtype == torch.bfloat16 else _F16, ws, wsn, _stream()))
+    return y
+
+
+def moe_combine(y_routed: torch.Tensor, pair_row: torch.Tensor, topk_weights: torch.Tensor) -> torch.Tensor:
+    T, k = topk_weights.shape
+    N = y_routed.shape[1]
+    out = torch.empty((T, N), dtype=y_routed.dtype, device=y_routed.device)
+    _check(load().exl3_moe_combine(_dev_ptr(y_routed, "y_routed", (torch.bfloat16, torch.float16)),
+                                   _BF16 if y_routed.dtype == torch.bfloat16 else _F16,
+                                   _dev_ptr(pair_row, "pair_row", (torch.int32,)),
+                                   _dev_ptr(topk_weights.contiguous(), "topk_weights", (torch.float32,)), T, k, N,
+                                   out.data_ptr(), _stream()))
+    return out
+
+
+def moe_forward(x: torch.Tensor, w: MoeWeight, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                block: int = 16, swiglu: bool = False) -> torch.Tensor:
+    """Routed experts: align, rotate each routed row with its expert's suh,
+    the grouped GEMM, and the ordered combine.  -> [T, N] in x's dtype."""
+    route = moe_align(topk_ids, w.E, block)
+    xr = moe_input_transform(x, w, route, topk_ids.shape[1], block, swiglu)
+    y = moe_linear(w, xr, route[1], block, x.dtype)
+    return moe_combine(y, route[2], topk_weights)

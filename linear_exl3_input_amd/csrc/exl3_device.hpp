@@ -202,15 +202,18 @@ template <bool OUT_BF16>
 __device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *__restrict__ svh,
                                            const uint16_t *__restrict__ bias, uint16_t *__restrict__ yrow, int n0,
                                            int lane) {
-  hadamard128_wave(z0, z1, lane);
+  // Branch-free bias: without one, add -0.0, the exact identity of fp32
+  // addition (+0 + -0 = +0, -0 + -0 = -0), and load svh's word in place of
+  // the bias's (a line already on its way).  The loads go first, so their
+  // latency overlaps the butterfly.
+  const bool has_bias = bias != nullptr;
   const uint32_t sv = *(const uint32_t *)(svh + n0 + 2 * lane);
-  float y0 = keep_f32((z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu));
-  float y1 = keep_f32((z1 * 0.125f) * f16_bits_to_f32(sv >> 16));
-  if (bias != nullptr) {
-    const uint32_t bv = *(const uint32_t *)(bias + n0 + 2 * lane);
-    y0 = keep_f32(y0 + f16_bits_to_f32(bv & 0xFFFFu));
-    y1 = keep_f32(y1 + f16_bits_to_f32(bv >> 16));
-  }
+  const uint32_t bv = *(const uint32_t *)((has_bias ? bias : svh) + n0 + 2 * lane);
+  hadamard128_wave(z0, z1, lane);
+  const float b0 = has_bias ? f16_bits_to_f32(bv & 0xFFFFu) : -0.0f;
+  const float b1 = has_bias ? f16_bits_to_f32(bv >> 16) : -0.0f;
+  const float y0 = keep_f32(keep_f32((z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu)) + b0);
+  const float y1 = keep_f32(keep_f32((z1 * 0.125f) * f16_bits_to_f32(sv >> 16)) + b1);
   uint32_t packed;
   if constexpr (OUT_BF16) packed = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
   else packed = f32_to_f16_bits(y0) | (f32_to_f16_bits(y1) << 16);

@@ -354,7 +354,8 @@ __device__ __forceinline__ void store_partial_coherent(__amdgpu_buffer_rsrc_t rs
 template <int U>
 __device__ __forceinline__ void fold_rows4_coherent(__amdgpu_buffer_rsrc_t rs, int n_slabs, int fq,
                                                     uint32_t slab_stride, int N, int m4, int n0,
-                                                    const GemmParams &p, int64_t row0, int rows, int lane) {
+                                                    const GemmParams &p, const uint16_t *svh, const uint16_t *bias,
+                                                    int64_t row0, int rows, int lane) {
   const uint32_t base = ((uint32_t)m4 * (uint32_t)N + (uint32_t)(n0 + 2 * lane)) * 16u;
   float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
   int iq = 0;
@@ -393,8 +394,8 @@ __device__ __forceinline__ void fold_rows4_coherent(__amdgpu_buffer_rsrc_t rs, i
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i < rows) {
-      if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, p.bias, y + (row0 + i) * N, n0, lane);
-      else output_row<false>(t0[i], t1[i], p.svh, p.bias, y + (row0 + i) * N, n0, lane);
+      if (p.out_bf16) output_row<true>(t0[i], t1[i], svh, bias, y + (row0 + i) * N, n0, lane);
+      else output_row<false>(t0[i], t1[i], svh, bias, y + (row0 + i) * N, n0, lane);
     }
 }
 
@@ -422,8 +423,9 @@ __device__ __forceinline__ bool arrive_last(const GemmParams &p, uint32_t tile, 
 // (first copied) and writes the rows.  The same fp32 adds in the same order as
 // reduce_rows4 (which serves when the items do not fit the LDS).  The
 // tile's counter is reset to zero for the next call.
-__device__ __forceinline__ void finish_tile(const GemmParams &p, uint32_t tile, int nb, int m0, int bm, int wave_all,
-                                            int n_waves, int lane, float *lds, int lds_bytes) {
+__device__ __forceinline__ void finish_tile(const GemmParams &p, const uint16_t *svh, const uint16_t *bias,
+                                            uint32_t tile, int nb, int m0, int bm, int wave_all, int n_waves, int lane,
+                                            float *lds, int lds_bytes) {
   const int rows = p.row_end - p.row_base;
   const int M4 = (rows + 3) >> 2;
   const int N = p.N;
@@ -473,15 +475,15 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, uint32_t tile, 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < nr) {
-          if (p.out_bf16) output_row<true>(t0[i], t1[i], p.svh, p.bias, y + (int64_t)(r0 + i) * N, n0, lane);
-          else output_row<false>(t0[i], t1[i], p.svh, p.bias, y + (int64_t)(r0 + i) * N, n0, lane);
+          if (p.out_bf16) output_row<true>(t0[i], t1[i], svh, bias, y + (int64_t)(r0 + i) * N, n0, lane);
+          else output_row<false>(t0[i], t1[i], svh, bias, y + (int64_t)(r0 + i) * N, n0, lane);
         }
     }
   } else {
     // one wave per 4-row group, slabs in order (reduce_rows4's order)
     for (int r = wave_all; r < r4; r += n_waves)
-      fold_rows4_coherent<4>(rs, n_slabs, fq, slab_stride, N, m4_0 + r, n0, p, m0 + 4 * r, min(4, p.row_end - (m0 + 4 * r)),
-                          lane);
+      fold_rows4_coherent<4>(rs, n_slabs, fq, slab_stride, N, m4_0 + r, n0, p, svh, bias, m0 + 4 * r,
+                             min(4, p.row_end - (m0 + 4 * r)), lane);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -522,7 +524,7 @@ struct SmallGeom {
 // wait only for LDS operations; the loads are waited for by count.  The
 // quads' part sums are then folded in part order through LDS.  Rows past the
 // launch's last row load that row (finite, never stored).
-template <int BITS, uint32_t CB, int MT, bool MULTI, int QD, int QW>
+template <int BITS, uint32_t CB, int MT, bool MULTI, int QD, int QW, bool MOE>
 __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) {
   using S = SmallGeom<BITS, MT, QW>;
   constexpr int BM = S::BM;
@@ -558,6 +560,18 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
   const int NT = N >> 4;
   const int KB = K >> 7;
 
+  // Grouped (MoE) calls: the row block's expert selects its trellis, svh
+  // and bias (experts stacked at fixed strides); a block of no expert (-1)
+  // has nothing to compute, for every workgroup of its tiles alike.
+  const uint16_t *trellis = p.trellis, *svh = p.svh, *bias = p.bias;
+  if constexpr (MOE) {
+    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[m0 / BM]);
+    if (e < 0) return;
+    trellis += (int64_t)e * p.expert_trellis;
+    svh += (int64_t)e * N;
+    if (bias != nullptr) bias += (int64_t)e * N;
+  }
+
   const int u0 = blockIdx.y * p.unit;  // first part of the workgroup's unit
   const int p_begin = QD > 1 ? u0 + qd : u0;
   const int p_end = QD > 1 ? p_begin + 1 : u0 + p.unit;
@@ -570,7 +584,7 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
   const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
 
   // load sources: 16-bit word offsets from the stage bases
-  const uint16_t *const t_base = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8 + c0 / 16) * (16 * BITS);
+  const uint16_t *const t_base = trellis + ((int64_t)kb_begin * 8 * NT + nb * 8 + c0 / 16) * (16 * BITS);
   const int64_t t_stage = (int64_t)8 * NT * (16 * BITS);
   uint32_t t_src[T_OPS];
 #pragma unroll
@@ -749,7 +763,7 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
     // the tile is the 128-column block: both halves' workgroups arrive
     const uint32_t tile = blockIdx.z * (gridDim.x * QW / 4) + nb;
     if (!arrive_last(p, tile, gridDim.y * (4 / QW))) return;
-    finish_tile(p, tile, nb, m0, BM, wave_all, QW * QD, lane, z, LDS_DW * 4);
+    finish_tile(p, svh, bias, tile, nb, m0, BM, wave_all, QW * QD, lane, z, LDS_DW * 4);
     return;
   }
 
@@ -773,8 +787,8 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
     if (row >= rend) break;
     const float z0 = z[r * Z_ROW + 2 * lane];
     const float z1 = z[r * Z_ROW + 2 * lane + 1];
-    if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
-    else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
+    if (p.out_bf16) output_row<true>(z0, z1, svh, bias, y + (int64_t)row * N, nb * 128, lane);
+    else output_row<false>(z0, z1, svh, bias, y + (int64_t)row * N, nb * 128, lane);
   }
   }
 }
@@ -1124,6 +1138,16 @@ __global__ __launch_bounds__(WG_THREADS) void decode_rate_kernel(const DecodePar
 
 // ---------------------------------------------------------------- launchers
 
+// One small-tile instance; the grouped (MoE) variant when the call routes
+// row blocks to experts.
+template <int BITS, uint32_t CB, int MT, bool MULTI, int QD, int QW>
+void launch_small(const GemmParams &p, dim3 grid, hipStream_t s) {
+  if (p.block_expert != nullptr)
+    hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, MULTI, QD, QW, true>), grid, dim3(64 * QW * QD), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, MULTI, QD, QW, false>), grid, dim3(64 * QW * QD), 0, s, p);
+}
+
 // quads > 1: one part per quad (no register fold); otherwise `multi` folds
 // the workgroup's parts in registers.  half: 64-column workgroups (quads of
 // two waves; slab mode only, no register fold).
@@ -1132,20 +1156,20 @@ hipError_t launch_gemm_t(int quads, bool half, bool multi, const GemmParams &p, 
   if (half) {
     if (multi || !p.slab_mode) return hipErrorInvalidValue;
     switch (quads) {
-      case 1: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 1, 2>), grid, dim3(128), 0, s, p); break;
-      case 2: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 2, 2>), grid, dim3(256), 0, s, p); break;
-      case 4: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 4, 2>), grid, dim3(512), 0, s, p); break;
+      case 1: launch_small<BITS, CB, MT, false, 1, 2>(p, grid, s); break;
+      case 2: launch_small<BITS, CB, MT, false, 2, 2>(p, grid, s); break;
+      case 4: launch_small<BITS, CB, MT, false, 4, 2>(p, grid, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (quads) {
     case 1:
-      if (multi) hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, true, 1, 4>), grid, dim3(WG_THREADS), 0, s, p);
-      else hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 1, 4>), grid, dim3(WG_THREADS), 0, s, p);
+      if (multi) launch_small<BITS, CB, MT, true, 1, 4>(p, grid, s);
+      else launch_small<BITS, CB, MT, false, 1, 4>(p, grid, s);
       break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 2, 4>), grid, dim3(2 * WG_THREADS), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<BITS, CB, MT, false, 4, 4>), grid, dim3(4 * WG_THREADS), 0, s, p); break;
+    case 2: launch_small<BITS, CB, MT, false, 2, 4>(p, grid, s); break;
+    case 4: launch_small<BITS, CB, MT, false, 4, 4>(p, grid, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

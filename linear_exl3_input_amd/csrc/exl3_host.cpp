@@ -331,7 +331,7 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
 
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
-                       bool with_output);
+                       bool with_output, const int32_t *block_expert = nullptr, int64_t expert_trellis = 0);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -581,9 +581,11 @@ namespace {
 // the plan has the finisher, else as a second kernel).
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
-                       bool with_output) {
+                       bool with_output, const int32_t *block_expert, int64_t expert_trellis) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
+  p.block_expert = block_expert;
+  p.expert_trellis = expert_trellis;
   p.trellis = w->trellis;
   p.x_rot = x_rot;
   p.svh = w->svh;
@@ -788,6 +790,160 @@ exl3_status exl3_tune(const exl3_weight *ws, int32_t n_w, const uint16_t *x_rot,
     best->workspace = win.workspace;
   }
   return EXL3_OK;
+}
+
+// ------------------------------------------------------ mixture of experts
+
+int32_t exl3_moe_rows_max(int32_t T, int32_t topk, int32_t E, int32_t block) {
+  if (T < 0 || topk < 1 || E < 1 || block < 1) return 0;
+  const int64_t pairs = (int64_t)T * topk;
+  const int64_t rows = pairs + std::min<int64_t>(E, pairs) * (block - 1);
+  const int64_t r = (rows + block - 1) / block * block;
+  return r > MAX_M ? 0 : (int32_t)r;
+}
+
+exl3_status exl3_moe_align(const int32_t *topk_ids, int32_t T, int32_t topk, int32_t E, int32_t block,
+                           int32_t *row_pair, int32_t *block_expert, int32_t *pair_row, void *stream) {
+  clear_error();
+  if (T < 0 || topk < 1 || topk > 64) return fail(EXL3_ERR_INVALID_ARG, "T=%d topk=%d: T >= 0, topk 1..64", T, topk);
+  if (E < 1 || E > 4096) return fail(EXL3_ERR_INVALID_ARG, "E=%d experts, must be 1..4096", E);
+  if (block != 16 && block != 32 && block != 64)
+    return fail(EXL3_ERR_INVALID_ARG, "block=%d rows, must be 16, 32 or 64 (a tile of the grouped GEMM)", block);
+  const int32_t rows = exl3_moe_rows_max(T, topk, E, block);
+  if (T > 0 && rows == 0)
+    return fail(EXL3_ERR_UNSUPPORTED, "%d tokens x %d experts each need more than %d routed rows", T, topk, MAX_M);
+  if (T == 0) return EXL3_OK;
+  exl3_status st;
+  if ((st = check_ptr(topk_ids, "topk_ids")) != EXL3_OK) return st;
+  if ((st = check_ptr(row_pair, "row_pair")) != EXL3_OK) return st;
+  if ((st = check_ptr(block_expert, "block_expert")) != EXL3_OK) return st;
+  if ((st = check_ptr(pair_row, "pair_row")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_moe_align(topk_ids, T * topk, E, block, rows, row_pair, block_expert, pair_row,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "moe align launch");
+}
+
+exl3_status exl3_moe_input_transform(const void *x, int32_t x_dtype, int32_t swiglu, int32_t T, int32_t K,
+                                     const uint16_t *suh, int32_t n_shards, int32_t E, const int32_t *row_pair,
+                                     const int32_t *block_expert, int32_t topk, int32_t block, int32_t rows,
+                                     uint16_t *x_rot, void *stream) {
+  clear_error();
+  if (x_dtype != EXL3_F16 && x_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "x_dtype=%d, must be 0 (fp16) or 1 (bf16)", x_dtype);
+  if (K <= 0 || K % 128 != 0 || K > MAX_KN)
+    return fail(EXL3_ERR_INVALID_ARG, "K=%d must be a positive multiple of 128 up to %d", K, MAX_KN);
+  if (n_shards < 1 || n_shards > EXL3_MAX_SHARDS)
+    return fail(EXL3_ERR_INVALID_ARG, "n_shards=%d, must be 1..%d", n_shards, EXL3_MAX_SHARDS);
+  if (E < 1 || E > 4096) return fail(EXL3_ERR_INVALID_ARG, "E=%d experts, must be 1..4096", E);
+  if (block != 16 && block != 32 && block != 64) return fail(EXL3_ERR_INVALID_ARG, "block=%d, must be 16, 32 or 64", block);
+  if (T < 0 || topk < 1) return fail(EXL3_ERR_INVALID_ARG, "T=%d topk=%d", T, topk);
+  if (rows != exl3_moe_rows_max(T, topk, E, block))
+    return fail(EXL3_ERR_INVALID_ARG, "rows=%d, the routed buffers of %d tokens x %d of %d experts in blocks of %d "
+                "have %d", rows, T, topk, E, block, exl3_moe_rows_max(T, topk, E, block));
+  if (T == 0) return EXL3_OK;
+  exl3_status st;
+  if ((st = check_ptr(x, "x")) != EXL3_OK) return st;
+  if ((st = check_ptr(suh, "suh")) != EXL3_OK) return st;
+  if ((st = check_ptr(row_pair, "row_pair")) != EXL3_OK) return st;
+  if ((st = check_ptr(block_expert, "block_expert")) != EXL3_OK) return st;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_input_transform(x, x_dtype == EXL3_BF16, swiglu != 0, rows, K, suh, n_shards,
+                                                    x_rot, (hipStream_t)stream, row_pair, block_expert, topk, block);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "moe input transform launch");
+}
+
+}  // extern "C"
+
+namespace {
+// The grouped GEMM's plan: the shape's own tree on the ALU tiles with
+// block-row tiles, with the output stage in the GEMM (fused, or the
+// finishing workgroup): a separate output kernel would need each block's
+// svh.
+exl3_status moe_plan(const exl3_weight *w, int32_t rows, int32_t block, Plan *pl) {
+  exl3_plan f;
+  f.parts = -1;
+  f.groups = -1;
+  f.mode = EXL3_MODE_AUTO;
+  f.bm = block;
+  f.decoder = EXL3_DECODER_ALU;
+  f.unit = -1;
+  f.launches = 0;
+  f.wg_cols = -1;
+  f.workspace = 0;
+  exl3_status st = make_plan(w, rows, &f, pl);
+  if (st != EXL3_OK) return st;
+  if (pl->mode == EXL3_MODE_SLABS && !pl->finisher) {
+    f.mode = EXL3_MODE_FUSED;
+    if (make_plan(w, rows, &f, pl) != EXL3_OK)
+      return fail(EXL3_ERR_UNSUPPORTED, "%d routed rows in blocks of %d: more tiles than the finishing counters "
+                  "hold and no fused schedule for this tree; route fewer rows per call", rows, block);
+  }
+  return EXL3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t exl3_moe_workspace_bytes(const exl3_weight *w, int32_t rows, int32_t block) {
+  clear_error();
+  if (validate_weight(w, false, false) != EXL3_OK) return 0;
+  if (rows < 0 || rows > MAX_M || (block != 16 && block != 32 && block != 64) || rows % block != 0) {
+    fail(EXL3_ERR_INVALID_ARG, "rows=%d block=%d: rows a multiple of block (16, 32 or 64)", rows, block);
+    return 0;
+  }
+  Plan pl;
+  if (moe_plan(w, rows, block, &pl) != EXL3_OK) return 0;
+  return pl.workspace;
+}
+
+exl3_status exl3_moe_linear(const exl3_weight *w, int32_t E, const uint16_t *x_rot, int32_t rows,
+                            const int32_t *block_expert, int32_t block, void *y, int32_t y_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, true);
+  if (st != EXL3_OK) return st;
+  if (E < 1 || E > 4096) return fail(EXL3_ERR_INVALID_ARG, "E=%d experts, must be 1..4096", E);
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (block != 16 && block != 32 && block != 64) return fail(EXL3_ERR_INVALID_ARG, "block=%d, must be 16, 32 or 64", block);
+  if (rows < 0 || rows > MAX_M || rows % block != 0)
+    return fail(EXL3_ERR_INVALID_ARG, "rows=%d must be a multiple of block=%d (remainder %d)", rows, block,
+                rows >= 0 ? rows % block : rows);
+  Plan pl;
+  if ((st = moe_plan(w, rows, block, &pl)) != EXL3_OK) return st;
+  if (rows == 0) return EXL3_OK;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  if ((st = check_ptr(block_expert, "block_expert")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  if (pl.workspace > 0) {
+    if (workspace == nullptr || workspace_bytes < pl.workspace)
+      return fail(EXL3_ERR_WORKSPACE, "workspace of %zu bytes; this plan needs %zu (short by %zu)", workspace_bytes,
+                  pl.workspace, pl.workspace > workspace_bytes ? pl.workspace - workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(EXL3_ERR_INVALID_ARG, "workspace=%p is not 16-byte aligned", workspace);
+  }
+  uint32_t *counters = static_cast<uint32_t *>(workspace);
+  float *slabs = pl.workspace > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.slab_off) : nullptr;
+  const int64_t expert_words = (int64_t)w->K / 16 * (w->N / 16) * 16 * w->bits;
+  return run_linear(w, x_rot, rows, y, y_dtype, counters, slabs, nullptr, pl, (hipStream_t)stream, true, block_expert,
+                    expert_words);
+}
+
+exl3_status exl3_moe_combine(const void *y_routed, int32_t dtype, const int32_t *pair_row, const float *topk_weights,
+                             int32_t T, int32_t topk, int32_t N, void *out, void *stream) {
+  clear_error();
+  if (dtype != EXL3_F16 && dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "dtype=%d, must be 0 (fp16) or 1 (bf16)", dtype);
+  if (T < 0 || topk < 1 || topk > 64) return fail(EXL3_ERR_INVALID_ARG, "T=%d topk=%d: T >= 0, topk 1..64", T, topk);
+  if (N <= 0 || N % 2 != 0) return fail(EXL3_ERR_INVALID_ARG, "N=%d must be positive and even", N);
+  if (T == 0) return EXL3_OK;
+  exl3_status st;
+  if ((st = check_ptr(y_routed, "y_routed")) != EXL3_OK) return st;
+  if ((st = check_ptr(pair_row, "pair_row")) != EXL3_OK) return st;
+  if ((st = check_ptr(topk_weights, "topk_weights")) != EXL3_OK) return st;
+  if ((st = check_ptr(out, "out")) != EXL3_OK) return st;
+  const hipError_t e = exl3::launch_moe_combine(y_routed, dtype == EXL3_BF16, pair_row, topk_weights, T, topk, N, out,
+                                                (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "moe combine launch");
 }
 
 exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_t M, float *z_parts,

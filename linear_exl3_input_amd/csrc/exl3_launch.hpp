@@ -14,7 +14,6 @@ struct GemmParams {
   const uint16_t *x_rot;    // [n_shards][K/32][M][32] fp16 bits (k-step tiles)
   const uint16_t *svh;      // [N] fp16 bits
   const uint16_t *dense;    // dense path: W_q as B fragments (dequant_kernel order)
-  const uint16_t *bias;     // [N] fp16 added before the output rounding, or null
   void *y;                  // [M][N] bf16/fp16
   float *slabs;             // [units][ceil(rows/4)][N][4] fp32 (slab mode)
   uint32_t *counters;       // slab mode: per-tile arrival counters (zero on
@@ -32,6 +31,10 @@ struct GemmParams {
   int32_t out_bf16;
   int32_t n_shards;
   int32_t shard_end_blk[MAX_SHARDS];  // exclusive end of shard s, in 128-col blocks
+  // (appended last: the fields above keep their argument offsets)
+  const uint16_t *bias;         // [N] fp16 added before the output rounding, or null
+  const int32_t *block_expert;  // grouped (MoE) calls: expert of each row block (-1: none), else null
+  int64_t expert_trellis;       // grouped calls: trellis words per expert
 };
 
 struct DecodeParams {
@@ -58,8 +61,17 @@ hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hi
 
 // swiglu: x is the gate_up output [M][2K]; the rotated value is
 // rne_dtype(silu(gate) * up) (see input_transform_kernel).
+// row_pair / block_expert (may be null): routed rows, see Route in exl3_misc.hip.
 hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32_t M, int32_t K,
-                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s);
+                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s,
+                                  const int32_t *row_pair = nullptr, const int32_t *block_expert = nullptr,
+                                  int32_t topk = 1, int32_t block = 16);
+// MoE routing: alignment of (token, expert) pairs into row blocks, and the
+// ordered combine of each token's routed rows (exl3_moe.hip).
+hipError_t launch_moe_align(const int32_t *topk_ids, int32_t pairs, int32_t E, int32_t block, int32_t rows_max,
+                            int32_t *row_pair, int32_t *block_expert, int32_t *pair_row, hipStream_t s);
+hipError_t launch_moe_combine(const void *y_routed, bool bf16, const int32_t *pair_row, const float *weights,
+                              int32_t T, int32_t topk, int32_t N, void *out, hipStream_t s);
 // Ordered sum of n_slabs partial slabs (groups of fold_q consecutive slabs
 // folded first, then the groups in order) + output transform, for rows
 // [row_base, row_end) (slab row r = row row_base + r).

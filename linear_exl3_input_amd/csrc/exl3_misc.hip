@@ -99,11 +99,20 @@ __device__ __forceinline__ float swiglu_act(uint32_t gbits, uint32_t ubits) {
   return X_BF16 ? bf16_bits_to_f32(f32_to_bf16_bits(a)) : f16_bits_to_f32(f32_to_f16_bits(a));
 }
 
-template <bool X_BF16, bool SWIGLU>
+// Routed rows (MoE): row m of x~ is the row of pair p = route.row_pair[m]
+// (token p / topk of x; -1: a padding row, rotated as zeros), with the suh
+// rows of its block's expert (suh + expert * n_shards * K).
+struct Route {
+  const int32_t *row_pair;      // null: row m is x's row m
+  const int32_t *block_expert;
+  int32_t topk, block;
+};
+
+template <bool X_BF16, bool SWIGLU, bool ROUTED>
 __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ suh,
                                                               uint16_t *__restrict__ x_rot, int32_t M,
-                                                              int32_t K, int32_t n_shards) {
+                                                              int32_t K, int32_t n_shards, Route route) {
   const int lane = threadIdx.x & 63;
   const int L = lane & 15;
   const int kblocks = K >> 7;
@@ -130,11 +139,21 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
   }
   const int j = L >> 2, q = L & 3;
   const int k0 = kb * 128 + 32 * j + 16 * (q >> 1) + 4 * (q & 1);  // the lane's first k; the second run at k0 + 8
+  int64_t src = m;  // x's row
+  const uint16_t *suh_e = suh;
+  bool zero = false;
+  if (ROUTED && live) {
+    const int32_t pr = route.row_pair[m];
+    const int32_t e = route.block_expert[m / route.block];
+    zero = pr < 0 || e < 0;
+    src = zero ? 0 : pr / route.topk;
+    suh_e = suh + (int64_t)(zero ? 0 : e) * n_shards * K;
+  }
   float xv[8];
   if constexpr (SWIGLU) {
     u32x2_t glo = {0u, 0u}, ghi = {0u, 0u}, ulo = {0u, 0u}, uhi = {0u, 0u};
-    if (live) {
-      const uint16_t *row = x + m * 2 * K;
+    if (live && !zero) {
+      const uint16_t *row = x + src * 2 * K;
       glo = *(const u32x2_t *)(row + k0);
       ghi = *(const u32x2_t *)(row + k0 + 8);
       ulo = *(const u32x2_t *)(row + K + k0);
@@ -149,9 +168,9 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
     }
   } else {
     u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
-    if (live) {
-      lo = *(const u32x2_t *)(x + m * K + k0);
-      hi = *(const u32x2_t *)(x + m * K + k0 + 8);
+    if (live && !zero) {
+      lo = *(const u32x2_t *)(x + src * K + k0);
+      hi = *(const u32x2_t *)(x + src * K + k0 + 8);
     }
     const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
@@ -161,8 +180,8 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
     }
   }
   for (int s = 0; s < n_shards; ++s) {
-    const u32x2_t slo = *(const u32x2_t *)(suh + (int64_t)s * K + k0);
-    const u32x2_t shi = *(const u32x2_t *)(suh + (int64_t)s * K + k0 + 8);
+    const u32x2_t slo = *(const u32x2_t *)(suh_e + (int64_t)s * K + k0);
+    const u32x2_t shi = *(const u32x2_t *)(suh_e + (int64_t)s * K + k0 + 8);
     const uint32_t sw[4] = {slo.x, slo.y, shi.x, shi.y};
     float t[8];
 #pragma unroll
@@ -190,19 +209,25 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
 }
 
 hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32_t M, int32_t K,
-                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s) {
+                                  const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s,
+                                  const int32_t *row_pair, const int32_t *block_expert, int32_t topk,
+                                  int32_t block) {
   const int64_t items = M >= 4 ? (((int64_t)M + 3) / 4) * (K / 128) : (int64_t)M * ((K / 128 + 3) / 4);
   const dim3 grid((unsigned)((items + 3) / 4));
   const uint16_t *xp = static_cast<const uint16_t *>(x);
-  if (x_bf16 && swiglu)
-    hipLaunchKernelGGL((input_transform_kernel<true, true>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K, n_shards);
-  else if (x_bf16)
-    hipLaunchKernelGGL((input_transform_kernel<true, false>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K, n_shards);
-  else if (swiglu)
-    hipLaunchKernelGGL((input_transform_kernel<false, true>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K, n_shards);
-  else
-    hipLaunchKernelGGL((input_transform_kernel<false, false>), grid, dim3(256), 0, s, xp, suh, x_rot, M, K,
-                       n_shards);
+  const Route r{row_pair, block_expert, topk, block};
+  const dim3 b(256);
+  const int sel = (x_bf16 ? 4 : 0) | (swiglu ? 2 : 0) | (row_pair != nullptr ? 1 : 0);
+  switch (sel) {
+    case 0: hipLaunchKernelGGL((input_transform_kernel<false, false, false>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    case 1: hipLaunchKernelGGL((input_transform_kernel<false, false, true>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    case 2: hipLaunchKernelGGL((input_transform_kernel<false, true, false>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    case 3: hipLaunchKernelGGL((input_transform_kernel<false, true, true>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    case 4: hipLaunchKernelGGL((input_transform_kernel<true, false, false>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    case 5: hipLaunchKernelGGL((input_transform_kernel<true, false, true>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    case 6: hipLaunchKernelGGL((input_transform_kernel<true, true, false>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+    default: hipLaunchKernelGGL((input_transform_kernel<true, true, true>), grid, b, 0, s, xp, suh, x_rot, M, K, n_shards, r); break;
+  }
   return hipGetLastError();
 }
 
@@ -220,7 +245,7 @@ template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t n_slabs,
                                                        int32_t fold_q, int32_t row_base, int32_t row_end,
                                                        int32_t N, const uint16_t *__restrict__ svh,
-                                                       const uint16_t *__restrict__ bias, uint16_t *__restrict__ y) {
+                                                       uint16_t *__restrict__ y, const uint16_t *__restrict__ bias) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nblocks = N >> 7;
@@ -241,10 +266,10 @@ hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, 
   const dim3 grid((unsigned)((items + 3) / 4));
   if (out_bf16)
     hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end, N,
-                       svh, bias, (uint16_t *)y);
+                       svh, (uint16_t *)y, bias);
   else
     hipLaunchKernelGGL((epilogue_kernel<false>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end,
-                       N, svh, bias, (uint16_t *)y);
+                       N, svh, (uint16_t *)y, bias);
   return hipGetLastError();
 }
 

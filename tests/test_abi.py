@@ -339,3 +339,19 @@ def test_bias_and_swiglu_transform_checks():
     assert L.exl3_input_transform_swiglu(None, 1, 4, 128, FAKE, 1, FAKE, None) == 1
     assert "gate_up is NULL" in last_error()
     assert L.exl3_input_transform_swiglu(FAKE, 1, 0, 128, FAKE, 1, FAKE, None) == 0  # no rows: nothing to do
+
+
+def test_moe_entry_points_check_arguments():
+    L = ex.load()
+    assert L.exl3_moe_rows_max(3, 2, 3, 16) == 64 and L.exl3_moe_rows_max(0, 2, 3, 16) == 0
+    assert L.exl3_moe_rows_max(1000, 8, 256, 16) == ((8000 + 256 * 15 + 15) // 16) * 16
+    assert L.exl3_moe_align(FAKE, 4, 2, 8, 24, FAKE, FAKE, FAKE, None) == 1
+    assert "block=24" in last_error()
+    assert L.exl3_moe_align(FAKE, 4, 2, 5000, 16, FAKE, FAKE, FAKE, None) == 1
+    w = view(1024, (256,), 4, 1)
+    assert L.exl3_moe_linear(ctypes.byref(w), 4, FAKE, 40, FAKE, 16, FAKE, 1, FAKE, 1 << 30, None) == 1
+    assert "multiple of block=16" in last_error()
+    assert L.exl3_moe_workspace_bytes(ctypes.byref(w), 64, 16) > 0
+    assert L.exl3_moe_input_transform(FAKE, 1, 0, 3, 1024, FAKE, 1, 3, FAKE, FAKE, 2, 16, 48, FAKE, None) == 1
+    assert "rows=48" in last_error()  # 3 tokens x 2 of 3 experts in blocks of 16: 64 routed rows
+    assert L.exl3_moe_combine(FAKE, 1, FAKE, FAKE, 2, 2, 7, FAKE, None) == 1
