@@ -1,6 +1,5 @@
 """Oracle for the routed-expert path (test infrastructure only: imported by
-tests, the entry's smoke check and the bench's CPU baseline, never by the
-library).
+the tests, never by the library).
 
 cuda-exl3 README, "What is supported": the (token, expert) pairs are sorted
 by expert and each expert's run padded to whole row blocks, so every block
