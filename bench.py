@@ -46,6 +46,10 @@ WORKLOADS = {
     "lm_head_4096x154880_b6_mul1": (["lm_head_4096x154880_b6_mul1"], (1, 16, 512)),
 }
 DEFAULT_WORKLOAD = "expert_4096x2048+2048x4096_b4_mcg"
+# Routed experts (grouped GEMM): the expert pair's shapes, 64 experts each,
+# top-8 synthetic routing, T tokens per call.
+MOE_WORKLOADS = {"moe_e64_top8_4096x2048+2048x4096_b4_mcg":
+                 (["expert_4096x2048_b4_mcg", "expert_2048x4096_b4_mcg"], 64, 8, (1, 16, 64))}
 
 KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_gemm_lut.hpp", "exl3_gemm_dense.hpp", "exl3_device.hpp",
                   "exl3_misc.hip"]
@@ -138,7 +142,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(MOE_WORKLOADS))
     ap.add_argument("--pool-mb", type=int, default=640, help="weight pool size (defeats the 256 MB cache)")
     ap.add_argument("--timing-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,6 +170,8 @@ def main():
     ex.load()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in MOE_WORKLOADS:
+        return moe_main(args, ex, wl, torch, np, dev)
     if args.copy_calibration:
         n = args.copy_calibration * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -444,6 +450,93 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(out + "\n")
+
+
+def moe_main(args, ex, wl, torch, np, dev):
+    """Routed experts: per layer and token count T, one call = alignment,
+    routed input rotation, grouped GEMM and ordered combine.  Routings are
+    drawn per call from a pool of 32 (so the experts touched change and
+    stream from HBM); SoL = max(trellis bytes of the distinct experts the
+    call touches / HBM, 2 * T * topk * K * N / MFMA peak)."""
+    names, E, k, Ts = MOE_WORKLOADS[args.workload]
+    layers = [wl.layer(n) for n in names]
+    rng = np.random.default_rng(20269000)
+    per = []
+    stream = torch.cuda.Stream()
+    spin = getattr(torch.cuda, "_sleep", None)
+
+    def time_calls(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for r in range(2):  # warm-up: first launches load the kernels
+            fn(r)
+        torch.cuda.synchronize()
+        if spin is not None:
+            spin(int(1e7))
+        e0.record(stream)
+        for r in range(reps):
+            fn(r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def d(a, dt=torch.int16):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+
+    sol_step, rows_out = 0.0, []
+    with torch.cuda.stream(stream):
+        for lay in layers:
+            tr = rng.integers(0, 65536, (E, lay.K // 16, lay.N // 16, 16 * lay.bits), dtype=np.uint16)
+            suh = np.where(rng.integers(0, 2, (E, 1, lay.K)) == 1, 0xBC00, 0x3C00).astype(np.uint16)
+            svh = np.where(rng.integers(0, 2, (E, lay.N)) == 1, 0xBC00, 0x3C00).astype(np.uint16)
+            w = ex.MoeWeight(d(tr), d(suh, torch.float16), d(svh, torch.float16), lay.bits, lay.codebook)
+            del tr
+            for T in Ts:
+                pool = [np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+                        for _ in range(32)]
+                ids = [torch.from_numpy(a).to(dev) for a in pool]
+                wts = [torch.from_numpy(rng.dirichlet(np.ones(k), T).astype(np.float32)).to(dev) for _ in pool]
+                x = d(wl.round_f32_to_bf16_bits(rng.standard_normal((T, lay.K)).astype(np.float32)), torch.bfloat16)
+                t_call = time_calls(lambda r: ex.moe_forward(x, w, ids[r % 32], wts[r % 32]), args.timing_reps)
+                routes = [ex.moe_align(i, E) for i in ids]
+                xrs = [ex.moe_input_transform(x, w, rt, k) for rt in routes]
+                t_gemm = time_calls(lambda r: ex.moe_linear(w, xrs[r % 32], routes[r % 32][1]), args.timing_reps)
+                touched = float(np.mean([len(np.unique(a)) for a in pool]))
+                byts = touched * lay.weight_bytes()
+                flops = 2.0 * T * k * lay.K * lay.N
+                sol = max(byts / HBM_BPS, flops / MFMA_F16_FLOPS)
+                sol_step += sol
+                per.append({"layer": lay.name, "experts": E, "topk": k, "T": T, "experts_touched": touched,
+                            "call_us": round(t_call, 3), "grouped_gemm_us": round(t_gemm, 3),
+                            "GBps": round(byts / (t_gemm * 1e-6) / 1e9, 1),
+                            "TFLOPS": round(flops / (t_gemm * 1e-6) / 1e12, 2),
+                            "pct_sol_call": round(100 * sol / (t_call * 1e-6), 2),
+                            "pct_sol_gemm": round(100 * sol / (t_gemm * 1e-6), 2)})
+                log(f"moe {lay.name} E={E} top{k} T={T}: {touched:.1f} experts touched, call {t_call:.2f} us, "
+                    f"grouped GEMM {t_gemm:.2f} us ({per[-1]['GBps']} GB/s, {per[-1]['pct_sol_gemm']}% SoL)")
+            del w
+    step_us = sum(p_["call_us"] for p_ in per)
+    gemm = sum(p_["grouped_gemm_us"] for p_ in per)
+    byts = sum(p_["experts_touched"] * wl.layer(p_["layer"]).weight_bytes() for p_ in per)
+    line = {
+        "metric": "EXL3 linear achieved GB/s + TFLOPS and %SoL vs max(HBM,MFMA) per (M,K,N,bits)",
+        "value": round(100.0 * sol_step / (step_us * 1e-6), 3),
+        "unit": "% of SoL (aggregate over the routed calls)",
+        "n_gpus": 1, "steps": args.timing_reps, "warmup": 2, "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded uniform trellis, +-1 suh/svh, N(0,1) bf16 x, uniform top-k routing)",
+        "config": {"workload": args.workload, "experts": E, "topk": k, "T": list(Ts),
+                   "layers": [{"K": l.K, "N": l.N, "bits": l.bits, "codebook": l.codebook} for l in layers],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(byts / (gemm * 1e-6) / 1e9, 1), "peak": HBM_BPS / 1e9,
+                     "unit": "GB/s", "frac": round(byts / (gemm * 1e-6) / HBM_BPS, 4), "traffic": None,
+                     "kernel": "exl3::gemm_kernel<4, 1u, 1, ..., true> (grouped)",
+                     "work_per_launch": "trellis bytes of the experts the call touches"},
+        "per_shape": per,
+    }
+    print(json.dumps(line), flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(json.dumps(line) + "\n")
 
 
 if __name__ == "__main__":
