@@ -1,6 +1,7 @@
 // Input rotation, ordered split-k output stage and the codebook hook.
 #include "exl3_device.hpp"
 #include "exl3_launch.hpp"
+#include <type_traits>
 
 namespace exl3 {
 
@@ -240,8 +241,12 @@ hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32
 // the four rows of one column are 16 contiguous bytes, which is what a GEMM
 // lane holds for one output column, so both the GEMM's stores and these
 // loads move whole cache lines.  One wave per (4-row group, 128-column
-// block) of rows [row_base, row_end).
-template <bool OUT_BF16>
+// block) of rows [row_base, row_end).  U slabs' loads are in flight per round
+// trip.  A launch of at most 64 rows has a few waves per column block, each
+// waiting out its trips one after another: the launcher picks the smallest
+// of 8, 16, 24 that covers every slab (one trip up to 24 slabs).  Larger
+// launches are bandwidth-bound and keep U = 8 and more waves per SIMD.
+template <bool OUT_BF16, int U>
 __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__ slabs, int32_t n_slabs,
                                                        int32_t fold_q, int32_t row_base, int32_t row_end,
                                                        int32_t N, const uint16_t *__restrict__ svh,
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(const float *__restrict__
   const int64_t m4 = item / nblocks;
   const int n0 = (int)(item - m4 * nblocks) * 128;
   const int64_t r0 = 4 * m4;
-  reduce_rows4<OUT_BF16>(slabs, n_slabs, fold_q, (int64_t)M4 * N * 4, N, m4, n0, svh, bias, y, row_base + r0,
+  reduce_rows4<OUT_BF16, U>(slabs, n_slabs, fold_q, (int64_t)M4 * N * 4, N, m4, n0, svh, bias, y, row_base + r0,
                          (int)min((int64_t)4, rows - r0), lane);
 }
 
@@ -264,12 +269,18 @@ hipError_t launch_epilogue(const float *slabs, int32_t n_slabs, int32_t fold_q, 
                            hipStream_t s) {
   const int64_t items = (int64_t)((row_end - row_base + 3) / 4) * (N / 128);
   const dim3 grid((unsigned)((items + 3) / 4));
-  if (out_bf16)
-    hipLaunchKernelGGL((epilogue_kernel<true>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end, N,
-                       svh, (uint16_t *)y, bias);
-  else
-    hipLaunchKernelGGL((epilogue_kernel<false>), grid, dim3(256), 0, s, slabs, n_slabs, fold_q, row_base, row_end,
-                       N, svh, (uint16_t *)y, bias);
+  auto go = [&](auto bf16_c, auto u_c) {
+    hipLaunchKernelGGL((epilogue_kernel<decltype(bf16_c)::value, decltype(u_c)::value>), grid, dim3(256), 0, s, slabs,
+                       n_slabs, fold_q, row_base, row_end, N, svh, (uint16_t *)y, bias);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using U8 = std::integral_constant<int, 8>;
+  using U16 = std::integral_constant<int, 16>;
+  using U24 = std::integral_constant<int, 24>;
+  if (n_slabs <= 8 || row_end - row_base > 64) out_bf16 ? go(T{}, U8{}) : go(F{}, U8{});
+  else if (n_slabs <= 16) out_bf16 ? go(T{}, U16{}) : go(F{}, U16{});
+  else out_bf16 ? go(T{}, U24{}) : go(F{}, U24{});
   return hipGetLastError();
 }
 

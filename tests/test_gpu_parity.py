@@ -78,7 +78,8 @@ def test_input_transform_one_hot_closed_form():
 
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("P,G,M,N", [(1, 1, 3, 128), (3, 3, 17, 384), (8, 8, 64, 256), (8, 2, 9, 256),
-                                     (12, 3, 5, 128)])
+                                     (12, 3, 5, 128), (16, 16, 7, 128), (17, 17, 1, 256), (20, 4, 64, 128),
+                                     (24, 8, 65, 128)])
 def test_output_stage_bit_exact(out_dtype, P, G, M, N):
     banner(f"epilogue {out_dtype} P={P} G={G} M={M} N={N}")
     rng = np.random.default_rng(2000 + P + M + N)
