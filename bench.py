@@ -44,6 +44,9 @@ WORKLOADS = {
                                (1, 8, 16, 24, 32, 64, 128, 256, 512)),
     "gate_up_5120x2x17408_b5_mul1": (["gate_up_5120x2x17408_b5_mul1"], (16, 128, 2048, 4096)),
     "lm_head_4096x154880_b6_mul1": (["lm_head_4096x154880_b6_mul1"], (1, 16, 512)),
+    # bit-width sweep: K = N = 4096 at 64 rows, 1..8 bits, every codebook
+    "sweep_4096x4096_b1-8_all_cb": ([f"sweep_4096x4096_b{b}_{cb}" for b in range(1, 9) for cb in ("3inst", "mcg", "mul1")],
+                                    (64,)),
 }
 DEFAULT_WORKLOAD = "expert_4096x2048+2048x4096_b4_mcg"
 # Routed experts (grouped GEMM): the expert pair's shapes, 64 experts each,

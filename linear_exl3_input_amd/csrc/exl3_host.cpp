@@ -86,8 +86,15 @@ exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_s
 // decode-size call stay in the 256 MB cache, so the cap is looser).  Shorter
 // groups help one-row calls little and cost batched ones partial traffic: at
 // K=4096, N=2048 eight groups against sixteen are 9% slower at one row and
-// 26% faster at 512 (when every group was one part).  G divides the number
-// of 128-k blocks so every group has the same length.
+// 26% faster at 512 (when every group was one part).  A small layer (fewer
+// than 512 block x group pairs, whose groups split into parts) keeps at most
+// 128 pairs: its one-row calls run four part quads per group anyway, and at
+// K = N = 4096 (32 blocks) 4 groups of 4 parts against 8 of 4 took 64 rows
+// from 19.6 to 18.3 us and one row from 12.2 to 10.7 us (4-bit mcg, calls
+// back to back; after a rotation in a graph the 64-row calls tie), while
+// at K = 4096, N = 2048 (16 blocks) the 8 groups stay (4 were faster at 1 and
+// 16 rows but slower at 512: 33.4 against 30.5 us).  G divides the number of
+// 128-k blocks so every group has the same length.
 int32_t choose_groups(int32_t K, int32_t N, int32_t bits) {
   const int32_t kb = K / 128;
   const int32_t nblk = N / 128;
@@ -95,6 +102,7 @@ int32_t choose_groups(int32_t K, int32_t N, int32_t bits) {
   const int32_t cap_len = std::max(1, std::max(kb / 4, std::min(kb / 2, 4)));
   const int32_t cap_traffic = std::max(1, (int32_t)(1.2 * (double)K * bits / 1024.0));
   int32_t gmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
+  if ((int64_t)nblk * gmax < 512) gmax = std::max(1, std::min(gmax, 128 / nblk));
   for (int32_t g = gmax; g >= 1; --g)
     if (kb % g == 0) return g;
   return 1;

@@ -148,9 +148,9 @@ def test_small_layers_split_groups_into_parts():
 def test_row_chunks_keep_slabs_bounded():
     """Several parts per group at a batch whose group slabs exceed 192 MiB:
     slab mode in row chunks (one chunk's slabs in the workspace)."""
-    w = view(4096, (4096,), 4, 1)  # 32 blocks x 8 groups of 4 parts
+    w = view(4096, (4096,), 4, 1)  # 32 blocks x 4 groups of 4 parts
     p = _plan(w, 4096)
-    assert p.mode == ex.EXL3_MODE_SLABS and p.groups == 8 and p.parts == 32
+    assert p.mode == ex.EXL3_MODE_SLABS and p.groups == 4 and p.parts == 16
     assert p.workspace <= CB + 192 * 2 ** 20 and p.launches > 2
     L = ex.load()
     assert L.exl3_workspace_bytes_ex(ctypes.byref(w), 4096, ctypes.byref(F(mode=ex.EXL3_MODE_FUSED))) == 0

@@ -344,19 +344,19 @@ def test_finisher_counters_stay_zero():
 
 
 def test_row_chunks():
-    """4096 x 4096, 4 bits (32 column blocks x 8 groups of 4 parts) at 1600
+    """4096 x 4096, 4 bits (32 column blocks x 4 groups of 4 parts) at 3200
     rows: the group slabs exceed 192 MiB, so the call runs in row chunks.
     Rows from both chunks equal the same rows computed alone, and sampled
     outputs are within the oracle's bound."""
-    lay = wl.small_layer("chunks", 4096, (4096,), 4, "mcg", (1600,), seed=96)
+    lay = wl.small_layer("chunks", 4096, (4096,), 4, "mcg", (3200,), seed=96)
     t = wl.gen_all(lay)
     w = weight(t)
-    pl = ex.plan(w, 1600)
+    pl = ex.plan(w, 3200)
     banner(f"row chunks: plan {pl}")
     assert pl["mode"] == ex.EXL3_MODE_SLABS and pl["launches"] > 2
     xr = ex.input_transform(x_dev(t.x), w.suh)
     y = bits16(ex.linear(w, xr, torch.bfloat16))
-    rows = [0, 777, 1599]
+    rows = [0, 1777, 3199]
     for r in rows:
         xr1 = ex.input_transform(x_dev(t.x[r:r + 1]), w.suh)
         assert np.array_equal(bits16(ex.linear(w, xr1, torch.bfloat16))[0], y[r]), f"row {r}"
@@ -484,6 +484,32 @@ FULL = [("small_1024x1024_b4_3inst", 16), ("expert_4096x2048_b4_mcg", 512), ("ex
         ("q_proj_5120x12288_b6_mul1", 128), ("q_proj_5120x12288_b6_mul1", 24), ("down_proj_17408x5120_b6_mul1", 16),
         ("down_proj_17408x5120_b6_mul1", 64),
         ("gate_up_5120x2x17408_b5_mul1", 2048), ("lm_head_4096x154880_b6_mul1", 16)]
+
+
+SWEEP = [(b, cb) for b in range(1, 9) for cb in ("3inst", "mcg", "mul1")]
+
+
+@pytest.mark.parametrize("bits,cb", SWEEP, ids=[f"b{b}-{cb}" for b, cb in SWEEP])
+def test_sweep_full_size_sampled(bits, cb):
+    """The bit-width sweep at its real shape (K = N = 4096, 64 rows): the
+    planner's call, the ALU and table decoders forced, and the first row
+    alone give the same bits; sampled rows and column blocks are within the
+    oracle's bound."""
+    lay = wl.sweep_layer(bits, cb)
+    banner(f"sweep {lay.name} M=64")
+    t = wl.gen_all(lay, M=64)
+    w = weight(t)
+    xr = ex.input_transform(x_dev(t.x), w.suh)
+    y = bits16(ex.linear(w, xr, torch.bfloat16))
+    for dec in (ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE):
+        assert np.array_equal(bits16(ex.linear(w, xr, torch.bfloat16, decoder=dec)), y), f"decoder {dec}"
+    y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
+    assert np.array_equal(y1[0], y[0])
+    rows, blocks = [0, 31, 63], [0, 13, 31]
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
+    res = olin.check(y[rows][:, ref.cols], ref, t.svh, lay.K, "bf16")
+    banner(f"{lay.name}: {res}")
+    assert res.ok, str(res)
 
 
 @pytest.mark.parametrize("name,M", FULL, ids=[f"{f[0]}-M{f[1]}" for f in FULL])

@@ -143,3 +143,21 @@ def test_column_block_selection_matches_full():
     part = ol.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x, col_blocks=[1])
     assert np.array_equal(part.y, ref.y[:, 128:256])
     assert np.array_equal(part.cols, np.arange(128, 256))
+
+
+def test_bench_workloads_name_known_layers():
+    """Every layer a bench workload names resolves, the bit-width sweep has all
+    24 (bits, codebook) layers at K = N = 4096 with distinct seeds, and its
+    first rows are the input recipe's (bf16 of standard normals)."""
+    import bench
+    for names, Ms in bench.WORKLOADS.values():
+        for n in names:
+            lay = wl.layer(n)
+            assert max(Ms) <= lay.M_max
+    sweep = [wl.layer(n) for n in bench.WORKLOADS["sweep_4096x4096_b1-8_all_cb"][0]]
+    assert sorted((l.bits, l.codebook) for l in sweep) == sorted(
+        (b, cb) for b in range(1, 9) for cb in ("3inst", "mcg", "mul1"))
+    assert all(l.K == 4096 and l.N == 4096 and l.M_values == (64,) for l in sweep)
+    assert len({l.seed_base for l in sweep}) == 24
+    t = wl.gen_all(sweep[0], M=2)
+    assert t.trellis.shape == (256, 256, 16) and t.x.shape == (2, 4096)

@@ -96,8 +96,11 @@ def sweep_layer(bits: int, codebook: str) -> Layer:
                  _sweep_seed(bits, cb))
 
 
+SWEEP: List[Layer] = [sweep_layer(b, cb) for b in range(1, 9) for cb in ("3inst", "mcg", "mul1")]
+
+
 def layer(name: str) -> Layer:
-    for lay in LAYERS:
+    for lay in LAYERS + SWEEP:
         if lay.name == name:
             return lay
     raise KeyError(name)
