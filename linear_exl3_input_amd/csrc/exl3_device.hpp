@@ -194,30 +194,45 @@ __device__ __forceinline__ void hadamard128_wave(float &x0, float &x1, int lane)
   x1 = b;
 }
 
+// The output stage's svh and bias words of lane l (columns n0 + 2l,
+// n0 + 2l + 1).  Without a bias svh's word is loaded in its place (a line
+// already on its way) and never used.
+struct OutWords {
+  uint32_t sv, bv;
+};
+__device__ __forceinline__ OutWords out_words(const uint16_t *__restrict__ svh, const uint16_t *__restrict__ bias,
+                                              int n0, int lane) {
+  return OutWords{*(const uint32_t *)(svh + n0 + 2 * lane),
+                  *(const uint32_t *)((bias != nullptr ? bias : svh) + n0 + 2 * lane)};
+}
+
 // Output stage for one 128-column block of one row, on one wave:
 // y = rne_out(svh * 2^-3 * H128(z) [+ bias]), the bias (fp16, optional)
 // added in fp32 before the one rounding; lane l owns columns n0 + 2l,
-// n0 + 2l + 1.
+// n0 + 2l + 1, whose svh and bias words are w.  Branch-free bias: without
+// one, add -0.0, the exact identity of fp32 addition (+0 + -0 = +0,
+// -0 + -0 = -0).
 template <bool OUT_BF16>
-__device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *__restrict__ svh,
-                                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ yrow, int n0,
-                                           int lane) {
-  // Branch-free bias: without one, add -0.0, the exact identity of fp32
-  // addition (+0 + -0 = +0, -0 + -0 = -0), and load svh's word in place of
-  // the bias's (a line already on its way).  The loads go first, so their
-  // latency overlaps the butterfly.
-  const bool has_bias = bias != nullptr;
-  const uint32_t sv = *(const uint32_t *)(svh + n0 + 2 * lane);
-  const uint32_t bv = *(const uint32_t *)((has_bias ? bias : svh) + n0 + 2 * lane);
+__device__ __forceinline__ void output_row_words(float z0, float z1, OutWords w, bool has_bias,
+                                                 uint16_t *__restrict__ yrow, int n0, int lane) {
   hadamard128_wave(z0, z1, lane);
-  const float b0 = has_bias ? f16_bits_to_f32(bv & 0xFFFFu) : -0.0f;
-  const float b1 = has_bias ? f16_bits_to_f32(bv >> 16) : -0.0f;
-  const float y0 = keep_f32(keep_f32((z0 * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu)) + b0);
-  const float y1 = keep_f32(keep_f32((z1 * 0.125f) * f16_bits_to_f32(sv >> 16)) + b1);
+  const float b0 = has_bias ? f16_bits_to_f32(w.bv & 0xFFFFu) : -0.0f;
+  const float b1 = has_bias ? f16_bits_to_f32(w.bv >> 16) : -0.0f;
+  const float y0 = keep_f32(keep_f32((z0 * 0.125f) * f16_bits_to_f32(w.sv & 0xFFFFu)) + b0);
+  const float y1 = keep_f32(keep_f32((z1 * 0.125f) * f16_bits_to_f32(w.sv >> 16)) + b1);
   uint32_t packed;
   if constexpr (OUT_BF16) packed = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
   else packed = f32_to_f16_bits(y0) | (f32_to_f16_bits(y1) << 16);
   *(uint32_t *)(yrow + n0 + 2 * lane) = packed;
+}
+
+// The same with the words loaded here, before the butterfly so that their
+// latency overlaps it.
+template <bool OUT_BF16>
+__device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *__restrict__ svh,
+                                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ yrow, int n0,
+                                           int lane) {
+  output_row_words<OUT_BF16>(z0, z1, out_words(svh, bias, n0, lane), bias != nullptr, yrow, n0, lane);
 }
 
 // Ordered sum of K-part partials for four rows of one 128-column block, then

@@ -354,7 +354,7 @@ __device__ __forceinline__ void store_partial_coherent(__amdgpu_buffer_rsrc_t rs
 template <int U>
 __device__ __forceinline__ void fold_rows4_coherent(__amdgpu_buffer_rsrc_t rs, int n_slabs, int fq,
                                                     uint32_t slab_stride, int N, int m4, int n0,
-                                                    const GemmParams &p, const uint16_t *svh, const uint16_t *bias,
+                                                    const GemmParams &p, OutWords ow, bool has_bias,
                                                     int64_t row0, int rows, int lane) {
   const uint32_t base = ((uint32_t)m4 * (uint32_t)N + (uint32_t)(n0 + 2 * lane)) * 16u;
   float4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, g0 = t0, g1 = t0;
@@ -394,8 +394,8 @@ __device__ __forceinline__ void fold_rows4_coherent(__amdgpu_buffer_rsrc_t rs, i
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i < rows) {
-      if (p.out_bf16) output_row<true>(t0[i], t1[i], svh, bias, y + (row0 + i) * N, n0, lane);
-      else output_row<false>(t0[i], t1[i], svh, bias, y + (row0 + i) * N, n0, lane);
+      if (p.out_bf16) output_row_words<true>(t0[i], t1[i], ow, has_bias, y + (row0 + i) * N, n0, lane);
+      else output_row_words<false>(t0[i], t1[i], ow, has_bias, y + (row0 + i) * N, n0, lane);
     }
 }
 
@@ -421,11 +421,12 @@ __device__ __forceinline__ bool arrive_last(const GemmParams &p, uint32_t tile, 
 // so all loads of a wave's item are in flight together and the waves' items
 // overlap; then wave r folds the group sums of 4-row group r in group order
 // (first copied) and writes the rows.  The same fp32 adds in the same order as
-// reduce_rows4 (which serves when the items do not fit the LDS).  The
+// reduce_rows4 (which serves when the items do not fit the LDS).  ow: the
+// lane's svh and bias words of the block, loaded before the arrival.  The
 // tile's counter is reset to zero for the next call.
-__device__ __forceinline__ void finish_tile(const GemmParams &p, const uint16_t *svh, const uint16_t *bias,
-                                            uint32_t tile, int nb, int m0, int bm, int wave_all, int n_waves, int lane,
-                                            float *lds, int lds_bytes) {
+__device__ __forceinline__ void finish_tile(const GemmParams &p, OutWords ow, bool has_bias, uint32_t tile, int nb,
+                                            int m0, int bm, int wave_all, int n_waves, int lane, float *lds,
+                                            int lds_bytes) {
   const int rows = p.row_end - p.row_base;
   const int M4 = (rows + 3) >> 2;
   const int N = p.N;
@@ -475,14 +476,14 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, const uint16_t 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < nr) {
-          if (p.out_bf16) output_row<true>(t0[i], t1[i], svh, bias, y + (int64_t)(r0 + i) * N, n0, lane);
-          else output_row<false>(t0[i], t1[i], svh, bias, y + (int64_t)(r0 + i) * N, n0, lane);
+          if (p.out_bf16) output_row_words<true>(t0[i], t1[i], ow, has_bias, y + (int64_t)(r0 + i) * N, n0, lane);
+          else output_row_words<false>(t0[i], t1[i], ow, has_bias, y + (int64_t)(r0 + i) * N, n0, lane);
         }
     }
   } else {
     // one wave per 4-row group, slabs in order (reduce_rows4's order)
     for (int r = wave_all; r < r4; r += n_waves)
-      fold_rows4_coherent<4>(rs, n_slabs, fq, slab_stride, N, m4_0 + r, n0, p, svh, bias, m0 + 4 * r,
+      fold_rows4_coherent<4>(rs, n_slabs, fq, slab_stride, N, m4_0 + r, n0, p, ow, has_bias, m0 + 4 * r,
                              min(4, p.row_end - (m0 + 4 * r)), lane);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -760,10 +761,14 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
           store_partial_coherent(rs, blockIdx.y, rows, N, m0 - p.row_base + mt * 16 + 4 * g,
                                  nb * 128 + c0 + lane_col(wave, j, h), acc[mt][h]);
     }
+    // The output stage's svh and bias words of the block, loaded now: the
+    // arrival waits for them together with the slab stores, so the last
+    // workgroup does not wait a round trip for them afterwards.
+    const OutWords ow = out_words(svh, bias, nb * 128, lane);
     // the tile is the 128-column block: both halves' workgroups arrive
     const uint32_t tile = blockIdx.z * (gridDim.x * QW / 4) + nb;
     if (!arrive_last(p, tile, gridDim.y * (4 / QW))) return;
-    finish_tile(p, svh, bias, tile, nb, m0, BM, wave_all, QW * QD, lane, z, LDS_DW * 4);
+    finish_tile(p, ow, bias != nullptr, tile, nb, m0, BM, wave_all, QW * QD, lane, z, LDS_DW * 4);
     return;
   }
 
