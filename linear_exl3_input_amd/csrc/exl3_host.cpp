@@ -6,6 +6,7 @@
 // for errors that say which check failed and by how much; the TensorFold PR
 // refuses what it cannot read, "What it adds").
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -121,21 +122,25 @@ int32_t choose_q(int32_t K, int32_t N, int32_t groups) {
   return len % 4 == 0 ? 4 : len % 2 == 0 ? 2 : 1;
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; calls from
+// several threads may race to fill an entry, all with the same value).
 hipError_t device_cus(int *out) {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // zero: not yet queried
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
-    return hipSuccess;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return hipSuccess;
+    }
   }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (n < 1) n = 1;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return hipSuccess;
 }
