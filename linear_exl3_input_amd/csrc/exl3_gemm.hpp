@@ -447,7 +447,22 @@ __device__ __forceinline__ void finish_tile(const GemmParams &p, OutWords ow, bo
   };
   if (r4 * G * 2048 <= lds_bytes && fq <= 4) {
     float4_t *const gs = reinterpret_cast<float4_t *>(lds);  // [r][gi][lane][2]
-    for (int it = wave_all; it < r4 * G; it += n_waves) {
+    int it = wave_all;
+    if (fq == 1) {
+      // one slab per item (its group sum): two items' loads per round trip
+      for (; it + n_waves < r4 * G; it += 2 * n_waves) {
+        const int ita = it, itb = it + n_waves;
+        const int ra = ita / G, rb = itb / G;
+        float4_t a0, a1, b0, b1;
+        load2(ita - ra * G, m4_0 + ra, a0, a1);
+        load2(itb - rb * G, m4_0 + rb, b0, b1);
+        gs[(ita * 64 + lane) * 2] = a0;
+        gs[(ita * 64 + lane) * 2 + 1] = a1;
+        gs[(itb * 64 + lane) * 2] = b0;
+        gs[(itb * 64 + lane) * 2 + 1] = b1;
+      }
+    }
+    for (; it < r4 * G; it += n_waves) {
       const int r = it / G;
       const int gi = it - r * G;
       float4_t v0[4], v1[4];
