@@ -7,11 +7,17 @@ A step is one pass of the whole hot path -- the input rotation and the
 trellis GEMM with its output transform -- over every (shape, M) of the
 workload, each on its own copy of the weights drawn from a pool larger than
 the GPU's caches (so every step reads its trellis from HBM, as a real model
-step does).  The default workload is the 4-bit mcg expert pair K=4096 N=2048
-and K=2048 N=4096 at M = 1, 16 and 512.
+step does).  The default workload, ``all_configs``, is every configuration
+of the metric in one step (57 calls): the 1024 x 1024 4-bit 3inst layer at
+1 and 16 rows; the 4-bit mcg expert pair (4096 x 2048, 2048 x 4096) at 1,
+16 and 512; the Qwen-27B-shaped 6-bit mul1 q_proj (5120 x 12288) and
+down_proj (17408 x 5120) at 1 .. 512 rows; the fused 5-bit mul1 gate_up
+(5120 x 2 x 17408) at 16 .. 4096 rows; the 6-bit mul1 lm_head (4096 x
+154880) at 1, 16 and 512; and the bit-width sweep (4096 x 4096, 1-8 bits,
+every codebook) at 64 rows.
 
-The timed region replays one HIP graph per step (the calls are launch-bound
-at these sizes), bracketed by synchronizations; ``value`` is the aggregate
+The timed region replays a HIP graph per step (the small calls are
+launch-bound), bracketed by synchronizations; ``value`` is the aggregate
 fraction of speed of light, 100 * sum(SoL) / measured time, with
 SoL = max(K*N*bits/8 / 8 TB/s, 2*M*K*N / 2.5 PFLOP/s) per call.
 
@@ -37,18 +43,30 @@ sys.path.insert(0, ROOT)
 HBM_BPS = 8.0e12
 MFMA_F16_FLOPS = 2.5e15
 
+M_SWEEP = (1, 8, 16, 24, 32, 64, 128, 256, 512)
+SWEEP_LAYERS = [f"sweep_4096x4096_b{b}_{cb}" for b in range(1, 9) for cb in ("3inst", "mcg", "mul1")]
+# Each workload is a list of (layer, row counts); a step runs every (layer, M).
 WORKLOADS = {
-    "expert_4096x2048+2048x4096_b4_mcg": (["expert_4096x2048_b4_mcg", "expert_2048x4096_b4_mcg"], (1, 16, 512)),
-    "small_1024x1024_b4_3inst": (["small_1024x1024_b4_3inst"], (1, 16)),
-    "qwen27b_q_down_b6_mul1": (["q_proj_5120x12288_b6_mul1", "down_proj_17408x5120_b6_mul1"],
-                               (1, 8, 16, 24, 32, 64, 128, 256, 512)),
-    "gate_up_5120x2x17408_b5_mul1": (["gate_up_5120x2x17408_b5_mul1"], (16, 128, 2048, 4096)),
-    "lm_head_4096x154880_b6_mul1": (["lm_head_4096x154880_b6_mul1"], (1, 16, 512)),
+    # every configuration of the metric in one step: the 1024 x 1024 3inst
+    # layer, the 4-bit mcg expert pair, the Qwen-27B-shaped q_proj and
+    # down_proj over the continuous-batching sweep, the fused gate_up pair up
+    # to 4096 rows, the lm_head, and the bit-width sweep at 64 rows
+    "all_configs": ([("small_1024x1024_b4_3inst", (1, 16)),
+                     ("expert_4096x2048_b4_mcg", (1, 16, 512)), ("expert_2048x4096_b4_mcg", (1, 16, 512)),
+                     ("q_proj_5120x12288_b6_mul1", M_SWEEP), ("down_proj_17408x5120_b6_mul1", M_SWEEP),
+                     ("gate_up_5120x2x17408_b5_mul1", (16, 128, 2048, 4096)),
+                     ("lm_head_4096x154880_b6_mul1", (1, 16, 512))]
+                    + [(n, (64,)) for n in SWEEP_LAYERS]),
+    "expert_4096x2048+2048x4096_b4_mcg": [("expert_4096x2048_b4_mcg", (1, 16, 512)),
+                                          ("expert_2048x4096_b4_mcg", (1, 16, 512))],
+    "small_1024x1024_b4_3inst": [("small_1024x1024_b4_3inst", (1, 16))],
+    "qwen27b_q_down_b6_mul1": [("q_proj_5120x12288_b6_mul1", M_SWEEP), ("down_proj_17408x5120_b6_mul1", M_SWEEP)],
+    "gate_up_5120x2x17408_b5_mul1": [("gate_up_5120x2x17408_b5_mul1", (16, 128, 2048, 4096))],
+    "lm_head_4096x154880_b6_mul1": [("lm_head_4096x154880_b6_mul1", (1, 16, 512))],
     # bit-width sweep: K = N = 4096 at 64 rows, 1..8 bits, every codebook
-    "sweep_4096x4096_b1-8_all_cb": ([f"sweep_4096x4096_b{b}_{cb}" for b in range(1, 9) for cb in ("3inst", "mcg", "mul1")],
-                                    (64,)),
+    "sweep_4096x4096_b1-8_all_cb": [(n, (64,)) for n in SWEEP_LAYERS],
 }
-DEFAULT_WORKLOAD = "expert_4096x2048+2048x4096_b4_mcg"
+DEFAULT_WORKLOAD = "all_configs"
 # Routed experts (grouped GEMM): the expert pair's shapes, 64 experts each,
 # top-8 synthetic routing, T tokens per call.
 MOE_WORKLOADS = {"moe_e64_top8_4096x2048+2048x4096_b4_mcg":
@@ -96,7 +114,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(layers, Ms, budget_s=24.0):
+def cpu_info():
+    """The host CPU's model name and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, avail
+
+
+def cpu_baseline(calls_spec, budget_s=24.0):
     """The oracle, as it stands, on a bounded sample of the same step: every
     (layer, M) call, each on as many 128-column blocks as its share of the
     time budget allows, scaled up to the full call."""
@@ -105,7 +141,7 @@ def cpu_baseline(layers, Ms, budget_s=24.0):
     import workloads as wl
     from oracle import linear as olin
 
-    calls = [(wl.layer(n), M) for n in layers for M in Ms]
+    calls = [(wl.layer(n), M) for n, Ms in calls_spec for M in Ms]
     share = budget_s / len(calls)
     total = 0.0
     parts = []
@@ -127,14 +163,17 @@ def cpu_baseline(layers, Ms, budget_s=24.0):
         total += full
         parts.append(f"{lay.name} M={M}: {blocks}/{nblk} blocks -> {full:.2f} s")
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    model, avail = cpu_info()
     sol = sum(sol_seconds(M, l.K, l.N, l.bits) for l, M in calls)
     return {
         "value": 100.0 * sol / total,
         "unit": "% of SoL (aggregate over the step)",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu_model": model,
+        "cores_available": int(avail),
         "sample": ("fp64 oracle (decode, rotation, GEMM, output transform) per call on a prefix of its "
-                   "128-column blocks, scaled to the whole call; " + "; ".join(parts)
+                   "128-column blocks, scaled to the whole call, BLAS on the stated threads; " + "; ".join(parts)
                    + f"; step total {total:.2f} s"),
         "seconds_per_step": total,
     }
@@ -184,89 +223,101 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {args.copy_calibration} MiB x {args.steps}")
         return
-    names, Ms = WORKLOADS[args.workload]
+    spec = list(WORKLOADS[args.workload])
     if args.only:
         oname, oM = args.only.split(":")
-        names, Ms = [oname], (int(oM),)
-    layers = [wl.layer(n) for n in names]
-    M_max = max(Ms)
+        spec = [(oname, (int(oM),))]
+    layers = [wl.layer(n) for n, _ in spec]
+    Ms_of = [tuple(Ms) for _, Ms in spec]
+    calls = [(li, M) for li in range(len(layers)) for M in Ms_of[li]]
 
     def d16(a, dt=torch.int16):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
 
-    # ---- inputs resident in HBM: a pool of weight copies per layer
-    step_bytes = sum(l.weight_bytes() for l in layers)
-    copies = max(1, int(math.ceil(args.pool_mb * 2 ** 20 / step_bytes)))
-    log(f"workload {args.workload}: {len(layers)} layers x M {Ms}, {copies} weight copies "
-        f"({copies * step_bytes / 2 ** 20:.0f} MB)")
+    # ---- inputs resident in HBM: per layer a pool of weight copies at least
+    # --pool-mb large (so calls cycling through it stream the trellis from
+    # HBM, not from the 256 MB cache), and at least one copy per call of
+    # the layer in a step (so no call of a step finds the previous call's
+    # weights in cache)
     per_layer = []
-    for lay in layers:
+    pool_bytes = 0
+    for li, lay in enumerate(layers):
+        Ms = Ms_of[li]
+        M_max = max(Ms)
         t = wl.gen_all(lay, M=M_max)
         tr = d16(t.trellis)
+        copies = min(2048, max(len(Ms), int(math.ceil(args.pool_mb * 2 ** 20 / lay.weight_bytes()))))
         pool = [tr] + [tr.clone() for _ in range(copies - 1)]
+        pool_bytes += copies * lay.weight_bytes()
         suh, svh = d16(t.suh, torch.float16), d16(t.svh, torch.float16)
-        ws = [ex.Exl3Weight(p, suh, svh, lay.bits, lay.codebook, lay.shards) for p in pool]
+        ws = [ex.Exl3Weight(p_, suh, svh, lay.bits, lay.codebook, lay.shards) for p_ in pool]
         x = d16(t.x, torch.bfloat16)
         xr = {M: torch.empty(ex.rot_shape(lay.n_shards, M, lay.K), dtype=torch.float16, device=dev) for M in Ms}
         y = {M: torch.empty((M, lay.N), dtype=torch.bfloat16, device=dev) for M in Ms}
         per_layer.append((lay, ws, x, xr, y))
+        del t
+    log(f"workload {args.workload}: {len(layers)} layers, {len(calls)} calls per step, weight pools "
+        f"{pool_bytes / 2 ** 30:.1f} GiB")
     tuned = {}
     if args.tune:
         ex.tune_clear()
-        for lay, ws, x, xr, y in per_layer:
-            for M in Ms:
-                ex.input_transform(x[:M], ws[0].suh, out=xr[M])
-                tuned[f"{lay.name} M={M}"] = ex.tune(ws, xr[M], reps=max(3, min(20, copies)))
-                log(f"tuned {lay.name} M={M}: {tuned[f'{lay.name} M={M}']}")
+        for li, M in calls:
+            lay, ws, x, xr, y = per_layer[li]
+            ex.input_transform(x[:M], ws[0].suh, out=xr[M])
+            tuned[f"{lay.name} M={M}"] = ex.tune(ws, xr[M], reps=max(3, min(20, len(ws))))
+            log(f"tuned {lay.name} M={M}: {tuned[f'{lay.name} M={M}']}")
     # workspace for the largest need, allocated before capture
-    need = max(ex.workspace_bytes(ws[0], M) for (lay, ws, x, xr, y) in per_layer for M in Ms)
+    need = max(ex.workspace_bytes(per_layer[li][1][0], M) for li, M in calls)
     if need:
         ex._workspace(need, dev)
 
     def call(li, M, copy):
         lay, ws, x, xr, y = per_layer[li]
-        w = ws[copy]
+        w = ws[copy % len(ws)]
         ex.input_transform(x[:M], w.suh, out=xr[M])
         ex.linear(w, xr[M], torch.bfloat16, out=y[M])
 
-    def step(copy):
+    def step(g):
+        # graph g: call j of a layer takes copy g * (calls of the layer) + j
         for li in range(len(per_layer)):
-            for M in Ms:
-                call(li, M, copy)
+            n = len(Ms_of[li])
+            for j, M in enumerate(Ms_of[li]):
+                call(li, M, g * n + j)
 
     stream = torch.cuda.Stream()
     if args.only:
         with torch.cuda.stream(stream):
             for i in range(args.warmup + args.steps):
-                step(i % copies)
+                step(i)
         torch.cuda.synchronize()
         log(f"ran {args.only} x {args.warmup + args.steps}")
         return
 
-    # ---- one graph per weight copy
+    # ---- HIP graphs of the step, each on its own weight copies
+    n_graphs = 2
     graphs = []
     with torch.cuda.stream(stream):
         step(0)
     torch.cuda.synchronize()
-    for c in range(copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            step(c)
-        graphs.append(g)
+    for g_ in range(n_graphs):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            step(g_)
+        graphs.append(gr)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        graphs[i % copies].replay()
+        graphs[i % n_graphs].replay()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps
     t0 = time.perf_counter()
     for i in range(args.steps):
-        graphs[i % copies].replay()
+        graphs[i % n_graphs].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    sol_step = sum(sol_seconds(M, l.K, l.N, l.bits) for l in layers for M in Ms)
+    sol_step = sum(sol_seconds(M, layers[li].K, layers[li].N, layers[li].bits) for li, M in calls)
     value = 100.0 * sol_step / (ms_per_step / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, SoL {sol_step * 1e3:.4f} ms -> {value:.2f}% SoL")
 
@@ -296,32 +347,33 @@ def main():
 
     per_shape = []
     with torch.cuda.stream(stream):
-        for li, (lay, ws, x, xr, y) in enumerate(per_layer):
-            for M in Ms:
-                pick = lambda r: ws[(r * 7 + 3) % copies]
-                t_in = time_calls(lambda r: ex.input_transform(x[:M], pick(r).suh, out=xr[M]), args.timing_reps)
-                t_lin, t_lin_min = time_batches(lambda r: ex.linear(pick(r), xr[M], torch.bfloat16, out=y[M]),
-                                                args.timing_reps)
-                # warm: the same weight copy every call (L2/MALL-resident when it fits)
-                t_warm = time_calls(lambda r: ex.linear(ws[0], xr[M], torch.bfloat16, out=y[M]), args.timing_reps)
-                pl = ex.plan(ws[0], M)
-                byts = lay.weight_bytes()
-                flops = 2.0 * M * lay.K * lay.N
-                sol = sol_seconds(M, lay.K, lay.N, lay.bits)
-                per_shape.append({
-                    "layer": lay.name, "M": M, "K": lay.K, "N": lay.N, "bits": lay.bits, "codebook": lay.codebook,
-                    "plan": pl, "transform_us": round(t_in, 3), "linear_us": round(t_lin, 3),
-                    "linear_us_min": round(t_lin_min, 3), "linear_us_warm": round(t_warm, 3),
-                    "kernels_per_linear": pl["launches"],
-                    "GBps": round(byts / (t_lin * 1e-6) / 1e9, 1),
-                    "TFLOPS": round(flops / (t_lin * 1e-6) / 1e12, 2),
-                    "pct_sol": round(100.0 * sol / (t_lin * 1e-6), 2),
-                    "pct_sol_with_transform": round(100.0 * sol / ((t_lin + t_in) * 1e-6), 2),
-                    "bound": "mfma" if flops / MFMA_F16_FLOPS > byts / HBM_BPS else "hbm",
-                })
-                log(f"{lay.name} M={M}: plan {pl}, transform {t_in:.2f} us, linear {t_lin:.2f} us "
-                    f"({per_shape[-1]['GBps']} GB/s, {per_shape[-1]['TFLOPS']} TFLOP/s, "
-                    f"{per_shape[-1]['pct_sol']}% SoL)")
+        for li, M in calls:
+            lay, ws, x, xr, y = per_layer[li]
+            copies = len(ws)
+            pick = lambda r: ws[(r * 7 + 3) % copies]
+            t_in = time_calls(lambda r: ex.input_transform(x[:M], pick(r).suh, out=xr[M]), args.timing_reps)
+            t_lin, t_lin_min = time_batches(lambda r: ex.linear(pick(r), xr[M], torch.bfloat16, out=y[M]),
+                                            args.timing_reps)
+            # warm: the same weight copy every call (L2/MALL-resident when it fits)
+            t_warm = time_calls(lambda r: ex.linear(ws[0], xr[M], torch.bfloat16, out=y[M]), args.timing_reps)
+            pl = ex.plan(ws[0], M)
+            byts = lay.weight_bytes()
+            flops = 2.0 * M * lay.K * lay.N
+            sol = sol_seconds(M, lay.K, lay.N, lay.bits)
+            per_shape.append({
+                "layer": lay.name, "M": M, "K": lay.K, "N": lay.N, "bits": lay.bits, "codebook": lay.codebook,
+                "plan": pl, "transform_us": round(t_in, 3), "linear_us": round(t_lin, 3),
+                "linear_us_min": round(t_lin_min, 3), "linear_us_warm": round(t_warm, 3),
+                "kernels_per_linear": pl["launches"],
+                "GBps": round(byts / (t_lin * 1e-6) / 1e9, 1),
+                "TFLOPS": round(flops / (t_lin * 1e-6) / 1e12, 2),
+                "pct_sol": round(100.0 * sol / (t_lin * 1e-6), 2),
+                "pct_sol_with_transform": round(100.0 * sol / ((t_lin + t_in) * 1e-6), 2),
+                "bound": "mfma" if flops / MFMA_F16_FLOPS > byts / HBM_BPS else "hbm",
+            })
+            log(f"{lay.name} M={M}: plan {pl}, transform {t_in:.2f} us, linear {t_lin:.2f} us "
+                f"({per_shape[-1]['GBps']} GB/s, {per_shape[-1]['TFLOPS']} TFLOP/s, "
+                f"{per_shape[-1]['pct_sol']}% SoL)")
 
     # ---- rulers measured in this run: a streaming read of 2 GiB, a pure fp16
     # matrix-core loop, and per layer the decode path alone (the tile
@@ -341,7 +393,7 @@ def main():
         decode = {}
         for li, (lay, ws, x, xr, y) in enumerate(per_layer):
             ro = torch.empty((lay.K // 128, lay.N // 128), dtype=torch.int32, device=dev)
-            t_dr = time_calls(lambda r: ex.debug_decode_rate(ws[(r * 7 + 3) % copies], out=ro), args.timing_reps)
+            t_dr = time_calls(lambda r: ex.debug_decode_rate(ws[(r * 7 + 3) % len(ws)], out=ro), args.timing_reps)
             decode[lay.name] = {"us": round(t_dr, 3),
                                 "weights_per_s": float(f"{lay.K * lay.N / (t_dr * 1e-6):.4g}"),
                                 "trellis_GBps": round(lay.weight_bytes() / (t_dr * 1e-6) / 1e9, 1)}
@@ -356,55 +408,80 @@ def main():
         s_["pct_attainable"] = round(100.0 * att / (s_["linear_us"] * 1e-6), 2)
         att_step += att
     rulers["step_pct_of_attainable"] = round(100.0 * att_step / (ms_per_step / 1e3), 3)
-    log(f"rulers: stream read {rulers['hbm_read_GBps']} GB/s, mfma {rulers['mfma_f16_TFLOPS']} TFLOP/s, "
-        f"decode {decode}; step at {rulers['step_pct_of_attainable']}% of the rulers' bound")
+    log(f"rulers: stream read {rulers['hbm_read_GBps']} GB/s, mfma {rulers['mfma_f16_TFLOPS']} TFLOP/s; "
+        f"step at {rulers['step_pct_of_attainable']}% of the rulers' bound")
 
-    # ---- roofline of the dominant kernel: the GEMM template instance with
-    # the most time per step.  A two-launch slab call is the GEMM plus the
-    # ordered part sum + output transform kernel; each is timed alone (the
-    # GEMM stage through the part-sums hook with the call's own plan and
-    # unit, the output stage through its hook), so the GEMM's average launch
-    # duration is the one rocprof reports for it.  A one-launch call (fused,
-    # or slabs summed by the tile's last workgroup) is its GEMM kernel.
+    # ---- roofline of the dominant kernel: the kernel template instance with
+    # the most time per step.  Each call's kernels are timed alone: a
+    # two-launch slab call is the GEMM stage (through the part-sums hook,
+    # with the call's own plan and unit) plus the ordered part sum + output
+    # transform (through its hook); a dense-decoder call is the dequantization
+    # (through its hook) plus the GEMM over the fragments (the call minus the
+    # dequantization); a one-launch call (fused, or slabs summed by the
+    # tile's last workgroup) is its GEMM kernel.  So each kernel's average
+    # launch duration is the one rocprof reports for it.
+    frag_buf = {}
     with torch.cuda.stream(stream):
         for s_ in per_shape:
-            s_["gemm_us"] = s_["linear_us"]
-            s_["epilogue_us"] = 0.0
-            if s_["plan"]["mode"] == ex.EXL3_MODE_SLABS and s_["plan"]["launches"] == 2:
-                li = [l.name for l in layers].index(s_["layer"])
-                lay_, ws_, xr_ = per_layer[li][0], per_layer[li][1], per_layer[li][3]
-                pl_ = s_["plan"]
+            li = [l.name for l in layers].index(s_["layer"])
+            lay_, ws_, xr_ = per_layer[li][0], per_layer[li][1], per_layer[li][3]
+            pl_ = s_["plan"]
+            gk = kernel_key(lay_, pl_)
+            kern = {gk: s_["linear_us"]}
+            if pl_["decoder"] == ex.EXL3_DECODER_DENSE:
+                if lay_.name not in frag_buf:
+                    frag_buf[lay_.name] = torch.empty((lay_.K // 32, lay_.N // 128, 8, 64, 8), dtype=torch.int16,
+                                                      device=dev)
+                fb = frag_buf[lay_.name]
+                t_dq = time_calls(lambda r: ex.debug_dequant(ws_[(r * 7 + 3) % len(ws_)], out=fb), args.timing_reps)
+                dk = f"exl3::dequant_kernel<{lay_.bits}, {lay_.cb}u>"
+                kern = {gk: round(s_["linear_us"] - t_dq, 3), dk: round(t_dq, 3)}
+            elif pl_["mode"] == ex.EXL3_MODE_SLABS and pl_["launches"] == 2:
                 n_sl = pl_["parts"] // pl_["unit"]
                 zp = torch.zeros((n_sl, (s_["M"] + 3) // 4, lay_.N, 4), dtype=torch.float32, device=dev)
                 yo = torch.empty((s_["M"], lay_.N), dtype=torch.bfloat16, device=dev)
                 t_epi = time_calls(lambda r: ex.debug_epilogue(ws_[0], zp, s_["M"], out=yo), args.timing_reps)
-                t_gemm = time_calls(lambda r: ex.debug_parts(ws_[(r * 7 + 3) % copies], xr_[s_["M"]],
+                t_gemm = time_calls(lambda r: ex.debug_parts(ws_[(r * 7 + 3) % len(ws_)], xr_[s_["M"]],
                                                              parts=pl_["parts"], groups=pl_["groups"],
                                                              unit=pl_["unit"], bm=pl_["bm"],
                                                              decoder=pl_["decoder"], out=zp), args.timing_reps)
-                s_["epilogue_us"] = round(t_epi, 3)
-                s_["gemm_us"] = round(t_gemm, 3)
+                kern = {gk: round(t_gemm, 3), "exl3::epilogue_kernel": round(t_epi, 3)}
                 del zp
-            s_["kernel"] = kernel_key(wl.layer(s_["layer"]), s_["plan"])
+            s_["kernels_us"] = kern
+            s_["kernel"] = gk
+            s_["gemm_us"] = kern[gk]
+    del frag_buf
     groups = {}
     for s_ in per_shape:
-        groups.setdefault(s_["kernel"], []).append(s_)
-    dom_key = max(groups, key=lambda k: sum(g["gemm_us"] for g in groups[k]))
+        for k_, us in s_["kernels_us"].items():
+            groups.setdefault(k_, []).append((s_, us))
+    dom_key = max(groups, key=lambda k: sum(us for _, us in groups[k]))
     dom = groups[dom_key]
-    secs = sum(g["gemm_us"] for g in dom) * 1e-6
-    bound = max(dom, key=lambda g: g["gemm_us"])["bound"]
-    if bound == "mfma":
-        work = sum(2.0 * g["M"] * g["K"] * g["N"] for g in dom)
-        roof = {"bound": "mfma", "achieved": round(work / secs / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s"}
-    else:
-        work = sum(g["K"] * g["N"] * g["bits"] / 8 for g in dom)
+    secs = sum(us for _, us in dom) * 1e-6
+    if dom_key.startswith("exl3::dequant_kernel"):
+        work = sum(g["K"] * g["N"] * (g["bits"] / 8 + 2) for g, _ in dom)
         roof = {"bound": "hbm", "achieved": round(work / secs / 1e9, 1), "peak": 8000.0, "unit": "GB/s"}
+        wpl = "K*N*bits/8 trellis bytes read + K*N*2 fragment bytes written"
+    elif dom_key == "exl3::epilogue_kernel":
+        work = sum((g["plan"]["parts"] // g["plan"]["unit"]) * g["M"] * g["N"] * 4 + g["M"] * g["N"] * 2
+                   for g, _ in dom)
+        roof = {"bound": "hbm", "achieved": round(work / secs / 1e9, 1), "peak": 8000.0, "unit": "GB/s"}
+        wpl = "fp32 slabs read + bf16 output written"
+    elif max(dom, key=lambda d: d[1])[0]["bound"] == "mfma":
+        work = sum(2.0 * g["M"] * g["K"] * g["N"] for g, _ in dom)
+        roof = {"bound": "mfma", "achieved": round(work / secs / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s"}
+        wpl = "2*M*K*N flops"
+    else:
+        work = sum(g["K"] * g["N"] * g["bits"] / 8 for g, _ in dom)
+        roof = {"bound": "hbm", "achieved": round(work / secs / 1e9, 1), "peak": 8000.0, "unit": "GB/s"}
+        wpl = "K*N*bits/8 trellis bytes"
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
     roof["kernel"] = dom_key
-    roof["launches"] = [f"{g['layer']} M={g['M']}" for g in dom]
+    roof["launches"] = [f"{g['layer']} M={g['M']}" for g, _ in dom]
     roof["avg_launch_us"] = round(secs * 1e6 / len(dom), 3)
-    roof["work_per_launch"] = ("2*M*K*N flops" if bound == "mfma" else "K*N*bits/8 trellis bytes")
+    roof["work_per_launch"] = wpl
+    roof["time_share_of_step"] = round(secs / (ms_per_step / 1e3), 4)
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         try:
@@ -414,8 +491,8 @@ def main():
                 n = len(dom)
                 roof["traffic"] = {"fetch_bytes_per_launch": ent["fetch_bytes"], "write_bytes_per_launch":
                                    ent["write_bytes"], "algorithmic_trellis_bytes_per_launch":
-                                   sum(g["K"] * g["N"] * g["bits"] / 8 for g in dom) / n,
-                                   "scale": ent.get("scale")}
+                                   sum(g["K"] * g["N"] * g["bits"] / 8 for g, _ in dom) / n,
+                                   "scale": ent.get("scale"), "measured_on": ent.get("measured_on")}
         except Exception as e:  # a malformed file only loses the traffic field
             log(f"traffic file unreadable: {e}")
     roof["ruler_peak"] = rulers["mfma_f16_TFLOPS"] if roof["unit"] == "TFLOP/s" else rulers["hbm_read_GBps"]
@@ -437,8 +514,9 @@ def main():
         "dtype": "f16",
         "data": "synthetic (seeded uniform trellis, +-1 suh/svh, N(0,1) bf16 x)",
         "config": {"workload": args.workload, "layers": [
-            {"K": l.K, "N": l.N, "shards": list(l.shards), "bits": l.bits, "codebook": l.codebook} for l in layers],
-            "M": list(Ms), "weight_copies": copies, "sol_ms_per_step": round(sol_step * 1e3, 5),
+            {"name": l.name, "K": l.K, "N": l.N, "shards": list(l.shards), "bits": l.bits, "codebook": l.codebook,
+             "M": list(Ms_of[i]), "weight_copies": len(per_layer[i][1])} for i, l in enumerate(layers)],
+            "calls_per_step": len(calls), "sol_ms_per_step": round(sol_step * 1e3, 5),
             "schedules": "tuned on the weight pool (same bits)" if args.tune else "planner",
             "parallelism": "single GPU"},
         "roofline": roof,
@@ -447,7 +525,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
-        line["cpu_baseline"] = cpu_baseline(names, Ms)
+        line["cpu_baseline"] = cpu_baseline(spec)
     out = json.dumps(line)
     print(out, flush=True)
     if args.json_out:

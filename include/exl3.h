@@ -293,6 +293,19 @@ exl3_status exl3_debug_codebook(int32_t codebook, uint16_t *out, void *stream);
  * unpacking path (TensorFold PR, "Tests (GB10)" second bullet). */
 exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream);
 
+/* The dense decoder's first stage alone: the whole W_q decoded once into
+ * matrix-core B fragments, the layout exl3_linear's dense decoder keeps in
+ * its workspace (TensorFold PR, "Tests (GB10)" second bullet: the decoded
+ * weights checked against the reference's).  frags (device, frag_bytes >=
+ * K*N*2) receives [K/32][N/128][8][64][8] fp16 bits: for the 32-k step ks,
+ * the 128-column block nb, fragment f = 2w + h and lane L = 16g + j, the 8
+ * values are W_q[32ks + k][128nb + c], c = 16(2w + j/8) + j%8 + 8h, at the 8
+ * k of the rotated activations' 16-byte piece g (4-element chunks c(2g) and
+ * c(2g+1), c = 0, 2, 1, 3, 4, 6, 5, 7), so a lane's B values meet its A
+ * values in one matrix-core product.  EXL3_ERR_WORKSPACE if frag_bytes is
+ * short. */
+exl3_status exl3_debug_dequant(const exl3_weight *w, uint16_t *frags, size_t frag_bytes, void *stream);
+
 /* The trellis GEMM stage alone, the kernel slab mode runs before the
  * output stage: the fp32 sum of every K part (unit 1, the default), or of
  * every group (force->unit = P/G, the automatic slab plan's own stage),

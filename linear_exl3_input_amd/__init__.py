@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "CODEBOOKS", "Exl3Weight", "Exl3Error", "load", "lib_path", "input_transform", "linear", "forward",
-    "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_epilogue", "debug_parts",
+    "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_dequant", "debug_epilogue", "debug_parts",
     "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops", "tune", "tune_clear",
     "input_transform_swiglu", "MoeWeight", "moe_rows_max", "moe_align", "moe_input_transform", "moe_linear",
     "moe_combine", "moe_forward",
@@ -108,6 +108,7 @@ def load() -> ctypes.CDLL:
             "exl3_debug_stream_read": (i32, [vp, sz, vp, vp]),
             "exl3_debug_mfma_loop": (i32, [i32, ctypes.c_uint16, vp, vp]),
             "exl3_debug_decode_rate": (i32, [W, vp, vp]),
+            "exl3_debug_dequant": (i32, [W, vp, sz, vp]),
             "exl3_tune": (i32, [W, i32, vp, i32, vp, i32, vp, sz, i32, vp, P]),
             "exl3_tune_workspace_bytes": (sz, [W, i32]),
             "exl3_tune_set": (i32, [W, i32, P]),
@@ -338,6 +339,19 @@ def debug_codebook(codebook: int | str, device="cuda") -> torch.Tensor:
 def debug_decode(w: Exl3Weight) -> torch.Tensor:
     out = torch.empty((w.K, w.N), dtype=torch.int16, device=w.trellis.device)
     _check(load().exl3_debug_decode(ctypes.byref(w.view()), out.data_ptr(), _stream()))
+    return out
+
+
+def debug_dequant(w: Exl3Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The dense decoder's first stage alone: W_q as matrix-core B fragments,
+    int16 [K/32, N/128, 8, 64, 8] (see exl3_debug_dequant in the header)."""
+    shape = (w.K // 32, w.N // 128, 8, 64, 8)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int16, device=w.trellis.device)
+    elif tuple(out.shape) != shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    _check(load().exl3_debug_dequant(ctypes.byref(w.view()), _dev_ptr(out, "frags", _U16), out.numel() * 2,
+                                     _stream()))
     return out
 
 

@@ -1032,6 +1032,24 @@ exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream) 
   return e == hipSuccess ? EXL3_OK : launch_error(e, "decode launch");
 }
 
+exl3_status exl3_debug_dequant(const exl3_weight *w, uint16_t *frags, size_t frag_bytes, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  if ((st = check_ptr(frags, "frags")) != EXL3_OK) return st;
+  const size_t need = (size_t)w->K * (size_t)w->N * 2;
+  if (frag_bytes < need)
+    return fail(EXL3_ERR_WORKSPACE, "frags holds %zu bytes; K*N fp16 need %zu (short by %zu)", frag_bytes, need,
+                need - frag_bytes);
+  exl3::DecodeParams p;
+  p.trellis = w->trellis;
+  p.wq = frags;
+  p.K = w->K;
+  p.N = w->N;
+  const hipError_t e = exl3::launch_dequant(w->bits, w->codebook, p, (hipStream_t)stream);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "dequant launch");
+}
+
 exl3_status exl3_debug_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
   clear_error();
   exl3_status st;

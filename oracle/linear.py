@@ -129,6 +129,38 @@ def bound(ref: Reference, svh_bits: np.ndarray, K: int, out_dtype: str) -> np.nd
     return u_o * np.abs(ref.y) + (1.0 + u_o) * scaled + A_OUT[out_dtype]
 
 
+def output_stage_reference(z_parts: np.ndarray, svh_bits: np.ndarray, out_dtype: str,
+                           bias_bits: np.ndarray | None = None):
+    """The output stage on given fp32 K-part sums, against its plain
+    definition: y* = H128(sum_p z_p) * 2**-3 * svh (+ bias) in float64, and
+    the per-element bound of any fp32 evaluation that adds the P parts in
+    some order and then runs the output stage of reading R11 (TensorFold PR,
+    "Arithmetic" step 3: output transform, svh and 2**-3, one rounding).
+
+    ``z_parts`` [P, M, N] float32.  Derivation as in ``bound`` with the
+    K-sum replaced by the sum of P fp32 terms in any order, which errs by
+    at most g_{P-1} * A, A = sum_p |z_p| (u = 2**-24, round to nearest):
+        B_mn = u_o |y*| + (1 + u_o) 2**-3 |svh_n|
+               * sum_{j in blk(n)} ( g_{P-1} A_mj + g_8 (|z*_mj| + g_{P-1} A_mj) ) + a_o
+    (plus the bias add's one rounding, as in ``bound``).  Returns (y*, B).
+    """
+    z = np.asarray(z_parts, dtype=np.float64)
+    P, M, N = z.shape
+    zs = z.sum(axis=0)
+    A = np.abs(z).sum(axis=0)
+    y = tf.output_transform_f64(zs, svh_bits, bias_bits)
+    g_p = gamma(max(P - 1, 0), U_F32)
+    g_8 = gamma(8, U_F32)
+    per = g_p * A + g_8 * (np.abs(zs) + g_p * A)
+    blk = np.repeat(per.reshape(M, N // 128, 128).sum(axis=-1), 128, axis=1)
+    svh = np.abs(tf.f16_from_bits(svh_bits).astype(np.float64))[None, :]
+    scaled = tf.OUTPUT_SCALE * svh * blk
+    if bias_bits is not None:
+        scaled = scaled + U_F32 * (np.abs(y) + scaled)
+    u_o = U_OUT[out_dtype]
+    return y, u_o * np.abs(y) + (1.0 + u_o) * scaled + A_OUT[out_dtype]
+
+
 def out_bits_to_f64(y_bits: np.ndarray, out_dtype: str) -> np.ndarray:
     if out_dtype == "bf16":
         return tf.bf16_bits_to_f32(y_bits).astype(np.float64)

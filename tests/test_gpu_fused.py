@@ -1,8 +1,10 @@
 """GPU: the fused activation and the bias.
 
 SwiGLU folded into the down projection's input transform (cuda-exl3 README,
-"MoE throughput"; reading R17): bit-exact against the oracle's act followed
-by its rotation.  The layer's bias (README "VRAM"; reading R16): bit-exact in
+"MoE throughput"; reading R17): against float64 silu(g) * u (the act within
+one output ulp, the rotated act within a bound derived from the rounding
+steps), and bit-exact against the oracle's fp32 act followed by its rotation
+(which checks reading R17's fixed exp sequence).  The layer's bias (README "VRAM"; reading R16): bit-exact in
 the output stage given z, the same bits from every kernel family, and within
 the oracle's bound for the whole linear."""
 import numpy as np
@@ -41,6 +43,100 @@ def test_swiglu_transform_bit_exact(dtype, M, K, S):
     assert bad.shape[0] == 0, f"{bad.shape[0]} values differ, first {bad[:4].tolist()}"
 
 
+def _silu_times_u_f64(gu_bits, dtype):
+    K = gu_bits.shape[1] // 2
+    to64 = (lambda b: otf.bf16_bits_to_f32(b).astype(np.float64)) if dtype == "bf16" else \
+        (lambda b: otf.f16_from_bits(b).astype(np.float64))
+    g, u = to64(gu_bits[:, :K]), to64(gu_bits[:, K:])
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u, u
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_swiglu_act_against_float64(dtype):
+    """The fused transform's act against float64 silu(g) * u, within one
+    output ulp.  One nonzero u per 128-block makes the block's rotation
+    exact (every entry is +-act * suh * 2**-4, a dtype value times a power
+    of two, representable in fp16 in the range used), so the kernel's act is
+    read back from x~.  Gates span the saturating ends (the exp argument is
+    clamped at +-104)."""
+    rng = np.random.default_rng(620)
+    M, K = 64, 512
+    nblk = K // 128
+    gmax = 90.0 if dtype == "bf16" else 10.0
+    g = rng.uniform(-gmax, gmax, (M, K)).astype(np.float32)
+    g[:, :6] = [0.0, -0.0, gmax, -gmax, 1e-3, -1e-3]
+    rnd = otf.f32_to_bf16_bits if dtype == "bf16" else otf.f32_to_f16_bits
+    to64 = (lambda b: otf.bf16_bits_to_f32(b).astype(np.float64)) if dtype == "bf16" else \
+        (lambda b: otf.f16_from_bits(b).astype(np.float64))
+    gb = rnd(g)
+    g64 = to64(gb)
+    silu = g64 / (1.0 + np.exp(-g64))
+    pos = rng.integers(0, 128, (M, nblk))
+    u = np.zeros((M, K), np.float32)
+    for b in range(nblk):
+        j = 128 * b + pos[:, b]
+        target = np.exp2(rng.uniform(-4, 6, M)) * np.where(rng.integers(0, 2, M) == 1, -1.0, 1.0)
+        s = silu[np.arange(M), j]
+        u[np.arange(M), j] = np.where(s != 0, target / np.where(s != 0, s, 1.0), 1.0).astype(np.float32)
+    gu = np.concatenate([gb, rnd(u)], axis=1)
+    suh = np.full((1, K), 0x3C00, np.uint16)
+    got = bits16(ex.input_transform_swiglu(x_dev(gu, dtype), dev16(suh, torch.float16)))
+    xr = got.reshape(1, K // 32, M, 32).transpose(0, 2, 1, 3).reshape(M, K // 32, 32)
+    exact, _ = _silu_times_u_f64(gu, dtype)
+    for b in range(nblk):
+        j = 128 * b + pos[:, b]
+        # stored position 0 of the block's first k-step is natural k = 128b
+        act_gpu = 16.0 * otf.f16_from_bits(xr[:, 4 * b, 0]).astype(np.float64)
+        want = exact[np.arange(M), j]
+        mant, emin = (7, -126) if dtype == "bf16" else (10, -14)
+        e = np.maximum(np.floor(np.log2(np.maximum(np.abs(want), 1e-300))), emin)
+        ulp = np.exp2(e - mant)
+        err = np.abs(act_gpu - want)
+        assert np.all(err <= ulp), f"block {b}: worst {np.max(err / ulp):.2f} ulp"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_swiglu_transform_within_float64_bound(dtype):
+    """The fused transform on general inputs against float64: x~* = 2**-4 *
+    H128(silu(g) * u * suh), exact.  Bound per element: the act carries at
+    most u_d + 2**-20 relative error (the dtype's rounding, and a few fp32
+    roundings in exp, the add, the divide and the product) plus an absolute
+    a_d + 2**-120 |u| (the dtype's subnormal half-spacing; silu underflows to
+    zero below g = -88.7, where |silu| < 2**-121); the fp32 butterfly adds
+    g_7 of the block's sum of |act * suh|; the fp16 rounding adds u_16 |x~*|
+    and 2**-25."""
+    rng = np.random.default_rng(630)
+    M, K, S = 33, 1024, 2
+    f = (rng.standard_normal((M, 2 * K)) * np.exp2(rng.uniform(-8, 6, (M, 2 * K)))).astype(np.float32)
+    f[:, :8] = [0.0, -0.0, 40.0, -40.0, 95.0, -95.0, 1e-3, -1e-3]
+    if dtype == "f16":
+        f = np.clip(f, -60000, 60000)
+    rnd = otf.f32_to_bf16_bits if dtype == "bf16" else otf.f32_to_f16_bits
+    gu = rnd(f)
+    suh = (np.where(rng.integers(0, 2, (S, K)) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, (S, K)))
+           ).astype(np.float16).view(np.uint16)
+    got = bits16(ex.input_transform_swiglu(x_dev(gu, dtype), dev16(suh, torch.float16)))
+    got = got.reshape(S, K // 32, M, 32).transpose(0, 2, 1, 3)  # [S, M, K/32, 32] stored order
+    perm = np.array([0, 2, 1, 3, 4, 6, 5, 7])
+    nat = got.reshape(S, M, K // 32, 8, 4)[..., np.argsort(perm), :].reshape(S, M, K)
+    act64, u64 = _silu_times_u_f64(gu, dtype)
+    u_d = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    a_d = 2.0 ** -134 if dtype == "bf16" else 2.0 ** -25
+    g7 = olin.gamma(7, 2.0 ** -24)
+    for s in range(S):
+        sv = otf.f16_from_bits(suh[s]).astype(np.float64)
+        t = act64 * sv
+        xstar = otf.butterfly(t) * 2.0 ** -4
+        e_act = ((u_d + 2.0 ** -20) * np.abs(act64) + a_d + 2.0 ** -120 * np.abs(u64)) * np.abs(sv)
+        blk = lambda a: np.repeat(a.reshape(M, K // 128, 128).sum(axis=-1), 128, axis=1)
+        b = (1 + 2.0 ** -11) * 2.0 ** -4 * (blk(e_act) + g7 * blk(np.abs(t) + e_act)) \
+            + 2.0 ** -11 * np.abs(xstar) + 2.0 ** -25
+        x = otf.f16_from_bits(nat[s]).astype(np.float64)
+        r = np.abs(x - xstar) / b
+        assert np.all(np.isfinite(x)) and np.max(r) <= 1.0, f"shard {s}: {np.max(r):.3f} of the bound"
+
+
 def _bias(N, seed):
     rng = np.random.default_rng(seed)
     return (rng.standard_normal(N) * 2).astype(np.float16).view(np.uint16)
@@ -60,7 +156,10 @@ def test_bias_output_stage_bit_exact(out_dtype):
                       bias=dev16(bias, torch.float16))
     dt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
     got = bits16(ex.debug_epilogue(w, torch.from_numpy(slab_layout(z)).cuda(), M, dt, groups=G))
-    want = otf.output_transform_f32(otf.reduce_parts_f32(z, G), svh, out_dtype, bias)
+    ystar, bnd = olin.output_stage_reference(z, svh, out_dtype, bias)
+    ratio = np.max(np.abs(olin.out_bits_to_f64(got, out_dtype) - ystar) / bnd)
+    assert ratio <= 1.0, f"output stage with bias {ratio:.3f} of the fp64 bound"
+    want = otf.output_transform_f32(otf.reduce_parts_f32(z, G), svh, out_dtype, bias)  # reading R15's order
     assert np.array_equal(got, want)
 
 

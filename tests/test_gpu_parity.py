@@ -92,6 +92,13 @@ def test_output_stage_bit_exact(out_dtype, P, G, M, N):
     w = ex.Exl3Weight(dev16(trellis), dev16(suh, torch.float16), dev16(svh, torch.float16), 4, "mcg", (N,))
     dt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
     got = bits16(ex.debug_epilogue(w, torch.from_numpy(slab_layout(z)).cuda(), M, dt, groups=G))
+    # against the plain definition: the fp64 sum of the parts through the
+    # exact output transform, within the bound of any fp32 fold of P terms
+    ystar, bnd = olin.output_stage_reference(z, svh, out_dtype)
+    ratio = np.max(np.abs(olin.out_bits_to_f64(got, out_dtype) - ystar) / bnd)
+    assert ratio <= 1.0, f"output stage {ratio:.3f} of the fp64 bound"
+    # and bit for bit the library's fold order (reading R15: parts of a group
+    # in order, then the groups in order)
     want = otf.output_transform_f32(otf.reduce_parts_f32(z, G), svh, out_dtype)
     assert np.array_equal(got, want)
     del lay
@@ -461,6 +468,31 @@ def test_mfma_loop_ruler_closed_form():
     assert torch.all(out == 16 * 32 * 100)
     half = ex.debug_mfma_loop(3, one=0x3800)  # 0.5: 16 * 32 * 3 * 0.25
     assert torch.all(half == 16 * 32 * 3 * 0.25)
+
+
+@pytest.mark.parametrize("bits,cb", [(2, "mul1"), (5, "3inst"), (7, "mcg")])
+def test_dequant_fragments_layout(bits, cb):
+    """The dense decoder's fragments are the oracle's W_q in the documented
+    B-fragment order: [K/32][N/128][f = 2w + h][lane 16g + j][8] holds
+    W_q[32ks + k][128nb + 16(2w + j/8) + j%8 + 8h] at the 8 k of piece g
+    (4-element chunks c(2g), c(2g+1) of 0, 2, 1, 3, 4, 6, 5, 7)."""
+    lay = wl.small_layer(f"dq_b{bits}_{cb}", 256, (384,), bits, cb, (1,), seed=330 + bits)
+    t = wl.gen_all(lay)
+    got = bits16(ex.debug_dequant(weight(t)))  # [K/32, N/128, 8, 64, 8]
+    wq = ofmt.dequantize_bits(t.trellis, bits, lay.cb)  # [K, N]
+    K, N = wq.shape
+    chunk = np.array([0, 2, 1, 3, 4, 6, 5, 7])
+    want = np.zeros_like(got)
+    for f in range(8):
+        w_, h = f // 2, f % 2
+        for lane in range(64):
+            g, j = lane // 16, lane % 16
+            c = 16 * (2 * w_ + j // 8) + j % 8 + 8 * h
+            ks = np.concatenate([4 * chunk[2 * g] + np.arange(4), 4 * chunk[2 * g + 1] + np.arange(4)])
+            for kt in range(K // 32):
+                for nb in range(N // 128):
+                    want[kt, nb, f, lane] = wq[32 * kt + ks, 128 * nb + c]
+    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("bits,cb", [(1, "3inst"), (4, "mcg"), (6, "mul1"), (8, "3inst")])

@@ -161,3 +161,64 @@ def test_bench_workloads_name_known_layers():
     assert len({l.seed_base for l in sweep}) == 24
     t = wl.gen_all(sweep[0], M=2)
     assert t.trellis.shape == (256, 256, 16) and t.x.shape == (2, 4096)
+
+
+def _bits_to_f64(y, out_dtype):
+    return ol.out_bits_to_f64(y, out_dtype)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("P", [1, 2, 5, 17])
+def test_output_stage_bound_holds_for_fp32_folds(out_dtype, P):
+    """The output stage's plain definition (fp64 sum of the parts, then
+    H128 * 2**-3 * svh) with its bound: float32 folds of the parts in
+    several orders (flat, reversed, grouped in two and four, pairwise),
+    each followed by the float32 output stage, all lie inside; with a bias
+    too."""
+    rng = np.random.default_rng(700 + P)
+    M, N = 9, 256
+    z = (rng.standard_normal((P, M, N)) * np.exp2(rng.integers(-6, 6, (P, M, N)))).astype(np.float32)
+    svh = (np.where(rng.integers(0, 2, N) == 1, -1.0, 1.0) * np.exp2(rng.uniform(-2, 2, N))
+           ).astype(np.float16).view(np.uint16)
+    bias = (rng.standard_normal(N) * 2).astype(np.float16).view(np.uint16)
+    folds = [z.sum(axis=0, dtype=np.float32)]  # numpy's pairwise order
+    for order in (list(range(P)), list(reversed(range(P)))):
+        acc = z[order[0]].copy()
+        for p in order[1:]:
+            acc = (acc + z[p]).astype(np.float32)
+        folds.append(acc)
+    for G in (2, 4):
+        if P % G == 0:
+            folds.append(tf.reduce_parts_f32(z, G))
+    for b in (None, bias):
+        ystar, B = ol.output_stage_reference(z, svh, out_dtype, b)
+        for f in folds:
+            y = _bits_to_f64(tf.output_transform_f32(f, svh, out_dtype, b), out_dtype)
+            r = np.abs(y - ystar) / B
+            assert np.max(r) <= 1.0, f"fold outside the bound: {np.max(r)}"
+
+
+def test_output_stage_bound_rejects_planted_mistakes():
+    """A dropped part, a flipped svh, a dropped 2**-3 and one block left
+    unrotated all fall outside the output stage's bound."""
+    rng = np.random.default_rng(710)
+    P, M, N = 4, 8, 256
+    z = (rng.standard_normal((P, M, N))).astype(np.float32)
+    svh = np.where(rng.integers(0, 2, N) == 1, 0xBC00, 0x3C00).astype(np.uint16)
+    ystar, B = ol.output_stage_reference(z, svh, "bf16")
+    full = tf.reduce_parts_f32(z)
+
+    def bad(y_bits):
+        return np.max(np.abs(_bits_to_f64(y_bits, "bf16") - ystar) / B) > 1.0
+
+    assert not bad(tf.output_transform_f32(full, svh, "bf16"))
+    assert bad(tf.output_transform_f32(tf.reduce_parts_f32(z[:3]), svh, "bf16"))
+    flipped = svh.copy()
+    flipped[5] ^= 0x8000
+    assert bad(tf.output_transform_f32(full, flipped, "bf16"))
+    y8 = tf.bf16_bits_to_f32(tf.output_transform_f32(full, svh, "bf16")) * np.float32(8)
+    assert bad(tf.f32_to_bf16_bits(y8))
+    raw = full * np.float32(0.125) * tf.f16_from_bits(svh).astype(np.float32)[None, :]
+    y = tf.output_transform_f32(full, svh, "bf16")
+    y[:, 128:] = tf.f32_to_bf16_bits(raw[:, 128:])
+    assert bad(y)
