@@ -268,8 +268,9 @@ def main():
             log(f"tuned {lay.name} M={M}: {tuned[f'{lay.name} M={M}']}")
     # workspace for the largest need, allocated before capture
     need = max(ex.workspace_bytes(per_layer[li][1][0], M) for li, M in calls)
+    stream = torch.cuda.Stream()
     if need:
-        ex._workspace(need, dev)
+        ex.reserve_workspace(need, dev, stream)
 
     def call(li, M, copy):
         lay, ws, x, xr, y = per_layer[li]
@@ -284,7 +285,6 @@ def main():
             for j, M in enumerate(Ms_of[li]):
                 call(li, M, g * n + j)
 
-    stream = torch.cuda.Stream()
     if args.only:
         with torch.cuda.stream(stream):
             for i in range(args.warmup + args.steps):

@@ -91,8 +91,11 @@ typedef struct exl3_weight {
  * zero; the P/G consecutive parts of a group are added in part order (first
  * part copied); the group sums are added in group order (first copied).  With
  * G == P this is the plain ((p0 + p1) + p2) + ... of the TensorFold PR
- * ("Arithmetic").  `mode`, `bm`, `decoder` and `unit` pick how the same
- * arithmetic is scheduled and never change a bit of the output. */
+ * ("Arithmetic": a number of parts fixed by the shape, added by the last
+ * part in part order).  G < P, the two-level grouping that small layers
+ * get, is this library's own choice, fixed by the shape like P.  `mode`,
+ * `bm`, `decoder` and `unit` pick how the same arithmetic is scheduled and
+ * never change a bit of the output. */
 typedef enum {
   EXL3_MODE_AUTO = -1,
   EXL3_MODE_FUSED = 0, /* one workgroup per (M-tile, 128 columns) runs all
@@ -193,8 +196,9 @@ exl3_status exl3_input_transform_swiglu(const void *gate_up, int32_t dtype, int3
                                         const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, void *stream);
 
 /* Bytes of workspace exl3_linear needs for `M` rows of weight `w` (0 when
- * the plan needs none).  Returns 0 and sets exl3_last_error() if `w` is
- * invalid. */
+ * the plan needs none): the split-k partials and arrival counters that the
+ * cuda-exl3 README ("VRAM") keeps in a process-wide workspace rather than
+ * per layer.  Returns 0 and sets exl3_last_error() if `w` is invalid. */
 size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M);
 
 /* The quantized linear on rotated activations (cuda-exl3 README, "One op per
@@ -221,8 +225,14 @@ size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M);
 exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y,
                         int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
-/* The plan exl3_linear would use for M rows (HOST output). */
+/* The plan exl3_linear would use for M rows (HOST output), and the one
+ * exl3_linear_ex would use with `force` (HOST, may be NULL).  The plan's
+ * workspace is the process-wide scratch of the cuda-exl3 README ("VRAM":
+ * activation and split-k workspaces are process-wide, not per layer); its
+ * shape-fixed parts are the TensorFold PR's ("Arithmetic").  Errors as
+ * exl3_linear_ex's plan checks (the call names the failed check). */
 exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan);
+exl3_status exl3_plan_query_ex(const exl3_weight *w, int32_t M, const exl3_plan *force, exl3_plan *plan);
 
 /* exl3_linear with parts of the plan forced (HOST `force`; a field <= 0, or
  * EXL3_MODE_AUTO / EXL3_DECODER_AUTO, keeps the automatic choice).  Forcing
@@ -277,7 +287,11 @@ exl3_status exl3_tune_set(const exl3_weight *w, int32_t M, const exl3_plan *plan
 /* Forget every tuned schedule. */
 void exl3_tune_clear(void);
 
-/* Human-readable status name, and the thread's last error message. */
+/* Human-readable status name, and the thread's last error message.  Calls
+ * refuse what they cannot run rather than misread it (TensorFold PR, "What
+ * it adds": a weight is refused when its format is not loaded) and the
+ * message says which check failed and by how much (cuda-exl3 README,
+ * "Loading into a dim vLLM has padded"). */
 const char *exl3_status_str(exl3_status s);
 const char *exl3_last_error(void);
 int32_t exl3_abi_version(void);
@@ -397,9 +411,9 @@ exl3_status exl3_moe_combine(const void *y_routed, int32_t dtype, const int32_t 
  * Not part of the layer API: simple kernels that measure, in the same run
  * as the layer timings, what this GPU's HBM, matrix cores and decode path
  * deliver, so the layer figures can be read against attainable rates as
- * well as the data-sheet peaks (speed of light as max of weight bytes over
- * HBM bandwidth and 2*M*K*N over fp16 matrix-core peak: EXL3 survey of the
- * pages, "Measurement").  Each writes EXL3_RULER_WORDS words (or one word
+ * well as the data-sheet peaks (cuda-exl3 README, "Measured": a matmul
+ * reads k*n*bits/8 bytes and does 2*m*k*n flops, speed of light is the max
+ * of the two limits, and the roofline there is itself measured).  Each writes EXL3_RULER_WORDS words (or one word
  * per weight block) to a caller-owned device buffer and is asynchronous on
  * `stream`. */
 #define EXL3_RULER_WORDS 262144

@@ -30,7 +30,7 @@ __all__ = [
     "workspace_bytes", "plan", "debug_codebook", "debug_decode", "debug_dequant", "debug_epilogue", "debug_parts",
     "debug_stream_read", "debug_mfma_loop", "debug_decode_rate", "mfma_loop_flops", "tune", "tune_clear",
     "input_transform_swiglu", "MoeWeight", "moe_rows_max", "moe_align", "moe_input_transform", "moe_linear",
-    "moe_combine", "moe_forward",
+    "moe_combine", "moe_forward", "reserve_workspace", "workspace_key",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +98,7 @@ def load() -> ctypes.CDLL:
             "exl3_linear": (i32, [W, vp, i32, vp, i32, vp, sz, vp]),
             "exl3_linear_ex": (i32, [W, vp, i32, vp, i32, vp, sz, vp, P]),
             "exl3_plan_query": (i32, [W, i32, P]),
+            "exl3_plan_query_ex": (i32, [W, i32, P, P]),
             "exl3_status_str": (ctypes.c_char_p, [i32]),
             "exl3_last_error": (ctypes.c_char_p, []),
             "exl3_abi_version": (i32, []),
@@ -201,23 +202,57 @@ class Exl3Weight:
         return self._view
 
 
-# Process-wide workspace per device (the cuda-exl3 page, "VRAM": the
-# activation and split-k workspaces are process-wide, not per layer).  It is
-# allocated zeroed: its first COUNTER_BYTES are the arrival counters that
-# every call expects zero and leaves zero.  Calls on one device's stream use
-# it one after another.
-_workspaces: Dict[int, torch.Tensor] = {}
+# Process-wide workspaces (the cuda-exl3 page, "VRAM": the activation and
+# split-k workspaces are process-wide, not per layer), one per (device,
+# stream): calls on one stream run one after another, so they may share one
+# workspace, while calls on two streams may overlap and get one each.  The
+# first COUNTER_BYTES of a workspace are the arrival counters that every call
+# expects zero and leaves zero.  A workspace is never freed once handed out
+# (a captured graph keeps its address): a larger one replaces it for later
+# calls and the old one is kept alive.  Allocated under graph capture, the
+# counters' zero fill is a kernel recorded in the graph (so every replay
+# starts from zero), and the first eager call on that stream zeroes them
+# before use.
+_ws_lock = threading.Lock()
+_workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
+_ws_needs_zero: set = set()
+_ws_retired: list = []
 
 
-def _workspace(nbytes: int, device: torch.device) -> Tuple[int, int]:
+def workspace_key(device: Optional[torch.device] = None, stream: Optional[torch.cuda.Stream] = None):
+    """The (device index, stream handle) a call's workspace is kept under."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    s = stream if stream is not None else torch.cuda.current_stream(idx)
+    return idx, int(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device: torch.device, stream: Optional[torch.cuda.Stream] = None) -> Tuple[int, int]:
     if nbytes == 0:
         return 0, 0
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(idx)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _workspaces[idx] = ws
+    key = workspace_key(device, stream)
+    capturing = torch.cuda.is_current_stream_capturing()
+    with _ws_lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            new = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", key[0]))
+            new[:COUNTER_BYTES].zero_()
+            if capturing:
+                _ws_needs_zero.add(key)
+            if ws is not None:
+                _ws_retired.append(ws)
+            _workspaces[key] = ws = new
+        elif key in _ws_needs_zero and not capturing:
+            ws[:COUNTER_BYTES].zero_()
+            _ws_needs_zero.discard(key)
     return ws.data_ptr(), ws.numel()
+
+
+def reserve_workspace(nbytes: int, device=None, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Size the workspace of (device, stream) now, e.g. before capturing a
+    graph on that stream (workspace_bytes gives a call's need)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    _workspace(nbytes, dev, stream)
 
 
 def _force(parts=None, mode=None, bm=None, decoder=None, groups=None, unit=None, wg_cols=None) -> Optional[_Plan]:
@@ -240,9 +275,12 @@ def workspace_bytes(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decod
     return n
 
 
-def plan(w: Exl3Weight, M: int) -> dict:
+def plan(w: Exl3Weight, M: int, parts=None, mode=None, bm=None, decoder=None, groups=None, unit=None,
+         wg_cols=None) -> dict:
+    """The plan exl3_linear uses for M rows (or with the given fields forced)."""
+    f = _force(parts, mode, bm, decoder, groups, unit, wg_cols)
     p = _Plan()
-    _check(load().exl3_plan_query(ctypes.byref(w.view()), M, ctypes.byref(p)))
+    _check(load().exl3_plan_query_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None, ctypes.byref(p)))
     return {"parts": p.parts, "groups": p.groups, "mode": p.mode, "bm": p.bm, "decoder": p.decoder,
             "unit": p.unit, "launches": p.launches, "wg_cols": p.wg_cols, "workspace": p.workspace}
 

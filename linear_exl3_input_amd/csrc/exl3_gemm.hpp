@@ -582,7 +582,7 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
   const uint16_t *trellis = p.trellis, *svh = p.svh, *bias = p.bias;
   if constexpr (MOE) {
     const int e = __builtin_amdgcn_readfirstlane(p.block_expert[m0 / BM]);
-    if (e < 0) return;
+    if (e < 0 || e >= p.n_experts) return;
     trellis += (int64_t)e * p.expert_trellis;
     svh += (int64_t)e * N;
     if (bias != nullptr) bias += (int64_t)e * N;

@@ -181,6 +181,8 @@ constexpr int32_t TABLE_MAX_M = 64;
 constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
 // Partial slabs beyond this go through the fused fold (or row chunks).
 constexpr double SLAB_CAP_BYTES = 192.0 * 1024 * 1024;
+// Slab bytes the finishing workgroup's 32-bit buffer offsets reach.
+constexpr double FINISHER_MAX_SLAB_BYTES = 2147483648.0;  // 2 GiB
 // Tiles the finisher's counters can hold (one 32-bit counter each).
 constexpr int64_t MAX_COUNTERS = EXL3_WORKSPACE_COUNTER_BYTES / 4;
 // Dense path (dequantize once, then a plain MFMA GEMM): batches and layers
@@ -195,7 +197,9 @@ size_t slab_bytes(int32_t n_slabs, int32_t rows, int32_t N) {
   return (size_t)n_slabs * (size_t)((rows + 3) / 4) * 4 * (size_t)N * sizeof(float);
 }
 
-exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out) {
+// slab_cap: the partial slabs a plan may keep at once (row chunks beyond it).
+exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out,
+                      double slab_cap = SLAB_CAP_BYTES) {
   Plan pl;
   const int32_t KB = w->K / 128;
   const int32_t nblk = w->N / 128;
@@ -260,7 +264,7 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   const size_t full_slabs = slab_bytes(pl.groups, M, w->N);
   if (pl.parts == 1 || pl.groups == 1) pl.mode = EXL3_MODE_FUSED;
   else if (Q > 1) pl.mode = EXL3_MODE_SLABS;
-  else pl.mode = (double)full_slabs <= SLAB_CAP_BYTES ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
+  else pl.mode = (double)full_slabs <= slab_cap ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
   if (force && force->mode != EXL3_MODE_AUTO && force->mode >= 0) {
     if (force->mode != EXL3_MODE_FUSED && force->mode != EXL3_MODE_SLABS)
       return fail(EXL3_ERR_INVALID_ARG, "forced mode=%d, must be 0 (fused) or 1 (slabs)", force->mode);
@@ -302,15 +306,19 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   }
   const int32_t n_slabs = pl.parts / pl.unit;
   pl.chunk = M;
-  if (pl.mode == EXL3_MODE_SLABS && (double)slab_bytes(n_slabs, M, w->N) > SLAB_CAP_BYTES) {
+  if (pl.mode == EXL3_MODE_SLABS && (double)slab_bytes(n_slabs, M, w->N) > slab_cap) {
     const double per_tile = (double)slab_bytes(n_slabs, pl.bm, w->N);
-    pl.chunk = (int32_t)std::max<double>(pl.bm, std::floor(SLAB_CAP_BYTES / per_tile) * pl.bm);
+    pl.chunk = (int32_t)std::max<double>(pl.bm, std::floor(slab_cap / per_tile) * pl.bm);
     pl.chunk = std::min(pl.chunk, M);
   }
   // (The table kernel keeps the second kernel: a finishing team inside it
   // measured slower, 21 -> 25 us on q_proj at one row.)
+  // The finishing workgroup addresses the slabs with 32-bit buffer offsets:
+  // a (forced) plan with 2 GiB of slabs or more sums them in the second
+  // kernel instead, which uses 64-bit addresses.
   pl.finisher = pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 &&
-                (int64_t)nblk * ((pl.chunk + pl.bm - 1) / pl.bm) <= MAX_COUNTERS;
+                (int64_t)nblk * ((pl.chunk + pl.bm - 1) / pl.bm) <= MAX_COUNTERS &&
+                (double)slab_bytes(n_slabs, pl.chunk, w->N) < FINISHER_MAX_SLAB_BYTES;
   // Small tiles in slab mode with fewer workgroups than CUs: split each
   // 128-column block between two workgroups of half the waves (the same
   // per-wave work on twice the CUs; the finishing workgroup or the output
@@ -344,7 +352,8 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
 
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
-                       bool with_output, const int32_t *block_expert = nullptr, int64_t expert_trellis = 0);
+                       bool with_output, const int32_t *block_expert = nullptr, int64_t expert_trellis = 0,
+                       int32_t n_experts = 0);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -535,13 +544,17 @@ size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan 
 size_t exl3_workspace_bytes(const exl3_weight *w, int32_t M) { return exl3_workspace_bytes_ex(w, M, nullptr); }
 
 exl3_status exl3_plan_query(const exl3_weight *w, int32_t M, exl3_plan *plan) {
+  return exl3_plan_query_ex(w, M, nullptr, plan);
+}
+
+exl3_status exl3_plan_query_ex(const exl3_weight *w, int32_t M, const exl3_plan *force, exl3_plan *plan) {
   clear_error();
   exl3_status st = validate_weight(w, false, false);
   if (st != EXL3_OK) return st;
   if (plan == nullptr) return fail(EXL3_ERR_INVALID_ARG, "plan (host output) is NULL");
   if (M < 0 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
   Plan pl;
-  if ((st = plan_for(w, M, nullptr, &pl)) != EXL3_OK) return st;
+  if ((st = plan_for(w, M, force, &pl)) != EXL3_OK) return st;
   plan->parts = pl.parts;
   plan->groups = pl.groups;
   plan->mode = pl.mode;
@@ -594,10 +607,11 @@ namespace {
 // the plan has the finisher, else as a second kernel).
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
-                       bool with_output, const int32_t *block_expert, int64_t expert_trellis) {
+                       bool with_output, const int32_t *block_expert, int64_t expert_trellis, int32_t n_experts) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.block_expert = block_expert;
+  p.n_experts = n_experts;
   p.expert_trellis = expert_trellis;
   p.trellis = w->trellis;
   p.x_rot = x_rot;
@@ -861,7 +875,7 @@ exl3_status exl3_moe_input_transform(const void *x, int32_t x_dtype, int32_t swi
   if ((st = check_ptr(block_expert, "block_expert")) != EXL3_OK) return st;
   if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
   const hipError_t e = exl3::launch_input_transform(x, x_dtype == EXL3_BF16, swiglu != 0, rows, K, suh, n_shards,
-                                                    x_rot, (hipStream_t)stream, row_pair, block_expert, topk, block);
+                                                    x_rot, (hipStream_t)stream, row_pair, block_expert, topk, block, E);
   return e == hipSuccess ? EXL3_OK : launch_error(e, "moe input transform launch");
 }
 
@@ -938,7 +952,7 @@ exl3_status exl3_moe_linear(const exl3_weight *w, int32_t E, const uint16_t *x_r
   float *slabs = pl.workspace > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.slab_off) : nullptr;
   const int64_t expert_words = (int64_t)w->K / 16 * (w->N / 16) * 16 * w->bits;
   return run_linear(w, x_rot, rows, y, y_dtype, counters, slabs, nullptr, pl, (hipStream_t)stream, true, block_expert,
-                    expert_words);
+                    expert_words, E);
 }
 
 exl3_status exl3_moe_combine(const void *y_routed, int32_t dtype, const int32_t *pair_row, const float *topk_weights,

@@ -35,6 +35,8 @@ struct GemmParams {
   const uint16_t *bias;         // [N] fp16 added before the output rounding, or null
   const int32_t *block_expert;  // grouped (MoE) calls: expert of each row block (-1: none), else null
   int64_t expert_trellis;       // grouped calls: trellis words per expert
+  int32_t n_experts;            // grouped calls: experts in the stack; a block's
+                                // expert outside 0..n_experts-1 is skipped like -1
 };
 
 struct DecodeParams {
@@ -65,7 +67,7 @@ hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hi
 hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32_t M, int32_t K,
                                   const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s,
                                   const int32_t *row_pair = nullptr, const int32_t *block_expert = nullptr,
-                                  int32_t topk = 1, int32_t block = 16);
+                                  int32_t topk = 1, int32_t block = 16, int32_t n_experts = 0);
 // MoE routing: alignment of (token, expert) pairs into row blocks, and the
 // ordered combine of each token's routed rows (exl3_moe.hip).
 hipError_t launch_moe_align(const int32_t *topk_ids, int32_t pairs, int32_t E, int32_t block, int32_t rows_max,

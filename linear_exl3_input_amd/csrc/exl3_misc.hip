@@ -102,11 +102,12 @@ __device__ __forceinline__ float swiglu_act(uint32_t gbits, uint32_t ubits) {
 
 // Routed rows (MoE): row m of x~ is the row of pair p = route.row_pair[m]
 // (token p / topk of x; -1: a padding row, rotated as zeros), with the suh
-// rows of its block's expert (suh + expert * n_shards * K).
+// rows of its block's expert (suh + expert * n_shards * K); a block whose
+// expert is outside 0 .. n_experts-1 rotates zeros like a padding row.
 struct Route {
   const int32_t *row_pair;      // null: row m is x's row m
   const int32_t *block_expert;
-  int32_t topk, block;
+  int32_t topk, block, n_experts;
 };
 
 template <bool X_BF16, bool SWIGLU, bool ROUTED>
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
   if (ROUTED && live) {
     const int32_t pr = route.row_pair[m];
     const int32_t e = route.block_expert[m / route.block];
-    zero = pr < 0 || e < 0;
+    zero = pr < 0 || e < 0 || e >= route.n_experts;
     src = zero ? 0 : pr / route.topk;
     suh_e = suh + (int64_t)(zero ? 0 : e) * n_shards * K;
   }
@@ -212,11 +213,11 @@ __global__ __launch_bounds__(256) void input_transform_kernel(const uint16_t *__
 hipError_t launch_input_transform(const void *x, bool x_bf16, bool swiglu, int32_t M, int32_t K,
                                   const uint16_t *suh, int32_t n_shards, uint16_t *x_rot, hipStream_t s,
                                   const int32_t *row_pair, const int32_t *block_expert, int32_t topk,
-                                  int32_t block) {
+                                  int32_t block, int32_t n_experts) {
   const int64_t items = M >= 4 ? (((int64_t)M + 3) / 4) * (K / 128) : (int64_t)M * ((K / 128 + 3) / 4);
   const dim3 grid((unsigned)((items + 3) / 4));
   const uint16_t *xp = static_cast<const uint16_t *>(x);
-  const Route r{row_pair, block_expert, topk, block};
+  const Route r{row_pair, block_expert, topk, block, n_experts};
   const dim3 b(256);
   const int sel = (x_bf16 ? 4 : 0) | (swiglu ? 2 : 0) | (row_pair != nullptr ? 1 : 0);
   switch (sel) {

@@ -57,6 +57,7 @@ U_ACC = 2.0 ** -23
 U_F32 = 2.0 ** -24
 U_OUT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 A_OUT = {"bf16": 2.0 ** -134, "f16": 2.0 ** -25}
+MIN_ROWS_FOR_COLUMNS = 8
 
 
 def gamma(n: int, u: float) -> float:
@@ -197,7 +198,12 @@ def check(y_bits: np.ndarray, ref: Reference, svh_bits: np.ndarray, K: int, out_
     worst = float(np.max(col_rel)) if col_rel.size else 0.0
     gmax = float(np.max(np.abs(ref.y))) if ref.y.size else 0.0
     mrel = float(np.max(err) / gmax) if gmax > 0 else 0.0
-    return CheckResult(ratio <= 1.0 and worst <= worst_col_limit, ratio, worst, mrel, int(y.size))
+    # A column's largest output over a handful of rows can sit arbitrarily
+    # close to zero (the one value of a one-row call, say), where any
+    # rounding is a large relative error; below MIN_ROWS_FOR_COLUMNS rows the
+    # worst column is still reported but the limit applies matrix-wide.
+    rel = worst if y.shape[0] >= MIN_ROWS_FOR_COLUMNS else mrel
+    return CheckResult(ratio <= 1.0 and rel <= worst_col_limit, ratio, worst, mrel, int(y.size))
 
 
 def dense_weight(trellis: np.ndarray, suh_bits: np.ndarray, svh_bits: np.ndarray,

@@ -355,3 +355,22 @@ def test_moe_entry_points_check_arguments():
     assert L.exl3_moe_input_transform(FAKE, 1, 0, 3, 1024, FAKE, 1, 3, FAKE, FAKE, 2, 16, 48, FAKE, None) == 1
     assert "rows=48" in last_error()  # 3 tokens x 2 of 3 experts in blocks of 16: 64 routed rows
     assert L.exl3_moe_combine(FAKE, 1, FAKE, FAKE, 2, 2, 7, FAKE, None) == 1
+
+
+def test_finisher_needs_slabs_under_two_gib():
+    """The finishing workgroup addresses slabs with 32-bit offsets: a forced
+    plan whose slabs reach 2 GiB sums them in the second kernel (64-bit
+    addresses) instead; the same plan with small slabs keeps one launch."""
+    L = ex.load()
+    w = view(16384, (154880,), 4, 1)
+    f = F(128, ex.EXL3_MODE_SLABS, 64, 0, unit=1)
+    p = ex._Plan()
+    assert L.exl3_plan_query_ex(ctypes.byref(w), 64, ctypes.byref(f), ctypes.byref(p)) == 0
+    assert p.workspace >= 2 ** 31 and p.launches == 2
+    small = view(16384, (1024,), 4, 1)
+    assert L.exl3_plan_query_ex(ctypes.byref(small), 64, ctypes.byref(f), ctypes.byref(p)) == 0
+    assert p.workspace < 2 ** 31 and p.launches == 1
+    # the unforced query is the automatic plan
+    q = ex._Plan()
+    assert L.exl3_plan_query_ex(ctypes.byref(w), 64, None, ctypes.byref(q)) == 0
+    assert (q.parts, q.mode, q.bm) == (_plan(w, 64).parts, _plan(w, 64).mode, _plan(w, 64).bm)

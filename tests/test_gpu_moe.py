@@ -3,6 +3,8 @@ supported" and "Determinism").  Synthetic routing; the alignment against the
 oracle's, every routed row bit-identical to the plain linear of its token on
 its expert's weight alone, the combine bit-exact against the oracle's, and the
 whole path within the oracle's bound."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -133,3 +135,46 @@ def test_moe_forward_within_the_oracle_bound(K, shards, bits, cb, E, T, k):
     err = np.abs(got - want)
     banner(f"moe forward K={K} E={E} T={T} k={k}: max err/limit {np.max(err / lim):.3f}")
     assert np.all(err <= lim)
+
+
+def test_out_of_range_block_experts_are_skipped():
+    """A caller-built routing whose block_expert holds an expert index past
+    the stack (or below -1) is treated as a padding block: the routed
+    rotation writes zeros for its rows and the grouped GEMM leaves its output
+    rows untouched, while the valid blocks keep their bits."""
+    E, block, T, k = 3, 16, 20, 2
+    lay, w, _ = _experts(E, 512, (256,), 4, "mcg", 760)
+    ids, _ = _routing(T, k, E, 761)
+    rng = np.random.default_rng(762)
+    x = x_dev(otf.f32_to_bf16_bits(rng.standard_normal((T, w.K)).astype(np.float32)))
+    row_pair, block_expert, pair_row = ex.moe_align(torch.from_numpy(ids).cuda(), E, block)
+    good = block_expert.clone()
+    xr_good = ex.moe_input_transform(x, w, (row_pair, good, pair_row), k, block)
+    y_good = bits16(ex.moe_linear(w, xr_good, good, block))
+    be = block_expert.cpu().numpy()
+    live = np.nonzero(be >= 0)[0]
+    assert live.size >= 3
+    bad_blocks = live[:2]
+    hacked = be.copy()
+    hacked[bad_blocks[0]] = E
+    hacked[bad_blocks[1]] = E + 1000
+    hacked_dev = torch.from_numpy(hacked).cuda()
+    xr = ex.moe_input_transform(x, w, (row_pair, hacked_dev, pair_row), k, block)
+    xr_n = bits16(xr).reshape(w.n_shards, w.K // 32, -1, 32)
+    for b in bad_blocks:
+        assert np.all(xr_n[:, :, block * b:block * (b + 1)] == 0), f"block {b} not rotated as zeros"
+    rows = xr.shape[2]
+    y = torch.full((rows, w.N), 7.0, dtype=torch.bfloat16, device="cuda")
+    L = ex.load()
+    need = L.exl3_moe_workspace_bytes(ctypes.byref(w.first.view()), rows, block)
+    ws, wsn = ex._workspace(need, torch.device("cuda"))
+    ex._check(L.exl3_moe_linear(ctypes.byref(w.first.view()), w.E, xr.data_ptr(), rows, hacked_dev.data_ptr(), block,
+                                y.data_ptr(), 1, ws, wsn, ex._stream()))
+    yb = bits16(y)
+    seven = bits16(torch.full((1,), 7.0, dtype=torch.bfloat16))[0]
+    for b in range(len(be)):
+        r = slice(block * b, block * (b + 1))
+        if b in bad_blocks:
+            assert np.all(yb[r] == seven), f"block {b} written"
+        elif be[b] >= 0:
+            assert np.array_equal(yb[r], y_good[r]), f"block {b}"

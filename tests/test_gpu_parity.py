@@ -345,7 +345,7 @@ def test_finisher_counters_stay_zero():
     for M in (1, 7, 33, 64, 16):
         _run(t, M=M)
     torch.cuda.synchronize()
-    ws = ex._workspaces[torch.cuda.current_device()]
+    ws = ex._workspaces[ex.workspace_key()]
     assert int(torch.count_nonzero(ws[:ex.COUNTER_BYTES])) == 0
     assert np.array_equal(_run(t, M=16), first)
 
@@ -512,10 +512,21 @@ def test_decode_rate_ruler_block_xor(bits, cb):
 
 # --------------------------------------------- full-size workloads, sampled
 
-FULL = [("small_1024x1024_b4_3inst", 16), ("expert_4096x2048_b4_mcg", 512), ("expert_2048x4096_b4_mcg", 16),
-        ("q_proj_5120x12288_b6_mul1", 128), ("q_proj_5120x12288_b6_mul1", 24), ("down_proj_17408x5120_b6_mul1", 16),
-        ("down_proj_17408x5120_b6_mul1", 64),
-        ("gate_up_5120x2x17408_b5_mul1", 2048), ("lm_head_4096x154880_b6_mul1", 16)]
+# Every (layer, M) point of the measured configurations except the bit-width
+# sweep (which has its own test below): 33 points, 57 with the sweep.
+FULL = [(lay.name, M) for lay in wl.LAYERS for M in lay.M_values]
+_FULL_CACHE = {}
+
+
+def _full_layer(name):
+    """Seeded tensors of a full-size layer (x drawn for its largest M) and its
+    device weight, kept for the points of the same layer."""
+    if name not in _FULL_CACHE:
+        _FULL_CACHE.clear()
+        lay = wl.layer(name)
+        t = wl.gen_all(lay)
+        _FULL_CACHE[name] = (lay, t, weight(t))
+    return _FULL_CACHE[name]
 
 
 SWEEP = [(b, cb) for b in range(1, 9) for cb in ("3inst", "mcg", "mul1")]
@@ -537,7 +548,7 @@ def test_sweep_full_size_sampled(bits, cb):
         assert np.array_equal(bits16(ex.linear(w, xr, torch.bfloat16, decoder=dec)), y), f"decoder {dec}"
     y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
     assert np.array_equal(y1[0], y[0])
-    rows, blocks = [0, 31, 63], [0, 13, 31]
+    rows, blocks = [0, 9, 18, 27, 36, 45, 54, 63], [0, 13, 31]
     ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
     res = olin.check(y[rows][:, ref.cols], ref, t.svh, lay.K, "bf16")
     banner(f"{lay.name}: {res}")
@@ -546,11 +557,15 @@ def test_sweep_full_size_sampled(bits, cb):
 
 @pytest.mark.parametrize("name,M", FULL, ids=[f"{f[0]}-M{f[1]}" for f in FULL])
 def test_full_size_sampled(name, M):
-    lay = wl.layer(name)
-    banner(f"full size {name} M={M}")
-    t = wl.gen_all(lay, M=M)
-    w = weight(t)
-    xr = ex.input_transform(x_dev(t.x), w.suh)
+    """A measured configuration at its real shape: the planner's call; the
+    first row alone gives the same bits (batch invariance); the other
+    decoders give the same bits (ALU and table up to 64 rows, ALU and dense
+    from 512); sampled rows and column blocks (both shards' first blocks)
+    within the oracle's bound."""
+    lay, t, w = _full_layer(name)
+    banner(f"full size {name} M={M} plan {ex.plan(w, M)}")
+    x = t.x[:M]
+    xr = ex.input_transform(x_dev(x), w.suh)
     y = bits16(ex.linear(w, xr, torch.bfloat16))
     # batch invariance at the real shape: the first row alone
     y1 = bits16(ex.linear(w, xr[:, :, :1].contiguous(), torch.bfloat16))
@@ -559,10 +574,10 @@ def test_full_size_sampled(name, M):
         for dec in (ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE) if M <= 64 else (ex.EXL3_DECODER_ALU,
                                                                                 ex.EXL3_DECODER_DENSE):
             assert np.array_equal(bits16(ex.linear(w, xr, torch.bfloat16, decoder=dec)), y), f"decoder {dec}"
-    rows = sorted({0, M // 2, M - 1})
+    rows = sorted(set(np.linspace(0, M - 1, min(M, 8)).astype(int).tolist()))
     nblk = lay.N // 128
     blocks = sorted({0, nblk // 3, nblk - 1} | ({lay.shards[0] // 128} if lay.n_shards > 1 else set()))
-    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, x[rows], col_blocks=blocks)
     ysel = y[rows][:, ref.cols]
     res = olin.check(ysel, ref, t.svh, lay.K, "bf16")
     banner(f"{name} M={M} sampled rows {rows} blocks {blocks}: {res}")

@@ -1,10 +1,11 @@
 """GPU: the single-GPU half of a column split, and padded layers.
 
-Column split (the EXL3 survey of the pages, "More than one GPU"): a GPU that
-owns whole 128-column blocks runs its slice of the trellis, svh and shard map
-on the replicated x; its columns have the bits of the full layer's when the
+Column split (cuda-exl3 README, "Tensor parallel" and "Notes on the format":
+trellis and svh concatenate along the output dimension, so a GPU that owns
+whole 128-column blocks runs its slice of the trellis, svh and shard map on
+the replicated x): its columns have the bits of the full layer's when the
 slice runs with the full layer's part tree (P and G come from the global
-shape), which a forced plan carries.
+shape), which a forced plan carries, and they lie within the oracle's bound.
 
 Padded layers (cuda-exl3 README, "Loading into a dim vLLM has padded"): whole
 128-column blocks of output padding with svh zeroed come out exactly zero
@@ -68,6 +69,13 @@ def test_column_slices_match_the_full_layer(M):
         own = ex.plan(ws, M)
         differs |= (own["parts"], own["groups"]) != (pl["parts"], pl["groups"])
     assert differs, "every slice's own plan has the full layer's tree: the forced tree was not exercised"
+    # the slices' columns against the oracle (sampled rows)
+    rows = sorted({0, M // 2, M - 1})
+    blocks = [0, 2944 // 128, 4864 // 128, 7936 // 128, 8064 // 128]
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
+    res = olin.check(y[rows][:, ref.cols], ref, t.svh, lay.K, "bf16")
+    banner(f"column split M={M} vs oracle: {res}")
+    assert res.ok, str(res)
 
 
 @pytest.mark.parametrize("out", [torch.bfloat16, torch.float16])
@@ -91,6 +99,10 @@ def test_padded_output_blocks_are_exact_zeros(out):
         pl = ex.plan(wp, M)
         yr = ex.linear(wr, ex.input_transform(x, wr.suh), out, parts=pl["parts"], groups=pl["groups"])
         assert np.array_equal(bits16(yp[:, :384]), bits16(yr)), f"M={M}"
+        od = "bf16" if out == torch.bfloat16 else "f16"
+        ref = olin.reference(t.trellis, t.suh, t.svh, real.shards, real.bits, real.cb, t.x[:M])
+        res = olin.check(bits16(yr), ref, t.svh, real.K, od)
+        assert res.ok, f"M={M}: {res}"
 
 
 def test_padded_input_positions():

@@ -9,6 +9,7 @@ import torch
 
 import linear_exl3_input_amd as ex
 import workloads as wl
+from oracle import linear as olin
 from gpu_util import banner, bits16, weight, x_dev
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +46,14 @@ def test_tune_keeps_bits_and_is_used(name, M):
         assert now[k] == best[k], k
     y1 = bits16(ex.linear(w, xr, torch.bfloat16))
     assert np.array_equal(y0, y1)
+    # the tuned schedule's output against the oracle (sampled rows and blocks)
+    rows = sorted(set(np.linspace(0, M - 1, min(M, 8)).astype(int).tolist()))
+    nblk = lay.N // 128
+    blocks = sorted({0, nblk // 2, nblk - 1})
+    ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[rows], col_blocks=blocks)
+    res = olin.check(y1[rows][:, ref.cols], ref, t.svh, lay.K, "bf16")
+    banner(f"tuned {name} M={M} vs oracle: {res}")
+    assert res.ok, str(res)
     ex.tune_clear()
     assert ex.plan(w, M) == planned
 

@@ -150,11 +150,16 @@ def test_bench_workloads_name_known_layers():
     24 (bits, codebook) layers at K = N = 4096 with distinct seeds, and its
     first rows are the input recipe's (bf16 of standard normals)."""
     import bench
-    for names, Ms in bench.WORKLOADS.values():
-        for n in names:
+    for spec in bench.WORKLOADS.values():
+        for n, Ms in spec:
             lay = wl.layer(n)
             assert max(Ms) <= lay.M_max
-    sweep = [wl.layer(n) for n in bench.WORKLOADS["sweep_4096x4096_b1-8_all_cb"][0]]
+    # the default step holds every measured configuration: each (layer, M)
+    # of the layer table and of the bit-width sweep
+    default = {(n, M) for n, Ms in bench.WORKLOADS[bench.DEFAULT_WORKLOAD] for M in Ms}
+    assert default == {(l.name, M) for l in wl.LAYERS + wl.SWEEP for M in l.M_values}
+    assert len(default) == 57
+    sweep = [wl.layer(n) for n, _ in bench.WORKLOADS["sweep_4096x4096_b1-8_all_cb"]]
     assert sorted((l.bits, l.codebook) for l in sweep) == sorted(
         (b, cb) for b in range(1, 9) for cb in ("3inst", "mcg", "mul1"))
     assert all(l.K == 4096 and l.N == 4096 and l.M_values == (64,) for l in sweep)
@@ -222,3 +227,19 @@ def test_output_stage_bound_rejects_planted_mistakes():
     y = tf.output_transform_f32(full, svh, "bf16")
     y[:, 128:] = tf.f32_to_bf16_bits(raw[:, 128:])
     assert bad(y)
+
+
+def test_worst_column_limit_needs_enough_rows():
+    """One row whose output in some column is near zero: the element-wise
+    bound holds and the column-relative error is large, so the check uses
+    the matrix-wide relative error there; from 8 rows the column limit
+    applies."""
+    lay = SMALL[0]
+    t, ref = _ref(lay)
+    good = _f32_emulation(t, lay, ref)
+    r1 = ol.Reference(ref.x_rot[:, :1], ref.z[:1], ref.absdot[:1], ref.y[:1], ref.cols)
+    res = ol.check(good[:1], r1, t.svh, lay.K, "bf16")
+    assert res.max_ratio <= 1.0 and res.ok
+    assert ref.y.shape[0] >= ol.MIN_ROWS_FOR_COLUMNS
+    full = ol.check(good, ref, t.svh, lay.K, "bf16")
+    assert full.ok and full.worst_col_rel <= 5e-3
