@@ -245,6 +245,24 @@ exl3_status exl3_linear_ex(const exl3_weight *w, const uint16_t *x_rot, int32_t 
                            int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream,
                            const exl3_plan *force);
 
+/* exl3_linear for callers that cannot allocate (code under graph capture,
+ * serving loops and harnesses that forbid hipMalloc): no workspace
+ * argument.  The split-k partials and arrival counters live in a device
+ * array of EXL3_NOALLOC_SCRATCH_BYTES that the library owns, one per GPU it
+ * runs on, held until the process ends.  The output has exactly the bits of
+ * exl3_linear (the same part tree): the planner's schedule when its
+ * workspace fits the array, else another schedule of the same tree that
+ * fits (no dequantized weights, row chunks of the partials, the one-level
+ * fused fold, or smaller row tiles).  The call allocates and frees nothing
+ * and calls no allocating routine; it is asynchronous on `stream`.  All
+ * calls on one GPU share that GPU's array and it keeps the last call's
+ * contents (the counters are left zero): calls that overlap on one GPU race.
+ * Errors as exl3_linear, and EXL3_ERR_UNSUPPORTED (naming the sizes) if no
+ * schedule of the layer's tree fits the array. */
+#define EXL3_NOALLOC_SCRATCH_BYTES (64u << 20)
+exl3_status exl3_linear_noalloc(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
+                                void *stream);
+
 /* Workspace bytes for exl3_linear_ex with the same `force`. */
 size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan *force);
 

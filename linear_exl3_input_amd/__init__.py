@@ -97,6 +97,7 @@ def load() -> ctypes.CDLL:
             "exl3_workspace_bytes_ex": (sz, [W, i32, P]),
             "exl3_linear": (i32, [W, vp, i32, vp, i32, vp, sz, vp]),
             "exl3_linear_ex": (i32, [W, vp, i32, vp, i32, vp, sz, vp, P]),
+            "exl3_linear_noalloc": (i32, [W, vp, i32, vp, i32, vp]),
             "exl3_plan_query": (i32, [W, i32, P]),
             "exl3_plan_query_ex": (i32, [W, i32, P, P]),
             "exl3_status_str": (ctypes.c_char_p, [i32]),

@@ -24,7 +24,7 @@ LIB_NAME = "libexl3.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["exl3_host.cpp", "exl3_misc.hip", "exl3_moe.hip", "exl3_rulers.hip", "gemm_dense.hip"] + [f"gemm_b{b}.hip" for b in range(1, 9)]
+SOURCES = ["exl3_host.cpp", "exl3_misc.hip", "exl3_moe.hip", "exl3_rulers.hip", "exl3_noalloc.hip", "gemm_dense.hip"] + [f"gemm_b{b}.hip" for b in range(1, 9)]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1118,3 +1118,87 @@ exl3_status exl3_debug_epilogue(const float *z_parts, int32_t n_parts, int32_t g
 }
 
 }  // extern "C"
+
+namespace {
+
+// A schedule of the layer's own part tree (so the same bits as exl3_linear)
+// whose workspace fits `bytes`: the planner's when it fits; else, without
+// dequantized fragments, partial slabs in row chunks within the space left
+// after the counters; else the one-level fused fold where the tree has one;
+// else slabs with smaller row tiles.  Every automatic tree fits a few MiB:
+// groups that split into parts (the only trees with no fused schedule) come
+// with fewer than 512 column-block x group pairs, 8 KB of slabs each per
+// 16-row tile.
+exl3_status scratch_plan(const exl3_weight *w, int32_t M, size_t bytes, Plan *out) {
+  Plan pl;
+  exl3_status st = plan_for(w, M, nullptr, &pl);
+  if (st != EXL3_OK) return st;
+  if (pl.workspace <= bytes) {
+    *out = pl;
+    return EXL3_OK;
+  }
+  const Plan want = pl;
+  const double cap = (double)bytes - EXL3_WORKSPACE_COUNTER_BYTES;
+  exl3_plan f;
+  f.parts = want.parts;
+  f.groups = want.groups;
+  f.mode = EXL3_MODE_AUTO;
+  f.bm = -1;
+  f.decoder = want.decoder == EXL3_DECODER_DENSE ? EXL3_DECODER_ALU : want.decoder;
+  f.unit = -1;
+  f.launches = 0;
+  f.wg_cols = -1;
+  f.workspace = 0;
+  auto fits = [&](const exl3_plan &g) { return make_plan(w, M, &g, &pl, cap) == EXL3_OK && pl.workspace <= bytes; };
+  bool ok = fits(f);
+  if (!ok) {
+    f.mode = EXL3_MODE_FUSED;
+    ok = fits(f);
+  }
+  const int32_t tiles[] = {256, 128, 64, 32, 16};
+  for (int i = 0; !ok && i < 5; ++i) {
+    f.mode = EXL3_MODE_SLABS;
+    f.decoder = EXL3_DECODER_ALU;
+    f.bm = tiles[i];
+    ok = fits(f);
+  }
+  clear_error();
+  if (!ok)
+    return fail(EXL3_ERR_UNSUPPORTED,
+                "no schedule of this layer's tree (%d parts, %d groups) fits the %zu-byte scratch at M=%d; the "
+                "planner's needs %zu (over by %zu)", want.parts, want.groups, bytes, M, want.workspace,
+                want.workspace - bytes);
+  *out = pl;
+  return EXL3_OK;
+}
+
+}  // namespace
+
+namespace exl3 {
+
+exl3_status linear_in_scratch(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
+                              void *scratch, size_t scratch_bytes, void *stream, bool launch) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, false);
+  if (st != EXL3_OK) return st;
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
+  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
+  Plan pl;
+  if ((st = scratch_plan(w, M, scratch_bytes, &pl)) != EXL3_OK) return st;
+  if (M == 0) return EXL3_OK;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  if (!launch) return EXL3_OK;
+  uint32_t *counters = static_cast<uint32_t *>(scratch);
+  float *slabs = pl.workspace > 0 ? reinterpret_cast<float *>(static_cast<char *>(scratch) + pl.slab_off) : nullptr;
+  uint16_t *dense = pl.decoder == EXL3_DECODER_DENSE
+                        ? reinterpret_cast<uint16_t *>(static_cast<char *>(scratch) + pl.dense_off)
+                        : nullptr;
+  return run_linear(w, x_rot, M, y, y_dtype, counters, slabs, dense, pl, (hipStream_t)stream, true);
+}
+
+exl3_status scratch_setup_error(hipError_t e, const char *what) { return launch_error(e, what); }
+
+}  // namespace exl3
