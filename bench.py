@@ -89,7 +89,7 @@ def kernel_key(lay, plan) -> str:
     if plan.get("decoder") == 1:
         return f"exl3::gemm_table_kernel<{lay.bits}, {cb}u, 2>"
     if plan.get("decoder") == 2:
-        return f"exl3::gemm_dense_kernel<{str(unit > 1).lower()}>"
+        return "exl3::gemm_dense_kernel<true>" if unit > 1 else "exl3::gemm_dense_wide_kernel"
     quads = unit if (bm <= 64 and unit in (2, 4) and (lay.K // 128) % plan["parts"] == 0) else 1
     multi = unit > 1 and quads == 1
     if bm <= 64:

@@ -226,9 +226,224 @@ __global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmPar
   }
 }
 
+// Wide tiles for one part per workgroup (one K part, or slab mode with one
+// part per slab): 256 rows x 256 columns (two column blocks of one shard) on
+// 8 waves, two per SIMD; wave w = 4 rw + cw owns rows 128 rw .. +127 (A
+// fragments 8 rw .. 8 rw + 7) and the 64 columns of fragments 4 (cw & 1) ..
+// +3 of column block cw >> 1: per 32-k step 8 A and 4 B fragment reads and 32
+// MFMAs into 128 accumulators.  Against 64 x 64 wave tiles on a 256 x 128
+// tile, each product needs a quarter less LDS reading, each k-step's
+// operand loads serve twice the products, and a barrier comes every 32
+// products instead of 16; the 128 accumulators leave no room for a second
+// set, so units of several parts keep gemm_dense_kernel.  The accumulators
+// live in accumulation registers (mfma_acc).  A shard with an odd number of
+// column blocks ends in a one-block tile whose second half is computed on a
+// copy of the first block's fragments and never stored.  Same fragments,
+// same k order and same chains as every other kernel, so the same bits.
+__device__ __forceinline__ void mfma_acc(float4_t &acc, const half8_t &a, const half8_t &b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Reads of asm-product accumulators by vector instructions wait here: the
+// compiler cannot see an asm product's latency (eight passes, plus the
+// accumulator-read hazard); 24 wait states cover both.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+constexpr int DW_THREADS = 512;
+constexpr int DW_PF = 4;                               // ring slots
+constexpr int DW_A_DW = 16 * 256;                      // 16 A fragments: 16 KB
+constexpr int DW_B_DW = 16 * 256;                      // 2 blocks x 8 B fragments: 16 KB
+constexpr int DW_SLOT_DW = DW_A_DW + DW_B_DW;
+constexpr int DW_LOADS = DW_SLOT_DW / DW_THREADS / 4;  // 16-byte loads per lane per k-step (4)
+
+// Column tiles of the wide kernel: each shard's blocks in pairs, an odd
+// shard ending in a one-block tile.  Tile t -> first block, blocks (1 or 2),
+// shard.
+__device__ __forceinline__ void wide_col_tile(const GemmParams &p, int t, int &nb, int &nbk, int &shard) {
+  int start = 0;
+  shard = 0;
+  for (int s = 0; s < p.n_shards; ++s) {
+    const int end = p.shard_end_blk[s];
+    const int tiles = (end - start + 1) >> 1;
+    if (t < tiles || s == p.n_shards - 1) {
+      nb = start + 2 * t;
+      nbk = end - nb >= 2 ? 2 : 1;
+      shard = s;
+      return;
+    }
+    t -= tiles;
+    start = end;
+  }
+}
+
+__global__ __launch_bounds__(DW_THREADS, 1) void gemm_dense_wide_kernel(const GemmParams p, int col_tiles) {
+  constexpr int PF = DW_PF;
+  constexpr int MAIN_DW = PF * DW_SLOT_DW;
+  constexpr int Z_DW = 64 * Z_ROW;
+  constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
+  static_assert(LDS_DW * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rw = wave >> 2;
+  const int cw = wave & 3;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  int ct, mt;
+  dense_tile(blockIdx.x, gridDim.x, (p.row_end - p.row_base + DN_BM - 1) / DN_BM, ct, mt);
+  (void)col_tiles;
+  int nb, nbk, shard;
+  wide_col_tile(p, ct, nb, nbk, shard);
+  const int m0 = p.row_base + mt * DN_BM;
+  const int rend = p.row_end;
+  const int M = p.M, K = p.K, N = p.N;
+  const int KB = K >> 7;
+  const int nblk = N >> 7;
+
+  // one part: blockIdx.y (slab mode, one part per slab) or all of K
+  const int part = blockIdx.y;
+  const int kb_begin = (int)((int64_t)part * KB / p.parts);
+  const int kb_end = (int)((int64_t)(part + 1) * KB / p.parts);
+  const int ks_begin = 4 * kb_begin;
+  const int nks = 4 * (kb_end - kb_begin);
+
+  const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
+  // the second block of a one-block tile reads the first block's fragments
+  const int b_second = nbk == 2 ? 8 * 64 * 8 : 0;
+
+  uint32_t a_src[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    int row = m0 + 16 * (8 * r + wave) + (lane & 15);
+    row = row < rend ? row : rend - 1;
+    a_src[r] = (uint32_t)(row * 32 + 8 * (lane >> 4));
+  }
+  auto issue = [&](int ks, int slot) __attribute__((always_inline)) {
+    const int kk = ks_begin + (ks < nks ? ks : nks - 1);
+    uint32_t *const sl = lds + slot * DW_SLOT_DW;
+    const uint16_t *const abase = xs + (int64_t)kk * M * 32;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(abase + a_src[r]),
+                                       (__attribute__((address_space(3))) void *)(sl + (8 * r + wave) * 256), 16, 0,
+                                       0);
+    const uint16_t *const bbase = p.dense + ((int64_t)kk * nblk + nb) * (8 * 64 * 8);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void *)(bbase + r * b_second + (wave * 64 + lane) * 8),
+          (__attribute__((address_space(3))) void *)(sl + DW_A_DW + (8 * r + wave) * 256), 16, 0, 0);
+  };
+
+  half8_t A[2][8], B[2][4];
+  auto read_frags = [&](int ks, int set) __attribute__((always_inline)) {
+    const uint32_t *const sl = lds + (ks % PF) * DW_SLOT_DW + 4 * lane;
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) B[set][fi] = *(const half8_t *)(sl + DW_A_DW + (4 * cw + fi) * 256);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) A[set][m] = *(const half8_t *)(sl + (8 * rw + m) * 256);
+  };
+
+  float4_t acc[8][4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) acc[m][fi] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i < PF; ++i) issue(i, i);
+  wait_vmcnt<DW_LOADS * (PF - 1)>();  // k-step 0 landed
+  barrier_lds();
+  read_frags(0, 0);
+
+  auto step = [&](int i, auto set_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(set_c)::value;
+    wait_vmcnt<DW_LOADS * (PF - 2)>();  // k-step i+1 landed
+    barrier_lds();                        // ... for every wave; slot i % PF is free
+    issue(i + PF, i % PF);
+    if (i + 1 < nks) read_frags(i + 1, cur ^ 1);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi) mfma_acc(acc[m][fi], A[cur][m], B[cur][fi]);
+  };
+  // nks is a multiple of 4: two k-steps per trip keep the register sets static
+  for (int i = 0; i < nks; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
+  }
+  mfma_drain();
+  wait_vmcnt<0>();  // the clamped tail loads land before LDS is reused
+  barrier_lds();
+
+  const int cb_w = cw >> 1;  // the wave's column block within the tile
+  int col[4];
+#pragma unroll
+  for (int fi = 0; fi < 4; ++fi) col[fi] = lane_col((4 * (cw & 1) + fi) >> 1, j, (4 * (cw & 1) + fi) & 1);
+
+  if (p.slab_mode) {
+    if (cb_w < nbk) {
+      const int rows = rend - p.row_base;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi)
+          store_partial(p.slabs, part, rows, N, m0 - p.row_base + 128 * rw + 16 * m + 4 * g,
+                        (nb + cb_w) * 128 + col[fi], acc[m][fi]);
+    }
+    return;
+  }
+
+  // output transform through LDS, 64 rows of one column block per pass:
+  // pass q = (half, row half, block) -> rows 128 rh + 64 half .. +63
+  float *z = reinterpret_cast<float *>(lds);
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int cb = pass & 1, rh = (pass >> 1) & 1, half = pass >> 2;
+    if (cb >= nbk) continue;  // uniform: the tile's block count
+    if (pass > 0) barrier_lds();
+    if (rw == rh && cb_w == cb) {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[(mm * 16 + 4 * g + e) * Z_ROW + col[fi]] = acc[4 * half + mm][fi][e];
+    }
+    barrier_lds();
+    for (int r = wave; r < 64; r += 8) {
+      const int row = m0 + rh * 128 + half * 64 + r;
+      if (row >= rend) break;
+      const float z0 = z[r * Z_ROW + 2 * lane];
+      const float z1 = z[r * Z_ROW + 2 * lane + 1];
+      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, (nb + cb) * 128, lane);
+      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, (nb + cb) * 128, lane);
+    }
+  }
+}
+
+// Column tiles of the wide kernel for a layer's shard map.
+int wide_col_tiles(const GemmParams &p) {
+  int start = 0, tiles = 0;
+  for (int s = 0; s < p.n_shards; ++s) {
+    tiles += (p.shard_end_blk[s] - start + 1) >> 1;
+    start = p.shard_end_blk[s];
+  }
+  return tiles;
+}
+
 hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (multi) hipLaunchKernelGGL((gemm_dense_kernel<true>), grid, dim3(DN_THREADS), 0, s, p);
-  else hipLaunchKernelGGL((gemm_dense_kernel<false>), grid, dim3(DN_THREADS), 0, s, p);
+  // grid: (column blocks x row tiles, units); the wide kernel takes units of
+  // one part (its column tiles pair the blocks of each shard)
+  if (multi) {
+    hipLaunchKernelGGL((gemm_dense_kernel<true>), grid, dim3(DN_THREADS), 0, s, p);
+  } else {
+    const int ct = wide_col_tiles(p);
+    const int mtiles = (int)grid.x / (p.N / 128);
+    const dim3 g2((unsigned)(ct * mtiles), grid.y, 1);
+    hipLaunchKernelGGL(gemm_dense_wide_kernel, g2, dim3(DW_THREADS), 0, s, p, ct);
+  }
   return hipGetLastError();
 }
 

@@ -374,3 +374,13 @@ def test_finisher_needs_slabs_under_two_gib():
     q = ex._Plan()
     assert L.exl3_plan_query_ex(ctypes.byref(w), 64, None, ctypes.byref(q)) == 0
     assert (q.parts, q.mode, q.bm) == (_plan(w, 64).parts, _plan(w, 64).mode, _plan(w, 64).bm)
+
+
+def test_wide_layers_keep_k_whole():
+    """From 256 column blocks a layer is one K part at every M (gate_up's
+    34816 columns, the lm_head's 154880); below, the split rule holds."""
+    for K, shards, bits in ((5120, (17408, 17408), 5), (4096, (154880,), 6), (5120, (32768,), 4)):
+        w = view(K, shards, bits, 2)
+        for M in (1, 16, 128, 2048):
+            assert (_plan(w, M).parts, _plan(w, M).groups) == (1, 1), (K, shards, M)
+    assert _plan(view(5120, (32640,), 4, 2), 1).parts > 1  # 255 blocks

@@ -72,7 +72,7 @@ def _violations(asm_path: str, window: int = 8) -> list:
 
 
 def test_every_mfma_operand_written_two_wait_states_earlier(tmp_path):
-    srcs = [os.path.join(b.CSRC, f"gemm_b{bits}.hip") for bits in range(1, 9)]
+    srcs = [os.path.join(b.CSRC, f"gemm_b{bits}.hip") for bits in range(1, 9)] + [os.path.join(b.CSRC, "gemm_dense.hip")]
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
         outs = list(ex.map(lambda s: _asm(s, str(tmp_path)), srcs))
     total = sum(sum(1 for l in open(o) if l.strip().startswith("v_mfma")) for o in outs)
@@ -93,3 +93,62 @@ def test_checker_sees_a_too_close_write(tmp_path):
                    "v_mfma_f32_16x16x32_f16 a[4:7], v[14:17], v[44:47], a[4:7]\n")
     bad = _violations(str(asm))
     assert len(bad) == 1 and "v41" in bad[0]
+
+
+# A vector instruction reading a matrix-core result needs more wait states
+# than the product has passes (gfx950: 8-pass 16x16x32 fp16 products need 11
+# before a VALU or accumulation-register read of their destination).  The
+# compiler counts them for the products it emits; the wide dense kernel's
+# products are asm (accumulators pinned to accumulation registers) and wait
+# behind an explicit drain, which this checks.
+MIN_RESULT_WAIT_STATES = 11
+
+
+def _result_violations(asm_path: str, window: int = 40) -> list:
+    lines = [l.strip() for l in open(asm_path)]
+    ins = [l for l in lines if l and not l.startswith((";", ".")) and not l.endswith(":")]
+    bad = []
+    for n, x in enumerate(ins):
+        if not x.startswith("v_mfma"):
+            continue
+        dst = _regs(x.split(None, 1)[1].split(",")[0])
+        waits = 0
+        for y in ins[n + 1:n + 1 + window]:
+            if y.startswith("s_nop"):
+                waits += int(y.split()[1]) + 1
+            else:
+                if not y.startswith("v_mfma") and " " in y:
+                    ops = y.split(None, 1)[1].split(",")
+                    reads = set().union(*[_regs(o) for o in ops[1:]]) if len(ops) > 1 else set()
+                    if y.startswith(("v_accvgpr_read", "global_store", "buffer_store", "ds_write", "scratch_store")):
+                        reads |= set().union(*[_regs(o) for o in ops])
+                    if reads & dst:
+                        if waits < MIN_RESULT_WAIT_STATES:
+                            bad.append(f"{os.path.basename(asm_path)}: {x[:50]} -> {waits} -> {y[:50]}")
+                        break
+                    if _regs(ops[0]) & dst and not y.startswith("v_mfma"):
+                        break  # overwritten before any read
+                waits += 1
+            if waits >= MIN_RESULT_WAIT_STATES:
+                break
+    return bad
+
+
+def test_mfma_results_read_after_their_passes(tmp_path):
+    out = _asm(os.path.join(b.CSRC, "gemm_dense.hip"), str(tmp_path))
+    assert sum(1 for l in open(out) if "v_mfma_f32_16x16x32_f16 a[" in l) > 32  # the asm products
+    bad = _result_violations(out)
+    assert not bad, f"{len(bad)} MFMA results read too soon, e.g. {bad[:3]}"
+
+
+def test_result_checker_sees_a_too_early_read(tmp_path):
+    asm = tmp_path / "planted_result.s"
+    asm.write_text("v_mfma_f32_16x16x32_f16 a[0:3], v[14:17], v[40:43], a[0:3]\n"
+                   "s_nop 3\n"
+                   "v_accvgpr_read_b32 v5, a2\n"
+                   "v_mfma_f32_16x16x32_f16 a[4:7], v[14:17], v[40:43], a[4:7]\n"
+                   "s_nop 7\n"
+                   "s_nop 7\n"
+                   "v_accvgpr_read_b32 v6, a5\n")
+    bad = _result_violations(str(asm))
+    assert len(bad) == 1 and "v5, a2" in bad[0]
