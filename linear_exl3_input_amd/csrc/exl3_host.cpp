@@ -191,6 +191,8 @@ constexpr int32_t TABLE_MAX_M = 64;
 constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
 // Partial slabs beyond this go through the fused fold (or row chunks).
 constexpr double SLAB_CAP_BYTES = 192.0 * 1024 * 1024;
+// Row tiles a tile-kernel launch can hold (the grid's third dimension).
+constexpr int32_t MAX_GRID_Z = 65535;
 // Slab bytes the finishing workgroup's 32-bit buffer offsets reach.
 constexpr double FINISHER_MAX_SLAB_BYTES = 2147483648.0;  // 2 GiB
 // Tiles the finisher's counters can hold (one 32-bit counter each).
@@ -316,10 +318,13 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   }
   const int32_t n_slabs = pl.parts / pl.unit;
   pl.chunk = M;
-  if (pl.mode == EXL3_MODE_SLABS && (double)slab_bytes(n_slabs, M, w->N) > slab_cap) {
+  // the tile kernels put row tiles on the grid's third dimension (at most
+  // 65535 a launch): a million rows in 16-row tiles run in two launches
+  if (pl.decoder == EXL3_DECODER_ALU && (int64_t)M > (int64_t)MAX_GRID_Z * pl.bm) pl.chunk = MAX_GRID_Z * pl.bm;
+  if (pl.mode == EXL3_MODE_SLABS && (double)slab_bytes(n_slabs, pl.chunk, w->N) > slab_cap) {
     const double per_tile = (double)slab_bytes(n_slabs, pl.bm, w->N);
     pl.chunk = (int32_t)std::max<double>(pl.bm, std::floor(slab_cap / per_tile) * pl.bm);
-    pl.chunk = std::min(pl.chunk, M);
+    pl.chunk = std::min(pl.chunk, std::min(M, MAX_GRID_Z * pl.bm));
   }
   // (The table kernel keeps the second kernel: a finishing team inside it
   // measured slower, 21 -> 25 us on q_proj at one row.)
@@ -1019,6 +1024,9 @@ exl3_status exl3_debug_parts(const exl3_weight *w, const uint16_t *x_rot, int32_
   }
   pl.chunk = M;
   pl.finisher = false;
+  if (pl.decoder == EXL3_DECODER_ALU && (int64_t)M > (int64_t)MAX_GRID_Z * pl.bm)
+    return fail(EXL3_ERR_UNSUPPORTED, "the part-sums hook runs one launch: M=%d rows in %d-row tiles exceed %d tiles",
+                M, pl.bm, MAX_GRID_Z);
   pl.half = f.wg_cols == 64 && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && !pl.multi;
   const int32_t n_slabs = pl.parts / pl.unit;
   const size_t need = slab_bytes(n_slabs, M, w->N);
