@@ -196,6 +196,9 @@ def main():
                          "run the fastest")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="counter runs: copy MB of device memory --steps times (a kernel of known bytes)")
+    ap.add_argument("--mfma-calibration", type=int, default=0, metavar="ITERS",
+                    help="counter runs: the matrix-core ruler (ITERS rounds, a kernel of known MFMA count) --steps "
+                         "times")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -222,6 +225,13 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copied {args.copy_calibration} MiB x {args.steps}")
+        return
+    if args.mfma_calibration:
+        out = torch.empty(ex.RULER_WORDS, dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            ex.debug_mfma_loop(args.mfma_calibration, out=out)
+        torch.cuda.synchronize()
+        log(f"mfma ruler x {args.steps}: {ex.mfma_loop_flops(args.mfma_calibration) / 16384:.0f} MFMAs each")
         return
     spec = list(WORKLOADS[args.workload])
     if args.only:

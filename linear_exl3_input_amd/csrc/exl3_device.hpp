@@ -235,6 +235,107 @@ __device__ __forceinline__ void output_row(float z0, float z1, const uint16_t *_
   output_row_words<OUT_BF16>(z0, z1, out_words(svh, bias, n0, lane), bias != nullptr, yrow, n0, lane);
 }
 
+// ---------------------------------------------- output stage, 8 rows a wave
+//
+// The same output stage on eight rows of a 128-column block at a time, with
+// most of the butterfly inside each lane.  Lane L takes row ((L >> 2) & 1) +
+// 2 (L >> 4) of the eight and the 16 consecutive columns 16q .. 16q + 15,
+// q = (L & 3) | (((L >> 3) & 1) << 2), so column bits 0-3 are the lane's
+// register index and column bits 4, 5 and 6 are lane bits 0, 1 and 3.  The
+// strides 1, 2, 4 and 8 are lane-local adds; 16, 32 and 64 pair lanes that
+// differ in bit 0, 1 or 3, whose values arrive by DPP moves (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_ror:8) with no LDS round trip.  The
+// stage order and every add are those of output_row_words, so the bits are
+// the same: the lane holding the upper element of a pair adds its negation
+// to the lower element (a + (-b), exactly a - b), the lower lane adds the
+// upper element to its own (b + a = a + b).
+struct OutWords16 {
+  u32x4_t sv[2], bv[2];  // fp16 svh and bias pairs of the lane's 16 columns
+};
+__device__ __forceinline__ int rows8_group(int lane) { return (lane & 3) | (((lane >> 3) & 1) << 2); }
+__device__ __forceinline__ int rows8_row(int lane) { return ((lane >> 2) & 1) + 2 * (lane >> 4); }
+
+__device__ __forceinline__ OutWords16 out_words16(const uint16_t *__restrict__ svh, const uint16_t *__restrict__ bias,
+                                                  int n0, int lane) {
+  const int c = n0 + 16 * rows8_group(lane);
+  const uint16_t *b = bias != nullptr ? bias : svh;
+  OutWords16 w;
+  w.sv[0] = *(const u32x4_t *)(svh + c);
+  w.sv[1] = *(const u32x4_t *)(svh + c + 8);
+  w.bv[0] = *(const u32x4_t *)(b + c);
+  w.bv[1] = *(const u32x4_t *)(b + c + 8);
+  return w;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void hadamard_lane_stage(float (&v)[16], bool upper) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float other = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[i]), CTRL, 0xF, 0xF, false));
+    v[i] = other + (upper ? -v[i] : v[i]);
+  }
+}
+
+// v: the lane's 16 values of its row (columns 16q .. 16q + 15 of the block),
+// yrow: the row of y, n0: the block's first column.
+template <bool OUT_BF16>
+__device__ __forceinline__ void output_row16(float (&v)[16], const OutWords16 &w, bool has_bias,
+                                             uint16_t *__restrict__ yrow, int n0, int lane) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int bit = 1 << s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!(i & bit)) {
+        const float a = v[i], b = v[i | bit];
+        v[i] = a + b;
+        v[i | bit] = a - b;
+      }
+  }
+  hadamard_lane_stage<0xB1>(v, (lane & 1) != 0);   // quad_perm [1,0,3,2]: stride 16
+  hadamard_lane_stage<0x4E>(v, (lane & 2) != 0);   // quad_perm [2,3,0,1]: stride 32
+  hadamard_lane_stage<0x128>(v, (lane & 8) != 0);  // row_ror:8: stride 64
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sv = w.sv[i >> 2][i & 3], bv = w.bv[i >> 2][i & 3];
+    const float b0 = has_bias ? f16_bits_to_f32(bv & 0xFFFFu) : -0.0f;
+    const float b1 = has_bias ? f16_bits_to_f32(bv >> 16) : -0.0f;
+    const float y0 = keep_f32(keep_f32((v[2 * i] * 0.125f) * f16_bits_to_f32(sv & 0xFFFFu)) + b0);
+    const float y1 = keep_f32(keep_f32((v[2 * i + 1] * 0.125f) * f16_bits_to_f32(sv >> 16)) + b1);
+    if constexpr (OUT_BF16) packed[i] = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+    else packed[i] = f32_to_f16_bits(y0) | (f32_to_f16_bits(y1) << 16);
+  }
+  uint16_t *dst = yrow + n0 + 16 * rows8_group(lane);
+  *(u32x4_t *)dst = u32x4_t{packed[0], packed[1], packed[2], packed[3]};
+  *(u32x4_t *)(dst + 8) = u32x4_t{packed[4], packed[5], packed[6], packed[7]};
+}
+
+// Eight rows r0 .. r0+7 of z (LDS, rows of `stride` floats, 16-byte
+// aligned) through the output stage into y rows row0 .. row0+7; rows at or
+// past rend are skipped.  The DPP partners of a lane always work on the same
+// row (they differ in lane bits 0, 1 and 3 only), so skipping whole rows
+// leaves every partner of a working lane active.
+template <bool OUT_BF16>
+__device__ __forceinline__ void output_rows8(const float *z, int stride, int r0, const OutWords16 &w, bool has_bias,
+                                             uint16_t *__restrict__ y, int64_t row0, int64_t rend, int N, int n0,
+                                             int lane) {
+  const int r = rows8_row(lane);
+  if (row0 + r >= rend) return;
+  const float *src = z + (r0 + r) * stride + 16 * rows8_group(lane);
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4_t t = *(const float4_t *)(src + 4 * i);
+    v[4 * i] = t[0];
+    v[4 * i + 1] = t[1];
+    v[4 * i + 2] = t[2];
+    v[4 * i + 3] = t[3];
+  }
+  output_row16<OUT_BF16>(v, w, has_bias, y + (row0 + r) * N, n0, lane);
+}
+
 // Ordered sum of K-part partials for four rows of one 128-column block, then
 // the output stage of those rows.  Slabs are [n_slabs][M4][N][4] fp32 (the
 // four rows of a column are 16 contiguous bytes); lane l holds columns

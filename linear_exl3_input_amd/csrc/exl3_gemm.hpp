@@ -800,15 +800,12 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
         for (int i = 0; i < 4; ++i) z[(mt * 16 + 4 * g + i) * Z_ROW + col] = acc[mt][h][i];
       }
   }
+  const OutWords16 ow = out_words16(svh, bias, nb * 128, lane);
   barrier_lds();
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-  for (int r = wave_all; r < BM; r += QW * QD) {
-    const int row = m0 + r;
-    if (row >= rend) break;
-    const float z0 = z[r * Z_ROW + 2 * lane];
-    const float z1 = z[r * Z_ROW + 2 * lane + 1];
-    if (p.out_bf16) output_row<true>(z0, z1, svh, bias, y + (int64_t)row * N, nb * 128, lane);
-    else output_row<false>(z0, z1, svh, bias, y + (int64_t)row * N, nb * 128, lane);
+  for (int r0 = 8 * wave_all; r0 < BM && m0 + r0 < rend; r0 += 8 * QW * QD) {
+    if (p.out_bf16) output_rows8<true>(z, Z_ROW, r0, ow, bias != nullptr, y, m0 + r0, rend, N, nb * 128, lane);
+    else output_rows8<false>(z, Z_ROW, r0, ow, bias != nullptr, y, m0 + r0, rend, N, nb * 128, lane);
   }
   }
 }
@@ -1017,6 +1014,7 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
   // output transform, 64 rows at a time through LDS
   float *z = reinterpret_cast<float *>(lds);
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+  const OutWords16 ow = out_words16(p.svh, p.bias, nb * 128, lane);
 #pragma unroll
   for (int pass = 0; pass < MT / 4; ++pass) {
     __syncthreads();
@@ -1031,13 +1029,11 @@ __global__ __launch_bounds__(WG_THREADS, 1) void gemm_big_kernel(const GemmParam
       }
     }
     __syncthreads();
-    for (int r = wave; r < ZROWS; r += 4) {
-      const int row = m0 + pass * ZROWS + r;
-      if (row >= rend) break;
-      const float z0 = z[r * Z_ROW + 2 * lane];
-      const float z1 = z[r * Z_ROW + 2 * lane + 1];
-      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
-      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
+    for (int r0 = 8 * wave; r0 < ZROWS && m0 + pass * ZROWS + r0 < rend; r0 += 32) {
+      if (p.out_bf16)
+        output_rows8<true>(z, Z_ROW, r0, ow, p.bias != nullptr, y, m0 + pass * ZROWS + r0, rend, N, nb * 128, lane);
+      else
+        output_rows8<false>(z, Z_ROW, r0, ow, p.bias != nullptr, y, m0 + pass * ZROWS + r0, rend, N, nb * 128, lane);
     }
   }
 }

@@ -201,6 +201,7 @@ __global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmPar
   }
 
   // output transform, 64 rows (one row of waves) per pass through LDS
+  const OutWords16 ow = out_words16(p.svh, p.bias, nb * 128, lane);
   float *z = reinterpret_cast<float *>(lds);
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
 #pragma unroll
@@ -215,14 +216,10 @@ __global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmPar
           for (int e = 0; e < 4; ++e) z[(m * 16 + 4 * g + e) * Z_ROW + col[fi]] = acc[m][fi][e];
     }
     barrier_lds();
-    for (int r = wave; r < 64; r += 8) {
-      const int row = m0 + pass * 64 + r;
-      if (row >= rend) break;
-      const float z0 = z[r * Z_ROW + 2 * lane];
-      const float z1 = z[r * Z_ROW + 2 * lane + 1];
-      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
-      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
-    }
+    if (p.out_bf16) output_rows8<true>(z, Z_ROW, 8 * wave, ow, p.bias != nullptr, y, m0 + pass * 64 + 8 * wave, rend, N,
+                                       nb * 128, lane);
+    else output_rows8<false>(z, Z_ROW, 8 * wave, ow, p.bias != nullptr, y, m0 + pass * 64 + 8 * wave, rend, N,
+                             nb * 128, lane);
   }
 }
 
@@ -278,7 +275,7 @@ __device__ __forceinline__ void wide_col_tile(const GemmParams &p, int t, int &n
 __global__ __launch_bounds__(DW_THREADS, 1) void gemm_dense_wide_kernel(const GemmParams p, int col_tiles) {
   constexpr int PF = DW_PF;
   constexpr int MAIN_DW = PF * DW_SLOT_DW;
-  constexpr int Z_DW = 64 * Z_ROW;
+  constexpr int Z_DW = DN_BM * Z_ROW;  // one column block of the tile, all rows
   constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
   static_assert(LDS_DW * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_DW];
@@ -318,30 +315,43 @@ __global__ __launch_bounds__(DW_THREADS, 1) void gemm_dense_wide_kernel(const Ge
     row = row < rend ? row : rend - 1;
     a_src[r] = (uint32_t)(row * 32 + 8 * (lane >> 4));
   }
-  auto issue = [&](int ks, int slot) __attribute__((always_inline)) {
+  // load q (0..3) of a k-step: A fragments wave and wave + 8, then the B
+  // fragments wave of each column block
+  auto issue_one = [&](int ks, int slot, int q) __attribute__((always_inline)) {
     const int kk = ks_begin + (ks < nks ? ks : nks - 1);
     uint32_t *const sl = lds + slot * DW_SLOT_DW;
-    const uint16_t *const abase = xs + (int64_t)kk * M * 32;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(abase + a_src[r]),
-                                       (__attribute__((address_space(3))) void *)(sl + (8 * r + wave) * 256), 16, 0,
+    if (q < 2) {
+      const uint16_t *const abase = xs + (int64_t)kk * M * 32;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(abase + a_src[q]),
+                                       (__attribute__((address_space(3))) void *)(sl + (8 * q + wave) * 256), 16, 0,
                                        0);
-    const uint16_t *const bbase = p.dense + ((int64_t)kk * nblk + nb) * (8 * 64 * 8);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
+    } else {
+      const uint16_t *const bbase = p.dense + ((int64_t)kk * nblk + nb) * (8 * 64 * 8);
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void *)(bbase + r * b_second + (wave * 64 + lane) * 8),
-          (__attribute__((address_space(3))) void *)(sl + DW_A_DW + (8 * r + wave) * 256), 16, 0, 0);
+          (const __attribute__((address_space(1))) void *)(bbase + (q - 2) * b_second + (wave * 64 + lane) * 8),
+          (__attribute__((address_space(3))) void *)(sl + DW_A_DW + (8 * (q - 2) + wave) * 256), 16, 0, 0);
+    }
+  };
+  auto issue = [&](int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) issue_one(ks, slot, q);
   };
 
   half8_t A[2][8], B[2][4];
-  auto read_frags = [&](int ks, int set) __attribute__((always_inline)) {
+  // fragment reads in three parts: B, then A 0..3, then A 4..7
+  auto read_part = [&](int ks, int set, int part) __attribute__((always_inline)) {
     const uint32_t *const sl = lds + (ks % PF) * DW_SLOT_DW + 4 * lane;
+    if (part == 0) {
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi) B[set][fi] = *(const half8_t *)(sl + DW_A_DW + (4 * cw + fi) * 256);
+      for (int fi = 0; fi < 4; ++fi) B[set][fi] = *(const half8_t *)(sl + DW_A_DW + (4 * cw + fi) * 256);
+    } else {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) A[set][m] = *(const half8_t *)(sl + (8 * rw + m) * 256);
+      for (int m = 4 * (part - 1); m < 4 * part; ++m) A[set][m] = *(const half8_t *)(sl + (8 * rw + m) * 256);
+    }
+  };
+  auto read_frags = [&](int ks, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int part = 0; part < 3; ++part) read_part(ks, set, part);
   };
 
   float4_t acc[8][4];
@@ -356,16 +366,26 @@ __global__ __launch_bounds__(DW_THREADS, 1) void gemm_dense_wide_kernel(const Ge
   barrier_lds();
   read_frags(0, 0);
 
+  // Each k-step's 32 products run in four groups of eight; one of the k-step's
+  // four direct loads and a part of the next k-step's fragment reads go out
+  // between groups, so no wave stalls on a burst of load issue before its
+  // products (a direct load of 64 x 16 bytes is slow to issue).
   auto step = [&](int i, auto set_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(set_c)::value;
     wait_vmcnt<DW_LOADS * (PF - 2)>();  // k-step i+1 landed
     barrier_lds();                        // ... for every wave; slot i % PF is free
-    issue(i + PF, i % PF);
-    if (i + 1 < nks) read_frags(i + 1, cur ^ 1);
+    const bool more = i + 1 < nks;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int q = 0; q < 4; ++q) {
+      issue_one(i + PF, i % PF, q);
+      if (q < 3 && more) read_part(i + 1, cur ^ 1, q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int fi = 0; fi < 4; ++fi) mfma_acc(acc[m][fi], A[cur][m], B[cur][fi]);
+      for (int m = 2 * q; m < 2 * q + 2; ++m)
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi) mfma_acc(acc[m][fi], A[cur][m], B[cur][fi]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // nks is a multiple of 4: two k-steps per trip keep the register sets static
   for (int i = 0; i < nks; i += 2) {
@@ -394,36 +414,33 @@ __global__ __launch_bounds__(DW_THREADS, 1) void gemm_dense_wide_kernel(const Ge
     return;
   }
 
-  // output transform through LDS, 64 rows of one column block per pass:
-  // pass q = (half, row half, block) -> rows 128 rh + 64 half .. +63
+  // output transform through LDS, one column block (all 256 rows) per pass:
+  // the four waves of the block write their accumulators, then every wave
+  // runs the output stage on 32 rows, eight at a time (output_rows8)
   float *z = reinterpret_cast<float *>(lds);
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+  const bool has_bias = p.bias != nullptr;
+  for (int cb = 0; cb < nbk; ++cb) {
+    const int n0 = (nb + cb) * 128;
+    const OutWords16 w = out_words16(p.svh, p.bias, n0, lane);
+    if (cb > 0) barrier_lds();
+    if (cb_w == cb) {
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int cb = pass & 1, rh = (pass >> 1) & 1, half = pass >> 2;
-    if (cb >= nbk) continue;  // uniform: the tile's block count
-    if (pass > 0) barrier_lds();
-    if (rw == rh && cb_w == cb) {
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[(mm * 16 + 4 * g + e) * Z_ROW + col[fi]] = acc[4 * half + mm][fi][e];
+          for (int e = 0; e < 4; ++e) z[(128 * rw + 16 * m + 4 * g + e) * Z_ROW + col[fi]] = acc[m][fi][e];
     }
     barrier_lds();
-    for (int r = wave; r < 64; r += 8) {
-      const int row = m0 + rh * 128 + half * 64 + r;
-      if (row >= rend) break;
-      const float z0 = z[r * Z_ROW + 2 * lane];
-      const float z1 = z[r * Z_ROW + 2 * lane + 1];
-      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, (nb + cb) * 128, lane);
-      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, (nb + cb) * 128, lane);
+#pragma unroll
+    for (int r0 = 8 * wave; r0 < DN_BM; r0 += 8 * 8) {
+      if (p.out_bf16) output_rows8<true>(z, Z_ROW, r0, w, has_bias, y, m0 + r0, rend, N, n0, lane);
+      else output_rows8<false>(z, Z_ROW, r0, w, has_bias, y, m0 + r0, rend, N, n0, lane);
     }
   }
 }
 
-// Column tiles of the wide kernel for a layer's shard map.
 int wide_col_tiles(const GemmParams &p) {
   int start = 0, tiles = 0;
   for (int s = 0; s < p.n_shards; ++s) {

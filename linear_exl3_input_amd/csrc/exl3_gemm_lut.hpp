@@ -340,15 +340,15 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
           zb[(4 * g + i) * 128 + lane_col(tw, j, 1)] = tot1[mt][i];
         }
         barrier_lds();
-        if (cu.nks > 0) {
+        if (cu.nks > 0 && tw < 2 && 16 * mt + 8 * tw < rows) {
           uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-          for (int r = tw; r < 16 && 16 * mt + r < rows; r += 4) {
-            const float z0 = zb[r * 128 + 2 * lane];
-            const float z1 = zb[r * 128 + 2 * lane + 1];
-            const int64_t row = p.row_base + 16 * mt + r;
-            if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + row * N, cu.nb * 128, lane);
-            else output_row<false>(z0, z1, p.svh, p.bias, y + row * N, cu.nb * 128, lane);
-          }
+          const OutWords16 ow = out_words16(p.svh, p.bias, cu.nb * 128, lane);
+          const int64_t row0 = p.row_base + 16 * mt + 8 * tw;
+          if (p.out_bf16)
+            output_rows8<true>(zb, 128, 8 * tw, ow, p.bias != nullptr, y, row0, p.row_base + rows, N, cu.nb * 128, lane);
+          else
+            output_rows8<false>(zb, 128, 8 * tw, ow, p.bias != nullptr, y, row0, p.row_base + rows, N, cu.nb * 128,
+                                lane);
         }
         barrier_lds();
       }

@@ -67,7 +67,10 @@ struct Wide {
   static constexpr bool AHEAD = PF >= 3 && RW == 128;
   static constexpr int ASLOTS = PF + 1;
   static constexpr int MAIN_DW = FIXED_DW + ASLOTS * ASLOT_DW;
-  static constexpr int Z_DW = 64 * Z_ROW;
+  // output stage: ZR rows (of one row half) per pass through LDS, a whole
+  // row half when the main loop's LDS holds it
+  static constexpr int ZR = MAIN_DW >= RW * Z_ROW ? RW : 64;
+  static constexpr int Z_DW = ZR * Z_ROW;
   static constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
   static constexpr int NY = Geom<BITS>::NY;
   static constexpr int NX = Geom<BITS>::NX;
@@ -417,17 +420,22 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
     return;
   }
 
-  // output transform, 64 rows per pass through LDS
+  // output transform, W::ZR rows of one row half per pass through LDS:
+  // the half's four waves write their accumulators, then every wave runs the
+  // output stage on eight rows at a time (output_rows8)
   float *z = reinterpret_cast<float *>(lds);
   uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-  constexpr int PPH = RW / 64;  // passes per row half
+  constexpr int ZR = W::ZR;
+  constexpr int PPH = RW / ZR;  // passes per row half
+  const OutWords16 ow = out_words16(p.svh, p.bias, nb * 128, lane);
+  const bool has_bias = p.bias != nullptr;
 #pragma unroll
   for (int pass = 0; pass < 2 * PPH; ++pass) {
     if (pass > 0) barrier_lds();
     if (rh == pass / PPH) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int mt = 4 * (pass % PPH) + q;
+      for (int q = 0; q < ZR / 16; ++q) {
+        const int mt = (ZR / 16) * (pass % PPH) + q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           z[(q * 16 + 4 * g + i) * Z_ROW + col_own] = acc[mt][0][i];
@@ -436,13 +444,10 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
       }
     }
     barrier_lds();
-    for (int r = wave; r < 64; r += W::WAVES) {
-      const int row = m0 + pass * 64 + r;
-      if (row >= rend) break;
-      const float z0 = z[r * Z_ROW + 2 * lane];
-      const float z1 = z[r * Z_ROW + 2 * lane + 1];
-      if (p.out_bf16) output_row<true>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
-      else output_row<false>(z0, z1, p.svh, p.bias, y + (int64_t)row * N, nb * 128, lane);
+#pragma unroll
+    for (int r0 = 8 * wave; r0 < ZR; r0 += 8 * W::WAVES) {
+      if (p.out_bf16) output_rows8<true>(z, Z_ROW, r0, ow, has_bias, y, m0 + pass * ZR + r0, rend, N, nb * 128, lane);
+      else output_rows8<false>(z, Z_ROW, r0, ow, has_bias, y, m0 + pass * ZR + r0, rend, N, nb * 128, lane);
     }
   }
 }
