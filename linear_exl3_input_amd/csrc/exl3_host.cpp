@@ -340,6 +340,17 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   // kernel sums both halves' slabs).
   pl.half = pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU && pl.bm <= 64 && !pl.multi &&
             (int64_t)nblk * n_slabs * ((pl.chunk + pl.bm - 1) / pl.bm) < device_cus_or_default();
+  // 33-64 rows that would need half-width workgroups to fill the CUs run
+  // as two 32-row tiles of full width instead: as many workgroups, each of
+  // twice the waves (the schedule tuner's choice on all 24 layers of the
+  // K = N = 4096 bit-width sweep at 64 rows, 3-7% faster)
+  if (pl.half && !bm_forced && pl.bm == 64 && M > 32 && !(force && force->wg_cols > 0)) {
+    pl.bm = 32;
+    pl.half = (int64_t)nblk * n_slabs * ((pl.chunk + pl.bm - 1) / pl.bm) < device_cus_or_default();
+    pl.finisher = pl.mode == EXL3_MODE_SLABS && pl.decoder == EXL3_DECODER_ALU &&
+                  (int64_t)nblk * ((pl.chunk + pl.bm - 1) / pl.bm) <= MAX_COUNTERS &&
+                  (double)slab_bytes(n_slabs, pl.chunk, w->N) < FINISHER_MAX_SLAB_BYTES;
+  }
   if (force && force->wg_cols > 0) {
     if (force->wg_cols != 64 && force->wg_cols != 128)
       return fail(EXL3_ERR_INVALID_ARG, "forced wg_cols=%d, must be 64 or 128", force->wg_cols);
