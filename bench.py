@@ -499,9 +499,15 @@ def main():
             ent = tj.get("entries", {}).get(dom_key)
             if ent and tj.get("kernel_hash") == kernel_hash():
                 n = len(dom)
-                roof["traffic"] = {"fetch_bytes_per_launch": ent["fetch_bytes"], "write_bytes_per_launch":
-                                   ent["write_bytes"], "algorithmic_trellis_bytes_per_launch":
-                                   sum(g["K"] * g["N"] * g["bits"] / 8 for g, _ in dom) / n,
+                # Bytes the kernel must move at least once: its weight operand (fp16 fragments for the
+                # dense GEMM, the trellis otherwise), the rotated activations and the bf16/fp16 output.
+                wbytes = (lambda g: g["K"] * g["N"] * 2) if "dense" in dom_key else \
+                         (lambda g: g["K"] * g["N"] * g["bits"] / 8)
+                alg = sum(wbytes(g) + g["M"] * g["K"] * 2 + g["M"] * g["N"] * 2 for g, _ in dom) / n
+                roof["traffic"] = {"hbm_bytes_per_launch": ent["fetch_bytes"] + ent["write_bytes"],
+                                   "fetch_bytes_per_launch": ent["fetch_bytes"],
+                                   "write_bytes_per_launch": ent["write_bytes"],
+                                   "algorithmic_bytes_per_launch": round(alg),
                                    "scale": ent.get("scale"), "measured_on": ent.get("measured_on")}
         except Exception as e:  # a malformed file only loses the traffic field
             log(f"traffic file unreadable: {e}")
