@@ -70,7 +70,7 @@ DEFAULT_WORKLOAD = "all_configs"
 # Routed experts (grouped GEMM): the expert pair's shapes, 64 experts each,
 # top-8 synthetic routing, T tokens per call.
 MOE_WORKLOADS = {"moe_e64_top8_4096x2048+2048x4096_b4_mcg":
-                 (["expert_4096x2048_b4_mcg", "expert_2048x4096_b4_mcg"], 64, 8, (1, 16, 64))}
+                 (["expert_4096x2048_b4_mcg", "expert_2048x4096_b4_mcg"], 64, 8, (1, 4, 16, 64))}
 
 KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_gemm_lut.hpp", "exl3_gemm_dense.hpp", "exl3_device.hpp",
                   "exl3_misc.hip"]
@@ -597,6 +597,10 @@ def moe_main(args, ex, wl, torch, np, dev):
                 routes = [ex.moe_align(i, E) for i in ids]
                 xrs = [ex.moe_input_transform(x, w, rt, k) for rt in routes]
                 t_gemm = time_calls(lambda r: ex.moe_linear(w, xrs[r % 32], routes[r % 32][1]), args.timing_reps)
+                # each decoder of the grouped GEMM forced, for the automatic choice's record
+                t_dec = {name: time_calls(lambda r: ex.moe_linear(w, xrs[r % 32], routes[r % 32][1], decoder=dc),
+                                          args.timing_reps)
+                         for name, dc in (("alu", ex.EXL3_DECODER_ALU), ("table", ex.EXL3_DECODER_TABLE))}
                 touched = float(np.mean([len(np.unique(a)) for a in pool]))
                 byts = touched * lay.weight_bytes()
                 flops = 2.0 * T * k * lay.K * lay.N
@@ -604,12 +608,14 @@ def moe_main(args, ex, wl, torch, np, dev):
                 sol_step += sol
                 per.append({"layer": lay.name, "experts": E, "topk": k, "T": T, "experts_touched": touched,
                             "call_us": round(t_call, 3), "grouped_gemm_us": round(t_gemm, 3),
+                            "grouped_gemm_us_by_decoder": {k_: round(v_, 3) for k_, v_ in t_dec.items()},
                             "GBps": round(byts / (t_gemm * 1e-6) / 1e9, 1),
                             "TFLOPS": round(flops / (t_gemm * 1e-6) / 1e12, 2),
                             "pct_sol_call": round(100 * sol / (t_call * 1e-6), 2),
                             "pct_sol_gemm": round(100 * sol / (t_gemm * 1e-6), 2)})
                 log(f"moe {lay.name} E={E} top{k} T={T}: {touched:.1f} experts touched, call {t_call:.2f} us, "
-                    f"grouped GEMM {t_gemm:.2f} us ({per[-1]['GBps']} GB/s, {per[-1]['pct_sol_gemm']}% SoL)")
+                    f"grouped GEMM {t_gemm:.2f} us ({per[-1]['GBps']} GB/s, {per[-1]['pct_sol_gemm']}% SoL; "
+                    f"ALU {t_dec['alu']:.2f} us, table {t_dec['table']:.2f} us)")
             del w
     step_us = sum(p_["call_us"] for p_ in per)
     gemm = sum(p_["grouped_gemm_us"] for p_ in per)
@@ -626,7 +632,8 @@ def moe_main(args, ex, wl, torch, np, dev):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(byts / (gemm * 1e-6) / 1e9, 1), "peak": HBM_BPS / 1e9,
                      "unit": "GB/s", "frac": round(byts / (gemm * 1e-6) / HBM_BPS, 4), "traffic": None,
-                     "kernel": "exl3::gemm_kernel<4, 1u, 1, ..., true> (grouped)",
+                     "kernel": "grouped GEMM (exl3::gemm_table_kernel<..., true> from 256 units, else "
+                               "exl3::gemm_kernel<..., true>)",
                      "work_per_launch": "trellis bytes of the experts the call touches"},
         "per_shape": per,
     }

@@ -418,6 +418,23 @@ exl3_status exl3_moe_linear(const exl3_weight *w, int32_t E, const uint16_t *x_r
                             const int32_t *block_expert, int32_t block, void *y, int32_t y_dtype, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* exl3_moe_linear with the decoder chosen by the caller: EXL3_DECODER_AUTO
+ * (what exl3_moe_linear does), EXL3_DECODER_ALU (the ALU tiles above), or
+ * EXL3_DECODER_TABLE: one persistent workgroup per CU decodes part of every
+ * weight through a 65,536-entry table in LDS (as exl3_linear's table
+ * decoder), each (16-row block, 128-column block) one fused unit that folds
+ * the shape's part tree in two levels (the parts of each group in order,
+ * then the groups in order, the first term copied each time), so each routed
+ * row still has exl3_linear's bits; it needs no workspace.  AUTO takes the
+ * table when block is 16, the stacked trellis is at most 2 GiB and there
+ * are at least 256 such units (enough to fill the GPU without splitting K;
+ * cuda-exl3 README, "What is supported": decode-bound expert GEMMs at a
+ * handful of rows per expert).  EXL3_ERR_UNSUPPORTED for TABLE with another
+ * block or a larger stack; EXL3_ERR_INVALID_ARG for another decoder. */
+exl3_status exl3_moe_linear_ex(const exl3_weight *w, int32_t E, const uint16_t *x_rot, int32_t rows,
+                               const int32_t *block_expert, int32_t block, void *y, int32_t y_dtype, void *workspace,
+                               size_t workspace_bytes, void *stream, int32_t decoder);
+
 /* out[t][n] = rne_dtype( sum over j of topk_weights[t][j] * y_routed[pair_row[t*topk+j]][n] ),
  * the sum in fp32 from 0 in j order, each product rounded to fp32 before it
  * is added; dropped pairs add nothing.  y_routed [rows][N] and out [T][N] in

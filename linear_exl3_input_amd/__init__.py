@@ -121,6 +121,7 @@ def load() -> ctypes.CDLL:
                                                vp]),
             "exl3_moe_workspace_bytes": (sz, [W, i32, i32]),
             "exl3_moe_linear": (i32, [W, i32, vp, i32, vp, i32, vp, i32, vp, sz, vp]),
+            "exl3_moe_linear_ex": (i32, [W, i32, vp, i32, vp, i32, vp, i32, vp, sz, vp, i32]),
             "exl3_moe_combine": (i32, [vp, i32, vp, vp, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -570,7 +571,8 @@ def moe_input_transform(x: torch.Tensor, w: MoeWeight, route, topk: int, block: 
 
 
 def moe_linear(w: MoeWeight, x_rot: torch.Tensor, block_expert: torch.Tensor, block: int = 16,
-               out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+               out_dtype: torch.dtype = torch.bfloat16, decoder: int = EXL3_DECODER_AUTO) -> torch.Tensor:
+    """The grouped GEMM (exl3_moe_linear_ex); decoder AUTO, ALU or TABLE."""
     rows = x_rot.shape[2]
     L = load()
     need = L.exl3_moe_workspace_bytes(ctypes.byref(w.first.view()), rows, block)
@@ -578,9 +580,9 @@ def moe_linear(w: MoeWeight, x_rot: torch.Tensor, block_expert: torch.Tensor, bl
         _check(1)
     ws, wsn = _workspace(need, x_rot.device)
     y = torch.empty((rows, w.N), dtype=out_dtype, device=x_rot.device)
-    _check(L.exl3_moe_linear(ctypes.byref(w.first.view()), w.E, _dev_ptr(x_rot, "x_rot", _H16), rows,
-                             _dev_ptr(block_expert, "block_expert", (torch.int32,)), block, y.data_ptr(),
-                             _BF16 if out_dtype == torch.bfloat16 else _F16, ws, wsn, _stream()))
+    _check(L.exl3_moe_linear_ex(ctypes.byref(w.first.view()), w.E, _dev_ptr(x_rot, "x_rot", _H16), rows,
+                                _dev_ptr(block_expert, "block_expert", (torch.int32,)), block, y.data_ptr(),
+                                _BF16 if out_dtype == torch.bfloat16 else _F16, ws, wsn, _stream(), int(decoder)))
     return y
 
 
@@ -597,10 +599,10 @@ def moe_combine(y_routed: torch.Tensor, pair_row: torch.Tensor, topk_weights: to
 
 
 def moe_forward(x: torch.Tensor, w: MoeWeight, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
-                block: int = 16, swiglu: bool = False) -> torch.Tensor:
+                block: int = 16, swiglu: bool = False, decoder: int = EXL3_DECODER_AUTO) -> torch.Tensor:
     """Routed experts: align, rotate each routed row with its expert's suh,
     the grouped GEMM, and the ordered combine.  -> [T, N] in x's dtype."""
     route = moe_align(topk_ids, w.E, block)
     xr = moe_input_transform(x, w, route, topk_ids.shape[1], block, swiglu)
-    y = moe_linear(w, xr, route[1], block, x.dtype)
+    y = moe_linear(w, xr, route[1], block, x.dtype, decoder)
     return moe_combine(y, route[2], topk_weights)

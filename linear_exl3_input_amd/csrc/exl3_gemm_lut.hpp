@@ -22,7 +22,13 @@
 //
 // Work: a unit is one 128-column block and the parts of one workgroup unit
 // (slab mode: p.unit consecutive parts, their sum stored as one slab) or all
-// parts (fused mode), folded in part order at every part end.  The 16
+// parts (fused mode), folded in part order at every part end.  Grouped
+// (MoE) calls, fused only: a unit is one 16-row block of routed rows and one
+// column block, multiplied by the block's expert (trellis, svh and bias at
+// fixed strides behind expert 0's), blocks of no expert skipped; the parts
+// are folded as the shape's two-level tree (p.fold_q parts a group, first
+// part of each group copied, then the groups in order, first copied), the
+// same adds as the output kernel and the finishing workgroup.  The 16
 // waves are 4 teams of 4 waves; wave tw of a team multiplies n-tiles 2tw,
 // 2tw+1 against the (up to) 16 rows.  Units are dealt to the workgroups in
 // turn (unit u to workgroup u mod G, team (u / G) mod 4).  A team walks its units as one
@@ -99,12 +105,14 @@ struct TblUnit {
   int nb, part;   // column block; first part of the unit
   int slab;       // slab mode: the unit's slab
   int kb_begin;
+  int rb, e;      // grouped calls: row block and its expert
 };
 
 // TEAMS teams of 4 waves: 4 (1024 threads, 128 VGPRs a wave) up to 32 rows,
 // 2 (512 threads, 256 VGPRs) for the four A fragments of up to 64 rows.
-template <int BITS, uint32_t CB, int TP, int MT, int TEAMS = 4>
+template <int BITS, uint32_t CB, int TP, int MT, int TEAMS = 4, bool MOE = false>
 __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmParams p) {
+  static_assert(!MOE || MT == 1, "grouped calls take 16-row blocks");
   using G = TblGeom<BITS>;
   constexpr int NX = G::NX, NY = G::NY, TILE_DW = G::TILE_DW;
   constexpr int DEPTH = TBL_DEPTH;
@@ -127,8 +135,8 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
   const int nblk = N >> 7;
   const bool slab = p.slab_mode != 0;
   const int NU = P / p.unit;  // units per column block (slab mode)
-  const int units = slab ? nblk * NU : nblk;
   const int rows = p.row_end - p.row_base;
+  const int units = MOE ? (rows >> 4) * nblk : slab ? nblk * NU : nblk;
   const int stride = gridDim.x * TEAMS;
   const int rounds = (units + stride - 1) / stride;
 
@@ -137,7 +145,8 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
   const char *const xrot = reinterpret_cast<const char *>(p.x_rot);
   // The trellis through a buffer resource (at most 2 GiB, checked on the
   // host): 32-bit offsets, and a read past its end returns zeros.
-  const uint32_t t_bytes = (uint32_t)((uint64_t)K * (uint64_t)N * BITS / 8);
+  const uint64_t expert_bytes = (uint64_t)K * (uint64_t)N * BITS / 8;
+  const uint32_t t_bytes = (uint32_t)(MOE ? expert_bytes * (uint64_t)p.n_experts : expert_bytes);
   const auto trs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.trellis), (short)0, (int)t_bytes,
                                                      0x00020000);
 
@@ -146,14 +155,28 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
     // units go round the workgroups first, so that fewer units than teams
     // still spread over every CU
     const int id = (r * TEAMS + team) * (int)gridDim.x + (int)blockIdx.x;
-    if (r >= rounds || id >= units) {
-      u.t = 0;
-      u.a = xrot;
-      u.nks = 0;
-      u.nb = 0;
-      u.part = 0;
-      u.slab = 0;
-      u.kb_begin = 0;
+    u.t = 0;
+    u.a = xrot;
+    u.nks = 0;
+    u.nb = 0;
+    u.part = 0;
+    u.slab = 0;
+    u.kb_begin = 0;
+    u.rb = 0;
+    u.e = 0;
+    if (r >= rounds || id >= units) return u;
+    if constexpr (MOE) {
+      // units run through the column blocks of one row block, then the next
+      u.rb = __builtin_amdgcn_readfirstlane(id / nblk);
+      u.nb = id - u.rb * nblk;
+      const int e = __builtin_amdgcn_readfirstlane(p.block_expert[u.rb]);
+      if (e < 0 || e >= p.n_experts) return u;  // no expert: skipped, nothing written
+      u.e = e;
+      u.nks = 4 * KB;
+      u.t = (uint32_t)((uint64_t)e * expert_bytes + (uint64_t)u.nb * 8 * (TILE_DW * 4));
+      int shard = 0;
+      while (shard + 1 < p.n_shards && u.nb >= p.shard_end_blk[shard]) ++shard;
+      u.a = xrot + ((int64_t)shard * M * K + (int64_t)u.rb * 16 * 32) * 2;
       return u;
     }
     // the divisions run on the vector unit: keep their (wave-uniform)
@@ -251,13 +274,15 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
   barrier_lds();
 
   for (int r = 0; r < rounds; ++r) {
-    float4_t acc0[MT], acc1[MT], tot0[MT], tot1[MT];
+    float4_t acc0[MT], acc1[MT], tot0[MT], tot1[MT], gs0[MT], gs1[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       acc0[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
       acc1[mt] = acc0[mt];
       tot0[mt] = acc0[mt];
       tot1[mt] = acc0[mt];
+      gs0[mt] = acc0[mt];
+      gs1[mt] = acc0[mt];
     }
     if (cu.nks > 0) {
       // fold at every part end (first part copied, later parts added in
@@ -305,7 +330,26 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
         if (ks0 + DEPTH == fold_ks) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            if (fold_part == cu.part) {
+            if constexpr (MOE) {
+              const int q = p.fold_q;
+              const int qi = fold_part % q;
+              if (qi == 0) {
+                gs0[mt] = acc0[mt];
+                gs1[mt] = acc1[mt];
+              } else {
+                gs0[mt] = gs0[mt] + acc0[mt];
+                gs1[mt] = gs1[mt] + acc1[mt];
+              }
+              if (qi == q - 1) {
+                if (fold_part == q - 1) {
+                  tot0[mt] = gs0[mt];
+                  tot1[mt] = gs1[mt];
+                } else {
+                  tot0[mt] = tot0[mt] + gs0[mt];
+                  tot1[mt] = tot1[mt] + gs1[mt];
+                }
+              }
+            } else if (fold_part == cu.part) {
               tot0[mt] = acc0[mt];
               tot1[mt] = acc1[mt];
             } else {
@@ -320,7 +364,7 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
         }
       }
     }
-    if (slab) {
+    if (slab && !MOE) {
       if (cu.nks > 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -342,13 +386,17 @@ __global__ __launch_bounds__(256 * TEAMS, 1) void gemm_table_kernel(const GemmPa
         barrier_lds();
         if (cu.nks > 0 && tw < 2 && 16 * mt + 8 * tw < rows) {
           uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
-          const OutWords16 ow = out_words16(p.svh, p.bias, cu.nb * 128, lane);
-          const int64_t row0 = p.row_base + 16 * mt + 8 * tw;
+          // grouped calls: the block's expert's svh and bias, its 16 rows
+          const uint16_t *const svh = MOE ? p.svh + (int64_t)cu.e * N : p.svh;
+          const uint16_t *const bias = MOE && p.bias != nullptr ? p.bias + (int64_t)cu.e * N : p.bias;
+          const int64_t rbase = MOE ? (int64_t)p.row_base + 16 * cu.rb : (int64_t)p.row_base;
+          const int64_t rlim = MOE ? rbase + 16 : (int64_t)p.row_base + rows;
+          const OutWords16 ow = out_words16(svh, bias, cu.nb * 128, lane);
+          const int64_t row0 = rbase + 16 * mt + 8 * tw;
           if (p.out_bf16)
-            output_rows8<true>(zb, 128, 8 * tw, ow, p.bias != nullptr, y, row0, p.row_base + rows, N, cu.nb * 128, lane);
+            output_rows8<true>(zb, 128, 8 * tw, ow, bias != nullptr, y, row0, rlim, N, cu.nb * 128, lane);
           else
-            output_rows8<false>(zb, 128, 8 * tw, ow, p.bias != nullptr, y, row0, p.row_base + rows, N, cu.nb * 128,
-                                lane);
+            output_rows8<false>(zb, 128, 8 * tw, ow, bias != nullptr, y, row0, rlim, N, cu.nb * 128, lane);
         }
         barrier_lds();
       }
@@ -375,6 +423,10 @@ template <int BITS, uint32_t CB>
 hipError_t launch_table_t(const GemmParams &p, int grid, hipStream_t s) {
   constexpr int TP = table_pairs(BITS);
   const int rows = p.row_end - p.row_base;
+  if (p.block_expert != nullptr) {
+    hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 1, 4, true>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
+    return hipGetLastError();
+  }
   if (rows <= 16) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 1>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
   else if (rows <= 32) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 2>), dim3(grid), dim3(TBL_THREADS), 0, s, p);
   else if (rows <= 64) hipLaunchKernelGGL((gemm_table_kernel<BITS, CB, TP, 4, 2>), dim3(grid), dim3(512), 0, s, p);

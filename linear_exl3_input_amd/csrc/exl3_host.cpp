@@ -187,6 +187,12 @@ struct Plan {
 constexpr double TABLE_MIN_WEIGHTS = 33554432.0;         // 2^25
 constexpr double TABLE_MIN_WEIGHTS_SMALL_M = 67108864.0;  // 2^26, M <= 16
 constexpr int32_t TABLE_MAX_M = 64;
+// Grouped (MoE) calls take the table decoder from this many (16-row block,
+// column block) units: with fewer the fused units leave CUs idle where the
+// ALU tiles split K.  Measured on the expert pair's shapes, 64 experts,
+// top-8: one token on 4096 x 2048 (128 units) 39.5 us ALU / 40.9 us table,
+// on 2048 x 4096 (256 units) 38.6 / 25.3 us; 16 tokens 216 / 89 us.
+constexpr int64_t MOE_TABLE_MIN_UNITS = 256;
 // The table kernel addresses the trellis with 32-bit byte offsets.
 constexpr double TABLE_MAX_TRELLIS_BYTES = 2147483648.0;  // 2 GiB
 // Partial slabs beyond this go through the fused fold (or row chunks).
@@ -912,6 +918,48 @@ namespace {
 // block-row tiles, with the output stage in the GEMM (fused, or the
 // finishing workgroup): a separate output kernel would need each block's
 // svh.
+// Grouped calls on the table decoder: one fused unit per (16-row block,
+// column block), the expert shape's own part tree folded in two levels in
+// the kernel, no workspace.
+exl3_status run_moe_table(const exl3_weight *w, int32_t E, const uint16_t *x_rot, int32_t rows,
+                          const int32_t *block_expert, void *y, int32_t y_dtype, hipStream_t s) {
+  exl3::GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  const int32_t G = choose_groups(w->K, w->N, w->bits);
+  const int32_t P = G * choose_q(w->K, w->N, G);
+  p.trellis = w->trellis;
+  p.x_rot = x_rot;
+  p.svh = w->svh;
+  p.bias = w->bias;
+  p.y = y;
+  p.M = rows;
+  p.row_base = 0;
+  p.row_end = rows;
+  p.K = w->K;
+  p.N = w->N;
+  p.parts = P;
+  p.unit = P;
+  p.fold_q = P / G;  // parts per group
+  p.slab_mode = 0;
+  p.out_bf16 = y_dtype == EXL3_BF16 ? 1 : 0;
+  p.n_shards = w->n_shards;
+  int32_t end = 0;
+  for (int i = 0; i < w->n_shards; ++i) {
+    end += w->shard_n[i] / 128;
+    p.shard_end_blk[i] = end;
+  }
+  p.block_expert = block_expert;
+  p.n_experts = E;
+  p.expert_trellis = (int64_t)w->K / 16 * (w->N / 16) * 16 * w->bits;
+  int cus = 0;
+  hipError_t e;
+  if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
+  const int64_t units = (int64_t)(rows / 16) * (w->N / 128);
+  const int grid = (int)std::min<int64_t>(cus, units);
+  e = exl3::launch_gemm_table(w->bits, w->codebook, p, grid, s);
+  return e == hipSuccess ? EXL3_OK : launch_error(e, "grouped table GEMM launch");
+}
+
 exl3_status moe_plan(const exl3_weight *w, int32_t rows, int32_t block, Plan *pl) {
   exl3_plan f;
   f.parts = -1;
@@ -952,6 +1000,13 @@ size_t exl3_moe_workspace_bytes(const exl3_weight *w, int32_t rows, int32_t bloc
 exl3_status exl3_moe_linear(const exl3_weight *w, int32_t E, const uint16_t *x_rot, int32_t rows,
                             const int32_t *block_expert, int32_t block, void *y, int32_t y_dtype, void *workspace,
                             size_t workspace_bytes, void *stream) {
+  return exl3_moe_linear_ex(w, E, x_rot, rows, block_expert, block, y, y_dtype, workspace, workspace_bytes, stream,
+                            EXL3_DECODER_AUTO);
+}
+
+exl3_status exl3_moe_linear_ex(const exl3_weight *w, int32_t E, const uint16_t *x_rot, int32_t rows,
+                               const int32_t *block_expert, int32_t block, void *y, int32_t y_dtype, void *workspace,
+                               size_t workspace_bytes, void *stream, int32_t decoder) {
   clear_error();
   exl3_status st = validate_weight(w, true, true);
   if (st != EXL3_OK) return st;
@@ -962,6 +1017,25 @@ exl3_status exl3_moe_linear(const exl3_weight *w, int32_t E, const uint16_t *x_r
   if (rows < 0 || rows > MAX_M || rows % block != 0)
     return fail(EXL3_ERR_INVALID_ARG, "rows=%d must be a multiple of block=%d (remainder %d)", rows, block,
                 rows >= 0 ? rows % block : rows);
+  if (decoder != EXL3_DECODER_AUTO && decoder != EXL3_DECODER_ALU && decoder != EXL3_DECODER_TABLE)
+    return fail(EXL3_ERR_INVALID_ARG, "decoder=%d, must be -1 (auto), 0 (alu) or 1 (table)", decoder);
+  const double stack_bytes = (double)E * w->K * (double)w->N * w->bits / 8.0;
+  if (decoder == EXL3_DECODER_TABLE && block != 16)
+    return fail(EXL3_ERR_UNSUPPORTED, "the grouped table decoder takes 16-row blocks; block=%d", block);
+  if (decoder == EXL3_DECODER_TABLE && stack_bytes > TABLE_MAX_TRELLIS_BYTES)
+    return fail(EXL3_ERR_UNSUPPORTED, "the table decoder reads at most %.0f trellis bytes; %d experts hold %.0f",
+                TABLE_MAX_TRELLIS_BYTES, E, stack_bytes);
+  const int64_t table_units = (int64_t)(rows / 16) * (w->N / 128);
+  const bool use_table = decoder == EXL3_DECODER_TABLE ||
+                         (decoder == EXL3_DECODER_AUTO && block == 16 && stack_bytes <= TABLE_MAX_TRELLIS_BYTES &&
+                          table_units >= MOE_TABLE_MIN_UNITS);
+  if (use_table) {
+    if (rows == 0) return EXL3_OK;
+    if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+    if ((st = check_ptr(block_expert, "block_expert")) != EXL3_OK) return st;
+    if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+    return run_moe_table(w, E, x_rot, rows, block_expert, y, y_dtype, (hipStream_t)stream);
+  }
   Plan pl;
   if ((st = moe_plan(w, rows, block, &pl)) != EXL3_OK) return st;
   if (rows == 0) return EXL3_OK;

@@ -148,8 +148,17 @@ int main() {
     for (int block : {16, 32, 64}) {
       const int rows = exl3_moe_rows_max(T, 8, 64, block);
       EXPECT(rows >= 0 && rows % block == 0);
-      (void)exl3_moe_workspace_bytes(&we, rows, block);
+      const size_t need = exl3_moe_workspace_bytes(&we, rows, block);
+      for (int dec : {EXL3_DECODER_AUTO, EXL3_DECODER_ALU, EXL3_DECODER_TABLE}) {
+        const exl3_status st = exl3_moe_linear_ex(&we, 64, fake(4 << 20), rows,
+                                                  reinterpret_cast<int32_t *>(fake(8 << 20)), block, fake(big), 1,
+                                                  fake(big), need, nullptr, dec);
+        if (dec == EXL3_DECODER_TABLE && block != 16) EXPECT(st == EXL3_ERR_UNSUPPORTED);
+        else EXPECT(st == EXL3_OK || st == EXL3_ERR_UNSUPPORTED);
+      }
     }
+  EXPECT(exl3_moe_linear_ex(&we, 64, fake(4 << 20), 64, reinterpret_cast<int32_t *>(fake(8 << 20)), 16, fake(big),
+                            1, fake(big), size_t(1) << 30, nullptr, 5) == EXL3_ERR_INVALID_ARG);
   std::printf("host checks done: %d failures, %ld launches\n", g_fail, g_launches);
   return g_fail ? 1 : 0;
 }

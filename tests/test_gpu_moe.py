@@ -67,11 +67,19 @@ def test_align_matches_the_oracle(T, k, E, block):
     assert np.all(pair_row[(flat < 0) | (flat >= E)] == -1)
 
 
+TABLE, ALU, AUTO = ex.EXL3_DECODER_TABLE, ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_AUTO
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
-@pytest.mark.parametrize("T,k,E,block,bias", [(21, 2, 4, 16, False), (9, 3, 5, 32, True), (40, 2, 3, 64, False)])
-def test_routed_rows_equal_the_plain_linear(T, k, E, block, bias, swiglu):
+@pytest.mark.parametrize("T,k,E,block,bias,decoder", [(21, 2, 4, 16, False, AUTO), (9, 3, 5, 32, True, AUTO),
+                                                      (40, 2, 3, 64, False, AUTO), (21, 2, 4, 16, False, TABLE),
+                                                      (33, 3, 6, 16, True, TABLE), (12, 2, 5, 16, True, ALU)])
+def test_routed_rows_equal_the_plain_linear(T, k, E, block, bias, decoder, swiglu):
     """Each live routed row has the bits of exl3_linear of its token alone on
-    its expert's weight (batch and grouping invariance)."""
+    its expert's weight (batch and grouping invariance), on either decoder of
+    the grouped GEMM: the table decoder folds the shape's tree (8 parts in 4
+    groups here) in two levels inside one fused unit, the ALU tiles through
+    the finishing workgroup."""
     lay, w, _ = _experts(E, 1024, (256, 256), 4, "mcg", 710 + T, bias)
     ids, wts = _routing(T, k, E, 711 + T)
     rng = np.random.default_rng(712)
@@ -79,7 +87,7 @@ def test_routed_rows_equal_the_plain_linear(T, k, E, block, bias, swiglu):
     x = x_dev(otf.f32_to_bf16_bits(rng.standard_normal((T, width)).astype(np.float32)))
     route = ex.moe_align(torch.from_numpy(ids).cuda(), E, block)
     xr = ex.moe_input_transform(x, w, route, k, block, swiglu)
-    y = bits16(ex.moe_linear(w, xr, route[1], block))
+    y = bits16(ex.moe_linear(w, xr, route[1], block, decoder=decoder))
     pair_row = route[2].cpu().numpy()
     for p in range(T * k):
         t, e = divmod(p, k)[0], ids.reshape(-1)[p]
@@ -88,7 +96,8 @@ def test_routed_rows_equal_the_plain_linear(T, k, E, block, bias, swiglu):
         xr1 = ex.input_transform_swiglu(xt, we.suh) if swiglu else ex.input_transform(xt, we.suh)
         want = bits16(ex.linear(we, xr1, torch.bfloat16))
         assert np.array_equal(y[pair_row[p]], want[0]), f"pair {p} (token {t}, expert {e})"
-    banner(f"moe rows T={T} k={k} E={E} block={block} swiglu={swiglu}: {T * k} routed rows bit-identical")
+    banner(f"moe rows T={T} k={k} E={E} block={block} decoder={decoder} swiglu={swiglu}: {T * k} routed rows "
+           "bit-identical")
 
 
 def test_combine_bit_exact():
@@ -106,9 +115,10 @@ def test_combine_bit_exact():
     assert np.array_equal(got, omoe.combine_bits(yb, "bf16", pair_row, wts))
 
 
-@pytest.mark.parametrize("K,shards,bits,cb,E,T,k", [(1024, (256,), 5, "mul1", 6, 23, 2),
-                                                  (4096, (2048,), 4, "mcg", 8, 48, 2)])
-def test_moe_forward_within_the_oracle_bound(K, shards, bits, cb, E, T, k):
+@pytest.mark.parametrize("K,shards,bits,cb,E,T,k,decoder", [(1024, (256,), 5, "mul1", 6, 23, 2, AUTO),
+                                                          (4096, (2048,), 4, "mcg", 8, 48, 2, AUTO),
+                                                          (1024, (256, 128), 6, "3inst", 5, 30, 3, TABLE)])
+def test_moe_forward_within_the_oracle_bound(K, shards, bits, cb, E, T, k, decoder):
     """out[t] against sum_j w_j * y*_j in float64 (y*_j the oracle's exact
     layer output of token t on expert j): within sum_j |w_j| (B_j + u_bf16
     |y*_j|) plus the combine's own roundings."""
@@ -116,7 +126,8 @@ def test_moe_forward_within_the_oracle_bound(K, shards, bits, cb, E, T, k):
     ids, wts = _routing(T, k, E, 731)
     rng = np.random.default_rng(732)
     xb = otf.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
-    out = bits16(ex.moe_forward(x_dev(xb), w, torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()))
+    out = bits16(ex.moe_forward(x_dev(xb), w, torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda(),
+                                decoder=decoder))
     got = olin.out_bits_to_f64(out, "bf16")
     N = sum(shards)
     want = np.zeros((T, N))
@@ -137,7 +148,8 @@ def test_moe_forward_within_the_oracle_bound(K, shards, bits, cb, E, T, k):
     assert np.all(err <= lim)
 
 
-def test_out_of_range_block_experts_are_skipped():
+@pytest.mark.parametrize("decoder", [AUTO, TABLE])
+def test_out_of_range_block_experts_are_skipped(decoder):
     """A caller-built routing whose block_expert holds an expert index past
     the stack (or below -1) is treated as a padding block: the routed
     rotation writes zeros for its rows and the grouped GEMM leaves its output
@@ -168,8 +180,8 @@ def test_out_of_range_block_experts_are_skipped():
     L = ex.load()
     need = L.exl3_moe_workspace_bytes(ctypes.byref(w.first.view()), rows, block)
     ws, wsn = ex._workspace(need, torch.device("cuda"))
-    ex._check(L.exl3_moe_linear(ctypes.byref(w.first.view()), w.E, xr.data_ptr(), rows, hacked_dev.data_ptr(), block,
-                                y.data_ptr(), 1, ws, wsn, ex._stream()))
+    ex._check(L.exl3_moe_linear_ex(ctypes.byref(w.first.view()), w.E, xr.data_ptr(), rows, hacked_dev.data_ptr(),
+                                   block, y.data_ptr(), 1, ws, wsn, ex._stream(), decoder))
     yb = bits16(y)
     seven = bits16(torch.full((1,), 7.0, dtype=torch.bfloat16))[0]
     for b in range(len(be)):
@@ -178,3 +190,40 @@ def test_out_of_range_block_experts_are_skipped():
             assert np.all(yb[r] == seven), f"block {b} written"
         elif be[b] >= 0:
             assert np.array_equal(yb[r], y_good[r]), f"block {b}"
+
+
+@pytest.mark.parametrize("K,N", [(4096, 2048), (2048, 4096)])
+def test_grouped_table_equals_alu_on_the_expert_pair(K, N):
+    """The expert pair's shapes (4-bit mcg, 32 parts in 8 groups and 16 in
+    4), 64 experts, 16 tokens routed to 8 each: the grouped table decoder
+    (which the automatic choice takes here) gives every live routed row the
+    bits of the grouped ALU tiles."""
+    E, T, k, block = 64, 16, 8, 16
+    lay, w, _ = _experts(E, K, (N,), 4, "mcg", 780 + K)
+    ids, _ = _routing(T, k, E, 781)
+    rng = np.random.default_rng(782)
+    x = x_dev(otf.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32)))
+    route = ex.moe_align(torch.from_numpy(ids).cuda(), E, block)
+    xr = ex.moe_input_transform(x, w, route, k, block)
+    y_alu = bits16(ex.moe_linear(w, xr, route[1], block, decoder=ALU))
+    y_tab = bits16(ex.moe_linear(w, xr, route[1], block, decoder=TABLE))
+    y_auto = bits16(ex.moe_linear(w, xr, route[1], block))
+    live = route[2].cpu().numpy()
+    live = live[live >= 0]
+    assert np.array_equal(y_tab[live], y_alu[live])
+    assert np.array_equal(y_auto[live], y_alu[live])
+    banner(f"grouped table == ALU: {K}x{N}, {live.size} routed rows over {int((route[1] >= 0).sum())} blocks")
+
+
+def test_grouped_table_refusals():
+    """The table decoder of the grouped GEMM takes 16-row blocks only, and
+    an unknown decoder is refused before any launch."""
+    E, block = 2, 32
+    lay, w, _ = _experts(E, 512, (256,), 4, "mcg", 790)
+    rows = 64
+    xr = torch.zeros(ex.rot_shape(1, rows, 512), dtype=torch.float16, device="cuda")
+    be = torch.zeros(rows // block, dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError, match="16-row blocks"):
+        ex.moe_linear(w, xr, be, block, decoder=TABLE)
+    with pytest.raises(RuntimeError, match="decoder=7"):
+        ex.moe_linear(w, xr, be, block, decoder=7)
