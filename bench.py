@@ -72,8 +72,14 @@ DEFAULT_WORKLOAD = "all_configs"
 MOE_WORKLOADS = {"moe_e64_top8_4096x2048+2048x4096_b4_mcg":
                  (["expert_4096x2048_b4_mcg", "expert_2048x4096_b4_mcg"], 64, 8, (1, 4, 16, 64))}
 
-KERNEL_SOURCES = ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_gemm_lut.hpp", "exl3_gemm_dense.hpp", "exl3_device.hpp",
-                  "exl3_misc.hip"]
+# Sources each kernel family is built from (its file and what it includes):
+# a stored counter figure is used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "dense": ["gemm_dense.hip", "exl3_gemm_dense.hpp", "exl3_gemm.hpp", "exl3_device.hpp", "exl3_launch.hpp"],
+    "tile": ["exl3_gemm.hpp", "exl3_gemm_wide.hpp", "exl3_device.hpp", "exl3_launch.hpp"],
+    "table": ["exl3_gemm_lut.hpp", "exl3_gemm.hpp", "exl3_device.hpp", "exl3_launch.hpp"],
+    "misc": ["exl3_misc.hip", "exl3_gemm.hpp", "exl3_device.hpp", "exl3_launch.hpp"],
+}
 
 
 def sol_seconds(M, K, N, bits):
@@ -102,9 +108,19 @@ def kernel_key(lay, plan) -> str:
     return name
 
 
-def kernel_hash() -> str:
+def kernel_family(key: str) -> str:
+    if "dense" in key:
+        return "dense"
+    if "table" in key:
+        return "table"
+    if "gemm" in key:
+        return "tile"
+    return "misc"
+
+
+def kernel_hash(family: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "linear_exl3_input_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -400,6 +416,10 @@ def main():
         rf = torch.empty(ex.RULER_WORDS, dtype=torch.float32, device=dev)
         t_mf = time_calls(lambda r: ex.debug_mfma_loop(iters, out=rf), 5)
         mfma_ruler = ex.mfma_loop_flops(iters) / (t_mf * 1e-6)
+        # the same loop on operands that change every product (real data's
+        # power draw: the clock drops)
+        t_mt = time_calls(lambda r: ex.debug_mfma_loop(iters, one=0, out=rf), 5)
+        mfma_toggle = ex.mfma_loop_flops(iters) / (t_mt * 1e-6)
         decode = {}
         for li, (lay, ws, x, xr, y) in enumerate(per_layer):
             ro = torch.empty((lay.K // 128, lay.N // 128), dtype=torch.int32, device=dev)
@@ -408,9 +428,11 @@ def main():
                                 "weights_per_s": float(f"{lay.K * lay.N / (t_dr * 1e-6):.4g}"),
                                 "trellis_GBps": round(lay.weight_bytes() / (t_dr * 1e-6) / 1e9, 1)}
     rulers = {"hbm_read_GBps": round(hbm_ruler / 1e9, 1), "mfma_f16_TFLOPS": round(mfma_ruler / 1e12, 1),
+              "mfma_f16_toggling_TFLOPS": round(mfma_toggle / 1e12, 1),
               "decode": decode, "spec": {"hbm_GBps": HBM_BPS / 1e9, "mfma_f16_TFLOPS": MFMA_F16_FLOPS / 1e12},
               "how": "stream read: 2 GiB, 262144 threads, 16-byte loads; mfma: 4096 waves x 16 independent "
-                     "v_mfma_f32_16x16x32_f16 chains x 2000; decode: trellis staging + decode per 128x128 block, "
+                     "v_mfma_f32_16x16x32_f16 chains x 2000, constant operands (toggling: two sets of hashed "
+                     "operands alternating); decode: trellis staging + decode per 128x128 block, "
                      "weight copies cycled"}
     att_step = 0.0
     for s_ in per_shape:
@@ -418,7 +440,8 @@ def main():
         s_["pct_attainable"] = round(100.0 * att / (s_["linear_us"] * 1e-6), 2)
         att_step += att
     rulers["step_pct_of_attainable"] = round(100.0 * att_step / (ms_per_step / 1e3), 3)
-    log(f"rulers: stream read {rulers['hbm_read_GBps']} GB/s, mfma {rulers['mfma_f16_TFLOPS']} TFLOP/s; "
+    log(f"rulers: stream read {rulers['hbm_read_GBps']} GB/s, mfma {rulers['mfma_f16_TFLOPS']} TFLOP/s "
+        f"({rulers['mfma_f16_toggling_TFLOPS']} on toggling operands); "
         f"step at {rulers['step_pct_of_attainable']}% of the rulers' bound")
 
     # ---- roofline of the dominant kernel: the kernel template instance with
@@ -497,7 +520,7 @@ def main():
         try:
             tj = json.load(open(tfile))
             ent = tj.get("entries", {}).get(dom_key)
-            if ent and tj.get("kernel_hash") == kernel_hash():
+            if ent and ent.get("source_hash") == kernel_hash(kernel_family(dom_key)):
                 n = len(dom)
                 # Bytes the kernel must move at least once: its weight operand (fp16 fragments for the
                 # dense GEMM, the trellis otherwise), the rotated activations and the bf16/fp16 output.
@@ -513,6 +536,9 @@ def main():
             log(f"traffic file unreadable: {e}")
     roof["ruler_peak"] = rulers["mfma_f16_TFLOPS"] if roof["unit"] == "TFLOP/s" else rulers["hbm_read_GBps"]
     roof["ruler_frac"] = round(roof["achieved"] / roof["ruler_peak"], 4)
+    if roof["unit"] == "TFLOP/s":
+        roof["ruler_peak_toggling"] = rulers["mfma_f16_toggling_TFLOPS"]
+        roof["ruler_frac_toggling"] = round(roof["achieved"] / roof["ruler_peak_toggling"], 4)
     log(f"roofline: {dom_key} over {roof['launches']}: {roof['achieved']} {roof['unit']} = "
         f"{100 * roof['frac']:.1f}% of peak, {roof['avg_launch_us']} us per launch")
 

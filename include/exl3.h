@@ -464,7 +464,12 @@ exl3_status exl3_debug_stream_read(const void *buf, size_t bytes, uint32_t *out,
  * 16 independent v_mfma_f32_16x16x32_f16 chains with every A and B element
  * the fp16 value `one` (bits); out[t] (float) = the sum of the lane's 16
  * chains' first elements = 512 * iters * one^2 while exact.  Work:
- * 16384 * 16 * iters * EXL3_RULER_WORDS / 64 flops.  iters in 1 .. 2^20. */
+ * 16384 * 16 * iters * EXL3_RULER_WORDS / 64 flops.  iters in 1 .. 2^20.
+ * With one = 0 the operands are instead two sets of pseudo-random fp16
+ * values (magnitudes in [0.5, 1), random signs, from a hash of the thread
+ * index) used alternately, so every product's inputs differ from the last
+ * one's, as on real data (constant operands let the chip hold a higher
+ * clock); then |out[t]| <= 512 * iters and every word is finite. */
 exl3_status exl3_debug_mfma_loop(int32_t iters, uint16_t one, float *out, void *stream);
 
 /* Decode ruler: every weight of `w` staged and decoded as the GEMM kernels

@@ -27,9 +27,10 @@ __global__ __launch_bounds__(AL_THREADS) void moe_align_kernel(const int32_t *__
                                                                int32_t *__restrict__ pair_row) {
   __shared__ int32_t cnt[AL_MAX_E];    // counts, then the running row of each expert
   __shared__ int32_t start[AL_MAX_E];  // first row of each expert's run
-  __shared__ int32_t part[AL_THREADS];
+  __shared__ int32_t wave_sum[AL_THREADS / 64];
   __shared__ int32_t total_rows;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += AL_THREADS) cnt[e] = 0;
   __syncthreads();
   for (int p = tid; p < pairs; p += AL_THREADS) {
@@ -42,19 +43,29 @@ __global__ __launch_bounds__(AL_THREADS) void moe_align_kernel(const int32_t *__
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int sum = 0;
   for (int e = e0; e < e1; ++e) sum += (cnt[e] + block - 1) / block * block;
-  part[tid] = sum;
+  // exclusive prefix of the threads' sums (integer adds, so any order gives
+  // the same result): within each wave by lane shifts, then over the waves
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < AL_THREADS; ++i) {
-      const int v = part[i];
-      part[i] = acc;
-      acc += v;
+  if (wave == 0) {
+    constexpr int W = AL_THREADS / 64;
+    int w = lane < W ? wave_sum[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < W; d <<= 1) {
+      const int t = __shfl_up(w, d, 64);
+      if (lane >= d) w += t;
     }
-    total_rows = acc;
+    if (lane < W) wave_sum[lane] = w;  // inclusive over the waves
+    if (lane == W - 1) total_rows = w;
   }
   __syncthreads();
-  int acc = part[tid];
+  int acc = (wave > 0 ? wave_sum[wave - 1] : 0) + incl - sum;
   for (int e = e0; e < e1; ++e) {
     start[e] = acc;
     acc += (cnt[e] + block - 1) / block * block;

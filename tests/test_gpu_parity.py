@@ -470,6 +470,51 @@ def test_mfma_loop_ruler_closed_form():
     assert torch.all(half == 16 * 32 * 3 * 0.25)
 
 
+def _toggle_operands(tid):
+    """The toggling ruler's operands of threads `tid` (its hash, restated):
+    -> a, b [n, 2 sets, 8] float64."""
+    t = tid.astype(np.uint64)
+    a = np.zeros((len(tid), 2, 8))
+    b = np.zeros((len(tid), 2, 8))
+    m32 = np.uint64(0xFFFFFFFF)
+    for s_ in range(2):
+        for e in range(8):
+            x = (t * np.uint64(0x9E3779B1) + np.uint64((s_ * 8 + e) * 0x85EBCA6B)) & m32
+            x ^= x >> np.uint64(15)
+            x = (x * np.uint64(0x2C1B3C6D)) & m32
+            x ^= x >> np.uint64(12)
+            a[:, s_, e] = ((x & np.uint64(0x83FF)) | np.uint64(0x3800)).astype(np.uint16).view(np.float16)
+            b[:, s_, e] = (((x >> np.uint64(16)) & np.uint64(0x83FF)) | np.uint64(0x3800)).astype(np.uint16).view(
+                np.float16)
+    return a, b
+
+
+def test_mfma_toggle_ruler_computes_its_products():
+    """one = 0: two sets of hashed operands alternate.  Lane l of a wave
+    holds A row l % 16 and B column l % 16 at k = 8 (l / 16) .. +7; its first
+    accumulator element is C[4 (l / 16)][l % 16], so out = 8 iters (C_0 +
+    C_1) at that position, against float64 within the fp32 accumulation's
+    rounding (checked on the first 64 waves)."""
+    iters = 5
+    out = ex.debug_mfma_loop(iters, one=0).cpu().numpy()
+    assert np.all(np.isfinite(out)) and np.all(np.abs(out) <= 512 * iters)
+    want = np.zeros(64 * 64)
+    for w in range(64):
+        tid = np.arange(64 * w, 64 * w + 64)
+        a, b = _toggle_operands(tid)
+        for s_ in range(2):
+            A = np.zeros((16, 32))
+            B = np.zeros((32, 16))
+            for l in range(64):
+                A[l % 16, 8 * (l // 16):8 * (l // 16) + 8] = a[l, s_]
+                B[8 * (l // 16):8 * (l // 16) + 8, l % 16] = b[l, s_]
+            C = A @ B
+            for l in range(64):
+                want[64 * w + l] += 8 * iters * C[4 * (l // 16), l % 16]
+    got = out[:64 * 64].astype(np.float64)
+    assert np.allclose(got, want, rtol=1e-5, atol=1e-3), np.max(np.abs(got - want))
+
+
 @pytest.mark.parametrize("bits,cb", [(2, "mul1"), (5, "3inst"), (7, "mcg")])
 def test_dequant_fragments_layout(bits, cb):
     """The dense decoder's fragments are the oracle's W_q in the documented
