@@ -1201,9 +1201,9 @@ hipError_t launch_big_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t 
 template <int BITS, uint32_t CB>
 hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
 
-// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128 -> gemm_big_kernel,
-// 256/512 -> gemm_wide_kernel (512 threads; 512 for a single part per
-// workgroup only).
+// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128 -> gemm_big_kernel
+// (or gemm_wide_kernel with 64-row waves for one fused part), 256/512 ->
+// gemm_wide_kernel (512 threads; 512 for a single part per workgroup only).
 template <int BITS, uint32_t CB>
 hipError_t launch_gemm_cb(int bm, int quads, bool half, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   if (bm > 64 && (quads != 1 || half)) return hipErrorInvalidValue;
@@ -1211,7 +1211,13 @@ hipError_t launch_gemm_cb(int bm, int quads, bool half, bool multi, const GemmPa
     case 16: return launch_gemm_t<BITS, CB, 1>(quads, half, multi, p, grid, s);
     case 32: return launch_gemm_t<BITS, CB, 2>(quads, half, multi, p, grid, s);
     case 64: return launch_gemm_t<BITS, CB, 4>(quads, half, multi, p, grid, s);
-    case 128: return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
+    case 128:
+      // one part over the whole K (layers of 256+ column blocks): the 8-wave
+      // tile with 64-row waves (gate_up 5120 x 34816 at 128 rows 170 -> 154
+      // us); split K keeps the 4-wave tile (q_proj / down_proj at 128 rows
+      // 55 / 63 us against 62 / 68)
+      if (!multi && p.parts == 1 && !p.slab_mode) return launch_wide_t<BITS, CB>(128, false, p, grid, s);
+      return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
     case 256:
     case 512: return launch_wide_t<BITS, CB>(bm, multi, p, grid, s);
     default: return hipErrorInvalidValue;

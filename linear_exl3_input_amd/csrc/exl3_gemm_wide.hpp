@@ -1,6 +1,7 @@
-// 256-row x 128-column GEMM tile for large M on gfx950.
+// 2*RW-row x 128-column GEMM tile for large M on gfx950 (RW = 128 or 256;
+// RW = 64 for 128-row tiles of one fused part).
 //
-// Eight waves: wave w = 4*rh + wq owns rows 128*rh .. 128*rh+127 of the tile
+// Eight waves: wave w = 4*rh + wq owns rows RW*rh .. RW*rh+RW-1 of the tile
 // and the 32 columns of n-tiles 2*wq and 2*wq+1 (as in gemm_kernel, one MFMA
 // B operand holds column half h = 0 or 1 of both n-tiles).  The two waves that
 // share a column quarter split the decode: wave (wq, rh) decodes half h = rh
@@ -452,11 +453,14 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   }
 }
 
-// bm 256: 128-row waves (both fold modes); bm 512: 256-row waves, single
-// part per workgroup only (the host never asks for the fold there).
+// bm 128: 64-row waves, one part only; bm 256: 128-row waves (both fold
+// modes); bm 512: 256-row waves, single part per workgroup only (the host
+// never asks for the fold there).
 template <int BITS, uint32_t CB>
 hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (bm == 256) {
+  if (bm == 128 && !multi) {
+    hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 64, false>), grid, dim3(512), 0, s, p);
+  } else if (bm == 256) {
     if (multi) hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 128, true>), grid, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 128, false>), grid, dim3(512), 0, s, p);
   } else if (bm == 512 && !multi) {

@@ -321,6 +321,23 @@ def test_grouped_tree_schedules_agree(M):
     _check(t, first)
 
 
+@pytest.mark.parametrize("M", [70, 128, 200])
+def test_one_part_schedules_agree(M):
+    """One part over the whole K, fused (the tree of layers of 256+
+    column blocks): 128-row tiles then run the 8-wave kernel with 64-row
+    waves; it gives the bits of the 16-, 64- and 256-row tiles and of the
+    dense decoder (ragged rows and two row tiles included), within the
+    oracle's bound."""
+    banner(f"one part M={M}")
+    lay = wl.small_layer("onepart", 1024, (384, 256), 6, "mul1", (M,), seed=99)
+    t = wl.gen_all(lay)
+    outs = {bm: _run(t, parts=1, bm=bm, mode=ex.EXL3_MODE_FUSED) for bm in (16, 64, 128, 256)}
+    outs["dense"] = _run(t, parts=1, decoder=ex.EXL3_DECODER_DENSE)
+    for key, y in outs.items():
+        assert np.array_equal(y, outs[128]), f"schedule {key} differs"
+    _check(t, outs[128])
+
+
 def test_grouped_tree_is_not_the_flat_fold():
     """The grouped tree and the flat fold of the same eight parts are both
     within the bound, and their bits differ somewhere (the tree is real)."""
