@@ -7,6 +7,7 @@
 // refuses what it cannot read, "What it adds").
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -79,9 +80,12 @@ exl3_status validate_weight(const exl3_weight *w, bool need_trellis, bool need_s
 
 // Column blocks from which a layer keeps K whole (choose_groups).
 constexpr int32_t WIDE_ONE_PART = 256;
+// Weights from which a layer takes the large-layer part rule.
+constexpr double SMALL_LAYER_WEIGHTS = 33554432.0;  // 2^25
 
-// K groups: a function of (K, N, bits) only.  Enough (column block, group)
-// pairs to occupy the GPU at decode sizes (about 1024), groups of at least
+// K groups: a function of (K, N, bits) only.  On a small layer (under 2^25
+// weights) enough (column block, group) pairs to occupy the GPU at decode
+// sizes (about 1024; large layers take about 512, below), groups of at least
 // four 128-k blocks (or four groups of two blocks, for short K), and the fp32
 // partial traffic at 16 rows kept near the trellis bytes it helps to stream
 // (the cuda-exl3 README caps split-k accumulator traffic at ~30% of the
@@ -109,10 +113,31 @@ int32_t choose_groups(int32_t K, int32_t N, int32_t bits) {
   // whose one-part GEMM runs 256-column tiles with twice the products per
   // barrier (2048 rows 971 -> 844 us, 4096 rows 1709 -> 1471 us).
   if (nblk >= WIDE_ONE_PART) return 1;
-  int32_t want = (1024 + nblk - 1) / nblk;
   const int32_t cap_len = std::max(1, std::max(kb / 4, std::min(kb / 2, 4)));
   const int32_t cap_traffic = std::max(1, (int32_t)(1.2 * (double)K * bits / 1024.0));
-  int32_t gmax = std::max(1, std::min(want, std::min(cap_len, cap_traffic)));
+  const int32_t cap = std::max(1, std::min(cap_len, cap_traffic));
+  if ((double)K * (double)N >= SMALL_LAYER_WEIGHTS) {
+    // A large layer takes about two workgroups per CU at one row (512
+    // pairs): the divisor of the block count nearest 512 / nblk in ratio.
+    // Fewer groups than a four-per-CU target cost the one-row call nothing
+    // and halve the partial traffic of batched calls: q_proj 5120 x 12288
+    // over its nine row counts 425 us in 10 groups, 374 us in 5 (256 rows
+    // 91 -> 66 us); down_proj 17408 x 5120 keeps 17 (536 us; 8 groups 541).
+    const double want = 512.0 / nblk;
+    int32_t best = 1;
+    double best_d = 1e30;
+    for (int32_t g = 1; g <= cap; ++g)
+      if (kb % g == 0) {
+        const double d = std::fabs(std::log((double)g / want));
+        if (d < best_d) {
+          best_d = d;
+          best = g;
+        }
+      }
+    return best;
+  }
+  int32_t want = (1024 + nblk - 1) / nblk;
+  int32_t gmax = std::max(1, std::min(want, cap));
   if ((int64_t)nblk * gmax < 512) gmax = std::max(1, std::min(gmax, 128 / nblk));
   for (int32_t g = gmax; g >= 1; --g)
     if (kb % g == 0) return g;
@@ -127,7 +152,7 @@ int32_t choose_groups(int32_t K, int32_t N, int32_t bits) {
 int32_t choose_q(int32_t K, int32_t N, int32_t groups) {
   const int32_t kb = K / 128;
   const int32_t nblk = N / 128;
-  if ((int64_t)nblk * groups >= 512 || nblk >= WIDE_ONE_PART) return 1;
+  if ((double)K * (double)N >= SMALL_LAYER_WEIGHTS || (int64_t)nblk * groups >= 512 || nblk >= WIDE_ONE_PART) return 1;
   const int32_t len = kb / groups;
   return len % 4 == 0 ? 4 : len % 2 == 0 ? 2 : 1;
 }

@@ -141,8 +141,10 @@ def test_small_layers_split_groups_into_parts():
     assert p.workspace == CB + 8 * 512 * 2048 * 4
     assert _plan(view(2048, (4096,), 4, 1), 16).parts == 16
     assert _plan(view(1024, (1024,), 4, 0), 1).parts == 8 and _plan(view(1024, (1024,), 4, 0), 1).groups == 4
-    q = _plan(view(5120, (12288,), 6, 2), 32)  # 96 blocks x 10 groups: one part per group
-    assert (q.parts, q.groups) == (10, 10)
+    q = _plan(view(5120, (12288,), 6, 2), 32)  # 96 blocks x 5 groups: one part per group
+    assert (q.parts, q.groups) == (5, 5)
+    d = _plan(view(17408, (5120,), 6, 2), 32)  # 40 blocks x 17 groups
+    assert (d.parts, d.groups) == (17, 17)
 
 
 def test_row_chunks_keep_slabs_bounded():
