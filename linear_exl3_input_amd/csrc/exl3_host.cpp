@@ -304,10 +304,15 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   // 192 MiB one workgroup folds all parts of its tile.  Several parts per
   // group in several groups: always partials, one slab per group (the fused
   // fold is one level), in row chunks that keep the slabs within 192 MiB.
+  // One part per group from 512 rows also folds in registers when the
+  // 256-row tiles of the fused plan cover three quarters of the CUs: the
+  // schedule tuner's choice on q_proj 5120 x 12288 at 512 rows (5 groups,
+  // 116 -> 108 us); down_proj's 40 blocks stay with the partials.
   const size_t full_slabs = slab_bytes(pl.groups, M, w->N);
+  const bool fused_fills = M >= 512 && (int64_t)nblk * ((M + 255) / 256) * 4 >= 3 * (int64_t)device_cus_or_default();
   if (pl.parts == 1 || pl.groups == 1) pl.mode = EXL3_MODE_FUSED;
   else if (Q > 1) pl.mode = EXL3_MODE_SLABS;
-  else pl.mode = (double)full_slabs <= slab_cap ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
+  else pl.mode = (double)full_slabs <= slab_cap && !fused_fills ? EXL3_MODE_SLABS : EXL3_MODE_FUSED;
   if (force && force->mode != EXL3_MODE_AUTO && force->mode >= 0) {
     if (force->mode != EXL3_MODE_FUSED && force->mode != EXL3_MODE_SLABS)
       return fail(EXL3_ERR_INVALID_ARG, "forced mode=%d, must be 0 (fused) or 1 (slabs)", force->mode);
