@@ -160,6 +160,14 @@ def _dev_ptr(t: torch.Tensor, name: str, dtypes) -> int:
     return t.data_ptr()
 
 
+def _out_ptr(t: torch.Tensor, name: str, shape: tuple, dtypes) -> int:
+    """Device pointer of a caller-supplied output after checking its shape:
+    the kernels write exactly `shape`, so a smaller tensor would be overrun."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return _dev_ptr(t, name, dtypes)
+
+
 _U16 = (torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16,)
 _H16 = (torch.float16,) + _U16
 
@@ -354,12 +362,13 @@ def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bf
         raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
     if out is None:
         out = torch.empty((M, w.N), dtype=out_dtype, device=x_rot.device)
+    y_ptr = _out_ptr(out, "out", (M, w.N), (out_dtype,))
     f = _force(parts, mode, bm, decoder, groups, unit, wg_cols)
     L = load()
     need = L.exl3_workspace_bytes_ex(ctypes.byref(w.view()), M, ctypes.byref(f) if f else None)
     ws, wsn = _workspace(need, x_rot.device)
     _check(L.exl3_linear_ex(ctypes.byref(w.view()), _dev_ptr(x_rot, "x_rot", _H16), M,
-                            _dev_ptr(out, "y", (out_dtype,)), _BF16 if out_dtype == torch.bfloat16 else _F16,
+                            y_ptr, _BF16 if out_dtype == torch.bfloat16 else _F16,
                             ws, wsn, _stream(), ctypes.byref(f) if f else None))
     return out
 
@@ -427,9 +436,10 @@ def debug_epilogue(w: Exl3Weight, z_parts: torch.Tensor, M: int, out_dtype=torch
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=z_parts.device)
     out_dtype = out.dtype
+    y_ptr = _out_ptr(out, "out", (M, N), (torch.bfloat16, torch.float16))
     _check(load().exl3_debug_epilogue(_dev_ptr(z_parts, "z_parts", (torch.float32,)), P, groups or P, M,
                                       ctypes.byref(w.view()),
-                                      out.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _F16, _stream()))
+                                      y_ptr, _BF16 if out_dtype == torch.bfloat16 else _F16, _stream()))
     return out
 
 
@@ -445,7 +455,8 @@ def debug_stream_read(buf: torch.Tensor, out: Optional[torch.Tensor] = None) -> 
     nbytes = buf.numel() * buf.element_size()
     if out is None:
         out = torch.empty(RULER_WORDS, dtype=torch.int32, device=buf.device)
-    _check(load().exl3_debug_stream_read(buf.data_ptr(), nbytes, _dev_ptr(out, "out", (torch.int32,)), _stream()))
+    _check(load().exl3_debug_stream_read(buf.data_ptr(), nbytes, _out_ptr(out, "out", (RULER_WORDS,), (torch.int32,)),
+                                         _stream()))
     return out
 
 
@@ -454,7 +465,7 @@ def debug_mfma_loop(iters: int, one: int = 0x3C00, device="cuda", out: Optional[
     16x16x32 with all operands `one` (fp16 bits); returns the lanes' sums."""
     if out is None:
         out = torch.empty(RULER_WORDS, dtype=torch.float32, device=device)
-    _check(load().exl3_debug_mfma_loop(iters, one, _dev_ptr(out, "out", (torch.float32,)), _stream()))
+    _check(load().exl3_debug_mfma_loop(iters, one, _out_ptr(out, "out", (RULER_WORDS,), (torch.float32,)), _stream()))
     return out
 
 
@@ -468,7 +479,8 @@ def debug_decode_rate(w: Exl3Weight, out: Optional[torch.Tensor] = None) -> torc
     half: odd k of the fp16 W_q values)."""
     if out is None:
         out = torch.empty((w.K // 128, w.N // 128), dtype=torch.int32, device=w.trellis.device)
-    _check(load().exl3_debug_decode_rate(ctypes.byref(w.view()), _dev_ptr(out, "out", (torch.int32,)), _stream()))
+    o_ptr = _out_ptr(out, "out", (w.K // 128, w.N // 128), (torch.int32,))
+    _check(load().exl3_debug_decode_rate(ctypes.byref(w.view()), o_ptr, _stream()))
     return out
 
 
@@ -561,11 +573,15 @@ def moe_input_transform(x: torch.Tensor, w: MoeWeight, route, topk: int, block: 
     if x.shape[1] != (2 * K if swiglu else K):
         raise ValueError(f"x has {x.shape[1]} columns, expected {2 * K if swiglu else K}")
     rows = moe_rows_max(T, topk, w.E, block)
+    if row_pair.numel() != rows or block_expert.numel() != rows // block:
+        raise ValueError(f"route has {row_pair.numel()} rows and {block_expert.numel()} blocks, expected "
+                         f"{rows} and {rows // block} for T={T}, topk={topk}, E={w.E}, block={block}")
     out = torch.empty(rot_shape(w.n_shards, rows, K), dtype=torch.float16, device=x.device)
     _check(load().exl3_moe_input_transform(_dev_ptr(x, "x", (torch.bfloat16, torch.float16)),
                                            _BF16 if x.dtype == torch.bfloat16 else _F16, int(swiglu), T, K,
                                            _dev_ptr(w.stack[1], "suh", _H16), w.n_shards, w.E,
-                                           row_pair.data_ptr(), block_expert.data_ptr(), topk, block, rows,
+                                           _dev_ptr(row_pair, "row_pair", (torch.int32,)),
+                                           _dev_ptr(block_expert, "block_expert", (torch.int32,)), topk, block, rows,
                                            out.data_ptr(), _stream()))
     return out
 
@@ -573,7 +589,11 @@ def moe_input_transform(x: torch.Tensor, w: MoeWeight, route, topk: int, block: 
 def moe_linear(w: MoeWeight, x_rot: torch.Tensor, block_expert: torch.Tensor, block: int = 16,
                out_dtype: torch.dtype = torch.bfloat16, decoder: int = EXL3_DECODER_AUTO) -> torch.Tensor:
     """The grouped GEMM (exl3_moe_linear_ex); decoder AUTO, ALU or TABLE."""
+    if x_rot.dim() != 4 or tuple(x_rot.shape) != rot_shape(w.n_shards, x_rot.shape[2], w.K):
+        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [{w.n_shards}, {w.K // 32}, rows, 32]")
     rows = x_rot.shape[2]
+    if block_expert.numel() != rows // block:
+        raise ValueError(f"block_expert has {block_expert.numel()} entries, expected rows/block = {rows // block}")
     L = load()
     need = L.exl3_moe_workspace_bytes(ctypes.byref(w.first.view()), rows, block)
     if need == 0 and L.exl3_last_error():
@@ -589,6 +609,8 @@ def moe_linear(w: MoeWeight, x_rot: torch.Tensor, block_expert: torch.Tensor, bl
 def moe_combine(y_routed: torch.Tensor, pair_row: torch.Tensor, topk_weights: torch.Tensor) -> torch.Tensor:
     T, k = topk_weights.shape
     N = y_routed.shape[1]
+    if pair_row.numel() != T * k:
+        raise ValueError(f"pair_row has {pair_row.numel()} entries, expected T*topk = {T * k}")
     out = torch.empty((T, N), dtype=y_routed.dtype, device=y_routed.device)
     _check(load().exl3_moe_combine(_dev_ptr(y_routed, "y_routed", (torch.bfloat16, torch.float16)),
                                    _BF16 if y_routed.dtype == torch.bfloat16 else _F16,
