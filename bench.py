@@ -101,10 +101,10 @@ def kernel_key(lay, plan) -> str:
     if bm <= 64:
         qw = plan["wg_cols"] // 32
         name = f"exl3::gemm_kernel<{lay.bits}, {cb}u, {bm // 16}, {str(multi).lower()}, {quads}, {qw}, false>"
-    elif bm == 128 and plan["parts"] == 1 and plan["mode"] == 0:
+    elif bm == 128 and not multi:
         name = f"exl3::gemm_wide_kernel<{lay.bits}, {cb}u, 64, false, 1>"
     elif bm == 128:
-        name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, {str(multi).lower()}>"
+        name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, true>"
     else:
         name = f"exl3::gemm_wide_kernel<{lay.bits}, {cb}u, {bm // 2}, {str(multi).lower()}, 1>"
     return name

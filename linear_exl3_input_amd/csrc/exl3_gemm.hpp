@@ -812,7 +812,9 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
 
 // -------------------------------------------------------------- big GEMM
 //
-// For M around 128: a BM = 16*MT row x 128 column tile (MT = 8) on 4 waves.
+// For M around 128 with a unit of several K parts per workgroup (their sums
+// folded in registers; one part per workgroup takes the 8-wave 128-row tile
+// of gemm_wide_kernel): a BM = 16*MT row x 128 column tile (MT = 8) on 4 waves.
 // As in gemm_kernel, wave w decodes the B operands of n-tiles 2w and 2w+1 and
 // keeps them in registers, now against all BM rows, so each trellis value is
 // decoded once per BM rows and feeds 2*MT MFMAs per lane-set.  The rotated
@@ -1191,19 +1193,20 @@ hipError_t launch_gemm_t(int quads, bool half, bool multi, const GemmParams &p, 
   return hipGetLastError();
 }
 
+// 128-row tiles of a unit of several parts (folded in registers)
 template <int BITS, uint32_t CB, int MT>
-hipError_t launch_big_t(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  if (multi) hipLaunchKernelGGL((gemm_big_kernel<BITS, CB, MT, true>), grid, dim3(WG_THREADS), 0, s, p);
-  else hipLaunchKernelGGL((gemm_big_kernel<BITS, CB, MT, false>), grid, dim3(WG_THREADS), 0, s, p);
+hipError_t launch_big_t(const GemmParams &p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_big_kernel<BITS, CB, MT, true>), grid, dim3(WG_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 template <int BITS, uint32_t CB>
 hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
 
-// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128 -> gemm_big_kernel
-// (or gemm_wide_kernel with 64-row waves for one fused part), 256/512 ->
-// gemm_wide_kernel (512 threads; 512 for a single part per workgroup only).
+// bm = rows per M-tile: 16/32/64 -> gemm_kernel, 128 -> gemm_wide_kernel
+// with 64-row waves (one part per workgroup) or gemm_big_kernel (a unit of
+// several parts), 256/512 -> gemm_wide_kernel (512 threads; 512 for a single
+// part per workgroup only).
 template <int BITS, uint32_t CB>
 hipError_t launch_gemm_cb(int bm, int quads, bool half, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   if (bm > 64 && (quads != 1 || half)) return hipErrorInvalidValue;
@@ -1212,12 +1215,11 @@ hipError_t launch_gemm_cb(int bm, int quads, bool half, bool multi, const GemmPa
     case 32: return launch_gemm_t<BITS, CB, 2>(quads, half, multi, p, grid, s);
     case 64: return launch_gemm_t<BITS, CB, 4>(quads, half, multi, p, grid, s);
     case 128:
-      // one part over the whole K (layers of 256+ column blocks): the 8-wave
-      // tile with 64-row waves (gate_up 5120 x 34816 at 128 rows 170 -> 154
-      // us); split K keeps the 4-wave tile (q_proj / down_proj at 128 rows
-      // 55 / 63 us against 62 / 68)
-      if (!multi && p.parts == 1 && !p.slab_mode) return launch_wide_t<BITS, CB>(128, false, p, grid, s);
-      return launch_big_t<BITS, CB, 8>(multi, p, grid, s);
+      // one part per workgroup: the 8-wave tile with 64-row waves, two
+      // workgroups per CU; a unit of several parts folded in registers: the
+      // 4-wave tile
+      if (!multi) return launch_wide_t<BITS, CB>(128, false, p, grid, s);
+      return launch_big_t<BITS, CB, 8>(p, grid, s);
     case 256:
     case 512: return launch_wide_t<BITS, CB>(bm, multi, p, grid, s);
     default: return hipErrorInvalidValue;

@@ -1,5 +1,16 @@
 // 2*RW-row x 128-column GEMM tile for large M on gfx950 (RW = 128 or 256;
-// RW = 64 for 128-row tiles of one fused part).
+// RW = 64 for 128-row tiles of one part per workgroup).
+//
+// RW = 64 is sized for two workgroups per CU (four waves per SIMD): two
+// trellis stage slots and at most 80 KB of LDS, at most 128 VGPRs.  At 128
+// rows the decode costs about six VALU instructions per MFMA, and with only
+// one workgroup's two waves per SIMD the SIMD sat idle half the time waiting
+// on its own dependences; the second workgroup fills those gaps (gate_up
+// 5120 x 34816 at 128 rows 155 -> 121 us, whose 272 tiles also no longer
+// leave a second round of 16; q_proj / down_proj at 128 rows in slabs
+// 50 / 70 -> 44 / 63 us against the 4-wave 128-row tile).  The same budget
+// at RW = 128 forces a one-k-step x~ prefetch and spills, and was slower
+// (q_proj / down_proj at 256 rows 68 / 96 -> 73 / 110 us).
 //
 // Eight waves: wave w = 4*rh + wq owns rows RW*rh .. RW*rh+RW-1 of the tile
 // and the 32 columns of n-tiles 2*wq and 2*wq+1 (as in gemm_kernel, one MFMA
@@ -53,12 +64,13 @@ struct Wide {
   static constexpr int T_OPS = (T_CHUNKS + 64 * LOADERS - 1) / (64 * LOADERS);  // per trellis wave per stage
   static constexpr int JUNK_CHUNKS = T_OPS * 64 * LOADERS - T_CHUNKS;           // landing area for the surplus
   static constexpr int TSLOT_DW = T_CHUNKS * 4;
-  static constexpr int TSLOTS = RW == 128 ? 4 : (BITS <= 6 ? 3 : 2);
+  static constexpr int OCC = RW == 64 ? 2 : 1;             // workgroups per CU
+  static constexpr int TSLOTS = OCC == 2 ? 2 : RW == 128 ? 4 : (BITS <= 6 ? 3 : 2);
   static constexpr int A_OPS = BM / 16 / LOADERS;        // direct loads per x~ wave per k-step
   static constexpr int ASLOT_DW = BM * 16;               // BM rows x 32 fp16
   static constexpr int XB_DW = WAVES * 256;              // one decoded B half per wave
   static constexpr int FIXED_DW = TSLOTS * TSLOT_DW + JUNK_CHUNKS * 4 + 2 * XB_DW;
-  static constexpr int LDS_LIMIT_DW = 160 * 1024 / 4;
+  static constexpr int LDS_LIMIT_DW = 160 * 1024 / 4 / OCC;
   // x~ prefetch distance in k-steps (as deep as LDS allows).  With PF >= 3
   // (AHEAD) x~ of k-step i+1 is complete at the barrier that ends k-step
   // i-1, and a wave reads its first fragments of k-step i+1 before the
@@ -92,8 +104,10 @@ struct Wide {
   }
 };
 
+// (launch bounds: 512 threads and, for RW = 64, at least four waves per SIMD,
+// which caps a wave at 128 VGPRs)
 template <int BITS, uint32_t CB, int RW, bool MULTI, int SCHED = 1>
-__global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
+__global__ __launch_bounds__(512, RW == 64 ? 4 : 1) void gemm_wide_kernel(const GemmParams p) {
   using W = Wide<BITS, RW>;
   constexpr int MF = W::MF;
   constexpr int PF = W::PF;
@@ -453,9 +467,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(const GemmParams p) {
   }
 }
 
-// bm 128: 64-row waves, one part only; bm 256: 128-row waves (both fold
-// modes); bm 512: 256-row waves, single part per workgroup only (the host
-// never asks for the fold there).
+// bm 128: 64-row waves, one part per workgroup (fused or slabs); bm 256:
+// 128-row waves (both fold modes); bm 512: 256-row waves, single part per
+// workgroup only (the host never asks for the fold there).
 template <int BITS, uint32_t CB>
 hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
   if (bm == 128 && !multi) {
