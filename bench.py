@@ -105,6 +105,8 @@ def kernel_key(lay, plan) -> str:
         name = f"exl3::gemm_wide_kernel<{lay.bits}, {cb}u, 64, false, 1>"
     elif bm == 128:
         name = f"exl3::gemm_big_kernel<{lay.bits}, {cb}u, 8, true>"
+    elif bm == 512:
+        name = f"exl3::gemm_wide4_kernel<{lay.bits}, {cb}u>"
     else:
         name = f"exl3::gemm_wide_kernel<{lay.bits}, {cb}u, {bm // 2}, {str(multi).lower()}, 1>"
     return name

@@ -1,5 +1,6 @@
-// 2*RW-row x 128-column GEMM tile for large M on gfx950 (RW = 128 or 256;
-// RW = 64 for 128-row tiles of one part per workgroup).
+// 2*RW-row x 128-column GEMM tile for large M on gfx950 (RW = 128; RW = 64
+// for 128-row tiles of one part per workgroup; 512-row tiles are
+// gemm_wide4_kernel below).
 //
 // RW = 64 is sized for two workgroups per CU (four waves per SIMD): two
 // trellis stage slots and at most 80 KB of LDS, at most 128 VGPRs.  At 128
@@ -65,7 +66,7 @@ struct Wide {
   static constexpr int JUNK_CHUNKS = T_OPS * 64 * LOADERS - T_CHUNKS;           // landing area for the surplus
   static constexpr int TSLOT_DW = T_CHUNKS * 4;
   static constexpr int OCC = RW == 64 ? 2 : 1;             // workgroups per CU
-  static constexpr int TSLOTS = OCC == 2 ? 2 : RW == 128 ? 4 : (BITS <= 6 ? 3 : 2);
+  static constexpr int TSLOTS = OCC == 2 ? 2 : 4;
   static constexpr int A_OPS = BM / 16 / LOADERS;        // direct loads per x~ wave per k-step
   static constexpr int ASLOT_DW = BM * 16;               // BM rows x 32 fp16
   static constexpr int XB_DW = WAVES * 256;              // one decoded B half per wave
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(512, RW == 64 ? 4 : 1) void gemm_wide_kernel(const 
   // second accumulator set needs the registers; none without AHEAD)
   constexpr int NPRE = !W::AHEAD ? 0 : (MULTI ? 4 : 8);
   static_assert(!W::AHEAD || MF == 8, "read-ahead schedule is for 128-row waves");
-  static_assert(!(MULTI && RW > 128), "two accumulator sets of 256 rows do not fit");
+  static_assert(RW == 64 || RW == 128, "512-row tiles are gemm_wide4_kernel");
   __shared__ __attribute__((aligned(16))) uint32_t lds[W::LDS_DW];
   uint32_t *const tring = lds;
   uint32_t *const junk = lds + TSLOTS * W::TSLOT_DW;
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(512, RW == 64 ? 4 : 1) void gemm_wide_kernel(const 
             });
           }
         };
-        // Without the read-ahead across the barrier (256-row waves): a ring
+        // Without the read-ahead across the barrier (64-row waves): a ring
         // of four x~ fragments read three ahead of their products, and the
         // decode cut into six pieces between the product pairs, each step
         // fenced so the compiler keeps the reads early (left to itself, at
@@ -467,8 +468,290 @@ __global__ __launch_bounds__(512, RW == 64 ? 4 : 1) void gemm_wide_kernel(const 
   }
 }
 
+// 512-row x 128-column tile on 8 waves as 4 row quarters x 2 column halves
+// (wave w: rows 128 (w >> 1) .. +127, the 64 columns of n-tiles 4 (w & 1) ..
+// +3).  Per 32-k step a wave reads 8 x~ fragments and 3 decoded B fragments
+// from LDS and issues 32 MFMAs into 128 accumulators; the four waves of a
+// column half each decode one of its four B fragments (pair 2ch + (rq >> 1),
+// half rq & 1) and share them through LDS.  Against two row halves of 256
+// rows (16 x~ fragments and one B fragment read per wave and k-step) that is
+// 88 KB of LDS reads per k-step instead of 136 KB, for the same decode work
+// per wave.  Loads, waits, ring slots and the k-step schedule are
+// gemm_wide_kernel's; same fragments, k order and chains, so the same bits.
+template <int BITS>
+struct Wide4 {
+  static constexpr int WAVES = 8;
+  static constexpr int MF = 8;   // 16-row fragments per wave
+  static constexpr int NF = 4;   // B fragments per wave
+  static constexpr int BM = 512;
+  static constexpr int LOADERS = 4;
+  static constexpr int TSTRIDE = 8 * BITS + 8;
+  static constexpr int T_CHUNKS = 64 * (2 * BITS + 2);
+  static constexpr int T_OPS = (T_CHUNKS + 64 * LOADERS - 1) / (64 * LOADERS);
+  static constexpr int JUNK_CHUNKS = T_OPS * 64 * LOADERS - T_CHUNKS;
+  static constexpr int TSLOT_DW = T_CHUNKS * 4;
+  static constexpr int TSLOTS = BITS <= 6 ? 3 : 2;
+  static constexpr int A_OPS = BM / 16 / LOADERS;
+  static constexpr int ASLOT_DW = BM * 16;
+  static constexpr int XB_DW = WAVES * 256;
+  static constexpr int FIXED_DW = TSLOTS * TSLOT_DW + JUNK_CHUNKS * 4 + 2 * XB_DW;
+  static constexpr int LDS_LIMIT_DW = 160 * 1024 / 4;
+  static constexpr int PF = FIXED_DW + 4 * ASLOT_DW <= LDS_LIMIT_DW ? 3 : 2;
+  static constexpr int ASLOTS = PF + 1;
+  static constexpr int MAIN_DW = FIXED_DW + ASLOTS * ASLOT_DW;
+  static constexpr int ZR = 128;  // output rows per pass: one row quarter
+  static constexpr int Z_DW = ZR * Z_ROW;
+  static constexpr int LDS_DW = MAIN_DW > Z_DW ? MAIN_DW : Z_DW;
+  static constexpr int NY = Geom<BITS>::NY;
+  static constexpr int NX = Geom<BITS>::NX;
+  static constexpr bool PERM = BITS % 2 == 0;
+  static_assert(T_CHUNKS % 64 == 0, "each direct load lands whole in a stage or in the surplus area");
+  static_assert(LDS_DW <= LDS_LIMIT_DW, "LDS budget");
+  static constexpr int A_WAIT = A_OPS * (PF - 1);
+  static constexpr int t_wait(int ks) {
+    return T_OPS * (TSLOTS - 1 + (ks == 3 ? 1 : 0) - (ks >= 2 ? 1 : 0));
+  }
+};
+
+template <int BITS, uint32_t CB>
+__global__ __launch_bounds__(512, 1) void gemm_wide4_kernel(const GemmParams p) {
+  using W = Wide4<BITS>;
+  constexpr int MF = W::MF;
+  constexpr int NF = W::NF;
+  constexpr int PF = W::PF;
+  constexpr int ASLOTS = W::ASLOTS;
+  constexpr int TSLOTS = W::TSLOTS;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[W::LDS_DW];
+  uint32_t *const tring = lds;
+  uint32_t *const junk = lds + TSLOTS * W::TSLOT_DW;
+  uint32_t *const xbuf = junk + W::JUNK_CHUNKS * 4;
+  uint32_t *const aring = xbuf + 2 * W::XB_DW;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lw = wave & 3;     // loader index
+  const int role = wave >> 2;  // 0: x~ loads; 1: trellis loads
+  const int ch = wave & 1;     // column half
+  const int rq = wave >> 1;    // row quarter; decodes fragment f = rq of its half
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nb = blockIdx.x;
+  const int m0 = p.row_base + blockIdx.z * W::BM;
+  const int rend = p.row_end;
+  const int M = p.M, K = p.K, N = p.N;
+  const int NT = N >> 4;
+  const int KB = K >> 7;
+
+  const int p_begin = blockIdx.y * p.unit;
+  const int kb_begin = (int)((int64_t)p_begin * KB / p.parts);
+  const int kb_end = (int)((int64_t)(p_begin + 1) * KB / p.parts);
+  const int nst = kb_end - kb_begin;
+  const int nks = 4 * nst;
+  const int k_begin = kb_begin * 128;
+
+  int shard = 0;
+  while (shard + 1 < p.n_shards && nb >= p.shard_end_blk[shard]) ++shard;
+  const uint16_t *__restrict__ xs = p.x_rot + (int64_t)shard * M * K;
+
+  const uint16_t *const a_base = xs + (int64_t)(k_begin >> 5) * M * 32;
+  const uint16_t *const t_base = p.trellis + ((int64_t)kb_begin * 8 * NT + nb * 8) * (16 * BITS);
+  uint32_t src[W::A_OPS > W::T_OPS ? W::A_OPS : W::T_OPS];
+  if (role == 0) {
+#pragma unroll
+    for (int t = 0; t < W::A_OPS; ++t) {
+      int row = m0 + 16 * (lw + W::LOADERS * t) + (lane & 15);
+      row = row < rend ? row : rend - 1;
+      src[t] = (uint32_t)(row * 32 + 8 * (lane >> 4));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < W::T_OPS; ++r) {
+      const int q = r * 64 * W::LOADERS + lw * 64 + lane;
+      uint32_t off;
+      if (q < W::T_CHUNKS) {
+        const int t = q / (2 * BITS + 2);
+        const int c = q - t * (2 * BITS + 2);
+        const int sc = c == 0 ? 2 * BITS - 1 : (c == 2 * BITS + 1 ? 0 : c - 1);
+        off = (uint32_t)(((t >> 3) * NT + (t & 7)) * (16 * BITS) + sc * 8);
+      } else {
+        off = (uint32_t)((lane % (2 * BITS)) * 8);
+      }
+      src[r] = off;
+    }
+  }
+  const int64_t a_kstep = (int64_t)M * 32;
+  const int64_t tr_stage = (int64_t)8 * NT * (16 * BITS);
+  auto issue_a = [&](int kstep, int slot) {
+    const uint16_t *const base = a_base + a_kstep * min(kstep, nks - 1);
+    uint32_t *const dst0 = aring + slot * W::ASLOT_DW;
+#pragma unroll
+    for (int t = 0; t < W::A_OPS; ++t)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + src[t]),
+                                       (__attribute__((address_space(3))) void *)(dst0 + (lw + W::LOADERS * t) * 256),
+                                       16, 0, 0);
+  };
+  auto issue_trellis = [&](int stage, int slot) {
+    const uint16_t *const base = t_base + tr_stage * min(stage, nst - 1);
+    uint32_t *const dst0 = tring + slot * W::TSLOT_DW;
+#pragma unroll
+    for (int r = 0; r < W::T_OPS; ++r) {
+      const int q0 = r * 64 * W::LOADERS + lw * 64;
+      uint32_t *dst = q0 < W::T_CHUNKS ? dst0 + q0 * 4 : junk + (q0 - W::T_CHUNKS) * 4;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + src[r]),
+                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+  };
+
+  // decode constants of the wave's own fragment: pair 2ch + (rq >> 1), half rq & 1
+  const int dpair = 2 * ch + (rq >> 1);
+  int doff, sh = 0;
+  uint32_t sel = 0;
+  if constexpr (W::PERM) {
+    lane_window_perm<BITS>(j, g, rq & 1, doff, sel);
+  } else {
+    lane_window<BITS>(j, g, rq & 1, doff, sh);
+  }
+  const int t_lane = ((g >> 1) * WG_NT + 2 * dpair + (j >> 3)) * W::TSTRIDE + doff;
+  auto decode_own = [&](const uint32_t *slot, int kp) -> u32x4_t {
+    const uint32_t *tp = slot + kp * 2 * WG_NT * W::TSTRIDE + t_lane;
+    uint32_t X[W::NX], Y[W::NY];
+#pragma unroll
+    for (int i = 0; i < W::NX; ++i) X[i] = tp[i];
+    raw_normalize<BITS>(X, sel, sh, Y);
+    return u32x4_t{frag_pair<BITS, CB, 0>(Y), frag_pair<BITS, CB, 1>(Y), frag_pair<BITS, CB, 2>(Y),
+                   frag_pair<BITS, CB, 3>(Y)};
+  };
+  // xbuf[buf][wave]: the fragment wave w decoded; fragment f of this wave's
+  // column half comes from wave 2f + ch
+  uint32_t *const xb_own0 = xbuf + wave * 256 + 4 * lane;
+  const uint32_t *const xb_half0 = xbuf + ch * 256 + 4 * lane;
+  const uint32_t *const a_lane = aring + rq * MF * 256 + 4 * lane;
+
+  float4_t acc[MF][NF];
+#pragma unroll
+  for (int mt = 0; mt < MF; ++mt)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[mt][f] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (role == 0) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) issue_a(i, i);
+  } else {
+#pragma unroll
+    for (int s = 0; s < TSLOTS; ++s) issue_trellis(s, s);
+  }
+  wait_vmcnt<0>();
+  barrier_lds();
+  *(u32x4_t *)xb_own0 = decode_own(tring, 0);
+  barrier_lds();
+
+  int st = 0;
+  int ts0 = 0;
+  int as_cur = 0;
+  auto run_stages = [&](auto ph_c) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph_c)::value;
+    for (; st < nst; ++st) {
+      const int ts1 = ts0 == TSLOTS - 1 ? 0 : ts0 + 1;
+      auto kstep = [&](auto ks_c) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ks_c)::value;
+        const int i = 4 * st + ks;
+        const int as = (as_cur + ks) % ASLOTS;
+        const int as_pf = as == 0 ? ASLOTS - 1 : as - 1;
+        if constexpr (PH == 0) issue_a(i + PF, as_pf);
+        else if constexpr (ks == 3) issue_trellis(st + TSLOTS, ts0);
+        asm volatile("" ::: "memory");
+        // the column half's four fragments (this wave's own among them),
+        // decoded during the last k-step
+        half8_t B[NF];
+        const uint32_t *xb = xb_half0 + (i & 1) * W::XB_DW;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) B[f] = *(const half8_t *)(xb + f * 512);
+        const uint32_t *tslot = tring + (ks < 3 ? ts0 : ts1) * W::TSLOT_DW;
+        const uint32_t *tp = tslot + ((ks + 1) & 3) * 2 * WG_NT * W::TSTRIDE + t_lane;
+        uint32_t X[W::NX], Y[W::NY];
+#pragma unroll
+        for (int q = 0; q < W::NX; ++q) X[q] = tp[q];
+        const uint32_t *as_p = a_lane + as * W::ASLOT_DW;
+        u32x4_t nb4;
+        // x~ fragments in a ring read three ahead of their four products;
+        // the next k-step's decode cut into six pieces between them
+        constexpr int RD = 3;
+        __builtin_amdgcn_sched_barrier(0);
+        half8_t af[4];
+#pragma unroll
+        for (int q = 0; q < RD; ++q) af[q] = *(const half8_t *)(as_p + q * 256);
+        static_for<0, MF>([&](auto mt_c) {
+          constexpr int mt = decltype(mt_c)::value;
+          if constexpr (mt + RD < MF) af[(mt + RD) % 4] = *(const half8_t *)(as_p + (mt + RD) * 256);
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            acc[mt][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt % 4], B[f], acc[mt][f], 0, 0, 0);
+          static_for<mt * 6 / MF, (mt + 1) * 6 / MF>([&](auto pc) {
+            constexpr int piece = decltype(pc)::value;
+            if constexpr (piece == 0) raw_normalize<BITS>(X, sel, sh, Y);
+            else if constexpr (piece < 5) nb4[piece - 1] = frag_pair<BITS, CB, piece - 1>(Y);
+            else *(u32x4_t *)(xb_own0 + ((i + 1) & 1) * W::XB_DW) = nb4;
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (PH == 0) wait_vmcnt<W::A_WAIT>();
+        else wait_vmcnt<W::t_wait(ks)>();
+        barrier_lds();
+      };
+      kstep(std::integral_constant<int, 0>{});
+      kstep(std::integral_constant<int, 1>{});
+      kstep(std::integral_constant<int, 2>{});
+      kstep(std::integral_constant<int, 3>{});
+      ts0 = ts1;
+      as_cur = (as_cur + 4) % ASLOTS;
+    }
+  };
+  if (role == 0) run_stages(std::integral_constant<int, 0>{});
+  else run_stages(std::integral_constant<int, 1>{});
+  wait_vmcnt<0>();
+  barrier_lds();
+
+  int col[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) col[f] = lane_col(2 * ch + (f >> 1), j, f & 1);
+  if (p.slab_mode) {
+    const int rows = rend - p.row_base;
+#pragma unroll
+    for (int mt = 0; mt < MF; ++mt) {
+      const int row0 = m0 - p.row_base + rq * 128 + mt * 16 + 4 * g;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) store_partial(p.slabs, blockIdx.y, rows, N, row0, nb * 128 + col[f], acc[mt][f]);
+    }
+    return;
+  }
+
+  // output transform, one row quarter (128 rows) per pass through LDS
+  float *z = reinterpret_cast<float *>(lds);
+  uint16_t *__restrict__ y = reinterpret_cast<uint16_t *>(p.y);
+  const OutWords16 ow = out_words16(p.svh, p.bias, nb * 128, lane);
+  const bool has_bias = p.bias != nullptr;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    if (pass > 0) barrier_lds();
+    if (rq == pass) {
+#pragma unroll
+      for (int mt = 0; mt < MF; ++mt)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[(mt * 16 + 4 * g + i) * Z_ROW + col[f]] = acc[mt][f][i];
+    }
+    barrier_lds();
+#pragma unroll
+    for (int r0 = 8 * wave; r0 < W::ZR; r0 += 8 * W::WAVES) {
+      if (p.out_bf16) output_rows8<true>(z, Z_ROW, r0, ow, has_bias, y, m0 + pass * W::ZR + r0, rend, N, nb * 128, lane);
+      else output_rows8<false>(z, Z_ROW, r0, ow, has_bias, y, m0 + pass * W::ZR + r0, rend, N, nb * 128, lane);
+    }
+  }
+}
+
 // bm 128: 64-row waves, one part per workgroup (fused or slabs); bm 256:
-// 128-row waves (both fold modes); bm 512: 256-row waves, single part per
+// 128-row waves (both fold modes); bm 512: gemm_wide4_kernel, single part per
 // workgroup only (the host never asks for the fold there).
 template <int BITS, uint32_t CB>
 hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
@@ -478,7 +761,7 @@ hipError_t launch_wide_t(int bm, bool multi, const GemmParams &p, dim3 grid, hip
     if (multi) hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 128, true>), grid, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 128, false>), grid, dim3(512), 0, s, p);
   } else if (bm == 512 && !multi) {
-    hipLaunchKernelGGL((gemm_wide_kernel<BITS, CB, 256, false>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_wide4_kernel<BITS, CB>), grid, dim3(512), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -180,7 +180,8 @@ def test_bias_every_kernel_family(M):
     pl = ex.plan(w, M)
     tree = dict(parts=pl["parts"], groups=pl["groups"])
     scheds = [dict(tree, bm=b, mode=ex.EXL3_MODE_SLABS) for b in (16, 64, 128, 256)]
-    scheds += [dict(tree, bm=16, mode=ex.EXL3_MODE_SLABS, wg_cols=64, unit=1),
+    scheds += [dict(tree, bm=512, mode=ex.EXL3_MODE_SLABS, unit=1),
+               dict(tree, bm=16, mode=ex.EXL3_MODE_SLABS, wg_cols=64, unit=1),
                dict(tree, decoder=ex.EXL3_DECODER_DENSE, mode=ex.EXL3_MODE_SLABS)]
     if M <= 64:
         scheds.append(dict(tree, decoder=ex.EXL3_DECODER_TABLE))
@@ -196,3 +197,11 @@ def test_bias_every_kernel_family(M):
     res = olin.check(first, ref, t.svh, lay.K, "bf16")
     banner(f"bias M={M} ({len(outs)} schedules): {res}")
     assert res.ok, str(res)
+    # one part: the output stage inside every tile kernel (fused), fp16 out
+    one = {b: bits16(ex.linear(w, xr, torch.float16, parts=1, mode=ex.EXL3_MODE_FUSED, bm=b))
+           for b in (16, 64, 128, 256, 512)}
+    for b, y in one.items():
+        assert np.array_equal(y, one[16]), f"one part, bm={b}"
+    res1 = olin.check(one[16], ref, t.svh, lay.K, "f16")
+    banner(f"bias M={M} one part, fp16 out: {res1}")
+    assert res1.ok, str(res1)

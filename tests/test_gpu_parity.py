@@ -177,17 +177,18 @@ def test_schedules_agree_bit_for_bit(parts):
     _check(t, first)
 
 
-@pytest.mark.parametrize("bits,cb", [(6, "mul1"), (5, "3inst"), (8, "mcg"), (3, "mul1")])
+@pytest.mark.parametrize("bits,cb", [(6, "mul1"), (5, "3inst"), (8, "mcg"), (3, "mul1"), (1, "mcg"), (2, "3inst"),
+                                     (4, "mul1"), (7, "mcg")])
 @pytest.mark.parametrize("M", [300, 600])
 def test_large_tiles_ragged(bits, cb, M):
-    """The 256- and 512-row tiles on a ragged last tile: bit-identical to the
-    64-row tile, for one part and for slabs of two parts."""
+    """The 128-, 256- and 512-row tiles on a ragged last tile: bit-identical
+    to the 64-row tile, for one part and for slabs of two parts."""
     banner(f"large tiles {bits}-bit {cb} M={M}")
     lay = wl.small_layer("tall", 1024, (256,), bits, cb, (M,), seed=30 + bits)
     t = wl.gen_all(lay)
     for parts, mode in ((1, ex.EXL3_MODE_FUSED), (2, ex.EXL3_MODE_SLABS)):
         ref = _run(t, parts=parts, mode=mode, bm=64)
-        for bm in (256, 512):
+        for bm in (128, 256, 512):
             assert np.array_equal(_run(t, parts=parts, mode=mode, bm=bm), ref), f"bm={bm} parts={parts}"
     _check(t, ref)
 
