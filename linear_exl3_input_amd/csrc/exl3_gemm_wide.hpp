@@ -470,13 +470,14 @@ __global__ __launch_bounds__(512, RW == 64 ? 4 : 1) void gemm_wide_kernel(const 
 
 // 512-row x 128-column tile on 8 waves as 4 row quarters x 2 column halves
 // (wave w: rows 128 (w >> 1) .. +127, the 64 columns of n-tiles 4 (w & 1) ..
-// +3).  Per 32-k step a wave reads 8 x~ fragments and 3 decoded B fragments
-// from LDS and issues 32 MFMAs into 128 accumulators; the four waves of a
-// column half each decode one of its four B fragments (pair 2ch + (rq >> 1),
-// half rq & 1) and share them through LDS.  Against two row halves of 256
-// rows (16 x~ fragments and one B fragment read per wave and k-step) that is
-// 88 KB of LDS reads per k-step instead of 136 KB, for the same decode work
-// per wave.  Loads, waits, ring slots and the k-step schedule are
+// +3).  Per 32-k step a wave reads 8 x~ fragments and the 4 decoded B
+// fragments of its column half from LDS and issues 32 MFMAs into 128
+// accumulators; the four waves of a column half each decode one of the four
+// B fragments (pair 2ch + (rq >> 1), half rq & 1) and share them through LDS
+// (a wave reads its own back too: keeping it in registers pushed the kernel
+// past 256 VGPRs into spills).  Against two row halves of 256 rows (16 x~
+// fragments and one B fragment read per wave and k-step) that is 96 KB of
+// LDS reads per k-step instead of 136 KB, for the same decode work per wave.  Loads, waits, ring slots and the k-step schedule are
 // gemm_wide_kernel's; same fragments, k order and chains, so the same bits.
 template <int BITS>
 struct Wide4 {
