@@ -2,8 +2,9 @@
 allocate, through the C ABI: every call's output has exactly the bits of
 exl3_linear with its workspace, on two calls in a row with the second one
 smaller -- plans whose workspace fits the library's scratch, one whose slabs
-need row chunks there, and one whose planner schedule (dequantized weights)
-does not fit and runs another schedule of the same part tree."""
+need row chunks there, one whose planner schedule (dequantized weights)
+does not fit and runs another schedule of the same part tree, and one-part
+plans on the 512- and 128-row tiles."""
 import ctypes
 
 import numpy as np
@@ -39,6 +40,9 @@ CASES = [
     ("row_chunks", 4096, (2048,), 4, "mcg", 3000, 517),
     ("dense_planner", 4096, (4096, 4096), 4, "mul1", 2048, 100),
     ("table", 5120, (12288,), 6, "mul1", 64, 24),
+    # one part over all of K (256 column blocks): 512-row tiles, then 128-row
+    # tiles two to a CU
+    ("wide_tiles", 1024, (32768,), 4, "mul1", 600, 128),
 ]
 
 
@@ -51,6 +55,8 @@ def test_noalloc_matches_linear(name, K, shards, bits, cb, m1, m2):
     banner(f"noalloc {name}: planner at M={m1} {plan1}")
     if name == "dense_planner":
         assert plan1["decoder"] == ex.EXL3_DECODER_DENSE and plan1["workspace"] > SCRATCH
+    if name == "wide_tiles":
+        assert plan1["bm"] == 512 and plan1["parts"] == 1 and ex.plan(w, m2)["bm"] == 128
     if name == "row_chunks":
         # the planner keeps 8 group slabs of all 3000 rows (196 MB); the
         # scratch takes them in row chunks
