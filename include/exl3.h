@@ -46,7 +46,7 @@ extern "C" {
 #endif
 
 #define EXL3_MAX_SHARDS 16
-#define EXL3_ABI_VERSION 5
+#define EXL3_ABI_VERSION 6
 
 /* The first EXL3_WORKSPACE_COUNTER_BYTES of every workspace hold per-tile
  * arrival counters (see exl3_linear): they must be zero before the first
@@ -265,6 +265,33 @@ exl3_status exl3_linear_noalloc(const exl3_weight *w, const uint16_t *x_rot, int
 
 /* Workspace bytes for exl3_linear_ex with the same `force`. */
 size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan *force);
+
+/* The whole layer in one call, from x instead of x_rot:
+ *   y = exl3_linear(w, exl3_input_transform(x, w->suh))
+ * with exactly those bits.  x is [M][K] in x_dtype (EXL3_BF16 or EXL3_F16),
+ * y [M][N] in y_dtype; `w` needs trellis and suh.  The cuda-exl3 README
+ * ("Two further departures") keeps the transform a separate kernel, where
+ * upstream fuses it into the GEMM behind a grid-wide sync; this entry point
+ * keeps both calls available and adds a third way for the plans whose GEMM
+ * is the small-tile kernel (16-64 row tiles) and whose workgroups' K ranges
+ * fit their LDS stage slots: every workgroup rotates its own rows and K
+ * range of x straight into LDS (the same fp32 arithmetic, rounded once to
+ * fp16), so the call is one launch with no x_rot in memory and no
+ * workgroup waits for another.  Other plans run the transform into the
+ * workspace, then the GEMM (two launches, as the separate calls would).
+ *   workspace at least exl3_forward_workspace_bytes(w, M) bytes: the plan's
+ *             own workspace (arrival counters first, zero on entry as for
+ *             exl3_linear), plus room for x_rot when the rotation does not
+ *             run in the GEMM.  x_rot then starts after both the plan's
+ *             workspace and the first EXL3_WORKSPACE_COUNTER_BYTES, so the
+ *             counters keep their zeros for the next call that shares the
+ *             workspace.
+ * Uses the tuned schedule of the shape and M bucket when one is set (see
+ * exl3_tune).  Errors as exl3_linear, and EXL3_ERR_INVALID_ARG for a bad
+ * x pointer or x_dtype. */
+exl3_status exl3_forward(const exl3_weight *w, const void *x, int32_t x_dtype, int32_t M, void *y, int32_t y_dtype,
+                         void *workspace, size_t workspace_bytes, void *stream);
+size_t exl3_forward_workspace_bytes(const exl3_weight *w, int32_t M);
 
 /* ------------------------------------------------ schedule autotuner
  * (cuda-exl3 README, "Where the time goes": the best tile tier depends on

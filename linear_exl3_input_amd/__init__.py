@@ -65,7 +65,7 @@ class _Plan(ctypes.Structure):
                 ("launches", ctypes.c_int32), ("wg_cols", ctypes.c_int32), ("workspace", ctypes.c_size_t)]
 
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 COUNTER_BYTES = 65536  # EXL3_WORKSPACE_COUNTER_BYTES: zeroed arrival counters at the workspace's start
 
 
@@ -98,6 +98,8 @@ def load() -> ctypes.CDLL:
             "exl3_linear": (i32, [W, vp, i32, vp, i32, vp, sz, vp]),
             "exl3_linear_ex": (i32, [W, vp, i32, vp, i32, vp, sz, vp, P]),
             "exl3_linear_noalloc": (i32, [W, vp, i32, vp, i32, vp]),
+            "exl3_forward": (i32, [W, vp, i32, i32, vp, i32, vp, sz, vp]),
+            "exl3_forward_workspace_bytes": (sz, [W, i32]),
             "exl3_plan_query": (i32, [W, i32, P]),
             "exl3_plan_query_ex": (i32, [W, i32, P, P]),
             "exl3_status_str": (ctypes.c_char_p, [i32]),
@@ -373,9 +375,36 @@ def linear(w: Exl3Weight, x_rot: torch.Tensor, out_dtype: torch.dtype = torch.bf
     return out
 
 
-def forward(w: Exl3Weight, x: torch.Tensor, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
-    """The whole layer in the caller's dtype: y = had(W_q . had(x*suh)) * svh."""
-    return linear(w, input_transform(x, w.suh), out_dtype or x.dtype)
+def forward_workspace_bytes(w: Exl3Weight, M: int) -> int:
+    L = load()
+    n = L.exl3_forward_workspace_bytes(ctypes.byref(w.view()), M)
+    err = L.exl3_last_error().decode()
+    if n == 0 and err:
+        raise Exl3Error(1, "EXL3_ERR_INVALID_ARG", err)
+    return n
+
+
+def forward(w: Exl3Weight, x: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer in one call (exl3_forward): y = had(W_q . had(x*suh)) * svh,
+    the same bits as linear(w, input_transform(x, w.suh)); x [M, K] bf16 or fp16,
+    y in out_dtype (default x's dtype)."""
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x shape {tuple(x.shape)} is not [M, {w.K}]")
+    out_dtype = out_dtype or x.dtype
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"out_dtype {out_dtype} is not bf16/fp16")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, w.N), dtype=out_dtype, device=x.device)
+    y_ptr = _out_ptr(out, "out", (M, w.N), (out_dtype,))
+    x_ptr = _dev_ptr(x, "x", (torch.bfloat16, torch.float16))
+    L = load()
+    need = forward_workspace_bytes(w, M)
+    ws, wsn = _workspace(need, x.device)
+    _check(L.exl3_forward(ctypes.byref(w.view()), x_ptr, _BF16 if x.dtype == torch.bfloat16 else _F16, M, y_ptr,
+                          _BF16 if out_dtype == torch.bfloat16 else _F16, ws, wsn, _stream()))
+    return out
 
 
 def debug_codebook(codebook: int | str, device="cuda") -> torch.Tensor:

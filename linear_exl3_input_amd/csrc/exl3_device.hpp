@@ -169,6 +169,86 @@ __device__ __forceinline__ int frag_order_k(int k) {
   return (k & ~31) | (cs << 2) | (k & 3);
 }
 
+// ------------------------------------------- input rotation, one piece
+//
+// x~[m][:] = fp16_rne(2^-4 * H128(x[m][:] * suh[:])) per 128-block, on
+// sixteen lanes per (row, block): lane L holds the 8 values that one 16-byte
+// piece of the k-step tile layout stores, of 32-group j = L/4 and piece
+// q = L%4, k = 32j + 16(q/2) + 4(q%2) + {0,1,2,3, 8,9,10,11} (the fragment
+// order of frag_order_k).  The butterfly strides 1, 2 and 8 pair values
+// inside the lane; strides 4, 16, 32 and 64 pair lane L with L^1, L^2, L^4
+// and L^8 (within its 16-lane DPP row), whose values arrive by DPP lane
+// moves.  The stages run in the fixed order 1, 2, 4, ..., 64, each pair
+// (a, b) -> (a + b, a - b) one fp32 add each, so any caller gets the same
+// bits; x * suh is exact in fp32.
+
+// Lane value of lane^1, ^2, ^4, ^8 (within 16 lanes) by DPP: quad_perm
+// [1,0,3,2]; quad_perm [2,3,0,1]; half-row mirror (i -> 7-i) then quad_perm
+// [3,2,1,0] (7 - (i^3) = i^4 for i < 8); row rotate by 8.
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (X == 1) r = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false);
+  else if constexpr (X == 2) r = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false);
+  else if constexpr (X == 4)
+    r = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF,
+                                    false);
+  else r = __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, r);
+}
+
+// One cross-lane butterfly stage: the lane whose bit is clear keeps a + b
+// (its value a, the partner's b), the other keeps b' - a' with its partner
+// a' = the clear lane's value: the same two fp32 operations as in-lane.
+template <int X>
+__device__ __forceinline__ void xstage(float (&t)[8], bool upper) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = lane_xor<X>(t[e]);
+    t[e] = upper ? p - t[e] : t[e] + p;
+  }
+}
+
+// In-lane stage: pairs (e, e + d) for e with bit d clear.
+template <int D>
+__device__ __forceinline__ void lstage(float (&t)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if ((e & D) == 0) {
+      const float a = t[e], b = t[e + D];
+      t[e] = a + b;
+      t[e + D] = a - b;
+    }
+}
+
+// The lane's piece: xv its 8 x values (fp32; t[0..3] = k0 + 0..3, t[4..7] =
+// k0 + 8..11), sw the suh words at the same k (two fp16 each), L the lane
+// within its 16.  Returns the 8 rotated fp16 values as one 16-byte piece.
+__device__ __forceinline__ u32x4_t rotate_piece(const float (&xv)[8], const uint32_t (&sw)[4], int L) {
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[2 * i] = xv[2 * i] * f16_bits_to_f32(sw[i] & 0xFFFFu);
+    t[2 * i + 1] = xv[2 * i + 1] * f16_bits_to_f32(sw[i] >> 16);
+  }
+  lstage<1>(t);                // stride 1
+  lstage<2>(t);                // stride 2
+  xstage<1>(t, (L & 1) != 0);  // stride 4: piece q ^ 1
+  lstage<4>(t);                // stride 8: the lane's two runs
+  xstage<2>(t, (L & 2) != 0);  // stride 16: piece q ^ 2
+  xstage<4>(t, (L & 4) != 0);  // stride 32: group j ^ 1
+  xstage<8>(t, (L & 8) != 0);  // stride 64: group j ^ 2
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_f16_bits(t[2 * i] * 0.0625f) | (f32_to_f16_bits(t[2 * i + 1] * 0.0625f) << 16);
+  return o;
+}
+
+// First k of lane L's piece within its 128-block.
+__device__ __forceinline__ int rotate_piece_k0(int L) { return 32 * (L >> 2) + 16 * ((L & 3) >> 1) + 4 * (L & 1); }
+
 // ------------------------------------------------ wavefront Hadamard (fp32)
 //
 // Lane l holds elements 2l and 2l+1 of one 128-element block.  Stage s pairs

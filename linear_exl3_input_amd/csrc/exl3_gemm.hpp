@@ -551,7 +551,8 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
   constexpr int OPS = S::OPS;
   constexpr int SLOT_DW = S::SLOT_DW;
   constexpr int TSTRIDE = S::TSTRIDE;
-  constexpr int NSLOT = QD * S::area(2) * 4 <= 152 * 1024 ? 2 : 1;
+  constexpr int NSLOT = small_tile_slots(BITS, MT, QW, QD);
+  static_assert(NSLOT == (QD * S::area(2) * 4 <= 152 * 1024 ? 2 : 1), "slot rule");
   constexpr int QUAD_DW = S::area(NSLOT);
   constexpr int MAIN_DW = QD * QUAD_DW;
   constexpr int Z_DW = BM * Z_ROW;
@@ -615,6 +616,8 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
     row = row < rend ? row : rend - 1;
     a_src[r] = (uint32_t)(((c / (4 * BM)) * M + row) * 32 + (c & 3) * 8);
   }
+  // the rotated activations come from x_rot, or are rotated here (rot_in)
+  const bool rot_in = !MOE && p.x_in != nullptr;
   auto issue_stage = [&](int stage, int slot) __attribute__((always_inline)) {
     uint32_t *const ts = qlds + slot * SLOT_DW;
 #pragma unroll
@@ -624,6 +627,7 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(t_base + stage * t_stage + t_src[r]),
                                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
+    if (rot_in) return;
 #pragma unroll
     for (int r = 0; r < A_OPS; ++r)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a_base + stage * a_stage + a_src[r]),
@@ -647,10 +651,47 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
   // Every quad has the same number of stages (the host gives a several-quad
   // unit equal parts), so all waves meet the same barriers.
   issue_stage(0, 0);
-  if (NSLOT == 2 && nst > 1) {
-    issue_stage(1, 1);
-    wait_vmcnt<OPS>();  // stage 0 landed (stage 1's loads were issued after it)
+  if (!rot_in) {
+    if (NSLOT == 2 && nst > 1) {
+      issue_stage(1, 1);
+      wait_vmcnt<OPS>();  // stage 0 landed (stage 1's loads were issued after it)
+    } else {
+      wait_vmcnt<0>();
+    }
   } else {
+    // Rotation in the GEMM: every stage of the quad's K range has a slot
+    // (the host's condition), so the loop below issues no further stage.
+    // Each 16-lane group rotates one (stage, row) 128-block per pass, the
+    // lane's piece straight into the slot's x~ area in the k-step tile
+    // layout (rows past the launch's last row rotate that row, as the
+    // direct loads read it).
+    if (NSLOT == 2 && nst > 1) issue_stage(1, 1);
+    if constexpr (!MOE) {
+      const int L = lane & 15;
+      const int kin = rotate_piece_k0(L);
+      const uint16_t *const suh_s = p.suh_in + (int64_t)shard * K;
+      for (int it = wave * 4 + (lane >> 4); it < BM * nst; it += QW * 4) {
+        const int s = it / BM;
+        const int r = it - s * BM;
+        const int m = m0 + r < rend ? m0 + r : rend - 1;
+        const int k0 = (kb_begin + s) * 128 + kin;
+        const uint16_t *const xrow = p.x_in + (int64_t)m * K;
+        const u32x2_t lo = *(const u32x2_t *)(xrow + k0);
+        const u32x2_t hi = *(const u32x2_t *)(xrow + k0 + 8);
+        const uint32_t xw[4] = {lo.x, lo.y, hi.x, hi.y};
+        float xv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[2 * i] = p.x_in_bf16 ? bf16_bits_to_f32(xw[i] & 0xFFFFu) : f16_bits_to_f32(xw[i] & 0xFFFFu);
+          xv[2 * i + 1] = p.x_in_bf16 ? bf16_bits_to_f32(xw[i] >> 16) : f16_bits_to_f32(xw[i] >> 16);
+        }
+        const u32x2_t slo = *(const u32x2_t *)(suh_s + k0);
+        const u32x2_t shi = *(const u32x2_t *)(suh_s + k0 + 8);
+        const uint32_t sw[4] = {slo.x, slo.y, shi.x, shi.y};
+        *(u32x4_t *)(qlds + s * SLOT_DW + S::TSLOT_DW + ((L >> 2) * BM + r) * 16 + 4 * (L & 3)) =
+            rotate_piece(xv, sw, L);
+      }
+    }
     wait_vmcnt<0>();
   }
   barrier_lds();

@@ -415,7 +415,7 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
                        bool with_output, const int32_t *block_expert = nullptr, int64_t expert_trellis = 0,
-                       int32_t n_experts = 0);
+                       int32_t n_experts = 0, const void *x_in = nullptr, bool x_in_bf16 = false);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -669,9 +669,13 @@ namespace {
 // the plan has the finisher, else as a second kernel).
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
-                       bool with_output, const int32_t *block_expert, int64_t expert_trellis, int32_t n_experts) {
+                       bool with_output, const int32_t *block_expert, int64_t expert_trellis, int32_t n_experts,
+                       const void *x_in, bool x_in_bf16) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
+  p.x_in = static_cast<const uint16_t *>(x_in);
+  p.suh_in = w->suh;
+  p.x_in_bf16 = x_in_bf16 ? 1 : 0;
   p.block_expert = block_expert;
   p.n_experts = n_experts;
   p.expert_trellis = expert_trellis;
@@ -745,6 +749,88 @@ extern "C" {
 exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                         void *workspace, size_t workspace_bytes, void *stream) {
   return exl3_linear_ex(w, x_rot, M, y, y_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The whole layer in one call: the rotation runs inside the GEMM when the
+// plan's kernel is the small-tile kernel and every stage of a quad's K range
+// has a stage slot there (one launch, no x~ in memory); otherwise the input
+// transform writes x~ into the workspace, after the plan's own part.
+bool rotation_in_gemm(const exl3_weight *w, const Plan &pl) {
+  if (pl.decoder != EXL3_DECODER_ALU || pl.bm > 64) return false;
+  const int64_t kb = w->K / 128;
+  const int64_t parts_per_quad = pl.quads > 1 ? 1 : pl.unit;
+  const int64_t stages = (parts_per_quad * kb + pl.parts - 1) / pl.parts;  // the longest quad's
+  return stages <= exl3::small_tile_slots(w->bits, pl.bm / 16, pl.half ? 2 : 4, pl.quads);
+}
+
+// x_rot goes after everything the plan uses and never inside the arrival
+// counters, which stay zero between calls even where the plan needs none.
+size_t forward_x_rot_offset(const Plan &pl) {
+  return (std::max(pl.workspace, (size_t)EXL3_WORKSPACE_COUNTER_BYTES) + 255) & ~(size_t)255;
+}
+
+size_t forward_workspace(const exl3_weight *w, int32_t M, const Plan &pl) {
+  if (M == 0 || rotation_in_gemm(w, pl)) return pl.workspace;
+  return forward_x_rot_offset(pl) + (size_t)w->n_shards * (size_t)M * (size_t)w->K * 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t exl3_forward_workspace_bytes(const exl3_weight *w, int32_t M) {
+  clear_error();
+  if (validate_weight(w, false, false) != EXL3_OK) return 0;
+  if (M < 0 || M > MAX_M) {
+    fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 0..%d", M, MAX_M);
+    return 0;
+  }
+  Plan pl;
+  if (plan_for(w, M, nullptr, &pl) != EXL3_OK) return 0;
+  return forward_workspace(w, M, pl);
+}
+
+exl3_status exl3_forward(const exl3_weight *w, const void *x, int32_t x_dtype, int32_t M, void *y, int32_t y_dtype,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, true, true);
+  if (st != EXL3_OK) return st;
+  if (x_dtype != EXL3_F16 && x_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "x_dtype=%d, must be 0 (fp16) or 1 (bf16)", x_dtype);
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (M < 0) return fail(EXL3_ERR_INVALID_ARG, "M=%d is negative", M);
+  if (M > MAX_M) return fail(EXL3_ERR_UNSUPPORTED, "M=%d exceeds the supported %d", M, MAX_M);
+  Plan pl;
+  if ((st = plan_for(w, M, nullptr, &pl)) != EXL3_OK) return st;
+  if (M == 0) return EXL3_OK;
+  if ((st = check_ptr(x, "x")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  const size_t need = forward_workspace(w, M, pl);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(EXL3_ERR_WORKSPACE, "workspace of %zu bytes at %p; this call needs %zu (short by %zu)",
+                  workspace_bytes, workspace, need, need > workspace_bytes ? need - workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(EXL3_ERR_INVALID_ARG, "workspace=%p is not 16-byte aligned", workspace);
+  }
+  uint32_t *counters = static_cast<uint32_t *>(workspace);
+  float *slabs = pl.workspace > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.slab_off) : nullptr;
+  uint16_t *dense =
+      pl.decoder == EXL3_DECODER_DENSE ? reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + pl.dense_off)
+                                       : nullptr;
+  const hipStream_t s = (hipStream_t)stream;
+  if (rotation_in_gemm(w, pl))
+    return run_linear(w, nullptr, M, y, y_dtype, counters, slabs, dense, pl, s, true, nullptr, 0, 0, x,
+                      x_dtype == EXL3_BF16);
+  uint16_t *x_rot = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + forward_x_rot_offset(pl));
+  const hipError_t e = exl3::launch_input_transform(x, x_dtype == EXL3_BF16, false, M, w->K, w->suh, w->n_shards,
+                                                    x_rot, s);
+  if (e != hipSuccess) return launch_error(e, "input transform launch");
+  return run_linear(w, x_rot, M, y, y_dtype, counters, slabs, dense, pl, s, true);
 }
 
 size_t exl3_tune_workspace_bytes(const exl3_weight *w, int32_t M) {

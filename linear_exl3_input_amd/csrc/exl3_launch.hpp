@@ -37,7 +37,27 @@ struct GemmParams {
   int64_t expert_trellis;       // grouped calls: trellis words per expert
   int32_t n_experts;            // grouped calls: experts in the stack; a block's
                                 // expert outside 0..n_experts-1 is skipped like -1
+  // Rotation in the GEMM (small tiles only, exl3_forward): when x_in is set,
+  // x_rot is unused and each workgroup rotates its own rows and K range of
+  // x [M][K] (bf16 if x_in_bf16, else fp16) with suh_in [n_shards][K] into
+  // its stage slots; the host sets it only when every stage of a quad's K
+  // range fits the slots (small_tile_slots).
+  const uint16_t *x_in;
+  const uint16_t *suh_in;
+  int32_t x_in_bf16;
 };
+
+// Stage slots per quad of the small-tile kernel (gemm_kernel): two when QD
+// quads of two fit in 152 KB of LDS, else one.  Host and device use this one
+// definition (the host to decide whether a quad's stages all fit the slots).
+constexpr int small_tile_slots(int bits, int mt, int qw, int qd) {
+  const int bm = 16 * mt, qt = 64 * qw, nts = 2 * qw;
+  const int t_chunks = 8 * nts * (2 * bits + 2);
+  const int t_ops = (t_chunks + qt - 1) / qt;
+  const int junk = t_ops * qt - t_chunks;
+  const int slot_dw = t_chunks * 4 + bm * 64;
+  return qd * (2 * slot_dw + junk * 4) * 4 <= 152 * 1024 ? 2 : 1;
+}
 
 struct DecodeParams {
   const uint16_t *trellis;

@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(L, name), name
-    assert L.exl3_abi_version() == ex.ABI_VERSION == 5
+    assert L.exl3_abi_version() == ex.ABI_VERSION == 6
 
 
 def test_status_strings():
@@ -386,3 +386,23 @@ def test_wide_layers_keep_k_whole():
         for M in (1, 16, 128, 2048):
             assert (_plan(w, M).parts, _plan(w, M).groups) == (1, 1), (K, shards, M)
     assert _plan(view(5120, (32640,), 4, 2), 1).parts > 1  # 255 blocks
+
+
+def test_forward_workspace_keeps_the_counters():
+    """Where exl3_forward stages x_rot in the workspace, x_rot lies after the
+    plan's workspace and after the arrival counters, also for a plan that
+    needs no workspace of its own (one part over all of K): the counters stay
+    zero for the next call that shares the workspace."""
+    L = ex.load()
+    for K, shards, bits, cb, M in ((1024, (32768,), 4, 0, 16), (1024, (32768,), 4, 0, 300),
+                                   (4096, (2048,), 4, 1, 512), (2048, (640,), 3, 0, 64)):
+        w = view(K, shards, bits, cb)
+        need = L.exl3_forward_workspace_bytes(ctypes.byref(w), M)
+        p = _plan(w, M)
+        x_rot = len(shards) * M * K * 2
+        if need == p.workspace:  # the rotation runs in the GEMM
+            continue
+        assert need >= max(p.workspace, CB) + x_rot, (K, shards, M, need, p.workspace)
+    w = view(1024, (32768,), 4, 0)
+    assert _plan(w, 16).workspace == 0  # the case that needs the rule
+    assert L.exl3_forward_workspace_bytes(ctypes.byref(w), 16) == CB + 16 * 1024 * 2
