@@ -4,10 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path -- the input rotation and the
-trellis GEMM with its output transform -- over every (shape, M) of the
-workload, each on its own copy of the weights drawn from a pool larger than
-the GPU's caches (so every step reads its trellis from HBM, as a real model
-step does).  The default workload, ``all_configs``, is every configuration
+trellis GEMM with its output transform, one exl3_forward call each -- over
+every (shape, M) of the workload, each on its own copy of the weights drawn
+from a pool larger than the GPU's caches (so every step reads its trellis
+from HBM, as a real model step does).  The default workload, ``all_configs``, is every configuration
 of the metric in one step (57 calls): the 1024 x 1024 4-bit 3inst layer at
 1 and 16 rows; the 4-bit mcg expert pair (4096 x 2048, 2048 x 4096) at 1,
 16 and 512; the Qwen-27B-shaped 6-bit mul1 q_proj (5120 x 12288) and
@@ -210,7 +210,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--only", default=None, metavar="LAYER:M",
-                    help="counter runs: launch only this call class (transform + linear), --steps times")
+                    help="counter runs: launch only this call class (its forward call), --steps times")
     ap.add_argument("--tune", action="store_true",
                     help="time every schedule of each call's part tree on the weight pool first (same bits) and "
                          "run the fastest")
@@ -296,17 +296,19 @@ def main():
             ex.input_transform(x[:M], ws[0].suh, out=xr[M])
             tuned[f"{lay.name} M={M}"] = ex.tune(ws, xr[M], reps=max(3, min(20, len(ws))))
             log(f"tuned {lay.name} M={M}: {tuned[f'{lay.name} M={M}']}")
-    # workspace for the largest need, allocated before capture
-    need = max(ex.workspace_bytes(per_layer[li][1][0], M) for li, M in calls)
+    # workspace for the largest need (forward's, which holds x_rot where the
+    # rotation does not run in the GEMM), allocated before capture
+    need = max(max(ex.workspace_bytes(per_layer[li][1][0], M), ex.forward_workspace_bytes(per_layer[li][1][0], M))
+               for li, M in calls)
     stream = torch.cuda.Stream()
     if need:
         ex.reserve_workspace(need, dev, stream)
 
     def call(li, M, copy):
+        # the whole layer in one call: the rotation inside the small-tile
+        # GEMM where it fits, else the transform into the workspace first
         lay, ws, x, xr, y = per_layer[li]
-        w = ws[copy % len(ws)]
-        ex.input_transform(x[:M], w.suh, out=xr[M])
-        ex.linear(w, xr[M], torch.bfloat16, out=y[M])
+        ex.forward(ws[copy % len(ws)], x[:M], torch.bfloat16, out=y[M])
 
     def step(g):
         # graph g: call j of a layer takes copy g * (calls of the layer) + j
@@ -386,6 +388,7 @@ def main():
                                             args.timing_reps)
             # warm: the same weight copy every call (L2/MALL-resident when it fits)
             t_warm = time_calls(lambda r: ex.linear(ws[0], xr[M], torch.bfloat16, out=y[M]), args.timing_reps)
+            t_fw = time_calls(lambda r: ex.forward(pick(r), x[:M], torch.bfloat16, out=y[M]), args.timing_reps)
             pl = ex.plan(ws[0], M)
             byts = lay.weight_bytes()
             flops = 2.0 * M * lay.K * lay.N
@@ -394,14 +397,16 @@ def main():
                 "layer": lay.name, "M": M, "K": lay.K, "N": lay.N, "bits": lay.bits, "codebook": lay.codebook,
                 "plan": pl, "transform_us": round(t_in, 3), "linear_us": round(t_lin, 3),
                 "linear_us_min": round(t_lin_min, 3), "linear_us_warm": round(t_warm, 3),
+                "forward_us": round(t_fw, 3), "rotation_in_gemm": ex.forward_workspace_bytes(ws[0], M) == pl["workspace"],
                 "kernels_per_linear": pl["launches"],
                 "GBps": round(byts / (t_lin * 1e-6) / 1e9, 1),
                 "TFLOPS": round(flops / (t_lin * 1e-6) / 1e12, 2),
                 "pct_sol": round(100.0 * sol / (t_lin * 1e-6), 2),
                 "pct_sol_with_transform": round(100.0 * sol / ((t_lin + t_in) * 1e-6), 2),
+                "pct_sol_forward": round(100.0 * sol / (t_fw * 1e-6), 2),
                 "bound": "mfma" if flops / MFMA_F16_FLOPS > byts / HBM_BPS else "hbm",
             })
-            log(f"{lay.name} M={M}: plan {pl}, transform {t_in:.2f} us, linear {t_lin:.2f} us "
+            log(f"{lay.name} M={M}: plan {pl}, transform {t_in:.2f} us, linear {t_lin:.2f} us, forward {t_fw:.2f} us "
                 f"({per_shape[-1]['GBps']} GB/s, {per_shape[-1]['TFLOPS']} TFLOP/s, "
                 f"{per_shape[-1]['pct_sol']}% SoL)")
 

@@ -273,12 +273,15 @@ size_t exl3_workspace_bytes_ex(const exl3_weight *w, int32_t M, const exl3_plan 
  * ("Two further departures") keeps the transform a separate kernel, where
  * upstream fuses it into the GEMM behind a grid-wide sync; this entry point
  * keeps both calls available and adds a third way for the plans whose GEMM
- * is the small-tile kernel (16-64 row tiles) and whose workgroups' K ranges
- * fit their LDS stage slots: every workgroup rotates its own rows and K
- * range of x straight into LDS (the same fp32 arithmetic, rounded once to
- * fp16), so the call is one launch with no x_rot in memory and no
- * workgroup waits for another.  Other plans run the transform into the
- * workspace, then the GEMM (two launches, as the separate calls would).
+ * is the small-tile kernel (16-64 row tiles), whose workgroups' K ranges
+ * fit their LDS stage slots, and whose tile rows times stages per quad is
+ * at most 16: every workgroup rotates its own rows and K range of x
+ * straight into LDS (the same fp32 arithmetic, rounded once to fp16), so
+ * the call is one launch with no x_rot in memory and no workgroup waits
+ * for another.  Since every workgroup of a row tile repeats that work, the
+ * last bound keeps it shorter than the launch it saves.  Other plans run
+ * the transform into the workspace, then the GEMM (two launches, as the
+ * separate calls would).
  *   workspace at least exl3_forward_workspace_bytes(w, M) bytes: the plan's
  *             own workspace (arrival counters first, zero on entry as for
  *             exl3_linear), plus room for x_rot when the rotation does not

@@ -663,33 +663,65 @@ __global__ __launch_bounds__(64 * QW * QD) void gemm_kernel(const GemmParams p) 
     // (the host's condition), so the loop below issues no further stage.
     // Each 16-lane group rotates one (stage, row) 128-block per pass, the
     // lane's piece straight into the slot's x~ area in the k-step tile
-    // layout (rows past the launch's last row rotate that row, as the
-    // direct loads read it).
+    // layout.  Only the tile's rows below the launch's last row are
+    // rotated: a matrix-core product row depends on its own A row alone, so
+    // whatever the other rows' x~ holds reaches only output rows that are
+    // never stored.  The x loads of up to 8 passes are all issued before
+    // the first rotation, so the passes share one load latency.
     if (NSLOT == 2 && nst > 1) issue_stage(1, 1);
     if constexpr (!MOE) {
+      constexpr int RG = QW * 4;  // 16-lane groups in a quad
+      constexpr int RB = (BM * NSLOT + RG - 1) / RG < 8 ? (BM * NSLOT + RG - 1) / RG : 8;
       const int L = lane & 15;
       const int kin = rotate_piece_k0(L);
-      const uint16_t *const suh_s = p.suh_in + (int64_t)shard * K;
-      for (int it = wave * 4 + (lane >> 4); it < BM * nst; it += QW * 4) {
-        const int s = it / BM;
-        const int r = it - s * BM;
-        const int m = m0 + r < rend ? m0 + r : rend - 1;
-        const int k0 = (kb_begin + s) * 128 + kin;
-        const uint16_t *const xrow = p.x_in + (int64_t)m * K;
-        const u32x2_t lo = *(const u32x2_t *)(xrow + k0);
-        const u32x2_t hi = *(const u32x2_t *)(xrow + k0 + 8);
-        const uint32_t xw[4] = {lo.x, lo.y, hi.x, hi.y};
-        float xv[8];
+      const int g0 = wave * 4 + (lane >> 4);
+      const uint16_t *const suh_s = p.suh_in + (int64_t)shard * K + kb_begin * 128 + kin;
+      uint32_t sw[NSLOT][4];  // the lane's suh words of each stage
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xv[2 * i] = p.x_in_bf16 ? bf16_bits_to_f32(xw[i] & 0xFFFFu) : f16_bits_to_f32(xw[i] & 0xFFFFu);
-          xv[2 * i + 1] = p.x_in_bf16 ? bf16_bits_to_f32(xw[i] >> 16) : f16_bits_to_f32(xw[i] >> 16);
+      for (int st = 0; st < NSLOT; ++st) {
+        if (st < nst) {
+          const u32x2_t lo = *(const u32x2_t *)(suh_s + st * 128);
+          const u32x2_t hi = *(const u32x2_t *)(suh_s + st * 128 + 8);
+          sw[st][0] = lo.x, sw[st][1] = lo.y, sw[st][2] = hi.x, sw[st][3] = hi.y;
+        } else {
+          sw[st][0] = sw[st][1] = sw[st][2] = sw[st][3] = 0u;
         }
-        const u32x2_t slo = *(const u32x2_t *)(suh_s + k0);
-        const u32x2_t shi = *(const u32x2_t *)(suh_s + k0 + 8);
-        const uint32_t sw[4] = {slo.x, slo.y, shi.x, shi.y};
-        *(u32x4_t *)(qlds + s * SLOT_DW + S::TSLOT_DW + ((L >> 2) * BM + r) * 16 + 4 * (L & 3)) =
-            rotate_piece(xv, sw, L);
+      }
+      const int rows = rend - m0 < BM ? rend - m0 : BM;  // >= 1
+      const int work = rows * nst;
+      for (int b0 = 0; b0 < work; b0 += RB * RG) {
+        u32x2_t xlo[RB], xhi[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int it = b0 + g0 + i * RG;
+          if (it < work) {
+            const int st = it / rows;
+            const int r = it - st * rows;
+            const uint16_t *const src = p.x_in + (int64_t)(m0 + r) * K + (kb_begin + st) * 128 + kin;
+            xlo[i] = *(const u32x2_t *)src;
+            xhi[i] = *(const u32x2_t *)(src + 8);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int it = b0 + g0 + i * RG;
+          if (it < work) {
+            const int st = it / rows;
+            const int r = it - st * rows;
+            const uint32_t xw[4] = {xlo[i].x, xlo[i].y, xhi[i].x, xhi[i].y};
+            float xv[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              xv[2 * j] = p.x_in_bf16 ? bf16_bits_to_f32(xw[j] & 0xFFFFu) : f16_bits_to_f32(xw[j] & 0xFFFFu);
+              xv[2 * j + 1] = p.x_in_bf16 ? bf16_bits_to_f32(xw[j] >> 16) : f16_bits_to_f32(xw[j] >> 16);
+            }
+            uint32_t sws[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sws[j] = NSLOT == 2 && st != 0 ? sw[NSLOT - 1][j] : sw[0][j];
+            *(u32x4_t *)(qlds + st * SLOT_DW + S::TSLOT_DW + ((L >> 2) * BM + r) * 16 + 4 * (L & 3)) =
+                rotate_piece(xv, sws, L);
+          }
+        }
       }
     }
     wait_vmcnt<0>();

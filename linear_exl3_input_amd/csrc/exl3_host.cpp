@@ -756,15 +756,23 @@ exl3_status exl3_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, 
 namespace {
 
 // The whole layer in one call: the rotation runs inside the GEMM when the
-// plan's kernel is the small-tile kernel and every stage of a quad's K range
-// has a stage slot there (one launch, no x~ in memory); otherwise the input
-// transform writes x~ into the workspace, after the plan's own part.
-bool rotation_in_gemm(const exl3_weight *w, const Plan &pl) {
+// plan's kernel is the small-tile kernel, every stage of a quad's K range
+// has a stage slot there (one launch, no x~ in memory), and a workgroup's
+// share of the rotation is short; otherwise the input transform writes x~
+// into the workspace, after the plan's own part.  Every workgroup of a row
+// tile rotates that tile's rows over its quads' K ranges again, ahead of
+// its first product: at most 16 (row, stage) 128-blocks per quad, i.e. one
+// pass of the 16-lane groups of a four-wave quad or two of a two-wave one,
+// save more than the separate launch costs (measured at 1 to 64 rows on
+// 1024- to 4096-wide layers: about 1.4 us saved at one pass per wave, 0.5
+// us at two, break-even at three, a loss from four).
+bool rotation_in_gemm(const exl3_weight *w, const Plan &pl, int32_t M) {
   if (pl.decoder != EXL3_DECODER_ALU || pl.bm > 64) return false;
   const int64_t kb = w->K / 128;
   const int64_t parts_per_quad = pl.quads > 1 ? 1 : pl.unit;
   const int64_t stages = (parts_per_quad * kb + pl.parts - 1) / pl.parts;  // the longest quad's
-  return stages <= exl3::small_tile_slots(w->bits, pl.bm / 16, pl.half ? 2 : 4, pl.quads);
+  if (stages > exl3::small_tile_slots(w->bits, pl.bm / 16, pl.half ? 2 : 4, pl.quads)) return false;
+  return std::min<int64_t>(pl.bm, M) * stages <= 16;
 }
 
 // x_rot goes after everything the plan uses and never inside the arrival
@@ -774,7 +782,7 @@ size_t forward_x_rot_offset(const Plan &pl) {
 }
 
 size_t forward_workspace(const exl3_weight *w, int32_t M, const Plan &pl) {
-  if (M == 0 || rotation_in_gemm(w, pl)) return pl.workspace;
+  if (M == 0 || rotation_in_gemm(w, pl, M)) return pl.workspace;
   return forward_x_rot_offset(pl) + (size_t)w->n_shards * (size_t)M * (size_t)w->K * 2;
 }
 
@@ -823,7 +831,7 @@ exl3_status exl3_forward(const exl3_weight *w, const void *x, int32_t x_dtype, i
       pl.decoder == EXL3_DECODER_DENSE ? reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + pl.dense_off)
                                        : nullptr;
   const hipStream_t s = (hipStream_t)stream;
-  if (rotation_in_gemm(w, pl))
+  if (rotation_in_gemm(w, pl, M))
     return run_linear(w, nullptr, M, y, y_dtype, counters, slabs, dense, pl, s, true, nullptr, 0, 0, x,
                       x_dtype == EXL3_BF16);
   uint16_t *x_rot = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + forward_x_rot_offset(pl));

@@ -406,3 +406,15 @@ def test_forward_workspace_keeps_the_counters():
     w = view(1024, (32768,), 4, 0)
     assert _plan(w, 16).workspace == 0  # the case that needs the rule
     assert L.exl3_forward_workspace_bytes(ctypes.byref(w), 16) == CB + 16 * 1024 * 2
+
+
+def test_forward_rotates_in_the_gemm_only_when_short():
+    """exl3_forward rotates inside the small-tile GEMM while a tile's rows
+    times the stages of a quad stay within 16, else stages x_rot."""
+    L = ex.load()
+    sweep = view(4096, (4096,), 4, 1)  # two stages a quad on 16-row tiles
+    expert = view(4096, (2048,), 4, 1)  # one stage a quad
+    for w, M, fused in ((sweep, 1, True), (sweep, 8, True), (sweep, 9, False), (sweep, 64, False),
+                        (expert, 16, True), (expert, 17, False)):
+        need = L.exl3_forward_workspace_bytes(ctypes.byref(w), M)
+        assert (need == _plan(w, M).workspace) == fused, (M, need, _plan(w, M).workspace)
