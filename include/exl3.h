@@ -368,6 +368,22 @@ exl3_status exl3_debug_decode(const exl3_weight *w, uint16_t *wq, void *stream);
  * short. */
 exl3_status exl3_debug_dequant(const exl3_weight *w, uint16_t *frags, size_t frag_bytes, void *stream);
 
+/* The dense decoder's second stage alone, over fragments that
+ * exl3_debug_dequant wrote (device, frag_bytes >= K*N*2), for timing its
+ * two launches apart.  The dense GEMM runs 256 x 256 workgroup tiles over
+ * whole rounds of the GPU's CUs and the column blocks after them as
+ * 256 x 128 tiles, twice as many workgroups of half the work (columns only
+ * split, so the bits are the same; see the plan's `launches`).  which: 1
+ * the 256 x 256 launch, 2 the 256 x 128 launch, 3 both (y then equals
+ * exl3_linear's with the dense decoder).  *bulk_blocks (HOST, may be NULL)
+ * receives the column blocks of the 256 x 256 launch (N/128 when nothing
+ * is split).  The plan is exl3_linear's with the dense decoder forced; it
+ * must be one part per workgroup, fused, in one row chunk, else
+ * EXL3_ERR_UNSUPPORTED.  Needs no workspace. */
+exl3_status exl3_debug_dense_gemm(const exl3_weight *w, const uint16_t *frags, size_t frag_bytes,
+                                  const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype, int32_t which,
+                                  int32_t *bulk_blocks, void *stream);
+
 /* The trellis GEMM stage alone, the kernel slab mode runs before the
  * output stage: the fp32 sum of every K part (unit 1, the default), or of
  * every group (force->unit = P/G, the automatic slab plan's own stage),

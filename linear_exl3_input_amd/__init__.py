@@ -113,6 +113,7 @@ def load() -> ctypes.CDLL:
             "exl3_debug_mfma_loop": (i32, [i32, ctypes.c_uint16, vp, vp]),
             "exl3_debug_decode_rate": (i32, [W, vp, vp]),
             "exl3_debug_dequant": (i32, [W, vp, sz, vp]),
+            "exl3_debug_dense_gemm": (i32, [W, vp, sz, vp, i32, vp, i32, i32, ctypes.POINTER(i32), vp]),
             "exl3_tune": (i32, [W, i32, vp, i32, vp, i32, vp, sz, i32, vp, P]),
             "exl3_tune_workspace_bytes": (sz, [W, i32]),
             "exl3_tune_set": (i32, [W, i32, P]),
@@ -431,6 +432,25 @@ def debug_dequant(w: Exl3Weight, out: Optional[torch.Tensor] = None) -> torch.Te
     _check(load().exl3_debug_dequant(ctypes.byref(w.view()), _dev_ptr(out, "frags", _U16), out.numel() * 2,
                                      _stream()))
     return out
+
+
+def debug_dense_gemm(w: Exl3Weight, frags: torch.Tensor, x_rot: torch.Tensor, which: int = 3,
+                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """The dense GEMM stage alone over debug_dequant's fragments: which = 1
+    the 256 x 256 launch, 2 the 256 x 128 launch over the column blocks after
+    it, 3 both.  Returns (y [M, N], column blocks of the 256 x 256 launch)."""
+    if x_rot.dim() != 4 or x_rot.shape[3] != 32:
+        raise ValueError(f"x_rot shape {tuple(x_rot.shape)} is not [S, K/32, M, 32]")
+    M = x_rot.shape[2]
+    if out is None:
+        out = torch.empty((M, w.N), dtype=out_dtype, device=x_rot.device)
+    y_ptr = _out_ptr(out, "out", (M, w.N), (out_dtype,))
+    bulk = ctypes.c_int32(0)
+    _check(load().exl3_debug_dense_gemm(ctypes.byref(w.view()), _dev_ptr(frags, "frags", (torch.int16,)),
+                                        frags.numel() * 2, _dev_ptr(x_rot, "x_rot", _H16), M, y_ptr,
+                                        _BF16 if out_dtype == torch.bfloat16 else _F16, which, ctypes.byref(bulk),
+                                        _stream()))
+    return out, bulk.value
 
 
 def debug_parts(w: Exl3Weight, x_rot: torch.Tensor, parts=None, bm=None, decoder=None,

@@ -58,8 +58,10 @@ __device__ __forceinline__ void dense_tile(int L, int total, int mtiles, int &nb
   mt = 8 * g + rem % gs;
 }
 
+// nb0: the first column block of the launch (a launch that covers the
+// blocks after a 256 x 256 launch's, see launch_gemm_dense).
 template <bool MULTI>
-__global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmParams p) {
+__global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmParams p, int nb0) {
   constexpr int PF = DN_PF;
   constexpr int MAIN_DW = PF * DN_SLOT_DW;
   constexpr int Z_DW = 64 * Z_ROW;
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(DN_THREADS, 1) void gemm_dense_kernel(const GemmPar
   const int g = lane >> 4;
   int nb, mt;
   dense_tile(blockIdx.x, gridDim.x, (p.row_end - p.row_base + DN_BM - 1) / DN_BM, nb, mt);
+  nb += nb0;
   const int m0 = p.row_base + mt * DN_BM;
   const int rend = p.row_end;
   const int M = p.M, K = p.K, N = p.N;
@@ -450,16 +453,44 @@ int wide_col_tiles(const GemmParams &p) {
   return tiles;
 }
 
-hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, hipStream_t s) {
-  // grid: (column blocks x row tiles, units); the wide kernel takes units of
-  // one part (its column tiles pair the blocks of each shard)
+// The first column block of 256 x 256 column tile t (wide_col_tile's order).
+static int wide_tile_first_block(const GemmParams &p, int t) {
+  int start = 0;
+  for (int s = 0; s < p.n_shards; ++s) {
+    const int end = p.shard_end_blk[s];
+    const int tiles = (end - start + 1) >> 1;
+    if (t < tiles) return start + 2 * t;
+    t -= tiles;
+    start = end;
+  }
+  return start;
+}
+
+hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, int bulk_tiles, int which, hipStream_t s) {
+  // grid: (column blocks x row tiles, units).  Several parts a unit: the
+  // 256 x 128 kernel.  Else the 256 x 256 kernel on column tiles
+  // 0 .. bulk_tiles-1 (which & 1), and the 256 x 128 kernel on the column
+  // blocks after them (which & 2): the host sizes the first launch to whole
+  // rounds of workgroups over the CUs and gives the rest of the columns to
+  // the narrower tiles, twice as many workgroups of half the work each.
+  // Columns only split: every output element keeps the same products in
+  // the same order, so the bits do not depend on the split.
   if (multi) {
-    hipLaunchKernelGGL((gemm_dense_kernel<true>), grid, dim3(DN_THREADS), 0, s, p);
-  } else {
-    const int ct = wide_col_tiles(p);
-    const int mtiles = (int)grid.x / (p.N / 128);
-    const dim3 g2((unsigned)(ct * mtiles), grid.y, 1);
-    hipLaunchKernelGGL(gemm_dense_wide_kernel, g2, dim3(DW_THREADS), 0, s, p, ct);
+    if (which & 1) hipLaunchKernelGGL((gemm_dense_kernel<true>), grid, dim3(DN_THREADS), 0, s, p, 0);
+    return hipGetLastError();
+  }
+  const int ct = wide_col_tiles(p);
+  const int nblk = p.N / 128;
+  const int mtiles = (int)grid.x / nblk;
+  const int bt = bulk_tiles < 0 || bulk_tiles > ct ? ct : bulk_tiles;
+  if ((which & 1) && bt > 0) {
+    const dim3 g2((unsigned)(bt * mtiles), grid.y, 1);
+    hipLaunchKernelGGL(gemm_dense_wide_kernel, g2, dim3(DW_THREADS), 0, s, p, bt);
+  }
+  if ((which & 2) && bt < ct) {
+    const int nb0 = wide_tile_first_block(p, bt);
+    const dim3 g3((unsigned)((nblk - nb0) * mtiles), grid.y, 1);
+    hipLaunchKernelGGL((gemm_dense_kernel<false>), g3, dim3(DN_THREADS), 0, s, p, nb0);
   }
   return hipGetLastError();
 }

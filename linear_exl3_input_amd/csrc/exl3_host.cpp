@@ -240,6 +240,49 @@ size_t slab_bytes(int32_t n_slabs, int32_t rows, int32_t N) {
   return (size_t)n_slabs * (size_t)((rows + 3) / 4) * 4 * (size_t)N * sizeof(float);
 }
 
+// Column tiles of the dense decoder's 256 x 256 kernel: each shard's
+// column blocks in pairs (an odd shard ends in a one-block tile).
+int32_t dense_col_tiles(const exl3_weight *w) {
+  int32_t t = 0;
+  for (int s = 0; s < w->n_shards; ++s) t += (w->shard_n[s] / 128 + 1) / 2;
+  return t;
+}
+
+// The first column block of 256 x 256 column tile t.
+int32_t dense_tile_first_block(const exl3_weight *w, int32_t t) {
+  int32_t start = 0;
+  for (int s = 0; s < w->n_shards; ++s) {
+    const int32_t blocks = w->shard_n[s] / 128;
+    const int32_t tiles = (blocks + 1) / 2;
+    if (t < tiles) return start + 2 * t;
+    t -= tiles;
+    start += blocks;
+  }
+  return start;
+}
+
+// Column tiles of the dense GEMM's 256 x 256 launch over `rows` rows and
+// `units` units; the column blocks after them run as 256 x 128 tiles in a
+// second launch.  One workgroup of 256 x 256 tiles fills a CU and they all
+// take about as long, so the kernel runs in rounds of `cus` workgroups, and
+// a last round of few workgroups leaves most CUs idle for most of a round
+// (gate_up 5120 x 2 x 17408: 816 tiles at 1536 rows and 952 at 1792 took
+// 551 and 581 us, 1088 at 2048 rows 711 us).  When the last round's tiles,
+// as twice as many 256 x 128 tiles of half the work, fit one round, they run
+// that way after whole rounds of the wide tiles.  Measured on gate_up: 727
+// -> 704 us at 2048 rows, 1376 -> 1370 us at 4096; less than the rounds
+// suggest, since a partial round runs faster than a full one (its few
+// workgroups share the clock and the memory with no others).
+int32_t dense_bulk_tiles(const exl3_weight *w, int32_t rows, int32_t units, int cus) {
+  const int64_t ct = dense_col_tiles(w);
+  const int64_t per_tile = (int64_t)((rows + 255) / 256) * units;  // workgroups per column tile
+  const int64_t r = ct * per_tile % cus;
+  if (r == 0) return (int32_t)ct;
+  const int64_t c = (r + per_tile - 1) / per_tile;  // column tiles of the last round
+  if (c >= ct || 2 * c * per_tile > cus) return (int32_t)ct;
+  return (int32_t)(ct - c);
+}
+
 // slab_cap: the partial slabs a plan may keep at once (row chunks beyond it).
 exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, Plan *out,
                       double slab_cap = SLAB_CAP_BYTES) {
@@ -399,7 +442,15 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
   }
   pl.launches = pl.mode == EXL3_MODE_SLABS && !pl.finisher ? 2 : 1;
   if (pl.chunk < M && M > 0) pl.launches *= (M + pl.chunk - 1) / pl.chunk;
-  if (pl.decoder == EXL3_DECODER_DENSE) pl.launches += 1;  // the dequantization
+  if (pl.decoder == EXL3_DECODER_DENSE) {
+    pl.launches += 1;  // the dequantization
+    if (!pl.multi && M > 0) {  // a 256 x 128 launch after the 256 x 256 one (dense_bulk_tiles)
+      const int cus = device_cus_or_default();
+      const int32_t units = pl.mode == EXL3_MODE_SLABS ? pl.parts / pl.unit : 1;
+      for (int32_t r0 = 0; r0 < M; r0 += pl.chunk)
+        if (dense_bulk_tiles(w, std::min(M, r0 + pl.chunk) - r0, units, cus) < dense_col_tiles(w)) pl.launches += 1;
+    }
+  }
   // counters, then slabs [n_slabs][ceil(chunk/4)][N][4] fp32, then (dense)
   // W_q as B fragments, K*N fp16
   pl.slab_off = EXL3_WORKSPACE_COUNTER_BYTES;
@@ -415,7 +466,8 @@ exl3_status make_plan(const exl3_weight *w, int32_t M, const exl3_plan *force, P
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
                        bool with_output, const int32_t *block_expert = nullptr, int64_t expert_trellis = 0,
-                       int32_t n_experts = 0, const void *x_in = nullptr, bool x_in_bf16 = false);
+                       int32_t n_experts = 0, const void *x_in = nullptr, bool x_in_bf16 = false,
+                       int dense_which = 3);
 
 exl3_status launch_error(hipError_t e, const char *what) {
   return fail(EXL3_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -670,7 +722,7 @@ namespace {
 exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype,
                        uint32_t *counters, float *slabs, uint16_t *dense, const Plan &pl, hipStream_t s,
                        bool with_output, const int32_t *block_expert, int64_t expert_trellis, int32_t n_experts,
-                       const void *x_in, bool x_in_bf16) {
+                       const void *x_in, bool x_in_bf16, int dense_which) {
   exl3::GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.x_in = static_cast<const uint16_t *>(x_in);
@@ -702,23 +754,29 @@ exl3_status run_linear(const exl3_weight *w, const uint16_t *x_rot, int32_t M, v
   }
   const int32_t n_units = p.slab_mode ? pl.parts / pl.unit : 1;
   hipError_t e;
-  if (pl.decoder == EXL3_DECODER_DENSE) {
+  // dense_which: 3 dequantizes into `dense`, then runs both GEMM launches;
+  // 1 or 2 (the dense GEMM hook) runs only that launch over `dense` as given
+  if (pl.decoder == EXL3_DECODER_DENSE && dense_which == 3) {
     exl3::DecodeParams dp;
     dp.trellis = w->trellis;
     dp.wq = dense;
     dp.K = w->K;
     dp.N = w->N;
     if ((e = exl3::launch_dequant(w->bits, w->codebook, dp, s)) != hipSuccess) return launch_error(e, "dequant launch");
-    p.dense = dense;
   }
+  p.dense = dense;
   for (int32_t r0 = 0; r0 < M; r0 += pl.chunk) {
     p.row_base = r0;
     p.row_end = std::min(M, r0 + pl.chunk);
     if (pl.decoder == EXL3_DECODER_DENSE) {
       // one dimension of tiles (column blocks x 256-row tiles), ordered
       // inside the kernel; units on y
-      const dim3 grid((unsigned)(w->N / 128 * ((p.row_end - p.row_base + 255) / 256)), (unsigned)n_units, 1);
-      e = exl3::launch_gemm_dense(pl.multi, p, grid, s);
+      const int32_t rows = p.row_end - p.row_base;
+      const dim3 grid((unsigned)(w->N / 128 * ((rows + 255) / 256)), (unsigned)n_units, 1);
+      int cus = 0;
+      if ((e = device_cus(&cus)) != hipSuccess) return launch_error(e, "device query");
+      const int bulk = pl.multi ? -1 : dense_bulk_tiles(w, rows, n_units, cus);
+      e = exl3::launch_gemm_dense(pl.multi, p, grid, bulk, dense_which, s);
       if (e != hipSuccess) return launch_error(e, "dense GEMM launch");
     } else if (pl.decoder == EXL3_DECODER_TABLE) {
       int cus = 0;
@@ -1289,6 +1347,46 @@ exl3_status exl3_debug_dequant(const exl3_weight *w, uint16_t *frags, size_t fra
   p.N = w->N;
   const hipError_t e = exl3::launch_dequant(w->bits, w->codebook, p, (hipStream_t)stream);
   return e == hipSuccess ? EXL3_OK : launch_error(e, "dequant launch");
+}
+
+exl3_status exl3_debug_dense_gemm(const exl3_weight *w, const uint16_t *frags, size_t frag_bytes,
+                                  const uint16_t *x_rot, int32_t M, void *y, int32_t y_dtype, int32_t which,
+                                  int32_t *bulk_blocks, void *stream) {
+  clear_error();
+  exl3_status st = validate_weight(w, false, false);
+  if (st != EXL3_OK) return st;
+  if (which < 1 || which > 3) return fail(EXL3_ERR_INVALID_ARG, "which=%d, must be 1, 2 or 3", which);
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_BF16)
+    return fail(EXL3_ERR_INVALID_ARG, "y_dtype=%d, must be 0 (fp16) or 1 (bf16)", y_dtype);
+  if (M < 1 || M > MAX_M) return fail(EXL3_ERR_INVALID_ARG, "M=%d out of range 1..%d", M, MAX_M);
+  exl3_plan f;
+  f.parts = -1;
+  f.groups = -1;
+  f.mode = EXL3_MODE_AUTO;
+  f.bm = -1;
+  f.decoder = EXL3_DECODER_DENSE;
+  f.unit = -1;
+  f.launches = 0;
+  f.wg_cols = -1;
+  f.workspace = 0;
+  Plan pl;
+  if ((st = make_plan(w, M, &f, &pl)) != EXL3_OK) return st;
+  if (pl.mode != EXL3_MODE_FUSED || pl.multi || pl.chunk < M)
+    return fail(EXL3_ERR_UNSUPPORTED, "the dense GEMM hook runs one-part fused plans in one row chunk (mode=%d "
+                "unit=%d chunk=%d)", pl.mode, pl.unit, pl.chunk);
+  if ((st = check_ptr(frags, "frags")) != EXL3_OK) return st;
+  if ((st = check_ptr(x_rot, "x_rot")) != EXL3_OK) return st;
+  if ((st = check_ptr(y, "y")) != EXL3_OK) return st;
+  const size_t need = (size_t)w->K * (size_t)w->N * 2;
+  if (frag_bytes < need)
+    return fail(EXL3_ERR_WORKSPACE, "frags holds %zu bytes; K*N fp16 need %zu (short by %zu)", frag_bytes, need,
+                need - frag_bytes);
+  int cus = 0;
+  const hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return launch_error(e, "device query");
+  if (bulk_blocks) *bulk_blocks = dense_tile_first_block(w, dense_bulk_tiles(w, M, 1, cus));
+  return run_linear(w, x_rot, M, y, y_dtype, nullptr, nullptr, const_cast<uint16_t *>(frags), pl,
+                    (hipStream_t)stream, true, nullptr, 0, 0, nullptr, false, which);
 }
 
 exl3_status exl3_debug_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {

@@ -76,7 +76,9 @@ hipError_t launch_debug_decode(int bits, int cb, const DecodeParams &p, hipStrea
 // dequant_kernel), and the dense GEMM over them (same arithmetic as the tile
 // kernels: p.trellis unused, p.dense the fragments), 256-row tiles.
 hipError_t launch_dequant(int bits, int cb, const DecodeParams &p, hipStream_t s);
-hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, hipStream_t s);
+// bulk_tiles: 256 x 256 column tiles of the first launch (-1: all); which:
+// 1 that launch, 2 the 256 x 128 launch over the remaining blocks, 3 both.
+hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, int bulk_tiles, int which, hipStream_t s);
 // Table-decode GEMM (M <= 16): `grid` persistent workgroups of 1024 threads,
 // one per CU; fused (parts folded in order) or slab mode as in p.
 hipError_t launch_gemm_table(int bits, int cb, const GemmParams &p, int grid, hipStream_t s);

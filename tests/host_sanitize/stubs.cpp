@@ -34,8 +34,9 @@ hipError_t launch_dequant(int, int, const DecodeParams &p, hipStream_t) {
   check_grid("dequant", dim3(p.N / 128, p.K / 128));
   return hipSuccess;
 }
-hipError_t launch_gemm_dense(bool, const GemmParams &p, dim3 grid, hipStream_t) {
+hipError_t launch_gemm_dense(bool multi, const GemmParams &p, dim3 grid, int bulk_tiles, int which, hipStream_t) {
   if (p.row_end <= p.row_base || p.row_end > p.M) std::abort();
+  if (which < 1 || which > 3 || (!multi && bulk_tiles < 0)) std::abort();
   check_grid("dense", grid);
   return hipSuccess;
 }

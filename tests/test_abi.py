@@ -166,6 +166,7 @@ def test_plan_modes_and_workspace():
     assert small.mode == ex.EXL3_MODE_SLABS and small.workspace == CB + small.parts * 16 * 5120 * 4
     # 4096 rows of a 89M-weight layer: dequantize once into K*N fp16, dense GEMM
     assert big.mode == ex.EXL3_MODE_FUSED and big.decoder == ex.EXL3_DECODER_DENSE
+    # dequantization, then 17 parts folded in registers by the 256 x 128 kernel
     assert big.workspace == CB + 17408 * 5120 * 2 and big.launches == 2
     assert small.bm == 16 and _plan(w, 24).bm == 32 and big.bm == 256
     assert _plan(w, 2047).decoder == ex.EXL3_DECODER_ALU and _plan(w, 2048).decoder == ex.EXL3_DECODER_DENSE
@@ -418,3 +419,19 @@ def test_forward_rotates_in_the_gemm_only_when_short():
                         (expert, 16, True), (expert, 17, False)):
         need = L.exl3_forward_workspace_bytes(ctypes.byref(w), M)
         assert (need == _plan(w, M).workspace) == fused, (M, need, _plan(w, M).workspace)
+
+
+def test_dense_gemm_splits_the_last_round():
+    """The dense GEMM runs its 256 x 256 tiles over whole rounds of the CUs
+    (256 without a GPU) and, when the last round's tiles fit one round as
+    twice as many 256 x 128 tiles, those columns in a second launch."""
+    gu = view(5120, (17408, 17408), 5, 2)  # 136 column tiles
+    for M, launches in ((2048, 3), (4096, 3), (2304, 2), (2560, 3)):
+        # 2048: 1088 tiles, 64 past 4 rounds -> 8 column tiles as 128 narrow;
+        # 4096: 2176, 128 past 8 -> 256 narrow; 2304 (9 row tiles): 200 past
+        # 4 rounds need 23 column tiles = 414 narrow workgroups > 256: no
+        # split; 2560 (10 row tiles): 1360, 80 past 5 -> 8 tiles, 160 narrow
+        p = _plan(gu, M)
+        assert p.decoder == ex.EXL3_DECODER_DENSE and p.launches == launches, (M, p.launches)
+    q = view(5120, (12288,), 6, 2)  # 48 column tiles x 16 row tiles = 768: 3 whole rounds
+    assert _plan(q, 4096).launches == 2

@@ -250,6 +250,44 @@ def test_dense_decoder_matches_alu(bits, cb, M):
         _check(t, y, M=M)
 
 
+# 288 column tiles of 256 x 256 with one 256-row tile: one round plus 32
+# tiles on 256 CUs; odd_shards: 151 + 138 tiles (the first shard ends in a
+# one-block tile), 33 past the round, the split inside the second shard
+@pytest.mark.parametrize("shards", [(73728,), (128 * 301, 128 * 275)], ids=["one_shard", "odd_shards"])
+def test_dense_split_last_round(shards):
+    """The dense GEMM's 256 x 256 launch over whole rounds of the CUs and its
+    256 x 128 launch over the column blocks after it: together the bits of
+    the ALU decoder and within the oracle's bound; run apart through the
+    hook, each writes exactly its own columns."""
+    M = 200
+    lay = wl.small_layer("dense_split", 256, shards, 4, "mcg", (M,), seed=140)
+    t = wl.gen_all(lay)
+    w = weight(t)
+    xr = ex.input_transform(x_dev(t.x[:M]), w.suh)
+    nblk = w.N // 128
+    pl = ex.plan(w, M, decoder=ex.EXL3_DECODER_DENSE)
+    y_alu = bits16(ex.linear(w, xr, torch.bfloat16, decoder=ex.EXL3_DECODER_ALU))
+    y_dense = bits16(ex.linear(w, xr, torch.bfloat16, decoder=ex.EXL3_DECODER_DENSE))
+    assert np.array_equal(y_dense, y_alu)
+    frags = ex.debug_dequant(w)
+    fill = torch.full((M, w.N), -3.0, dtype=torch.bfloat16, device="cuda")
+    mark = bits16(fill)[0, 0]
+    y1, bulk = ex.debug_dense_gemm(w, frags, xr, which=1, out=fill.clone())
+    y2, bulk2 = ex.debug_dense_gemm(w, frags, xr, which=2, out=fill.clone())
+    y3, _ = ex.debug_dense_gemm(w, frags, xr, which=3)
+    torch.cuda.synchronize()
+    banner(f"dense split {shards}: {bulk} of {nblk} column blocks in 256 x 256 tiles, plan {pl}")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert bulk == (512 if len(shards) == 1 else 511) and pl["launches"] == 3
+    assert bulk == bulk2 and 0 < bulk <= nblk
+    c = 128 * bulk
+    b1, b2 = bits16(y1), bits16(y2)
+    assert np.array_equal(b1[:, :c], y_alu[:, :c]) and (b1[:, c:] == mark).all()
+    assert np.array_equal(b2[:, c:], y_alu[:, c:]) and (b2[:, :c] == mark).all()
+    assert np.array_equal(bits16(y3), y_alu)
+    _check(t, y_dense, M=M)
+
+
 @pytest.mark.parametrize("decoder", [ex.EXL3_DECODER_ALU, ex.EXL3_DECODER_TABLE])
 @pytest.mark.parametrize("parts", [1, 3, 8])
 def test_part_sums_stage(decoder, parts):
