@@ -435,3 +435,34 @@ def test_dense_gemm_splits_the_last_round():
         assert p.decoder == ex.EXL3_DECODER_DENSE and p.launches == launches, (M, p.launches)
     q = view(5120, (12288,), 6, 2)  # 48 column tiles x 16 row tiles = 768: 3 whole rounds
     assert _plan(q, 4096).launches == 2
+
+
+def test_forward_argument_checks():
+    """exl3_forward validates every argument before any HIP call: dtypes, M,
+    the x and y pointers, suh, and a workspace short of
+    exl3_forward_workspace_bytes (staged and rotated-in-GEMM plans)."""
+    L = ex.load()
+    w = view(4096, (2048,), 4, 1)
+    need = L.exl3_forward_workspace_bytes(ctypes.byref(w), 16)
+    assert need > 0
+    assert L.exl3_forward(ctypes.byref(w), FAKE, 7, 16, FAKE, 1, FAKE, need, None) == 1
+    assert "x_dtype=7" in last_error()
+    assert L.exl3_forward(ctypes.byref(w), FAKE, 1, 16, FAKE, 3, FAKE, need, None) == 1
+    assert "y_dtype=3" in last_error()
+    assert L.exl3_forward(ctypes.byref(w), FAKE, 1, -1, FAKE, 1, FAKE, need, None) == 1
+    assert L.exl3_forward(ctypes.byref(w), None, 1, 16, FAKE, 1, FAKE, need, None) == 1
+    assert "x" in last_error()
+    assert L.exl3_forward(ctypes.byref(w), FAKE + 2, 1, 16, FAKE, 1, FAKE, need, None) == 1
+    assert L.exl3_forward(ctypes.byref(w), FAKE, 1, 16, None, 1, FAKE, need, None) == 1
+    assert "y" in last_error()
+    assert L.exl3_forward(ctypes.byref(w), FAKE, 1, 16, FAKE, 1, FAKE, need - 16, None) == 3
+    assert "short by 16" in last_error()
+    assert L.exl3_forward(ctypes.byref(w), FAKE, 1, 16, FAKE, 1, FAKE + 8, need, None) == 1
+    assert "aligned" in last_error()
+    nosuh = view(4096, (2048,), 4, 1, suh=0)
+    assert L.exl3_forward(ctypes.byref(nosuh), FAKE, 1, 16, FAKE, 1, FAKE, need, None) == 1
+    assert "suh" in last_error()
+    staged = view(1024, (32768,), 4, 0)  # no workspace of its own: x_rot after the counters
+    n2 = L.exl3_forward_workspace_bytes(ctypes.byref(staged), 16)
+    assert L.exl3_forward(ctypes.byref(staged), FAKE, 1, 16, FAKE, 1, FAKE, n2 - 2, None) == 3
+    assert L.exl3_forward(ctypes.byref(w), None, 1, 0, None, 1, None, 0, None) == 0  # zero rows: nothing
