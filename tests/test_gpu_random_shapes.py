@@ -3,8 +3,10 @@ force on them.  Each case draws K, the shard widths, the width, the codebook
 and the row count from a fixed seed; every forced tile size and fold mode
 that the library accepts for the shape's own part tree must give the
 automatic plan's bits (the tree fixes the arithmetic, the schedule only
-orders the work), and the automatic plan's output must sit within the
-oracle's rounding bound.  Shapes stay small enough for the fp64 oracle."""
+orders the work), exl3_forward from x must give the same rows at the
+case's M and at 1, 5 and 16 rows, and the automatic plan's output must sit
+within the oracle's rounding bound.  Shapes stay small enough for the fp64
+oracle."""
 import numpy as np
 import pytest
 import torch
@@ -67,8 +69,17 @@ def test_random_shape_every_schedule(i):
             ran += 1
         except ex.Exl3Error as e:
             assert e.status in (1, 2)
+    # the whole layer from x (exl3_forward) at the case's M and at a few
+    # rows, where the rotation runs inside the small-tile GEMM when it is
+    # short: a row's bits are the same at every M, so each equals `first`'s
+    fused = 0
+    for Mf in sorted({1, 5, 16, M} & set(range(1, M + 1))):
+        got = bits16(ex.forward(w, x_dev(t.x[:Mf]), torch.bfloat16))
+        assert np.array_equal(got, first[:Mf]), f"case {i} forward M={Mf}"
+        fused += ex.forward_workspace_bytes(w, Mf) == ex.plan(w, Mf)["workspace"]
     ref = olin.reference(t.trellis, t.suh, t.svh, lay.shards, lay.bits, lay.cb, t.x[:M], "bf16")
     res = olin.check(first, ref, t.svh, lay.K, "bf16")
-    banner(f"random case {i}: K={K} shards={shards} {bits}-bit {cb} M={M} plan {auto}: {ran} schedules, {res}")
+    banner(f"random case {i}: K={K} shards={shards} {bits}-bit {cb} M={M} plan {auto}: {ran} schedules, "
+           f"{fused} forward calls rotated in the GEMM, {res}")
     assert ran >= 4
     assert res.ok, str(res)
