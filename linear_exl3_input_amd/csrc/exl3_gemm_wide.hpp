@@ -477,8 +477,13 @@ __global__ __launch_bounds__(512, RW == 64 ? 4 : 1) void gemm_wide_kernel(const 
 // (a wave reads its own back too: keeping it in registers pushed the kernel
 // past 256 VGPRs into spills).  Against two row halves of 256 rows (16 x~
 // fragments and one B fragment read per wave and k-step) that is 96 KB of
-// LDS reads per k-step instead of 136 KB, for the same decode work per wave.  Loads, waits, ring slots and the k-step schedule are
-// gemm_wide_kernel's; same fragments, k order and chains, so the same bits.
+// LDS reads per k-step instead of 136 KB, for the same decode work per wave.
+// The decode runs two k-steps ahead, so a wave reads the next k-step's B
+// fragments between this k-step's products and, after each barrier, waits
+// only for its first x~ fragments (the products of a k-step used to wait for
+// all four B fragments and three x~ fragments of every wave, 56 KB of LDS
+// reads, after the barrier).  Loads and ring slots are gemm_wide_kernel's;
+// same fragments, k order and chains, so the same bits.
 template <int BITS>
 struct Wide4 {
   static constexpr int WAVES = 8;
@@ -491,12 +496,17 @@ struct Wide4 {
   static constexpr int T_OPS = (T_CHUNKS + 64 * LOADERS - 1) / (64 * LOADERS);
   static constexpr int JUNK_CHUNKS = T_OPS * 64 * LOADERS - T_CHUNKS;
   static constexpr int TSLOT_DW = T_CHUNKS * 4;
-  static constexpr int TSLOTS = BITS <= 6 ? 3 : 2;
   static constexpr int A_OPS = BM / 16 / LOADERS;
   static constexpr int ASLOT_DW = BM * 16;
   static constexpr int XB_DW = WAVES * 256;
-  static constexpr int FIXED_DW = TSLOTS * TSLOT_DW + JUNK_CHUNKS * 4 + 2 * XB_DW;
+  // decoded B fragments: during k-step i the waves read k-step i+1's from
+  // buffer (i+1) & 1 and decode k-step i+2's into buffer i & 1, whose
+  // k-step i fragments they read into registers during k-step i-1
+  static constexpr int XBUFS = 2;
   static constexpr int LDS_LIMIT_DW = 160 * 1024 / 4;
+  static constexpr int fixed_dw(int tslots) { return tslots * TSLOT_DW + JUNK_CHUNKS * 4 + XBUFS * XB_DW; }
+  static constexpr int TSLOTS = fixed_dw(3) + 3 * ASLOT_DW <= LDS_LIMIT_DW ? 3 : 2;
+  static constexpr int FIXED_DW = fixed_dw(TSLOTS);
   static constexpr int PF = FIXED_DW + 4 * ASLOT_DW <= LDS_LIMIT_DW ? 3 : 2;
   static constexpr int ASLOTS = PF + 1;
   static constexpr int MAIN_DW = FIXED_DW + ASLOTS * ASLOT_DW;
@@ -509,8 +519,13 @@ struct Wide4 {
   static_assert(T_CHUNKS % 64 == 0, "each direct load lands whole in a stage or in the surplus area");
   static_assert(LDS_DW <= LDS_LIMIT_DW, "LDS budget");
   static constexpr int A_WAIT = A_OPS * (PF - 1);
+  // Trellis stage st + TSLOTS is issued at ks == 2 of stage st (the last
+  // decode from its slot, of k-step 4st+3, ran during ks == 1).  The decode
+  // during k-step i+1 reads stage (i + 3) / 4, which must have landed by the
+  // end of k-step i: the stages issued after it number
+  // TSLOTS - 1 + [ks >= 2] - [ks >= 1].
   static constexpr int t_wait(int ks) {
-    return T_OPS * (TSLOTS - 1 + (ks == 3 ? 1 : 0) - (ks >= 2 ? 1 : 0));
+    return T_OPS * (TSLOTS - 1 + (ks >= 2 ? 1 : 0) - (ks >= 1 ? 1 : 0));
   }
 };
 
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide4_kernel(const GemmParams p) 
   uint32_t *const tring = lds;
   uint32_t *const junk = lds + TSLOTS * W::TSLOT_DW;
   uint32_t *const xbuf = junk + W::JUNK_CHUNKS * 4;
-  uint32_t *const aring = xbuf + 2 * W::XB_DW;
+  uint32_t *const aring = xbuf + W::XBUFS * W::XB_DW;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -644,7 +659,15 @@ __global__ __launch_bounds__(512, 1) void gemm_wide4_kernel(const GemmParams p) 
   wait_vmcnt<0>();
   barrier_lds();
   *(u32x4_t *)xb_own0 = decode_own(tring, 0);
+  *(u32x4_t *)(xb_own0 + W::XB_DW) = decode_own(tring, 1);
   barrier_lds();
+  // B[i & 1]: the column half's four fragments (this wave's own among them)
+  // of k-step i = 4 st + ks, read during k-step i-1 from the buffer the
+  // waves decoded them into during k-step i-2, so that a k-step's products
+  // wait after its barrier only for its first x~ reads
+  half8_t B[2][NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) B[0][f] = *(const half8_t *)(xb_half0 + f * 512);
 
   int st = 0;
   int ts0 = 0;
@@ -655,27 +678,25 @@ __global__ __launch_bounds__(512, 1) void gemm_wide4_kernel(const GemmParams p) 
       const int ts1 = ts0 == TSLOTS - 1 ? 0 : ts0 + 1;
       auto kstep = [&](auto ks_c) __attribute__((always_inline)) {
         constexpr int ks = decltype(ks_c)::value;
+        constexpr int cur = ks & 1;
         const int i = 4 * st + ks;
         const int as = (as_cur + ks) % ASLOTS;
         const int as_pf = as == 0 ? ASLOTS - 1 : as - 1;
         if constexpr (PH == 0) issue_a(i + PF, as_pf);
-        else if constexpr (ks == 3) issue_trellis(st + TSLOTS, ts0);
+        else if constexpr (ks == 2) issue_trellis(st + TSLOTS, ts0);
         asm volatile("" ::: "memory");
-        // the column half's four fragments (this wave's own among them),
-        // decoded during the last k-step
-        half8_t B[NF];
-        const uint32_t *xb = xb_half0 + (i & 1) * W::XB_DW;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) B[f] = *(const half8_t *)(xb + f * 512);
-        const uint32_t *tslot = tring + (ks < 3 ? ts0 : ts1) * W::TSLOT_DW;
-        const uint32_t *tp = tslot + ((ks + 1) & 3) * 2 * WG_NT * W::TSTRIDE + t_lane;
+        // the decode of k-step i+2: stage st (ks < 2) or st+1
+        const uint32_t *tslot = tring + (ks < 2 ? ts0 : ts1) * W::TSLOT_DW;
+        const uint32_t *tp = tslot + ((ks + 2) & 3) * 2 * WG_NT * W::TSTRIDE + t_lane;
         uint32_t X[W::NX], Y[W::NY];
 #pragma unroll
         for (int q = 0; q < W::NX; ++q) X[q] = tp[q];
         const uint32_t *as_p = a_lane + as * W::ASLOT_DW;
+        const uint32_t *xbn = xb_half0 + (cur ^ 1) * W::XB_DW;  // k-step i+1's fragments
         u32x4_t nb4;
-        // x~ fragments in a ring read three ahead of their four products;
-        // the next k-step's decode cut into six pieces between them
+        // x~ fragments in a ring read three ahead of their four products,
+        // the next k-step's B fragments one per two products, and the decode
+        // of k-step i+2 cut into six pieces between them
         constexpr int RD = 3;
         __builtin_amdgcn_sched_barrier(0);
         half8_t af[4];
@@ -684,14 +705,15 @@ __global__ __launch_bounds__(512, 1) void gemm_wide4_kernel(const GemmParams p) 
         static_for<0, MF>([&](auto mt_c) {
           constexpr int mt = decltype(mt_c)::value;
           if constexpr (mt + RD < MF) af[(mt + RD) % 4] = *(const half8_t *)(as_p + (mt + RD) * 256);
+          if constexpr (mt % 2 == 1) B[cur ^ 1][mt / 2] = *(const half8_t *)(xbn + (mt / 2) * 512);
 #pragma unroll
           for (int f = 0; f < NF; ++f)
-            acc[mt][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt % 4], B[f], acc[mt][f], 0, 0, 0);
+            acc[mt][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt % 4], B[cur][f], acc[mt][f], 0, 0, 0);
           static_for<mt * 6 / MF, (mt + 1) * 6 / MF>([&](auto pc) {
             constexpr int piece = decltype(pc)::value;
             if constexpr (piece == 0) raw_normalize<BITS>(X, sel, sh, Y);
             else if constexpr (piece < 5) nb4[piece - 1] = frag_pair<BITS, CB, piece - 1>(Y);
-            else *(u32x4_t *)(xb_own0 + ((i + 1) & 1) * W::XB_DW) = nb4;
+            else *(u32x4_t *)(xb_own0 + cur * W::XB_DW) = nb4;  // k-step i+2's
           });
           __builtin_amdgcn_sched_barrier(0);
         });
