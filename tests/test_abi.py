@@ -466,3 +466,27 @@ def test_forward_argument_checks():
     n2 = L.exl3_forward_workspace_bytes(ctypes.byref(staged), 16)
     assert L.exl3_forward(ctypes.byref(staged), FAKE, 1, 16, FAKE, 1, FAKE, n2 - 2, None) == 3
     assert L.exl3_forward(ctypes.byref(w), None, 1, 0, None, 1, None, 0, None) == 0  # zero rows: nothing
+
+
+def test_dense_gemm_hook_checks():
+    """exl3_debug_dense_gemm validates which, y_dtype, M, its pointers and
+    the fragment bytes, and refuses plans that are not one part fused."""
+    L = ex.load()
+    gu = view(5120, (17408, 17408), 5, 2)
+    nbytes = 5120 * 34816 * 2
+    bulk = ctypes.c_int32(-1)
+    assert L.exl3_debug_dense_gemm(ctypes.byref(gu), FAKE, nbytes, FAKE, 2048, FAKE, 1, 0, ctypes.byref(bulk),
+                                   None) == 1
+    assert "which=0" in last_error()
+    assert L.exl3_debug_dense_gemm(ctypes.byref(gu), FAKE, nbytes, FAKE, 2048, FAKE, 5, 3, None, None) == 1
+    assert "y_dtype=5" in last_error()
+    assert L.exl3_debug_dense_gemm(ctypes.byref(gu), FAKE, nbytes, FAKE, 0, FAKE, 1, 3, None, None) == 1
+    assert L.exl3_debug_dense_gemm(ctypes.byref(gu), None, nbytes, FAKE, 2048, FAKE, 1, 3, None, None) == 1
+    assert "frags" in last_error()
+    assert L.exl3_debug_dense_gemm(ctypes.byref(gu), FAKE, nbytes - 2, FAKE, 2048, FAKE, 1, 3, None, None) == 3
+    assert "short by 2" in last_error()
+    down = view(17408, (5120,), 6, 2)  # 17 parts folded in registers: not one part a workgroup
+    assert L.exl3_debug_dense_gemm(ctypes.byref(down), FAKE, 17408 * 5120 * 2, FAKE, 4096, FAKE, 1, 3, None,
+                                   None) == 2
+    assert "one-part fused" in last_error()
+    assert bulk.value == -1  # nothing written on a refused call
