@@ -79,7 +79,7 @@ def test_input_transform_one_hot_closed_form():
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("P,G,M,N", [(1, 1, 3, 128), (3, 3, 17, 384), (8, 8, 64, 256), (8, 2, 9, 256),
                                      (12, 3, 5, 128), (16, 16, 7, 128), (17, 17, 1, 256), (20, 4, 64, 128),
-                                     (24, 8, 65, 128)])
+                                     (24, 8, 65, 128), (17, 17, 300, 128), (10, 5, 129, 256)])
 def test_output_stage_bit_exact(out_dtype, P, G, M, N):
     banner(f"epilogue {out_dtype} P={P} G={G} M={M} N={N}")
     rng = np.random.default_rng(2000 + P + M + N)
